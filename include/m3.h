@@ -1,0 +1,186 @@
+/*
+ * m3.h -- C ABI of libm3.so: the Mamba-3 SSM core recurrence on AMD MI355X (gfx950).
+ *
+ * The operation. Per (batch b, head h) the state h_t is an N x P fp32 matrix
+ * whose rows (2k, 2k+1) hold one complex number per column (complex-valued SSM
+ * with decay A and rotation frequency omega, real part taken at the output:
+ * "复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构", §2.1). Each token t
+ * brings x_t (P x R), B_t and C_t (N x R), a step dt_t > 0 and a trapezoid
+ * weight lambda_t in [0, 1]. With alpha = exp(dt*A_h), gamma = lambda*dt and
+ * delta = (1 - lambda)*dt (exponential-trapezoidal rule, same digest §2.2 and
+ * "Mamba-3架构技术解析：新一代语言建模的范式转移" §2.1):
+ *
+ *   h_t = alpha_t Rot(dt_t omega_h) (h_{t-1} + delta_t B_{t-1} x_{t-1}^T) + gamma_t B_t x_t^T
+ *   y_t = h_t^T C_t + D_h x_t                    (y_t is P x R; MIMO rank R, digest §2.3)
+ *
+ * where Rot(theta) turns pair k by +theta_k = dt_t * omega_{h,k} (the 2x2 block
+ * [[cos, -sin], [sin, cos]] on rows (2k, 2k+1)). Written in the rotating frame
+ * (B and C turned by the cumulative angle, data-dependent RoPE: arXiv 2603.15569
+ * summary page, contribution 2) this is h_t = alpha_t h_{t-1} +
+ * beta_t B_{t-1}x_{t-1}^T + gamma_t B_t x_t^T with beta_t = delta_t alpha_t.
+ * (B_{t-1}, x_{t-1}) of the first token is the "carry": zero unless given.
+ *
+ * Layout. All tensors are dense, row-major, device memory, 16-byte aligned:
+ *   x, y        [b][L][H][R][P]   io dtype (bf16 or fp32)
+ *   B, C        [b][L][G][R][N]   io dtype; head h uses group h / (H/G)
+ *   dt, lambda  [b][L][H]         fp32
+ *   A, D        [H]               fp32 (A < 0 decays)
+ *   omega       [H][N/2]          fp32
+ *   h0, h_out   [b][H][N][P]      fp32 (the state is always fp32)
+ *   carry_B     [b][G][R][N]      io dtype; carry_x [b][H][R][P] io dtype
+ * Decode-step tensors drop the L axis.
+ *
+ * Ownership. The caller owns every buffer (inputs, outputs, workspace, decode
+ * state); the library allocates no memory and keeps no global state apart from
+ * a thread-local error message. Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL is the null stream): a device fault surfaces at the
+ * caller's next synchronisation. Nothing throws across this ABI.
+ *
+ * Errors. Every argument is checked before any HIP call; a bad argument returns
+ * a status != M3_OK and launches nothing. m3_last_error() then names the
+ * argument. Launch failures return M3_EHIP.
+ */
+#ifndef M3_H
+#define M3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum m3_dtype { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+typedef enum m3_status {
+    M3_OK = 0,
+    M3_EINVAL = 1,       /* null required pointer, bad size, odd N, R < 1, chunk < 1, G not dividing H, y aliasing an input */
+    M3_ESHAPE = 2,       /* inconsistent sizes (e.g. R differs from the decode state's) */
+    M3_EDTYPE = 3,       /* unknown io dtype */
+    M3_EALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+    M3_EUNSUPPORTED = 5, /* valid but not implemented (chunk above 4096) */
+    M3_EHIP = 6,         /* a HIP runtime call or kernel launch failed */
+    M3_EWORKSPACE = 7    /* workspace missing or smaller than m3_prefill_workspace_size() */
+} m3_status;
+
+/* Problem sizes. seqlen is ignored by the decode calls. */
+typedef struct m3_dims {
+    int64_t batch;    /* b >= 0 */
+    int64_t seqlen;   /* L >= 0 */
+    int32_t heads;    /* H >= 1 */
+    int32_t groups;   /* G >= 1, divides H */
+    int32_t headdim;  /* P >= 1 */
+    int32_t dstate;   /* N >= 2, even (N/2 rotation pairs) */
+} m3_dims;
+
+/* How m3_prefill will split the work (all integers, exact). */
+typedef struct m3_plan {
+    int64_t n_chunks;        /* ceil(L / chunk) */
+    int64_t last_chunk_len;  /* L - (n_chunks - 1) * chunk, 0 when L == 0 */
+    int32_t segments;        /* sequence segments per (b, h) walked in parallel */
+    int64_t chunks_per_segment;
+    int32_t path;            /* M3_PATH_* below */
+    size_t workspace_bytes;  /* what m3_prefill needs (0 allowed when this is 0) */
+} m3_plan;
+
+enum { M3_PATH_GENERIC = 0, M3_PATH_MFMA = 1 };
+
+/*
+ * m3_prefill -- chunked evaluation of the recurrence over L tokens.
+ *
+ * Passage: the parallel form of the trapezoid recurrence, whose mask is the
+ * cumulative decay times a width-2 convolution ("复值SSM × 广义梯形离散 × MIMO",
+ * Fig. 2), evaluated chunk by chunk with the fp32 state passed between chunks.
+ *
+ * x, dt, A, omega, lambda, B, C, D: inputs as laid out above (required).
+ * R:      MIMO rank (>= 1).  chunk: tokens per chunk (1 .. 4096); any value gives
+ *         the same result up to rounding; 64 is the tuned one.
+ * h0:     initial state, or NULL for zero.
+ * y:      output [b][L][H][R][P], must not overlap any input.
+ * h_out:  final state h_L, or NULL. May alias h0.
+ * dims:   sizes; io_dtype: dtype of x, B, C, y, carry_B, carry_x.
+ * carry_B, carry_x: the token before the first (both or neither), else NULL.
+ * workspace, workspace_bytes: device scratch of at least
+ *         m3_prefill_workspace_size() bytes (may be NULL when that is 0). The
+ *         library clears what it needs on `stream`; calls sharing one
+ *         workspace must be ordered on one stream.
+ */
+m3_status m3_prefill(const void* x, const float* dt, const float* A, const float* omega,
+                     const float* lambda, const void* B, const void* C, const float* D,
+                     int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
+                     const m3_dims* dims, m3_dtype io_dtype,
+                     const void* carry_B, const void* carry_x,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes m3_prefill needs for these sizes (0 on invalid sizes). Host only. */
+size_t m3_prefill_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype);
+
+/* Fill *plan with the integers m3_prefill will use. Host only, no HIP call. */
+m3_status m3_prefill_plan(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype,
+                          m3_plan* plan);
+
+/*
+ * Decode state: the fp32 state plus the previous token's (B, x), which the
+ * trapezoid rule needs for the next step. Buffers are caller-owned device memory:
+ *   h        [b][H][N][P] fp32
+ *   carry_B  [2][b][G][R][N] io dtype  (two slots: slot (t+1)&1 holds token t-1)
+ *   carry_x  [2][b][H][R][P] io dtype
+ * t counts the tokens consumed so far (a prefill of L tokens hands over t = L).
+ */
+typedef struct m3_decode_state {
+    float* h;
+    void* carry_B;
+    void* carry_x;
+    int64_t t;
+    m3_dims dims;
+    int32_t R;
+    m3_dtype io_dtype;
+} m3_decode_state;
+
+/* Bytes of the carry buffers (which = 0: carry_B, 1: carry_x). Host only. */
+size_t m3_decode_carry_bytes(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int32_t which);
+
+/*
+ * m3_decode_state_init -- bind caller buffers and set the starting point.
+ *
+ * Copies h0 (or zeros) into h_buf and (B_last, x_last) (or zeros) into the
+ * carry slot read by the next step, on `stream`. B_last [b][G][R][N] and x_last
+ * [b][H][R][P] are the last token already consumed (e.g. the prefill's last
+ * token); both or neither. t0 >= 0 is the number of tokens already consumed.
+ * h0 may equal h_buf (then it is left in place).
+ */
+m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t R, m3_dtype io_dtype,
+                               float* h_buf, void* carry_B_buf, void* carry_x_buf,
+                               const float* h0, const void* B_last, const void* x_last, int64_t t0,
+                               void* stream);
+
+/*
+ * m3_decode_step -- one token of the recurrence for every (b, h), in place.
+ *
+ * Passage: the recurrent (decode) form; the state is read and written once per
+ * token, and MIMO raises the work per state byte without more state traffic
+ * ("复值SSM × 广义梯形离散 × MIMO", §2.3 and §3.3; "Mamba-3架构技术解析", §2.3).
+ *
+ * x_t [b][H][R][P], B_t/C_t [b][G][R][N] (io dtype), dt_t/lambda_t [b][H] fp32,
+ * A, D [H], omega [H][N/2]; y_t [b][H][R][P] io dtype (must not overlap the
+ * inputs or the state). R must equal st->R. On success st->t is incremented.
+ * Steps on one state must be ordered on one stream.
+ */
+m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t, const float* A,
+                         const float* omega, const float* lambda_t, const void* B_t, const void* C_t,
+                         const float* D, int32_t R, void* y_t, void* stream);
+
+/* Static text for a status code. */
+const char* m3_status_string(m3_status s);
+
+/* Detail of the last error on this thread ("" when none). */
+const char* m3_last_error(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+#define M3_ABI_VERSION 1
+int32_t m3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* M3_H */

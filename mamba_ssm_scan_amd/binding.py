@@ -1,0 +1,240 @@
+"""ctypes binding of libm3.so: torch tensors in, the C entry points of include/m3.h called.
+
+Argument marshalling only: shapes and dtypes are read off the tensors, outputs
+and the workspace are allocated with torch (device memory is torch's job), and
+the call goes to the HIP library on torch's current stream. There is no other
+implementation behind these functions: if libm3.so is missing they raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libm3.so")
+
+M3_F32, M3_BF16 = 0, 1
+M3_PATH_GENERIC, M3_PATH_MFMA = 0, 1
+STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EALIGN",
+          5: "M3_EUNSUPPORTED", 6: "M3_EHIP", 7: "M3_EWORKSPACE"}
+
+# every symbol include/m3.h declares
+EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_decode_carry_bytes",
+           "m3_decode_state_init", "m3_decode_step", "m3_status_string", "m3_last_error",
+           "m3_abi_version"]
+
+
+class M3Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32)]
+
+
+class M3Plan(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int64), ("last_chunk_len", ctypes.c_int64),
+                ("segments", ctypes.c_int32), ("chunks_per_segment", ctypes.c_int64),
+                ("path", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class M3DecodeState(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("carry_B", ctypes.c_void_p), ("carry_x", ctypes.c_void_p),
+                ("t", ctypes.c_int64), ("dims", M3Dims), ("R", ctypes.c_int32), ("io_dtype", ctypes.c_int)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libm3.so (no GPU needed to load it). Raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m mamba_ssm_scan_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dims_p = ctypes.POINTER(M3Dims)
+    lib.m3_prefill.argtypes = [vp] * 8 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.m3_prefill.restype = ctypes.c_int
+    lib.m3_prefill_workspace_size.argtypes = [dims_p, i32, i32, ctypes.c_int]
+    lib.m3_prefill_workspace_size.restype = sz
+    lib.m3_prefill_plan.argtypes = [dims_p, i32, i32, ctypes.c_int, ctypes.POINTER(M3Plan)]
+    lib.m3_prefill_plan.restype = ctypes.c_int
+    lib.m3_decode_carry_bytes.argtypes = [dims_p, i32, ctypes.c_int, i32]
+    lib.m3_decode_carry_bytes.restype = sz
+    lib.m3_decode_state_init.argtypes = [ctypes.POINTER(M3DecodeState), dims_p, i32, ctypes.c_int,
+                                         vp, vp, vp, vp, vp, vp, i64, vp]
+    lib.m3_decode_state_init.restype = ctypes.c_int
+    lib.m3_decode_step.argtypes = [ctypes.POINTER(M3DecodeState)] + [vp] * 8 + [i32, vp, vp]
+    lib.m3_decode_step.restype = ctypes.c_int
+    lib.m3_status_string.argtypes = [ctypes.c_int]
+    lib.m3_status_string.restype = ctypes.c_char_p
+    lib.m3_last_error.argtypes = []
+    lib.m3_last_error.restype = ctypes.c_char_p
+    lib.m3_abi_version.argtypes = []
+    lib.m3_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def check(status: int):
+    if status != 0:
+        raise M3Error(status, load().m3_last_error().decode())
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return M3_BF16
+    if dtype == torch.float32:
+        return M3_F32
+    raise TypeError(f"io dtype must be bfloat16 or float32, got {dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype] = None, shape=None):
+    """Check a tensor argument; return it, or an aligned copy if its data is not 16-byte aligned."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.data_ptr() % 16:
+        t = t.clone()
+    return t
+
+
+def _need_out(t, name, dtype, shape):
+    """Outputs are written in place, so they must already be aligned."""
+    if t is None:
+        return
+    if _need(t, name, dtype, shape) is not t:
+        raise ValueError(f"{name} must be 16-byte aligned")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dims(batch, seqlen, heads, groups, headdim, dstate) -> M3Dims:
+    return M3Dims(batch, seqlen, heads, groups, headdim, dstate)
+
+
+def plan(d: M3Dims, R: int, chunk: int, io_dtype: int) -> M3Plan:
+    p = M3Plan()
+    check(load().m3_prefill_plan(ctypes.byref(d), R, chunk, io_dtype, ctypes.byref(p)))
+    return p
+
+
+def prefill(x, dt, A, omega, lam, B, C, D, R: int, chunk: int, h0=None, *, carry_B=None, carry_x=None,
+            y=None, h_out=None, workspace=None, return_state: bool = True, stream=None):
+    """m3_prefill on torch device tensors; returns (y, h_out).
+
+    x [b][L][H][R][P], B/C [b][L][G][R][N] (bf16 or fp32, one dtype), dt/lam
+    [b][L][H] fp32, A/D [H], omega [H][N/2], h0 [b][H][N][P] fp32 or None.
+    """
+    if x.dim() != 5 or B.dim() != 5:
+        raise ValueError("x must be [b][L][H][R][P] and B [b][L][G][R][N]")
+    b, L, H, R_, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    if R_ != R or B.shape[3] != R:
+        raise ValueError(f"rank mismatch: R={R}, x has {R_}, B has {B.shape[3]}")
+    io = x.dtype
+    x = _need(x, "x", io)
+    B = _need(B, "B", io, (b, L, G, R, N))
+    C = _need(C, "C", io, (b, L, G, R, N))
+    dt = _need(dt, "dt", torch.float32, (b, L, H))
+    lam = _need(lam, "lambda", torch.float32, (b, L, H))
+    A = _need(A, "A", torch.float32, (H,))
+    D = _need(D, "D", torch.float32, (H,))
+    omega = _need(omega, "omega", torch.float32, (H, N // 2))
+    h0 = _need(h0, "h0", torch.float32, (b, H, N, P))
+    carry_B = _need(carry_B, "carry_B", io, (b, G, R, N))
+    carry_x = _need(carry_x, "carry_x", io, (b, H, R, P))
+    if y is None:
+        y = torch.empty_like(x)
+    _need_out(y, "y", io, x.shape)
+    if h_out is None and return_state:
+        h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=x.device)
+    _need_out(h_out, "h_out", torch.float32, (b, H, N, P))
+    d = dims(b, L, H, G, P, N)
+    code = _io_code(io)
+    lib = load()
+    need = lib.m3_prefill_workspace_size(ctypes.byref(d), R, chunk, code)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.m3_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(omega), _ptr(lam), _ptr(B), _ptr(C), _ptr(D),
+                         R, chunk, _ptr(h0), _ptr(y), _ptr(h_out), ctypes.byref(d), code,
+                         _ptr(carry_B), _ptr(carry_x), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y, h_out
+
+
+class DecodeState:
+    """Caller-owned decode state: fp32 h plus the two carry slots, bound to libm3."""
+
+    def __init__(self, batch, heads, groups, headdim, dstate, R, io_dtype=torch.bfloat16, device="cuda",
+                 h0=None, B_last=None, x_last=None, t0: int = 0, stream=None):
+        self.dims = dims(batch, 1, heads, groups, headdim, dstate)
+        self.R = R
+        self.io_dtype = io_dtype
+        self.h = torch.empty((batch, heads, dstate, headdim), dtype=torch.float32, device=device)
+        self.carry_B = torch.empty((2, batch, groups, R, dstate), dtype=io_dtype, device=device)
+        self.carry_x = torch.empty((2, batch, heads, R, headdim), dtype=io_dtype, device=device)
+        h0 = _need(h0, "h0", torch.float32, self.h.shape)
+        B_last = _need(B_last, "B_last", io_dtype, (batch, groups, R, dstate))
+        x_last = _need(x_last, "x_last", io_dtype, (batch, heads, R, headdim))
+        self._st = M3DecodeState()
+        check(load().m3_decode_state_init(ctypes.byref(self._st), ctypes.byref(self.dims), R, _io_code(io_dtype),
+                                          _ptr(self.h), _ptr(self.carry_B), _ptr(self.carry_x), _ptr(h0),
+                                          _ptr(B_last), _ptr(x_last), t0, _stream(stream)))
+        self._keep = (h0, B_last, x_last)
+
+    @property
+    def t(self) -> int:
+        return int(self._st.t)
+
+    def step(self, x_t, dt_t, A, omega, lam_t, B_t, C_t, D, y_t=None, stream=None):
+        """m3_decode_step: one token for every (b, h); returns y_t [b][H][R][P]."""
+        b, H, G = self.dims.batch, self.dims.heads, self.dims.groups
+        P, N, R = self.dims.headdim, self.dims.dstate, self.R
+        x_t = _need(x_t, "x_t", self.io_dtype, (b, H, R, P))
+        B_t = _need(B_t, "B_t", self.io_dtype, (b, G, R, N))
+        C_t = _need(C_t, "C_t", self.io_dtype, (b, G, R, N))
+        dt_t = _need(dt_t, "dt_t", torch.float32, (b, H))
+        lam_t = _need(lam_t, "lambda_t", torch.float32, (b, H))
+        A = _need(A, "A", torch.float32, (H,))
+        D = _need(D, "D", torch.float32, (H,))
+        omega = _need(omega, "omega", torch.float32, (H, N // 2))
+        if y_t is None:
+            y_t = torch.empty_like(x_t)
+        _need_out(y_t, "y_t", self.io_dtype, x_t.shape)
+        check(load().m3_decode_step(ctypes.byref(self._st), _ptr(x_t), _ptr(dt_t), _ptr(A), _ptr(omega),
+                                    _ptr(lam_t), _ptr(B_t), _ptr(C_t), _ptr(D), R, _ptr(y_t), _stream(stream)))
+        return y_t
+
+    def step_raw(self, x_t, dt_t, A, omega, lam_t, B_t, C_t, D, y_t, stream_handle: ctypes.c_void_p):
+        """The same call with no checks on the Python side (shapes were checked once by the caller)."""
+        check(_lib.m3_decode_step(ctypes.byref(self._st), ctypes.c_void_p(x_t), ctypes.c_void_p(dt_t),
+                                  ctypes.c_void_p(A), ctypes.c_void_p(omega), ctypes.c_void_p(lam_t),
+                                  ctypes.c_void_p(B_t), ctypes.c_void_p(C_t), ctypes.c_void_p(D), self.R,
+                                  ctypes.c_void_p(y_t), stream_handle))

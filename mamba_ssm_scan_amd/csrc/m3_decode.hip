@@ -1,0 +1,224 @@
+// m3_decode.hip -- one recurrent step of the Mamba-3 SSM for every (batch, head).
+//
+// Per (b, h), with alpha = e^{dt A}, gamma = lambda dt, delta = (1 - lambda) dt
+// (exponential-trapezoidal rule, "复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构"
+// §2.2) and the rotation of pair k by +dt*omega_k (complex state, same digest §2.1):
+//
+//   g   = h + delta * B_prev x_prev^T            (previous token, from the carry slot)
+//   h'  = alpha * Rot(dt omega) g + gamma * B x^T   (rank-R: N x R times R x P, §2.3)
+//   y   = h'^T C + D x
+//
+// The fp32 state is read and written once (the step is bound by that traffic:
+// "Mamba-3架构技术解析：新一代语言建模的范式转移" §2.3 on decode being state-I/O
+// bound). The current (B, x) is copied into the other carry slot for the next
+// step; slots alternate, so no workgroup overwrites a value another one of the
+// same launch still reads (B is shared by the H/G heads of a group).
+#include "m3_device.h"
+#include "m3_internal.h"
+
+namespace m3 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// N = 128, P = 64: thread (kk, q) owns rows (2k, 2k+1), k = kk + 16*it, it < 4,
+// and columns 4q..4q+3, loaded and stored as float4 (a wave covers four 256-byte
+// row segments per access).
+template <typename T, int R>
+__global__ void __launch_bounds__(kThreads)
+decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
+                       const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+                       const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
+                       const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
+                       int G) {
+    constexpr int N = 128, P = 64, K = 64;
+    __shared__ float sB[R][N], sBp[R][N], sC[R][N];
+    __shared__ float sx[R][P], sxp[R][P];
+    __shared__ float red[kThreads / 64][R][P];
+
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const int g = h / (H / G);
+    const int64_t bg = b * G + g;
+    float* hs = hstate + bh * (N * P);
+    const int q = tid & 15, kk = tid >> 4;
+
+    float4 v0[4], v1[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int k = kk + 16 * it;
+        v0[it] = *reinterpret_cast<const float4*>(hs + (2 * k) * P + 4 * q);
+        v1[it] = *reinterpret_cast<const float4*>(hs + (2 * k + 1) * P + 4 * q);
+    }
+
+    const T* Bt = B + bg * (R * N);
+    const T* Ct = C + bg * (R * N);
+    const T* Bp = carry_B + (int64_t(rd_slot) * nb * G + bg) * (R * N);
+    const T* xt = x + bh * (R * P);
+    const T* xp = carry_x + (int64_t(rd_slot) * nb * H + bh) * (R * P);
+    for (int e = tid; e < R * N; e += kThreads) {
+        (&sB[0][0])[e] = Io<T>::load(Bt, e);
+        (&sBp[0][0])[e] = Io<T>::load(Bp, e);
+        (&sC[0][0])[e] = Io<T>::load(Ct, e);
+    }
+    for (int e = tid; e < R * P; e += kThreads) {
+        (&sx[0][0])[e] = Io<T>::load(xt, e);
+        (&sxp[0][0])[e] = Io<T>::load(xp, e);
+    }
+    const float d = dt[bh], lm = lam[bh];
+    const float alpha = expf(d * A[h]);
+    const float gamma = lm * d, delta = (1.f - lm) * d;
+    __syncthreads();
+
+    float yacc[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) yacc[r][c] = 0.f;
+
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int k = kk + 16 * it;
+        float sn, cs;
+        sincosf(d * omega[int64_t(h) * K + k], &sn, &cs);
+        float e0[4] = {v0[it].x, v0[it].y, v0[it].z, v0[it].w};
+        float e1[4] = {v1[it].x, v1[it].y, v1[it].z, v1[it].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int p = 4 * q + c;
+            float up0 = 0.f, up1 = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                up0 += sBp[r][2 * k] * sxp[r][p];
+                up1 += sBp[r][2 * k + 1] * sxp[r][p];
+                u0 += sB[r][2 * k] * sx[r][p];
+                u1 += sB[r][2 * k + 1] * sx[r][p];
+            }
+            const float g0 = e0[c] + delta * up0, g1 = e1[c] + delta * up1;
+            const float n0 = alpha * (cs * g0 - sn * g1) + gamma * u0;
+            const float n1 = alpha * (sn * g0 + cs * g1) + gamma * u1;
+            e0[c] = n0;
+            e1[c] = n1;
+#pragma unroll
+            for (int r = 0; r < R; ++r) yacc[r][c] += n0 * sC[r][2 * k] + n1 * sC[r][2 * k + 1];
+        }
+        *reinterpret_cast<float4*>(hs + (2 * k) * P + 4 * q) = make_float4(e0[0], e0[1], e0[2], e0[3]);
+        *reinterpret_cast<float4*>(hs + (2 * k + 1) * P + 4 * q) = make_float4(e1[0], e1[1], e1[2], e1[3]);
+    }
+
+    // reduce over the 16 row groups: 4 in a wave (lanes 16 apart), then 4 waves
+    const int wave = tid >> 6;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float v = yacc[r][c];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if ((tid & 63) < 16) red[wave][r][4 * q + c] = v;
+        }
+    __syncthreads();
+    const float Dh = D[h];
+    for (int e = tid; e < R * P; e += kThreads) {
+        const int r = e / P, p = e % P;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) s += red[w][r][p];
+        Io<T>::store(y, bh * (R * P) + e, s + Dh * sx[r][p]);
+    }
+
+    // this token becomes the carry of the next step
+    const int wr = rd_slot ^ 1;
+    for (int e = tid; e < R * P; e += kThreads) carry_x[(int64_t(wr) * nb * H + bh) * (R * P) + e] = xt[e];
+    if (h % (H / G) == 0)
+        for (int e = tid; e < R * N; e += kThreads) carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = Bt[e];
+}
+
+// Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
+                      const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+                      const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
+                      const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
+                      int G, int P, int N, int R) {
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const int g = h / (H / G);
+    const int64_t bg = b * G + g;
+    const int K = N / 2;
+    float* hs = hstate + bh * int64_t(N) * P;
+    const T* Bt = B + bg * int64_t(R) * N;
+    const T* Ct = C + bg * int64_t(R) * N;
+    const T* Bp = carry_B + (int64_t(rd_slot) * nb * G + bg) * int64_t(R) * N;
+    const T* xt = x + bh * int64_t(R) * P;
+    const T* xp = carry_x + (int64_t(rd_slot) * nb * H + bh) * int64_t(R) * P;
+    const float d = dt[bh], lm = lam[bh];
+    const float alpha = expf(d * A[h]);
+    const float gamma = lm * d, delta = (1.f - lm) * d;
+
+    for (int e = tid; e < K * P; e += kThreads) {
+        const int k = e / P, p = e % P;
+        float up0 = 0.f, up1 = 0.f, u0 = 0.f, u1 = 0.f;
+        for (int r = 0; r < R; ++r) {
+            const float xpv = Io<T>::load(xp, int64_t(r) * P + p), xv = Io<T>::load(xt, int64_t(r) * P + p);
+            up0 += Io<T>::load(Bp, int64_t(r) * N + 2 * k) * xpv;
+            up1 += Io<T>::load(Bp, int64_t(r) * N + 2 * k + 1) * xpv;
+            u0 += Io<T>::load(Bt, int64_t(r) * N + 2 * k) * xv;
+            u1 += Io<T>::load(Bt, int64_t(r) * N + 2 * k + 1) * xv;
+        }
+        float sn, cs;
+        sincosf(d * omega[int64_t(h) * K + k], &sn, &cs);
+        const float g0 = hs[int64_t(2 * k) * P + p] + delta * up0;
+        const float g1 = hs[int64_t(2 * k + 1) * P + p] + delta * up1;
+        hs[int64_t(2 * k) * P + p] = alpha * (cs * g0 - sn * g1) + gamma * u0;
+        hs[int64_t(2 * k + 1) * P + p] = alpha * (sn * g0 + cs * g1) + gamma * u1;
+    }
+    __syncthreads();
+    const float Dh = D[h];
+    for (int e = tid; e < R * P; e += kThreads) {
+        const int r = e / P, p = e % P;
+        float s = 0.f;
+        for (int n = 0; n < N; ++n) s += hs[int64_t(n) * P + p] * Io<T>::load(Ct, int64_t(r) * N + n);
+        Io<T>::store(y, bh * int64_t(R) * P + e, s + Dh * Io<T>::load(xt, e));
+    }
+    const int wr = rd_slot ^ 1;
+    for (int e = tid; e < R * P; e += kThreads) carry_x[(int64_t(wr) * nb * H + bh) * int64_t(R) * P + e] = xt[e];
+    if (h % (H / G) == 0)
+        for (int e = tid; e < R * N; e += kThreads)
+            carry_B[(int64_t(wr) * nb * G + bg) * int64_t(R) * N + e] = Bt[e];
+}
+
+template <typename T>
+hipError_t launch_t(const DecodeArgs& a) {
+    const dim3 grid(unsigned(a.b * a.H));
+    T* cB = static_cast<T*>(a.carry_B);
+    T* cx = static_cast<T*>(a.carry_x);
+    const T* x = static_cast<const T*>(a.x);
+    const T* B = static_cast<const T*>(a.B);
+    const T* C = static_cast<const T*>(a.C);
+    T* y = static_cast<T*>(a.y);
+    if (a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4)) {
+        auto kern = a.R == 1 ? decode_n128_p64_kernel<T, 1>
+                  : a.R == 2 ? decode_n128_p64_kernel<T, 2> : decode_n128_p64_kernel<T, 4>;
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A,
+                           a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+    } else {
+        hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x,
+                           a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G, a.P, a.N, a.R);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a) {
+    if (a.b * a.H > 0x7fffffff) return hipErrorInvalidValue;
+    return a.io == M3_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
+}
+
+}  // namespace m3

@@ -1,0 +1,344 @@
+// m3_host.cpp -- the C entry points of libm3.so: argument checks, planning and
+// dispatch. Host code only: every check runs before the first HIP call, so the
+// error paths can be exercised on a machine without a GPU.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "m3_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+m3_status fail(m3_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+size_t io_size(m3_dtype t) { return t == M3_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range rng(const char* name, const void* p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+m3_status check_dims(const m3_dims* d, int32_t R) {
+    if (!d) return fail(M3_EINVAL, "dims is NULL");
+    if (d->batch < 0) return fail(M3_EINVAL, "batch %lld < 0", (long long)d->batch);
+    if (d->seqlen < 0) return fail(M3_EINVAL, "seqlen %lld < 0", (long long)d->seqlen);
+    if (d->heads < 1) return fail(M3_EINVAL, "heads %d < 1", d->heads);
+    if (d->groups < 1) return fail(M3_EINVAL, "groups %d < 1", d->groups);
+    if (d->heads % d->groups != 0)
+        return fail(M3_EINVAL, "groups %d does not divide heads %d", d->groups, d->heads);
+    if (d->headdim < 1) return fail(M3_EINVAL, "headdim %d < 1", d->headdim);
+    if (d->dstate < 2 || d->dstate % 2 != 0)
+        return fail(M3_EINVAL, "dstate %d must be even and >= 2 (rotation pairs)", d->dstate);
+    if (R < 1) return fail(M3_EINVAL, "rank R %d < 1", R);
+    if (d->headdim > 65536 || d->dstate > 65536 || R > 1024 || d->heads > (1 << 24))
+        return fail(M3_EUNSUPPORTED, "sizes beyond the supported range");
+    return M3_OK;
+}
+
+m3_status check_dtype(m3_dtype t) {
+    if (t != M3_F32 && t != M3_BF16) return fail(M3_EDTYPE, "unknown io dtype %d", (int)t);
+    return M3_OK;
+}
+
+int32_t choose_segments(int64_t bh, int64_t n_chunks) {
+    // Enough (b, h, segment) walks to give every compute unit one, with at
+    // least 8 chunks per segment so the look-back stays a small fraction.
+    const char* env = getenv("M3_PREFILL_SEGMENTS");
+    int64_t s;
+    if (env && atoi(env) > 0) {
+        s = atoi(env);
+    } else {
+        const int64_t target = 256;
+        s = bh >= target ? 1 : (target + bh - 1) / bh;
+        s = std::min<int64_t>(s, std::max<int64_t>(1, n_chunks / 8));
+    }
+    s = std::max<int64_t>(1, std::min<int64_t>(s, std::max<int64_t>(1, n_chunks)));
+    return (int32_t)std::min<int64_t>(s, 4096);
+}
+
+m3_status make_plan(const m3_dims* d, int32_t R, int32_t chunk, m3_dtype io, m3_plan* p) {
+    m3_status s = check_dims(d, R);
+    if (s != M3_OK) return s;
+    if ((s = check_dtype(io)) != M3_OK) return s;
+    if (chunk < 1) return fail(M3_EINVAL, "chunk %d < 1", chunk);
+    if (chunk > 4096) return fail(M3_EUNSUPPORTED, "chunk %d above 4096", chunk);
+    std::memset(p, 0, sizeof *p);
+    const int64_t L = d->seqlen;
+    p->n_chunks = (L + chunk - 1) / chunk;
+    p->last_chunk_len = L == 0 ? 0 : L - (p->n_chunks - 1) * chunk;
+    const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
+    p->path = mfma ? M3_PATH_MFMA : M3_PATH_GENERIC;
+    p->segments = mfma ? choose_segments(d->batch * d->heads, p->n_chunks) : 1;
+    p->chunks_per_segment = p->segments > 0 ? (p->n_chunks + p->segments - 1) / p->segments : 0;
+    if (mfma && p->chunks_per_segment > 0)  // no empty trailing segment
+        p->segments = (int32_t)((p->n_chunks + p->chunks_per_segment - 1) / p->chunks_per_segment);
+    if (p->segments < 1) p->segments = 1;
+    p->workspace_bytes = m3::prefill_workspace_layout(d->batch, d->heads, d->headdim, d->dstate,
+                                                      p->segments, p->path).total;
+    return M3_OK;
+}
+
+}  // namespace
+
+namespace m3 {
+
+static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32_t N, int32_t segments,
+                                          int32_t path) {
+    PrefillWorkspace w{};
+    const size_t bh = size_t(b) * size_t(H);
+    size_t off = 0;
+    if (path == M3_PATH_GENERIC) {
+        w.state_off = off;
+        off += up256(bh * size_t(N) * size_t(P) * 4);
+    } else if (segments > 1) {
+        const size_t nseg = bh * size_t(segments);
+        w.ctrl_off = off;
+        off += up256(256 + nseg * 4);
+        w.agg_off = off;
+        off += up256(nseg * size_t(N) * size_t(P) * 4);
+        w.incl_off = off;
+        off += up256(nseg * size_t(N) * size_t(P) * 4);
+        w.tr_off = off;
+        off += up256(nseg * 4);
+    }
+    w.total = off;
+    return w;
+}
+
+}  // namespace m3
+
+extern "C" {
+
+int32_t m3_abi_version(void) { return M3_ABI_VERSION; }
+
+const char* m3_last_error(void) { return g_err; }
+
+const char* m3_status_string(m3_status s) {
+    switch (s) {
+        case M3_OK: return "ok";
+        case M3_EINVAL: return "invalid argument";
+        case M3_ESHAPE: return "inconsistent shapes";
+        case M3_EDTYPE: return "unsupported dtype";
+        case M3_EALIGN: return "pointer not 16-byte aligned";
+        case M3_EUNSUPPORTED: return "unsupported configuration";
+        case M3_EHIP: return "HIP runtime error";
+        case M3_EWORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+m3_status m3_prefill_plan(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype, m3_plan* plan) {
+    g_err[0] = 0;
+    if (!plan) return fail(M3_EINVAL, "plan is NULL");
+    return make_plan(dims, R, chunk, io_dtype, plan);
+}
+
+size_t m3_prefill_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype) {
+    m3_plan p;
+    if (make_plan(dims, R, chunk, io_dtype, &p) != M3_OK) return 0;
+    return p.workspace_bytes;
+}
+
+m3_status m3_prefill(const void* x, const float* dt, const float* A, const float* omega,
+                     const float* lambda, const void* B, const void* C, const float* D,
+                     int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
+                     const m3_dims* dims, m3_dtype io_dtype,
+                     const void* carry_B, const void* carry_x,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    m3_plan plan;
+    m3_status s = make_plan(dims, R, chunk, io_dtype, &plan);
+    if (s != M3_OK) return s;
+    const int64_t b = dims->batch, L = dims->seqlen;
+    const int64_t H = dims->heads, G = dims->groups, P = dims->headdim, N = dims->dstate;
+    const size_t es = io_size(io_dtype);
+    const bool tokens = b > 0 && L > 0;
+    const bool heads = b > 0;
+
+    struct Req { const char* name; const void* p; bool needed; };
+    const Req req[] = {{"x", x, tokens}, {"dt", dt, tokens}, {"lambda", lambda, tokens},
+                       {"B", B, tokens}, {"C", C, tokens}, {"y", y, tokens},
+                       {"A", A, heads}, {"omega", omega, heads}, {"D", D, heads}};
+    for (const Req& r : req)
+        if (r.needed && !r.p) return fail(M3_EINVAL, "%s is NULL", r.name);
+    if ((carry_B == nullptr) != (carry_x == nullptr))
+        return fail(M3_EINVAL, "carry_B and carry_x must be given together");
+
+    const void* ptrs[] = {x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x};
+    const char* names[] = {"x", "dt", "A", "omega", "lambda", "B", "C", "D", "h0", "y", "h_out",
+                           "carry_B", "carry_x"};
+    for (size_t i = 0; i < sizeof ptrs / sizeof ptrs[0]; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(M3_EALIGN, "%s is not 16-byte aligned", names[i]);
+
+    const size_t tok = size_t(b) * size_t(L);
+    const Range ry = rng("y", y, tok * H * R * P * es);
+    const Range inputs[] = {rng("x", x, tok * H * R * P * es), rng("dt", dt, tok * H * 4),
+                            rng("lambda", lambda, tok * H * 4), rng("B", B, tok * G * R * N * es),
+                            rng("C", C, tok * G * R * N * es), rng("A", A, H * 4),
+                            rng("omega", omega, H * (N / 2) * 4), rng("D", D, H * 4),
+                            rng("h0", h0, size_t(b) * H * N * P * 4),
+                            rng("h_out", h_out, size_t(b) * H * N * P * 4),
+                            rng("carry_B", carry_B, size_t(b) * G * R * N * es),
+                            rng("carry_x", carry_x, size_t(b) * H * R * P * es)};
+    for (const Range& r : inputs)
+        if (overlaps(ry, r)) return fail(M3_EINVAL, "y overlaps %s", r.name);
+    const Range rh = rng("h_out", h_out, size_t(b) * H * N * P * 4);
+    for (const Range& r : inputs) {
+        if (!std::strcmp(r.name, "h_out")) continue;
+        if (!std::strcmp(r.name, "h0") && h0 == h_out) continue;  // exact alias is allowed
+        if (overlaps(rh, r)) return fail(M3_EINVAL, "h_out overlaps %s", r.name);
+    }
+    if (plan.workspace_bytes > 0 && b > 0) {
+        if (!workspace) return fail(M3_EWORKSPACE, "workspace of %zu bytes required", plan.workspace_bytes);
+        if (workspace_bytes < plan.workspace_bytes)
+            return fail(M3_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                        plan.workspace_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(M3_EALIGN, "workspace is not 256-byte aligned");
+    }
+    if (b == 0) return M3_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (L == 0) {  // nothing to scan: h_L = h0
+        if (h_out && h_out != h0)
+            e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(h_out),
+                                        reinterpret_cast<const uint32_t*>(h0), int64_t(b) * H * N * P, st);
+        else
+            e = hipSuccess;
+    } else {
+        m3::PrefillArgs a{x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x,
+                          b, L, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R, chunk, io_dtype,
+                          plan, workspace, st};
+        e = plan.path == M3_PATH_MFMA ? m3::launch_prefill_mfma(a) : m3::launch_prefill_generic(a);
+    }
+    if (e != hipSuccess) return fail(M3_EHIP, "launch failed: %s", hipGetErrorString(e));
+    return M3_OK;
+}
+
+size_t m3_decode_carry_bytes(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int32_t which) {
+    if (check_dims(dims, R) != M3_OK || check_dtype(io_dtype) != M3_OK) return 0;
+    const size_t es = io_size(io_dtype);
+    if (which == 0) return 2 * size_t(dims->batch) * dims->groups * R * dims->dstate * es;
+    if (which == 1) return 2 * size_t(dims->batch) * dims->heads * R * dims->headdim * es;
+    return 0;
+}
+
+m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t R, m3_dtype io_dtype,
+                               float* h_buf, void* carry_B_buf, void* carry_x_buf,
+                               const float* h0, const void* B_last, const void* x_last, int64_t t0,
+                               void* stream) {
+    g_err[0] = 0;
+    if (!st) return fail(M3_EINVAL, "state is NULL");
+    m3_status s = check_dims(dims, R);
+    if (s != M3_OK) return s;
+    if ((s = check_dtype(io_dtype)) != M3_OK) return s;
+    if (t0 < 0) return fail(M3_EINVAL, "t0 %lld < 0", (long long)t0);
+    const int64_t b = dims->batch;
+    if (b > 0 && (!h_buf || !carry_B_buf || !carry_x_buf))
+        return fail(M3_EINVAL, "state buffers must not be NULL");
+    if ((B_last == nullptr) != (x_last == nullptr))
+        return fail(M3_EINVAL, "B_last and x_last must be given together");
+    const void* ptrs[] = {h_buf, carry_B_buf, carry_x_buf, h0, B_last, x_last};
+    const char* names[] = {"h", "carry_B", "carry_x", "h0", "B_last", "x_last"};
+    for (int i = 0; i < 6; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(M3_EALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t es = io_size(io_dtype);
+    const size_t hbytes = size_t(b) * dims->heads * dims->dstate * dims->headdim * 4;
+    const size_t cb = size_t(b) * dims->groups * R * dims->dstate * es;  // one slot
+    const size_t cx = size_t(b) * dims->heads * R * dims->headdim * es;
+    if (h0 && h0 != h_buf && overlaps(rng("h0", h0, hbytes), rng("h", h_buf, hbytes)))
+        return fail(M3_EINVAL, "h0 partially overlaps the state buffer");
+    if ((cb % 4) || (cx % 4)) return fail(M3_EUNSUPPORTED, "carry slot size not a multiple of 4 bytes");
+
+    st->h = h_buf;
+    st->carry_B = carry_B_buf;
+    st->carry_x = carry_x_buf;
+    st->t = t0;
+    st->dims = *dims;
+    st->dims.seqlen = 1;
+    st->R = R;
+    st->io_dtype = io_dtype;
+    if (b == 0) return M3_OK;
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int slot = int((t0 + 1) & 1);  // slot holding token t0 - 1
+    hipError_t e = hipSuccess;
+    if (h0 != h_buf)
+        e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(h_buf), reinterpret_cast<const uint32_t*>(h0),
+                                    int64_t(hbytes / 4), hs);
+    if (e == hipSuccess)
+        e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(static_cast<char*>(carry_B_buf) + slot * cb),
+                                    reinterpret_cast<const uint32_t*>(B_last), int64_t(cb / 4), hs);
+    if (e == hipSuccess)
+        e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(static_cast<char*>(carry_x_buf) + slot * cx),
+                                    reinterpret_cast<const uint32_t*>(x_last), int64_t(cx / 4), hs);
+    if (e != hipSuccess) return fail(M3_EHIP, "state init failed: %s", hipGetErrorString(e));
+    return M3_OK;
+}
+
+m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t, const float* A,
+                         const float* omega, const float* lambda_t, const void* B_t, const void* C_t,
+                         const float* D, int32_t R, void* y_t, void* stream) {
+    g_err[0] = 0;
+    if (!st) return fail(M3_EINVAL, "state is NULL");
+    m3_status s = check_dims(&st->dims, st->R);
+    if (s != M3_OK) return s;
+    if ((s = check_dtype(st->io_dtype)) != M3_OK) return s;
+    if (R != st->R) return fail(M3_ESHAPE, "R %d differs from the state's %d", R, st->R);
+    const m3_dims& d = st->dims;
+    const int64_t b = d.batch;
+    if (b == 0) { st->t += 1; return M3_OK; }
+    struct Req { const char* name; const void* p; };
+    const Req req[] = {{"x_t", x_t}, {"dt_t", dt_t}, {"A", A}, {"omega", omega}, {"lambda_t", lambda_t},
+                       {"B_t", B_t}, {"C_t", C_t}, {"D", D}, {"y_t", y_t}, {"state h", st->h},
+                       {"state carry_B", st->carry_B}, {"state carry_x", st->carry_x}};
+    for (const Req& r : req) {
+        if (!r.p) return fail(M3_EINVAL, "%s is NULL", r.name);
+        if (!aligned16(r.p)) return fail(M3_EALIGN, "%s is not 16-byte aligned", r.name);
+    }
+    const size_t es = io_size(st->io_dtype);
+    const int64_t H = d.heads, G = d.groups, P = d.headdim, N = d.dstate;
+    const Range ry = rng("y_t", y_t, size_t(b) * H * R * P * es);
+    const Range others[] = {rng("x_t", x_t, size_t(b) * H * R * P * es), rng("dt_t", dt_t, size_t(b) * H * 4),
+                            rng("lambda_t", lambda_t, size_t(b) * H * 4),
+                            rng("B_t", B_t, size_t(b) * G * R * N * es), rng("C_t", C_t, size_t(b) * G * R * N * es),
+                            rng("state h", st->h, size_t(b) * H * N * P * 4),
+                            rng("state carry_B", st->carry_B, 2 * size_t(b) * G * R * N * es),
+                            rng("state carry_x", st->carry_x, 2 * size_t(b) * H * R * P * es)};
+    for (const Range& r : others)
+        if (overlaps(ry, r)) return fail(M3_EINVAL, "y_t overlaps %s", r.name);
+
+    m3::DecodeArgs a{st->h, st->carry_B, st->carry_x, int32_t((st->t + 1) & 1), x_t, dt_t, A, omega,
+                     lambda_t, B_t, C_t, D, y_t, b, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R,
+                     st->io_dtype, reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = m3::launch_decode(a);
+    if (e != hipSuccess) return fail(M3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    st->t += 1;
+    return M3_OK;
+}
+
+}  // extern "C"

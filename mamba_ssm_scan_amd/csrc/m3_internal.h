@@ -1,0 +1,75 @@
+// m3_internal.h -- what the host entry points (m3_host.cpp) hand to the kernel
+// launchers (*.hip). Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/m3.h"
+
+namespace m3 {
+
+struct PrefillArgs {
+    const void* x;
+    const float* dt;
+    const float* A;
+    const float* omega;
+    const float* lam;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h0;       // nullable
+    void* y;
+    float* h_out;          // nullable
+    const void* carry_B;   // nullable (both or neither)
+    const void* carry_x;
+    int64_t b, L;
+    int32_t H, G, P, N, R, chunk;
+    m3_dtype io;
+    m3_plan plan;
+    void* workspace;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    float* h;
+    void* carry_B;         // [2][b][G][R][N]
+    void* carry_x;         // [2][b][H][R][P]
+    int32_t rd_slot;       // slot holding the previous token
+    const void* x;
+    const float* dt;
+    const float* A;
+    const float* omega;
+    const float* lam;
+    const void* B;
+    const void* C;
+    const float* D;
+    void* y;
+    int64_t b;
+    int32_t H, G, P, N, R;
+    m3_dtype io;
+    hipStream_t stream;
+};
+
+// Layout of the prefill workspace (byte offsets), shared by host and launchers.
+struct PrefillWorkspace {
+    size_t state_off;      // generic path: running state [b][H][N][P] fp32
+    size_t ctrl_off;       // segmented path: ticket counter + flags
+    size_t agg_off;        // segmented path: per-segment local end state [b*H*S][N][P] fp32
+    size_t incl_off;       // segmented path: per-segment inclusive end state
+    size_t tr_off;         // segmented path: per-segment transfer (cum dt) [b*H*S] fp32
+    size_t total;
+};
+
+PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32_t N, int32_t segments,
+                                          int32_t path);
+
+bool mfma_path_supported(int32_t P, int32_t N, int32_t R, int32_t chunk, m3_dtype io);
+
+hipError_t launch_prefill_generic(const PrefillArgs& a);
+hipError_t launch_prefill_mfma(const PrefillArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+// dst[i] = src ? src[i] : 0 for n 32-bit words (a kernel, so it is safe under graph capture)
+hipError_t launch_copy_or_zero(uint32_t* dst, const uint32_t* src, int64_t n_words, hipStream_t s);
+
+}  // namespace m3

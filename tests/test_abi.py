@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/m3.h
+declares, plans chunks exactly, and rejects bad arguments before any HIP call.
+
+Pointers here are fake, 16-byte aligned addresses: every call below fails
+validation, which never dereferences them.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from mamba_ssm_scan_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from mamba_ssm_scan_amd import build
+        build.build()
+    return bd.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "m3.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(bd.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.m3_abi_version() == 1
+    assert lib.m3_status_string(0) == b"ok"
+    assert lib.m3_status_string(6) == b"HIP runtime error"
+
+
+def _dims(b=1, L=100, H=4, G=1, P=8, N=16):
+    return bd.dims(b, L, H, G, P, N)
+
+
+@pytest.mark.parametrize("L", [0, 1, 15, 16, 17, 64, 127, 128, 129, 2048, 32768, 33024])
+@pytest.mark.parametrize("chunk", [1, 3, 16, 64, 100, 4096])
+def test_plan_integers(lib, L, chunk):
+    p = bd.plan(_dims(L=L), 1, chunk, bd.M3_F32)
+    n = math.ceil(L / chunk)
+    assert p.n_chunks == n
+    assert p.last_chunk_len == (0 if L == 0 else L - (n - 1) * chunk)
+    assert 1 <= p.segments
+    assert p.segments * p.chunks_per_segment >= n
+    assert (p.segments - 1) * p.chunks_per_segment < max(n, 1)
+
+
+def test_plan_generic_workspace(lib):
+    d = _dims(b=3, H=4, P=8, N=16)
+    p = bd.plan(d, 2, 16, bd.M3_F32)
+    assert p.path == bd.M3_PATH_GENERIC
+    assert p.workspace_bytes >= 3 * 4 * 16 * 8 * 4
+    assert lib.m3_prefill_workspace_size(ctypes.byref(d), 2, 16, bd.M3_F32) == p.workspace_bytes
+
+
+FAKE = 1 << 40  # never dereferenced
+
+
+def _call(lib, d, R=1, chunk=16, io=bd.M3_F32, **over):
+    # disjoint fake regions, 1 GiB apart
+    names = ["x", "dt", "A", "omega", "lam", "B", "C", "D", "h0", "y", "h_out", "cB", "cx", "ws"]
+    ptr = {n: FAKE + i * (1 << 30) for i, n in enumerate(names)}
+    ptr["h0"] = ptr["cB"] = ptr["cx"] = None
+    ptr["ws"] = None
+    ptr.update(over)
+    v = lambda n: None if ptr[n] is None else ctypes.c_void_p(ptr[n])
+    ws_bytes = over.get("ws_bytes", 0)
+    dp = None if d is None else ctypes.byref(d)
+    st = lib.m3_prefill(v("x"), v("dt"), v("A"), v("omega"), v("lam"), v("B"), v("C"), v("D"), R, chunk,
+                        v("h0"), v("y"), v("h_out"), dp, io, v("cB"), v("cx"), v("ws"), ws_bytes, None)
+    return st, lib.m3_last_error().decode()
+
+
+def test_prefill_argument_errors(lib):
+    assert _call(lib, None)[0] == 1
+    assert _call(lib, _dims(N=15))[0] == 1                       # odd state dim
+    assert _call(lib, _dims(N=0))[0] == 1
+    assert _call(lib, _dims(H=4, G=3))[0] == 1                   # G does not divide H
+    assert _call(lib, _dims(), R=0)[0] == 1
+    assert _call(lib, _dims(), chunk=0)[0] == 1
+    assert _call(lib, _dims(), chunk=4097)[0] == 5
+    assert _call(lib, _dims(), io=7)[0] == 3
+    st, msg = _call(lib, _dims(), x=None)
+    assert st == 1 and "x" in msg
+    assert _call(lib, _dims(), cB=FAKE + 50 * (1 << 30))[0] == 1  # carry_B without carry_x
+    st, msg = _call(lib, _dims(), B=FAKE + 5 * (1 << 30) + 8)
+    assert st == 4 and "B" in msg                                  # misaligned
+    st, msg = _call(lib, _dims(), y=FAKE + 16)                     # y inside x
+    assert st == 1 and "overlaps x" in msg
+    st, msg = _call(lib, _dims(), h_out=FAKE + 6 * (1 << 30) + 32)  # h_out inside C
+    assert st == 1 and "h_out" in msg
+    # the generic path needs a workspace
+    st, msg = _call(lib, _dims())
+    assert st == 7, msg
+    d = _dims()
+    need = lib.m3_prefill_workspace_size(ctypes.byref(d), 1, 16, bd.M3_F32)
+    st, msg = _call(lib, d, ws=FAKE + 20 * (1 << 30), ws_bytes=need - 1)
+    assert st == 7
+    st, msg = _call(lib, d, ws=FAKE + 20 * (1 << 30) + 16, ws_bytes=need)
+    assert st == 4 and "workspace" in msg
+
+
+def test_prefill_empty_batch_is_a_no_op(lib):
+    # b = 0: valid, nothing to launch
+    assert _call(lib, _dims(b=0))[0] == 0
+
+
+def test_decode_argument_errors(lib):
+    st = bd.M3DecodeState()
+    d = _dims()
+    f = lambda i: ctypes.c_void_p(FAKE + i * (1 << 30))
+    assert lib.m3_decode_state_init(None, ctypes.byref(d), 1, 0, f(0), f(1), f(2), None, None, None, 0, None) == 1
+    bad = _dims(N=9)
+    assert lib.m3_decode_state_init(ctypes.byref(st), ctypes.byref(bad), 1, 0, f(0), f(1), f(2), None, None, None,
+                                    0, None) == 1
+    assert lib.m3_decode_state_init(ctypes.byref(st), ctypes.byref(d), 1, 0, f(0), f(1), f(2), None, f(3), None,
+                                    0, None) == 1          # B_last without x_last
+    assert lib.m3_decode_state_init(ctypes.byref(st), ctypes.byref(d), 1, 0, f(0), f(1), f(2), None, None, None,
+                                    -1, None) == 1
+    assert lib.m3_decode_state_init(ctypes.byref(st), ctypes.byref(d), 1, 0, ctypes.c_void_p(FAKE + 4), f(1), f(2),
+                                    None, None, None, 0, None) == 4
+    # a state bound by hand (no HIP call): a step with another rank is a shape error
+    st.h, st.carry_B, st.carry_x, st.t = FAKE, FAKE + (1 << 30), FAKE + 2 * (1 << 30), 5
+    st.dims, st.R, st.io_dtype = d, 2, 0
+    args = [f(10 + i) for i in range(8)]
+    assert lib.m3_decode_step(ctypes.byref(st), *args, 1, f(30), None) == 2
+    assert lib.m3_decode_step(ctypes.byref(st), *args[:7], None, 2, f(30), None) == 1   # D NULL
+    assert lib.m3_decode_step(ctypes.byref(st), *args, 2, ctypes.c_void_p(FAKE + 10 * (1 << 30) + 64), None) == 1
+    assert st.t == 5                                  # failed steps do not advance the counter
+
+
+def test_carry_bytes(lib):
+    d = _dims(b=3, H=4, G=2, P=8, N=16)
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 0) == 2 * 3 * 2 * 2 * 16 * 2
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 1) == 2 * 3 * 4 * 2 * 8 * 2
