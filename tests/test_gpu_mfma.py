@@ -1,0 +1,138 @@
+"""GPU parity of the bf16-MFMA chunked prefill (N = 128, P = 64, R in {1, 2, 4}).
+
+Small cases cover every chunk size class, ragged tails, groups, initial state and
+carry; full-size workloads compare sampled (batch, head) walks with the oracle.
+Tolerance: max-relative error per (batch, head) slice <= 2e-2 (bf16 I/O, fp32 state).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mamba_ssm_scan_amd import binding, inputs
+from tests.test_gpu_generic import dyadic_problem, run_decode
+from tests.util import TOL, assert_close, f64, gpu_prefill, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+def _path(b, L, H, G, R, chunk):
+    return binding.plan(binding.dims(b, L, H, G, 64, 128), R, chunk, binding.M3_BF16).path
+
+
+CASES = [
+    # b, L, H, G, R, chunk, h0_std, carry
+    (1, 64, 2, 1, 1, 64, 0.0, False),
+    (2, 200, 3, 1, 1, 64, 0.1, True),
+    (1, 130, 4, 4, 1, 64, 0.1, False),
+    (1, 100, 2, 1, 2, 64, 0.0, True),
+    (2, 150, 2, 2, 2, 32, 0.1, False),
+    (1, 257, 2, 1, 4, 64, 0.1, True),
+    (1, 90, 3, 3, 4, 64, 0.0, False),
+    (1, 77, 2, 1, 4, 16, 0.1, False),
+    (1, 50, 2, 1, 1, 7, 0.1, True),
+    (1, 41, 2, 1, 4, 1, 0.0, True),
+    (1, 1, 2, 1, 4, 64, 0.1, True),
+    (1, 65, 1, 1, 1, 33, 0.1, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_mfma_small(case):
+    b, L, H, G, R, chunk, h0s, carry = case
+    assert _path(b, L, H, G, R, chunk) == binding.M3_PATH_MFMA
+    _flush(f"mfma case {case}")
+    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=128, rank=R, io_dtype="bf16",
+                            dist="lm", wid=800 + CASES.index(case), h0_std=h0s, with_carry=carry)
+    y_ref, h_ref = oracle.scan(p)
+    y, h = gpu_prefill(p, chunk)
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+@pytest.mark.parametrize("R,Q", [(1, 64), (4, 64), (2, 16), (4, 5)])
+def test_mfma_dyadic_exact(R, Q):
+    """Exact index bookkeeping: integer impulses around chunk edges, exact arithmetic."""
+    p, expect = dyadic_problem(300, Q, "bf16", R=R, H=2, P=64, N=128, n0=77)
+    assert _path(1, 300, 2, 1, R, Q) == binding.M3_PATH_MFMA
+    y, _ = gpu_prefill(p, Q)
+    got = f64(y)
+    assert np.array_equal(got[0, :, :, 0, :], expect), np.argwhere(got[0, :, :, 0, :] != expect)[:5]
+    assert np.all(got[0, :, :, 1:, :] == 0)
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_mfma_coverage_and_guards(R):
+    p = to_dev(inputs.make_problem(batch=2, seqlen=99, heads=3, groups=1, headdim=64, dstate=128, rank=R,
+                                   io_dtype="bf16", wid=850, h0_std=0.1))
+    guard = 4096
+    ny, nh = p["x"].numel(), 2 * 3 * 128 * 64
+    ybuf = torch.full((ny + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    hbuf = torch.full((nh + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    y = ybuf[guard:guard + ny].view(p["x"].shape)
+    h = hbuf[guard:guard + nh].view(2, 3, 128, 64)
+    ypat, hpat = ybuf.view(torch.int16).clone(), hbuf.view(torch.int32).clone()
+    binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], R, 64, p["h0"],
+                    y=y, h_out=h)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(h).all()
+    yv, hv = ybuf.view(torch.int16), hbuf.view(torch.int32)
+    assert torch.equal(yv[:guard], ypat[:guard]) and torch.equal(yv[-guard:], ypat[-guard:])
+    assert torch.equal(hv[:guard], hpat[:guard]) and torch.equal(hv[-guard:], hpat[-guard:])
+
+
+def test_mfma_chunk_sweep_agrees():
+    """Different chunk sizes give the same result within the bf16 tolerance of the oracle."""
+    p = inputs.make_problem(batch=1, seqlen=181, heads=2, groups=1, headdim=64, dstate=128, rank=2,
+                            io_dtype="bf16", dist="lm", wid=860, h0_std=0.1, with_carry=True)
+    y_ref, h_ref = oracle.scan(p)
+    for Q in (1, 2, 3, 8, 13, 31, 32, 63, 64):
+        y, h = gpu_prefill(p, Q)
+        assert_close(y, y_ref, TOL["bf16"], f"y chunk {Q}")
+        assert_close(h, h_ref, TOL["bf16"], f"h chunk {Q}")
+
+
+SAMPLE_HEADS = [0, 21, 42, 63]
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_workload_full_size(wid):
+    """Workloads 1 (R=1) and 2 (R=4) at full size, chunk 64; oracle on 4 heads x all batches."""
+    _flush(f"workload {wid} full size")
+    p = inputs.workload_prefill(wid, device="cuda")
+    w = inputs.WORKLOADS[wid]
+    assert _path(w.batch, w.seqlen, w.heads, 1, w.rank, w.chunk) == binding.M3_PATH_MFMA
+    y, h = binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], w.rank, w.chunk)
+    torch.cuda.synchronize()
+    sub = to_host(inputs.select_heads(p, SAMPLE_HEADS))
+    y_ref, h_ref = oracle.scan(sub)
+    idx = torch.tensor(SAMPLE_HEADS, device="cuda")
+    assert_close(y.index_select(2, idx), y_ref, TOL["bf16"], "y")
+    assert_close(h.index_select(1, idx), h_ref, TOL["bf16"], "h_out")
+    assert torch.isfinite(y).all()
+
+
+def test_workload4_prefill_then_decode():
+    """Workload 4: prefill of 32768 tokens (R=4), then 256 decode steps, against one 33024-token oracle run."""
+    w = inputs.WORKLOADS[4]
+    _flush("workload 4: long prefill + decode handoff")
+    p = inputs.long_sequence(4, device="cuda")
+    L = w.seqlen
+    pre = inputs.slice_tokens(p, 0, L)
+    y1, h1 = binding.prefill(pre["x"], pre["dt"], pre["A"], pre["omega"], pre["lam"], pre["B"], pre["C"], pre["D"],
+                             w.rank, w.chunk)
+    st = binding.DecodeState(1, w.heads, 1, w.headdim, w.dstate, w.rank, io_dtype=torch.bfloat16, h0=h1,
+                             B_last=p["B"][:, L - 1].contiguous(), x_last=p["x"][:, L - 1].contiguous(), t0=L)
+    y2, st = run_decode(p, steps_from=L, state=st)
+    assert st.t == L + w.decode_steps
+    heads = [5, 40]
+    sub = to_host(inputs.select_heads(p, heads))
+    y_ref, h_ref = oracle.scan(sub)
+    idx = torch.tensor(heads, device="cuda")
+    y = torch.cat([y1, y2], 1).index_select(2, idx)
+    assert_close(y, y_ref, TOL["bf16"], "y (prefill + decode)")
+    assert_close(st.h.index_select(1, idx), h_ref, TOL["bf16"], "final state")

@@ -30,5 +30,6 @@ def gpu_prefill(p, chunk, **kw):
 
 def assert_close(got, ref, tol, what=""):
     err = oracle.max_rel_err(f64(got) if isinstance(got, torch.Tensor) else got, ref)
+    print(f"  {what}: max-rel error {err:.3e} (tol {tol:.0e})", flush=True)
     assert np.isfinite(err) and err <= tol, f"{what}: max-rel error {err:.3e} > {tol:.1e}"
     return err
