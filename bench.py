@@ -1,0 +1,305 @@
+"""Throughput of the Mamba-3 SSM recurrence on one MI355X, through the C ABI.
+
+One step = one m3_prefill call over the SISO prefill workload (batch 4, 64
+heads, P 64, N 128, 2048 tokens, chunk 64, bf16 I/O, fp32 state, B/C shared by
+all heads). `value` is prefill tokens/s. The same run measures the decode step
+loop (batch 128, 64 heads, 1024 steps, R = 1 and R = 4), the MIMO R = 4 prefill
+and the long R = 4 prefill (32768 tokens) + 256 decode steps, and reports each
+against the HBM and bf16-MFMA roofline with algorithmic bytes / flops. The CPU
+oracle is timed on the host cores on a bounded sample of the prefill workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + decode steps/s on 1 GPU; % of HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+N_COPIES = 4                 # input copies rotated through so the 256 MB MALL cannot hold them
+
+
+def prefill_bytes(b, L, H, G, P, N, R, io_bytes=2, h0=False, h_out=True):
+    """Compulsory HBM bytes of one prefill: x, y, B, C (once per group), dt, lambda, h_out (+ h0)."""
+    tok = b * L
+    by = 2 * tok * H * R * P * io_bytes + 2 * tok * G * R * N * io_bytes + 2 * tok * H * 4
+    by += H * (2 + N // 2) * 4
+    if h_out:
+        by += b * H * N * P * 4
+    if h0:
+        by += b * H * N * P * 4
+    return by
+
+
+def prefill_flops(b, L, H, P, N, R, Q):
+    """Algorithmic flops: causal intra-chunk scores and masked product, inter-chunk output, state update."""
+    full, last = divmod(L, Q)
+
+    def chunk(q):
+        return q * (q + 1) * R * R * (N + P) + 4 * q * R * N * P
+
+    return b * H * (full * chunk(Q) + (chunk(last) if last else 0))
+
+
+def decode_bytes(b, H, G, P, N, R, io_bytes=2):
+    """Per step: state read + write, x_t, y_t, x_prev, x carry write, B_t, C_t, B_prev, B carry write, dt, lambda."""
+    return b * H * N * P * 8 + 4 * b * H * R * P * io_bytes + 4 * b * G * R * N * io_bytes + 2 * b * H * 4
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_prefill(wid, steps, warmup, log):
+    import torch
+    from mamba_ssm_scan_amd import binding, inputs
+    w = inputs.WORKLOADS[wid]
+    copies = [inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=1, headdim=w.headdim,
+                                  dstate=w.dstate, rank=w.rank, io_dtype=w.io_dtype, dist=w.dist, wid=wid,
+                                  step=k, device="cuda") for k in range(N_COPIES)]
+    y = torch.empty_like(copies[0]["x"])
+    h = torch.empty((w.batch, w.heads, w.dstate, w.headdim), dtype=torch.float32, device="cuda")
+    plan = binding.plan(binding.dims(w.batch, w.seqlen, w.heads, 1, w.headdim, w.dstate), w.rank, w.chunk,
+                        binding.M3_BF16)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def run(k):
+        p = copies[k % N_COPIES]
+        binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], w.rank, w.chunk,
+                        y=y, h_out=h, workspace=ws)
+
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for k in range(steps):
+        run(k)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    by = prefill_bytes(w.batch, w.seqlen, w.heads, 1, w.headdim, w.dstate, w.rank)
+    fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
+    r = {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
+         "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
+         "bytes": by, "flops": fl, "path": "mfma" if plan.path == binding.M3_PATH_MFMA else "generic",
+         "segments": plan.segments}
+    r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
+    r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
+    log(f"prefill {w.name}: {ms * 1e3:.1f} us/call, {r['tokens_per_s'] / 1e6:.1f} M tok/s, "
+        f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM), {r['mfma_tflops']:.1f} TFLOP/s "
+        f"({100 * r['mfma_frac']:.1f}% bf16 MFMA)")
+    return r
+
+
+def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
+    import torch
+    from mamba_ssm_scan_amd import binding, inputs
+    w = inputs.WORKLOADS[wid]
+    b = w.batch if batch is None else batch
+    di = inputs.decode_inputs(wid, steps_total, device="cuda", rank=R, batch=b)
+    y = torch.empty_like(di["x"])
+    st = binding.DecodeState(b, w.heads, 1, w.headdim, w.dstate, R, io_dtype=torch.bfloat16, h0=di["h0"])
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    A, om, D = di["A"].data_ptr(), di["omega"].data_ptr(), di["D"].data_ptr()
+    ptrs = [(di["x"][t].data_ptr(), di["dt"][t].data_ptr(), di["lam"][t].data_ptr(), di["B"][t].data_ptr(),
+             di["C"][t].data_ptr(), y[t].data_ptr()) for t in range(steps_total)]
+
+    def loop():
+        for (xp, dp, lp, bp, cp, yp) in ptrs:
+            st.step_raw(xp, dp, A, om, lp, bp, cp, D, yp, sh)
+
+    loop()  # warm-up pass over all steps
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(reps):
+        loop()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * steps_total)
+    by = decode_bytes(b, w.heads, 1, w.headdim, w.dstate, R)
+    r = {"workload": f"decode_b{b}_h{w.heads}_p{w.headdim}_n{w.dstate}_r{R}_{steps_total}_steps",
+         "us_per_step": ms_step * 1e3, "steps_per_s": 1e3 / ms_step, "hbm_gbs": by / (ms_step * 1e-3) / 1e9,
+         "bytes_per_step": by}
+    r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
+    log(f"decode R={R} b={b}: {ms_step * 1e3:.1f} us/step, {r['steps_per_s']:.0f} steps/s, "
+        f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM)")
+    return r
+
+
+def bench_long(log):
+    """Workload 4: prefill of 32768 tokens (R = 4) then 256 decode steps, batch 1."""
+    import torch
+    from mamba_ssm_scan_amd import binding, inputs
+    w = inputs.WORKLOADS[4]
+    p = inputs.long_sequence(4, device="cuda")
+    L = w.seqlen
+    pre = inputs.slice_tokens(p, 0, L)
+    y = torch.empty_like(pre["x"])
+    h = torch.empty((1, w.heads, w.dstate, w.headdim), dtype=torch.float32, device="cuda")
+    plan = binding.plan(binding.dims(1, L, w.heads, 1, w.headdim, w.dstate), w.rank, w.chunk, binding.M3_BF16)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def pf():
+        binding.prefill(pre["x"], pre["dt"], pre["A"], pre["omega"], pre["lam"], pre["B"], pre["C"], pre["D"],
+                        w.rank, w.chunk, y=y, h_out=h, workspace=ws)
+
+    for _ in range(2):
+        pf()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        pf()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    by = prefill_bytes(1, L, w.heads, 1, w.headdim, w.dstate, w.rank)
+    fl = prefill_flops(1, L, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
+    # decode handoff: 256 steps from the prefill's final state
+    st = binding.DecodeState(1, w.heads, 1, w.headdim, w.dstate, w.rank, io_dtype=torch.bfloat16, h0=h,
+                             B_last=p["B"][:, L - 1].contiguous(), x_last=p["x"][:, L - 1].contiguous(), t0=L)
+    steps = w.decode_steps
+    xs = [p["x"][:, t].contiguous() for t in range(L, L + steps)]
+    Bs = [p["B"][:, t].contiguous() for t in range(L, L + steps)]
+    Cs = [p["C"][:, t].contiguous() for t in range(L, L + steps)]
+    ds = [p["dt"][:, t].contiguous() for t in range(L, L + steps)]
+    ls = [p["lam"][:, t].contiguous() for t in range(L, L + steps)]
+    ys = [torch.empty_like(xs[0]) for _ in range(steps)]
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(steps):
+        st.step_raw(xs[k].data_ptr(), ds[k].data_ptr(), p["A"].data_ptr(), p["omega"].data_ptr(), ls[k].data_ptr(),
+                    Bs[k].data_ptr(), Cs[k].data_ptr(), p["D"].data_ptr(), ys[k].data_ptr(), sh)
+    e1.record()
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / steps
+    r = {"workload": w.name, "prefill_ms": ms, "prefill_tokens_per_s": L / (ms * 1e-3),
+         "prefill_hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+         "prefill_mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "segments": plan.segments,
+         "decode_us_per_step": dms * 1e3, "decode_steps_per_s": 1e3 / dms}
+    log(f"long prefill {L} tokens R=4: {ms:.3f} ms, {r['prefill_tokens_per_s'] / 1e6:.1f} M tok/s "
+        f"({100 * r['prefill_mfma_frac']:.1f}% MFMA, {100 * r['prefill_hbm_frac']:.1f}% HBM, "
+        f"{plan.segments} segments); decode b=1: {dms * 1e3:.1f} us/step")
+    return r
+
+
+def copy_probe(log, nbytes=1 << 30):
+    """A plain device-to-device copy of known size (reference for the HBM byte counters)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    log(f"copy {nbytes >> 20} MiB: {ms * 1e3:.1f} us, {2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s (read + write)")
+
+
+def cpu_baseline(log, budget_s=12.0):
+    """The oracle (fp64 C, OpenMP) on the host cores, on the first heads of the prefill workload."""
+    import torch
+    import oracle
+    from mamba_ssm_scan_amd import inputs
+    w = inputs.WORKLOADS[1]
+    p = inputs.workload_prefill(1, device="cuda")
+    threads = oracle.default_threads()
+    heads_done, secs = 0, 0.0
+    block = 4
+    while heads_done < w.heads and secs < budget_s:
+        hs = list(range(heads_done, min(w.heads, heads_done + block)))
+        sub = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inputs.select_heads(p, hs).items()}
+        t0 = time.perf_counter()
+        oracle.scan(sub, nthreads=threads)
+        secs += time.perf_counter() - t0
+        heads_done += len(hs)
+        block = min(16, 2 * block)
+    tok_s = w.batch * w.seqlen * (heads_done / w.heads) / secs
+    log(f"cpu oracle: {heads_done}/{w.heads} heads x {w.batch} batches x {w.seqlen} tokens in {secs:.1f} s on "
+        f"{threads} threads -> {tok_s:.0f} tokens/s")
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: heads 0..{heads_done - 1} of {w.heads} (all {w.batch} batches, all {w.seqlen} "
+                      f"tokens), fp64 sequential recurrence, {secs:.1f} s wall; tokens/s scaled by the head fraction"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy: run just "
+                                               "these (profiling runs); copy = a 1 GiB device copy for counter scaling")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mamba_ssm_scan_amd import binding
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    if args.only:
+        for item in args.only.split(","):
+            if item == "prefill1":
+                bench_prefill(1, args.steps, args.warmup, log)
+            elif item == "prefill2":
+                bench_prefill(2, args.steps, args.warmup, log)
+            elif item in ("decode1", "decode4"):
+                bench_decode(int(item[-1]), 1024, 1, log)
+            elif item == "long":
+                bench_long(log)
+            elif item == "copy":
+                copy_probe(log)
+            else:
+                raise SystemExit(f"unknown --only item {item!r}")
+        return
+
+    head = bench_prefill(1, args.steps, args.warmup, log)
+    out = {
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_call"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": head["workload"], "batch": 4, "seqlen": 2048, "heads": 64, "groups": 1,
+                   "headdim": 64, "dstate": 128, "rank": 1, "chunk": 64, "state_dtype": "f32",
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["hbm_frac"], "traffic": None,
+                     "kernel": "prefill_mfma_kernel<1,4>", "bytes_per_launch": head["bytes"],
+                     "mfma": {"achieved": head["mfma_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": head["mfma_frac"], "flops_per_launch": head["flops"]}},
+    }
+    if not args.quick:
+        out["decode"] = {f"r{R}": bench_decode(R, 1024, 3, log) for R in (1, 4)}
+        out["prefill_mimo_r4"] = bench_prefill(2, args.steps, args.warmup, log)
+        out["long_prefill_decode"] = bench_long(log)
+    if not args.no_cpu and not args.quick:
+        out["cpu_baseline"] = cpu_baseline(log)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,16 +17,21 @@
 // the previous token's trapezoid term already added; it stays in registers
 // (fp32) for the whole walk.
 //
-// The three contractions run on v_mfma_f32_16x16x32_bf16:
+// The contractions run on v_mfma_f32_16x16x32_bf16:
 //   scores^T  [rho_j][rho_i] = B~ (A operand, LDS) x C~^T (B operand, registers), K = N
-//   y         [rho_i][p]     = (M o scores) (A operand, straight from the score
-//                              accumulators) x X (B operand, X^T in LDS), K = rho_j
-//             [rho_i][p]    += C~ (A operand, the same registers) x g (g^T in LDS), K = N
+//   y^T       [p][rho_i]     = X^T (A operand, LDS) x (M o scores^T) (B operand, straight
+//                              from the score accumulators), K = rho_j
+//             [p][rho_i]    += g^T (A operand, LDS) x C~^T (B operand, the same registers), K = N
 //   state     [n][p]        += (w B~)^T (A operand, gathered from LDS) x X, K = rho
 // An accumulator lane holds 4 consecutive rows of one column, which is exactly
 // half of an A/B operand's 8 consecutive k values: two score tiles form one
 // K = 32 operand (the k order inside an MFMA is free as long as A and B agree),
 // so the masked scores never leave registers.
+//
+// The rotation angles are the same for B and C of a token and for all R ranks;
+// each (token, pair) angle is evaluated once: the thread that stages a token's
+// B rows also turns its C rows (into LDS when they fit, R <= 2), and at R = 4
+// the four lanes holding one token's C rows share angles through DPP.
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -40,10 +45,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int N = 128;   // state rows
-constexpr int P = 64;    // head dim
-constexpr int K = 64;    // rotation pairs
-constexpr int NS = N + 8;  // LDS row stride (bf16 elements) of B~ and g^T
+constexpr int N = 128;     // state rows
+constexpr int P = 64;      // head dim
+constexpr int K = 64;      // rotation pairs
+constexpr int NS = N + 8;  // LDS row stride (bf16 elements) of B~, C~ and g^T
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInv2Pi = 0.15915494309189535f;
 
@@ -55,7 +60,7 @@ __device__ __forceinline__ floatx4 mfma16(u32x2 a, u32x2 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b),
                                                      c, 0, 0, 0);
 }
-// two floats -> packed bf16 (round to nearest even)
+// two floats -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
     bf16x2 v;
     v[0] = (__bf16)lo;
@@ -65,27 +70,42 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
 __device__ __forceinline__ float lo16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// rotate the 4 pairs packed in w (8 bf16) by -Phi: (b0, b1) -> (c b0 + s b1, c b1 - s b0)
-__device__ __forceinline__ u32x4 rot_neg(u32x4 w, const float2* cs) {
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float b0 = lo16(w[j]), b1 = hi16(w[j]);
-        const float2 t = cs[j];
-        o[j] = pack2(t.x * b0 + t.y * b1, t.x * b1 - t.y * b0);
-    }
-    return o;
+// (cos, sin) of 2 pi * rev
+struct CS {
+    float c, s;
+};
+__device__ __forceinline__ CS cs_rev(float om_rev, float T) {
+    const float r = __builtin_amdgcn_fractf(om_rev * T);
+    return CS{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
+}
+// one packed pair (b0, b1) turned by -Phi: (c b0 + s b1, c b1 - s b0)
+__device__ __forceinline__ unsigned rot_pair(unsigned w, CS t) {
+    const float b0 = lo16(w), b1 = hi16(w);
+    return pack2(t.c * b0 + t.s * b1, t.c * b1 - t.s * b0);
+}
+// broadcast lane j of every DPP quad
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, false));
 }
 
-template <int R, int NW>
+template <int R_, int NW_>
 struct Shape {
-    static constexpr int QRP = 64 * R;       // padded rows per chunk
-    static constexpr int NT = 64 * NW;       // threads
-    static constexpr int XS = QRP + 8;       // LDS row stride (bf16) of X^T
-    static constexpr int NSTRIP = QRP / 16;  // 16-row output strips
-    static constexpr int SPW = NSTRIP / NW;  // strips per wave
-    static constexpr int TPW = 32 / NW;      // 16x16 state tiles per wave
-    static_assert(NSTRIP % NW == 0 && 32 % NW == 0 && TPW % 4 == 0, "tiling");
+    static constexpr int R = R_, NW = NW_;
+    static constexpr int LR = R == 1 ? 0 : R == 2 ? 1 : 2;  // log2 R
+    static constexpr int QRP = 64 * R;                     // padded rows per chunk
+    static constexpr int NT = 64 * NW;                     // threads
+    static constexpr int XS = QRP + 8;                     // LDS row stride (bf16) of X^T
+    static constexpr int NSTRIP = QRP / 16;                // 16-row output strips
+    static constexpr int PTG = NW > NSTRIP ? NW / NSTRIP : 1;  // p-tile groups per strip
+    static constexpr int PTW = 4 / PTG;                    // 16-column p tiles per work item
+    static constexpr int SPW = NSTRIP * PTG / NW;          // work items (strip, p group) per wave
+    static constexpr int TPW = 32 / NW;                    // 16x16 state tiles per wave
+    static constexpr bool C_LDS = R <= 2;                  // C~ staged in LDS (else built per strip)
+    static constexpr int UPT = 64 * 16 / NT;               // (token, 8-column piece) staging units per thread
+    static constexpr int XU = QRP * 4;                     // (row pair, 8 columns) units of X
+    static constexpr int XPT = (XU + NT - 1) / NT;         // ... per thread
+    static_assert((NSTRIP * PTG) % NW == 0 && 32 % NW == 0 && TPW % 4 == 0 && UPT >= 1, "tiling");
 };
 
 // strips are dealt to waves in snake order so every wave gets a similar share
@@ -93,6 +113,93 @@ struct Shape {
 template <int NW>
 __device__ __forceinline__ int strip_of(int wave, int si) {
     return si * NW + ((si & 1) ? (NW - 1 - wave) : wave);
+}
+
+// Wait for this wave's LDS traffic, then meet the other waves. Unlike
+// __syncthreads() this does not wait for outstanding global loads, so the next
+// chunk's prefetch stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Global operands of one chunk, held in registers until they are staged.
+template <class S>
+struct ChunkRegs {
+    float d, l, dn, ln;                    // lane = token: dt, lambda, and of the next token
+    u32x4 b[S::UPT][S::R];                 // B rows (token, rank) of this thread's units
+    u32x4 c[S::C_LDS ? S::UPT : 1][S::R];  // C rows, when staged in LDS
+    u32x4 x0[S::XPT], x1[S::XPT];
+    u32x4 cs[S::C_LDS ? 1 : 4];            // C rows of the wave's first strip, when not in LDS
+};
+
+// Row addressing inside one chunk: token i, rank r of B/C sits at (i*G*R + r)*N
+// elements past the chunk's first row, of x/y at (i*H*R + r)*P. Tokens past
+// the chunk's end are clamped to its last token, so every load is
+// unconditional and finite; such rows never reach a result: their mask
+// entries and state weights are zero (their dt is taken as 0) and their
+// outputs are not stored.
+struct ChunkBase {
+    const uint16_t* B;
+    const uint16_t* C;
+    const uint16_t* x;
+    int nq;
+};
+
+__device__ __forceinline__ u32x4 load_tok(const uint16_t* base, int i, int nq, int tok_stride, int off) {
+    const int ic = i < nq ? i : nq - 1;
+    return *reinterpret_cast<const u32x4*>(base + (ic * tok_stride + off));
+}
+
+template <class S>
+__device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb, const float* __restrict__ dt,
+                                           const float* __restrict__ lam, int64_t tok0, int64_t L, int64_t c0, int H,
+                                           int G, int tid, int lane) {
+    constexpr int R = S::R;
+    const int nq = cb.nq;
+    {
+        const int ic = lane < nq ? lane : nq - 1;
+        const int64_t ti = (tok0 + ic) * H;
+        const float d = dt[ti], l = lam[ti];
+        const bool has_next = c0 + ic + 1 < L;
+        const float dn = dt[has_next ? ti + H : ti], ln = lam[has_next ? ti + H : ti];
+        cr.d = lane < nq ? d : 0.f;
+        cr.l = lane < nq ? l : 0.f;
+        cr.dn = (lane < nq && has_next) ? dn : 0.f;
+        cr.ln = (lane < nq && has_next) ? ln : 0.f;
+    }
+    const int pc = tid & 15;
+#pragma unroll
+    for (int m = 0; m < S::UPT; ++m) {
+        const int i = (tid >> 4) + m * (S::NT / 16);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            cr.b[m][r] = load_tok(cb.B, i, nq, G * R * N, r * N + 8 * pc);
+            if constexpr (S::C_LDS) cr.c[m][r] = load_tok(cb.C, i, nq, G * R * N, r * N + 8 * pc);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < S::XPT; ++m) {
+        if (S::XU % S::NT != 0 && tid + m * S::NT >= S::XU) break;
+        const unsigned rho0 = 2u * ((tid >> 3) + m * (S::NT / 8));
+        const int i0 = int(rho0 >> S::LR), r0 = int(rho0 & (R - 1));
+        const int i1 = int((rho0 + 1) >> S::LR), r1 = int((rho0 + 1) & (R - 1));
+        cr.x0[m] = load_tok(cb.x, i0, nq, H * R * P, r0 * P + 8 * (tid & 7));
+        cr.x1[m] = load_tok(cb.x, i1, nq, H * R * P, r1 * P + 8 * (tid & 7));
+    }
+}
+
+// C rows of one 16-row strip in the B-operand layout: row 16 s + l16, n = 32 ks + 8 g4 + 0..7
+template <class S>
+__device__ __forceinline__ void load_strip_c(u32x4 (&c)[4], const ChunkBase& cb, int s, int G, int lane) {
+    const unsigned rho = 16u * s + (lane & 15);
+    const int i = int(rho >> S::LR), r = int(rho & (S::R - 1));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        c[ks] = load_tok(cb.C, i, cb.nq, G * S::R * N, r * N + 32 * ks + 8 * (lane >> 4));
+}
+
+// M_ij (decay x width-2 convolution mask) for row token tj and column token ti
+__device__ __forceinline__ float mask_coef(int tj, int ti, float S2i, const float* w) {
+    if (tj > ti) return 0.f;
+    return __builtin_amdgcn_exp2f(S2i - w[tj]) * (w[64 + tj] + (tj < ti ? w[128 + tj] : 0.f));
 }
 
 template <int R, int NW>
@@ -104,14 +211,14 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
                     int64_t nbh) {
     using S = Shape<R, NW>;
-    constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW;
+    using CR = ChunkRegs<S>;
+    constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW, LR = S::LR;
 
-    __shared__ __attribute__((aligned(16))) uint16_t sBt[QRP * NS];  // B~ [rho][n]
-    __shared__ __attribute__((aligned(16))) uint16_t sXT[P * XS];    // X^T [p][rho]
-    __shared__ __attribute__((aligned(16))) uint16_t sGT[P * NS];    // g^T [p][n] (bf16 copy of the state)
-    __shared__ __attribute__((aligned(16))) float2 sCS[64 * K];      // (cos, sin)(Phi_{i,k}) [i][k]
-    __shared__ float sT[64], sS2[64], sGam[64], sDln[64], sExpS[64], sW[64];
-    __shared__ float sOm[K];
+    __shared__ __attribute__((aligned(16))) uint16_t sBt[QRP * NS];                 // B~ [rho][n]
+    __shared__ __attribute__((aligned(16))) uint16_t sCt[S::C_LDS ? QRP * NS : 8];  // C~ [rho][n]
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[P * XS];                   // X^T [p][rho]
+    __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];                // g^T [p][n], bf16, 2 buffers
+    __shared__ float sW[NW][6 * 64];  // per wave: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -129,7 +236,36 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
     const float Dh = Dv[h];
-    for (int k = tid; k < K; k += NT) sOm[k] = omega[int64_t(h) * K + k] * kInv2Pi;
+    float* wsc = sW[wave];
+
+    // rotation rates (revolutions per unit step) of the pairs this thread turns
+    const float* omh = omega + int64_t(h) * K;
+    float omB[4], omC[4], omS[TPW / 4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) omB[j] = omh[4 * (tid & 15) + j] * kInv2Pi;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) omC[ks] = omh[16 * ks + 4 * g4 + (l16 & 3)] * kInv2Pi;
+#pragma unroll
+    for (int mr = 0; mr < TPW / 4; ++mr)
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omh[8 * ((wave * TPW) / 4 + mr) + 2 * g4 + hp] * kInv2Pi;
+
+    auto chunk_base = [&](int64_t cc) {
+        const int64_t c0 = cc * Q, tok0 = b * L + c0;
+        ChunkBase cb;
+        cb.B = Bm + (tok0 * G + grp) * int64_t(R * N);
+        cb.C = Cm + (tok0 * G + grp) * int64_t(R * N);
+        cb.x = x + (tok0 * H + h) * int64_t(R * P);
+        cb.nq = int(L - c0 < Q ? L - c0 : Q);
+        return cb;
+    };
+
+    CR pre;
+    {
+        const ChunkBase cb = chunk_base(0);
+        load_chunk<S>(pre, cb, dt + h, lam + h, b * L, L, 0, H, G, tid, lane);
+        if constexpr (!S::C_LDS) load_strip_c<S>(pre.cs, cb, strip_of<NW>(wave, 0) / S::PTG, G, lane);
+    }
 
     // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
     floatx4 gst[TPW];
@@ -154,200 +290,216 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                 }
                 gst[m][e] = v;
             }
-            *reinterpret_cast<u32x2*>(sGT + p * NS + 16 * nt + 4 * g4) =
+            *reinterpret_cast<u32x2*>(&sGT[0][p * NS + 16 * nt + 4 * g4]) =
                 u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
         }
     }
-    __syncthreads();
 
+#pragma unroll 1
     for (int64_t c = 0; c < n_chunks; ++c) {
-        const int64_t c0 = c * Q;
-        const int nq = int(L - c0 < Q ? L - c0 : Q);  // tokens in this chunk
+        const ChunkBase cb = chunk_base(c);
+        const int nq = cb.nq;
+        const uint16_t* gT = sGT[c & 1];
+        uint16_t* gTn = sGT[(c + 1) & 1];
 
-        // ---- 1. per-token scalars (one wavefront, lane = token)
-        if (wave == 0) {
-            const int i = lane;
-            float d = 0.f, lm = 0.f, dln = 0.f;
-            if (i < nq) {
-                const int64_t ti = (b * L + c0 + i) * H + h;
-                d = dt[ti];
-                lm = lam[ti];
-                if (c0 + i + 1 < L) dln = (1.f - lam[ti + H]) * dt[ti + H];
-            }
-            float T = d;
+        // ---- 1. per-token scalars, computed by every wave for itself (lane = token)
+        float T = pre.d;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float v = __shfl_up(T, off);
-                if (lane >= off) T += v;
-            }
-            const float S2 = A2 * T;
-            const float S2e = __shfl(S2, nq - 1);
-            const float gam = lm * d;
-            sT[i] = T;
-            sS2[i] = S2;
-            sGam[i] = gam;
-            sDln[i] = dln;
-            sExpS[i] = __builtin_amdgcn_exp2f(S2);
-            sW[i] = __builtin_amdgcn_exp2f(S2e - S2) * (gam + dln);
+        for (int off = 1; off < 64; off <<= 1) {
+            const float v = __shfl_up(T, off);
+            if (lane >= off) T += v;
         }
-        __syncthreads();
+        const float S2 = A2 * T;
+        const float S2e = __shfl(S2, nq - 1);
+        const float Te = __shfl(T, nq - 1);
+        {
+            const float gam = pre.l * pre.d, dln = (1.f - pre.ln) * pre.dn;
+            wsc[lane] = S2;
+            wsc[64 + lane] = gam;
+            wsc[128 + lane] = dln;
+            wsc[192 + lane] = __builtin_amdgcn_exp2f(S2);
+            wsc[256 + lane] = __builtin_amdgcn_exp2f(S2e - S2) * (gam + dln);
+            wsc[320 + lane] = T;
+        }
 
-        // ---- 2. rotation table (cos, sin)(omega_k T_i), angles in revolutions
-        for (int e = tid; e < 64 * K; e += NT) {
-            const int i = e / K, k = e % K;
-            const float rev = __builtin_amdgcn_fractf(sOm[k] * sT[i]);
-            sCS[e] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-        }
-        __syncthreads();
-
-        // ---- 3. stage B~ and X^T in LDS, C~ strips in registers
-        for (int u = tid; u < QRP * 16; u += NT) {
-            const int rho = u >> 4, pc = u & 15;
-            const int i = rho / R, r = rho % R;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (i < nq)
-                v = *reinterpret_cast<const u32x4*>(Bm + (((b * L + c0 + i) * G + grp) * R + r) * N + 8 * pc);
-            *reinterpret_cast<u32x4*>(sBt + rho * NS + 8 * pc) = rot_neg(v, sCS + i * K + 4 * pc);
-        }
-        for (int u = tid; u < QRP * 4; u += NT) {
-            const int rp = u >> 3, pc = u & 7;
-            const int rho0 = 2 * rp;
-            u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-            {
-                const int i = rho0 / R, r = rho0 % R;
-                if (i < nq) v0 = *reinterpret_cast<const u32x4*>(x + (((b * L + c0 + i) * H + h) * R + r) * P + 8 * pc);
+        // ---- 2. stage B~ (and C~ when it lives in LDS) and X^T; one angle per (token, pair)
+#pragma unroll
+        for (int m = 0; m < S::UPT; ++m) {
+            const int i = (tid >> 4) + m * (NT / 16);
+            const float Ti = wsc[320 + i];
+            CS t[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[j] = cs_rev(omB[j], Ti);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int rho = i * R + r;
+                const u32x4 vb = pre.b[m][r];
+                *reinterpret_cast<u32x4*>(sBt + rho * NS + 8 * (tid & 15)) =
+                    u32x4{rot_pair(vb[0], t[0]), rot_pair(vb[1], t[1]), rot_pair(vb[2], t[2]), rot_pair(vb[3], t[3])};
+                if constexpr (S::C_LDS) {
+                    const u32x4 vc = pre.c[m][r];
+                    *reinterpret_cast<u32x4*>(sCt + rho * NS + 8 * (tid & 15)) = u32x4{
+                        rot_pair(vc[0], t[0]), rot_pair(vc[1], t[1]), rot_pair(vc[2], t[2]), rot_pair(vc[3], t[3])};
+                }
             }
-            {
-                const int i = (rho0 + 1) / R, r = (rho0 + 1) % R;
-                if (i < nq) v1 = *reinterpret_cast<const u32x4*>(x + (((b * L + c0 + i) * H + h) * R + r) * P + 8 * pc);
-            }
+        }
+#pragma unroll
+        for (int m = 0; m < S::XPT; ++m) {
+            if (S::XU % NT != 0 && tid + m * NT >= S::XU) break;
+            const int rho0 = 2 * ((tid >> 3) + m * (NT / 8));
+            const int pc = tid & 7;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int p = 8 * pc + 2 * j;
-                *reinterpret_cast<unsigned*>(sXT + p * XS + rho0) = (v0[j] & 0xffffu) | (v1[j] << 16);
-                *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) = (v0[j] >> 16) | (v1[j] & 0xffff0000u);
+                *reinterpret_cast<unsigned*>(sXT + p * XS + rho0) = (pre.x0[m][j] & 0xffffu) | (pre.x1[m][j] << 16);
+                *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) =
+                    (pre.x0[m][j] >> 16) | (pre.x1[m][j] & 0xffff0000u);
             }
         }
-        u32x4 cr[SPW][4];  // C~ of this wave's strips: row 16s + l16, n = 32 ks + 8 g4 + 0..7
+        u32x4 craw[4];
+        if constexpr (!S::C_LDS) {
 #pragma unroll
-        for (int si = 0; si < SPW; ++si) {
-            const int rho = 16 * strip_of<NW>(wave, si) + l16;
-            const int i = rho / R, r = rho % R;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (i < nq)
-                    v = *reinterpret_cast<const u32x4*>(Cm + (((b * L + c0 + i) * G + grp) * R + r) * N + 32 * ks +
-                                                        8 * g4);
-                cr[si][ks] = rot_neg(v, sCS + i * K + 16 * ks + 4 * g4);
-            }
+            for (int ks = 0; ks < 4; ++ks) craw[ks] = pre.cs[ks];
         }
-        __syncthreads();
 
-        // ---- 4. outputs of this wave's strips
-#pragma unroll
+        // ---- 3. prefetch the next chunk's scalars, B, C and X (in flight through the compute below)
+        const bool more = c + 1 < n_chunks;
+        const ChunkBase cbn = chunk_base(more ? c + 1 : c);
+        if (more) load_chunk<S>(pre, cbn, dt + h, lam + h, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
+        lds_barrier();
+
+        // ---- 4. outputs: work item = (16-row strip, group of PTW p tiles), y^T accumulated
+        //         (an accumulator lane holds y[rho_i][p..p+3] of one row: 8-byte stores)
+#pragma unroll 1
         for (int si = 0; si < SPW; ++si) {
-            const int s = strip_of<NW>(wave, si);
-            floatx4 acc[4];
+            const int item = strip_of<NW>(wave, si);
+            const int s = item / S::PTG, pt0 = (item % S::PTG) * S::PTW;
+            u32x4 cr[4];  // C~ rows of the strip, B-operand layout (col rho_i = 16 s + l16, k = n)
+            if constexpr (S::C_LDS) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < 4; ++ks)
+                    cr[ks] = *reinterpret_cast<const u32x4*>(sCt + (16 * s + l16) * NS + 32 * ks + 8 * g4);
+            } else {
+                // the 4 lanes of a DPP quad hold the 4 ranks of one token: each
+                // evaluates one of the quad's 4 angles and shares it
+                const float Ti = wsc[320 + ((16 * s + l16) >> LR)];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const u32x4 gb = *reinterpret_cast<const u32x4*>(sGT + (16 * pt + l16) * NS + 32 * ks + 8 * g4);
-                    acc[pt] = mfma32(cr[si][ks], gb, acc[pt]);
+                    const CS own = cs_rev(omC[ks], Ti);
+                    const CS t0{quad_bcast<0>(own.c), quad_bcast<0>(own.s)};
+                    const CS t1{quad_bcast<1>(own.c), quad_bcast<1>(own.s)};
+                    const CS t2{quad_bcast<2>(own.c), quad_bcast<2>(own.s)};
+                    const CS t3{quad_bcast<3>(own.c), quad_bcast<3>(own.s)};
+                    const u32x4 v = craw[ks];
+                    cr[ks] = u32x4{rot_pair(v[0], t0), rot_pair(v[1], t1), rot_pair(v[2], t2), rot_pair(v[3], t3)};
                 }
+                if (si + 1 < SPW) load_strip_c<S>(craw, cb, strip_of<NW>(wave, si + 1) / S::PTG, G, lane);
             }
+            const int ti = int((16u * s + l16) >> LR);  // token of this lane's column rho_i
+            const float S2i = wsc[ti];
+            // inter-chunk part: y^T[p][rho_i] = e^{S_i} sum_n g^T[p][n] C~[rho_i][n]
+            floatx4 acc[S::PTW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float f = sExpS[(16 * s + 4 * g4 + e) / R];
+            for (int q = 0; q < S::PTW; ++q) {
+                acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) acc[pt][e] *= f;
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u32x4 ga =
+                        *reinterpret_cast<const u32x4*>(gT + (16 * (pt0 + q) + l16) * NS + 32 * ks + 8 * g4);
+                    acc[q] = mfma32(ga, cr[ks], acc[q]);
+                }
+                acc[q] *= wsc[192 + ti];
             }
-            const int ti = (16 * s + l16) / R;  // token of this lane's score column
-            const float S2i = sS2[ti];
-            for (int jt = 0; jt <= s; jt += 2) {
-                const bool two = jt + 1 <= s;
-                floatx4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+            // score tiles in pairs, the next pair's MFMAs issued before this pair is masked
+            auto scores = [&](int jt, floatx4& t0, floatx4& t1) {
+                t0 = floatx4{0.f, 0.f, 0.f, 0.f};
+                t1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const u32x4 a0 = *reinterpret_cast<const u32x4*>(sBt + (16 * jt + l16) * NS + 32 * ks + 8 * g4);
-                    t0 = mfma32(a0, cr[si][ks], t0);
+                    t0 = mfma32(a0, cr[ks], t0);
                 }
-                if (two) {
+                if (jt + 1 <= s) {
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
                         const u32x4 a1 =
                             *reinterpret_cast<const u32x4*>(sBt + (16 * jt + 16 + l16) * NS + 32 * ks + 8 * g4);
-                        t1 = mfma32(a1, cr[si][ks], t1);
+                        t1 = mfma32(a1, cr[ks], t1);
                     }
                 }
+            };
+            floatx4 c0t, c1t;
+            scores(0, c0t, c1t);
+#pragma unroll 1
+            for (int jt = 0; jt <= s; jt += 2) {
+                floatx4 n0t, n1t;
+                if (jt + 2 <= s) scores(jt + 2, n0t, n1t);
+                const bool two = jt + 1 <= s;
+                const unsigned rj0 = 16u * jt + 4u * g4, rj1 = rj0 + 16u;
                 float m0[4], m1[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int tj0 = (16 * jt + 4 * g4 + e) / R;
-                    const float c0f = tj0 > ti ? 0.f
-                                               : __builtin_amdgcn_exp2f(S2i - sS2[tj0]) *
-                                                     (sGam[tj0] + (tj0 < ti ? sDln[tj0] : 0.f));
-                    m0[e] = t0[e] * c0f;
-                    const int tj1 = (16 * jt + 16 + 4 * g4 + e) / R;
-                    const float c1f = (!two || tj1 > ti) ? 0.f
-                                                         : __builtin_amdgcn_exp2f(S2i - sS2[tj1]) *
-                                                               (sGam[tj1] + (tj1 < ti ? sDln[tj1] : 0.f));
-                    m1[e] = t1[e] * c1f;
+                    m0[e] = c0t[e] * mask_coef(int((rj0 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc);
+                    m1[e] = two ? c1t[e] * mask_coef(int((rj1 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc) : 0.f;
                 }
                 const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
+                // y^T[p][rho_i] += sum_{rho_j} X^T[p][rho_j] (M o scores^T)[rho_j][rho_i]
                 if (two) {
-                    const u32x4 pa = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
+                    const u32x4 pb = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const uint16_t* xr = sXT + (16 * pt + l16) * XS + 16 * jt + 4 * g4;
+                    for (int q = 0; q < S::PTW; ++q) {
+                        const uint16_t* xr = sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4;
                         const u32x2 xa = *reinterpret_cast<const u32x2*>(xr);
                         const u32x2 xb = *reinterpret_cast<const u32x2*>(xr + 16);
-                        acc[pt] = mfma32(pa, u32x4{xa[0], xa[1], xb[0], xb[1]}, acc[pt]);
+                        acc[q] = mfma32(u32x4{xa[0], xa[1], xb[0], xb[1]}, pb, acc[q]);
                     }
                 } else {
-                    const u32x2 pa = {p00, p01};
+                    const u32x2 pb = {p00, p01};
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const u32x2 xa = *reinterpret_cast<const u32x2*>(sXT + (16 * pt + l16) * XS + 16 * jt + 4 * g4);
-                        acc[pt] = mfma16(pa, xa, acc[pt]);
+                    for (int q = 0; q < S::PTW; ++q) {
+                        const u32x2 xa =
+                            *reinterpret_cast<const u32x2*>(sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4);
+                        acc[q] = mfma16(xa, pb, acc[q]);
                     }
                 }
+                c0t = n0t;
+                c1t = n1t;
             }
-            // epilogue: + D x, store the valid rows
+            // epilogue: + D x, 4 consecutive p of row rho_i per lane
+            const unsigned rho = 16u * s + l16;
+            if (int(rho >> LR) < nq) {
+                const int i = int(rho >> LR), r = int(rho & (R - 1));
+                uint16_t* yr = y + ((b * L + c * Q) * H + h) * int64_t(R * P) + (i * H * R + r) * P;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rho = 16 * s + 4 * g4 + e;
-                const int i = rho / R, r = rho % R;
-                if (i < nq) {
-                    uint16_t* yr = y + (((b * L + c0 + i) * H + h) * R + r) * P;
+                for (int q = 0; q < S::PTW; ++q) {
+                    const int p = 16 * (pt0 + q) + 4 * g4;
+                    float v[4];
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const int p = 16 * pt + l16;
-                        const float xv = bf16_to_f32(sXT[p * XS + rho]);
-                        yr[p] = f32_to_bf16(acc[pt][e] + Dh * xv);
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] = acc[q][e] + Dh * bf16_to_f32(sXT[(p + e) * XS + rho]);
+                    *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
                 }
             }
         }
-        __syncthreads();  // every wave is done reading g^T
 
-        // ---- 5. state passed to the next chunk
+        // ---- 5. state passed to the next chunk (written to the other g^T buffer)
+        if constexpr (!S::C_LDS) {
+            if (more) load_strip_c<S>(pre.cs, cbn, strip_of<NW>(wave, 0) / S::PTG, G, lane);
+        }
         const int te = nq - 1;
-        const float decE = sExpS[te];
+        const float decE = wsc[192 + te];
 #pragma unroll
         for (int m = 0; m < TPW; ++m) gst[m] *= decE;
 #pragma unroll
         for (int mr = 0; mr < TPW / 4; ++mr) {
             const int nt = (wave * TPW) / 4 + mr;
             const int n = 16 * nt + l16;
-#pragma unroll
+#pragma unroll 2
             for (int ks = 0; ks < QRP / 32; ++ks) {
-                const int rb = 32 * ks + 8 * g4;
+                const unsigned rb = 32u * ks + 8u * g4;
                 float wv[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) wv[j] = bf16_to_f32(sBt[(rb + j) * NS + n]) * sW[(rb + j) / R];
+                for (int j = 0; j < 8; ++j)
+                    wv[j] = bf16_to_f32(sBt[(rb + j) * NS + n]) * wsc[256 + ((rb >> LR) + (unsigned(j) >> LR))];
                 const u32x4 a = {pack2(wv[0], wv[1]), pack2(wv[2], wv[3]), pack2(wv[4], wv[5]), pack2(wv[6], wv[7])};
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
@@ -357,21 +509,25 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             }
         }
 #pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
-            const int k0 = 8 * nt + 2 * g4;
+        for (int mr = 0; mr < TPW / 4; ++mr) {
+            const CS t0 = cs_rev(omS[mr][0], Te), t1 = cs_rev(omS[mr][1], Te);
+            const int nt = (wave * TPW) / 4 + mr;
 #pragma unroll
-            for (int hp = 0; hp < 2; ++hp) {
-                const float2 t = sCS[te * K + k0 + hp];
-                const float a0 = gst[m][2 * hp], a1 = gst[m][2 * hp + 1];
-                gst[m][2 * hp] = t.x * a0 - t.y * a1;
-                gst[m][2 * hp + 1] = t.y * a0 + t.x * a1;
+            for (int pt = 0; pt < 4; ++pt) {
+                const int m = mr * 4 + pt;
+                float a0 = gst[m][0], a1 = gst[m][1];
+                gst[m][0] = t0.c * a0 - t0.s * a1;
+                gst[m][1] = t0.s * a0 + t0.c * a1;
+                a0 = gst[m][2];
+                a1 = gst[m][3];
+                gst[m][2] = t1.c * a0 - t1.s * a1;
+                gst[m][3] = t1.s * a0 + t1.c * a1;
+                const int p = 16 * pt + l16;
+                *reinterpret_cast<u32x2*>(gTn + p * NS + 16 * nt + 4 * g4) =
+                    u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
             }
-            const int p = 16 * pt + l16;
-            *reinterpret_cast<u32x2*>(sGT + p * NS + 16 * nt + 4 * g4) =
-                u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (h_out) {
@@ -405,7 +561,7 @@ bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dt
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
     if (a.b * a.H > 0x7fffffff || a.plan.segments != 1) return hipErrorInvalidValue;
     switch (a.R) {
-        case 1: return launch_r<1, 4>(a);
+        case 1: return launch_r<1, 8>(a);
         case 2: return launch_r<2, 4>(a);
         case 4: return launch_r<4, 4>(a);
     }
