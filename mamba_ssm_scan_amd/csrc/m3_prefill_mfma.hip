@@ -541,6 +541,349 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     }
 }
 
+// ---------------------------------------------------------------------------
+// R = 1 with wave specialisation: 8 waves, waves 0-3 compute chunk c (scores,
+// masked product, inter-chunk term, state update) while waves 4-7 load, rotate
+// and stage chunk c+1 into the other half of double-buffered LDS and prefetch
+// chunk c+2 into registers. One barrier per chunk hands the buffers over. The
+// rotation and staging VALU work of one chunk thus runs next to the MFMA and
+// masking work of the previous one on every SIMD.
+namespace ws1 {
+
+constexpr int QRP = 64;      // rows per chunk (R = 1)
+constexpr int XS = QRP + 8;  // X^T row stride
+constexpr int NCW = 4;       // compute waves
+constexpr int TPW = 32 / NCW;
+
+struct StageRegs {
+    float d, l, dn, ln;
+    u32x4 b[4], c[4];  // token (stid >> 4) + 16 m, 8 columns at 8 (stid & 15)
+    u32x4 x0, x1;      // X rows 2 (stid >> 3), +1, 8 columns at 8 (stid & 7)
+};
+
+__device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, const float* __restrict__ dt,
+                                           const float* __restrict__ lam, int64_t tok0, int64_t L, int64_t c0, int H,
+                                           int G, int stid, int lane) {
+    const int nq = cb.nq;
+    {
+        const int ic = lane < nq ? lane : nq - 1;
+        const int64_t ti = (tok0 + ic) * H;
+        const float d = dt[ti], l = lam[ti];
+        const bool has_next = c0 + ic + 1 < L;
+        const float dn = dt[has_next ? ti + H : ti], ln = lam[has_next ? ti + H : ti];
+        r.d = lane < nq ? d : 0.f;
+        r.l = lane < nq ? l : 0.f;
+        r.dn = (lane < nq && has_next) ? dn : 0.f;
+        r.ln = (lane < nq && has_next) ? ln : 0.f;
+    }
+    const int pc = stid & 15;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = (stid >> 4) + 16 * m;
+        r.b[m] = load_tok(cb.B, i, nq, G * N, 8 * pc);
+        r.c[m] = load_tok(cb.C, i, nq, G * N, 8 * pc);
+    }
+    const int rho0 = 2 * (stid >> 3);
+    r.x0 = load_tok(cb.x, rho0, nq, H * P, 8 * (stid & 7));
+    r.x1 = load_tok(cb.x, rho0 + 1, nq, H * P, 8 * (stid & 7));
+}
+
+// rotate and write one chunk into LDS buffer `buf`; staging wave 0 also writes the scalars
+__device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2, const float* omB, uint16_t* sBt,
+                                            uint16_t* sCt, uint16_t* sXT, float* sSc, int stid, int lane) {
+    float T = r.d;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float v = __shfl_up(T, off);
+        if (lane >= off) T += v;
+    }
+    if (stid < 64) {
+        const float S2 = A2 * T;
+        const float S2e = __shfl(S2, nq - 1);
+        const float gam = r.l * r.d, dln = (1.f - r.ln) * r.dn;
+        sSc[lane] = S2;
+        sSc[64 + lane] = gam;
+        sSc[128 + lane] = dln;
+        sSc[192 + lane] = __builtin_amdgcn_exp2f(S2);
+        sSc[256 + lane] = __builtin_amdgcn_exp2f(S2e - S2) * (gam + dln);
+        sSc[320 + lane] = T;
+    }
+    const int pc = stid & 15;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = (stid >> 4) + 16 * m;
+        const float Ti = __shfl(T, i);
+        CS t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = cs_rev(omB[j], Ti);
+        const u32x4 vb = r.b[m], vc = r.c[m];
+        *reinterpret_cast<u32x4*>(sBt + i * NS + 8 * pc) =
+            u32x4{rot_pair(vb[0], t[0]), rot_pair(vb[1], t[1]), rot_pair(vb[2], t[2]), rot_pair(vb[3], t[3])};
+        *reinterpret_cast<u32x4*>(sCt + i * NS + 8 * pc) =
+            u32x4{rot_pair(vc[0], t[0]), rot_pair(vc[1], t[1]), rot_pair(vc[2], t[2]), rot_pair(vc[3], t[3])};
+    }
+    const int rho0 = 2 * (stid >> 3);
+    const int pcx = stid & 7;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int p = 8 * pcx + 2 * j;
+        *reinterpret_cast<unsigned*>(sXT + p * XS + rho0) = (r.x0[j] & 0xffffu) | (r.x1[j] << 16);
+        *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) = (r.x0[j] >> 16) | (r.x1[j] & 0xffff0000u);
+    }
+}
+
+}  // namespace ws1
+
+__global__ void __launch_bounds__(512)
+prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
+                     const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
+                     const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
+                     uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
+                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
+                     int64_t nbh) {
+    using namespace ws1;
+    __shared__ __attribute__((aligned(16))) uint16_t sBt[2][QRP * NS];  // B~ [rho][n]
+    __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NS];  // C~ [rho][n]
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];    // X^T [p][rho]
+    __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];    // g^T [p][n], bf16
+    __shared__ float sSc[2][6 * 64];  // S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    int64_t bh;
+    {
+        const int64_t bid = blockIdx.x, q8 = nbh / 8, r8 = nbh % 8;
+        const int64_t xcd = bid % 8, slot = bid / 8;
+        bh = xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+    }
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const int grp = h / (H / G);
+    const float A2 = Av[h] * kLog2e;
+    const float Dh = Dv[h];
+    const float* omh = omega + int64_t(h) * K;
+    auto chunk_base = [&](int64_t cc) {
+        const int64_t c0 = cc * Q, tok0 = b * L + c0;
+        ChunkBase cb;
+        cb.B = Bm + (tok0 * G + grp) * int64_t(N);
+        cb.C = Cm + (tok0 * G + grp) * int64_t(N);
+        cb.x = x + (tok0 * H + h) * int64_t(P);
+        cb.nq = int(L - c0 < Q ? L - c0 : Q);
+        return cb;
+    };
+
+    if (wave >= NCW) {
+        // ===================== staging waves
+        const int stid = tid - 64 * NCW;
+        float omB[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) omB[j] = omh[4 * (stid & 15) + j] * kInv2Pi;
+        StageRegs r;
+        {
+            const ChunkBase cb = chunk_base(0);
+            stage_load(r, cb, dt + h, lam + h, b * L, L, 0, H, G, stid, lane);
+            stage_write(r, cb.nq, A2, omB, sBt[0], sCt[0], sXT[0], sSc[0], stid, lane);
+        }
+        if (n_chunks > 1) stage_load(r, chunk_base(1), dt + h, lam + h, b * L + Q, L, Q, H, G, stid, lane);
+        lds_barrier();
+#pragma unroll 1
+        for (int64_t c = 0; c < n_chunks; ++c) {
+            if (c + 1 < n_chunks) {
+                const int bn = int((c + 1) & 1);
+                stage_write(r, chunk_base(c + 1).nq, A2, omB, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid, lane);
+                if (c + 2 < n_chunks)
+                    stage_load(r, chunk_base(c + 2), dt + h, lam + h, b * L + (c + 2) * Q, L, (c + 2) * Q, H, G, stid,
+                               lane);
+            }
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ========================= compute waves: strip `wave`, state tiles 8 wave .. 8 wave + 7
+    float omS[2][2];
+#pragma unroll
+    for (int mr = 0; mr < 2; ++mr)
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omh[8 * (2 * wave + mr) + 2 * g4 + hp] * kInv2Pi;
+    floatx4 gst[TPW];
+    {
+        const int64_t t0 = (b * L) * H + h;
+        const float dl0 = (1.f - lam[t0]) * dt[t0];
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+            const int p = 16 * pt + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = 16 * nt + 4 * g4 + e;
+                float v = h0 ? h0[(bh * N + n) * P + p] : 0.f;
+                if (carry_B)
+                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * N + n]) * bf16_to_f32(carry_x[bh * P + p]);
+                gst[m][e] = v;
+            }
+            *reinterpret_cast<u32x2*>(&sGT[0][p * NS + 16 * nt + 4 * g4]) =
+                u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
+        }
+    }
+    lds_barrier();
+
+    const int s = wave;
+    const int ti = 16 * s + l16;  // token of this lane's column
+#pragma unroll 1
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        const int buf = int(c & 1);
+        const int nq = int(L - c * Q < Q ? L - c * Q : Q);
+        const uint16_t* Bt = sBt[buf];
+        const uint16_t* Ct = sCt[buf];
+        const uint16_t* XT = sXT[buf];
+        const float* sc = sSc[buf];
+        const uint16_t* gT = sGT[buf];
+        uint16_t* gTn = sGT[buf ^ 1];
+
+        u32x4 cr[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) cr[ks] = *reinterpret_cast<const u32x4*>(Ct + ti * NS + 32 * ks + 8 * g4);
+        const float S2i = sc[ti];
+        floatx4 acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 ga = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
+                acc[q] = mfma32(ga, cr[ks], acc[q]);
+            }
+            acc[q] *= sc[192 + ti];
+        }
+        auto scores = [&](int jt, floatx4& t0, floatx4& t1) {
+            t0 = floatx4{0.f, 0.f, 0.f, 0.f};
+            t1 = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(Bt + (16 * jt + l16) * NS + 32 * ks + 8 * g4);
+                t0 = mfma32(a0, cr[ks], t0);
+            }
+            if (jt + 1 <= s) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(Bt + (16 * jt + 16 + l16) * NS + 32 * ks + 8 * g4);
+                    t1 = mfma32(a1, cr[ks], t1);
+                }
+            }
+        };
+        floatx4 c0t, c1t;
+        scores(0, c0t, c1t);
+#pragma unroll 1
+        for (int jt = 0; jt <= s; jt += 2) {
+            floatx4 n0t, n1t;
+            if (jt + 2 <= s) scores(jt + 2, n0t, n1t);
+            const bool two = jt + 1 <= s;
+            const int rj0 = 16 * jt + 4 * g4, rj1 = rj0 + 16;
+            float m0[4], m1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                m0[e] = c0t[e] * mask_coef(rj0 + e, ti, S2i, sc);
+                m1[e] = two ? c1t[e] * mask_coef(rj1 + e, ti, S2i, sc) : 0.f;
+            }
+            const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
+            if (two) {
+                const u32x4 pb = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint16_t* xr = XT + (16 * q + l16) * XS + 16 * jt + 4 * g4;
+                    const u32x2 xa = *reinterpret_cast<const u32x2*>(xr);
+                    const u32x2 xb = *reinterpret_cast<const u32x2*>(xr + 16);
+                    acc[q] = mfma32(u32x4{xa[0], xa[1], xb[0], xb[1]}, pb, acc[q]);
+                }
+            } else {
+                const u32x2 pb = {p00, p01};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 xa = *reinterpret_cast<const u32x2*>(XT + (16 * q + l16) * XS + 16 * jt + 4 * g4);
+                    acc[q] = mfma16(xa, pb, acc[q]);
+                }
+            }
+            c0t = n0t;
+            c1t = n1t;
+        }
+        if (ti < nq) {
+            uint16_t* yr = y + ((b * L + c * Q + ti) * H + h) * int64_t(P);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int p = 16 * q + 4 * g4;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[q][e] + Dh * bf16_to_f32(XT[(p + e) * XS + ti]);
+                *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+            }
+        }
+
+        // state update
+        const int te = nq - 1;
+        const float decE = sc[192 + te];
+        const float Te = sc[320 + te];
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) gst[m] *= decE;
+#pragma unroll
+        for (int mr = 0; mr < 2; ++mr) {
+            const int n = 16 * (2 * wave + mr) + l16;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rb = 32 * ks + 8 * g4;
+                float wv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) wv[j] = bf16_to_f32(Bt[(rb + j) * NS + n]) * sc[256 + rb + j];
+                const u32x4 a = {pack2(wv[0], wv[1]), pack2(wv[2], wv[3]), pack2(wv[4], wv[5]), pack2(wv[6], wv[7])};
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const u32x4 xb = *reinterpret_cast<const u32x4*>(XT + (16 * pt + l16) * XS + rb);
+                    gst[mr * 4 + pt] = mfma32(a, xb, gst[mr * 4 + pt]);
+                }
+            }
+        }
+#pragma unroll
+        for (int mr = 0; mr < 2; ++mr) {
+            const CS t0 = cs_rev(omS[mr][0], Te), t1 = cs_rev(omS[mr][1], Te);
+            const int nt = 2 * wave + mr;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int m = mr * 4 + pt;
+                float a0 = gst[m][0], a1 = gst[m][1];
+                gst[m][0] = t0.c * a0 - t0.s * a1;
+                gst[m][1] = t0.s * a0 + t0.c * a1;
+                a0 = gst[m][2];
+                a1 = gst[m][3];
+                gst[m][2] = t1.c * a0 - t1.s * a1;
+                gst[m][3] = t1.s * a0 + t1.c * a1;
+                const int p = 16 * pt + l16;
+                *reinterpret_cast<u32x2*>(gTn + p * NS + 16 * nt + 4 * g4) =
+                    u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
+            }
+        }
+        lds_barrier();
+    }
+    if (h_out) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+            const int p = 16 * pt + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = gst[m][e];
+        }
+    }
+}
+
+hipError_t launch_ws_r1(const PrefillArgs& a) {
+    const int64_t nbh = a.b * a.H;
+    hipLaunchKernelGGL(prefill_ws_r1_kernel, dim3(unsigned(nbh)), dim3(512), 0, a.stream,
+                       static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
+                       static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
+                       static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
+                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
+    return hipGetLastError();
+}
+
 template <int R, int NW>
 hipError_t launch_r(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
@@ -561,7 +904,7 @@ bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dt
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
     if (a.b * a.H > 0x7fffffff || a.plan.segments != 1) return hipErrorInvalidValue;
     switch (a.R) {
-        case 1: return launch_r<1, 8>(a);
+        case 1: return launch_ws_r1(a);
         case 2: return launch_r<2, 4>(a);
         case 4: return launch_r<4, 4>(a);
     }
