@@ -89,7 +89,7 @@ m3_status make_plan(const m3_dims* d, int32_t R, int32_t chunk, m3_dtype io, m3_
     p->last_chunk_len = L == 0 ? 0 : L - (p->n_chunks - 1) * chunk;
     const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
     p->path = mfma ? M3_PATH_MFMA : M3_PATH_GENERIC;
-    p->segments = 1;
+    p->segments = (mfma && m3::mfma_segments_supported(R)) ? choose_segments(d->batch * d->heads, p->n_chunks) : 1;
     p->chunks_per_segment = p->segments > 0 ? (p->n_chunks + p->segments - 1) / p->segments : 0;
     if (mfma && p->chunks_per_segment > 0)  // no empty trailing segment
         p->segments = (int32_t)((p->n_chunks + p->chunks_per_segment - 1) / p->chunks_per_segment);
@@ -122,7 +122,7 @@ PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32
         w.incl_off = off;
         off += up256(nseg * size_t(N) * size_t(P) * 4);
         w.tr_off = off;
-        off += up256(nseg * 4);
+        off += up256(nseg * 8);
     }
     w.total = off;
     return w;

@@ -57,7 +57,7 @@ struct PrefillWorkspace {
     size_t ctrl_off;       // segmented path: ticket counter + flags
     size_t agg_off;        // segmented path: per-segment local end state [b*H*S][N][P] fp32
     size_t incl_off;       // segmented path: per-segment inclusive end state
-    size_t tr_off;         // segmented path: per-segment transfer (cum dt) [b*H*S] fp32
+    size_t tr_off;         // segmented path: per-segment total step (sum of dt) [b*H*S] fp64
     size_t total;
 };
 
@@ -65,6 +65,8 @@ PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32
                                           int32_t path);
 
 bool mfma_path_supported(int32_t P, int32_t N, int32_t R, int32_t chunk, m3_dtype io);
+// the MFMA path splits the sequence into segments (look-back) at these ranks
+bool mfma_segments_supported(int32_t R);
 
 hipError_t launch_prefill_generic(const PrefillArgs& a);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);

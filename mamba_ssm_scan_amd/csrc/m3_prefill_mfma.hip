@@ -202,6 +202,37 @@ __device__ __forceinline__ float mask_coef(int tj, int ti, float S2i, const floa
     return __builtin_amdgcn_exp2f(S2i - w[tj]) * (w[64 + tj] + (tj < ti ? w[128 + tj] : 0.f));
 }
 
+// Sequence segments (decoupled look-back). Workspace layout, per (b, h, segment)
+// index bs = (b*H + h) * nseg + seg: ctrl[0] ticket counter, ctrl[1] error flag
+// (a look-back wait that ran out of patience), ctrl[2 + bs] state flag
+// (1 = local end state published, 2 = inclusive end state published);
+// agg/incl [bs][N][P] fp32; tr[bs] the segment's total step (sum of dt).
+struct SegArgs {
+    int nseg;
+    int64_t cps;  // chunks per segment
+    unsigned* ctrl;
+    float* agg;
+    float* incl;
+    double* tr;
+};
+constexpr long kSpinLimit = 1L << 24;
+
+// The state map of a stretch with total step T: pair k turned by omega_k T and
+// scaled by e^{A T}; om_rev = omega_k / 2 pi of the lane's two pairs.
+__device__ __forceinline__ floatx4 transfer(floatx4 v, float A2, const float* om_rev, double T) {
+    const float dec = __builtin_amdgcn_exp2f(float(double(A2) * T));
+    floatx4 o;
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+        const double rv = double(om_rev[hp]) * T;
+        const float r = float(rv - floor(rv));
+        const float c = __builtin_amdgcn_cosf(r) * dec, sn = __builtin_amdgcn_sinf(r) * dec;
+        o[2 * hp] = c * v[2 * hp] - sn * v[2 * hp + 1];
+        o[2 * hp + 1] = sn * v[2 * hp] + c * v[2 * hp + 1];
+    }
+    return o;
+}
+
 template <int R, int NW>
 __global__ void __launch_bounds__(64 * NW)
 prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
@@ -209,7 +240,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                     const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                     uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                    int64_t nbh) {
+                    int64_t nbh, SegArgs sa) {
     using S = Shape<R, NW>;
     using CR = ChunkRegs<S>;
     constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW, LR = S::LR;
@@ -223,14 +254,26 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    // XCD-aware order: the 8 XCDs take blocks round-robin; give each a
-    // contiguous run of (b, h) so heads sharing B/C share an L2.
+    __shared__ unsigned sTicket;
     int64_t bh;
-    {
+    int seg = 0;
+    if (sa.nseg > 1) {
+        // segments in ticket order, segment-major: a workgroup only ever waits
+        // for lower tickets, which are already running
+        if (tid == 0) sTicket = __hip_atomic_fetch_add(&sa.ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int64_t t = sTicket;
+        seg = int(t / nbh);
+        bh = t % nbh;
+    } else {
+        // XCD-aware order: the 8 XCDs take blocks round-robin; give each a
+        // contiguous run of (b, h) so heads sharing B/C share an L2.
         const int64_t bid = blockIdx.x, q8 = nbh / 8, r8 = nbh % 8;
         const int64_t xcd = bid % 8, slot = bid / 8;
         bh = xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
     }
+    const int64_t c_begin = int64_t(seg) * sa.cps;
+    const int64_t c_end = c_begin + sa.cps < n_chunks ? c_begin + sa.cps : n_chunks;
     const int64_t b = bh / H;
     const int h = int(bh % H);
     const int grp = h / (H / G);
@@ -262,14 +305,22 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 
     CR pre;
     {
-        const ChunkBase cb = chunk_base(0);
-        load_chunk<S>(pre, cb, dt + h, lam + h, b * L, L, 0, H, G, tid, lane);
+        const ChunkBase cb = chunk_base(c_begin);
+        load_chunk<S>(pre, cb, dt + h, lam + h, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
         if constexpr (!S::C_LDS) load_strip_c<S>(pre.cs, cb, strip_of<NW>(wave, 0) / S::PTG, G, lane);
     }
 
     // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
+    //      (a later segment starts from zero: its incoming state is added afterwards)
     floatx4 gst[TPW];
-    {
+    if (seg > 0) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+            gst[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<u32x2*>(&sGT[0][(16 * pt + l16) * NS + 16 * nt + 4 * g4]) = u32x2{0u, 0u};
+        }
+    } else {
         const int64_t t0 = (b * L) * H + h;
         const float dl0 = (1.f - lam[t0]) * dt[t0];
 #pragma unroll
@@ -295,12 +346,13 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         }
     }
 
+    double segT = 0.0;  // total step of this segment
 #pragma unroll 1
-    for (int64_t c = 0; c < n_chunks; ++c) {
+    for (int64_t c = c_begin; c < c_end; ++c) {
         const ChunkBase cb = chunk_base(c);
         const int nq = cb.nq;
-        const uint16_t* gT = sGT[c & 1];
-        uint16_t* gTn = sGT[(c + 1) & 1];
+        const uint16_t* gT = sGT[(c - c_begin) & 1];
+        uint16_t* gTn = sGT[(c - c_begin + 1) & 1];
 
         // ---- 1. per-token scalars, computed by every wave for itself (lane = token)
         float T = pre.d;
@@ -363,9 +415,10 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         }
 
         // ---- 3. prefetch the next chunk's scalars, B, C and X (in flight through the compute below)
-        const bool more = c + 1 < n_chunks;
+        const bool more = c + 1 < c_end;
         const ChunkBase cbn = chunk_base(more ? c + 1 : c);
         if (more) load_chunk<S>(pre, cbn, dt + h, lam + h, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
+        segT += double(Te);
         lds_barrier();
 
         // ---- 4. outputs: work item = (16-row strip, group of PTW p tiles), y^T accumulated
@@ -530,6 +583,160 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         lds_barrier();
     }
 
+    if (sa.nseg > 1) {
+        // ================= sequence segments: look-back and correction
+        __shared__ unsigned sFlag;
+        const int64_t bs = bh * sa.nseg + seg;
+        auto tile_ptr = [&](float* base, int m) {  // this lane's first element of state tile m
+            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+            return base + (16 * nt + 4 * g4) * P + 16 * pt + l16;
+        };
+        auto publish = [&](float* dst, const floatx4* v, unsigned flag, bool with_total) {
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                float* q = tile_ptr(dst + bs * (N * P), m);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e * P] = v[m][e];
+            }
+            __syncthreads();
+            if (tid == 0) {
+                if (with_total) sa.tr[bs] = segT;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(&sa.ctrl[2 + bs], flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        floatx4 gin[TPW];  // state entering this segment (g form)
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) gin[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (seg == 0) {
+            publish(sa.incl, gst, 2u, false);
+        } else {
+            publish(sa.agg, gst, 1u, true);
+            double Tacc = 0.0;  // total step between predecessor j's end and this segment's start
+            for (int j = seg - 1; j >= 0; --j) {
+                const int64_t bj = bh * sa.nseg + j;
+                if (tid == 0) {
+                    unsigned f;
+                    long spins = 0;
+                    while ((f = __hip_atomic_load(&sa.ctrl[2 + bj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+                           0u) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins > kSpinLimit) {
+                            __hip_atomic_store(&sa.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            f = 2u;
+                            break;
+                        }
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    sFlag = f;
+                }
+                __syncthreads();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                const unsigned f = sFlag;
+                const float* src = (f == 2u ? sa.incl : sa.agg) + bj * (N * P);
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    const float* q = tile_ptr(const_cast<float*>(src), m);
+                    const floatx4 v = {q[0], q[P], q[2 * P], q[3 * P]};
+                    gin[m] += transfer(v, A2, omS[m >> 2], Tacc);
+                }
+                if (f == 2u) break;
+                Tacc += sa.tr[bj];
+                __syncthreads();
+            }
+            // inclusive end state = transfer(segment) g_in + local end state
+            floatx4 inc[TPW];
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) inc[m] = transfer(gin[m], A2, omS[m >> 2], segT) + gst[m];
+            publish(sa.incl, inc, 2u, false);
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) gst[m] = inc[m];
+
+            // correction: y_t += e^{S_t} C~_t^T g_c for the part g_c of the chunk-entry
+            // state that comes from g_in, chunk by chunk until its decay is exactly 0
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+                *reinterpret_cast<u32x2*>(&sGT[0][(16 * pt + l16) * NS + 16 * nt + 4 * g4]) =
+                    u32x2{pack2(gin[m][0], gin[m][1]), pack2(gin[m][2], gin[m][3])};
+            }
+            __syncthreads();
+            double Tcum = 0.0;
+#pragma unroll 1
+            for (int64_t c = c_begin; c < c_end; ++c) {
+                if (__builtin_amdgcn_exp2f(float(double(A2) * Tcum)) == 0.f) break;
+                const int64_t c0 = c * Q;
+                const int nq = int(L - c0 < Q ? L - c0 : Q);
+                float T = 0.f;
+                if (lane < nq) T = dt[(b * L + c0 + lane) * H + h];
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float v = __shfl_up(T, off);
+                    if (lane >= off) T += v;
+                }
+                const float Te = __shfl(T, nq - 1);
+                wsc[192 + lane] = __builtin_amdgcn_exp2f(A2 * T);
+                wsc[320 + lane] = T;
+                const ChunkBase cbc = chunk_base(c);
+                const uint16_t* gT = sGT[(c - c_begin) & 1];
+#pragma unroll 1
+                for (int si = 0; si < SPW; ++si) {
+                    const int item = strip_of<NW>(wave, si);
+                    const int s = item / S::PTG, pt0 = (item % S::PTG) * S::PTW;
+                    const unsigned rho = 16u * s + l16;
+                    const int ti = int(rho >> LR);
+                    const float Ti = wsc[320 + ti];
+                    u32x4 craw2[4], cr[4];
+                    load_strip_c<S>(craw2, cbc, s, G, lane);
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        CS t[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            t[j] = cs_rev(omh[16 * ks + 4 * g4 + j] * kInv2Pi, Ti);
+                        cr[ks] = u32x4{rot_pair(craw2[ks][0], t[0]), rot_pair(craw2[ks][1], t[1]),
+                                       rot_pair(craw2[ks][2], t[2]), rot_pair(craw2[ks][3], t[3])};
+                    }
+                    floatx4 a[S::PTW];
+#pragma unroll
+                    for (int q = 0; q < S::PTW; ++q) {
+                        a[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks) {
+                            const u32x4 ga = *reinterpret_cast<const u32x4*>(gT + (16 * (pt0 + q) + l16) * NS +
+                                                                             32 * ks + 8 * g4);
+                            a[q] = mfma32(ga, cr[ks], a[q]);
+                        }
+                    }
+                    if (ti < nq) {
+                        uint16_t* yr = y + ((b * L + c0) * H + h) * int64_t(R * P) +
+                                       (ti * H * R + int(rho & (R - 1))) * P;
+                        const float f = wsc[192 + ti];
+#pragma unroll
+                        for (int q = 0; q < S::PTW; ++q) {
+                            const int pp = 16 * (pt0 + q) + 4 * g4;
+                            const u32x2 old = *reinterpret_cast<const u32x2*>(yr + pp);
+                            *reinterpret_cast<u32x2*>(yr + pp) =
+                                u32x2{pack2(lo16(old[0]) + f * a[q][0], hi16(old[0]) + f * a[q][1]),
+                                      pack2(lo16(old[1]) + f * a[q][2], hi16(old[1]) + f * a[q][3])};
+                        }
+                    }
+                }
+                // g_{c+1} = e^{S_e} Rot(Phi_e) g_c (no input)
+                uint16_t* gTn = sGT[(c - c_begin + 1) & 1];
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+                    gin[m] = transfer(gin[m], A2, omS[m >> 2], double(Te));
+                    *reinterpret_cast<u32x2*>(gTn + (16 * pt + l16) * NS + 16 * nt + 4 * g4) =
+                        u32x2{pack2(gin[m][0], gin[m][1]), pack2(gin[m][2], gin[m][3])};
+                }
+                Tcum += double(Te);
+                __syncthreads();
+            }
+        }
+        if (seg != sa.nseg - 1) return;
+    }
     if (h_out) {
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
@@ -887,11 +1094,24 @@ hipError_t launch_ws_r1(const PrefillArgs& a) {
 template <int R, int NW>
 hipError_t launch_r(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
-    hipLaunchKernelGGL((prefill_mfma_kernel<R, NW>), dim3(unsigned(nbh)), dim3(64 * NW), 0, a.stream,
+    SegArgs sa{a.plan.segments, a.plan.chunks_per_segment, nullptr, nullptr, nullptr, nullptr};
+    if (sa.nseg > 1) {
+        const PrefillWorkspace w = prefill_workspace_layout(a.b, a.H, a.P, a.N, a.plan.segments, a.plan.path);
+        char* base = static_cast<char*>(a.workspace);
+        sa.ctrl = reinterpret_cast<unsigned*>(base + w.ctrl_off);
+        sa.agg = reinterpret_cast<float*>(base + w.agg_off);
+        sa.incl = reinterpret_cast<float*>(base + w.incl_off);
+        sa.tr = reinterpret_cast<double*>(base + w.tr_off);
+        // ticket, error flag and per-segment flags start at zero (a kernel, so
+        // the call stays capturable in a graph)
+        const hipError_t e = launch_copy_or_zero(sa.ctrl, nullptr, 2 + nbh * sa.nseg, a.stream);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((prefill_mfma_kernel<R, NW>), dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW), 0, a.stream,
                        static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                        static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                        static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
+                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, sa);
     return hipGetLastError();
 }
 
@@ -901,8 +1121,11 @@ bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dt
     return io == M3_BF16 && N_ == N && P_ == P && (R == 1 || R == 2 || R == 4) && chunk >= 1 && chunk <= 64;
 }
 
+bool mfma_segments_supported(int32_t R) { return R != 1; }
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
-    if (a.b * a.H > 0x7fffffff || a.plan.segments != 1) return hipErrorInvalidValue;
+    if (a.b * a.H * a.plan.segments > 0x7fffffff) return hipErrorInvalidValue;
+    if (a.R == 1 && a.plan.segments != 1) return hipErrorInvalidValue;
     switch (a.R) {
         case 1: return launch_ws_r1(a);
         case 2: return launch_r<2, 4>(a);

@@ -147,3 +147,17 @@ def test_carry_bytes(lib):
     d = _dims(b=3, H=4, G=2, P=8, N=16)
     assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 0) == 2 * 3 * 2 * 2 * 16 * 2
     assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 1) == 2 * 3 * 4 * 2 * 8 * 2
+
+
+def test_plan_segments_for_few_heads(lib):
+    # b*H = 64 walks over 512 chunks: split into segments so every CU has one
+    d = bd.dims(1, 32768, 64, 1, 64, 128)
+    p = bd.plan(d, 4, 64, bd.M3_BF16)
+    assert p.path == bd.M3_PATH_MFMA
+    assert p.segments == 4 and p.chunks_per_segment == 128
+    assert p.workspace_bytes >= 2 * 64 * 4 * 128 * 64 * 4
+    # enough walks already: one segment, no workspace
+    p1 = bd.plan(bd.dims(4, 2048, 64, 1, 64, 128), 4, 64, bd.M3_BF16)
+    assert p1.segments == 1 and p1.workspace_bytes == 0
+    # the R=1 kernel walks whole sequences
+    assert bd.plan(d, 1, 64, bd.M3_BF16).segments == 1
