@@ -196,10 +196,13 @@ __device__ __forceinline__ void load_strip_c(u32x4 (&c)[4], const ChunkBase& cb,
         c[ks] = load_tok(cb.C, i, cb.nq, G * S::R * N, r * N + 32 * ks + 8 * (lane >> 4));
 }
 
-// M_ij (decay x width-2 convolution mask) for row token tj and column token ti
+// M_ij (decay x width-2 convolution mask) for row token tj and column token ti.
+// Branch-free: the loads are always in range (tj < 64) and the causal cut is a
+// select, so a wavefront whose lanes straddle the diagonal does not diverge.
 __device__ __forceinline__ float mask_coef(int tj, int ti, float S2i, const float* w) {
-    if (tj > ti) return 0.f;
-    return __builtin_amdgcn_exp2f(S2i - w[tj]) * (w[64 + tj] + (tj < ti ? w[128 + tj] : 0.f));
+    const float s2j = w[tj], gam = w[64 + tj], dln = w[128 + tj];
+    const float coef = __builtin_amdgcn_exp2f(S2i - s2j) * (gam + (tj < ti ? dln : 0.f));
+    return tj > ti ? 0.f : coef;
 }
 
 // Sequence segments (decoupled look-back). Workspace layout, per (b, h, segment)
@@ -493,7 +496,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     m0[e] = c0t[e] * mask_coef(int((rj0 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc);
-                    m1[e] = two ? c1t[e] * mask_coef(int((rj1 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc) : 0.f;
+                    m1[e] = c1t[e] * mask_coef(int((rj1 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc);
                 }
                 const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
                 // y^T[p][rho_i] += sum_{rho_j} X^T[p][rho_j] (M o scores^T)[rho_j][rho_i]
@@ -991,7 +994,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 m0[e] = c0t[e] * mask_coef(rj0 + e, ti, S2i, sc);
-                m1[e] = two ? c1t[e] * mask_coef(rj1 + e, ti, S2i, sc) : 0.f;
+                m1[e] = c1t[e] * mask_coef(rj1 + e, ti, S2i, sc);
             }
             const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
             if (two) {
