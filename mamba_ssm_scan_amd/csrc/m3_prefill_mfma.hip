@@ -254,7 +254,8 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];                // g^T [p][n], bf16, 2 buffers
     __shared__ float sW[NW][6 * 64];  // per wave: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int l16 = lane & 15, g4 = lane >> 4;
 
     __shared__ unsigned sTicket;
@@ -858,7 +859,8 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];    // g^T [p][n], bf16
     __shared__ float sSc[2][6 * 64];  // S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int l16 = lane & 15, g4 = lane >> 4;
     int64_t bh;
     {
