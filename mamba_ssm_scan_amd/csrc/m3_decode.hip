@@ -19,22 +19,42 @@
 namespace m3 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // generic kernel
+constexpr float kInv2Pi = 0.15915494309189535f;
 
-// N = 128, P = 64: thread (kk, q) owns rows (2k, 2k+1), k = kk + 16*it, it < 4,
-// and columns 4q..4q+3, loaded and stored as float4 (a wave covers four 256-byte
-// row segments per access).
-template <typename T, int R>
-__global__ void __launch_bounds__(kThreads)
+// (cos, sin) of theta = dt * omega through the hardware sine/cosine, which take
+// revolutions: the per-step angle is a few radians at most, so after fract()
+// the result is accurate to ~1e-6 absolute.
+__device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
+    const float r = __builtin_amdgcn_fractf(theta * kInv2Pi);
+    *s = __builtin_amdgcn_sinf(r);
+    *c = __builtin_amdgcn_cosf(r);
+}
+
+// Threads per workgroup of the N = 128, P = 64 kernel, per rank class.
+#ifndef M3_DECODE_THREADS_R1
+#define M3_DECODE_THREADS_R1 512
+#endif
+#ifndef M3_DECODE_THREADS_R4
+#define M3_DECODE_THREADS_R4 1024
+#endif
+
+// N = 128, P = 64: thread (kk, q) owns rows (2k, 2k+1), k = kk + (NTH/16)*it,
+// it < 1024/NTH, and columns 4q..4q+3, loaded and stored as float4 (a wave
+// covers four 256-byte row segments per access).
+template <typename T, int R, int NTH>
+__global__ void __launch_bounds__(NTH)
 decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
                        const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                        const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                        const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
                        int G) {
     constexpr int N = 128, P = 64, K = 64;
+    constexpr int IT = 1024 / NTH;  // row pairs per thread
+    constexpr int KS = NTH / 16;    // row-pair stride between a thread's iterations
     __shared__ float sB[R][N], sBp[R][N], sC[R][N];
     __shared__ float sx[R][P], sxp[R][P];
-    __shared__ float red[kThreads / 64][R][P];
+    __shared__ float red[NTH / 64][R][P];
 
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -45,10 +65,10 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
     float* hs = hstate + bh * (N * P);
     const int q = tid & 15, kk = tid >> 4;
 
-    float4 v0[4], v1[4];
+    float4 v0[IT], v1[IT];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int k = kk + 16 * it;
+    for (int it = 0; it < IT; ++it) {
+        const int k = kk + KS * it;
         v0[it] = *reinterpret_cast<const float4*>(hs + (2 * k) * P + 4 * q);
         v1[it] = *reinterpret_cast<const float4*>(hs + (2 * k + 1) * P + 4 * q);
     }
@@ -58,12 +78,12 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
     const T* Bp = carry_B + (int64_t(rd_slot) * nb * G + bg) * (R * N);
     const T* xt = x + bh * (R * P);
     const T* xp = carry_x + (int64_t(rd_slot) * nb * H + bh) * (R * P);
-    for (int e = tid; e < R * N; e += kThreads) {
+    for (int e = tid; e < R * N; e += NTH) {
         (&sB[0][0])[e] = Io<T>::load(Bt, e);
         (&sBp[0][0])[e] = Io<T>::load(Bp, e);
         (&sC[0][0])[e] = Io<T>::load(Ct, e);
     }
-    for (int e = tid; e < R * P; e += kThreads) {
+    for (int e = tid; e < R * P; e += NTH) {
         (&sx[0][0])[e] = Io<T>::load(xt, e);
         (&sxp[0][0])[e] = Io<T>::load(xp, e);
     }
@@ -79,10 +99,12 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
         for (int c = 0; c < 4; ++c) yacc[r][c] = 0.f;
 
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int k = kk + 16 * it;
+    for (int it = 0; it < IT; ++it) {
+        const int k = kk + KS * it;
         float sn, cs;
-        sincosf(d * omega[int64_t(h) * K + k], &sn, &cs);
+        sincos_step(d * omega[int64_t(h) * K + k], &sn, &cs);
+        sn *= alpha;  // alpha folded into the rotation
+        cs *= alpha;
         float e0[4] = {v0[it].x, v0[it].y, v0[it].z, v0[it].w};
         float e1[4] = {v1[it].x, v1[it].y, v1[it].z, v1[it].w};
 #pragma unroll
@@ -97,8 +119,8 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
                 u1 += sB[r][2 * k + 1] * sx[r][p];
             }
             const float g0 = e0[c] + delta * up0, g1 = e1[c] + delta * up1;
-            const float n0 = alpha * (cs * g0 - sn * g1) + gamma * u0;
-            const float n1 = alpha * (sn * g0 + cs * g1) + gamma * u1;
+            const float n0 = (cs * g0 - sn * g1) + gamma * u0;
+            const float n1 = (sn * g0 + cs * g1) + gamma * u1;
             e0[c] = n0;
             e1[c] = n1;
 #pragma unroll
@@ -108,7 +130,7 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
         *reinterpret_cast<float4*>(hs + (2 * k + 1) * P + 4 * q) = make_float4(e1[0], e1[1], e1[2], e1[3]);
     }
 
-    // reduce over the 16 row groups: 4 in a wave (lanes 16 apart), then 4 waves
+    // reduce over the row groups: 4 in a wave (lanes 16 apart), then across waves
     const int wave = tid >> 6;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -121,19 +143,19 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
         }
     __syncthreads();
     const float Dh = D[h];
-    for (int e = tid; e < R * P; e += kThreads) {
+    for (int e = tid; e < R * P; e += NTH) {
         const int r = e / P, p = e % P;
         float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < kThreads / 64; ++w) s += red[w][r][p];
+        for (int w = 0; w < NTH / 64; ++w) s += red[w][r][p];
         Io<T>::store(y, bh * (R * P) + e, s + Dh * sx[r][p]);
     }
 
     // this token becomes the carry of the next step
     const int wr = rd_slot ^ 1;
-    for (int e = tid; e < R * P; e += kThreads) carry_x[(int64_t(wr) * nb * H + bh) * (R * P) + e] = xt[e];
+    for (int e = tid; e < R * P; e += NTH) carry_x[(int64_t(wr) * nb * H + bh) * (R * P) + e] = xt[e];
     if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += kThreads) carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = Bt[e];
+        for (int e = tid; e < R * N; e += NTH) carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = Bt[e];
 }
 
 // Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
@@ -172,7 +194,7 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
             u1 += Io<T>::load(Bt, int64_t(r) * N + 2 * k + 1) * xv;
         }
         float sn, cs;
-        sincosf(d * omega[int64_t(h) * K + k], &sn, &cs);
+        sincos_step(d * omega[int64_t(h) * K + k], &sn, &cs);
         const float g0 = hs[int64_t(2 * k) * P + p] + delta * up0;
         const float g1 = hs[int64_t(2 * k + 1) * P + p] + delta * up1;
         hs[int64_t(2 * k) * P + p] = alpha * (cs * g0 - sn * g1) + gamma * u0;
@@ -203,9 +225,11 @@ hipError_t launch_t(const DecodeArgs& a) {
     const T* C = static_cast<const T*>(a.C);
     T* y = static_cast<T*>(a.y);
     if (a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4)) {
-        auto kern = a.R == 1 ? decode_n128_p64_kernel<T, 1>
-                  : a.R == 2 ? decode_n128_p64_kernel<T, 2> : decode_n128_p64_kernel<T, 4>;
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A,
+        auto kern = a.R == 1 ? decode_n128_p64_kernel<T, 1, M3_DECODE_THREADS_R1>
+                  : a.R == 2 ? decode_n128_p64_kernel<T, 2, M3_DECODE_THREADS_R4>
+                             : decode_n128_p64_kernel<T, 4, M3_DECODE_THREADS_R4>;
+        const int nth = a.R == 1 ? M3_DECODE_THREADS_R1 : M3_DECODE_THREADS_R4;
+        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A,
                            a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     } else {
         hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x,

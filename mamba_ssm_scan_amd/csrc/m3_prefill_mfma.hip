@@ -89,6 +89,29 @@ __device__ __forceinline__ float quad_bcast(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, false));
 }
 
+__device__ __forceinline__ float lane_read(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Inclusive prefix sum over the 64 lanes of a wavefront, kept off the LDS
+// crossbar (a ds_bpermute shuffle would queue behind the MFMA operand reads and
+// serialise every step): DPP right shifts inside each 16-lane row, then the
+// row totals carried across rows through scalar registers.
+__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));
+    const float r0 = lane_read(v, 15), r1 = lane_read(v, 31), r2 = lane_read(v, 47);
+    const int row = lane >> 4;
+    return v + ((row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f));
+}
+// value of lane 16 * (lane / 16) + 15 (the last lane of each row)
+__device__ __forceinline__ float row_last(float v, int lane) {
+    const float r0 = lane_read(v, 15), r1 = lane_read(v, 31), r2 = lane_read(v, 47), r3 = lane_read(v, 63);
+    const int row = lane >> 4;
+    return row == 0 ? r0 : row == 1 ? r1 : row == 2 ? r2 : r3;
+}
+
 template <int R_, int NW_>
 struct Shape {
     static constexpr int R = R_, NW = NW_;
@@ -359,15 +382,10 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         uint16_t* gTn = sGT[(c - c_begin + 1) & 1];
 
         // ---- 1. per-token scalars, computed by every wave for itself (lane = token)
-        float T = pre.d;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float v = __shfl_up(T, off);
-            if (lane >= off) T += v;
-        }
+        const float T = wave_prefix_sum(pre.d, lane);
         const float S2 = A2 * T;
-        const float S2e = __shfl(S2, nq - 1);
-        const float Te = __shfl(T, nq - 1);
+        const float S2e = lane_read(S2, nq - 1);
+        const float Te = lane_read(T, nq - 1);
         {
             const float gam = pre.l * pre.d, dln = (1.f - pre.ln) * pre.dn;
             wsc[lane] = S2;
@@ -673,12 +691,8 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                 const int nq = int(L - c0 < Q ? L - c0 : Q);
                 float T = 0.f;
                 if (lane < nq) T = dt[(b * L + c0 + lane) * H + h];
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float v = __shfl_up(T, off);
-                    if (lane >= off) T += v;
-                }
-                const float Te = __shfl(T, nq - 1);
+                T = wave_prefix_sum(T, lane);
+                const float Te = lane_read(T, nq - 1);
                 wsc[192 + lane] = __builtin_amdgcn_exp2f(A2 * T);
                 wsc[320 + lane] = T;
                 const ChunkBase cbc = chunk_base(c);
@@ -761,56 +775,63 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 // masking work of the previous one on every SIMD.
 namespace ws1 {
 
-constexpr int QRP = 64;      // rows per chunk (R = 1)
-constexpr int XS = QRP + 8;  // X^T row stride
-constexpr int NCW = 4;       // compute waves
+constexpr int QRP = 64;             // rows per chunk (R = 1)
+constexpr int XS = QRP + 8;         // X^T row stride
+constexpr int NCW = 4;              // compute waves
+constexpr int NSW = 8;              // staging waves
+constexpr int NST = 64 * NSW;       // staging threads
+constexpr int TSTEP = NST / 16;     // token step between a staging thread's rows
+constexpr int MT = QRP / TSTEP;     // B/C rows (8 columns each) per staging thread
+constexpr int NXT = 256;            // staging threads that move X (32 row pairs x 8 pieces)
 constexpr int TPW = 32 / NCW;
+static_assert(MT >= 1 && QRP % TSTEP == 0 && NST >= NXT, "staging split");
 
 struct StageRegs {
-    float d, l, dn, ln;
-    u32x4 b[4], c[4];  // token (stid >> 4) + 16 m, 8 columns at 8 (stid & 15)
-    u32x4 x0, x1;      // X rows 2 (stid >> 3), +1, 8 columns at 8 (stid & 7)
+    float d, l, dn, ln;  // lane = token; l, dn, ln only in the scalar wave
+    u32x4 b[MT], c[MT];  // token (stid >> 4) + TSTEP m, 8 columns at 8 (stid & 15)
+    u32x4 x0, x1;        // X rows 2 (stid >> 3), +1, 8 columns at 8 (stid & 7), stid < NXT
 };
 
 __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, const float* __restrict__ dt,
                                            const float* __restrict__ lam, int64_t tok0, int64_t L, int64_t c0, int H,
-                                           int G, int stid, int lane) {
+                                           int G, int stid, int lane, bool scal) {
     const int nq = cb.nq;
     {
         const int ic = lane < nq ? lane : nq - 1;
         const int64_t ti = (tok0 + ic) * H;
-        const float d = dt[ti], l = lam[ti];
-        const bool has_next = c0 + ic + 1 < L;
-        const float dn = dt[has_next ? ti + H : ti], ln = lam[has_next ? ti + H : ti];
+        const float d = dt[ti];
         r.d = lane < nq ? d : 0.f;
-        r.l = lane < nq ? l : 0.f;
-        r.dn = (lane < nq && has_next) ? dn : 0.f;
-        r.ln = (lane < nq && has_next) ? ln : 0.f;
+        if (scal) {
+            const float l = lam[ti];
+            const bool has_next = c0 + ic + 1 < L;
+            const float dn = dt[has_next ? ti + H : ti], ln = lam[has_next ? ti + H : ti];
+            r.l = lane < nq ? l : 0.f;
+            r.dn = (lane < nq && has_next) ? dn : 0.f;
+            r.ln = (lane < nq && has_next) ? ln : 0.f;
+        }
     }
     const int pc = stid & 15;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int i = (stid >> 4) + 16 * m;
+    for (int m = 0; m < MT; ++m) {
+        const int i = (stid >> 4) + TSTEP * m;
         r.b[m] = load_tok(cb.B, i, nq, G * N, 8 * pc);
         r.c[m] = load_tok(cb.C, i, nq, G * N, 8 * pc);
     }
-    const int rho0 = 2 * (stid >> 3);
-    r.x0 = load_tok(cb.x, rho0, nq, H * P, 8 * (stid & 7));
-    r.x1 = load_tok(cb.x, rho0 + 1, nq, H * P, 8 * (stid & 7));
+    if (stid < NXT) {
+        const int rho0 = 2 * (stid >> 3);
+        r.x0 = load_tok(cb.x, rho0, nq, H * P, 8 * (stid & 7));
+        r.x1 = load_tok(cb.x, rho0 + 1, nq, H * P, 8 * (stid & 7));
+    }
 }
 
-// rotate and write one chunk into LDS buffer `buf`; staging wave 0 also writes the scalars
+// rotate and write one chunk into one LDS buffer; the scalar wave also writes
+// the per-token scalars
 __device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2, const float* omB, uint16_t* sBt,
-                                            uint16_t* sCt, uint16_t* sXT, float* sSc, int stid, int lane) {
-    float T = r.d;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(T, off);
-        if (lane >= off) T += v;
-    }
-    if (stid < 64) {
+                                            uint16_t* sCt, uint16_t* sXT, float* sSc, int stid, int lane, bool scal) {
+    const float T = wave_prefix_sum(r.d, lane);
+    if (scal) {
         const float S2 = A2 * T;
-        const float S2e = __shfl(S2, nq - 1);
+        const float S2e = lane_read(S2, nq - 1);
         const float gam = r.l * r.d, dln = (1.f - r.ln) * r.dn;
         sSc[lane] = S2;
         sSc[64 + lane] = gam;
@@ -818,12 +839,20 @@ __device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2
         sSc[192 + lane] = __builtin_amdgcn_exp2f(S2);
         sSc[256 + lane] = __builtin_amdgcn_exp2f(S2e - S2) * (gam + dln);
         sSc[320 + lane] = T;
+        // weight of row token j against the last token of its 16-token tile
+        const float S2r = row_last(S2, lane);
+        sSc[384 + lane] = __builtin_amdgcn_exp2f(S2r - S2) * (gam + dln);
     }
     const int pc = stid & 15;
+    // a staging wave's lanes cover tokens tb + row + TSTEP m (row = lane / 16)
+    const int tb = __builtin_amdgcn_readfirstlane(stid >> 4) & ~3;
+    const int row = lane >> 4;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int i = (stid >> 4) + 16 * m;
-        const float Ti = __shfl(T, i);
+    for (int m = 0; m < MT; ++m) {
+        const int i = (stid >> 4) + TSTEP * m;
+        const float t0 = lane_read(T, tb + TSTEP * m), t1 = lane_read(T, tb + TSTEP * m + 1);
+        const float t2 = lane_read(T, tb + TSTEP * m + 2), t3 = lane_read(T, tb + TSTEP * m + 3);
+        const float Ti = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : t3;
         CS t[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) t[j] = cs_rev(omB[j], Ti);
@@ -833,19 +862,21 @@ __device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2
         *reinterpret_cast<u32x4*>(sCt + i * NS + 8 * pc) =
             u32x4{rot_pair(vc[0], t[0]), rot_pair(vc[1], t[1]), rot_pair(vc[2], t[2]), rot_pair(vc[3], t[3])};
     }
-    const int rho0 = 2 * (stid >> 3);
-    const int pcx = stid & 7;
+    if (stid < NXT) {
+        const int rho0 = 2 * (stid >> 3);
+        const int pcx = stid & 7;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int p = 8 * pcx + 2 * j;
-        *reinterpret_cast<unsigned*>(sXT + p * XS + rho0) = (r.x0[j] & 0xffffu) | (r.x1[j] << 16);
-        *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) = (r.x0[j] >> 16) | (r.x1[j] & 0xffff0000u);
+        for (int j = 0; j < 4; ++j) {
+            const int p = 8 * pcx + 2 * j;
+            *reinterpret_cast<unsigned*>(sXT + p * XS + rho0) = (r.x0[j] & 0xffffu) | (r.x1[j] << 16);
+            *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) = (r.x0[j] >> 16) | (r.x1[j] & 0xffff0000u);
+        }
     }
 }
 
 }  // namespace ws1
 
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(64 * (ws1::NCW + ws1::NSW))
 prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                      const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                      const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
@@ -857,7 +888,8 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NS];  // C~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];    // X^T [p][rho]
     __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];    // g^T [p][n], bf16
-    __shared__ float sSc[2][6 * 64];  // S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T
+    // per token: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T, tile weight
+    __shared__ float sSc[2][7 * 64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -885,29 +917,38 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     };
 
     if (wave >= NCW) {
-        // ===================== staging waves
+        // ===================== staging waves. Two register sets: chunk k lives in
+        // set k & 1, and its loads are issued two chunks ahead of its rotation.
         const int stid = tid - 64 * NCW;
+        const bool scal = wave == NCW + NSW - 1;  // the wave that also stages the per-token scalars
         float omB[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) omB[j] = omh[4 * (stid & 15) + j] * kInv2Pi;
-        StageRegs r;
-        {
-            const ChunkBase cb = chunk_base(0);
-            stage_load(r, cb, dt + h, lam + h, b * L, L, 0, H, G, stid, lane);
-            stage_write(r, cb.nq, A2, omB, sBt[0], sCt[0], sXT[0], sSc[0], stid, lane);
-        }
-        if (n_chunks > 1) stage_load(r, chunk_base(1), dt + h, lam + h, b * L + Q, L, Q, H, G, stid, lane);
+        StageRegs ra, rb;
+        auto load = [&](StageRegs& r, int64_t cc) {
+            stage_load(r, chunk_base(cc), dt + h, lam + h, b * L + cc * Q, L, cc * Q, H, G, stid, lane, scal);
+        };
+        auto write = [&](const StageRegs& r, int64_t cc) {
+            const int bn = int(cc & 1);
+            stage_write(r, chunk_base(cc).nq, A2, omB, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid, lane, scal);
+        };
+        load(ra, 0);
+        if (n_chunks > 1) load(rb, 1);
+        write(ra, 0);
+        if (n_chunks > 2) load(ra, 2);
         lds_barrier();
-#pragma unroll 1
-        for (int64_t c = 0; c < n_chunks; ++c) {
+        // during chunk c: write chunk c + 1, then issue the loads of chunk c + 3 into the freed set
+        auto step = [&](StageRegs& r, int64_t c) {
             if (c + 1 < n_chunks) {
-                const int bn = int((c + 1) & 1);
-                stage_write(r, chunk_base(c + 1).nq, A2, omB, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid, lane);
-                if (c + 2 < n_chunks)
-                    stage_load(r, chunk_base(c + 2), dt + h, lam + h, b * L + (c + 2) * Q, L, (c + 2) * Q, H, G, stid,
-                               lane);
+                write(r, c + 1);
+                if (c + 3 < n_chunks) load(r, c + 3);
             }
             lds_barrier();
+        };
+#pragma unroll 1
+        for (int64_t c = 0; c < n_chunks; c += 2) {
+            step(rb, c);
+            if (c + 1 < n_chunks) step(ra, c + 1);
         }
         return;
     }
@@ -968,6 +1009,24 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             }
             acc[q] *= sc[192 + ti];
         }
+        // M o scores for row tile jt. Below the diagonal tile (jt < s, every
+        // j < i) the decay splits at the tile's last token r = 16 jt + 15:
+        // e^{S_i-S_j} = e^{S_i-S_r} e^{S_r-S_j}, both factors <= 1, the second
+        // staged per token with the width-2 weight; one exp per lane and tile.
+        // The diagonal tile takes the full mask, plus D on i = j (the skip term
+        // D x_i rides along in the same contraction).
+        auto mask_tile = [&](const floatx4& t, int jt, float* m) {
+            if (jt < s) {
+                const float a = __builtin_amdgcn_exp2f(S2i - sc[16 * jt + 15]);
+                const floatx4 bw = *reinterpret_cast<const floatx4*>(sc + 384 + 16 * jt + 4 * g4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = t[e] * (bw[e] * a);
+            } else {
+                const int rj = 16 * jt + 4 * g4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = t[e] * mask_coef(rj + e, ti, S2i, sc) + (rj + e == ti ? Dh : 0.f);
+            }
+        };
         auto scores = [&](int jt, floatx4& t0, floatx4& t1) {
             t0 = floatx4{0.f, 0.f, 0.f, 0.f};
             t1 = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -991,13 +1050,9 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             floatx4 n0t, n1t;
             if (jt + 2 <= s) scores(jt + 2, n0t, n1t);
             const bool two = jt + 1 <= s;
-            const int rj0 = 16 * jt + 4 * g4, rj1 = rj0 + 16;
             float m0[4], m1[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                m0[e] = c0t[e] * mask_coef(rj0 + e, ti, S2i, sc);
-                m1[e] = c1t[e] * mask_coef(rj1 + e, ti, S2i, sc);
-            }
+            mask_tile(c0t, jt, m0);
+            if (two) mask_tile(c1t, jt + 1, m1);
             const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
             if (two) {
                 const u32x4 pb = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
@@ -1026,7 +1081,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
                 const int p = 16 * q + 4 * g4;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[q][e] + Dh * bf16_to_f32(XT[(p + e) * XS + ti]);
+                for (int e = 0; e < 4; ++e) v[e] = acc[q][e];
                 *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
             }
         }
@@ -1088,7 +1143,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 
 hipError_t launch_ws_r1(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
-    hipLaunchKernelGGL(prefill_ws_r1_kernel, dim3(unsigned(nbh)), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL(prefill_ws_r1_kernel, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
                        static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                        static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                        static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
