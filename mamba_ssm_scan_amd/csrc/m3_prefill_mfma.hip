@@ -51,6 +51,7 @@ constexpr int K = 64;      // rotation pairs
 constexpr int NS = N + 8;  // LDS row stride (bf16 elements) of B~, C~ and g^T
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInv2Pi = 0.15915494309189535f;
+constexpr double kInv2PiD = 0.15915494309189533577;
 
 __device__ __forceinline__ floatx4 mfma32(u32x4 a, u32x4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -826,8 +827,13 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
 
 // rotate and write one chunk into one LDS buffer; the scalar wave also writes
 // the per-token scalars
-__device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2, const float* omB, uint16_t* sBt,
-                                            uint16_t* sCt, uint16_t* sXT, float* sSc, int stid, int lane, bool scal) {
+// Returns the chunk's total step (sum of dt). base[j] = frac(omega_j T0 / 2 pi)
+// for the thread's four pairs, T0 the total step before the chunk: B and C are
+// turned by the absolute angle omega (T0 + T_i), so the carried state needs
+// no rotation of its own.
+__device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A2, const float* omB, const float* base,
+                                             uint16_t* sBt, uint16_t* sCt, uint16_t* sXT, float* sSc, int stid,
+                                             int lane, bool scal) {
     const float T = wave_prefix_sum(r.d, lane);
     if (scal) {
         const float S2 = A2 * T;
@@ -855,7 +861,10 @@ __device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2
         const float Ti = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : t3;
         CS t[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] = cs_rev(omB[j], Ti);
+        for (int j = 0; j < 4; ++j) {
+            const float rv = __builtin_amdgcn_fractf(base[j] + omB[j] * Ti);
+            t[j] = CS{__builtin_amdgcn_cosf(rv), __builtin_amdgcn_sinf(rv)};
+        }
         const u32x4 vb = r.b[m], vc = r.c[m];
         *reinterpret_cast<u32x4*>(sBt + i * NS + 8 * pc) =
             u32x4{rot_pair(vb[0], t[0]), rot_pair(vb[1], t[1]), rot_pair(vb[2], t[2]), rot_pair(vb[3], t[3])};
@@ -872,6 +881,7 @@ __device__ __forceinline__ void stage_write(const StageRegs& r, int nq, float A2
             *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) = (r.x0[j] >> 16) | (r.x1[j] & 0xffff0000u);
         }
     }
+    return lane_read(T, 63);  // tokens past the chunk's end carry dt = 0
 }
 
 }  // namespace ws1
@@ -922,15 +932,27 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         const int stid = tid - 64 * NCW;
         const bool scal = wave == NCW + NSW - 1;  // the wave that also stages the per-token scalars
         float omB[4];
+        double omD[4];  // omega / 2 pi of the thread's four pairs, for the chunk base angles
 #pragma unroll
-        for (int j = 0; j < 4; ++j) omB[j] = omh[4 * (stid & 15) + j] * kInv2Pi;
+        for (int j = 0; j < 4; ++j) {
+            omB[j] = omh[4 * (stid & 15) + j] * kInv2Pi;
+            omD[j] = double(omh[4 * (stid & 15) + j]) * kInv2PiD;
+        }
+        double Tacc = 0.0;  // total step before the chunk being written
         StageRegs ra, rb;
         auto load = [&](StageRegs& r, int64_t cc) {
             stage_load(r, chunk_base(cc), dt + h, lam + h, b * L + cc * Q, L, cc * Q, H, G, stid, lane, scal);
         };
         auto write = [&](const StageRegs& r, int64_t cc) {
             const int bn = int(cc & 1);
-            stage_write(r, chunk_base(cc).nq, A2, omB, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid, lane, scal);
+            float base[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double rv = omD[j] * Tacc;
+                base[j] = float(rv - floor(rv));
+            }
+            Tacc += stage_write(r, chunk_base(cc).nq, A2, omB, base, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid, lane,
+                                scal);
         };
         load(ra, 0);
         if (n_chunks > 1) load(rb, 1);
@@ -954,11 +976,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     }
 
     // ========================= compute waves: strip `wave`, state tiles 8 wave .. 8 wave + 7
-    float omS[2][2];
-#pragma unroll
-    for (int mr = 0; mr < 2; ++mr)
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omh[8 * (2 * wave + mr) + 2 * g4 + hp] * kInv2Pi;
+    double Tacc = 0.0;  // total step so far: the angle that turns the state back at the end
     floatx4 gst[TPW];
     {
         const int64_t t0 = (b * L) * H + h;
@@ -1086,10 +1104,10 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             }
         }
 
-        // state update
+        // state update (decay and the chunk's inputs; no rotation in the absolute frame)
         const int te = nq - 1;
         const float decE = sc[192 + te];
-        const float Te = sc[320 + te];
+        Tacc += sc[320 + te];
 #pragma unroll
         for (int m = 0; m < TPW; ++m) gst[m] *= decE;
 #pragma unroll
@@ -1111,18 +1129,10 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         }
 #pragma unroll
         for (int mr = 0; mr < 2; ++mr) {
-            const CS t0 = cs_rev(omS[mr][0], Te), t1 = cs_rev(omS[mr][1], Te);
             const int nt = 2 * wave + mr;
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const int m = mr * 4 + pt;
-                float a0 = gst[m][0], a1 = gst[m][1];
-                gst[m][0] = t0.c * a0 - t0.s * a1;
-                gst[m][1] = t0.s * a0 + t0.c * a1;
-                a0 = gst[m][2];
-                a1 = gst[m][3];
-                gst[m][2] = t1.c * a0 - t1.s * a1;
-                gst[m][3] = t1.s * a0 + t1.c * a1;
                 const int p = 16 * pt + l16;
                 *reinterpret_cast<u32x2*>(gTn + p * NS + 16 * nt + 4 * g4) =
                     u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
@@ -1131,12 +1141,30 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         lds_barrier();
     }
     if (h_out) {
+        // back from the absolute frame: pair k turned by omega_k times the total step
 #pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
-            const int p = 16 * pt + l16;
+        for (int mr = 0; mr < 2; ++mr) {
+            CS t[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = gst[m][e];
+            for (int hp = 0; hp < 2; ++hp) {
+                const double rv = double(omh[8 * (2 * wave + mr) + 2 * g4 + hp]) * kInv2PiD * Tacc;
+                const float r = float(rv - floor(rv));
+                t[hp] = CS{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
+            }
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int m = mr * 4 + pt, nt = 2 * wave + mr;
+                const int p = 16 * pt + l16;
+                float v[4];
+#pragma unroll
+                for (int hp = 0; hp < 2; ++hp) {
+                    const float a0 = gst[m][2 * hp], a1 = gst[m][2 * hp + 1];
+                    v[2 * hp] = t[hp].c * a0 - t[hp].s * a1;
+                    v[2 * hp + 1] = t[hp].s * a0 + t[hp].c * a1;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = v[e];
+            }
         }
     }
 }
