@@ -112,6 +112,20 @@ __device__ __forceinline__ float row_last(float v, int lane) {
     const int row = lane >> 4;
     return row == 0 ? r0 : row == 1 ? r1 : row == 2 ? r2 : r3;
 }
+// value of the last lane of each group of 16 / R lanes (lane = token: the last
+// token whose rows fall in the same 16-row tile)
+template <int LR>
+__device__ __forceinline__ float tile_last(float v, int lane) {
+    if constexpr (LR == 2) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false));
+    } else if constexpr (LR == 1) {
+        const int q = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false);  // lane 4k+3
+        const int u = __builtin_amdgcn_update_dpp(q, q, 0x104, 0xf, 0xf, false);  // row_shl:4 -> lane 8k+7
+        return __builtin_bit_cast(float, (lane & 4) ? q : u);
+    } else {
+        return row_last(v, lane);
+    }
+}
 
 template <int R_, int NW_>
 struct Shape {
@@ -276,7 +290,8 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     __shared__ __attribute__((aligned(16))) uint16_t sCt[S::C_LDS ? QRP * NS : 8];  // C~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sXT[P * XS];                   // X^T [p][rho]
     __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];                // g^T [p][n], bf16, 2 buffers
-    __shared__ float sW[NW][6 * 64];  // per wave: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T
+    // per wave, per token: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T, tile weight
+    __shared__ float sW[NW][7 * 64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -395,6 +410,8 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             wsc[192 + lane] = __builtin_amdgcn_exp2f(S2);
             wsc[256 + lane] = __builtin_amdgcn_exp2f(S2e - S2) * (gam + dln);
             wsc[320 + lane] = T;
+            // weight of row token j against the last token of its 16-row tile
+            wsc[384 + lane] = __builtin_amdgcn_exp2f(tile_last<LR>(S2, lane) - S2) * (gam + dln);
         }
 
         // ---- 2. stage B~ (and C~ when it lives in LDS) and X^T; one angle per (token, pair)
@@ -486,73 +503,97 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                 }
                 acc[q] *= wsc[192 + ti];
             }
-            // score tiles in pairs, the next pair's MFMAs issued before this pair is masked
-            auto scores = [&](int jt, floatx4& t0, floatx4& t1) {
+            // M o scores for row tile jt. Below the diagonal tile (jt < s: every
+            // row token precedes every column token) the decay splits at the
+            // tile's last token r: e^{S_i-S_j} = e^{S_i-S_r} e^{S_r-S_j}, both
+            // factors <= 1, the second staged per token with the width-2
+            // weight, so one exp per lane and tile. The diagonal tile takes the
+            // full mask, plus D on rho_j = rho_i (the skip term D x rides along
+            // in the same contraction).
+            const int rho_i = 16 * s + l16;
+            auto mask_tile = [&](const floatx4& t, int jt, float* m) {
+                const unsigned rj = 16u * jt + 4u * g4;
+                if (jt < s) {
+                    const float a = __builtin_amdgcn_exp2f(S2i - wsc[(16 * jt + 15) >> LR]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m[e] = t[e] * (wsc[384 + ((rj + e) >> LR)] * a);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        m[e] = t[e] * mask_coef(int((rj + e) >> LR), ti, S2i, wsc) + (int(rj + e) == rho_i ? Dh : 0.f);
+                }
+            };
+            // Score tiles go in pairs (jt, jt + 1): two 16x16 tiles make one K = 32
+            // operand of the y^T contraction. Software pipeline: the B~ operands
+            // of pair jt + 4 are loaded while pair jt is masked, and the MFMAs of
+            // pair jt + 2 are issued before it, so no LDS load is waited for
+            // right before the MFMA that needs it.
+            auto load_pair = [&](int jt, u32x4* a0, u32x4* a1) {
+                const int r0 = 16 * jt + l16;
+                const int r1 = r0 + 16 < QRP ? r0 + 16 : QRP - 1;  // a missing second tile reads a valid row
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    a0[ks] = *reinterpret_cast<const u32x4*>(sBt + r0 * NS + 32 * ks + 8 * g4);
+                    a1[ks] = *reinterpret_cast<const u32x4*>(sBt + r1 * NS + 32 * ks + 8 * g4);
+                }
+            };
+            auto score_pair = [&](const u32x4* a0, const u32x4* a1, bool two, floatx4& t0, floatx4& t1) {
                 t0 = floatx4{0.f, 0.f, 0.f, 0.f};
                 t1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(sBt + (16 * jt + l16) * NS + 32 * ks + 8 * g4);
-                    t0 = mfma32(a0, cr[ks], t0);
-                }
-                if (jt + 1 <= s) {
+                for (int ks = 0; ks < 4; ++ks) t0 = mfma32(a0[ks], cr[ks], t0);
+                if (two) {
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const u32x4 a1 =
-                            *reinterpret_cast<const u32x4*>(sBt + (16 * jt + 16 + l16) * NS + 32 * ks + 8 * g4);
-                        t1 = mfma32(a1, cr[ks], t1);
-                    }
+                    for (int ks = 0; ks < 4; ++ks) t1 = mfma32(a1[ks], cr[ks], t1);
                 }
             };
+            u32x4 pa0[4], pa1[4];
+            load_pair(0, pa0, pa1);
             floatx4 c0t, c1t;
-            scores(0, c0t, c1t);
+            score_pair(pa0, pa1, 1 <= s, c0t, c1t);
+            if (2 <= s) load_pair(2, pa0, pa1);
 #pragma unroll 1
             for (int jt = 0; jt <= s; jt += 2) {
-                floatx4 n0t, n1t;
-                if (jt + 2 <= s) scores(jt + 2, n0t, n1t);
                 const bool two = jt + 1 <= s;
-                const unsigned rj0 = 16u * jt + 4u * g4, rj1 = rj0 + 16u;
-                float m0[4], m1[4];
+                // X^T operands of this pair: columns 16 jt .. 16 jt + 31 (always inside the chunk)
+                u32x2 xa[S::PTW], xb[S::PTW];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    m0[e] = c0t[e] * mask_coef(int((rj0 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc);
-                    m1[e] = c1t[e] * mask_coef(int((rj1 >> LR) + (unsigned(e) >> LR)), ti, S2i, wsc);
+                for (int q = 0; q < S::PTW; ++q) {
+                    const uint16_t* xr = sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4;
+                    xa[q] = *reinterpret_cast<const u32x2*>(xr);
+                    xb[q] = *reinterpret_cast<const u32x2*>(xr + 16);
                 }
+                floatx4 n0t = c0t, n1t = c1t;
+                if (jt + 2 <= s) {
+                    score_pair(pa0, pa1, jt + 3 <= s, n0t, n1t);
+                    if (jt + 4 <= s) load_pair(jt + 4, pa0, pa1);
+                }
+                float m0[4], m1[4];
+                mask_tile(c0t, jt, m0);
+                if (two) mask_tile(c1t, jt + 1, m1);
                 const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
                 // y^T[p][rho_i] += sum_{rho_j} X^T[p][rho_j] (M o scores^T)[rho_j][rho_i]
                 if (two) {
                     const u32x4 pb = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
 #pragma unroll
-                    for (int q = 0; q < S::PTW; ++q) {
-                        const uint16_t* xr = sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4;
-                        const u32x2 xa = *reinterpret_cast<const u32x2*>(xr);
-                        const u32x2 xb = *reinterpret_cast<const u32x2*>(xr + 16);
-                        acc[q] = mfma32(u32x4{xa[0], xa[1], xb[0], xb[1]}, pb, acc[q]);
-                    }
+                    for (int q = 0; q < S::PTW; ++q) acc[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, acc[q]);
                 } else {
                     const u32x2 pb = {p00, p01};
 #pragma unroll
-                    for (int q = 0; q < S::PTW; ++q) {
-                        const u32x2 xa =
-                            *reinterpret_cast<const u32x2*>(sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4);
-                        acc[q] = mfma16(xa, pb, acc[q]);
-                    }
+                    for (int q = 0; q < S::PTW; ++q) acc[q] = mfma16(xa[q], pb, acc[q]);
                 }
                 c0t = n0t;
                 c1t = n1t;
             }
-            // epilogue: + D x, 4 consecutive p of row rho_i per lane
-            const unsigned rho = 16u * s + l16;
-            if (int(rho >> LR) < nq) {
-                const int i = int(rho >> LR), r = int(rho & (R - 1));
+            // epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
+            if ((rho_i >> LR) < nq) {
+                const int i = rho_i >> LR, r = rho_i & (R - 1);
                 uint16_t* yr = y + ((b * L + c * Q) * H + h) * int64_t(R * P) + (i * H * R + r) * P;
 #pragma unroll
                 for (int q = 0; q < S::PTW; ++q) {
                     const int p = 16 * (pt0 + q) + 4 * g4;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = acc[q][e] + Dh * bf16_to_f32(sXT[(p + e) * XS + rho]);
-                    *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+                    *reinterpret_cast<u32x2*>(yr + p) =
+                        u32x2{pack2(acc[q][0], acc[q][1]), pack2(acc[q][2], acc[q][3])};
                 }
             }
         }
