@@ -84,6 +84,18 @@ __device__ __forceinline__ unsigned rot_pair(unsigned w, CS t) {
     const float b0 = lo16(w), b1 = hi16(w);
     return pack2(t.c * b0 + t.s * b1, t.c * b1 - t.s * b0);
 }
+// Transposing LDS load (ds_read_b64_tr_b16): in each group of 16 lanes, lane t
+// gives the address of 4 consecutive 16-bit values of row t / 4 (columns
+// 4 (t % 4) ..); lane j receives column j of those 4 rows. From a row-major
+// [k][m] tile this yields the MFMA operand layout "lane = m, 4 consecutive k".
+typedef short shortx4_tr __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 load_tr(const uint16_t* p) {
+    const shortx4_tr v =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_tr*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+// a packed bf16 pair times (wl, wh), repacked
+__device__ __forceinline__ unsigned scale2(unsigned w, float wl, float wh) { return pack2(lo16(w) * wl, hi16(w) * wh); }
 // broadcast lane j of every DPP quad
 template <int J>
 __device__ __forceinline__ float quad_bcast(float v) {
@@ -606,23 +618,26 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         const float decE = wsc[192 + te];
 #pragma unroll
         for (int m = 0; m < TPW; ++m) gst[m] *= decE;
-#pragma unroll
-        for (int mr = 0; mr < TPW / 4; ++mr) {
-            const int nt = (wave * TPW) / 4 + mr;
-            const int n = 16 * nt + l16;
+        // A operand (w B~)^T: row n, k = 8 consecutive rho, read straight from the
+        // row-major B~ with transposing LDS loads and scaled by the state weight
 #pragma unroll 2
-            for (int ks = 0; ks < QRP / 32; ++ks) {
-                const unsigned rb = 32u * ks + 8u * g4;
-                float wv[8];
+        for (int ks = 0; ks < QRP / 32; ++ks) {
+            const unsigned rb = 32u * ks + 8u * g4;
+            u32x4 xb[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    wv[j] = bf16_to_f32(sBt[(rb + j) * NS + n]) * wsc[256 + ((rb >> LR) + (unsigned(j) >> LR))];
-                const u32x4 a = {pack2(wv[0], wv[1]), pack2(wv[2], wv[3]), pack2(wv[4], wv[5]), pack2(wv[6], wv[7])};
+            for (int pt = 0; pt < 4; ++pt) xb[pt] = *reinterpret_cast<const u32x4*>(sXT + (16 * pt + l16) * XS + rb);
+            float wr[8];
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const u32x4 xb = *reinterpret_cast<const u32x4*>(sXT + (16 * pt + l16) * XS + rb);
-                    gst[mr * 4 + pt] = mfma32(a, xb, gst[mr * 4 + pt]);
-                }
+            for (int j = 0; j < 8; ++j) wr[j] = wsc[256 + ((rb + j) >> LR)];
+#pragma unroll
+            for (int mr = 0; mr < TPW / 4; ++mr) {
+                const int n0 = 16 * ((wave * TPW) / 4 + mr);
+                const u32x2 lo = load_tr(sBt + (rb + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                const u32x2 hi = load_tr(sBt + (rb + 4 + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                const u32x4 a = {scale2(lo[0], wr[0], wr[1]), scale2(lo[1], wr[2], wr[3]), scale2(hi[0], wr[4], wr[5]),
+                                 scale2(hi[1], wr[6], wr[7])};
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) gst[mr * 4 + pt] = mfma32(a, xb[pt], gst[mr * 4 + pt]);
             }
         }
 #pragma unroll
