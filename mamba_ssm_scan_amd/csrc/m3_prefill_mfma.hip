@@ -1166,21 +1166,25 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         Tacc += sc[320 + te];
 #pragma unroll
         for (int m = 0; m < TPW; ++m) gst[m] *= decE;
+        // A operand (w B~)^T: row n, k = 8 consecutive rho, from the row-major B~
+        // through transposing LDS loads, scaled by the state weight
 #pragma unroll
-        for (int mr = 0; mr < 2; ++mr) {
-            const int n = 16 * (2 * wave + mr) + l16;
+        for (int ks = 0; ks < 2; ++ks) {
+            const int rb = 32 * ks + 8 * g4;
+            u32x4 xb[4];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int rb = 32 * ks + 8 * g4;
-                float wv[8];
+            for (int pt = 0; pt < 4; ++pt) xb[pt] = *reinterpret_cast<const u32x4*>(XT + (16 * pt + l16) * XS + rb);
+            const floatx4 w0 = *reinterpret_cast<const floatx4*>(sc + 256 + rb);
+            const floatx4 w1 = *reinterpret_cast<const floatx4*>(sc + 260 + rb);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) wv[j] = bf16_to_f32(Bt[(rb + j) * NS + n]) * sc[256 + rb + j];
-                const u32x4 a = {pack2(wv[0], wv[1]), pack2(wv[2], wv[3]), pack2(wv[4], wv[5]), pack2(wv[6], wv[7])};
+            for (int mr = 0; mr < 2; ++mr) {
+                const int n0 = 16 * (2 * wave + mr);
+                const u32x2 lo = load_tr(Bt + (rb + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                const u32x2 hi = load_tr(Bt + (rb + 4 + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                const u32x4 a = {scale2(lo[0], w0[0], w0[1]), scale2(lo[1], w0[2], w0[3]), scale2(hi[0], w1[0], w1[1]),
+                                 scale2(hi[1], w1[2], w1[3])};
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const u32x4 xb = *reinterpret_cast<const u32x4*>(XT + (16 * pt + l16) * XS + rb);
-                    gst[mr * 4 + pt] = mfma32(a, xb, gst[mr * 4 + pt]);
-                }
+                for (int pt = 0; pt < 4; ++pt) gst[mr * 4 + pt] = mfma32(a, xb[pt], gst[mr * 4 + pt]);
             }
         }
 #pragma unroll
