@@ -31,10 +31,10 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # KiB -> bytes; scale from a 1 GiB copy), valid only for the kernel source it was
 # taken on (sha256 prefix of the .hip file); see profiles/.
 MEASURED_TRAFFIC = {
-    "prefill1": ("m3_prefill_mfma.hip", "c7486c9004a9da9f", (2.0 * 39180.1875 + 73728.0) * 1024),
-    "prefill2": ("m3_prefill_mfma.hip", "c7486c9004a9da9f", (2.0 * 149737.104 + 270336.0) * 1024),
-    "decode1": ("m3_decode.hip", "8833d93bedd91eaa", (2.0 * 133587.904 + 264224.0) * 1024),
-    "decode4": ("m3_decode.hip", "8833d93bedd91eaa", (2.0 * 139419.047 + 270464.0) * 1024),
+    "prefill1": ("m3_prefill_mfma.hip", "314ab54843cacd90", (2.0 * 39133.521 + 73728.0) * 1024),
+    "prefill2": ("m3_prefill_mfma.hip", "314ab54843cacd90", (2.0 * 149738.479 + 270336.0) * 1024),
+    "decode1": ("m3_decode.hip", "f7647b4a124306a8", (2.0 * 133255.342 + 264224.0) * 1024),
+    "decode4": ("m3_decode.hip", "f7647b4a124306a8", (2.0 * 137275.731 + 270464.0) * 1024),
 }
 
 
