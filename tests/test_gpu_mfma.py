@@ -136,3 +136,18 @@ def test_workload4_prefill_then_decode():
     y = torch.cat([y1, y2], 1).index_select(2, idx)
     assert_close(y, y_ref, TOL["bf16"], "y (prefill + decode)")
     assert_close(st.h.index_select(1, idx), h_ref, TOL["bf16"], "final state")
+
+
+def test_mfma_long_siso_absolute_angle():
+    """R=1, 32768 tokens (512 chunks): B and C are turned by the absolute angle
+    omega * (total step), which reaches thousands of radians; the per-chunk base
+    angle must keep the rotation accurate to the end (y of late tokens, h_out)."""
+    _flush("long SISO sequence, 32768 tokens")
+    p = inputs.make_problem(batch=1, seqlen=32768, heads=2, groups=1, headdim=64, dstate=128, rank=1,
+                            io_dtype="bf16", dist="lm", wid=870, h0_std=0.1, with_carry=True)
+    assert _path(1, 32768, 2, 1, 1, 64) == binding.M3_PATH_MFMA
+    y_ref, h_ref = oracle.scan(p)
+    y, h = gpu_prefill(p, 64)
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(y[:, -2048:], y_ref[:, -2048:], TOL["bf16"], "y, last 2048 tokens")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
