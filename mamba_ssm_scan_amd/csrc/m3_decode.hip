@@ -13,6 +13,8 @@
 // bound). The current (B, x) is copied into the other carry slot for the next
 // step; slots alternate, so no workgroup overwrites a value another one of the
 // same launch still reads (B is shared by the H/G heads of a group).
+#include <type_traits>
+
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -158,6 +160,157 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
         for (int e = tid; e < R * N; e += NTH) carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = Bt[e];
 }
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 mfma_k16(u32x2 a, u32x2 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c,
+                                                     0, 0, 0);
+}
+// two floats -> packed bf16 (round to nearest even)
+__device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(unsigned, v);
+}
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// bf16 I/O, N = 128, P = 64, R in {2, 4}: the rank-R contractions on MFMA
+// (v_mfma_f32_16x16x16_bf16). One 256-thread workgroup per (b, h); wave w owns
+// state columns 16 w .. 16 w + 15 and all 128 rows. In row tile nt, lane
+// (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column 16 w + l16: two whole
+// rotation pairs, and exactly the accumulator layout of the MFMA, so
+//   U[n][p]  = sum_r B[r][n] x[r][p]      (A: B^T, rows n, k = r; B: x, k = r,
+//   Up[n][p] = the same for the previous token   cols p; k = R..15 are zero)
+// land in the lanes that own h[n][p], and
+//   y[r][p] += sum_n C[r][n] h'[n][p]      (A: C, rows r (zero past R), k = n;
+//                                           B: h', k = n, cols p)
+// takes the lane's 4 new state values as its B operand. h' goes in as two bf16
+// terms (hi + lo), which keeps y at fp32 accuracy; the products of bf16 inputs
+// in U and Up are exact. No cross-lane reduction is left.
+template <int R>
+__global__ void __launch_bounds__(256)
+decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
+                   int rd_slot, const bf16_t* __restrict__ x, const float* __restrict__ dt,
+                   const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
+                   const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
+                   bf16_t* __restrict__ y, int64_t nb, int H, int G) {
+    constexpr int N = 128, P = 64, K = 64, CS_ = N + 4;
+    __shared__ __attribute__((aligned(16))) uint16_t sBt[N][4];   // B^T: ranks contiguous, zero past R
+    __shared__ __attribute__((aligned(16))) uint16_t sBpt[N][4];  // B_prev^T
+    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][4];   // x^T
+    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][4];  // x_prev^T
+    __shared__ __attribute__((aligned(16))) uint16_t sC[R][CS_];  // C rows (padded: no bank conflicts)
+    __shared__ __attribute__((aligned(16))) float sCS[K][2];      // alpha * (cos, sin) of pair k
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const int64_t bg = b * G + h / (H / G);
+    float* hs = hstate + bh * (N * P);
+    const int p = 16 * w + l16;
+
+    float st[8][4];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[nt][e] = hs[(16 * nt + 4 * g4 + e) * P + p];
+
+    const uint16_t* Bt = reinterpret_cast<const uint16_t*>(B) + bg * (R * N);
+    const uint16_t* Ct = reinterpret_cast<const uint16_t*>(C) + bg * (R * N);
+    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + (int64_t(rd_slot) * nb * G + bg) * (R * N);
+    const uint16_t* xt = reinterpret_cast<const uint16_t*>(x) + bh * (R * P);
+    const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + (int64_t(rd_slot) * nb * H + bh) * (R * P);
+    for (int e = tid; e < 4 * (N / 2); e += 256) {  // rank r, pair of rows (2 j, 2 j + 1): one 32-bit load
+        const int r = e / (N / 2), j = e % (N / 2);
+        const unsigned vb = r < R ? reinterpret_cast<const unsigned*>(Bt + r * N)[j] : 0u;
+        const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(Bp + r * N)[j] : 0u;
+        sBt[2 * j][r] = uint16_t(vb);
+        sBt[2 * j + 1][r] = uint16_t(vb >> 16);
+        sBpt[2 * j][r] = uint16_t(vp);
+        sBpt[2 * j + 1][r] = uint16_t(vp >> 16);
+    }
+    for (int e = tid; e < 4 * (P / 2); e += 256) {  // rank r, pair of columns: one 32-bit load
+        const int r = e / (P / 2), j = e % (P / 2);
+        const unsigned vx = r < R ? reinterpret_cast<const unsigned*>(xt + r * P)[j] : 0u;
+        const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(xp + r * P)[j] : 0u;
+        sXt[2 * j][r] = uint16_t(vx);
+        sXt[2 * j + 1][r] = uint16_t(vx >> 16);
+        sXpt[2 * j][r] = uint16_t(vp);
+        sXpt[2 * j + 1][r] = uint16_t(vp >> 16);
+    }
+    for (int e = tid; e < R * (N / 2); e += 256)
+        reinterpret_cast<unsigned*>(&sC[e / (N / 2)][0])[e % (N / 2)] = reinterpret_cast<const unsigned*>(Ct)[e];
+    const float d = dt[bh], lm = lam[bh];
+    const float alpha = expf(d * A[h]);
+    const float gamma = lm * d, delta = (1.f - lm) * d;
+    if (tid < K) {
+        float sn, cs;
+        sincos_step(d * omega[int64_t(h) * K + tid], &sn, &cs);
+        sCS[tid][0] = alpha * cs;
+        sCS[tid][1] = alpha * sn;
+    }
+    __syncthreads();
+
+    const u32x2 zero = {0u, 0u};
+    const u32x2 xo = g4 == 0 ? *reinterpret_cast<const u32x2*>(&sXt[p][0]) : zero;
+    const u32x2 xpo = g4 == 0 ? *reinterpret_cast<const u32x2*>(&sXpt[p][0]) : zero;
+    const int rc = l16 < R ? l16 : 0;
+    floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int nt = 0; nt < 8; ++nt) {
+        const int n0 = 16 * nt;
+        const u32x2 ab = *reinterpret_cast<const u32x2*>(&sBt[n0 + l16][0]);
+        const u32x2 abp = *reinterpret_cast<const u32x2*>(&sBpt[n0 + l16][0]);
+        const floatx4 U = mfma_k16(g4 == 0 ? ab : zero, xo, floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 Up = mfma_k16(g4 == 0 ? abp : zero, xpo, floatx4{0.f, 0.f, 0.f, 0.f});
+        // pairs 8 nt + 2 g4 (rows e = 0, 1) and 8 nt + 2 g4 + 1 (rows e = 2, 3)
+        const floatx4 cs = *reinterpret_cast<const floatx4*>(&sCS[8 * nt + 2 * g4][0]);
+        float nv[4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            const float c = cs[2 * hp], sn = cs[2 * hp + 1];
+            const float g0 = st[nt][2 * hp] + delta * Up[2 * hp];
+            const float g1 = st[nt][2 * hp + 1] + delta * Up[2 * hp + 1];
+            nv[2 * hp] = (c * g0 - sn * g1) + gamma * U[2 * hp];
+            nv[2 * hp + 1] = (sn * g0 + c * g1) + gamma * U[2 * hp + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hs[(n0 + 4 * g4 + e) * P + p] = nv[e];
+        const unsigned h01 = pk_bf16(nv[0], nv[1]), h23 = pk_bf16(nv[2], nv[3]);
+        const u32x2 hi = {h01, h23};
+        const u32x2 lo = {pk_bf16(nv[0] - bf_lo(h01), nv[1] - bf_hi(h01)),
+                          pk_bf16(nv[2] - bf_lo(h23), nv[3] - bf_hi(h23))};
+        const u32x2 cv = *reinterpret_cast<const u32x2*>(&sC[rc][n0 + 4 * g4]);
+        const u32x2 ac = l16 < R ? cv : zero;
+        yacc = mfma_k16(ac, hi, yacc);
+        yacc = mfma_k16(ac, lo, yacc);
+    }
+    // yacc lane (g4 = 0) holds y[r = e][p]
+    if (g4 == 0) {
+        const float Dh = D[h];
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const float xv = __uint_as_float(unsigned(sXt[p][e]) << 16);
+            Io<bf16_t>::store(y, bh * (R * P) + e * P + p, yacc[e] + Dh * xv);
+        }
+    }
+
+    // this token becomes the carry of the next step
+    const int wr = rd_slot ^ 1;
+    for (int e = tid; e < R * P; e += 256) carry_x[(int64_t(wr) * nb * H + bh) * (R * P) + e] = x[bh * (R * P) + e];
+    if (h % (H / G) == 0)
+        for (int e = tid; e < R * N; e += 256)
+            carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = B[bg * (R * N) + e];
+}
+
 // Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
@@ -224,6 +377,14 @@ hipError_t launch_t(const DecodeArgs& a) {
     const T* B = static_cast<const T*>(a.B);
     const T* C = static_cast<const T*>(a.C);
     T* y = static_cast<T*>(a.y);
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if (a.N == 128 && a.P == 64 && (a.R == 2 || a.R == 4)) {
+            auto kern = a.R == 2 ? decode_mfma_kernel<2> : decode_mfma_kernel<4>;
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A, a.omega,
+                               a.lam, B, C, a.D, y, a.b, a.H, a.G);
+            return hipGetLastError();
+        }
+    }
     if (a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4)) {
         auto kern = a.R == 1 ? decode_n128_p64_kernel<T, 1, M3_DECODE_THREADS_R1>
                   : a.R == 2 ? decode_n128_p64_kernel<T, 2, M3_DECODE_THREADS_R4>

@@ -96,6 +96,8 @@ DCASES = [
     (1, 12, 2, 1, 64, 128, 4, "f32", True),
     (3, 10, 4, 1, 64, 128, 1, "bf16", True),
     (2, 10, 4, 2, 64, 128, 4, "bf16", False),
+    (2, 10, 3, 3, 64, 128, 2, "bf16", True),
+    (1, 8, 4, 1, 64, 128, 4, "bf16", True),
 ]
 
 
