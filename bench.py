@@ -33,8 +33,8 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 MEASURED_TRAFFIC = {
     "prefill1": ("m3_prefill_mfma.hip", "314ab54843cacd90", (2.0 * 39133.521 + 73728.0) * 1024),
     "prefill2": ("m3_prefill_mfma.hip", "314ab54843cacd90", (2.0 * 149738.479 + 270336.0) * 1024),
-    "decode1": ("m3_decode.hip", "f7647b4a124306a8", (2.0 * 133255.342 + 264224.0) * 1024),
-    "decode4": ("m3_decode.hip", "f7647b4a124306a8", (2.0 * 137275.731 + 270464.0) * 1024),
+    "decode1": ("m3_decode.hip", "e5b2228d93302ee1", (2.0 * 133248.607 + 264224.0) * 1024),
+    "decode4": ("m3_decode.hip", "e5b2228d93302ee1", (2.0 * 139018.869 + 270730.838) * 1024),
 }
 
 
