@@ -82,7 +82,8 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(wid, steps, warmup, log):
+def bench_prefill(wid, steps, warmup, log, special=""):
+    """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both."""
     import torch
     from mamba_ssm_scan_amd import binding, inputs
     w = inputs.WORKLOADS[wid]
@@ -95,10 +96,12 @@ def bench_prefill(wid, steps, warmup, log):
                         binding.M3_BF16)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
 
+    no_om, no_lam = "real" in special, "euler" in special
+
     def run(k):
         p = copies[k % N_COPIES]
-        binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], w.rank, w.chunk,
-                        y=y, h_out=h, workspace=ws)
+        binding.prefill(p["x"], p["dt"], p["A"], None if no_om else p["omega"], None if no_lam else p["lam"],
+                        p["B"], p["C"], p["D"], w.rank, w.chunk, y=y, h_out=h, workspace=ws)
 
     for k in range(warmup):
         run(k)
@@ -111,14 +114,17 @@ def bench_prefill(wid, steps, warmup, log):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     by = prefill_bytes(w.batch, w.seqlen, w.heads, 1, w.headdim, w.dstate, w.rank)
+    if no_lam:
+        by -= w.batch * w.seqlen * w.heads * 4
     fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
-    r = {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
+    name = w.name + (f" ({special})" if special else "")
+    r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
          "bytes": by, "flops": fl, "path": "mfma" if plan.path == binding.M3_PATH_MFMA else "generic",
          "segments": plan.segments}
     r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
     r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
-    log(f"prefill {w.name}: {ms * 1e3:.1f} us/call, {r['tokens_per_s'] / 1e6:.1f} M tok/s, "
+    log(f"prefill {name}: {ms * 1e3:.1f} us/call, {r['tokens_per_s'] / 1e6:.1f} M tok/s, "
         f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM), {r['mfma_tflops']:.1f} TFLOP/s "
         f"({100 * r['mfma_frac']:.1f}% bf16 MFMA)")
     return r
@@ -276,8 +282,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
-    ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy: run just "
-                                               "these (profiling runs); copy = a 1 GiB device copy for counter scaling")
+    ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy, "
+                                               "prefill1_real/_euler/_real_euler: run just these (profiling runs); "
+                                               "copy = a 1 GiB device copy for counter scaling")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -298,6 +305,8 @@ def main():
                 bench_prefill(1, args.steps, args.warmup, log)
             elif item == "prefill2":
                 bench_prefill(2, args.steps, args.warmup, log)
+            elif item.startswith("prefill1_"):
+                bench_prefill(1, args.steps, args.warmup, log, special=item[len("prefill1_"):])
             elif item in ("decode1", "decode4"):
                 bench_decode(int(item[-1]), 1024, 1, log)
             elif item == "long":
@@ -329,6 +338,9 @@ def main():
         out["prefill_mimo_r4"] = bench_prefill(2, args.steps, args.warmup, log)
         out["prefill_mimo_r4"]["traffic"] = measured_traffic("prefill2")
         out["long_prefill_decode"] = bench_long(log)
+        # the pages' special cases on the same workload: omega = 0 (no rotation), lambda = 1 (Euler)
+        out["prefill_special_cases"] = {sp: bench_prefill(1, args.steps, args.warmup, log, special=sp)
+                                        for sp in ("real", "euler", "real_euler")}
     if not args.no_cpu and not args.quick:
         out["cpu_baseline"] = cpu_baseline(log)
     print(json.dumps(out), flush=True)

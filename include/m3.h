@@ -92,7 +92,11 @@ enum { M3_PATH_GENERIC = 0, M3_PATH_MFMA = 1 };
  * cumulative decay times a width-2 convolution ("复值SSM × 广义梯形离散 × MIMO",
  * Fig. 2), evaluated chunk by chunk with the fp32 state passed between chunks.
  *
- * x, dt, A, omega, lambda, B, C, D: inputs as laid out above (required).
+ * x, dt, A, B, C, D: inputs as laid out above (required).
+ * omega:  rotation rates, or NULL for omega = 0: the real-valued state of the
+ *         pages' ablations (no RoPE on B and C; a faster path at R = 1).
+ * lambda: trapezoid weights, or NULL for lambda = 1: the Euler rule, which the
+ *         pages identify with Mamba-2 (no previous-input term).
  * R:      MIMO rank (>= 1).  chunk: tokens per chunk (1 .. 4096); any value gives
  *         the same result up to rounding; 64 is the tuned one.
  * h0:     initial state, or NULL for zero.
@@ -163,7 +167,8 @@ m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t
  *
  * x_t [b][H][R][P], B_t/C_t [b][G][R][N] (io dtype), dt_t/lambda_t [b][H] fp32,
  * A, D [H], omega [H][N/2]; y_t [b][H][R][P] io dtype (must not overlap the
- * inputs or the state). R must equal st->R. On success st->t is incremented.
+ * inputs or the state). omega and lambda_t may be NULL (omega = 0, lambda = 1,
+ * as for m3_prefill). R must equal st->R. On success st->t is incremented.
  * Steps on one state must be ordered on one stream.
  */
 m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t, const float* A,

@@ -89,7 +89,7 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
         (&sx[0][0])[e] = Io<T>::load(xt, e);
         (&sxp[0][0])[e] = Io<T>::load(xp, e);
     }
-    const float d = dt[bh], lm = lam[bh];
+    const float d = dt[bh], lm = lam_at(lam, bh);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
     __syncthreads();
@@ -104,7 +104,7 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
     for (int it = 0; it < IT; ++it) {
         const int k = kk + KS * it;
         float sn, cs;
-        sincos_step(d * omega[int64_t(h) * K + k], &sn, &cs);
+        sincos_step(d * om_at(omega, int64_t(h) * K + k), &sn, &cs);
         sn *= alpha;  // alpha folded into the rotation
         cs *= alpha;
         float e0[4] = {v0[it].x, v0[it].y, v0[it].z, v0[it].w};
@@ -248,12 +248,12 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     }
     for (int e = tid; e < R * (N / 2); e += 256)
         reinterpret_cast<unsigned*>(&sC[e / (N / 2)][0])[e % (N / 2)] = reinterpret_cast<const unsigned*>(Ct)[e];
-    const float d = dt[bh], lm = lam[bh];
+    const float d = dt[bh], lm = lam_at(lam, bh);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
     if (tid < K) {
         float sn, cs;
-        sincos_step(d * omega[int64_t(h) * K + tid], &sn, &cs);
+        sincos_step(d * om_at(omega, int64_t(h) * K + tid), &sn, &cs);
         sCS[tid][0] = alpha * cs;
         sCS[tid][1] = alpha * sn;
     }
@@ -332,7 +332,7 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
     const T* Bp = carry_B + (int64_t(rd_slot) * nb * G + bg) * int64_t(R) * N;
     const T* xt = x + bh * int64_t(R) * P;
     const T* xp = carry_x + (int64_t(rd_slot) * nb * H + bh) * int64_t(R) * P;
-    const float d = dt[bh], lm = lam[bh];
+    const float d = dt[bh], lm = lam_at(lam, bh);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
 
@@ -347,7 +347,7 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
             u1 += Io<T>::load(Bt, int64_t(r) * N + 2 * k + 1) * xv;
         }
         float sn, cs;
-        sincos_step(d * omega[int64_t(h) * K + k], &sn, &cs);
+        sincos_step(d * om_at(omega, int64_t(h) * K + k), &sn, &cs);
         const float g0 = hs[int64_t(2 * k) * P + p] + delta * up0;
         const float g1 = hs[int64_t(2 * k + 1) * P + p] + delta * up1;
         hs[int64_t(2 * k) * P + p] = alpha * (cs * g0 - sn * g1) + gamma * u0;

@@ -12,6 +12,12 @@ struct bf16_t {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// A NULL lambda array means lambda = 1 for every token (the Euler / Mamba-2
+// special case of the trapezoidal rule: no previous-input term); a NULL omega
+// array means omega = 0 (real-valued state, no rotation).
+__device__ __forceinline__ float lam_at(const float* lam, int64_t i) { return lam ? lam[i] : 1.f; }
+__device__ __forceinline__ float om_at(const float* om, int64_t i) { return om ? om[i] : 0.f; }
+
 // fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);

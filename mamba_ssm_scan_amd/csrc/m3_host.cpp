@@ -179,9 +179,9 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
     const bool heads = b > 0;
 
     struct Req { const char* name; const void* p; bool needed; };
-    const Req req[] = {{"x", x, tokens}, {"dt", dt, tokens}, {"lambda", lambda, tokens},
-                       {"B", B, tokens}, {"C", C, tokens}, {"y", y, tokens},
-                       {"A", A, heads}, {"omega", omega, heads}, {"D", D, heads}};
+    // omega and lambda may be NULL: omega = 0 (real-valued state) and lambda = 1 (Euler / Mamba-2)
+    const Req req[] = {{"x", x, tokens}, {"dt", dt, tokens}, {"B", B, tokens}, {"C", C, tokens},
+                       {"y", y, tokens}, {"A", A, heads}, {"D", D, heads}};
     for (const Req& r : req)
         if (r.needed && !r.p) return fail(M3_EINVAL, "%s is NULL", r.name);
     if ((carry_B == nullptr) != (carry_x == nullptr))
@@ -312,12 +312,17 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
     const m3_dims& d = st->dims;
     const int64_t b = d.batch;
     if (b == 0) { st->t += 1; return M3_OK; }
-    struct Req { const char* name; const void* p; };
-    const Req req[] = {{"x_t", x_t}, {"dt_t", dt_t}, {"A", A}, {"omega", omega}, {"lambda_t", lambda_t},
-                       {"B_t", B_t}, {"C_t", C_t}, {"D", D}, {"y_t", y_t}, {"state h", st->h},
-                       {"state carry_B", st->carry_B}, {"state carry_x", st->carry_x}};
+    struct Req { const char* name; const void* p; bool optional; };
+    // omega and lambda_t may be NULL: omega = 0 (real-valued state) and lambda = 1 (Euler / Mamba-2)
+    const Req req[] = {{"x_t", x_t, false}, {"dt_t", dt_t, false}, {"A", A, false}, {"omega", omega, true},
+                       {"lambda_t", lambda_t, true}, {"B_t", B_t, false}, {"C_t", C_t, false}, {"D", D, false},
+                       {"y_t", y_t, false}, {"state h", st->h, false}, {"state carry_B", st->carry_B, false},
+                       {"state carry_x", st->carry_x, false}};
     for (const Req& r : req) {
-        if (!r.p) return fail(M3_EINVAL, "%s is NULL", r.name);
+        if (!r.p) {
+            if (r.optional) continue;
+            return fail(M3_EINVAL, "%s is NULL", r.name);
+        }
         if (!aligned16(r.p)) return fail(M3_EALIGN, "%s is not 16-byte aligned", r.name);
     }
     const size_t es = io_size(st->io_dtype);

@@ -42,11 +42,11 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
     const int g = h / (H / G);
     const int K = N / 2;
     const float Ah = A[h], Dh = D[h];
-    const float* om = omega + int64_t(h) * K;
+    const float* om = omega ? omega + int64_t(h) * K : nullptr;
     float* st = state + bh * int64_t(N) * P;
 
     // g = h0 + delta_0 * carry_B^T carry_x
-    const float d0 = (1.f - lam[(b * L) * H + h]) * dt[(b * L) * H + h];
+    const float d0 = (1.f - lam_at(lam, (b * L) * H + h)) * dt[(b * L) * H + h];
     for (int e = tid; e < N * P; e += kThreads) {
         const int n = e / P, p = e % P;
         float v = h0 ? h0[bh * int64_t(N) * P + e] : 0.f;
@@ -70,9 +70,9 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
                 const float d = dt[ti];
                 acc += d;
                 Tc[i] = acc;
-                gam[i] = lam[ti] * d;
+                gam[i] = lam_at(lam, ti) * d;
                 const int64_t tn = c0 + i + 1;
-                dln[i] = tn < L ? (1.f - lam[(b * L + tn) * H + h]) * dt[(b * L + tn) * H + h] : 0.f;
+                dln[i] = tn < L ? (1.f - lam_at(lam, (b * L + tn) * H + h)) * dt[(b * L + tn) * H + h] : 0.f;
             }
         }
         __syncthreads();
@@ -85,7 +85,7 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
             float inter = 0.f;
             for (int k = 0; k < K; ++k) {
                 float s, c;
-                sincosf(om[k] * Ti, &s, &c);
+                sincosf(om_at(om, k) * Ti, &s, &c);
                 const float c0v = Io<T>::load(Ci, 2 * k), c1v = Io<T>::load(Ci, 2 * k + 1);
                 inter += (c * c0v + s * c1v) * st[(2 * k) * P + p] + (c * c1v - s * c0v) * st[(2 * k + 1) * P + p];
             }
@@ -99,7 +99,7 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
                     float sc = 0.f;
                     for (int k = 0; k < K; ++k) {
                         float s, c;
-                        sincosf(om[k] * dT, &s, &c);
+                        sincosf(om_at(om, k) * dT, &s, &c);
                         const float b0 = Io<T>::load(Bj, int64_t(rr) * N + 2 * k);
                         const float b1 = Io<T>::load(Bj, int64_t(rr) * N + 2 * k + 1);
                         const float c0v = Io<T>::load(Ci, 2 * k), c1v = Io<T>::load(Ci, 2 * k + 1);
@@ -122,7 +122,7 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
             for (int j = 0; j < nt; ++j) {
                 const float w = expf(Ah * (Te - Tc[j])) * (gam[j] + dln[j]);
                 float s, c;
-                sincosf(om[k] * Tc[j], &s, &c);
+                sincosf(om_at(om, k) * Tc[j], &s, &c);
                 const T* Bj = B + ((b * L + c0 + j) * G + g) * int64_t(R) * N;
                 const T* xj = x + ((b * L + c0 + j) * H + h) * int64_t(R) * P;
                 for (int r = 0; r < R; ++r) {
@@ -134,7 +134,7 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
                 }
             }
             float s, c;
-            sincosf(om[k] * Te, &s, &c);
+            sincosf(om_at(om, k) * Te, &s, &c);
             st[(2 * k) * P + p] = c * a0 - s * a1;
             st[(2 * k + 1) * P + p] = s * a0 + c * a1;
         }

@@ -207,9 +207,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb
     {
         const int ic = lane < nq ? lane : nq - 1;
         const int64_t ti = (tok0 + ic) * H;
-        const float d = dt[ti], l = lam[ti];
+        const float d = dt[ti], l = lam_at(lam, ti);
         const bool has_next = c0 + ic + 1 < L;
-        const float dn = dt[has_next ? ti + H : ti], ln = lam[has_next ? ti + H : ti];
+        const float dn = dt[has_next ? ti + H : ti], ln = lam_at(lam, has_next ? ti + H : ti);
         cr.d = lane < nq ? d : 0.f;
         cr.l = lane < nq ? l : 0.f;
         cr.dn = (lane < nq && has_next) ? dn : 0.f;
@@ -337,16 +337,16 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     float* wsc = sW[wave];
 
     // rotation rates (revolutions per unit step) of the pairs this thread turns
-    const float* omh = omega + int64_t(h) * K;
+    const float* omh = omega ? omega + int64_t(h) * K : nullptr;
     float omB[4], omC[4], omS[TPW / 4][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) omB[j] = omh[4 * (tid & 15) + j] * kInv2Pi;
+    for (int j = 0; j < 4; ++j) omB[j] = om_at(omh, 4 * (tid & 15) + j) * kInv2Pi;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) omC[ks] = omh[16 * ks + 4 * g4 + (l16 & 3)] * kInv2Pi;
+    for (int ks = 0; ks < 4; ++ks) omC[ks] = om_at(omh, 16 * ks + 4 * g4 + (l16 & 3)) * kInv2Pi;
 #pragma unroll
     for (int mr = 0; mr < TPW / 4; ++mr)
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omh[8 * ((wave * TPW) / 4 + mr) + 2 * g4 + hp] * kInv2Pi;
+        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = om_at(omh, 8 * ((wave * TPW) / 4 + mr) + 2 * g4 + hp) * kInv2Pi;
 
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
@@ -361,7 +361,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     CR pre;
     {
         const ChunkBase cb = chunk_base(c_begin);
-        load_chunk<S>(pre, cb, dt + h, lam + h, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
+        load_chunk<S>(pre, cb, dt + h, lam ? lam + h : nullptr, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
         if constexpr (!S::C_LDS) load_strip_c<S>(pre.cs, cb, strip_of<NW>(wave, 0) / S::PTG, G, lane);
     }
 
@@ -377,7 +377,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         }
     } else {
         const int64_t t0 = (b * L) * H + h;
-        const float dl0 = (1.f - lam[t0]) * dt[t0];
+        const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
@@ -469,7 +469,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         // ---- 3. prefetch the next chunk's scalars, B, C and X (in flight through the compute below)
         const bool more = c + 1 < c_end;
         const ChunkBase cbn = chunk_base(more ? c + 1 : c);
-        if (more) load_chunk<S>(pre, cbn, dt + h, lam + h, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
+        if (more) load_chunk<S>(pre, cbn, dt + h, lam ? lam + h : nullptr, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
         segT += double(Te);
         lds_barrier();
 
@@ -768,7 +768,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                         CS t[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            t[j] = cs_rev(omh[16 * ks + 4 * g4 + j] * kInv2Pi, Ti);
+                            t[j] = cs_rev(om_at(omh, 16 * ks + 4 * g4 + j) * kInv2Pi, Ti);
                         cr[ks] = u32x4{rot_pair(craw2[ks][0], t[0]), rot_pair(craw2[ks][1], t[1]),
                                        rot_pair(craw2[ks][2], t[2]), rot_pair(craw2[ks][3], t[3])};
                     }
@@ -859,9 +859,9 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
         const float d = dt[ti];
         r.d = lane < nq ? d : 0.f;
         if (scal) {
-            const float l = lam[ti];
+            const float l = lam_at(lam, ti);
             const bool has_next = c0 + ic + 1 < L;
-            const float dn = dt[has_next ? ti + H : ti], ln = lam[has_next ? ti + H : ti];
+            const float dn = dt[has_next ? ti + H : ti], ln = lam_at(lam, has_next ? ti + H : ti);
             r.l = lane < nq ? l : 0.f;
             r.dn = (lane < nq && has_next) ? dn : 0.f;
             r.ln = (lane < nq && has_next) ? ln : 0.f;
@@ -886,7 +886,8 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
 // Returns the chunk's total step (sum of dt). base[j] = frac(omega_j T0 / 2 pi)
 // for the thread's four pairs, T0 the total step before the chunk: B and C are
 // turned by the absolute angle omega (T0 + T_i), so the carried state needs
-// no rotation of its own.
+// no rotation of its own. ROT = false: omega = 0, B and C are staged as given.
+template <bool ROT>
 __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A2, const float* omB, const float* base,
                                              uint16_t* sBt, uint16_t* sCt, uint16_t* sXT, float* sSc, int stid,
                                              int lane, bool scal) {
@@ -912,6 +913,11 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int i = (stid >> 4) + TSTEP * m;
+        if constexpr (!ROT) {
+            *reinterpret_cast<u32x4*>(sBt + i * NS + 8 * pc) = r.b[m];
+            *reinterpret_cast<u32x4*>(sCt + i * NS + 8 * pc) = r.c[m];
+            continue;
+        }
         const float t0 = lane_read(T, tb + TSTEP * m), t1 = lane_read(T, tb + TSTEP * m + 1);
         const float t2 = lane_read(T, tb + TSTEP * m + 2), t3 = lane_read(T, tb + TSTEP * m + 3);
         const float Ti = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : t3;
@@ -942,6 +948,7 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
 
 }  // namespace ws1
 
+template <bool ROT>
 __global__ void __launch_bounds__(64 * (ws1::NCW + ws1::NSW))
 prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                      const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
@@ -971,7 +978,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
     const float Dh = Dv[h];
-    const float* omh = omega + int64_t(h) * K;
+    const float* omh = omega ? omega + int64_t(h) * K : nullptr;
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
@@ -991,13 +998,13 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         double omD[4];  // omega / 2 pi of the thread's four pairs, for the chunk base angles
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            omB[j] = omh[4 * (stid & 15) + j] * kInv2Pi;
-            omD[j] = double(omh[4 * (stid & 15) + j]) * kInv2PiD;
+            omB[j] = om_at(omh, 4 * (stid & 15) + j) * kInv2Pi;
+            omD[j] = double(om_at(omh, 4 * (stid & 15) + j)) * kInv2PiD;
         }
         double Tacc = 0.0;  // total step before the chunk being written
         StageRegs ra, rb;
         auto load = [&](StageRegs& r, int64_t cc) {
-            stage_load(r, chunk_base(cc), dt + h, lam + h, b * L + cc * Q, L, cc * Q, H, G, stid, lane, scal);
+            stage_load(r, chunk_base(cc), dt + h, lam ? lam + h : nullptr, b * L + cc * Q, L, cc * Q, H, G, stid, lane, scal);
         };
         auto write = [&](const StageRegs& r, int64_t cc) {
             const int bn = int(cc & 1);
@@ -1007,8 +1014,8 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
                 const double rv = omD[j] * Tacc;
                 base[j] = float(rv - floor(rv));
             }
-            Tacc += stage_write(r, chunk_base(cc).nq, A2, omB, base, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid, lane,
-                                scal);
+            Tacc += stage_write<ROT>(r, chunk_base(cc).nq, A2, omB, base, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid,
+                                     lane, scal);
         };
         load(ra, 0);
         if (n_chunks > 1) load(rb, 1);
@@ -1036,7 +1043,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     floatx4 gst[TPW];
     {
         const int64_t t0 = (b * L) * H + h;
-        const float dl0 = (1.f - lam[t0]) * dt[t0];
+        const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
@@ -1207,7 +1214,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             CS t[2];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-                const double rv = double(omh[8 * (2 * wave + mr) + 2 * g4 + hp]) * kInv2PiD * Tacc;
+                const double rv = double(om_at(omh, 8 * (2 * wave + mr) + 2 * g4 + hp)) * kInv2PiD * Tacc;
                 const float r = float(rv - floor(rv));
                 t[hp] = CS{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
             }
@@ -1231,7 +1238,8 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 
 hipError_t launch_ws_r1(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
-    hipLaunchKernelGGL(prefill_ws_r1_kernel, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
+    auto kern = a.omega ? prefill_ws_r1_kernel<true> : prefill_ws_r1_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
                        static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                        static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                        static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),

@@ -161,3 +161,19 @@ def test_plan_segments_for_few_heads(lib):
     assert p1.segments == 1 and p1.workspace_bytes == 0
     # the R=1 kernel walks whole sequences
     assert bd.plan(d, 1, 64, bd.M3_BF16).segments == 1
+
+
+def test_omega_lambda_may_be_null(lib):
+    # omega NULL (omega = 0) and lambda NULL (lambda = 1) pass validation: the
+    # prefill call gets as far as the workspace check, the decode step as far as
+    # the overlap check (both run before any HIP call)
+    st, msg = _call(lib, _dims(), omega=None, lam=None)
+    assert st == 7, msg
+    s = bd.M3DecodeState()
+    s.h, s.carry_B, s.carry_x, s.t = FAKE, FAKE + (1 << 30), FAKE + 2 * (1 << 30), 0
+    s.dims, s.R, s.io_dtype = _dims(), 1, 0
+    f = lambda i: ctypes.c_void_p(FAKE + i * (1 << 30))
+    y_in_x = ctypes.c_void_p(FAKE + 10 * (1 << 30) + 64)
+    assert lib.m3_decode_step(ctypes.byref(s), f(10), f(11), f(12), None, None, f(15), f(16), f(17), 1,
+                              y_in_x, None) == 1
+    assert "y_t overlaps" in lib.m3_last_error().decode()
