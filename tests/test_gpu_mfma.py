@@ -151,3 +151,31 @@ def test_mfma_long_siso_absolute_angle():
     assert_close(y, y_ref, TOL["bf16"], "y")
     assert_close(y[:, -2048:], y_ref[:, -2048:], TOL["bf16"], "y, last 2048 tokens")
     assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_workload3_decode_full_size(R):
+    """Workload 3 at full size, as bench.py runs it: b 128, H 64, 1024 decode steps,
+    bf16 I/O from an fp32 state h0 ~ N(0, 0.1); the oracle runs 3 x 3 sampled
+    (batch, head) walks over all 1024 tokens."""
+    w = inputs.WORKLOADS[3]
+    steps = 1024
+    _flush(f"workload 3 full size, R={R}")
+    di = inputs.decode_inputs(3, steps, device="cuda", rank=R)
+    st = binding.DecodeState(w.batch, w.heads, 1, w.headdim, w.dstate, R, io_dtype=torch.bfloat16, h0=di["h0"])
+    ys = [st.step(di["x"][t], di["dt"][t], di["A"], di["omega"], di["lam"][t], di["B"][t], di["C"][t], di["D"])
+          for t in range(steps)]
+    torch.cuda.synchronize()
+    bs, hs = [0, 77, 127], [0, 31, 63]
+    bi, hi = torch.tensor(bs, device="cuda"), torch.tensor(hs, device="cuda")
+    sel = lambda t: t.index_select(1, bi).transpose(0, 1)      # [steps][b]... -> [b'][steps]...
+    sub = {"x": sel(di["x"]).index_select(2, hi), "B": sel(di["B"]), "C": sel(di["C"]),
+           "dt": sel(di["dt"]).index_select(2, hi), "lam": sel(di["lam"]).index_select(2, hi),
+           "A": di["A"][hi], "omega": di["omega"][hi], "D": di["D"][hi],
+           "h0": di["h0"].index_select(0, bi).index_select(1, hi), "R": R, "io_dtype": "bf16",
+           "carry_B": None, "carry_x": None}
+    y_ref, h_ref = oracle.scan(to_host({k: (v.contiguous() if isinstance(v, torch.Tensor) else v)
+                                        for k, v in sub.items()}))
+    y = torch.stack(ys, 1).index_select(0, bi).index_select(2, hi)
+    assert_close(y, y_ref, TOL["bf16"], "y (1024 steps)")
+    assert_close(st.h.index_select(0, bi).index_select(1, hi), h_ref, TOL["bf16"], "state after 1024 steps")

@@ -404,3 +404,35 @@ def test_max_rel_err_metric():
     got = ref.copy()
     got[0, 1, 1, 0, 2] += 1e-5
     assert abs(oracle.max_rel_err(got, ref) - 1e-2) < 1e-12
+
+
+# ---------------------------------------------------------------- randomised shapes
+
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+
+@st.composite
+def _shapes(draw):
+    H = draw(st.integers(1, 3))
+    G = draw(st.sampled_from([g for g in (1, 2, 3) if H % g == 0]))
+    L = draw(st.integers(1, 70))
+    return dict(seed=draw(st.integers(0, 10_000)), b=draw(st.integers(1, 2)), L=L, H=H, G=G,
+                P=draw(st.integers(1, 8)), N=2 * draw(st.integers(1, 8)), R=draw(st.integers(1, 4)),
+                Q=draw(st.integers(1, L + 3)), h0=draw(st.booleans()), carry=draw(st.booleans()),
+                dist=draw(st.sampled_from(["tiny", "lm"])))
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(_shapes())
+def test_random_shapes_three_forms_agree(s):
+    """On drawn shapes (N even 2-16, P 1-8, R 1-4, L 1-70, chunk 1-L+3, groups,
+    initial state and carry on or off), the sequential oracle, the chunked form
+    and the complex-state form agree."""
+    p = inputs.make_problem(batch=s["b"], seqlen=s["L"], heads=s["H"], groups=s["G"], headdim=s["P"],
+                            dstate=s["N"], rank=s["R"], io_dtype="f32", dist=s["dist"], wid=5000 + s["seed"],
+                            h0_std=0.3 if s["h0"] else 0.0, with_carry=s["carry"])
+    y, hN = oracle.scan(p)
+    yc, hc = chunked(p, s["Q"])
+    assert _rel(yc, y) < 1e-10 and _rel(hc, hN) < 1e-10
+    yz, hz = complex_state(p)
+    assert _rel(yz, y) < 1e-10 and _rel(hz, hN) < 1e-10
