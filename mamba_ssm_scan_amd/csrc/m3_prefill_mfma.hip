@@ -298,12 +298,24 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     using CR = ChunkRegs<S>;
     constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW, LR = S::LR;
 
-    __shared__ __attribute__((aligned(16))) uint16_t sBt[QRP * NS];                 // B~ [rho][n]
-    __shared__ __attribute__((aligned(16))) uint16_t sCt[S::C_LDS ? QRP * NS : 8];  // C~ [rho][n]
-    __shared__ __attribute__((aligned(16))) uint16_t sXT[P * XS];                   // X^T [p][rho]
-    __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];                // g^T [p][n], bf16, 2 buffers
-    // per wave, per token: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T, tile weight
-    __shared__ float sW[NW][7 * 64];
+    // One LDS block, carved with the arrays addressed through per-lane indices
+    // plus constants first, so those constants fit the 16-bit offset field of
+    // the LDS instructions (a separate array past 64 KiB costs an address add
+    // per access):
+    //   sW   per wave, per token: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T, tile weight
+    //   sXT  X^T [p][rho]
+    //   sGT  g^T [p][n], bf16, 2 buffers
+    //   sBt  B~ [rho][n]
+    //   sCt  C~ [rho][n] (R <= 2)
+    constexpr int kW = NW * 7 * 64 * 4, kXT = P * XS * 2, kGT = 2 * P * NS * 2, kBT = QRP * NS * 2;
+    constexpr int kCT = S::C_LDS ? QRP * NS * 2 : 0;
+    static_assert(kW % 16 == 0 && kXT % 16 == 0 && kGT % 16 == 0 && kBT % 16 == 0, "LDS carve alignment");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kW + kXT + kGT + kBT + kCT];
+    auto* const sW = reinterpret_cast<float(*)[7 * 64]>(smem);
+    uint16_t* const sXT = reinterpret_cast<uint16_t*>(smem + kW);
+    auto* const sGT = reinterpret_cast<uint16_t(*)[P * NS]>(smem + kW + kXT);
+    uint16_t* const sBt = reinterpret_cast<uint16_t*>(smem + kW + kXT + kGT);
+    uint16_t* const sCt = reinterpret_cast<uint16_t*>(smem + kW + kXT + kGT + kBT);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -523,79 +535,115 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             // full mask, plus D on rho_j = rho_i (the skip term D x rides along
             // in the same contraction).
             const int rho_i = 16 * s + l16;
-            auto mask_tile = [&](const floatx4& t, int jt, float* m) {
+            auto read_below = [&](int jt, float& sr, float (&tw)[4]) {
                 const unsigned rj = 16u * jt + 4u * g4;
-                if (jt < s) {
-                    const float a = __builtin_amdgcn_exp2f(S2i - wsc[(16 * jt + 15) >> LR]);
+                sr = wsc[(16 * jt + 15) >> LR];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) m[e] = t[e] * (wsc[384 + ((rj + e) >> LR)] * a);
-                } else {
+                for (int e = 0; e < 4; ++e) tw[e] = wsc[384 + ((rj + e) >> LR)];
+            };
+            auto mask_below = [&](const floatx4& t, float sr, const float (&tw)[4], float* m) {
+                const float a = __builtin_amdgcn_exp2f(S2i - sr);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        m[e] = t[e] * mask_coef(int((rj + e) >> LR), ti, S2i, wsc) + (int(rj + e) == rho_i ? Dh : 0.f);
-                }
+                for (int e = 0; e < 4; ++e) m[e] = t[e] * (tw[e] * a);
+            };
+            auto mask_diag = [&](const floatx4& t, int jt, float* m) {
+                const unsigned rj = 16u * jt + 4u * g4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    m[e] = t[e] * mask_coef(int((rj + e) >> LR), ti, S2i, wsc) + (int(rj + e) == rho_i ? Dh : 0.f);
             };
             // Score tiles go in pairs (jt, jt + 1): two 16x16 tiles make one K = 32
-            // operand of the y^T contraction. Software pipeline: the B~ operands
-            // of pair jt + 4 are loaded while pair jt is masked, and the MFMAs of
-            // pair jt + 2 are issued before it, so no LDS load is waited for
-            // right before the MFMA that needs it.
+            // operand of the y^T contraction. Software pipeline: the MFMAs of pair
+            // jt + 2 are issued before pair jt is masked, and the B~ operands of
+            // pair jt + 4 are loaded meanwhile. The pairs wholly below the
+            // diagonal tile run a branch-free body that issues its LDS reads for
+            // the mask and X^T before that prefetch (LDS loads complete in order,
+            // so waiting for a later load would also wait for the prefetch); the
+            // pair holding the diagonal tile comes last. Operand rows past the
+            // chunk (the prefetch beyond the strip, the tile after an even
+            // diagonal tile) are clamped to valid rows; their products are never
+            // used or are masked to zero.
             auto load_pair = [&](int jt, u32x4* a0, u32x4* a1) {
-                const int r0 = 16 * jt + l16;
-                const int r1 = r0 + 16 < QRP ? r0 + 16 : QRP - 1;  // a missing second tile reads a valid row
+                const int r0 = 16 * jt + l16 < QRP ? 16 * jt + l16 : QRP - 1;
+                const int r1 = r0 + 16 < QRP ? r0 + 16 : QRP - 1;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     a0[ks] = *reinterpret_cast<const u32x4*>(sBt + r0 * NS + 32 * ks + 8 * g4);
                     a1[ks] = *reinterpret_cast<const u32x4*>(sBt + r1 * NS + 32 * ks + 8 * g4);
                 }
             };
-            auto score_pair = [&](const u32x4* a0, const u32x4* a1, bool two, floatx4& t0, floatx4& t1) {
+            auto score_pair = [&](const u32x4* a0, const u32x4* a1, floatx4& t0, floatx4& t1) {
                 t0 = floatx4{0.f, 0.f, 0.f, 0.f};
                 t1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) t0 = mfma32(a0[ks], cr[ks], t0);
-                if (two) {
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) t1 = mfma32(a1[ks], cr[ks], t1);
+                for (int ks = 0; ks < 4; ++ks) {
+                    t0 = mfma32(a0[ks], cr[ks], t0);
+                    t1 = mfma32(a1[ks], cr[ks], t1);
                 }
             };
-            u32x4 pa0[4], pa1[4];
-            load_pair(0, pa0, pa1);
-            floatx4 c0t, c1t;
-            score_pair(pa0, pa1, 1 <= s, c0t, c1t);
-            if (2 <= s) load_pair(2, pa0, pa1);
-#pragma unroll 1
-            for (int jt = 0; jt <= s; jt += 2) {
-                const bool two = jt + 1 <= s;
-                // X^T operands of this pair: columns 16 jt .. 16 jt + 31 (always inside the chunk)
-                u32x2 xa[S::PTW], xb[S::PTW];
+            // X^T operands of pair jt: columns 16 jt .. 16 jt + 31 (always inside the chunk)
+            auto load_x = [&](int jt, u32x2* xa, u32x2* xb) {
 #pragma unroll
                 for (int q = 0; q < S::PTW; ++q) {
                     const uint16_t* xr = sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4;
                     xa[q] = *reinterpret_cast<const u32x2*>(xr);
                     xb[q] = *reinterpret_cast<const u32x2*>(xr + 16);
                 }
-                floatx4 n0t = c0t, n1t = c1t;
-                if (jt + 2 <= s) {
-                    score_pair(pa0, pa1, jt + 3 <= s, n0t, n1t);
-                    if (jt + 4 <= s) load_pair(jt + 4, pa0, pa1);
-                }
+            };
+            // y^T[p][rho_i] += sum_{rho_j} X^T[p][rho_j] (M o scores^T)[rho_j][rho_i]
+            auto y_pair = [&](const u32x2* xa, const u32x2* xb, const float* m0, const float* m1) {
+                const u32x4 pb = {pack2(m0[0], m0[1]), pack2(m0[2], m0[3]), pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
+#pragma unroll
+                for (int q = 0; q < S::PTW; ++q)
+                    acc[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, acc[q]);
+            };
+            u32x4 pa0[4], pa1[4];
+            load_pair(0, pa0, pa1);
+            floatx4 c0t, c1t;
+            score_pair(pa0, pa1, c0t, c1t);
+            if (2 <= s) load_pair(2, pa0, pa1);
+            int jt = 0;
+#pragma unroll 1
+            for (; jt + 1 < s; jt += 2) {
+                // The phases are fenced off from the scheduler so the loads keep
+                // this order: mask scalars, X^T, prefetch. The memory clobber
+                // after the prefetch also keeps the compiler from folding the
+                // loop-carried operands into loads at their use in the next
+                // iteration, which would undo the pipeline.
+                float sr0, sr1, tw0[4], tw1[4];
+                read_below(jt, sr0, tw0);
+                read_below(jt + 1, sr1, tw1);
+                __builtin_amdgcn_sched_barrier(0);
+                u32x2 xa[S::PTW], xb[S::PTW];
+                load_x(jt, xa, xb);
+                floatx4 n0t, n1t;
+                score_pair(pa0, pa1, n0t, n1t);  // pair jt + 2 <= s
+                __builtin_amdgcn_sched_barrier(0);
+                load_pair(jt + 4, pa0, pa1);
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
                 float m0[4], m1[4];
-                mask_tile(c0t, jt, m0);
-                if (two) mask_tile(c1t, jt + 1, m1);
-                const unsigned p00 = pack2(m0[0], m0[1]), p01 = pack2(m0[2], m0[3]);
-                // y^T[p][rho_i] += sum_{rho_j} X^T[p][rho_j] (M o scores^T)[rho_j][rho_i]
-                if (two) {
-                    const u32x4 pb = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
-#pragma unroll
-                    for (int q = 0; q < S::PTW; ++q) acc[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, acc[q]);
-                } else {
-                    const u32x2 pb = {p00, p01};
-#pragma unroll
-                    for (int q = 0; q < S::PTW; ++q) acc[q] = mfma16(xa[q], pb, acc[q]);
-                }
+                mask_below(c0t, sr0, tw0, m0);
+                mask_below(c1t, sr1, tw1, m1);
+                y_pair(xa, xb, m0, m1);
                 c0t = n0t;
                 c1t = n1t;
+            }
+            {  // the pair holding the diagonal tile: jt = s & ~1
+                u32x2 xa[S::PTW], xb[S::PTW];
+                load_x(jt, xa, xb);
+                float m0[4], m1[4];
+                if (s & 1) {
+                    float sr0, tw0[4];
+                    read_below(jt, sr0, tw0);
+                    mask_below(c0t, sr0, tw0, m0);
+                    mask_diag(c1t, jt + 1, m1);
+                } else {
+                    mask_diag(c0t, jt, m0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m1[e] = 0.f;
+                }
+                y_pair(xa, xb, m0, m1);
             }
             // epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
             if ((rho_i >> LR) < nq) {
