@@ -487,6 +487,15 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 
         // ---- 4. outputs: work item = (16-row strip, group of PTW p tiles), y^T accumulated
         //         (an accumulator lane holds y[rho_i][p..p+3] of one row: 8-byte stores)
+        // The g^T operands of the inter-chunk part are the same for all of a
+        // wave's strips (its p tiles do not change): loaded once per chunk.
+        static_assert(S::PTG == 1, "one p-tile group per wave");
+        u32x4 gop[S::PTW][4];
+#pragma unroll
+        for (int q = 0; q < S::PTW; ++q)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                gop[q][ks] = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
 #pragma unroll 1
         for (int si = 0; si < SPW; ++si) {
             const int item = strip_of<NW>(wave, si);
@@ -515,18 +524,16 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             const int ti = int((16u * s + l16) >> LR);  // token of this lane's column rho_i
             const float S2i = wsc[ti];
             // inter-chunk part: y^T[p][rho_i] = e^{S_i} sum_n g^T[p][n] C~[rho_i][n]
+            // (the p tiles' accumulation chains interleaved)
             floatx4 acc[S::PTW];
 #pragma unroll
-            for (int q = 0; q < S::PTW; ++q) {
-                acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < S::PTW; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const u32x4 ga =
-                        *reinterpret_cast<const u32x4*>(gT + (16 * (pt0 + q) + l16) * NS + 32 * ks + 8 * g4);
-                    acc[q] = mfma32(ga, cr[ks], acc[q]);
-                }
-                acc[q] *= wsc[192 + ti];
-            }
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int q = 0; q < S::PTW; ++q) acc[q] = mfma32(gop[q][ks], cr[ks], acc[q]);
+#pragma unroll
+            for (int q = 0; q < S::PTW; ++q) acc[q] *= wsc[192 + ti];
             // M o scores for row tile jt. Below the diagonal tile (jt < s: every
             // row token precedes every column token) the decay splits at the
             // tile's last token r: e^{S_i-S_j} = e^{S_i-S_r} e^{S_r-S_j}, both
@@ -892,7 +899,8 @@ constexpr int TPW = 32 / NCW;
 static_assert(MT >= 1 && QRP % TSTEP == 0 && NST >= NXT, "staging split");
 
 struct StageRegs {
-    float d, l, dn, ln;  // lane = token; l, dn, ln only in the scalar wave
+    float d, l, dn, ln;  // lane = token, as loaded; l, dn, ln only in the scalar wave
+    unsigned ok;         // bit 0: token inside the chunk, bit 1: and a next token exists
     u32x4 b[MT], c[MT];  // token (stid >> 4) + TSTEP m, 8 columns at 8 (stid & 15)
     u32x4 x0, x1;        // X rows 2 (stid >> 3), +1, 8 columns at 8 (stid & 7), stid < NXT
 };
@@ -904,15 +912,18 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
     {
         const int ic = lane < nq ? lane : nq - 1;
         const int64_t ti = (tok0 + ic) * H;
-        const float d = dt[ti];
-        r.d = lane < nq ? d : 0.f;
+        // Kept as loaded: masking them here would wait for these loads, and
+        // with them for the other register set's (the counter is in order).
+        // Without lambda (lambda = 1) dt stands in as a valid address and the
+        // value is replaced at use.
+        r.d = dt[ti];
+        const bool has_next = c0 + ic + 1 < L;
+        r.ok = (lane < nq ? 1u : 0u) | ((lane < nq && has_next) ? 2u : 0u) | (lam ? 4u : 0u);
         if (scal) {
-            const float l = lam_at(lam, ti);
-            const bool has_next = c0 + ic + 1 < L;
-            const float dn = dt[has_next ? ti + H : ti], ln = lam_at(lam, has_next ? ti + H : ti);
-            r.l = lane < nq ? l : 0.f;
-            r.dn = (lane < nq && has_next) ? dn : 0.f;
-            r.ln = (lane < nq && has_next) ? ln : 0.f;
+            const float* lp = lam ? lam : dt;
+            r.l = lp[ti];
+            r.dn = dt[has_next ? ti + H : ti];
+            r.ln = lp[has_next ? ti + H : ti];
         }
     }
     const int pc = stid & 15;
@@ -939,11 +950,15 @@ template <bool ROT>
 __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A2, const float* omB, const float* base,
                                              uint16_t* sBt, uint16_t* sCt, uint16_t* sXT, float* sSc, int stid,
                                              int lane, bool scal) {
-    const float T = wave_prefix_sum(r.d, lane);
+    const float rd = (r.ok & 1u) ? r.d : 0.f;
+    const float T = wave_prefix_sum(rd, lane);
     if (scal) {
         const float S2 = A2 * T;
         const float S2e = lane_read(S2, nq - 1);
-        const float gam = r.l * r.d, dln = (1.f - r.ln) * r.dn;
+        const float rdn = (r.ok & 2u) ? r.dn : 0.f;
+        const float rl = (r.ok & 1u) ? ((r.ok & 4u) ? r.l : 1.f) : 0.f;
+        const float rln = (r.ok & 2u) ? ((r.ok & 4u) ? r.ln : 1.f) : 0.f;
+        const float gam = rl * rd, dln = (1.f - rln) * rdn;
         sSc[lane] = S2;
         sSc[64 + lane] = gam;
         sSc[128 + lane] = dln;
