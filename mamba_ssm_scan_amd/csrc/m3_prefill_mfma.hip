@@ -895,8 +895,8 @@ constexpr int NST = 64 * NSW;       // staging threads
 constexpr int TSTEP = NST / 16;     // token step between a staging thread's rows
 constexpr int MT = QRP / TSTEP;     // B/C rows (8 columns each) per staging thread
 constexpr int NXT = 256;            // staging threads that move X (32 row pairs x 8 pieces)
-constexpr int TPW = 32 / NCW;
-static_assert(MT >= 1 && QRP % TSTEP == 0 && NST >= NXT, "staging split");
+constexpr int MRW = 3;  // most state row tiles (of 16 rows) a compute wave holds (split 3, 3, 1, 1)
+static_assert(MT >= 1 && QRP % TSTEP == 0 && NST >= NXT && NCW == 4, "staging split");
 
 struct StageRegs {
     float d, l, dn, ln;  // lane = token, as loaded; l, dn, ln only in the scalar wave
@@ -1101,15 +1101,22 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         return;
     }
 
-    // ========================= compute waves: strip `wave`, state tiles 8 wave .. 8 wave + 7
+    // ========================= compute waves: output strip `wave`; state row tiles
+    // nt0 .. nt0 + ntc - 1 (all 4 column tiles each). The strips' score work
+    // grows with the strip index, so the state rows are dealt unevenly
+    // (3, 3, 1, 1 row tiles) to even out the waves' time per chunk.
+    const int nt0 = wave == 0 ? 0 : wave == 1 ? 3 : wave == 2 ? 6 : 7;
+    const int ntc = wave < 2 ? 3 : 1;
     double Tacc = 0.0;  // total step so far: the angle that turns the state back at the end
-    floatx4 gst[TPW];
+    floatx4 gst[MRW * 4];
     {
         const int64_t t0 = (b * L) * H + h;
         const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
 #pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-            const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
+        for (int m = 0; m < MRW * 4; ++m) {
+            gst[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if ((m >> 2) >= ntc) continue;
+            const int nt = nt0 + (m >> 2), pt = m & 3;
             const int p = 16 * pt + l16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1142,17 +1149,18 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) cr[ks] = *reinterpret_cast<const u32x4*>(Ct + ti * NS + 32 * ks + 8 * g4);
         const float S2i = sc[ti];
-        floatx4 acc[4];
+        floatx4 acc[4];  // the p tiles' accumulation chains interleaved
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
                 const u32x4 ga = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
                 acc[q] = mfma32(ga, cr[ks], acc[q]);
             }
-            acc[q] *= sc[192 + ti];
-        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] *= sc[192 + ti];
         // M o scores for row tile jt. Below the diagonal tile (jt < s, every
         // j < i) the decay splits at the tile's last token r = 16 jt + 15:
         // e^{S_i-S_j} = e^{S_i-S_r} e^{S_r-S_j}, both factors <= 1, the second
@@ -1235,7 +1243,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         const float decE = sc[192 + te];
         Tacc += sc[320 + te];
 #pragma unroll
-        for (int m = 0; m < TPW; ++m) gst[m] *= decE;
+        for (int m = 0; m < MRW * 4; ++m) gst[m] *= decE;
         // A operand (w B~)^T: row n, k = 8 consecutive rho, from the row-major B~
         // through transposing LDS loads, scaled by the state weight
 #pragma unroll
@@ -1247,8 +1255,9 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             const floatx4 w0 = *reinterpret_cast<const floatx4*>(sc + 256 + rb);
             const floatx4 w1 = *reinterpret_cast<const floatx4*>(sc + 260 + rb);
 #pragma unroll
-            for (int mr = 0; mr < 2; ++mr) {
-                const int n0 = 16 * (2 * wave + mr);
+            for (int mr = 0; mr < MRW; ++mr) {
+                if (mr >= ntc) continue;
+                const int n0 = 16 * (nt0 + mr);
                 const u32x2 lo = load_tr(Bt + (rb + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
                 const u32x2 hi = load_tr(Bt + (rb + 4 + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
                 const u32x4 a = {scale2(lo[0], w0[0], w0[1]), scale2(lo[1], w0[2], w0[3]), scale2(hi[0], w1[0], w1[1]),
@@ -1258,8 +1267,9 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             }
         }
 #pragma unroll
-        for (int mr = 0; mr < 2; ++mr) {
-            const int nt = 2 * wave + mr;
+        for (int mr = 0; mr < MRW; ++mr) {
+            if (mr >= ntc) continue;
+            const int nt = nt0 + mr;
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const int m = mr * 4 + pt;
@@ -1273,17 +1283,18 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     if (h_out) {
         // back from the absolute frame: pair k turned by omega_k times the total step
 #pragma unroll
-        for (int mr = 0; mr < 2; ++mr) {
+        for (int mr = 0; mr < MRW; ++mr) {
+            if (mr >= ntc) continue;
             CS t[2];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-                const double rv = double(om_at(omh, 8 * (2 * wave + mr) + 2 * g4 + hp)) * kInv2PiD * Tacc;
+                const double rv = double(om_at(omh, 8 * (nt0 + mr) + 2 * g4 + hp)) * kInv2PiD * Tacc;
                 const float r = float(rv - floor(rv));
                 t[hp] = CS{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
             }
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const int m = mr * 4 + pt, nt = 2 * wave + mr;
+                const int m = mr * 4 + pt, nt = nt0 + mr;
                 const int p = 16 * pt + l16;
                 float v[4];
 #pragma unroll
