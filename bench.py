@@ -31,10 +31,10 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # KiB -> bytes; scale from a 1 GiB copy), valid only for the kernel source it was
 # taken on (sha256 prefix of the .hip file); see profiles/.
 MEASURED_TRAFFIC = {
-    "prefill1": ("m3_prefill_mfma.hip", "314ab54843cacd90", (2.0 * 39133.521 + 73728.0) * 1024),
-    "prefill2": ("m3_prefill_mfma.hip", "314ab54843cacd90", (2.0 * 149738.479 + 270336.0) * 1024),
-    "decode1": ("m3_decode.hip", "e5b2228d93302ee1", (2.0 * 133248.607 + 264224.0) * 1024),
-    "decode4": ("m3_decode.hip", "e5b2228d93302ee1", (2.0 * 139018.869 + 270730.838) * 1024),
+    "prefill1": ("m3_prefill_mfma.hip", "041ae6b23ea550bf", (2.0 * 39168.208 + 73728.0) * 1024),
+    "prefill2": ("m3_prefill_mfma.hip", "041ae6b23ea550bf", (2.0 * 149743.292 + 270336.0) * 1024),
+    "decode1": ("m3_decode.hip", "862eb63ba701956b", (2.0 * 133303.754 + 264224.0) * 1024),
+    "decode4": ("m3_decode.hip", "862eb63ba701956b", (2.0 * 139045.784 + 270763.285) * 1024),
 }
 
 
