@@ -3,8 +3,9 @@
 Only the tests, the smoke check and the bench's CPU-baseline leg may import
 this package. It wraps `m3_oracle.c` (plain C, double precision, OpenMP over
 (batch, head)) through ctypes; see that file for the recurrence it runs and
-the passages of the pages it follows. Nothing here is shared with the HIP
-library.
+the passages of the pages it follows. The input prologue (QK-norm and bias on
+B and C, softplus / sigmoid on the step and the trapezoid weight) is the numpy
+module `prologue.py`. Nothing here is shared with the HIP library.
 """
 from __future__ import annotations
 
@@ -13,6 +14,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from .prologue import prologue, qk_norm, rms_rows, sigmoid, softplus  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "m3_oracle.c")
