@@ -215,13 +215,90 @@ def bench_long(log):
     e1.record()
     torch.cuda.synchronize()
     dms = e0.elapsed_time(e1) / steps
+    # the same 256 steps captured in one HIP graph: at batch 1 a step is a few
+    # microseconds of GPU work and the launches from Python dominate; replaying
+    # the captured loop (it continues from the state the eager loop left, which
+    # changes nothing in the work) times the GPU side
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        shg = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for k in range(steps):
+            st.step_raw(xs[k].data_ptr(), ds[k].data_ptr(), p["A"].data_ptr(), p["omega"].data_ptr(),
+                        ls[k].data_ptr(), Bs[k].data_ptr(), Cs[k].data_ptr(), p["D"].data_ptr(), ys[k].data_ptr(),
+                        shg)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gms = e0.elapsed_time(e1) / steps
     r = {"workload": w.name, "prefill_ms": ms, "prefill_tokens_per_s": L / (ms * 1e-3),
          "prefill_hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
          "prefill_mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "segments": plan.segments,
-         "decode_us_per_step": dms * 1e3, "decode_steps_per_s": 1e3 / dms}
+         "decode_us_per_step": dms * 1e3, "decode_steps_per_s": 1e3 / dms,
+         "decode_graph_us_per_step": gms * 1e3, "decode_graph_steps_per_s": 1e3 / gms}
     log(f"long prefill {L} tokens R=4: {ms:.3f} ms, {r['prefill_tokens_per_s'] / 1e6:.1f} M tok/s "
         f"({100 * r['prefill_mfma_frac']:.1f}% MFMA, {100 * r['prefill_hbm_frac']:.1f}% HBM, "
-        f"{plan.segments} segments); decode b=1: {dms * 1e3:.1f} us/step")
+        f"{plan.segments} segments); decode b=1: {dms * 1e3:.1f} us/step eager, {gms * 1e3:.1f} us/step "
+        f"as a captured graph")
+    return r
+
+
+def bench_prologue(log, steps=20, warmup=3, wid=2, tokens=None, copies=16):
+    """m3_prologue (QK-norm + bias on B, C; softplus / sigmoid on dt, lambda) on a workload's raw projections.
+
+    Inputs rotate through `copies` resident sets so the 256 MB MALL cannot hold
+    them all; bytes = raw B, C, dt, lambda read + the four outputs written (+
+    the small weight / bias arrays).
+    """
+    import torch
+    from mamba_ssm_scan_amd import binding, inputs
+    w = inputs.WORKLOADS[wid]
+    tok = (w.batch, w.seqlen) if tokens is None else tuple(tokens)
+    G, R, N, H = 1, w.rank, w.dstate, w.heads
+    sets = [inputs.prologue_inputs(tokens=tok, heads=H, groups=G, rank=R, dstate=N, io_dtype=w.io_dtype, wid=300,
+                                   step=k, device="cuda") for k in range(copies)]
+    outs = [torch.empty_like(sets[0][k]) for k in ("B_raw", "C_raw", "dt_raw", "lambda_raw")]
+
+    def run(k):
+        p = sets[k % copies]
+        binding.prologue(p["B_raw"], p["C_raw"], B_weight=p["B_weight"], B_bias=p["B_bias"], C_weight=p["C_weight"],
+                         C_bias=p["C_bias"], eps=1e-6, dt_raw=p["dt_raw"], dt_bias=p["dt_bias"],
+                         lambda_raw=p["lambda_raw"], B=outs[0], C=outs[1], dt=outs[2], lam=outs[3])
+
+    # one call is a few microseconds of GPU work, less than the Python binding's
+    # own overhead: the calls over all copies are captured in a HIP graph and
+    # the graph is replayed, so the events time the GPU work
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(warmup):
+            run(k)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(copies):
+            run(k)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, steps // copies)
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * copies)
+    ntok = 1
+    for v in tok:
+        ntok *= v
+    by = 2 * 2 * ntok * G * R * N * 2 + 2 * 2 * ntok * H * 4 + 4 * G * R * N * 4 + H * 4
+    r = {"workload": f"prologue tokens={'x'.join(map(str, tok))} H={H} G={G} R={R} N={N} {w.io_dtype}",
+         "ms_per_call": ms, "bytes": by, "hbm_gbs": by / (ms * 1e-3) / 1e9}
+    r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
+    log(f"{r['workload']}: {ms * 1e3:.2f} us/call, {r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM)")
     return r
 
 
@@ -282,7 +359,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
-    ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy, "
+    ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy,prologue, "
                                                "prefill1_real/_euler/_real_euler: run just these (profiling runs); "
                                                "copy = a 1 GiB device copy for counter scaling")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -313,6 +390,10 @@ def main():
                 bench_long(log)
             elif item == "copy":
                 copy_probe(log)
+            elif item == "prologue":
+                bench_prologue(log, args.steps, args.warmup)
+            elif item == "prologue_decode":
+                bench_prologue(log, args.steps, args.warmup, wid=3, tokens=(128,))
             else:
                 raise SystemExit(f"unknown --only item {item!r}")
         return
@@ -341,6 +422,9 @@ def main():
         # the pages' special cases on the same workload: omega = 0 (no rotation), lambda = 1 (Euler)
         out["prefill_special_cases"] = {sp: bench_prefill(1, args.steps, args.warmup, log, special=sp)
                                         for sp in ("real", "euler", "real_euler")}
+        # the input prologue on the R 4 prefill's raw projections and on one decode step's
+        out["prologue"] = {"prefill_r4": bench_prologue(log, args.steps, args.warmup),
+                           "decode_step_b128": bench_prologue(log, args.steps, args.warmup, wid=3, tokens=(128,))}
     if not args.no_cpu and not args.quick:
         out["cpu_baseline"] = cpu_baseline(log)
     print(json.dumps(out), flush=True)

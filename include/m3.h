@@ -175,6 +175,38 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
                          const float* omega, const float* lambda_t, const void* B_t, const void* C_t,
                          const float* D, int32_t R, void* y_t, void* stream);
 
+/*
+ * m3_prologue -- the input prologue in front of the recurrence, one pass over
+ * the raw projections of ntok tokens (b * L for a prefill, b for a decode step).
+ *
+ * Passage: a QK-norm and a learnable additive bias follow the B/C projection
+ * ("复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构", §2.4 and Fig. 4; §3.4 on the
+ * bias); the step and the trapezoid weight come through softplus and sigmoid
+ * (the workloads' input recipe). The pages print no formulas; the reading
+ * taken, per (token t, group g, rank r) row of N entries:
+ *
+ *   B[t][g][r][n] = B_raw[t][g][r][n] / sqrt(mean_n' B_raw[t][g][r][n']^2 + eps)
+ *                   * B_weight[g][r][n] + B_bias[g][r][n]          (C likewise)
+ *   dt[t][h]      = softplus(dt_raw[t][h] + dt_bias[h])   = log(1 + e^x)
+ *   lambda[t][h]  = sigmoid(lambda_raw[t][h])             = 1 / (1 + e^-x)
+ *
+ * dims: heads, groups, dstate are used (batch, seqlen, headdim are not); R >= 1.
+ * B_raw, C_raw -> B, C: [ntok][G][R][N] io dtype, fp32 arithmetic, the output
+ *   rounded to the io dtype (nearest even). B_weight, C_weight, B_bias, C_bias:
+ *   [G][R][N] fp32, each NULL for all-ones weight / zero bias. eps >= 0.
+ * dt_raw -> dt: [ntok][H] fp32; dt_bias [H] fp32 or NULL.
+ * lambda_raw -> lambda: [ntok][H] fp32.
+ * Each of the four parts runs only when both its input and its output are
+ * given (B_raw/B, C_raw/C, dt_raw/dt, lambda_raw/lambda); one of a pair alone
+ * is an error. An output may be its own input (in place) but must not overlap
+ * any other argument. Asynchronous on `stream`; the kernels hold no state.
+ */
+m3_status m3_prologue(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int64_t ntok,
+                      const void* B_raw, const void* C_raw, const float* B_weight, const float* B_bias,
+                      const float* C_weight, const float* C_bias, float eps,
+                      const float* dt_raw, const float* dt_bias, const float* lambda_raw,
+                      void* B, void* C, float* dt, float* lambda, void* stream);
+
 /* Static text for a status code. */
 const char* m3_status_string(m3_status s);
 

@@ -23,7 +23,7 @@ STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EAL
 
 # every symbol include/m3.h declares
 EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_decode_carry_bytes",
-           "m3_decode_state_init", "m3_decode_step", "m3_status_string", "m3_last_error",
+           "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_status_string", "m3_last_error",
            "m3_abi_version"]
 
 
@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.m3_decode_state_init.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [ctypes.POINTER(M3DecodeState)] + [vp] * 8 + [i32, vp, vp]
     lib.m3_decode_step.restype = ctypes.c_int
+    lib.m3_prologue.argtypes = [dims_p, i32, ctypes.c_int, i64] + [vp] * 6 + [ctypes.c_float] + [vp] * 7 + [vp]
+    lib.m3_prologue.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     lib.m3_last_error.argtypes = []
@@ -238,3 +240,64 @@ class DecodeState:
                                   ctypes.c_void_p(A), ctypes.c_void_p(omega), ctypes.c_void_p(lam_t),
                                   ctypes.c_void_p(B_t), ctypes.c_void_p(C_t), ctypes.c_void_p(D), self.R,
                                   ctypes.c_void_p(y_t), stream_handle))
+
+
+def prologue(B_raw=None, C_raw=None, *, B_weight=None, B_bias=None, C_weight=None, C_bias=None, eps: float = 1e-6,
+             dt_raw=None, dt_bias=None, lambda_raw=None, heads: Optional[int] = None,
+             B=None, C=None, dt=None, lam=None, stream=None):
+    """m3_prologue on torch device tensors; returns (B, C, dt, lambda), None for parts not given.
+
+    B_raw, C_raw [..., G, R, N] (bf16 or fp32, one dtype); B/C weights and biases
+    [G, R, N] fp32; dt_raw, lambda_raw [..., H] fp32 with the same leading axes
+    (the token axes); dt_bias [H]. Outputs are allocated unless given (an output
+    may be its own input: in place).
+    """
+    rows = B_raw if B_raw is not None else C_raw
+    scal = dt_raw if dt_raw is not None else lambda_raw
+    if rows is None and scal is None:
+        raise ValueError("nothing to do: give B_raw / C_raw and / or dt_raw / lambda_raw")
+    if rows is not None:
+        if rows.dim() < 3:
+            raise ValueError("B_raw / C_raw must be [..., G, R, N]")
+        G, R, N = rows.shape[-3:]
+        lead = tuple(rows.shape[:-3])
+        io = rows.dtype
+    if scal is not None:
+        H = scal.shape[-1]
+        if rows is not None and tuple(scal.shape[:-1]) != lead:
+            raise ValueError("dt_raw / lambda_raw token axes differ from B_raw / C_raw")
+        lead = tuple(scal.shape[:-1])
+    else:
+        H = heads or G
+    if rows is None:
+        G, R, N, io = 1, 1, 2, torch.bfloat16
+    ntok = 1
+    for v in lead:
+        ntok *= v
+    B_raw = _need(B_raw, "B_raw", io, lead + (G, R, N))
+    C_raw = _need(C_raw, "C_raw", io, lead + (G, R, N))
+    B_weight = _need(B_weight, "B_weight", torch.float32, (G, R, N))
+    B_bias = _need(B_bias, "B_bias", torch.float32, (G, R, N))
+    C_weight = _need(C_weight, "C_weight", torch.float32, (G, R, N))
+    C_bias = _need(C_bias, "C_bias", torch.float32, (G, R, N))
+    dt_raw = _need(dt_raw, "dt_raw", torch.float32, lead + (H,))
+    dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,))
+    lambda_raw = _need(lambda_raw, "lambda_raw", torch.float32, lead + (H,))
+    if B_raw is not None and B is None:
+        B = torch.empty_like(B_raw)
+    if C_raw is not None and C is None:
+        C = torch.empty_like(C_raw)
+    if dt_raw is not None and dt is None:
+        dt = torch.empty_like(dt_raw)
+    if lambda_raw is not None and lam is None:
+        lam = torch.empty_like(lambda_raw)
+    _need_out(B, "B", io, lead + (G, R, N))
+    _need_out(C, "C", io, lead + (G, R, N))
+    _need_out(dt, "dt", torch.float32, lead + (H,))
+    _need_out(lam, "lambda", torch.float32, lead + (H,))
+    d = dims(ntok, 1, H, G, 1, N)
+    check(load().m3_prologue(ctypes.byref(d), R, _io_code(io), ntok, _ptr(B_raw), _ptr(C_raw), _ptr(B_weight),
+                             _ptr(B_bias), _ptr(C_weight), _ptr(C_bias), ctypes.c_float(eps), _ptr(dt_raw),
+                             _ptr(dt_bias), _ptr(lambda_raw), _ptr(B), _ptr(C), _ptr(dt), _ptr(lam),
+                             _stream(stream)))
+    return B, C, dt, lam

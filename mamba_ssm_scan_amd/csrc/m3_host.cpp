@@ -346,4 +346,63 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
     return M3_OK;
 }
 
+m3_status m3_prologue(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int64_t ntok,
+                      const void* B_raw, const void* C_raw, const float* B_weight, const float* B_bias,
+                      const float* C_weight, const float* C_bias, float eps,
+                      const float* dt_raw, const float* dt_bias, const float* lambda_raw,
+                      void* B, void* C, float* dt, float* lambda, void* stream) {
+    g_err[0] = 0;
+    m3_status s = check_dims(dims, R);
+    if (s != M3_OK) return s;
+    if ((s = check_dtype(io_dtype)) != M3_OK) return s;
+    if (ntok < 0) return fail(M3_EINVAL, "ntok %lld < 0", (long long)ntok);
+    if (!(eps >= 0.f) || eps > 3.0e38f) return fail(M3_EINVAL, "eps must be finite and >= 0");
+    struct Pair { const char* in_name; const void* in; const char* out_name; const void* out; };
+    const Pair pairs[] = {{"B_raw", B_raw, "B", B}, {"C_raw", C_raw, "C", C}, {"dt_raw", dt_raw, "dt", dt},
+                          {"lambda_raw", lambda_raw, "lambda", lambda}};
+    for (const Pair& p : pairs)
+        if ((p.in == nullptr) != (p.out == nullptr))
+            return fail(M3_EINVAL, "%s and %s must be given together", p.in_name, p.out_name);
+    if (!B && (B_weight || B_bias)) return fail(M3_EINVAL, "B_weight / B_bias given without B");
+    if (!C && (C_weight || C_bias)) return fail(M3_EINVAL, "C_weight / C_bias given without C");
+    if (!dt && dt_bias) return fail(M3_EINVAL, "dt_bias given without dt");
+
+    const int64_t H = dims->heads, G = dims->groups, N = dims->dstate;
+    const size_t es = io_size(io_dtype);
+    const size_t nrow = size_t(ntok) * size_t(G) * size_t(R) * size_t(N) * es;
+    const size_t npar = size_t(G) * size_t(R) * size_t(N) * 4, nsc = size_t(ntok) * size_t(H) * 4;
+    const Range in[] = {rng("B_raw", B_raw, nrow), rng("C_raw", C_raw, nrow), rng("B_weight", B_weight, npar),
+                        rng("B_bias", B_bias, npar), rng("C_weight", C_weight, npar), rng("C_bias", C_bias, npar),
+                        rng("dt_raw", dt_raw, nsc), rng("dt_bias", dt_bias, size_t(H) * 4),
+                        rng("lambda_raw", lambda_raw, nsc)};
+    const Range out[] = {rng("B", B, nrow), rng("C", C, nrow), rng("dt", dt, nsc), rng("lambda", lambda, nsc)};
+    const int own[] = {0, 1, 6, 8};  // the input each output may replace in place
+    for (const Range& r : in)
+        if (r.lo && !aligned16(reinterpret_cast<const void*>(r.lo)))
+            return fail(M3_EALIGN, "%s is not 16-byte aligned", r.name);
+    for (const Range& r : out)
+        if (r.lo && !aligned16(reinterpret_cast<const void*>(r.lo)))
+            return fail(M3_EALIGN, "%s is not 16-byte aligned", r.name);
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < int(sizeof in / sizeof in[0]); ++i) {
+            if (!overlaps(out[o], in[i])) continue;
+            if (i == own[o] && out[o].lo == in[i].lo) continue;  // in place
+            return fail(M3_EINVAL, "%s overlaps %s", out[o].name, in[i].name);
+        }
+        for (int q = o + 1; q < 4; ++q)
+            if (overlaps(out[o], out[q])) return fail(M3_EINVAL, "%s overlaps %s", out[o].name, out[q].name);
+    }
+    if (ntok == 0) return M3_OK;
+    const int64_t rows = ntok * G * R;
+    if ((B || C) && (rows + 15) / 16 > 0x3fffffff) return fail(M3_EUNSUPPORTED, "too many rows");
+    if ((dt || lambda) && (ntok * H + 255) / 256 > 0x3fffffff) return fail(M3_EUNSUPPORTED, "too many tokens");
+
+    m3::PrologueArgs a{B_raw, C_raw, B_weight, B_bias, C_weight, C_bias, eps, dt_raw, dt_bias, lambda_raw,
+                       B, C, dt, lambda, ntok, (int32_t)H, (int32_t)(G * R), (int32_t)N, io_dtype,
+                       reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = m3::launch_prologue(a);
+    if (e != hipSuccess) return fail(M3_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
+    return M3_OK;
+}
+
 }  // extern "C"

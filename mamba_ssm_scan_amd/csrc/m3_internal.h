@@ -51,6 +51,27 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 
+struct PrologueArgs {
+    const void* B_raw;     // [ntok][G][R][N] io dtype (with B, or both NULL)
+    const void* C_raw;
+    const float* B_weight; // [G][R][N] or NULL (1)
+    const float* B_bias;   // [G][R][N] or NULL (0)
+    const float* C_weight;
+    const float* C_bias;
+    float eps;
+    const float* dt_raw;   // [ntok][H] (with dt, or both NULL)
+    const float* dt_bias;  // [H] or NULL
+    const float* lambda_raw;
+    void* B;
+    void* C;
+    float* dt;
+    float* lambda;
+    int64_t ntok;
+    int32_t H, GR, N;      // GR = G * R rows per token
+    m3_dtype io;
+    hipStream_t stream;
+};
+
 // Layout of the prefill workspace (byte offsets), shared by host and launchers.
 struct PrefillWorkspace {
     size_t state_off;      // generic path: running state [b][H][N][P] fp32
@@ -71,6 +92,7 @@ bool mfma_segments_supported(int32_t R);
 hipError_t launch_prefill_generic(const PrefillArgs& a);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prologue(const PrologueArgs& a);
 // dst[i] = src ? src[i] : 0 for n 32-bit words (a kernel, so it is safe under graph capture)
 hipError_t launch_copy_or_zero(uint32_t* dst, const uint32_t* src, int64_t n_words, hipStream_t s);
 

@@ -40,7 +40,8 @@ ROOT_SEED = 20261203
 
 # tensor ids used in the seed sequence
 _TID = {"x": 1, "B": 2, "C": 3, "dt": 4, "lam": 5, "A": 6, "omega": 7, "D": 8,
-        "h0": 9, "carry_B": 10, "carry_x": 11}
+        "h0": 9, "carry_B": 10, "carry_x": 11, "B_raw": 12, "C_raw": 13, "B_weight": 14, "B_bias": 15,
+        "C_weight": 16, "C_bias": 17, "dt_raw": 18, "dt_bias": 19, "lambda_raw": 20, "row_scale": 21}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -249,3 +250,35 @@ def slice_tokens(p: dict, start: int, stop: int) -> dict:
     for k in ("x", "B", "C", "dt", "lam"):
         out[k] = p[k][:, start:stop].contiguous()
     return out
+
+
+def prologue_inputs(*, tokens, heads, groups, rank, dstate, io_dtype="bf16", wid=200, step=0,
+                    device="cpu") -> dict:
+    """Raw projections for the input prologue (random draws only, no prologue arithmetic).
+
+    tokens: the token axes, e.g. (b, L) for a prefill or (b,) for a decode step.
+    B_raw, C_raw [*tokens][G][R][N] (io dtype): N(0, 1) times a per-row scale
+    drawn from U(0.25, 4), so rows arrive at different magnitudes;
+    B/C weights ~ N(1, 0.1) and biases ~ N(0, 0.1), [G][R][N] fp32 (stand-ins
+    for learned parameters); dt_raw ~ N(-1, 0.5) and lambda_raw ~ N(0, 1)
+    [*tokens][H] (softplus and sigmoid of these are the workloads' dt and
+    lambda); dt_bias ~ N(0, 0.2) [H].
+    """
+    tokens = tuple(int(t) for t in tokens)
+    G, R, N, H = groups, rank, dstate, heads
+    dt_ = _torch_dtype(io_dtype)
+
+    def rows(name):
+        t = _normal(tokens + (G, R, N), _gen(device, wid, name, step), device)
+        scale = _uniform(tokens + (G, R, 1), _gen(device, wid, "row_scale", step + (0 if name == "B_raw" else 1)),
+                         device, 0.25, 4.0)
+        return (t * scale).to(dt_)
+
+    par = lambda name, mean, std: _normal((G, R, N), _gen(device, wid, name), device, mean, std)
+    return dict(B_raw=rows("B_raw"), C_raw=rows("C_raw"),
+                B_weight=par("B_weight", 1.0, 0.1), B_bias=par("B_bias", 0.0, 0.1),
+                C_weight=par("C_weight", 1.0, 0.1), C_bias=par("C_bias", 0.0, 0.1),
+                dt_raw=_normal(tokens + (H,), _gen(device, wid, "dt_raw", step), device, -1.0, 0.5),
+                dt_bias=_normal((H,), _gen(device, wid, "dt_bias"), device, 0.0, 0.2),
+                lambda_raw=_normal(tokens + (H,), _gen(device, wid, "lambda_raw", step), device),
+                io_dtype=io_dtype)

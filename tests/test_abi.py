@@ -177,3 +177,53 @@ def test_omega_lambda_may_be_null(lib):
     assert lib.m3_decode_step(ctypes.byref(s), f(10), f(11), f(12), None, None, f(15), f(16), f(17), 1,
                               y_in_x, None) == 1
     assert "y_t overlaps" in lib.m3_last_error().decode()
+
+
+def _prologue(lib, d, R=1, io=bd.M3_F32, ntok=10, eps=1e-6, **over):
+    names = ["B_raw", "C_raw", "B_weight", "B_bias", "C_weight", "C_bias", "dt_raw", "dt_bias", "lambda_raw",
+             "B", "C", "dt", "lambda"]
+    ptr = {n: FAKE + i * (1 << 30) for i, n in enumerate(names)}
+    ptr.update(over)
+    v = lambda n: None if ptr[n] is None else ctypes.c_void_p(ptr[n])
+    dp = None if d is None else ctypes.byref(d)
+    st = lib.m3_prologue(dp, R, io, ntok, v("B_raw"), v("C_raw"), v("B_weight"), v("B_bias"), v("C_weight"),
+                         v("C_bias"), ctypes.c_float(eps), v("dt_raw"), v("dt_bias"), v("lambda_raw"), v("B"), v("C"),
+                         v("dt"), v("lambda"), None)
+    return st, lib.m3_last_error().decode()
+
+
+def test_prologue_argument_errors(lib):
+    assert _prologue(lib, None)[0] == 1
+    assert _prologue(lib, _dims(N=7))[0] == 1
+    assert _prologue(lib, _dims(), R=0)[0] == 1
+    assert _prologue(lib, _dims(), io=9)[0] == 3
+    assert _prologue(lib, _dims(), ntok=-1)[0] == 1
+    assert _prologue(lib, _dims(), eps=-1.0)[0] == 1
+    assert _prologue(lib, _dims(), eps=float("nan"))[0] == 1
+    st, msg = _prologue(lib, _dims(), B=None)                      # B_raw without B
+    assert st == 1 and "B_raw" in msg
+    st, msg = _prologue(lib, _dims(), dt_raw=None)                 # dt without dt_raw
+    assert st == 1 and "dt" in msg
+    st, msg = _prologue(lib, _dims(), C_raw=None, C=None)          # C weight without C
+    assert st == 1 and "C_weight" in msg
+    st, msg = _prologue(lib, _dims(), dt_raw=None, dt=None)        # dt_bias without dt
+    assert st == 1 and "dt_bias" in msg
+    st, msg = _prologue(lib, _dims(), C=FAKE + 1 * (1 << 30) + 8)  # misaligned
+    assert st == 4 and "C" in msg
+    st, msg = _prologue(lib, _dims(), B=FAKE + 16)                 # B inside B_raw, not in place
+    assert st == 1 and "B overlaps B_raw" in msg
+    st, msg = _prologue(lib, _dims(), dt=FAKE + 8 * (1 << 30))     # dt on lambda_raw
+    assert st == 1 and "dt overlaps lambda_raw" in msg
+    st, msg = _prologue(lib, _dims(), lam=None, **{"lambda": FAKE + 11 * (1 << 30)})  # lambda on dt
+    assert st == 1 and "overlaps" in msg
+
+
+def test_prologue_in_place_and_empty_pass_checks(lib):
+    # outputs on their own inputs are allowed; with ntok = 0 nothing is launched
+    same = {"B": FAKE, "C": FAKE + (1 << 30), "dt": FAKE + 6 * (1 << 30), "lambda": FAKE + 8 * (1 << 30)}
+    assert _prologue(lib, _dims(), ntok=0, **same)[0] == 0
+    assert _prologue(lib, _dims(), ntok=0)[0] == 0
+    # nothing given at all is a valid no-op
+    none = {n: None for n in ["B_raw", "C_raw", "B_weight", "B_bias", "C_weight", "C_bias", "dt_raw", "dt_bias",
+                              "lambda_raw", "B", "C", "dt", "lambda"]}
+    assert _prologue(lib, _dims(), **none)[0] == 0
