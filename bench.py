@@ -82,17 +82,21 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(wid, steps, warmup, log, special=""):
-    """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both."""
+def bench_prefill(wid, steps, warmup, log, special="", groups=1):
+    """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
+
+    groups: 1 (B, C shared by all heads, the primary reading) or H (one B, C per head).
+    """
     import torch
     from mamba_ssm_scan_amd import binding, inputs
     w = inputs.WORKLOADS[wid]
-    copies = [inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=1, headdim=w.headdim,
+    G = groups
+    copies = [inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=G, headdim=w.headdim,
                                   dstate=w.dstate, rank=w.rank, io_dtype=w.io_dtype, dist=w.dist, wid=wid,
                                   step=k, device="cuda") for k in range(N_COPIES)]
     y = torch.empty_like(copies[0]["x"])
     h = torch.empty((w.batch, w.heads, w.dstate, w.headdim), dtype=torch.float32, device="cuda")
-    plan = binding.plan(binding.dims(w.batch, w.seqlen, w.heads, 1, w.headdim, w.dstate), w.rank, w.chunk,
+    plan = binding.plan(binding.dims(w.batch, w.seqlen, w.heads, G, w.headdim, w.dstate), w.rank, w.chunk,
                         binding.M3_BF16)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
 
@@ -113,11 +117,11 @@ def bench_prefill(wid, steps, warmup, log, special=""):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    by = prefill_bytes(w.batch, w.seqlen, w.heads, 1, w.headdim, w.dstate, w.rank)
+    by = prefill_bytes(w.batch, w.seqlen, w.heads, G, w.headdim, w.dstate, w.rank)
     if no_lam:
         by -= w.batch * w.seqlen * w.heads * 4
     fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
-    name = w.name + (f" ({special})" if special else "")
+    name = w.name + (f" ({special})" if special else "") + (f" G={G}" if G != 1 else "")
     r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
          "bytes": by, "flops": fl, "path": "mfma" if plan.path == binding.M3_PATH_MFMA else "generic",
@@ -382,6 +386,8 @@ def main():
                 bench_prefill(1, args.steps, args.warmup, log)
             elif item == "prefill2":
                 bench_prefill(2, args.steps, args.warmup, log)
+            elif item in ("prefill1_g64", "prefill2_g64"):
+                bench_prefill(int(item[7]), args.steps, args.warmup, log, groups=64)
             elif item.startswith("prefill1_"):
                 bench_prefill(1, args.steps, args.warmup, log, special=item[len("prefill1_"):])
             elif item in ("decode1", "decode4"):
@@ -422,6 +428,9 @@ def main():
         # the pages' special cases on the same workload: omega = 0 (no rotation), lambda = 1 (Euler)
         out["prefill_special_cases"] = {sp: bench_prefill(1, args.steps, args.warmup, log, special=sp)
                                         for sp in ("real", "euler", "real_euler")}
+        # the secondary reading: one B, C per head (64x the B/C bytes)
+        out["prefill_groups_eq_heads"] = {f"r{w}": bench_prefill(wid, args.steps, args.warmup, log, groups=64)
+                                          for w, wid in ((1, 1), (4, 2))}
         # the input prologue on the R 4 prefill's raw projections and on one decode step's
         out["prologue"] = {"prefill_r4": bench_prologue(log, args.steps, args.warmup),
                            "decode_step_b128": bench_prologue(log, args.steps, args.warmup, wid=3, tokens=(128,))}

@@ -99,13 +99,18 @@ def test_mfma_chunk_sweep_agrees():
 SAMPLE_HEADS = [0, 21, 42, 63]
 
 
+@pytest.mark.parametrize("groups", [1, 64])
 @pytest.mark.parametrize("wid", [1, 2])
-def test_workload_full_size(wid):
-    """Workloads 1 (R=1) and 2 (R=4) at full size, chunk 64; oracle on 4 heads x all batches."""
-    _flush(f"workload {wid} full size")
-    p = inputs.workload_prefill(wid, device="cuda")
+def test_workload_full_size(wid, groups):
+    """Workloads 1 (R=1) and 2 (R=4) at full size, chunk 64; oracle on 4 heads x all batches.
+
+    groups 1 is the primary reading (B, C shared by all heads); groups 64 gives
+    every head its own B, C (the secondary reading, 64x the B/C bytes).
+    """
+    _flush(f"workload {wid} full size, G {groups}")
+    p = inputs.workload_prefill(wid, device="cuda", groups=groups)
     w = inputs.WORKLOADS[wid]
-    assert _path(w.batch, w.seqlen, w.heads, 1, w.rank, w.chunk) == binding.M3_PATH_MFMA
+    assert _path(w.batch, w.seqlen, w.heads, groups, w.rank, w.chunk) == binding.M3_PATH_MFMA
     y, h = binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], w.rank, w.chunk)
     torch.cuda.synchronize()
     sub = to_host(inputs.select_heads(p, SAMPLE_HEADS))
