@@ -207,6 +207,38 @@ m3_status m3_prologue(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int64_t
                       const float* dt_raw, const float* dt_bias, const float* lambda_raw,
                       void* B, void* C, float* dt, float* lambda, void* stream);
 
+/*
+ * m3_prefill_backward -- gradients of one m3_prefill call (training).
+ *
+ * Passage: the same recurrence, differentiated in reverse ("复值SSM × 广义梯形离散
+ * × MIMO", §2.1-§2.3; the pages' kernels serve training as well as inference).
+ * Given dy = dLoss/dy [b][L][H][R][P] (io dtype) and dh_out = dLoss/dh_out
+ * [b][H][N][P] fp32 (NULL: zero), it writes dLoss/d of every input, fp32:
+ *   dx [b][L][H][R][P], dB and dC [b][L][G][R][N] (summed over the heads of a
+ *   group), ddt and dlambda [b][L][H], dA and dD [H] and domega [H][N/2]
+ *   (summed over batch and tokens), dh0 [b][H][N][P], dcarry_B [b][G][R][N]
+ *   and dcarry_x [b][H][R][P].
+ * The forward inputs are those of m3_prefill (same layouts, same NULL rules for
+ * omega, lambda, h0 and the carry). dlambda, domega and dh0 may be NULL (not
+ * wanted); dcarry_B / dcarry_x are given together, and only with the carry.
+ * Supported: N <= 128, P <= 64, R <= 4 (else M3_EUNSUPPORTED). The arithmetic is
+ * fp32; the states are recomputed from checkpoints kept in `workspace` (at least
+ * m3_prefill_backward_workspace_size() bytes). The summed gradients are added
+ * with device atomics, so their last bits can vary from call to call. No
+ * output may overlap an input or another output. Asynchronous on `stream`.
+ */
+m3_status m3_prefill_backward(const void* x, const float* dt, const float* A, const float* omega,
+                              const float* lambda, const void* B, const void* C, const float* D,
+                              int32_t R, const float* h0, const void* carry_B, const void* carry_x,
+                              const void* dy, const float* dh_out,
+                              float* dx, float* dB, float* dC, float* ddt, float* dlambda, float* dA,
+                              float* domega, float* dD, float* dh0, float* dcarry_B, float* dcarry_x,
+                              const m3_dims* dims, m3_dtype io_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes m3_prefill_backward needs (0 on invalid or unsupported sizes). Host only. */
+size_t m3_prefill_backward_workspace_size(const m3_dims* dims, int32_t R);
+
 /* Static text for a status code. */
 const char* m3_status_string(m3_status s);
 

@@ -23,8 +23,8 @@ STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EAL
 
 # every symbol include/m3.h declares
 EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_decode_carry_bytes",
-           "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_status_string", "m3_last_error",
-           "m3_abi_version"]
+           "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_prefill_backward",
+           "m3_prefill_backward_workspace_size", "m3_status_string", "m3_last_error", "m3_abi_version"]
 
 
 class M3Dims(ctypes.Structure):
@@ -79,6 +79,10 @@ def load(path: str = LIB_PATH):
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_prologue.argtypes = [dims_p, i32, ctypes.c_int, i64] + [vp] * 6 + [ctypes.c_float] + [vp] * 7 + [vp]
     lib.m3_prologue.restype = ctypes.c_int
+    lib.m3_prefill_backward.argtypes = [vp] * 8 + [i32] + [vp] * 16 + [dims_p, ctypes.c_int, vp, sz, vp]
+    lib.m3_prefill_backward.restype = ctypes.c_int
+    lib.m3_prefill_backward_workspace_size.argtypes = [dims_p, i32]
+    lib.m3_prefill_backward_workspace_size.restype = sz
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     lib.m3_last_error.argtypes = []
@@ -301,3 +305,53 @@ def prologue(B_raw=None, C_raw=None, *, B_weight=None, B_bias=None, C_weight=Non
                              _ptr(dt_bias), _ptr(lambda_raw), _ptr(B), _ptr(C), _ptr(dt), _ptr(lam),
                              _stream(stream)))
     return B, C, dt, lam
+
+
+def prefill_backward(x, dt, A, omega, lam, B, C, D, R: int, dy, h0=None, dh_out=None, *, carry_B=None,
+                     carry_x=None, want_lambda=True, want_omega=True, want_h0=True, workspace=None, stream=None):
+    """m3_prefill_backward on torch device tensors; returns a dict of fp32 gradients.
+
+    Keys: x, B, C, dt, lam, A, omega, D, h0, carry_B, carry_x (None for gradients
+    not asked for or without a carry). Inputs as for `prefill`; dy like y.
+    """
+    if x.dim() != 5 or B.dim() != 5:
+        raise ValueError("x must be [b][L][H][R][P] and B [b][L][G][R][N]")
+    b, L, H, R_, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    if R_ != R or B.shape[3] != R:
+        raise ValueError(f"rank mismatch: R={R}, x has {R_}, B has {B.shape[3]}")
+    io = x.dtype
+    x = _need(x, "x", io)
+    B = _need(B, "B", io, (b, L, G, R, N))
+    C = _need(C, "C", io, (b, L, G, R, N))
+    dy = _need(dy, "dy", io, (b, L, H, R, P))
+    dt = _need(dt, "dt", torch.float32, (b, L, H))
+    lam = _need(lam, "lambda", torch.float32, (b, L, H))
+    A = _need(A, "A", torch.float32, (H,))
+    D = _need(D, "D", torch.float32, (H,))
+    omega = _need(omega, "omega", torch.float32, (H, N // 2))
+    h0 = _need(h0, "h0", torch.float32, (b, H, N, P))
+    dh_out = _need(dh_out, "dh_out", torch.float32, (b, H, N, P))
+    carry_B = _need(carry_B, "carry_B", io, (b, G, R, N))
+    carry_x = _need(carry_x, "carry_x", io, (b, H, R, P))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"x": torch.empty((b, L, H, R, P), **f32), "B": torch.empty((b, L, G, R, N), **f32),
+         "C": torch.empty((b, L, G, R, N), **f32), "dt": torch.empty((b, L, H), **f32),
+         "lam": torch.empty((b, L, H), **f32) if want_lambda else None, "A": torch.empty((H,), **f32),
+         "omega": torch.empty((H, N // 2), **f32) if want_omega else None, "D": torch.empty((H,), **f32),
+         "h0": torch.empty((b, H, N, P), **f32) if want_h0 else None,
+         "carry_B": torch.empty((b, G, R, N), **f32) if carry_B is not None else None,
+         "carry_x": torch.empty((b, H, R, P), **f32) if carry_x is not None else None}
+    d = dims(b, L, H, G, P, N)
+    lib = load()
+    need = lib.m3_prefill_backward_workspace_size(ctypes.byref(d), R)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.m3_prefill_backward(_ptr(x), _ptr(dt), _ptr(A), _ptr(omega), _ptr(lam), _ptr(B), _ptr(C), _ptr(D),
+                                  R, _ptr(h0), _ptr(carry_B), _ptr(carry_x), _ptr(dy), _ptr(dh_out),
+                                  _ptr(g["x"]), _ptr(g["B"]), _ptr(g["C"]), _ptr(g["dt"]), _ptr(g["lam"]),
+                                  _ptr(g["A"]), _ptr(g["omega"]), _ptr(g["D"]), _ptr(g["h0"]), _ptr(g["carry_B"]),
+                                  _ptr(g["carry_x"]), ctypes.byref(d), _io_code(io), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
+    return g

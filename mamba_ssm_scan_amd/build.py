@@ -23,7 +23,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["m3_host.cpp", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_decode.hip", "m3_prologue.hip"]
+SOURCES = ["m3_host.cpp", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_decode.hip", "m3_prologue.hip",
+           "m3_backward.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

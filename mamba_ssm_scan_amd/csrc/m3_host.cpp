@@ -346,6 +346,84 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
     return M3_OK;
 }
 
+size_t m3_prefill_backward_workspace_size(const m3_dims* dims, int32_t R) {
+    if (check_dims(dims, R) != M3_OK) return 0;
+    if (!m3::backward_supported(dims->headdim, dims->dstate, R)) return 0;
+    return m3::backward_workspace_bytes(dims->batch, dims->heads, dims->seqlen);
+}
+
+m3_status m3_prefill_backward(const void* x, const float* dt, const float* A, const float* omega,
+                              const float* lambda, const void* B, const void* C, const float* D,
+                              int32_t R, const float* h0, const void* carry_B, const void* carry_x,
+                              const void* dy, const float* dh_out,
+                              float* dx, float* dB, float* dC, float* ddt, float* dlambda, float* dA,
+                              float* domega, float* dD, float* dh0, float* dcarry_B, float* dcarry_x,
+                              const m3_dims* dims, m3_dtype io_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    m3_status s = check_dims(dims, R);
+    if (s != M3_OK) return s;
+    if ((s = check_dtype(io_dtype)) != M3_OK) return s;
+    const int64_t b = dims->batch, L = dims->seqlen;
+    const int64_t H = dims->heads, G = dims->groups, P = dims->headdim, N = dims->dstate;
+    if (!m3::backward_supported((int32_t)P, (int32_t)N, R))
+        return fail(M3_EUNSUPPORTED, "backward supports N <= 128, P <= 64, R <= 4 (got N %lld, P %lld, R %d)",
+                    (long long)N, (long long)P, R);
+    const bool tokens = b > 0 && L > 0;
+    struct Req { const char* name; const void* p; bool needed; };
+    const Req req[] = {{"x", x, tokens}, {"dt", dt, tokens}, {"B", B, tokens}, {"C", C, tokens},
+                       {"dy", dy, tokens}, {"dx", dx, tokens}, {"dB", dB, tokens}, {"dC", dC, tokens},
+                       {"ddt", ddt, tokens}, {"A", A, b > 0}, {"D", D, b > 0}, {"dA", dA, b > 0}, {"dD", dD, b > 0}};
+    for (const Req& r : req)
+        if (r.needed && !r.p) return fail(M3_EINVAL, "%s is NULL", r.name);
+    if ((carry_B == nullptr) != (carry_x == nullptr))
+        return fail(M3_EINVAL, "carry_B and carry_x must be given together");
+    if ((dcarry_B == nullptr) != (dcarry_x == nullptr))
+        return fail(M3_EINVAL, "dcarry_B and dcarry_x must be given together");
+    if (dcarry_B && !carry_B) return fail(M3_EINVAL, "dcarry_B / dcarry_x given without a carry");
+
+    const size_t es = io_size(io_dtype);
+    const size_t tok = size_t(b) * size_t(L);
+    const size_t nx = tok * H * R * P, nbc = tok * G * R * N, nsc = tok * H, nst = size_t(b) * H * N * P;
+    const Range in[] = {rng("x", x, nx * es), rng("dt", dt, nsc * 4), rng("A", A, H * 4),
+                        rng("omega", omega, H * (N / 2) * 4), rng("lambda", lambda, nsc * 4),
+                        rng("B", B, nbc * es), rng("C", C, nbc * es), rng("D", D, H * 4), rng("h0", h0, nst * 4),
+                        rng("carry_B", carry_B, size_t(b) * G * R * N * es),
+                        rng("carry_x", carry_x, size_t(b) * H * R * P * es), rng("dy", dy, nx * es),
+                        rng("dh_out", dh_out, nst * 4), rng("workspace", workspace, workspace_bytes)};
+    const Range out[] = {rng("dx", dx, nx * 4), rng("dB", dB, nbc * 4), rng("dC", dC, nbc * 4),
+                         rng("ddt", ddt, nsc * 4), rng("dlambda", dlambda, nsc * 4), rng("dA", dA, H * 4),
+                         rng("domega", domega, H * (N / 2) * 4), rng("dD", dD, H * 4), rng("dh0", dh0, nst * 4),
+                         rng("dcarry_B", dcarry_B, size_t(b) * G * R * N * 4),
+                         rng("dcarry_x", dcarry_x, size_t(b) * H * R * P * 4)};
+    for (const Range& r : in)
+        if (r.lo && !aligned16(reinterpret_cast<const void*>(r.lo)))
+            return fail(M3_EALIGN, "%s is not 16-byte aligned", r.name);
+    for (const Range& r : out)
+        if (r.lo && !aligned16(reinterpret_cast<const void*>(r.lo)))
+            return fail(M3_EALIGN, "%s is not 16-byte aligned", r.name);
+    const int nout = int(sizeof out / sizeof out[0]);
+    for (int o = 0; o < nout; ++o) {
+        for (const Range& r : in)
+            if (overlaps(out[o], r)) return fail(M3_EINVAL, "%s overlaps %s", out[o].name, r.name);
+        for (int q = o + 1; q < nout; ++q)
+            if (overlaps(out[o], out[q])) return fail(M3_EINVAL, "%s overlaps %s", out[o].name, out[q].name);
+    }
+    const size_t need = m3::backward_workspace_bytes(b, (int32_t)H, L);
+    if (tokens && (!workspace || workspace_bytes < need))
+        return fail(M3_EWORKSPACE, "backward needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (b == 0) return M3_OK;
+    if (b * H > 0x7fffffff) return fail(M3_EUNSUPPORTED, "b * H above 2^31 - 1");
+
+    m3::BackwardArgs a{x, dt, A, omega, lambda, B, C, D, h0, carry_B, carry_x, dy, dh_out,
+                       dx, dB, dC, ddt, dlambda, dA, domega, dD, dh0, dcarry_B, dcarry_x,
+                       b, L, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R, io_dtype,
+                       static_cast<float*>(workspace), reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = m3::launch_backward(a);
+    if (e != hipSuccess) return fail(M3_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+    return M3_OK;
+}
+
 m3_status m3_prologue(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int64_t ntok,
                       const void* B_raw, const void* C_raw, const float* B_weight, const float* B_bias,
                       const float* C_weight, const float* C_bias, float eps,

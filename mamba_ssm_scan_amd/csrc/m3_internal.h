@@ -72,6 +72,46 @@ struct PrologueArgs {
     hipStream_t stream;
 };
 
+struct BackwardArgs {
+    // the forward's inputs
+    const void* x;
+    const float* dt;
+    const float* A;
+    const float* omega;    // nullable (omega = 0)
+    const float* lam;      // nullable (lambda = 1)
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h0;       // nullable
+    const void* carry_B;   // nullable (both or neither)
+    const void* carry_x;
+    // incoming gradients
+    const void* dy;        // [b][L][H][R][P] io dtype
+    const float* dh_out;   // [b][H][N][P] or NULL
+    // gradients (fp32); the accumulated ones are cleared by the launcher
+    float* dx;             // [b][L][H][R][P]
+    float* dB;             // [b][L][G][R][N] (summed over the heads of a group)
+    float* dC;
+    float* ddt;            // [b][L][H]
+    float* dlam;           // [b][L][H] or NULL
+    float* dA;             // [H] (summed over batch and tokens)
+    float* domega;         // [H][N/2] or NULL
+    float* dD;             // [H]
+    float* dh0;            // [b][H][N][P] or NULL
+    float* dcarry_B;       // [b][G][R][N] or NULL (with the carry)
+    float* dcarry_x;       // [b][H][R][P] or NULL
+    int64_t b, L;
+    int32_t H, G, P, N, R;
+    m3_dtype io;
+    float* workspace;      // backward_workspace_floats(b, H, L) floats
+    hipStream_t stream;
+};
+
+// Tokens between the backward's state checkpoints, and its workspace size.
+constexpr int kBackwardCheckpoint = 32;
+size_t backward_workspace_bytes(int64_t b, int32_t H, int64_t L);
+bool backward_supported(int32_t P, int32_t N, int32_t R);
+
 // Layout of the prefill workspace (byte offsets), shared by host and launchers.
 struct PrefillWorkspace {
     size_t state_off;      // generic path: running state [b][H][N][P] fp32
@@ -93,6 +133,7 @@ hipError_t launch_prefill_generic(const PrefillArgs& a);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prologue(const PrologueArgs& a);
+hipError_t launch_backward(const BackwardArgs& a);
 // dst[i] = src ? src[i] : 0 for n 32-bit words (a kernel, so it is safe under graph capture)
 hipError_t launch_copy_or_zero(uint32_t* dst, const uint32_t* src, int64_t n_words, hipStream_t s);
 

@@ -227,3 +227,46 @@ def test_prologue_in_place_and_empty_pass_checks(lib):
     none = {n: None for n in ["B_raw", "C_raw", "B_weight", "B_bias", "C_weight", "C_bias", "dt_raw", "dt_bias",
                               "lambda_raw", "B", "C", "dt", "lambda"]}
     assert _prologue(lib, _dims(), **none)[0] == 0
+
+
+def _backward(lib, d, R=1, io=bd.M3_F32, ws_bytes=None, **over):
+    names = ["x", "dt", "A", "omega", "lam", "B", "C", "D", "h0", "cB", "cx", "dy", "dh", "dx", "dB", "dC", "ddt",
+             "dlam", "dA", "domega", "dD", "dh0", "dcB", "dcx", "ws"]
+    ptr = {n: FAKE + i * (1 << 30) for i, n in enumerate(names)}
+    ptr["h0"] = ptr["cB"] = ptr["cx"] = ptr["dh"] = ptr["dcB"] = ptr["dcx"] = None
+    ptr.update(over)
+    v = lambda n: None if ptr[n] is None else ctypes.c_void_p(ptr[n])
+    if ws_bytes is None:
+        ws_bytes = 0 if d is None else lib.m3_prefill_backward_workspace_size(ctypes.byref(d), R)
+    dp = None if d is None else ctypes.byref(d)
+    st = lib.m3_prefill_backward(v("x"), v("dt"), v("A"), v("omega"), v("lam"), v("B"), v("C"), v("D"), R, v("h0"),
+                                 v("cB"), v("cx"), v("dy"), v("dh"), v("dx"), v("dB"), v("dC"), v("ddt"), v("dlam"),
+                                 v("dA"), v("domega"), v("dD"), v("dh0"), v("dcB"), v("dcx"), dp, io, v("ws"),
+                                 ws_bytes, None)
+    return st, lib.m3_last_error().decode()
+
+
+def test_backward_argument_errors(lib):
+    d = _dims()
+    assert lib.m3_prefill_backward_workspace_size(ctypes.byref(d), 1) > 0
+    assert lib.m3_prefill_backward_workspace_size(ctypes.byref(_dims(N=256)), 1) == 0   # unsupported
+    assert _backward(lib, None)[0] == 1
+    assert _backward(lib, _dims(N=256))[0] == 5
+    assert _backward(lib, _dims(P=65))[0] == 5
+    assert _backward(lib, _dims(), R=5)[0] == 5
+    st, msg = _backward(lib, _dims(), dy=None)
+    assert st == 1 and "dy" in msg
+    st, msg = _backward(lib, _dims(), cB=FAKE + 40 * (1 << 30))
+    assert st == 1 and "carry" in msg
+    st, msg = _backward(lib, _dims(), dcB=FAKE + 40 * (1 << 30), dcx=FAKE + 41 * (1 << 30))
+    assert st == 1 and "without a carry" in msg
+    st, msg = _backward(lib, _dims(), dB=FAKE + 14 * (1 << 30) + 8)
+    assert st == 4 and "dB" in msg
+    st, msg = _backward(lib, _dims(), dC=FAKE + 14 * (1 << 30))          # dC on dB
+    assert st == 1 and "overlaps" in msg
+    st, msg = _backward(lib, _dims(), dx=FAKE + 16)                      # dx inside x
+    assert st == 1 and "dx overlaps x" in msg
+    st, msg = _backward(lib, _dims(), ws_bytes=16)
+    assert st == 7 and "workspace" in msg
+    # no tokens: valid, nothing launched
+    assert _backward(lib, _dims(b=0))[0] == 0
