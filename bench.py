@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s + decode steps/s on 1 GPU; % of HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (VALU), TFLOP/s
 N_COPIES = 4                 # input copies rotated through so the 256 MB MALL cannot hold them
 
 # HBM traffic per launch measured with rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
@@ -249,6 +250,48 @@ def bench_long(log):
     return r
 
 
+def backward_flops(b, L, H, P, N, R):
+    """fp32 VALU flops of the sequential backward as built: per state entry and token, two forward
+    passes (the checkpoint pass and the block recompute, 2R + 7 each) and the reverse step (12R + 18)."""
+    return b * L * H * N * P * (2 * (2 * R + 7) + 12 * R + 18)
+
+
+def bench_backward(wid, steps, warmup, log):
+    """m3_prefill_backward on a prefill workload's inputs with a random dy (bf16) and dh_out."""
+    import torch
+    from mamba_ssm_scan_amd import binding, inputs
+    w = inputs.WORKLOADS[wid]
+    p = inputs.workload_prefill(wid, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dy = torch.randn(p["x"].shape, generator=g, device="cuda").to(p["x"].dtype)
+    dh = torch.randn((w.batch, w.heads, w.dstate, w.headdim), generator=g, device="cuda")
+    need = binding.load().m3_prefill_backward_workspace_size(
+        ctypes.byref(binding.dims(w.batch, w.seqlen, w.heads, 1, w.headdim, w.dstate)), w.rank)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def run():
+        binding.prefill_backward(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], w.rank, dy,
+                                 None, dh, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = backward_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank)
+    r = {"workload": w.name + " backward", "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
+         "valu_tflops": fl / (ms * 1e-3) / 1e12, "flops": fl, "workspace_bytes": need}
+    r["valu_frac"] = r["valu_tflops"] / FP32_VALU_PEAK_TFLOPS
+    log(f"backward {w.name}: {ms:.3f} ms/call, {r['tokens_per_s'] / 1e6:.2f} M tok/s, "
+        f"{r['valu_tflops']:.1f} TFLOP/s fp32 VALU ({100 * r['valu_frac']:.1f}% of {FP32_VALU_PEAK_TFLOPS})")
+    return r
+
+
 def bench_prologue(log, steps=20, warmup=3, wid=2, tokens=None, copies=16):
     """m3_prologue (QK-norm + bias on B, C; softplus / sigmoid on dt, lambda) on a workload's raw projections.
 
@@ -396,6 +439,8 @@ def main():
                 bench_long(log)
             elif item == "copy":
                 copy_probe(log)
+            elif item in ("backward1", "backward2"):
+                bench_backward(int(item[-1]), max(2, args.steps // 4), 1, log)
             elif item == "prologue":
                 bench_prologue(log, args.steps, args.warmup)
             elif item == "prologue_decode":
@@ -431,6 +476,8 @@ def main():
         # the secondary reading: one B, C per head (64x the B/C bytes)
         out["prefill_groups_eq_heads"] = {f"r{w}": bench_prefill(wid, args.steps, args.warmup, log, groups=64)
                                           for w, wid in ((1, 1), (4, 2))}
+        # the backward pass (training) on workloads 1 and 2
+        out["backward"] = {f"r{R}": bench_backward(wid, 5, 1, log) for R, wid in ((1, 1), (4, 2))}
         # the input prologue on the R 4 prefill's raw projections and on one decode step's
         out["prologue"] = {"prefill_r4": bench_prologue(log, args.steps, args.warmup),
                            "decode_step_b128": bench_prologue(log, args.steps, args.warmup, wid=3, tokens=(128,))}

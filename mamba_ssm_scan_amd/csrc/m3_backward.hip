@@ -36,19 +36,42 @@ namespace m3 {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 1024;         // threads per workgroup
-constexpr int KMAX = 64;         // rotation pairs (N <= 128)
-constexpr int PMAX = 64;         // columns (P <= 64)
-constexpr int SV = 8;            // state entries per thread
-constexpr int CK = kBackwardCheckpoint;
-constexpr int STATE = NT * SV;   // floats per stored state (covers 128 x 64)
+constexpr int NT = 1024;          // threads per workgroup
+constexpr int NW = NT / 64;       // waves
+constexpr int KMAX = 64;          // rotation pairs (N <= 128)
+constexpr int PMAX = 64;          // columns (P <= 64)
+constexpr int SV = 8;             // state entries per thread
+constexpr int BT = kBackwardCheckpoint;  // tokens per block: staged in LDS at once, one checkpoint each
+constexpr int STATE = NT * SV;    // floats per stored state (covers 128 x 64)
 
-// staged token inputs, fp32, 4 ranks per row (ranks past R are zero)
-struct Stage {
-    floatx4 B[2 * KMAX], C[2 * KMAX], Bp[2 * KMAX];  // [n][r]
-    floatx4 X[PMAX], DY[PMAX], Xp[PMAX];            // [p][r]
-    float dt, lam;
+// the 4 ranks of one row (ranks past R are zero) in the I/O type
+template <typename T>
+struct Row4;
+template <>
+struct Row4<float> {
+    floatx4 v;
+    __device__ floatx4 get() const { return v; }
+    __device__ void set(int r, float x) { v[r] = x; }
+};
+template <>
+struct Row4<bf16_t> {
+    u32x2 v;
+    __device__ floatx4 get() const {
+        return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                       __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+    }
+};
+
+// LDS image of one block: B and x of tokens t0 - 1 .. t1 - 1, C and dy of t0 .. t1 - 1
+template <typename T>
+struct Block {
+    Row4<T> B[BT + 1][2 * KMAX];
+    Row4<T> X[BT + 1][PMAX];
+    Row4<T> C[BT][2 * KMAX];
+    Row4<T> DY[BT][PMAX];
+    float dt[BT], lam[BT];
 };
 
 template <int CTRL>
@@ -76,83 +99,12 @@ __device__ __forceinline__ float wave_sum(float v) {
     v = row_sum16(v);
     return lane_read(v, 0) + lane_read(v, 16) + lane_read(v, 32) + lane_read(v, 48);
 }
-
-template <typename T>
-struct Bw {
-    const BackwardArgs& a;
-    int64_t b;
-    int h, g, K;
-    int tid, k, c;
-    __device__ Bw(const BackwardArgs& a_, int64_t bh) : a(a_) {
-        b = bh / a.H;
-        h = int(bh % a.H);
-        g = h / (a.H / a.G);
-        K = a.N / 2;
-        tid = threadIdx.x;
-        k = tid >> 4;
-        c = tid & 15;
-    }
-    __device__ const T* brow(int64_t t) const {  // B of token t (t = -1: the carry)
-        return t >= 0 ? static_cast<const T*>(a.B) + ((b * a.L + t) * a.G + g) * int64_t(a.R * a.N)
-                      : (a.carry_B ? static_cast<const T*>(a.carry_B) + (b * a.G + g) * int64_t(a.R * a.N) : nullptr);
-    }
-    __device__ const T* xrow(int64_t t) const {
-        return t >= 0 ? static_cast<const T*>(a.x) + ((b * a.L + t) * a.H + h) * int64_t(a.R * a.P)
-                      : (a.carry_x ? static_cast<const T*>(a.carry_x) + (b * a.H + h) * int64_t(a.R * a.P) : nullptr);
-    }
-    // rows [n][r] of an [R][rows] source (NULL: zeros) into dst[rows][4]
-    __device__ void put_rows(floatx4* dst, const T* src, int rows) const {
-        for (int e = tid; e < rows * a.R; e += NT) {
-            const int n = e % rows, r = e / rows;
-            reinterpret_cast<float*>(dst)[4 * n + r] = src ? Io<T>::load(src, int64_t(r) * rows + n) : 0.f;
-        }
-    }
-    __device__ void stage_bx(Stage& s, int64_t t) const {  // B_t, x_t only
-        put_rows(s.B, brow(t), a.N);
-        put_rows(s.X, xrow(t), a.P);
-        if (tid == 0 && t >= 0) {
-            const int64_t i = (b * a.L + t) * a.H + h;
-            s.dt = a.dt[i];
-            s.lam = lam_at(a.lam, i);
-        }
-    }
-    __device__ void stage_full(Stage& s, int64_t t) const {
-        stage_bx(s, t);
-        put_rows(s.C, static_cast<const T*>(a.C) + ((b * a.L + t) * a.G + g) * int64_t(a.R * a.N), a.N);
-        put_rows(s.DY, static_cast<const T*>(a.dy) + ((b * a.L + t) * a.H + h) * int64_t(a.R * a.P), a.P);
-        put_rows(s.Bp, brow(t - 1), a.N);
-        put_rows(s.Xp, xrow(t - 1), a.P);
-    }
-    __device__ float om_k() const { return k < K ? om_at(a.omega ? a.omega + int64_t(h) * K : nullptr, k) : 0.f; }
-    // u = B x^T at this thread's entries, from staged rows
-    __device__ void outer(const floatx4* Bs, const floatx4* Xs, float (&u)[2][4]) const {
-        const floatx4 b0 = Bs[2 * k], b1 = Bs[2 * k + 1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const floatx4 xv = Xs[c + 16 * j];
-            u[0][j] = b0[0] * xv[0] + b0[1] * xv[1] + b0[2] * xv[2] + b0[3] * xv[3];
-            u[1][j] = b1[0] * xv[0] + b1[1] * xv[1] + b1[2] * xv[2] + b1[3] * xv[3];
-        }
-    }
-    // one forward step on this thread's entries
-    __device__ void fwd_step(const Stage& s, float (&hs)[2][4], float (&up)[2][4], float A, float om) const {
-        float u[2][4];
-        outer(s.B, s.X, u);
-        const float d = s.dt, l = s.lam;
-        const float al = expf(d * A), gam = l * d, del = (1.f - l) * d;
-        float sn, cs;
-        sincosf(d * om, &sn, &cs);
-        const float ca = al * cs, sa = al * sn;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float g0 = hs[0][j] + del * up[0][j], g1 = hs[1][j] + del * up[1][j];
-            hs[0][j] = ca * g0 - sa * g1 + gam * u[0][j];
-            hs[1][j] = sa * g0 + ca * g1 + gam * u[1][j];
-            up[0][j] = u[0][j];
-            up[1][j] = u[1][j];
-        }
-    }
-};
+// sum over the 4 DPP rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float rows_sum4(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
 
 __device__ __forceinline__ void store8(float* p, const float (&v)[2][4]) {
     reinterpret_cast<floatx4*>(p)[0] = floatx4{v[0][0], v[0][1], v[0][2], v[0][3]};
@@ -168,45 +120,133 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[2][4]) {
 }
 
 template <typename T>
+struct Bw {
+    const BackwardArgs& a;
+    Block<T>& s;
+    int64_t b;
+    int h, g, K;
+    int tid, k, c;
+    __device__ Bw(const BackwardArgs& a_, Block<T>& s_, int64_t bh) : a(a_), s(s_) {
+        b = bh / a.H;
+        h = int(bh % a.H);
+        g = h / (a.H / a.G);
+        K = a.N / 2;
+        tid = threadIdx.x;
+        k = tid >> 4;
+        c = tid & 15;
+    }
+    __device__ const T* brow(int64_t t) const {  // B of token t (t = -1: the carry; NULL: zeros)
+        return t >= 0 ? static_cast<const T*>(a.B) + ((b * a.L + t) * a.G + g) * int64_t(a.R * a.N)
+                      : (a.carry_B ? static_cast<const T*>(a.carry_B) + (b * a.G + g) * int64_t(a.R * a.N) : nullptr);
+    }
+    __device__ const T* xrow(int64_t t) const {
+        return t >= 0 ? static_cast<const T*>(a.x) + ((b * a.L + t) * a.H + h) * int64_t(a.R * a.P)
+                      : (a.carry_x ? static_cast<const T*>(a.carry_x) + (b * a.H + h) * int64_t(a.R * a.P) : nullptr);
+    }
+    __device__ static void put(Row4<T>& dst, int r, const T* src, int64_t i) {
+        if constexpr (sizeof(T) == 4) {
+            dst.v[r] = src ? Io<T>::load(src, i) : 0.f;
+        } else {
+            reinterpret_cast<uint16_t*>(&dst.v)[r] = src ? reinterpret_cast<const uint16_t*>(src)[i] : uint16_t(0);
+        }
+    }
+    // Stage tokens [t0, t1): B, x also of t0 - 1; C, dy only when full. One pass of
+    // global loads for the whole block (its latency is paid once per block).
+    __device__ void load_block(int64_t t0, int64_t t1, bool full) {
+        const int nt = int(t1 - t0), R = a.R, N = a.N, P = a.P;
+        const int nB = (nt + 1) * R * N, nX = (nt + 1) * R * P;
+        const int nC = full ? nt * R * N : 0, nY = full ? nt * R * P : 0;
+        const int total = nB + nX + nC + nY;
+        for (int e = tid; e < total; e += NT) {
+            if (e < nB) {
+                const int j = e / (R * N), q = e % (R * N), r = q / N, n = q % N;
+                put(s.B[j][n], r, brow(t0 - 1 + j), int64_t(r) * N + n);
+            } else if (e < nB + nX) {
+                const int f = e - nB, j = f / (R * P), q = f % (R * P), r = q / P, p = q % P;
+                put(s.X[j][p], r, xrow(t0 - 1 + j), int64_t(r) * P + p);
+            } else if (e < nB + nX + nC) {
+                const int f = e - nB - nX, j = f / (R * N), q = f % (R * N), r = q / N, n = q % N;
+                put(s.C[j][n], r, static_cast<const T*>(a.C) + ((b * a.L + t0 + j) * a.G + g) * int64_t(R * N),
+                    int64_t(r) * N + n);
+            } else {
+                const int f = e - nB - nX - nC, j = f / (R * P), q = f % (R * P), r = q / P, p = q % P;
+                put(s.DY[j][p], r, static_cast<const T*>(a.dy) + ((b * a.L + t0 + j) * a.H + h) * int64_t(R * P),
+                    int64_t(r) * P + p);
+            }
+        }
+        if (tid < nt) {
+            const int64_t i = (b * a.L + t0 + tid) * a.H + h;
+            s.dt[tid] = a.dt[i];
+            s.lam[tid] = lam_at(a.lam, i);
+        }
+    }
+    __device__ float om_k() const { return k < K ? om_at(a.omega ? a.omega + int64_t(h) * K : nullptr, k) : 0.f; }
+    // u = B x^T at this thread's entries, from block token slot j
+    __device__ void outer(int j, float (&u)[2][4]) const {
+        const floatx4 b0 = s.B[j][2 * k].get(), b1 = s.B[j][2 * k + 1].get();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const floatx4 xv = s.X[j][c + 16 * q].get();
+            u[0][q] = b0[0] * xv[0] + b0[1] * xv[1] + b0[2] * xv[2] + b0[3] * xv[3];
+            u[1][q] = b1[0] * xv[0] + b1[1] * xv[1] + b1[2] * xv[2] + b1[3] * xv[3];
+        }
+    }
+    // forward step of block slot j (token t0 + j) on this thread's entries
+    __device__ void fwd_step(int j, float (&hs)[2][4], float (&up)[2][4], float A, float om) const {
+        float u[2][4];
+        outer(j + 1, u);
+        const float d = s.dt[j], l = s.lam[j];
+        const float al = expf(d * A), gam = l * d, del = (1.f - l) * d;
+        float sn, cs;
+        sincosf(d * om, &sn, &cs);
+        const float ca = al * cs, sa = al * sn;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float g0 = hs[0][q] + del * up[0][q], g1 = hs[1][q] + del * up[1][q];
+            hs[0][q] = ca * g0 - sa * g1 + gam * u[0][q];
+            hs[1][q] = sa * g0 + ca * g1 + gam * u[1][q];
+            up[0][q] = u[0][q];
+            up[1][q] = u[1][q];
+        }
+    }
+};
+
+template <typename T>
 __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
-    __shared__ Stage sIn[2];
-    __shared__ floatx4 sRed[KMAX * PMAX];  // dx partials [k][p][r]
-    __shared__ float sScal[NT / 64][4];
+    __shared__ Block<T> sBlk;
+    __shared__ floatx4 sRed[2][NW][PMAX];  // dx partials: rows of each wave summed, double-buffered
+    __shared__ float sScal[2][NW][4];
 
     const int64_t bh = blockIdx.x;
-    Bw<T> w(a, bh);
-    const int tid = w.tid, k = w.k, c = w.c, K = w.K;
+    Bw<T> w(a, sBlk, bh);
+    const int tid = w.tid, k = w.k, c = w.c, K = w.K, wave = tid >> 6;
     const int64_t L = a.L;
     const float A = a.A[w.h], Dh = a.D[w.h];
     const float om = w.om_k();
-    const int64_t nblk = (L + CK - 1) / CK;
-    float* ck = a.workspace + bh * nblk * int64_t(STATE);                           // checkpoints
-    float* scr = a.workspace + (a.b * a.H) * nblk * int64_t(STATE) + bh * int64_t(CK) * STATE;  // block states
+    const int64_t nblk = (L + BT - 1) / BT;
+    float* ck = a.workspace + bh * nblk * int64_t(STATE);                                      // checkpoints
+    float* scr = a.workspace + (a.b * a.H) * nblk * int64_t(STATE) + bh * int64_t(BT) * STATE;  // block states
 
-    // zero both staging buffers once: ranks past R, rows past N and columns past P stay zero
-    for (int e = tid; e < int(2 * sizeof(Stage) / 4); e += NT) reinterpret_cast<float*>(sIn)[e] = 0.f;
+    // zero the block image once: ranks past R, rows past N, columns past P stay zero
+    for (int e = tid; e < int(sizeof(Block<T>) / 4); e += NT) reinterpret_cast<float*>(&sBlk)[e] = 0.f;
     __syncthreads();
 
-    // ---- 1. forward over the sequence, the state stored before every block of CK tokens
+    // ---- 1. forward over the sequence, the state stored before every block
     float hs[2][4], up[2][4];
-    {
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = 2 * k + r, p = c + 16 * j;
-                hs[r][j] = (a.h0 && k < K && p < a.P) ? a.h0[(bh * a.N + n) * int64_t(a.P) + p] : 0.f;
-            }
-        w.stage_bx(sIn[1], -1);  // the carry (zeros without one)
+        for (int q = 0; q < 4; ++q) {
+            const int n = 2 * k + r, p = c + 16 * q;
+            hs[r][q] = (a.h0 && k < K && p < a.P) ? a.h0[(bh * a.N + n) * int64_t(a.P) + p] : 0.f;
+        }
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+        const int64_t t0 = blk * BT, t1 = t0 + BT < L ? t0 + BT : L;
+        store8(ck + blk * int64_t(STATE) + tid * SV, hs);
+        w.load_block(t0, t1, false);
         __syncthreads();
-        w.outer(sIn[1].B, sIn[1].X, up);
-        if (L > 0) w.stage_bx(sIn[0], 0);
-        __syncthreads();
-    }
-    for (int64_t t = 0; t < L; ++t) {
-        if (t % CK == 0) store8(ck + (t / CK) * int64_t(STATE) + tid * SV, hs);
-        if (t + 1 < L) w.stage_bx(sIn[(t + 1) & 1], t + 1);
-        w.fwd_step(sIn[t & 1], hs, up, A, om);
+        w.outer(0, up);
+        for (int j = 0; j < int(t1 - t0); ++j) w.fwd_step(j, hs, up, A, om);
         __syncthreads();
     }
 
@@ -215,82 +255,77 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = 2 * k + r, p = c + 16 * j;
-            ad[r][j] = (a.dh_out && k < K && p < a.P) ? a.dh_out[(bh * a.N + n) * int64_t(a.P) + p] : 0.f;
-            e[r][j] = 0.f;
+        for (int q = 0; q < 4; ++q) {
+            const int n = 2 * k + r, p = c + 16 * q;
+            ad[r][q] = (a.dh_out && k < K && p < a.P) ? a.dh_out[(bh * a.N + n) * int64_t(a.P) + p] : 0.f;
+            e[r][q] = 0.f;
         }
     float dA_acc = 0.f, dom_acc = 0.f, dD_acc = 0.f;
-    const int ro = tid >> 2, part = tid & 3;  // reducer: output (p, r) = (ro / 4, ro % 4), k quarter
+    const int ro = tid >> 2, part = tid & 3;  // reducer: output (p, r) = (ro / 4, ro % 4), waves part*4 .. +3
     const int rp = ro >> 2, rr = ro & 3;
     const bool red_ok = rp < a.P && rr < a.R;
 
     for (int64_t blk = nblk - 1; blk >= 0; --blk) {
-        const int64_t t0 = blk * CK, t1 = t0 + CK < L ? t0 + CK : L;
-        // 2a. this block's states, from its checkpoint
+        const int64_t t0 = blk * BT, t1 = t0 + BT < L ? t0 + BT : L;
+        const int nt = int(t1 - t0);
+        // 2a. this block's inputs, and its states from the checkpoint
+        w.load_block(t0, t1, true);
         load8(ck + blk * int64_t(STATE) + tid * SV, hs);
-        w.stage_bx(sIn[1], t0 - 1);
         __syncthreads();
-        w.outer(sIn[1].B, sIn[1].X, up);
-        w.stage_bx(sIn[0], t0);
-        __syncthreads();
-        for (int64_t t = t0; t < t1; ++t) {
-            if (t + 1 < t1) w.stage_bx(sIn[(t + 1 - t0) & 1], t + 1);
-            w.fwd_step(sIn[(t - t0) & 1], hs, up, A, om);
-            store8(scr + (t - t0) * int64_t(STATE) + tid * SV, hs);
-            __syncthreads();
+        w.outer(0, up);
+        for (int j = 0; j < nt; ++j) {
+            w.fwd_step(j, hs, up, A, om);
+            store8(scr + j * int64_t(STATE) + tid * SV, hs);  // read back by this thread only
         }
-        // 2b. walk the block back
-        w.stage_full(sIn[(t1 - 1) & 1], t1 - 1);
-        __syncthreads();
-        for (int64_t t = t1 - 1; t >= t0; --t) {
-            const Stage& s = sIn[t & 1];
+        // 2b. walk the block back (one barrier per token: partials double-buffered)
+        for (int j = nt - 1; j >= 0; --j) {
+            const int64_t t = t0 + j;
+            const int par = j & 1;
             float ht[2][4], u[2][4], uq[2][4];
-            load8(scr + (t - t0) * int64_t(STATE) + tid * SV, ht);
-            w.outer(s.B, s.X, u);
-            w.outer(s.Bp, s.Xp, uq);
-            const float d = s.dt, l = s.lam;
+            load8(scr + j * int64_t(STATE) + tid * SV, ht);
+            w.outer(j + 1, u);
+            w.outer(j, uq);
+            const float d = sBlk.dt[j], l = sBlk.lam[j];
             const float al = expf(d * A), gam = l * d, del = (1.f - l) * d;
             float sn, cs;
             sincosf(d * om, &sn, &cs);
-            const floatx4 c0 = s.C[2 * k], c1 = s.C[2 * k + 1];
-            const floatx4 b0 = s.B[2 * k], b1 = s.B[2 * k + 1];
+            const floatx4 c0 = sBlk.C[j][2 * k].get(), c1 = sBlk.C[j][2 * k + 1].get();
+            const floatx4 b0 = sBlk.B[j + 1][2 * k].get(), b1 = sBlk.B[j + 1][2 * k + 1].get();
             float dc0[4] = {0.f, 0.f, 0.f, 0.f}, dc1[4] = {0.f, 0.f, 0.f, 0.f};
             float db0[4] = {0.f, 0.f, 0.f, 0.f}, db1[4] = {0.f, 0.f, 0.f, 0.f};
+            float dxp[4][4];
             float s_al = 0.f, s_ga = 0.f, s_de = 0.f, dth = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int p = c + 16 * j;
-                const floatx4 dy = s.DY[p], xv = s.X[p];
+            for (int q = 0; q < 4; ++q) {
+                const int p = c + 16 * q;
+                const floatx4 dy = sBlk.DY[j][p].get(), xv = sBlk.X[j + 1][p].get();
                 // a += C dy^T
-                ad[0][j] += c0[0] * dy[0] + c0[1] * dy[1] + c0[2] * dy[2] + c0[3] * dy[3];
-                ad[1][j] += c1[0] * dy[0] + c1[1] * dy[1] + c1[2] * dy[2] + c1[3] * dy[3];
+                ad[0][q] += c0[0] * dy[0] + c0[1] * dy[1] + c0[2] * dy[2] + c0[3] * dy[3];
+                ad[1][q] += c1[0] * dy[0] + c1[1] * dy[1] + c1[2] * dy[2] + c1[3] * dy[3];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    dc0[r] += ht[0][j] * dy[r];
-                    dc1[r] += ht[1][j] * dy[r];
+                    dc0[r] += ht[0][q] * dy[r];
+                    dc1[r] += ht[1][q] * dy[r];
                 }
-                const float w0 = ht[0][j] - gam * u[0][j], w1 = ht[1][j] - gam * u[1][j];
-                s_al += w0 * ad[0][j] + w1 * ad[1][j];
-                dth += w0 * ad[1][j] - w1 * ad[0][j];
-                s_ga += u[0][j] * ad[0][j] + u[1][j] * ad[1][j];
+                const float w0 = ht[0][q] - gam * u[0][q], w1 = ht[1][q] - gam * u[1][q];
+                s_al += w0 * ad[0][q] + w1 * ad[1][q];
+                dth += w0 * ad[1][q] - w1 * ad[0][q];
+                s_ga += u[0][q] * ad[0][q] + u[1][q] * ad[1][q];
                 // dg = alpha Rot^T a
-                const float g0 = al * (cs * ad[0][j] + sn * ad[1][j]);
-                const float g1 = al * (cs * ad[1][j] - sn * ad[0][j]);
-                const float du0 = gam * ad[0][j] + e[0][j], du1 = gam * ad[1][j] + e[1][j];
-                s_de += uq[0][j] * g0 + uq[1][j] * g1;
+                const float g0 = al * (cs * ad[0][q] + sn * ad[1][q]);
+                const float g1 = al * (cs * ad[1][q] - sn * ad[0][q]);
+                const float du0 = gam * ad[0][q] + e[0][q], du1 = gam * ad[1][q] + e[1][q];
+                s_de += uq[0][q] * g0 + uq[1][q] * g1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     db0[r] += du0 * xv[r];
                     db1[r] += du1 * xv[r];
+                    dxp[q][r] = du0 * b0[r] + du1 * b1[r];  // dx over this thread's two rows
                 }
-                // dx partial over this thread's two rows
-                sRed[k * PMAX + p] = floatx4{du0 * b0[0] + du1 * b1[0], du0 * b0[1] + du1 * b1[1],
-                                             du0 * b0[2] + du1 * b1[2], du0 * b0[3] + du1 * b1[3]};
-                ad[0][j] = g0;
-                ad[1][j] = g1;
-                e[0][j] = del * g0;
-                e[1][j] = del * g1;
+                ad[0][q] = g0;
+                ad[1][q] = g1;
+                e[0][q] = del * g0;
+                e[1][q] = del * g1;
             }
             // column reductions inside the 16-lane row: dC, dB, the pair's angle
             dth = row_sum16(dth);
@@ -310,46 +345,52 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
             }
             if (c == 0) dom_acc += d * dth;
             const float s_om = (c == 0) ? om * dth : 0.f;
+            // dx: the wave's four row pairs summed, one partial per wave and column
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                floatx4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = rows_sum4(dxp[q][r]);
+                if ((tid & 63) < 16) sRed[par][wave][c + 16 * q] = v;
+            }
             {
                 const float v0 = wave_sum(s_al), v1 = wave_sum(s_ga), v2 = wave_sum(s_de), v3 = wave_sum(s_om);
                 if ((tid & 63) == 0) {
-                    sScal[tid >> 6][0] = v0;
-                    sScal[tid >> 6][1] = v1;
-                    sScal[tid >> 6][2] = v2;
-                    sScal[tid >> 6][3] = v3;
+                    sScal[par][wave][0] = v0;
+                    sScal[par][wave][1] = v1;
+                    sScal[par][wave][2] = v2;
+                    sScal[par][wave][3] = v3;
                 }
             }
             __syncthreads();
-            // row reduction of dx through LDS: 4 lanes per (p, r), 16 pairs each
             {
                 float v = 0.f;
                 if (red_ok) {
-                    const int kb = 16 * part, ke = kb + 16 < K ? kb + 16 : K;
-                    for (int kk = kb; kk < ke; ++kk) v += sRed[kk * PMAX + rp][rr];
+#pragma unroll
+                    for (int q = 0; q < NW / 4; ++q) v += sRed[par][part * (NW / 4) + q][rp][rr];
                 }
                 v = quad_sum(v);
                 if (red_ok && part == 0) {
-                    const float dyv = s.DY[rp][rr], xv = s.X[rp][rr];
+                    const float dyv = sBlk.DY[j][rp].get()[rr], xv = sBlk.X[j + 1][rp].get()[rr];
                     a.dx[((w.b * L + t) * a.H + w.h) * int64_t(a.R * a.P) + rr * a.P + rp] = v + Dh * dyv;
                     dD_acc += dyv * xv;
                 }
             }
             if (tid == 0) {
                 float sa = 0.f, sg = 0.f, sd = 0.f, so = 0.f;
-                for (int q = 0; q < NT / 64; ++q) {
-                    sa += sScal[q][0];
-                    sg += sScal[q][1];
-                    sd += sScal[q][2];
-                    so += sScal[q][3];
+                for (int q = 0; q < NW; ++q) {
+                    sa += sScal[par][q][0];
+                    sg += sScal[par][q][1];
+                    sd += sScal[par][q][2];
+                    so += sScal[par][q][3];
                 }
                 const int64_t i = (w.b * L + t) * a.H + w.h;
                 a.ddt[i] = A * sa + so + l * sg + (1.f - l) * sd;
                 if (a.dlam) a.dlam[i] = d * (sg - sd);
                 dA_acc += d * sa;
             }
-            if (t > t0) w.stage_full(sIn[(t - 1) & 1], t - 1);
-            __syncthreads();
         }
+        __syncthreads();  // the reducers are done with this block's image before the next load
     }
 
     // ---- 3. what is left: dh0, the carry, and the summed parameter gradients
@@ -357,26 +398,24 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int p = c + 16 * j;
-                if (p < a.P) a.dh0[(bh * a.N + 2 * k + r) * int64_t(a.P) + p] = ad[r][j];
+            for (int q = 0; q < 4; ++q) {
+                const int p = c + 16 * q;
+                if (p < a.P) a.dh0[(bh * a.N + 2 * k + r) * int64_t(a.P) + p] = ad[r][q];
             }
     if (a.dcarry_B) {
-        // du_0 = e; the carry's B and x are in the staging buffer of token 0 (Bp, Xp)
-        const Stage& s = sIn[0];
-        const floatx4 b0 = s.Bp[2 * k], b1 = s.Bp[2 * k + 1];
+        // du_0 = e; the carry's B and x are in block slot 0 of the first block (still staged)
+        const floatx4 b0 = sBlk.B[0][2 * k].get(), b1 = sBlk.B[0][2 * k + 1].get();
         float db0[4] = {0.f, 0.f, 0.f, 0.f}, db1[4] = {0.f, 0.f, 0.f, 0.f};
+        float dxp[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = c + 16 * j;
-            const floatx4 xv = s.Xp[p];
+        for (int q = 0; q < 4; ++q) {
+            const floatx4 xv = sBlk.X[0][c + 16 * q].get();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                db0[r] += e[0][j] * xv[r];
-                db1[r] += e[1][j] * xv[r];
+                db0[r] += e[0][q] * xv[r];
+                db1[r] += e[1][q] * xv[r];
+                dxp[q][r] = e[0][q] * b0[r] + e[1][q] * b1[r];
             }
-            sRed[k * PMAX + p] = floatx4{e[0][j] * b0[0] + e[1][j] * b1[0], e[0][j] * b0[1] + e[1][j] * b1[1],
-                                         e[0][j] * b0[2] + e[1][j] * b1[2], e[0][j] * b0[3] + e[1][j] * b1[3]};
         }
         if (k < K) {
             const int64_t rowb = (w.b * a.G + w.g) * int64_t(a.R * a.N);
@@ -389,11 +428,18 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
                 }
             }
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            floatx4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = rows_sum4(dxp[q][r]);
+            if ((tid & 63) < 16) sRed[0][wave][c + 16 * q] = v;
+        }
         __syncthreads();
         float v = 0.f;
         if (red_ok) {
-            const int kb = 16 * part, ke = kb + 16 < K ? kb + 16 : K;
-            for (int kk = kb; kk < ke; ++kk) v += sRed[kk * PMAX + rp][rr];
+#pragma unroll
+            for (int q = 0; q < NW / 4; ++q) v += sRed[0][part * (NW / 4) + q][rp][rr];
         }
         v = quad_sum(v);
         if (red_ok && part == 0) a.dcarry_x[(w.b * a.H + w.h) * int64_t(a.R * a.P) + rr * a.P + rp] = v;
@@ -419,8 +465,8 @@ struct Z0 {
 };
 
 size_t backward_workspace_bytes(int64_t b, int32_t H, int64_t L) {
-    const int64_t nblk = (L + CK - 1) / CK;
-    return size_t(b) * size_t(H) * size_t(nblk + CK) * STATE * sizeof(float);
+    const int64_t nblk = (L + BT - 1) / BT;
+    return size_t(b) * size_t(H) * size_t(nblk + BT) * STATE * sizeof(float);
 }
 
 bool backward_supported(int32_t P, int32_t N, int32_t R) { return N <= 2 * KMAX && P <= PMAX && R <= 4; }

@@ -108,7 +108,7 @@ struct BackwardArgs {
 };
 
 // Tokens between the backward's state checkpoints, and its workspace size.
-constexpr int kBackwardCheckpoint = 32;
+constexpr int kBackwardCheckpoint = 16;
 size_t backward_workspace_bytes(int64_t b, int32_t H, int64_t L);
 bool backward_supported(int32_t P, int32_t N, int32_t R);
 
