@@ -19,12 +19,15 @@
 // One workgroup of 1024 threads per (b, h). Thread (k, c) = (tid / 16, tid % 16)
 // holds state rows 2k, 2k+1 (one rotation pair) at columns c + 16 j, j < 4:
 // reductions over the columns (dC, dB, the pair's angle) stay inside a 16-lane
-// DPP row; the one over rows (dx) goes through LDS. The token's B, C, x, dy
-// (and the previous token's B, x) are staged in LDS as fp32, [row][4 ranks].
+// DPP row; the one over rows (dx) goes through LDS. A block of tokens' B, C,
+// x, dy (and the previous token's B, x) is staged in LDS in the I/O type, one
+// LDS word per row holding its RK ranks (RK = R rounded up to 1, 2 or 4, a
+// compile-time count, so the rank loops do no padded work).
 //
-// h_t is needed in reverse order: a first pass stores the state every 32
-// tokens in the workspace; each 32-token block is then run forward again from
-// its checkpoint, keeping its states in a per-(b, h) scratch, and walked back.
+// h_t is needed in reverse order: a first pass stores the state before every
+// block of kBackwardCheckpoint tokens in the workspace; each block is then run
+// forward again from its checkpoint, keeping its states in a per-(b, h)
+// scratch, and walked back.
 // Gradients summed over several workgroups (dB and dC over the heads of a
 // group, dA, domega, dD over batch and tokens, dcarry_B) are added with device
 // atomics into arrays the launcher clears first; their summation order is not
@@ -46,31 +49,60 @@ constexpr int SV = 8;             // state entries per thread
 constexpr int BT = kBackwardCheckpoint;  // tokens per block: staged in LDS at once, one checkpoint each
 constexpr int STATE = NT * SV;    // floats per stored state (covers 128 x 64)
 
-// the 4 ranks of one row (ranks past R are zero) in the I/O type
-template <typename T>
-struct Row4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// an LDS word of 2 .. 16 bytes, read and written as one access
+template <int BYTES>
+struct Word;
 template <>
-struct Row4<float> {
-    floatx4 v;
-    __device__ floatx4 get() const { return v; }
-    __device__ void set(int r, float x) { v[r] = x; }
+struct Word<2> {
+    typedef uint16_t type;
 };
 template <>
-struct Row4<bf16_t> {
-    u32x2 v;
-    __device__ floatx4 get() const {
-        return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
-                       __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+struct Word<4> {
+    typedef uint32_t type;
+};
+template <>
+struct Word<8> {
+    typedef u32x2 type;
+};
+template <>
+struct Word<16> {
+    typedef u32x4 type;
+};
+
+template <int RK>
+struct Vr {
+    float f[RK];
+};
+
+// the RK ranks of one row (ranks past R are zero) in the I/O type
+template <typename T, int RK>
+struct Row {
+    typedef typename Word<int(sizeof(T)) * RK>::type W;
+    W w;
+    __device__ Vr<RK> get() const {
+        const W x = w;
+        Vr<RK> out;
+        if constexpr (sizeof(T) == 4) {
+            __builtin_memcpy(out.f, &x, sizeof(x));
+        } else {
+            uint16_t u[RK];
+            __builtin_memcpy(u, &x, sizeof(x));
+#pragma unroll
+            for (int r = 0; r < RK; ++r) out.f[r] = __uint_as_float(uint32_t(u[r]) << 16);
+        }
+        return out;
     }
 };
 
 // LDS image of one block: B and x of tokens t0 - 1 .. t1 - 1, C and dy of t0 .. t1 - 1
-template <typename T>
+template <typename T, int RK>
 struct Block {
-    Row4<T> B[BT + 1][2 * KMAX];
-    Row4<T> X[BT + 1][PMAX];
-    Row4<T> C[BT][2 * KMAX];
-    Row4<T> DY[BT][PMAX];
+    Row<T, RK> B[BT + 1][2 * KMAX];
+    Row<T, RK> X[BT + 1][PMAX];
+    Row<T, RK> C[BT][2 * KMAX];
+    Row<T, RK> DY[BT][PMAX];
     float dt[BT], lam[BT];
 };
 
@@ -119,14 +151,14 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[2][4]) {
     }
 }
 
-template <typename T>
+template <typename T, int RK>
 struct Bw {
     const BackwardArgs& a;
-    Block<T>& s;
+    Block<T, RK>& s;
     int64_t b;
     int h, g, K;
     int tid, k, c;
-    __device__ Bw(const BackwardArgs& a_, Block<T>& s_, int64_t bh) : a(a_), s(s_) {
+    __device__ Bw(const BackwardArgs& a_, Block<T, RK>& s_, int64_t bh) : a(a_), s(s_) {
         b = bh / a.H;
         h = int(bh % a.H);
         g = h / (a.H / a.G);
@@ -143,11 +175,11 @@ struct Bw {
         return t >= 0 ? static_cast<const T*>(a.x) + ((b * a.L + t) * a.H + h) * int64_t(a.R * a.P)
                       : (a.carry_x ? static_cast<const T*>(a.carry_x) + (b * a.H + h) * int64_t(a.R * a.P) : nullptr);
     }
-    __device__ static void put(Row4<T>& dst, int r, const T* src, int64_t i) {
+    __device__ static void put(Row<T, RK>& dst, int r, const T* src, int64_t i) {
         if constexpr (sizeof(T) == 4) {
-            dst.v[r] = src ? Io<T>::load(src, i) : 0.f;
+            reinterpret_cast<float*>(&dst.w)[r] = src ? Io<T>::load(src, i) : 0.f;
         } else {
-            reinterpret_cast<uint16_t*>(&dst.v)[r] = src ? reinterpret_cast<const uint16_t*>(src)[i] : uint16_t(0);
+            reinterpret_cast<uint16_t*>(&dst.w)[r] = src ? reinterpret_cast<const uint16_t*>(src)[i] : uint16_t(0);
         }
     }
     // Stage tokens [t0, t1): B, x also of t0 - 1; C, dy only when full. One pass of
@@ -183,12 +215,18 @@ struct Bw {
     __device__ float om_k() const { return k < K ? om_at(a.omega ? a.omega + int64_t(h) * K : nullptr, k) : 0.f; }
     // u = B x^T at this thread's entries, from block token slot j
     __device__ void outer(int j, float (&u)[2][4]) const {
-        const floatx4 b0 = s.B[j][2 * k].get(), b1 = s.B[j][2 * k + 1].get();
+        const Vr<RK> b0 = s.B[j][2 * k].get(), b1 = s.B[j][2 * k + 1].get();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const floatx4 xv = s.X[j][c + 16 * q].get();
-            u[0][q] = b0[0] * xv[0] + b0[1] * xv[1] + b0[2] * xv[2] + b0[3] * xv[3];
-            u[1][q] = b1[0] * xv[0] + b1[1] * xv[1] + b1[2] * xv[2] + b1[3] * xv[3];
+            const Vr<RK> xv = s.X[j][c + 16 * q].get();
+            float s0 = b0.f[0] * xv.f[0], s1 = b1.f[0] * xv.f[0];
+#pragma unroll
+            for (int r = 1; r < RK; ++r) {
+                s0 += b0.f[r] * xv.f[r];
+                s1 += b1.f[r] * xv.f[r];
+            }
+            u[0][q] = s0;
+            u[1][q] = s1;
         }
     }
     // forward step of block slot j (token t0 + j) on this thread's entries
@@ -211,14 +249,15 @@ struct Bw {
     }
 };
 
-template <typename T>
+template <typename T, int RK>
 __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
-    __shared__ Block<T> sBlk;
+    static_assert(sizeof(Block<T, RK>) % 4 == 0, "the block image is cleared in 4-byte words");
+    __shared__ Block<T, RK> sBlk;
     __shared__ floatx4 sRed[2][NW][PMAX];  // dx partials: rows of each wave summed, double-buffered
     __shared__ float sScal[2][NW][4];
 
     const int64_t bh = blockIdx.x;
-    Bw<T> w(a, sBlk, bh);
+    Bw<T, RK> w(a, sBlk, bh);
     const int tid = w.tid, k = w.k, c = w.c, K = w.K, wave = tid >> 6;
     const int64_t L = a.L;
     const float A = a.A[w.h], Dh = a.D[w.h];
@@ -228,7 +267,7 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
     float* scr = a.workspace + (a.b * a.H) * nblk * int64_t(STATE) + bh * int64_t(BT) * STATE;  // block states
 
     // zero the block image once: ranks past R, rows past N, columns past P stay zero
-    for (int e = tid; e < int(sizeof(Block<T>) / 4); e += NT) reinterpret_cast<float*>(&sBlk)[e] = 0.f;
+    for (int e = tid; e < int(sizeof(Block<T, RK>) / 4); e += NT) reinterpret_cast<float*>(&sBlk)[e] = 0.f;
     __syncthreads();
 
     // ---- 1. forward over the sequence, the state stored before every block
@@ -277,35 +316,41 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
             w.fwd_step(j, hs, up, A, om);
             store8(scr + j * int64_t(STATE) + tid * SV, hs);  // read back by this thread only
         }
-        // 2b. walk the block back (one barrier per token: partials double-buffered)
+        // 2b. walk the block back (one barrier per token: partials double-buffered);
+        // u of token t - 1 is u of the next (earlier) step
+        float u[2][4];
+        w.outer(nt, u);
         for (int j = nt - 1; j >= 0; --j) {
             const int64_t t = t0 + j;
             const int par = j & 1;
-            float ht[2][4], u[2][4], uq[2][4];
+            float ht[2][4], uq[2][4];
             load8(scr + j * int64_t(STATE) + tid * SV, ht);
-            w.outer(j + 1, u);
             w.outer(j, uq);
             const float d = sBlk.dt[j], l = sBlk.lam[j];
             const float al = expf(d * A), gam = l * d, del = (1.f - l) * d;
             float sn, cs;
             sincosf(d * om, &sn, &cs);
-            const floatx4 c0 = sBlk.C[j][2 * k].get(), c1 = sBlk.C[j][2 * k + 1].get();
-            const floatx4 b0 = sBlk.B[j + 1][2 * k].get(), b1 = sBlk.B[j + 1][2 * k + 1].get();
-            float dc0[4] = {0.f, 0.f, 0.f, 0.f}, dc1[4] = {0.f, 0.f, 0.f, 0.f};
-            float db0[4] = {0.f, 0.f, 0.f, 0.f}, db1[4] = {0.f, 0.f, 0.f, 0.f};
-            float dxp[4][4];
+            const Vr<RK> c0 = sBlk.C[j][2 * k].get(), c1 = sBlk.C[j][2 * k + 1].get();
+            const Vr<RK> b0 = sBlk.B[j + 1][2 * k].get(), b1 = sBlk.B[j + 1][2 * k + 1].get();
+            float dc0[RK], dc1[RK], db0[RK], db1[RK];
+#pragma unroll
+            for (int r = 0; r < RK; ++r) dc0[r] = dc1[r] = db0[r] = db1[r] = 0.f;
+            float dxp[4][RK];
             float s_al = 0.f, s_ga = 0.f, s_de = 0.f, dth = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int p = c + 16 * q;
-                const floatx4 dy = sBlk.DY[j][p].get(), xv = sBlk.X[j + 1][p].get();
+                const Vr<RK> dy = sBlk.DY[j][p].get(), xv = sBlk.X[j + 1][p].get();
                 // a += C dy^T
-                ad[0][q] += c0[0] * dy[0] + c0[1] * dy[1] + c0[2] * dy[2] + c0[3] * dy[3];
-                ad[1][q] += c1[0] * dy[0] + c1[1] * dy[1] + c1[2] * dy[2] + c1[3] * dy[3];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    dc0[r] += ht[0][q] * dy[r];
-                    dc1[r] += ht[1][q] * dy[r];
+                for (int r = 0; r < RK; ++r) {
+                    ad[0][q] += c0.f[r] * dy.f[r];
+                    ad[1][q] += c1.f[r] * dy.f[r];
+                }
+#pragma unroll
+                for (int r = 0; r < RK; ++r) {
+                    dc0[r] += ht[0][q] * dy.f[r];
+                    dc1[r] += ht[1][q] * dy.f[r];
                 }
                 const float w0 = ht[0][q] - gam * u[0][q], w1 = ht[1][q] - gam * u[1][q];
                 s_al += w0 * ad[0][q] + w1 * ad[1][q];
@@ -317,22 +362,24 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
                 const float du0 = gam * ad[0][q] + e[0][q], du1 = gam * ad[1][q] + e[1][q];
                 s_de += uq[0][q] * g0 + uq[1][q] * g1;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    db0[r] += du0 * xv[r];
-                    db1[r] += du1 * xv[r];
-                    dxp[q][r] = du0 * b0[r] + du1 * b1[r];  // dx over this thread's two rows
+                for (int r = 0; r < RK; ++r) {
+                    db0[r] += du0 * xv.f[r];
+                    db1[r] += du1 * xv.f[r];
+                    dxp[q][r] = du0 * b0.f[r] + du1 * b1.f[r];  // dx over this thread's two rows
                 }
                 ad[0][q] = g0;
                 ad[1][q] = g1;
                 e[0][q] = del * g0;
                 e[1][q] = del * g1;
+                u[0][q] = uq[0][q];
+                u[1][q] = uq[1][q];
             }
             // column reductions inside the 16-lane row: dC, dB, the pair's angle
             dth = row_sum16(dth);
             if (k < K) {
                 const int64_t rowb = ((w.b * L + t) * a.G + w.g) * int64_t(a.R * a.N);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 0; r < RK; ++r) {
                     const float v0 = row_sum16(dc0[r]), v1 = row_sum16(dc1[r]);
                     const float u0 = row_sum16(db0[r]), u1 = row_sum16(db1[r]);
                     if (c == 0 && r < a.R) {
@@ -348,9 +395,9 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
             // dx: the wave's four row pairs summed, one partial per wave and column
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                floatx4 v;
+                floatx4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = rows_sum4(dxp[q][r]);
+                for (int r = 0; r < RK; ++r) v[r] = rows_sum4(dxp[q][r]);
                 if ((tid & 63) < 16) sRed[par][wave][c + 16 * q] = v;
             }
             {
@@ -371,7 +418,7 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
                 }
                 v = quad_sum(v);
                 if (red_ok && part == 0) {
-                    const float dyv = sBlk.DY[j][rp].get()[rr], xv = sBlk.X[j + 1][rp].get()[rr];
+                    const float dyv = sBlk.DY[j][rp].get().f[rr], xv = sBlk.X[j + 1][rp].get().f[rr];
                     a.dx[((w.b * L + t) * a.H + w.h) * int64_t(a.R * a.P) + rr * a.P + rp] = v + Dh * dyv;
                     dD_acc += dyv * xv;
                 }
@@ -404,23 +451,25 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
             }
     if (a.dcarry_B) {
         // du_0 = e; the carry's B and x are in block slot 0 of the first block (still staged)
-        const floatx4 b0 = sBlk.B[0][2 * k].get(), b1 = sBlk.B[0][2 * k + 1].get();
-        float db0[4] = {0.f, 0.f, 0.f, 0.f}, db1[4] = {0.f, 0.f, 0.f, 0.f};
-        float dxp[4][4];
+        const Vr<RK> b0 = sBlk.B[0][2 * k].get(), b1 = sBlk.B[0][2 * k + 1].get();
+        float db0[RK], db1[RK];
+#pragma unroll
+        for (int r = 0; r < RK; ++r) db0[r] = db1[r] = 0.f;
+        float dxp[4][RK];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const floatx4 xv = sBlk.X[0][c + 16 * q].get();
+            const Vr<RK> xv = sBlk.X[0][c + 16 * q].get();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                db0[r] += e[0][q] * xv[r];
-                db1[r] += e[1][q] * xv[r];
-                dxp[q][r] = e[0][q] * b0[r] + e[1][q] * b1[r];
+            for (int r = 0; r < RK; ++r) {
+                db0[r] += e[0][q] * xv.f[r];
+                db1[r] += e[1][q] * xv.f[r];
+                dxp[q][r] = e[0][q] * b0.f[r] + e[1][q] * b1.f[r];
             }
         }
         if (k < K) {
             const int64_t rowb = (w.b * a.G + w.g) * int64_t(a.R * a.N);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < RK; ++r) {
                 const float v0 = row_sum16(db0[r]), v1 = row_sum16(db1[r]);
                 if (c == 0 && r < a.R) {
                     atomicAdd(a.dcarry_B + rowb + r * a.N + 2 * k, v0);
@@ -430,9 +479,9 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            floatx4 v;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = rows_sum4(dxp[q][r]);
+            for (int r = 0; r < RK; ++r) v[r] = rows_sum4(dxp[q][r]);
             if ((tid & 63) < 16) sRed[0][wave][c + 16 * q] = v;
         }
         __syncthreads();
@@ -449,11 +498,16 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
     if (red_ok && part == 0) atomicAdd(a.dD + w.h, dD_acc);
 }
 
+template <typename T, int RK>
+hipError_t launch_rk(const BackwardArgs& a) {
+    const int64_t nbh = a.b * a.H;
+    hipLaunchKernelGGL((backward_kernel<T, RK>), dim3(unsigned(nbh)), dim3(NT), 0, a.stream, a);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_t(const BackwardArgs& a) {
-    const int64_t nbh = a.b * a.H;
-    hipLaunchKernelGGL(backward_kernel<T>, dim3(unsigned(nbh)), dim3(NT), 0, a.stream, a);
-    return hipGetLastError();
+    return a.R == 1 ? launch_rk<T, 1>(a) : a.R == 2 ? launch_rk<T, 2>(a) : launch_rk<T, 4>(a);
 }
 
 }  // namespace
