@@ -83,14 +83,19 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(wid, steps, warmup, log, special="", groups=1):
+def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, rank=None):
     """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
 
     groups: 1 (B, C shared by all heads, the primary reading) or H (one B, C per head).
+    dstate / rank: the workload's shape with a larger state or rank (N 256, R 8: the generic kernel).
     """
+    import dataclasses
     import torch
     from mamba_ssm_scan_amd import binding, inputs
     w = inputs.WORKLOADS[wid]
+    base = w.name
+    if dstate is not None or rank is not None:
+        w = dataclasses.replace(w, dstate=dstate or w.dstate, rank=rank or w.rank)
     G = groups
     copies = [inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=G, headdim=w.headdim,
                                   dstate=w.dstate, rank=w.rank, io_dtype=w.io_dtype, dist=w.dist, wid=wid,
@@ -122,7 +127,9 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1):
     if no_lam:
         by -= w.batch * w.seqlen * w.heads * 4
     fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
-    name = w.name + (f" ({special})" if special else "") + (f" G={G}" if G != 1 else "")
+    name = base + (f" ({special})" if special else "") + (f" G={G}" if G != 1 else "")
+    if w.dstate != inputs.WORKLOADS[wid].dstate or w.rank != inputs.WORKLOADS[wid].rank:
+        name += f" with N={w.dstate} R={w.rank}"
     r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
          "bytes": by, "flops": fl, "path": "mfma" if plan.path == binding.M3_PATH_MFMA else "generic",
@@ -429,6 +436,10 @@ def main():
                 bench_prefill(1, args.steps, args.warmup, log)
             elif item == "prefill2":
                 bench_prefill(2, args.steps, args.warmup, log)
+            elif item == "prefill1_n256":
+                bench_prefill(1, args.steps, args.warmup, log, dstate=256)
+            elif item == "prefill2_r8":
+                bench_prefill(2, args.steps, args.warmup, log, rank=8)
             elif item in ("prefill1_g64", "prefill2_g64"):
                 bench_prefill(int(item[7]), args.steps, args.warmup, log, groups=64)
             elif item.startswith("prefill1_"):
@@ -476,6 +487,9 @@ def main():
         # the secondary reading: one B, C per head (64x the B/C bytes)
         out["prefill_groups_eq_heads"] = {f"r{w}": bench_prefill(wid, args.steps, args.warmup, log, groups=64)
                                           for w, wid in ((1, 1), (4, 2))}
+        # larger state / rank on the same token shapes (the generic fp32 kernel)
+        out["prefill_larger_sizes"] = {"n256_r1": bench_prefill(1, 3, 1, log, dstate=256),
+                                       "n128_r8": bench_prefill(2, 3, 1, log, rank=8)}
         # the backward pass (training) on workloads 1 and 2
         out["backward"] = {f"r{R}": bench_backward(wid, 5, 1, log) for R, wid in ((1, 1), (4, 2))}
         # the input prologue on the R 4 prefill's raw projections and on one decode step's

@@ -1,7 +1,7 @@
 """GPU parity of m3_prefill_backward against the fp64 oracle backward (oracle/backward.py).
 
 Both sides read the same input bytes and the same dy / dh_out. The HIP path
-computes in fp32 (its states recomputed from checkpoints every 32 tokens); the
+computes in fp32 (its states recomputed from checkpoints every 16 tokens); the
 oracle differentiates the plain fp64 loop (pinned by finite differences in
 tests/test_backward_pins.py). Bars: max-relative error per gradient tensor,
 per (batch, head) slice for the token- and state-shaped ones (x, h0, dt,
