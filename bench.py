@@ -132,7 +132,7 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
         name += f" with N={w.dstate} R={w.rank}"
     r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
-         "bytes": by, "flops": fl, "path": "mfma" if plan.path == binding.M3_PATH_MFMA else "generic",
+         "bytes": by, "flops": fl, "path": {binding.M3_PATH_MFMA: "mfma", binding.M3_PATH_SCAN: "scan"}.get(plan.path, "generic"),
          "segments": plan.segments}
     r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
     r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS

@@ -83,7 +83,12 @@ typedef struct m3_plan {
     size_t workspace_bytes;  /* what m3_prefill needs (0 allowed when this is 0) */
 } m3_plan;
 
-enum { M3_PATH_GENERIC = 0, M3_PATH_MFMA = 1 };
+/* GENERIC: chunked, fp32 arithmetic, any sizes (the fp32 I/O path).
+ * MFMA:    chunked on matrix cores, bf16 I/O, N 128, P 64, R 1, 2, 4, chunk <= 64.
+ * SCAN:    token-by-token walk with the state in registers and the rank
+ *          contractions on matrix cores, bf16 I/O, N and P multiples of 16 with
+ *          N <= 256, P <= 64, R <= 8, where MFMA does not apply (chunk unused). */
+enum { M3_PATH_GENERIC = 0, M3_PATH_MFMA = 1, M3_PATH_SCAN = 2 };
 
 /*
  * m3_prefill -- chunked evaluation of the recurrence over L tokens.

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libm3.so")
 
 M3_F32, M3_BF16 = 0, 1
-M3_PATH_GENERIC, M3_PATH_MFMA = 0, 1
+M3_PATH_GENERIC, M3_PATH_MFMA, M3_PATH_SCAN = 0, 1, 2
 STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EALIGN",
           5: "M3_EUNSUPPORTED", 6: "M3_EHIP", 7: "M3_EWORKSPACE"}
 

@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["m3_host.cpp", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_decode.hip", "m3_prologue.hip",
-           "m3_backward.hip"]
+           "m3_backward.hip", "m3_prefill_scan.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -88,7 +88,8 @@ m3_status make_plan(const m3_dims* d, int32_t R, int32_t chunk, m3_dtype io, m3_
     p->n_chunks = (L + chunk - 1) / chunk;
     p->last_chunk_len = L == 0 ? 0 : L - (p->n_chunks - 1) * chunk;
     const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
-    p->path = mfma ? M3_PATH_MFMA : M3_PATH_GENERIC;
+    p->path = mfma ? M3_PATH_MFMA
+                   : m3::scan_path_supported(d->headdim, d->dstate, R, io) ? M3_PATH_SCAN : M3_PATH_GENERIC;
     p->segments = (mfma && m3::mfma_segments_supported(R)) ? choose_segments(d->batch * d->heads, p->n_chunks) : 1;
     p->chunks_per_segment = p->segments > 0 ? (p->n_chunks + p->segments - 1) / p->segments : 0;
     if (mfma && p->chunks_per_segment > 0)  // no empty trailing segment
@@ -233,7 +234,9 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
         m3::PrefillArgs a{x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x,
                           b, L, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R, chunk, io_dtype,
                           plan, workspace, st};
-        e = plan.path == M3_PATH_MFMA ? m3::launch_prefill_mfma(a) : m3::launch_prefill_generic(a);
+        e = plan.path == M3_PATH_MFMA   ? m3::launch_prefill_mfma(a)
+            : plan.path == M3_PATH_SCAN ? m3::launch_prefill_scan(a)
+                                        : m3::launch_prefill_generic(a);
     }
     if (e != hipSuccess) return fail(M3_EHIP, "launch failed: %s", hipGetErrorString(e));
     return M3_OK;

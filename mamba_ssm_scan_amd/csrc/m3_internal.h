@@ -129,6 +129,9 @@ bool mfma_path_supported(int32_t P, int32_t N, int32_t R, int32_t chunk, m3_dtyp
 // the MFMA path splits the sequence into segments (look-back) at these ranks
 bool mfma_segments_supported(int32_t R);
 
+// the token-walk path (bf16, N, P multiples of 16, N <= 256, P <= 64, R <= 8)
+bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io);
+hipError_t launch_prefill_scan(const PrefillArgs& a);
 hipError_t launch_prefill_generic(const PrefillArgs& a);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);

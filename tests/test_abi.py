@@ -67,6 +67,19 @@ def test_plan_generic_workspace(lib):
     assert lib.m3_prefill_workspace_size(ctypes.byref(d), 2, 16, bd.M3_F32) == p.workspace_bytes
 
 
+@pytest.mark.parametrize("N,P,R,io,path", [
+    (128, 64, 1, "bf16", "MFMA"), (128, 64, 4, "bf16", "MFMA"), (128, 64, 3, "bf16", "SCAN"),
+    (256, 64, 1, "bf16", "SCAN"), (128, 64, 8, "bf16", "SCAN"), (256, 32, 6, "bf16", "SCAN"),
+    (128, 64, 9, "bf16", "GENERIC"), (272, 64, 1, "bf16", "GENERIC"), (128, 72, 1, "bf16", "GENERIC"),
+    (120, 64, 1, "bf16", "GENERIC"), (256, 64, 8, "f32", "GENERIC")])
+def test_plan_path_choice(lib, N, P, R, io, path):
+    """Which kernel family takes a shape; the token-walk path needs no workspace."""
+    p = bd.plan(_dims(b=2, H=4, P=P, N=N), R, 64, bd.M3_BF16 if io == "bf16" else bd.M3_F32)
+    assert p.path == getattr(bd, "M3_PATH_" + path)
+    if path == "SCAN":
+        assert p.workspace_bytes == 0 and p.segments == 1
+
+
 FAKE = 1 << 40  # never dereferenced
 
 

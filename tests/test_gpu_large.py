@@ -2,8 +2,10 @@
 ranks R = 6 and 8 (the state-size and rank knobs of "Mamba-3架构技术解析" §4.3
 and the MIMO rank of "复值SSM × 广义梯形离散 × MIMO" §2.3).
 
-These shapes run on the generic kernels (chunked fp32 prefill, generic decode
-step): the MFMA prefill is built for N 128, P 64, R 1/2/4. The oracle runs the
+With bf16 I/O the prefill runs the token-walk kernel (state in registers, rank
+contractions on MFMA; N, P multiples of 16 up to 256 and 64, R up to 8), which
+also takes the ranks the chunked MFMA kernels do not (3, 5, 6, 7); fp32 I/O
+runs the generic chunked kernel, decode the generic step. The oracle runs the
 same problem in fp64; bars are the recurrence's own (1e-4 fp32, 2e-2 bf16 I/O,
 max-relative per (batch, head) slice).
 """
@@ -12,17 +14,28 @@ import torch
 
 import oracle
 from mamba_ssm_scan_amd import binding, inputs
-from tests.util import TOL, assert_close, gpu_prefill, to_dev
+from tests.util import TOL, assert_close, gpu_prefill, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
 PCASES = [
     # b, L, H, G, P, N, R, io, chunk
-    (1, 150, 2, 1, 64, 256, 1, "bf16", 64),   # N 256, ragged last chunk
+    (1, 150, 2, 1, 64, 256, 1, "bf16", 64),   # N 256, a ragged last block
     (2, 70, 2, 1, 64, 128, 8, "bf16", 32),    # R 8
     (1, 90, 3, 3, 64, 256, 6, "bf16", 64),    # N 256 and R 6, one B, C per head
-    (1, 45, 2, 1, 16, 256, 8, "f32", 16),     # fp32, both large
+    (2, 41, 4, 2, 64, 128, 3, "bf16", 64),    # R 3 (the MFMA kernels take 1, 2, 4); b*H = 8: XCD order
+    (1, 33, 2, 1, 32, 64, 5, "bf16", 64),     # P 32 (two waves idle), N 64, R 5
+    (1, 17, 2, 1, 48, 208, 7, "bf16", 64),    # N 208 (13 row tiles), P 48, R 7
+    (3, 1, 2, 1, 64, 256, 2, "bf16", 64),     # one token
+    (1, 45, 2, 1, 16, 256, 8, "f32", 16),     # fp32: the generic kernel
 ]
+
+
+def _path(p, chunk):
+    b, L, H, R, P = p["x"].shape
+    G, N = p["B"].shape[2], p["B"].shape[4]
+    io = binding.M3_BF16 if p["x"].dtype == torch.bfloat16 else binding.M3_F32
+    return binding.plan(binding.dims(b, L, H, G, P, N), R, chunk, io).path
 
 
 @pytest.mark.parametrize("case", PCASES, ids=[str(c) for c in PCASES])
@@ -31,10 +44,54 @@ def test_prefill_large_state_and_rank(case):
     print(f"prefill large case {case}", flush=True)
     p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=P, dstate=N, rank=R, io_dtype=io,
                             dist="lm", wid=1000 + PCASES.index(case), h0_std=0.1, with_carry=True)
+    assert _path(p, chunk) == (binding.M3_PATH_SCAN if io == "bf16" else binding.M3_PATH_GENERIC)
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
     assert_close(y, y_ref, TOL[io], "y")
     assert_close(h, h_ref, TOL[io], "h_out")
+
+
+@pytest.mark.parametrize("drop", ["omega", "lam", "both"])
+def test_scan_special_cases(drop):
+    """omega NULL (omega = 0) and lambda NULL (lambda = 1) on the token-walk kernel."""
+    print(f"scan special case {drop}", flush=True)
+    p = inputs.make_problem(batch=2, seqlen=60, heads=2, groups=1, headdim=64, dstate=256, rank=6, io_dtype="bf16",
+                            dist="lm", wid=1030, h0_std=0.1, with_carry=True)
+    q = dict(p)
+    no_om, no_lam = drop in ("omega", "both"), drop in ("lam", "both")
+    if no_om:
+        q["omega"] = torch.zeros_like(p["omega"])
+    if no_lam:
+        q["lam"] = torch.ones_like(p["lam"])
+    y_ref, h_ref = oracle.scan(q)
+    d = to_dev(p)
+    y, h = binding.prefill(d["x"], d["dt"], d["A"], None if no_om else d["omega"], None if no_lam else d["lam"],
+                           d["B"], d["C"], d["D"], 6, 64, d["h0"], carry_B=d["carry_B"], carry_x=d["carry_x"])
+    torch.cuda.synchronize()
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+SAMPLE_HEADS = [0, 37, 63]
+
+
+@pytest.mark.parametrize("wid,dstate,rank", [(1, 256, None), (2, None, 8)])
+def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
+    """Workload 1's shape with N 256, workload 2's with R 8 (b 4, L 2048, H 64): oracle on 3 heads x all batches."""
+    w = inputs.WORKLOADS[wid]
+    N, R = dstate or w.dstate, rank or w.rank
+    print(f"workload {wid} shape with N {N}, R {R}", flush=True)
+    p = inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=1, headdim=w.headdim, dstate=N,
+                            rank=R, io_dtype=w.io_dtype, dist=w.dist, wid=wid, device="cuda")
+    assert _path(p, w.chunk) == binding.M3_PATH_SCAN
+    y, h = binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], R, w.chunk)
+    torch.cuda.synchronize()
+    sub = to_host(inputs.select_heads(p, SAMPLE_HEADS))
+    y_ref, h_ref = oracle.scan(sub)
+    idx = torch.tensor(SAMPLE_HEADS, device="cuda")
+    assert_close(y.index_select(2, idx), y_ref, TOL["bf16"], "y")
+    assert_close(h.index_select(1, idx), h_ref, TOL["bf16"], "h_out")
+    assert torch.isfinite(y).all()
 
 
 DCASES = [
