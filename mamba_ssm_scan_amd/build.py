@@ -25,12 +25,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 
 SOURCES = ["m3_host.cpp", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_decode.hip", "m3_prologue.hip",
            "m3_backward.hip", "m3_prefill_scan.hip"]
+# per-source flags: the token-walk kernel reads every MFMA result with VALU
+# ops, so its MFMAs write arch VGPRs (no accumulator-register copies)
+EXTRA = {"m3_prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

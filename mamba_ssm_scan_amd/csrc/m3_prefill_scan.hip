@@ -15,13 +15,20 @@
 //   U_t[n][p]  = sum_r B_t[r][n] x_t[r][p]   (A: B^T, k = rank; B: x)
 // lands in the lanes that own h[n][p], and
 //   y_t[r][p]  = sum_n C_t[r][n] h[n][p]     (A: C, k = n; B: the new state)
-// takes the lane's four new state values as its B operand, as a bf16 hi + lo
-// pair (y keeps fp32 accuracy; the products in U are exact). No cross-lane
-// reduction is left. U_{t-1} is carried in registers from the previous step.
+// takes the lane's four new state values, rounded to bf16, as its B operand
+// (as the chunked kernels feed the carried state to their inter-chunk term;
+// the products in U are exact). No cross-lane reduction is left. Only one
+// operand of each product needs its padding zeroed: x^T past rank R (so the
+// A operand of U may hold any finite values there), and the output rows of y
+// past R are not stored (so the A operand of y takes a clamped row).
 //
-// A block of tokens is staged in LDS with one pass of global loads: B^T and
-// x^T with the ranks of a row contiguous, C row-major, alpha (cos, sin) per
-// (token, pair) and gamma, delta per token. Two barriers per block.
+// A block of tokens is staged in LDS with one pass of global loads (all of a
+// thread's loads issued before its first LDS store): B, x and C as row-major
+// copies of their rank rows, alpha (cos, sin) per (token, pair) and gamma,
+// delta per token. The operands that need a rank-major layout (B^T, x^T) come
+// out of row-major LDS through transposing reads (ds_read_b64_tr_b16: in each
+// 16-lane group, lane t addresses 4 values of row t / 4 at column 4 (t % 4);
+// lane j receives column j of those 4 rows). Two barriers per block.
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -32,10 +39,16 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short shortx4_tr __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;  // threads: 4 waves, 16 state columns each
 constexpr float kInv2Pi = 0.15915494309189535f;
 
+__device__ __forceinline__ u32x2 load_tr(const uint16_t* p) {
+    const shortx4_tr v =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_tr*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
 __device__ __forceinline__ floatx4 mfma16(u32x2 a, u32x2 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c,
                                                      0, 0, 0);
@@ -47,28 +60,31 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(unsigned, v);
 }
-__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
 // sizes of one instance: NTL row tiles (N <= 16 NTL), RG groups of 4 ranks (R <= 4 RG)
 template <int NTL, int RG>
 struct ScanShape {
     static constexpr int NMAX = 16 * NTL, KMAX = NMAX / 2, RK = 4 * RG;
     static constexpr int BT = (NTL == 16 && RG == 2) ? 8 : 16;  // tokens per staged block
-    static constexpr int NS = NMAX + 4;                         // C row stride (bf16)
+    static constexpr int NS = NMAX + 4;                         // B, C row stride (bf16)
+    static constexpr int XS = 64 + 4;                           // x row stride (bf16)
+    // staging: rows of N / 2 (B, C) or P / 2 (x) 32-bit words, several rows per pass
+    static constexpr int WB = NMAX / 2, RPB = NT / WB, MAXB = BT * RK / RPB;
+    static constexpr int RPX = NT / 32, MAXX = BT * RK / RPX;
+    static constexpr int MAXCS = BT * KMAX / NT;
 };
 
 template <int NTL, int RG>
 struct ScanLds {
     typedef ScanShape<NTL, RG> S;
-    uint16_t B[S::BT][S::NMAX][S::RK];  // B^T of the block's tokens (ranks past R zero)
-    uint16_t X[S::BT][64][S::RK];       // x^T
-    uint16_t C[S::BT][S::RK][S::NS];    // C rows
+    uint16_t B[S::BT][S::RK][S::NS];  // B rank rows of the block's tokens (rows past R zero)
+    uint16_t X[S::BT][S::RK][S::XS];  // x rank rows (rows past R zero)
+    uint16_t C[S::BT][S::RK][S::NS];  // C rank rows
     float CS[S::BT][S::KMAX][2];        // alpha * (cos, sin) of each pair's step angle
     float GD[S::BT][2];                 // gamma, delta
 };
 
-template <int NTL, int RG>
+template <int NTL, int RG, bool FULL>
 __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
     typedef ScanShape<NTL, RG> S;
     constexpr int BT = S::BT;
@@ -85,107 +101,157 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
     const int64_t b = bh / a.H;
     const int h = int(bh % a.H);
     const int g = h / (a.H / a.G);
-    const int N = a.N, P = a.P, R = a.R, K = N / 2, ntl = N / 16;
+    const int N = FULL ? S::NMAX : a.N, P = a.P, R = a.R, K = N / 2, ntl = FULL ? NTL : N / 16;
     const int64_t L = a.L;
     const int p = 16 * w + l16;
     const bool active = 16 * w < P;  // uniform per wave
     const float Ah = a.A[h], Dh = a.D[h];
     const float* omh = a.omega ? a.omega + int64_t(h) * K : nullptr;
-    const uint16_t* Bg = static_cast<const uint16_t*>(a.B);
-    const uint16_t* Cg = static_cast<const uint16_t*>(a.C);
-    const uint16_t* Xg = static_cast<const uint16_t*>(a.x);
-    uint16_t* Yg = static_cast<uint16_t*>(a.y);
+    const int64_t rowB = int64_t(a.G) * R * N, rowX = int64_t(a.H) * R * P;  // per-token strides
+    const uint16_t* Bg = static_cast<const uint16_t*>(a.B) + (b * L * a.G + g) * int64_t(R) * N;
+    const uint16_t* Cg = static_cast<const uint16_t*>(a.C) + (b * L * a.G + g) * int64_t(R) * N;
+    const uint16_t* Xg = static_cast<const uint16_t*>(a.x) + (b * L * a.H + h) * int64_t(R) * P;
+    uint16_t* Yg = static_cast<uint16_t*>(a.y) + (b * L * a.H + h) * int64_t(R) * P;
+    const float* dtg = a.dt + b * L * a.H + h;
+    const float* lmg = a.lam ? a.lam + b * L * a.H + h : nullptr;
 
     // ranks past R stay zero in B^T and x^T for the whole walk
     for (int e = tid; e < int(sizeof(s.B) / 4); e += NT) reinterpret_cast<uint32_t*>(&s.B)[e] = 0u;
     for (int e = tid; e < int(sizeof(s.X) / 4); e += NT) reinterpret_cast<uint32_t*>(&s.X)[e] = 0u;
 
-    // B rows of one token (rank r, rows 2i, 2i + 1 per 32-bit load) into slot j
-    auto stage_bx = [&](int j, const uint16_t* brow, const uint16_t* xrow) {
-        for (int e = tid; e < R * (N / 2); e += NT) {
-            const int r = e / (N / 2), i = e % (N / 2);
-            const unsigned v = reinterpret_cast<const unsigned*>(brow + r * N)[i];
-            s.B[j][2 * i][r] = uint16_t(v);
-            s.B[j][2 * i + 1][r] = uint16_t(v >> 16);
-        }
-        for (int e = tid; e < R * (P / 2); e += NT) {
-            const int r = e / (P / 2), i = e % (P / 2);
-            const unsigned v = reinterpret_cast<const unsigned*>(xrow + r * P)[i];
-            s.X[j][2 * i][r] = uint16_t(v);
-            s.X[j][2 * i + 1][r] = uint16_t(v >> 16);
-        }
+    // (token j, rank r) of staging row q: j = q / R for q < 128, R <= 8 (exact)
+    const unsigned invR = (65536u + unsigned(R) - 1u) / unsigned(R);
+    auto delta_at = [&](int64_t t) {  // (1 - lambda) dt of token t, zero past the end
+        return t < L ? (1.f - (lmg ? lmg[t * a.H] : 1.f)) * dtg[t * a.H] : 0.f;
     };
 
-    float st[NTL][4], up[NTL][4];
+    // The walk carries g_t = h_t + delta_{t+1} U_t, the state the next step turns:
+    //   h_t = alpha_t Rot g_{t-1} + gamma_t U_t,  y_t = h_t^T C_t + D x_t,  g_t = h_t + delta_{t+1} U_t
+    // so U_t is formed once. g_0 = h0 + delta_1 U_0 with U_0 from the caller's carry.
+    float st[NTL][4];
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int n = 16 * nt + 4 * g4 + e;
             st[nt][e] = (a.h0 && active && nt < ntl) ? a.h0[(bh * N + n) * int64_t(P) + p] : 0.f;
-            up[nt][e] = 0.f;
         }
     const u32x2 zero = {0u, 0u};
+    const int gk = g4 < RG ? g4 : 0;  // in-range rank group for the lanes whose operand is zero
+    const int rc = l16 < R ? l16 : 0;
 
-    // U of the token before the first (the caller's carry), else zero
     if (a.carry_B) {
         __syncthreads();
-        stage_bx(0, static_cast<const uint16_t*>(a.carry_B) + (b * a.G + g) * int64_t(R) * N,
-                 static_cast<const uint16_t*>(a.carry_x) + bh * int64_t(R) * P);
+        const uint16_t* cb = static_cast<const uint16_t*>(a.carry_B) + (b * a.G + g) * int64_t(R) * N;
+        const uint16_t* cx = static_cast<const uint16_t*>(a.carry_x) + bh * int64_t(R) * P;
+        for (int e = tid; e < R * (N / 2); e += NT)
+            reinterpret_cast<unsigned*>(&s.B[0][e / (N / 2)][0])[e % (N / 2)] = reinterpret_cast<const unsigned*>(cb)[e];
+        for (int e = tid; e < R * (P / 2); e += NT)
+            reinterpret_cast<unsigned*>(&s.X[0][e / (P / 2)][0])[e % (P / 2)] = reinterpret_cast<const unsigned*>(cx)[e];
         __syncthreads();
+        const float d1 = delta_at(0);
         if (active) {
-            const int gc = g4 < RG ? g4 : 0;
-            const u32x2 xo = g4 < RG ? *reinterpret_cast<const u32x2*>(&s.X[0][p][4 * gc]) : zero;
+            const u32x2 xv = load_tr(&s.X[0][4 * gk + (l16 >> 2)][16 * w + 4 * (l16 & 3)]);
+            const u32x2 xo = g4 < RG ? xv : zero;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt)
-                if (nt < ntl) {
-                    const u32x2 ab = g4 < RG ? *reinterpret_cast<const u32x2*>(&s.B[0][16 * nt + l16][4 * gc]) : zero;
+                if (FULL || nt < ntl) {
+                    const u32x2 ab = load_tr(&s.B[0][4 * gk + (l16 >> 2)][16 * nt + 4 * (l16 & 3)]);
                     const floatx4 U = mfma16(ab, xo, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) up[nt][e] = U[e];
+                    for (int e = 0; e < 4; ++e) st[nt][e] += d1 * U[e];
                 }
         }
     }
 
-    const int rc = l16 < R ? l16 : 0;
-    const int gk = g4 < RG ? g4 : 0;  // in-range rank group for the lanes whose operand is zero
     for (int64_t t0 = 0; t0 < L; t0 += BT) {
         const int nt_ = int(L - t0 < BT ? L - t0 : BT);
-        __syncthreads();  // the previous block's readers are done
-        for (int j = 0; j < nt_; ++j)
-            stage_bx(j, Bg + ((b * L + t0 + j) * a.G + g) * int64_t(R) * N,
-                     Xg + ((b * L + t0 + j) * a.H + h) * int64_t(R) * P);
-        for (int e = tid; e < nt_ * R * (N / 2); e += NT) {
-            const int j = e / (R * (N / 2)), q = e % (R * (N / 2)), r = q / (N / 2), i = q % (N / 2);
-            reinterpret_cast<unsigned*>(&s.C[j][r][0])[i] =
-                reinterpret_cast<const unsigned*>(Cg + ((b * L + t0 + j) * a.G + g) * int64_t(R) * N + r * N)[i];
-        }
-        for (int e = tid; e < nt_ * K; e += NT) {
-            const int j = e / K, k = e % K;
-            const float d = a.dt[(b * L + t0 + j) * a.H + h];
-            const float al = expf(d * Ah);
-            const float rv = __builtin_amdgcn_fractf(d * om_at(omh, k) * kInv2Pi);
-            s.CS[j][k][0] = al * __builtin_amdgcn_cosf(rv);
-            s.CS[j][k][1] = al * __builtin_amdgcn_sinf(rv);
+        // every load of the block first, then the barrier, then the LDS stores
+        const int nrow = nt_ * R;
+        // 32-bit word offsets from the block's first token (uniform bases)
+        const unsigned* Bb = reinterpret_cast<const unsigned*>(Bg + t0 * rowB);
+        const unsigned* Cb = reinterpret_cast<const unsigned*>(Cg + t0 * rowB);
+        const unsigned* Xb = reinterpret_cast<const unsigned*>(Xg + t0 * rowX);
+        const float* db = dtg + t0 * a.H;
+        const unsigned wB = unsigned(rowB / 2), wX = unsigned(rowX / 2);
+        unsigned vb[S::MAXB], vc[S::MAXB], vx[S::MAXX];
+        float dcs[S::MAXCS];
+        {
+            const int wi = tid % S::WB, rs = tid / S::WB;
+#pragma unroll
+            for (int u = 0; u < S::MAXB; ++u) {
+                const int q = u * S::RPB + rs;
+                if (q < nrow && wi < N / 2) {
+                    const unsigned j = (unsigned(q) * invR) >> 16, r = unsigned(q) - j * unsigned(R);
+                    const unsigned o = j * wB + r * unsigned(N / 2) + unsigned(wi);
+                    vb[u] = Bb[o];
+                    vc[u] = Cb[o];
+                }
+            }
+            const int xi = tid % 32, xs = tid / 32;
+#pragma unroll
+            for (int u = 0; u < S::MAXX; ++u) {
+                const int q = u * S::RPX + xs;
+                if (q < nrow && xi < P / 2) {
+                    const unsigned j = (unsigned(q) * invR) >> 16, r = unsigned(q) - j * unsigned(R);
+                    vx[u] = Xb[j * wX + r * unsigned(P / 2) + unsigned(xi)];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < S::MAXCS; ++u) {
+                const int e = tid + u * NT, j = e / K;
+                if (j < nt_) dcs[u] = db[unsigned(j) * unsigned(a.H)];
+            }
+            __syncthreads();  // every wave is done reading the previous block (its loads are in flight)
+#pragma unroll
+            for (int u = 0; u < S::MAXB; ++u) {
+                const int q = u * S::RPB + rs;
+                if (q < nrow && wi < N / 2) {
+                    const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                    reinterpret_cast<unsigned*>(&s.B[j][r][0])[wi] = vb[u];
+                    reinterpret_cast<unsigned*>(&s.C[j][r][0])[wi] = vc[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < S::MAXX; ++u) {
+                const int q = u * S::RPX + xs;
+                if (q < nrow && xi < P / 2) {
+                    const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                    reinterpret_cast<unsigned*>(&s.X[j][r][0])[xi] = vx[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < S::MAXCS; ++u) {
+                const int e = tid + u * NT, j = e / K, k = e - j * K;
+                if (j < nt_) {
+                    const float d = dcs[u];
+                    const float al = expf(d * Ah);
+                    const float rv = __builtin_amdgcn_fractf(d * om_at(omh, k) * kInv2Pi);
+                    s.CS[j][k][0] = al * __builtin_amdgcn_cosf(rv);
+                    s.CS[j][k][1] = al * __builtin_amdgcn_sinf(rv);
+                }
+            }
         }
         if (tid < nt_) {
-            const int64_t i = (b * L + t0 + tid) * a.H + h;
-            const float d = a.dt[i], lm = lam_at(a.lam, i);
-            s.GD[tid][0] = lm * d;
-            s.GD[tid][1] = (1.f - lm) * d;
+            const int64_t t = t0 + tid;
+            s.GD[tid][0] = (lmg ? lmg[t * a.H] : 1.f) * dtg[t * a.H];
+            s.GD[tid][1] = delta_at(t + 1);
         }
         __syncthreads();
         if (!active) continue;
 
         for (int j = 0; j < nt_; ++j) {
-            const float gam = s.GD[j][0], del = s.GD[j][1];
-            const u32x2 xo = g4 < RG ? *reinterpret_cast<const u32x2*>(&s.X[j][p][4 * gk]) : zero;
-            floatx4 ya = {0.f, 0.f, 0.f, 0.f}, yb = {0.f, 0.f, 0.f, 0.f};
+            const float gam = s.GD[j][0], dnx = s.GD[j][1];
+            const u32x2 xv = load_tr(&s.X[j][4 * gk + (l16 >> 2)][16 * w + 4 * (l16 & 3)]);
+            const u32x2 xo = g4 < RG ? xv : zero;
+            floatx4 yacc[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yacc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                if (nt >= ntl) continue;
+                if (!FULL && nt >= ntl) continue;
                 const int n0 = 16 * nt;
-                const u32x2 ab = g4 < RG ? *reinterpret_cast<const u32x2*>(&s.B[j][n0 + l16][4 * gk]) : zero;
+                const u32x2 ab = load_tr(&s.B[j][4 * gk + (l16 >> 2)][n0 + 4 * (l16 & 3)]);
                 const floatx4 U = mfma16(ab, xo, floatx4{0.f, 0.f, 0.f, 0.f});
                 // pairs 8 nt + 2 g4 (rows e = 0, 1) and 8 nt + 2 g4 + 1 (rows e = 2, 3)
                 const floatx4 cs = *reinterpret_cast<const floatx4*>(&s.CS[j][(n0 >> 1) + 2 * g4][0]);
@@ -193,54 +259,46 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int hp = 0; hp < 2; ++hp) {
                     const float c = cs[2 * hp], sn = cs[2 * hp + 1];
-                    const float g0 = st[nt][2 * hp] + del * up[nt][2 * hp];
-                    const float g1 = st[nt][2 * hp + 1] + del * up[nt][2 * hp + 1];
+                    const float g0 = st[nt][2 * hp], g1 = st[nt][2 * hp + 1];
                     nv[2 * hp] = (c * g0 - sn * g1) + gam * U[2 * hp];
                     nv[2 * hp + 1] = (sn * g0 + c * g1) + gam * U[2 * hp + 1];
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    st[nt][e] = nv[e];
-                    up[nt][e] = U[e];
-                }
-                const unsigned h01 = pk_bf16(nv[0], nv[1]), h23 = pk_bf16(nv[2], nv[3]);
-                const u32x2 hi = {h01, h23};
-                const u32x2 lo = {pk_bf16(nv[0] - bf_lo(h01), nv[1] - bf_hi(h01)),
-                                  pk_bf16(nv[2] - bf_lo(h23), nv[3] - bf_hi(h23))};
-                const u32x2 cv = *reinterpret_cast<const u32x2*>(&s.C[j][rc][n0 + 4 * g4]);
-                const u32x2 ac = l16 < R ? cv : zero;
-                if (nt & 1) {
-                    yb = mfma16(ac, hi, yb);
-                    yb = mfma16(ac, lo, yb);
-                } else {
-                    ya = mfma16(ac, hi, ya);
-                    ya = mfma16(ac, lo, ya);
-                }
+                for (int e = 0; e < 4; ++e) st[nt][e] = nv[e] + dnx * U[e];
+                const u32x2 hb = {pk_bf16(nv[0], nv[1]), pk_bf16(nv[2], nv[3])};
+                const u32x2 ac = *reinterpret_cast<const u32x2*>(&s.C[j][rc][n0 + 4 * g4]);
+                yacc[nt & 3] = mfma16(ac, hb, yacc[nt & 3]);
             }
             // lane (l16, g4) holds y[r = 4 g4 + e][p]
-            const int64_t yrow = ((b * L + t0 + j) * a.H + h) * int64_t(R) * P;
+            uint16_t* yrow = Yg + (t0 + j) * rowX;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g4 + e;
                 if (r < R) {
-                    const float xv = bf16_to_f32(s.X[j][p][r]);
-                    Yg[yrow + r * P + p] = f32_to_bf16(ya[e] + yb[e] + Dh * xv);
+                    const float xv = bf16_to_f32(s.X[j][r][p]);
+                    const float v = (yacc[0][e] + yacc[1][e]) + (yacc[2][e] + yacc[3][e]);
+                    yrow[r * P + p] = f32_to_bf16(v + Dh * xv);
                 }
             }
         }
     }
 
+    // after the last token delta_{L+1} = 0, so the carried g is h_L
     if (a.h_out && active)
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
-            if (nt < ntl)
+            if (FULL || nt < ntl)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a.h_out[(bh * N + 16 * nt + 4 * g4 + e) * int64_t(P) + p] = st[nt][e];
 }
 
 template <int NTL, int RG>
 hipError_t launch_ntl_rg(const PrefillArgs& a) {
-    hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG>), dim3(unsigned(a.b * a.H)), dim3(NT), 0, a.stream, a);
+    if (a.N == 16 * NTL)
+        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, true>), dim3(unsigned(a.b * a.H)), dim3(NT), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, false>), dim3(unsigned(a.b * a.H)), dim3(NT), 0, a.stream,
+                           a);
     return hipGetLastError();
 }
 
