@@ -41,7 +41,8 @@ ROOT_SEED = 20261203
 # tensor ids used in the seed sequence
 _TID = {"x": 1, "B": 2, "C": 3, "dt": 4, "lam": 5, "A": 6, "omega": 7, "D": 8,
         "h0": 9, "carry_B": 10, "carry_x": 11, "B_raw": 12, "C_raw": 13, "B_weight": 14, "B_bias": 15,
-        "C_weight": 16, "C_bias": 17, "dt_raw": 18, "dt_bias": 19, "lambda_raw": 20, "row_scale": 21}
+        "C_weight": 16, "C_bias": 17, "dt_raw": 18, "dt_bias": 19, "lambda_raw": 20, "row_scale": 21,
+        "u": 22, "W_x": 23, "W_z": 24, "W_B": 25, "W_C": 26, "W_dt": 27, "W_lambda": 28, "W_out": 29}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -282,3 +283,36 @@ def prologue_inputs(*, tokens, heads, groups, rank, dstate, io_dtype="bf16", wid
                 dt_bias=_normal((H,), _gen(device, wid, "dt_bias"), device, 0.0, 0.2),
                 lambda_raw=_normal(tokens + (H,), _gen(device, wid, "lambda_raw", step), device),
                 io_dtype=io_dtype)
+
+
+def mixer_inputs(*, batch, seqlen, d_model, heads, groups, headdim, dstate, rank, wid=500, step=0,
+                 device="cpu") -> dict:
+    """Synthetic weights and tokens of one mixer block (random draws only).
+
+    u [b][L][d_model] bf16 ~ N(0, 1); projection weights bf16, row-major [in][out]:
+    W_x, W_z [d_model][H*R*P] and W_B, W_C [d_model][G*R*N] and W_lambda
+    [d_model][H] ~ N(0, 1/d_model) (unit-variance outputs), W_dt [d_model][H] ~
+    N(0, 0.25/d_model) with dt_bias [H] ~ N(-1, 0.2) (so dt_raw + bias is near the
+    workloads' N(-1, 0.5)), W_out [H*R*P][d_model] ~ N(0, 1/(H*R*P)); B/C weights
+    ~ N(1, 0.1), biases ~ N(0, 0.1) [G][R][N] fp32; A, omega, D as the "lm" family.
+    Stand-ins for trained weights, which are not available.
+    """
+    H, G, R, P, N = heads, groups, rank, headdim, dstate
+    HRP, GRN = H * R * P, G * R * N
+    bf = torch.bfloat16
+
+    def mat(name, rows, cols, std):
+        return _normal((rows, cols), _gen(device, wid, name), device, 0.0, std).to(bf)
+
+    A, omega, D = _head_params(wid, H, N, "lm", device)
+    par = lambda name, mean, std: _normal((G, R, N), _gen(device, wid, name), device, mean, std)
+    return dict(u=_normal((batch, seqlen, d_model), _gen(device, wid, "u", step), device).to(bf),
+                W_x=mat("W_x", d_model, HRP, d_model ** -0.5), W_z=mat("W_z", d_model, HRP, d_model ** -0.5),
+                W_B=mat("W_B", d_model, GRN, d_model ** -0.5), W_C=mat("W_C", d_model, GRN, d_model ** -0.5),
+                W_dt=mat("W_dt", d_model, H, 0.5 * d_model ** -0.5),
+                W_lambda=mat("W_lambda", d_model, H, d_model ** -0.5),
+                W_out=mat("W_out", HRP, d_model, HRP ** -0.5),
+                B_weight=par("B_weight", 1.0, 0.1), B_bias=par("B_bias", 0.0, 0.1),
+                C_weight=par("C_weight", 1.0, 0.1), C_bias=par("C_bias", 0.0, 0.1),
+                dt_bias=_normal((H,), _gen(device, wid, "dt_bias"), device, -1.0, 0.2),
+                A=A, omega=omega, D=D, eps=1e-6, H=H, G=G, R=R, P=P, N=N, d_model=d_model)
