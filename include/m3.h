@@ -244,6 +244,72 @@ m3_status m3_prefill_backward(const void* x, const float* dt, const float* A, co
 /* Workspace bytes m3_prefill_backward needs (0 on invalid or unsupported sizes). Host only. */
 size_t m3_prefill_backward_workspace_size(const m3_dims* dims, int32_t R);
 
+/*
+ * The mixer block around the recurrence (training-free forward: prefill and
+ * decode step). The PaperWeekly digest ("复值SSM × 广义梯形离散 × MIMO，线性模型的全面
+ * 重构", §2.4 and Fig. 4) lists what a Mamba-3 block holds without a block
+ * formula; the reading taken is the Mamba-2 block layout with those changes.
+ * Per token u (d_model entries, bf16):
+ *   x = u W_x, z = u W_z           [H][R][P]     (bf16)
+ *   B_raw = u W_B, C_raw = u W_C   [G][R][N]     (bf16)
+ *   dt_raw = u W_dt, lambda_raw = u W_lambda  [H] (fp32)
+ *   B, C, dt, lambda = m3_prologue(...) with the weights' B/C norm weights and biases, dt_bias, eps
+ *   y = the recurrence (m3_prefill, or m3_decode_step) with A, omega, D
+ *   out = (y * silu(z)) W_out      [d_model]     (bf16; silu(v) = v sigmoid(v))
+ * Weights are bf16, row-major [in][out]: W_x, W_z [d_model][H*R*P], W_B, W_C
+ * [d_model][G*R*N], W_dt, W_lambda [d_model][H], W_out [H*R*P][d_model]. The
+ * projections run as hipBLASLt GEMMs (fp32 accumulation); omega, the norm
+ * weights, biases and dt_bias may be NULL as for m3_prologue / m3_prefill.
+ * The intermediates live in the caller's workspace. A mixer object holds the
+ * hipBLASLt handle and the GEMM algorithms chosen per shape: create it once,
+ * use it from one thread at a time, destroy it at the end.
+ */
+typedef struct m3_mixer m3_mixer;
+typedef struct m3_mixer_weights {
+    int32_t d_model;
+    const void* W_x;
+    const void* W_z;
+    const void* W_B;
+    const void* W_C;
+    const void* W_dt;
+    const void* W_lambda;
+    const void* W_out;
+    const float* B_weight;  /* [G][R][N] or NULL */
+    const float* B_bias;
+    const float* C_weight;
+    const float* C_bias;
+    const float* dt_bias;   /* [H] or NULL */
+    const float* A;         /* [H] */
+    const float* omega;     /* [H][N/2] or NULL */
+    const float* D;         /* [H] */
+    float eps;
+} m3_mixer_weights;
+
+/* Create / destroy a mixer object (host call; creates a hipBLASLt handle on the current device). */
+m3_status m3_mixer_create(m3_mixer** out);
+void m3_mixer_destroy(m3_mixer* m);
+
+/* Workspace bytes of m3_mixer_prefill for these sizes (dims->seqlen tokens per
+ * sequence; 1 for m3_mixer_decode_step), 0 on invalid sizes. Host only. */
+size_t m3_mixer_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, int32_t d_model);
+
+/*
+ * m3_mixer_prefill -- the block over u [b][L][d_model] bf16 -> out [b][L][d_model] bf16.
+ * h0 (nullable) and h_out (nullable) as for m3_prefill; chunk as for m3_prefill.
+ * st (nullable): a decode state whose buffers are bound (m3_decode_state_init)
+ * with the same sizes; it receives h_L, the last token's (B, x) as the carry and
+ * t = L, so m3_mixer_decode_step continues the sequences. Asynchronous on `stream`.
+ */
+m3_status m3_mixer_prefill(m3_mixer* m, const m3_mixer_weights* w, const m3_dims* dims, int32_t R, int32_t chunk,
+                           const void* u, void* out, const float* h0, float* h_out, m3_decode_state* st,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* m3_mixer_decode_step -- the block for one token per sequence, u_t [b][d_model] ->
+ * out_t [b][d_model], advancing st (bf16) by one token. Workspace: at least
+ * m3_mixer_workspace_size() with seqlen 1. */
+m3_status m3_mixer_decode_step(m3_mixer* m, const m3_mixer_weights* w, m3_decode_state* st, const void* u_t,
+                               void* out_t, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* m3_status_string(m3_status s);
 

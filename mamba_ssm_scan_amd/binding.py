@@ -24,7 +24,8 @@ STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EAL
 # every symbol include/m3.h declares
 EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_decode_carry_bytes",
            "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_prefill_backward",
-           "m3_prefill_backward_workspace_size", "m3_status_string", "m3_last_error", "m3_abi_version"]
+           "m3_prefill_backward_workspace_size", "m3_mixer_create", "m3_mixer_destroy", "m3_mixer_workspace_size",
+           "m3_mixer_prefill", "m3_mixer_decode_step", "m3_status_string", "m3_last_error", "m3_abi_version"]
 
 
 class M3Dims(ctypes.Structure):
@@ -41,6 +42,12 @@ class M3Plan(ctypes.Structure):
 class M3DecodeState(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("carry_B", ctypes.c_void_p), ("carry_x", ctypes.c_void_p),
                 ("t", ctypes.c_int64), ("dims", M3Dims), ("R", ctypes.c_int32), ("io_dtype", ctypes.c_int)]
+
+
+class M3MixerWeights(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32)] + [(n, ctypes.c_void_p) for n in (
+        "W_x", "W_z", "W_B", "W_C", "W_dt", "W_lambda", "W_out", "B_weight", "B_bias", "C_weight", "C_bias",
+        "dt_bias", "A", "omega", "D")] + [("eps", ctypes.c_float)]
 
 
 class M3Error(RuntimeError):
@@ -83,6 +90,18 @@ def load(path: str = LIB_PATH):
     lib.m3_prefill_backward.restype = ctypes.c_int
     lib.m3_prefill_backward_workspace_size.argtypes = [dims_p, i32]
     lib.m3_prefill_backward_workspace_size.restype = sz
+    lib.m3_mixer_create.argtypes = [ctypes.POINTER(vp)]
+    lib.m3_mixer_create.restype = ctypes.c_int
+    lib.m3_mixer_destroy.argtypes = [vp]
+    lib.m3_mixer_destroy.restype = None
+    lib.m3_mixer_workspace_size.argtypes = [dims_p, i32, i32, i32]
+    lib.m3_mixer_workspace_size.restype = sz
+    lib.m3_mixer_prefill.argtypes = [vp, ctypes.POINTER(M3MixerWeights), dims_p, i32, i32, vp, vp, vp, vp,
+                                     ctypes.POINTER(M3DecodeState), vp, sz, vp]
+    lib.m3_mixer_prefill.restype = ctypes.c_int
+    lib.m3_mixer_decode_step.argtypes = [vp, ctypes.POINTER(M3MixerWeights), ctypes.POINTER(M3DecodeState), vp, vp,
+                                         vp, sz, vp]
+    lib.m3_mixer_decode_step.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     lib.m3_last_error.argtypes = []
@@ -355,3 +374,89 @@ def prefill_backward(x, dt, A, omega, lam, B, C, D, R: int, dy, h0=None, dh_out=
                                   _ptr(g["carry_x"]), ctypes.byref(d), _io_code(io), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
     return g
+
+
+class Mixer:
+    """The mixer block (m3_mixer_*): projections, prologue, recurrence, silu gate, output projection.
+
+    w: a dict with the bf16 weights W_x, W_z, W_B, W_C, W_dt, W_lambda [d_model][*]
+    and W_out [H*R*P][d_model] (row-major [in][out]), fp32 B_weight, B_bias,
+    C_weight, C_bias [G][R][N], dt_bias, A, D [H], omega [H][N/2] (the optional
+    ones may be None), eps, and the sizes H, G, R, P, N, d_model.
+    """
+
+    def __init__(self, w: dict):
+        lib = load()
+        self.H, self.G, self.R, self.P, self.N, self.d_model = (int(w[k]) for k in ("H", "G", "R", "P", "N",
+                                                                                    "d_model"))
+        HRP, GRN, dm = self.H * self.R * self.P, self.G * self.R * self.N, self.d_model
+        bf, f32 = torch.bfloat16, torch.float32
+        shapes = {"W_x": (dm, HRP, bf), "W_z": (dm, HRP, bf), "W_B": (dm, GRN, bf), "W_C": (dm, GRN, bf),
+                  "W_dt": (dm, self.H, bf), "W_lambda": (dm, self.H, bf), "W_out": (HRP, dm, bf)}
+        keep = {k: _need(w[k], k, dt, (r, c)) for k, (r, c, dt) in shapes.items()}
+        par = (self.G, self.R, self.N)
+        for k in ("B_weight", "B_bias", "C_weight", "C_bias"):
+            keep[k] = _need(w.get(k), k, f32, par)
+        keep["dt_bias"] = _need(w.get("dt_bias"), "dt_bias", f32, (self.H,))
+        keep["A"] = _need(w["A"], "A", f32, (self.H,))
+        keep["D"] = _need(w["D"], "D", f32, (self.H,))
+        keep["omega"] = _need(w.get("omega"), "omega", f32, (self.H, self.N // 2))
+        self._keep = keep
+        self._w = M3MixerWeights(dm, *[_ptr(keep[k]) for k in ("W_x", "W_z", "W_B", "W_C", "W_dt", "W_lambda",
+                                                                 "W_out", "B_weight", "B_bias", "C_weight", "C_bias",
+                                                                 "dt_bias", "A", "omega", "D")], float(w["eps"]))
+        h = ctypes.c_void_p()
+        check(lib.m3_mixer_create(ctypes.byref(h)))
+        self._h = h
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.m3_mixer_destroy(h)
+            self._h = None
+
+    def workspace(self, batch: int, seqlen: int, chunk: int = 64) -> torch.Tensor:
+        d = dims(batch, seqlen, self.H, self.G, self.P, self.N)
+        n = load().m3_mixer_workspace_size(ctypes.byref(d), self.R, chunk, self.d_model)
+        if n == 0:
+            raise ValueError("invalid block sizes")
+        key = (batch, seqlen, chunk)
+        if key not in self._ws or self._ws[key].numel() < n:
+            self._ws[key] = torch.empty(n, dtype=torch.uint8, device="cuda")
+        return self._ws[key]
+
+    def decode_state(self, batch: int) -> DecodeState:
+        return DecodeState(batch, self.H, self.G, self.P, self.N, self.R, io_dtype=torch.bfloat16)
+
+    def prefill(self, u, chunk: int = 64, h0=None, out=None, h_out=None, state: Optional[DecodeState] = None,
+                stream=None):
+        """u [b][L][d_model] bf16 -> out [b][L][d_model]; h_out [b][H][N][P] fp32 when requested (True or a tensor)."""
+        b, L, dm = u.shape
+        u = _need(u, "u", torch.bfloat16, (b, L, self.d_model))
+        if out is None:
+            out = torch.empty_like(u)
+        _need_out(out, "out", torch.bfloat16, u.shape)
+        hs = (b, self.H, self.N, self.P)
+        h0 = _need(h0, "h0", torch.float32, hs)
+        if h_out is True:
+            h_out = torch.empty(hs, dtype=torch.float32, device=u.device)
+        _need_out(h_out, "h_out", torch.float32, hs)
+        d = dims(b, L, self.H, self.G, self.P, self.N)
+        ws = self.workspace(b, L, chunk)
+        st = ctypes.byref(state._st) if state is not None else None
+        check(load().m3_mixer_prefill(self._h, ctypes.byref(self._w), ctypes.byref(d), self.R, chunk, _ptr(u),
+                                      _ptr(out), _ptr(h0), _ptr(h_out), st, _ptr(ws), ws.numel(), _stream(stream)))
+        return out, h_out
+
+    def decode_step(self, state: DecodeState, u_t, out_t=None, stream=None):
+        """u_t [b][d_model] bf16 -> out_t [b][d_model], advancing the state by one token."""
+        b = state.dims.batch
+        u_t = _need(u_t, "u_t", torch.bfloat16, (b, self.d_model))
+        if out_t is None:
+            out_t = torch.empty_like(u_t)
+        _need_out(out_t, "out_t", torch.bfloat16, u_t.shape)
+        ws = self.workspace(b, 1)
+        check(load().m3_mixer_decode_step(self._h, ctypes.byref(self._w), ctypes.byref(state._st), _ptr(u_t),
+                                          _ptr(out_t), _ptr(ws), ws.numel(), _stream(stream)))
+        return out_t

@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["m3_host.cpp", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_decode.hip", "m3_prologue.hip",
-           "m3_backward.hip", "m3_prefill_scan.hip"]
+           "m3_backward.hip", "m3_prefill_scan.hip", "m3_gate.hip", "m3_mixer.cpp"]
 # per-source flags: the token-walk kernel reads every MFMA result with VALU
 # ops, so its MFMAs write arch VGPRs (no accumulator-register copies)
 EXTRA = {"m3_prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
@@ -50,7 +50,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

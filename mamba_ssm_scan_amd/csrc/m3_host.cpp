@@ -23,6 +23,18 @@ m3_status fail(m3_status s, const char* fmt, ...) {
 
 size_t io_size(m3_dtype t) { return t == M3_BF16 ? 2 : 4; }
 
+}  // namespace
+
+m3_status m3::set_error(m3_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Range {

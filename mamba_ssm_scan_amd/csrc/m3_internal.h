@@ -133,6 +133,10 @@ bool mfma_segments_supported(int32_t R);
 bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io);
 hipError_t launch_prefill_scan(const PrefillArgs& a);
 hipError_t launch_prefill_generic(const PrefillArgs& a);
+// the mixer block's output gate: y <- bf16(y * silu(z)) over n bf16 entries, in place
+hipError_t launch_gate(void* y, const void* z, int64_t n, hipStream_t s);
+// set the thread's error detail (m3_last_error) and return s
+m3_status set_error(m3_status s, const char* fmt, ...);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prologue(const PrologueArgs& a);
