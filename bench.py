@@ -299,6 +299,87 @@ def bench_backward(wid, steps, warmup, log):
     return r
 
 
+def mixer_gemm_flops(T, d_model, H, G, P, N, R):
+    """The block's projections: in (x, z, B, C, dt, lambda) and out, 2 flops per multiply-add."""
+    HRP, GRN = H * R * P, G * R * N
+    return 2 * T * d_model * (2 * HRP + 2 * GRN + 2 * H) + 2 * T * HRP * d_model
+
+
+def bench_mixer(wid, steps, warmup, log, d_model=2048, decode_batch=128, decode_steps=64):
+    """The mixer block (projections + prologue + recurrence + gate + output projection) on a
+    prefill workload's token shape with d_model 2048 (H P = 4096 = 2 d_model, the Mamba-2
+    expansion), then decode steps at batch 128 continuing from a prefill, eager and as a graph."""
+    import torch
+    from mamba_ssm_scan_amd import binding, inputs
+    w = inputs.WORKLOADS[wid]
+    b, L, H, P, N, R = w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank
+    wt = inputs.mixer_inputs(batch=b, seqlen=L, d_model=d_model, heads=H, groups=1, headdim=P, dstate=N, rank=R,
+                             wid=700, device="cuda")
+    m = binding.Mixer(wt)
+    u, out = wt["u"], torch.empty_like(wt["u"])
+    for _ in range(warmup):
+        m.prefill(u, chunk=w.chunk, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(steps):
+        m.prefill(u, chunk=w.chunk, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    T = b * L
+    fl = mixer_gemm_flops(T, d_model, H, 1, P, N, R) + prefill_flops(b, L, H, P, N, R, w.chunk)
+    r = {"workload": f"mixer block d_model {d_model} on {w.name}", "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+         "tflops": fl / (ms * 1e-3) / 1e12, "flops": fl}
+    r["mfma_frac"] = r["tflops"] / BF16_PEAK_TFLOPS
+    log(f"mixer prefill {r['workload']}: {ms:.3f} ms/call, {r['tokens_per_s'] / 1e6:.1f} M tok/s, "
+        f"{r['tflops']:.0f} TFLOP/s ({100 * r['mfma_frac']:.1f}% bf16 MFMA)")
+
+    # decode: batch decode_batch sequences, a 64-token prefill, then steps
+    bd = decode_batch
+    wd = inputs.mixer_inputs(batch=bd, seqlen=64 + decode_steps, d_model=d_model, heads=H, groups=1, headdim=P,
+                             dstate=N, rank=R, wid=701, device="cuda")
+    md = binding.Mixer(wd)
+    st = md.decode_state(bd)
+    md.prefill(wd["u"][:, :64].contiguous(), chunk=w.chunk, state=st)
+    us = [wd["u"][:, 64 + t].contiguous() for t in range(decode_steps)]
+    outs = [torch.empty_like(us[0]) for _ in range(decode_steps)]
+    for t in range(4):
+        md.decode_step(st, us[t], outs[t])
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(decode_steps):
+        md.decode_step(st, us[t], outs[t])
+    e1.record()
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / decode_steps
+    # the same steps captured once (an even number of steps: the carry slots end where they began)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        md.decode_step(st, us[0], outs[0])
+        md.decode_step(st, us[1], outs[1])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(decode_steps):
+            md.decode_step(st, us[t], outs[t])
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(4):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gms = e0.elapsed_time(e1) / (4 * decode_steps)
+    r.update({"decode_batch": bd, "decode_ms_per_step": dms, "decode_graph_ms_per_step": gms,
+              "decode_tokens_per_s": bd / (gms * 1e-3)})
+    log(f"mixer decode step, batch {bd}: {dms * 1e3:.1f} us eager, {gms * 1e3:.1f} us as a captured graph "
+        f"({r['decode_tokens_per_s'] / 1e6:.2f} M tok/s)")
+    return r
+
+
 def bench_prologue(log, steps=20, warmup=3, wid=2, tokens=None, copies=16):
     """m3_prologue (QK-norm + bias on B, C; softplus / sigmoid on dt, lambda) on a workload's raw projections.
 
@@ -452,6 +533,8 @@ def main():
                 copy_probe(log)
             elif item in ("backward1", "backward2"):
                 bench_backward(int(item[-1]), max(2, args.steps // 4), 1, log)
+            elif item in ("mixer1", "mixer2"):
+                bench_mixer(int(item[-1]), args.steps, args.warmup, log)
             elif item == "prologue":
                 bench_prologue(log, args.steps, args.warmup)
             elif item == "prologue_decode":
@@ -490,6 +573,8 @@ def main():
         # larger state / rank on the same token shapes (the generic fp32 kernel)
         out["prefill_larger_sizes"] = {"n256_r1": bench_prefill(1, 3, 1, log, dstate=256),
                                        "n128_r8": bench_prefill(2, 3, 1, log, rank=8)}
+        # the mixer block around the recurrence (d_model 2048), prefill and batch-128 decode
+        out["mixer"] = {f"r{R}": bench_mixer(wid, max(3, args.steps // 4), 1, log) for R, wid in ((1, 1), (4, 2))}
         # the backward pass (training) on workloads 1 and 2
         out["backward"] = {f"r{R}": bench_backward(wid, 5, 1, log) for R, wid in ((1, 1), (4, 2))}
         # the input prologue on the R 4 prefill's raw projections and on one decode step's

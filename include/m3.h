@@ -250,14 +250,15 @@ size_t m3_prefill_backward_workspace_size(const m3_dims* dims, int32_t R);
  * 重构", §2.4 and Fig. 4) lists what a Mamba-3 block holds without a block
  * formula; the reading taken is the Mamba-2 block layout with those changes.
  * Per token u (d_model entries, bf16):
- *   x = u W_x, z = u W_z           [H][R][P]     (bf16)
- *   B_raw = u W_B, C_raw = u W_C   [G][R][N]     (bf16)
- *   dt_raw = u W_dt, lambda_raw = u W_lambda  [H] (fp32)
+ *   x = u W_x^T, z = u W_z^T       [H][R][P]     (bf16)
+ *   B_raw = u W_B^T, C_raw = u W_C^T   [G][R][N] (bf16)
+ *   dt_raw = u W_dt^T, lambda_raw = u W_lambda^T  [H] (fp32)
  *   B, C, dt, lambda = m3_prologue(...) with the weights' B/C norm weights and biases, dt_bias, eps
  *   y = the recurrence (m3_prefill, or m3_decode_step) with A, omega, D
- *   out = (y * silu(z)) W_out      [d_model]     (bf16; silu(v) = v sigmoid(v))
- * Weights are bf16, row-major [in][out]: W_x, W_z [d_model][H*R*P], W_B, W_C
- * [d_model][G*R*N], W_dt, W_lambda [d_model][H], W_out [H*R*P][d_model]. The
+ *   out = (y * silu(z)) W_out^T    [d_model]     (bf16; silu(v) = v sigmoid(v))
+ * Weights are bf16, row-major [out][in] as a linear layer stores them (x = u W_x^T):
+ * W_x, W_z [H*R*P][d_model], W_B, W_C [G*R*N][d_model], W_dt, W_lambda
+ * [H][d_model], W_out [d_model][H*R*P]. The
  * projections run as hipBLASLt GEMMs (fp32 accumulation); omega, the norm
  * weights, biases and dt_bias may be NULL as for m3_prologue / m3_prefill.
  * The intermediates live in the caller's workspace. A mixer object holds the

@@ -379,8 +379,8 @@ def prefill_backward(x, dt, A, omega, lam, B, C, D, R: int, dy, h0=None, dh_out=
 class Mixer:
     """The mixer block (m3_mixer_*): projections, prologue, recurrence, silu gate, output projection.
 
-    w: a dict with the bf16 weights W_x, W_z, W_B, W_C, W_dt, W_lambda [d_model][*]
-    and W_out [H*R*P][d_model] (row-major [in][out]), fp32 B_weight, B_bias,
+    w: a dict with the bf16 weights W_x, W_z, W_B, W_C, W_dt, W_lambda [*][d_model]
+    and W_out [d_model][H*R*P] (row-major [out][in], as a linear layer), fp32 B_weight, B_bias,
     C_weight, C_bias [G][R][N], dt_bias, A, D [H], omega [H][N/2] (the optional
     ones may be None), eps, and the sizes H, G, R, P, N, d_model.
     """
@@ -391,8 +391,8 @@ class Mixer:
                                                                                     "d_model"))
         HRP, GRN, dm = self.H * self.R * self.P, self.G * self.R * self.N, self.d_model
         bf, f32 = torch.bfloat16, torch.float32
-        shapes = {"W_x": (dm, HRP, bf), "W_z": (dm, HRP, bf), "W_B": (dm, GRN, bf), "W_C": (dm, GRN, bf),
-                  "W_dt": (dm, self.H, bf), "W_lambda": (dm, self.H, bf), "W_out": (HRP, dm, bf)}
+        shapes = {"W_x": (HRP, dm, bf), "W_z": (HRP, dm, bf), "W_B": (GRN, dm, bf), "W_C": (GRN, dm, bf),
+                  "W_dt": (self.H, dm, bf), "W_lambda": (self.H, dm, bf), "W_out": (dm, HRP, bf)}
         keep = {k: _need(w[k], k, dt, (r, c)) for k, (r, c, dt) in shapes.items()}
         par = (self.G, self.R, self.N)
         for k in ("B_weight", "B_bias", "C_weight", "C_bias"):

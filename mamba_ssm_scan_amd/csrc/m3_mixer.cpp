@@ -7,14 +7,17 @@
 // the trapezoid rule, MIMO inputs, QK-norm plus bias after the B/C projection,
 // no short convolution) without a block formula; the block here is the Mamba-2
 // layout with those changes:
-//   x = u W_x, z = u W_z, B_raw = u W_B, C_raw = u W_C, dt_raw = u W_dt, lambda_raw = u W_lambda
+//   x = u W_x^T, z = u W_z^T, B_raw = u W_B^T, C_raw = u W_C^T, dt_raw = u W_dt^T, lambda_raw = u W_lambda^T
 //   (B, C, dt, lambda) = prologue(...);  y = recurrence(x, dt, A, omega, lambda, B, C, D)
-//   out = (y * silu(z)) W_out
+//   out = (y * silu(z)) W_out^T          (weights [out][in], as a linear layer stores them)
 // The projections are plain library GEMMs (hipBLASLt, bf16 operands, fp32
 // accumulation; dt_raw and lambda_raw are written in fp32, the rest in bf16);
 // every other step is one of this library's kernels. Intermediates live in the
 // caller's workspace; the mixer object holds the hipBLASLt handle and the
 // chosen GEMM algorithms (per shape), so it must not be shared between threads.
+// The first call for a GEMM shape times the library's candidate algorithms on
+// the call's own operands and synchronises the stream once; calls captured in
+// a graph should therefore follow one eager call of the same sizes.
 #include <hipblaslt/hipblaslt.h>
 
 #include <cstdio>
@@ -27,6 +30,7 @@
 namespace {
 
 constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch inside the caller's workspace
+constexpr int kCandidates = 16;                       // algorithms timed per GEMM shape at first use
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -85,8 +89,9 @@ struct m3_mixer {
         if (lt) hipblasLtDestroy(lt);
     }
 
-    // D[M][N] = U[M][K] W[K][N], all row-major; U, W bf16, D bf16 (f32out = 0) or fp32.
-    // In hipBLASLt's column-major terms: D^T (N x M) = W^T (N x K) U^T (K x M), no transposes.
+    // D[M][N] = U[M][K] W[N][K]^T, all row-major (W as a linear layer stores it, [out][in]);
+    // U, W bf16, D bf16 (f32out = 0) or fp32. In hipBLASLt's column-major terms
+    // D^T (N x M) = op(W') U^T with W' the K x N matrix of W's bytes and op a transpose.
     m3_status gemm(int64_t M, int64_t N, int64_t K, const void* U, const void* W, void* D, bool f32out, void* ws,
                    hipStream_t s) {
         if (M == 0 || N == 0) return M3_OK;
@@ -95,21 +100,24 @@ struct m3_mixer {
         if (it == gemms.end()) {
             Gemm g;
             const hipDataType dtD = f32out ? HIP_R_32F : HIP_R_16BF;
+            const int32_t opT = HIPBLAS_OP_T;
             bool ok = hipblasLtMatmulDescCreate(&g.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
-                      hipblasLtMatrixLayoutCreate(&g.a, HIP_R_16BF, uint64_t(N), uint64_t(K), N) ==
+                      hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof opT) ==
+                          HIPBLAS_STATUS_SUCCESS &&
+                      hipblasLtMatrixLayoutCreate(&g.a, HIP_R_16BF, uint64_t(K), uint64_t(N), K) ==
                           HIPBLAS_STATUS_SUCCESS &&
                       hipblasLtMatrixLayoutCreate(&g.b, HIP_R_16BF, uint64_t(K), uint64_t(M), K) ==
                           HIPBLAS_STATUS_SUCCESS &&
                       hipblasLtMatrixLayoutCreate(&g.d, dtD, uint64_t(N), uint64_t(M), N) == HIPBLAS_STATUS_SUCCESS;
             hipblasLtMatmulPreference_t pref = nullptr;
             int found = 0;
-            hipblasLtMatmulHeuristicResult_t res[1];
+            hipblasLtMatmulHeuristicResult_t res[kCandidates];
             if (ok) {
                 uint64_t cap = kGemmWorkspace;
                 ok = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
                      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap,
                                                            sizeof cap) == HIPBLAS_STATUS_SUCCESS &&
-                     hipblasLtMatmulAlgoGetHeuristic(lt, g.op, g.a, g.b, g.d, g.d, pref, 1, res, &found) ==
+                     hipblasLtMatmulAlgoGetHeuristic(lt, g.op, g.a, g.b, g.d, g.d, pref, kCandidates, res, &found) ==
                          HIPBLAS_STATUS_SUCCESS &&
                      found > 0;
             }
@@ -122,16 +130,56 @@ struct m3_mixer {
                 return m3::set_error(M3_EHIP, "no hipBLASLt algorithm for a %lld x %lld x %lld bf16 GEMM (%s out)",
                                      (long long)M, (long long)N, (long long)K, f32out ? "fp32" : "bf16");
             }
-            g.algo = res[0].algo;
-            g.ws = res[0].workspaceSize;
+            // the heuristic's first choice can leave most of the chip idle on skinny
+            // shapes (few output tiles): time its candidates once on the real operands
+            // and keep the fastest (not while the stream is being captured)
+            int best = 0;
+            hipStreamCaptureStatus cap_st = hipStreamCaptureStatusNone;
+            if (found > 1 && hipStreamIsCapturing(s, &cap_st) == hipSuccess && cap_st == hipStreamCaptureStatusNone)
+                best = fastest(g, res, found, U, W, D, ws, s);
+            g.algo = res[best].algo;
+            g.ws = res[best].workspaceSize;
             it = gemms.emplace(key, g).first;
         }
         const Gemm& g = it->second;
+        return run(g, g.algo, U, W, D, ws, s);
+    }
+
+    m3_status run(const Gemm& g, const hipblasLtMatmulAlgo_t& algo, const void* U, const void* W, void* D, void* ws,
+                  hipStream_t s) {
         const float one = 1.f, zero = 0.f;
-        const hipblasStatus_t st = hipblasLtMatmul(lt, g.op, &one, W, g.a, U, g.b, &zero, D, g.d, D, g.d, &g.algo,
-                                                   ws, kGemmWorkspace, s);
+        const hipblasStatus_t st = hipblasLtMatmul(lt, g.op, &one, W, g.a, U, g.b, &zero, D, g.d, D, g.d, &algo, ws,
+                                                   kGemmWorkspace, s);
         if (st != HIPBLAS_STATUS_SUCCESS) return m3::set_error(M3_EHIP, "hipblasLtMatmul failed (%d)", int(st));
         return M3_OK;
+    }
+
+    // index of the fastest candidate: one warm-up call and 3 timed calls each (HIP events on s)
+    int fastest(const Gemm& g, const hipblasLtMatmulHeuristicResult_t* res, int n, const void* U, const void* W,
+                void* D, void* ws, hipStream_t s) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+            if (e0) hipEventDestroy(e0);
+            return 0;
+        }
+        int best = 0;
+        float best_ms = 3.0e38f;
+        for (int i = 0; i < n; ++i) {
+            if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > kGemmWorkspace) continue;
+            if (run(g, res[i].algo, U, W, D, ws, s) != M3_OK) continue;
+            hipEventRecord(e0, s);
+            for (int k = 0; k < 3; ++k) run(g, res[i].algo, U, W, D, ws, s);
+            hipEventRecord(e1, s);
+            float ms = 0.f;
+            if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
+                ms < best_ms) {
+                best_ms = ms;
+                best = i;
+            }
+        }
+        hipEventDestroy(e0);
+        hipEventDestroy(e1);
+        return best;
     }
 };
 

@@ -289,11 +289,11 @@ def mixer_inputs(*, batch, seqlen, d_model, heads, groups, headdim, dstate, rank
                  device="cpu") -> dict:
     """Synthetic weights and tokens of one mixer block (random draws only).
 
-    u [b][L][d_model] bf16 ~ N(0, 1); projection weights bf16, row-major [in][out]:
-    W_x, W_z [d_model][H*R*P] and W_B, W_C [d_model][G*R*N] and W_lambda
-    [d_model][H] ~ N(0, 1/d_model) (unit-variance outputs), W_dt [d_model][H] ~
+    u [b][L][d_model] bf16 ~ N(0, 1); projection weights bf16, row-major [out][in]:
+    W_x, W_z [H*R*P][d_model] and W_B, W_C [G*R*N][d_model] and W_lambda
+    [H][d_model] ~ N(0, 1/d_model) (unit-variance outputs), W_dt [H][d_model] ~
     N(0, 0.25/d_model) with dt_bias [H] ~ N(-1, 0.2) (so dt_raw + bias is near the
-    workloads' N(-1, 0.5)), W_out [H*R*P][d_model] ~ N(0, 1/(H*R*P)); B/C weights
+    workloads' N(-1, 0.5)), W_out [d_model][H*R*P] ~ N(0, 1/(H*R*P)); B/C weights
     ~ N(1, 0.1), biases ~ N(0, 0.1) [G][R][N] fp32; A, omega, D as the "lm" family.
     Stand-ins for trained weights, which are not available.
     """
@@ -307,11 +307,11 @@ def mixer_inputs(*, batch, seqlen, d_model, heads, groups, headdim, dstate, rank
     A, omega, D = _head_params(wid, H, N, "lm", device)
     par = lambda name, mean, std: _normal((G, R, N), _gen(device, wid, name), device, mean, std)
     return dict(u=_normal((batch, seqlen, d_model), _gen(device, wid, "u", step), device).to(bf),
-                W_x=mat("W_x", d_model, HRP, d_model ** -0.5), W_z=mat("W_z", d_model, HRP, d_model ** -0.5),
-                W_B=mat("W_B", d_model, GRN, d_model ** -0.5), W_C=mat("W_C", d_model, GRN, d_model ** -0.5),
-                W_dt=mat("W_dt", d_model, H, 0.5 * d_model ** -0.5),
-                W_lambda=mat("W_lambda", d_model, H, d_model ** -0.5),
-                W_out=mat("W_out", HRP, d_model, HRP ** -0.5),
+                W_x=mat("W_x", HRP, d_model, d_model ** -0.5), W_z=mat("W_z", HRP, d_model, d_model ** -0.5),
+                W_B=mat("W_B", GRN, d_model, d_model ** -0.5), W_C=mat("W_C", GRN, d_model, d_model ** -0.5),
+                W_dt=mat("W_dt", H, d_model, 0.5 * d_model ** -0.5),
+                W_lambda=mat("W_lambda", H, d_model, d_model ** -0.5),
+                W_out=mat("W_out", d_model, HRP, HRP ** -0.5),
                 B_weight=par("B_weight", 1.0, 0.1), B_bias=par("B_bias", 0.0, 0.1),
                 C_weight=par("C_weight", 1.0, 0.1), C_bias=par("C_bias", 0.0, 0.1),
                 dt_bias=_normal((H,), _gen(device, wid, "dt_bias"), device, -1.0, 0.2),

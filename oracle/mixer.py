@@ -10,15 +10,15 @@ bias after the B/C projection, and no short convolution. It prints no block
 formula; the reading taken is the Mamba-2 block the pages compare against, with
 those changes: per token u_t (d_model entries)
 
-  x      = u W_x        z = u W_z             [H][R][P] each (one column block per head and rank)
-  B_raw  = u W_B        C_raw = u W_C         [G][R][N]
-  dt_raw = u W_dt       lambda_raw = u W_lambda   [H]
+  x      = u W_x^T      z = u W_z^T           [H][R][P] each (one row block of W per head and rank)
+  B_raw  = u W_B^T      C_raw = u W_C^T       [G][R][N]
+  dt_raw = u W_dt^T     lambda_raw = u W_lambda^T   [H]
   B, C, dt, lambda = prologue(B_raw, C_raw, dt_raw, lambda_raw)   (QK-norm + bias, softplus, sigmoid)
   y      = the recurrence over the tokens (x, dt, A, omega, lambda, B, C, D)
-  out    = (y * silu(z)) W_out                  silu(v) = v * sigmoid(v)
+  out    = (y * silu(z)) W_out^T                silu(v) = v * sigmoid(v)
 
-Weights are row-major [in][out]. With io_round (the default) the values the
-block hands between its stages in bf16 -- x, z, B_raw, C_raw, B, C, y and the
+Weights are row-major [out][in], as a linear layer stores them. With io_round
+(the default) the values the block hands between its stages in bf16 -- x, z, B_raw, C_raw, B, C, y and the
 gated y -- are rounded to bf16 (nearest, ties to even) where they are formed,
 as the block's storage types say; dt_raw, lambda_raw, dt and lambda stay fp32
 (dt, lambda rounded to fp32). Everything else is double precision. With
@@ -66,8 +66,8 @@ def silu(v):
 def forward(w: dict, u, h0=None, io_round: bool = True, nthreads=None):
     """Block output for tokens u [b][L][d_model]; returns (out [b][L][d_model], h_L, parts).
 
-    w: W_x, W_z [d_model][H*R*P]; W_B, W_C [d_model][G*R*N]; W_dt, W_lambda
-    [d_model][H]; W_out [H*R*P][d_model]; B_weight, B_bias, C_weight, C_bias
+    w: W_x, W_z [H*R*P][d_model]; W_B, W_C [G*R*N][d_model]; W_dt, W_lambda
+    [H][d_model]; W_out [d_model][H*R*P]; B_weight, B_bias, C_weight, C_bias
     [G][R][N] (or None); dt_bias [H] (or None); A, D [H]; omega [H][N/2]; eps;
     and the sizes H, G, R, P, N. parts holds the intermediate tensors.
     """
@@ -76,7 +76,7 @@ def forward(w: dict, u, h0=None, io_round: bool = True, nthreads=None):
     H, G, R, P, N = (int(w[k]) for k in ("H", "G", "R", "P", "N"))
     u = _np64(u)
     b, L, dm = u.shape
-    W = {k: _np64(w[k]) for k in ("W_x", "W_z", "W_B", "W_C", "W_dt", "W_lambda", "W_out")}
+    W = {k: _np64(w[k]).T for k in ("W_x", "W_z", "W_B", "W_C", "W_dt", "W_lambda", "W_out")}  # [in][out] views
     x = rb(u @ W["W_x"]).reshape(b, L, H, R, P)
     z = rb(u @ W["W_z"]).reshape(b, L, H, R, P)
     B_raw = rb(u @ W["W_B"]).reshape(b, L, G, R, N)

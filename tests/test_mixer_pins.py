@@ -71,10 +71,10 @@ def test_skip_path_alone():
     u = _np(w["u"])
     b, L, _ = u.shape
     H, R, P = w["H"], w["R"], w["P"]
-    x = (u @ _np(w["W_x"])).reshape(b, L, H, R, P)
-    z = (u @ _np(w["W_z"])).reshape(b, L, H, R, P)
+    x = (u @ _np(w["W_x"]).T).reshape(b, L, H, R, P)
+    z = (u @ _np(w["W_z"]).T).reshape(b, L, H, R, P)
     y = _np(w["D"])[None, None, :, None, None] * x
-    ref = (y * z / (1.0 + np.exp(-z))).reshape(b, L, -1) @ _np(w["W_out"])
+    ref = (y * z / (1.0 + np.exp(-z))).reshape(b, L, -1) @ _np(w["W_out"]).T
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
@@ -84,24 +84,24 @@ def test_single_token_closed_form():
     u = _np(w["u"])
     b = u.shape[0]
     H, G, R, P, N = w["H"], w["G"], w["R"], w["P"], w["N"]
-    x = (u @ _np(w["W_x"])).reshape(b, H, R, P)
-    z = (u @ _np(w["W_z"])).reshape(b, H, R, P)
+    x = (u @ _np(w["W_x"]).T).reshape(b, H, R, P)
+    z = (u @ _np(w["W_z"]).T).reshape(b, H, R, P)
 
     def qk(raw, wt, bias):
         r = raw / np.sqrt(np.mean(raw * raw, axis=-1, keepdims=True) + w["eps"])
         return r * _np(wt) + _np(bias)
 
-    Bm = qk((u @ _np(w["W_B"])).reshape(b, G, R, N), w["B_weight"], w["B_bias"])
-    Cm = qk((u @ _np(w["W_C"])).reshape(b, G, R, N), w["C_weight"], w["C_bias"])
-    dt = np.log1p(np.exp((u @ _np(w["W_dt"])).reshape(b, H) + _np(w["dt_bias"])))
-    lam = 1.0 / (1.0 + np.exp(-(u @ _np(w["W_lambda"])).reshape(b, H)))
+    Bm = qk((u @ _np(w["W_B"]).T).reshape(b, G, R, N), w["B_weight"], w["B_bias"])
+    Cm = qk((u @ _np(w["W_C"]).T).reshape(b, G, R, N), w["C_weight"], w["C_bias"])
+    dt = np.log1p(np.exp((u @ _np(w["W_dt"]).T).reshape(b, H) + _np(w["dt_bias"])))
+    lam = 1.0 / (1.0 + np.exp(-(u @ _np(w["W_lambda"]).T).reshape(b, H)))
     y = np.empty((b, H, R, P))
     for bb in range(b):
         for h in range(H):
             g = h // (H // G)
             gram = Cm[bb, g] @ Bm[bb, g].T            # [R][R']: C_r . B_r'
             y[bb, h] = lam[bb, h] * dt[bb, h] * (gram @ x[bb, h]) + _np(w["D"])[h] * x[bb, h]
-    ref = (y * z / (1.0 + np.exp(-z))).reshape(b, 1, -1) @ _np(w["W_out"])
+    ref = (y * z / (1.0 + np.exp(-z))).reshape(b, 1, -1) @ _np(w["W_out"]).T
     np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
 
 
