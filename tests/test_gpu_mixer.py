@@ -90,3 +90,21 @@ def test_mixer_zero_gate_and_h0():
     assert torch.count_nonzero(out) == 0
     _, h_ref, _ = omix.forward(w, w["u"], h0=h0)
     assert _rel_per_batch(f64(h), h_ref) <= TOL
+
+
+def test_mixer_decode_batch_over_128():
+    """Batch 130 decode steps (projection GEMMs with 130 rows, more decode workgroups than
+    CUs): 3 prefill tokens, then 2 steps, against the oracle."""
+    b, L, k, dm, H, P, N, R = 130, 5, 3, 64, 2, 16, 32, 2
+    print("mixer decode at batch 130", flush=True)
+    w, d = _weights(batch=b, seqlen=L, d_model=dm, heads=H, groups=1, headdim=P, dstate=N, rank=R, wid=695)
+    m = binding.Mixer(d)
+    st = m.decode_state(b)
+    out_pre, _ = m.prefill(d["u"][:, :k].contiguous(), state=st)
+    outs = [m.decode_step(st, d["u"][:, t].contiguous()) for t in range(k, L)]
+    torch.cuda.synchronize()
+    ref, h_ref, _ = omix.forward(w, w["u"])
+    e_dec = _rel_per_batch(f64(torch.stack(outs, 1)), ref[:, k:])
+    e_h = _rel_per_batch(f64(st.h), h_ref)
+    print(f"  decode out {e_dec:.2e}, state {e_h:.2e}", flush=True)
+    assert e_dec <= TOL and e_h <= TOL
