@@ -173,8 +173,15 @@ def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
          "us_per_step": ms_step * 1e3, "steps_per_s": 1e3 / ms_step, "hbm_gbs": by / (ms_step * 1e-3) / 1e9,
          "bytes_per_step": by}
     r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
+    # the rank-R contractions of a step (u_t = B_t x_t^T and y_t = h_t^T C_t, 2 N P R flops each per
+    # head; the previous token's u is the last step's): what the MFMA decode kernel puts on the matrix
+    # cores at R 2/4, against the bf16 peak -- tiny, the step is bound by the state stream
+    fl = 4 * b * w.heads * w.dstate * w.headdim * R
+    r["mfma_tflops"] = fl / (ms_step * 1e-3) / 1e12
+    r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
     log(f"decode R={R} b={b}: {ms_step * 1e3:.1f} us/step, {r['steps_per_s']:.0f} steps/s, "
-        f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM)")
+        f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM), rank contractions "
+        f"{r['mfma_tflops']:.1f} TFLOP/s ({100 * r['mfma_frac']:.2f}% of bf16 MFMA peak)")
     return r
 
 
