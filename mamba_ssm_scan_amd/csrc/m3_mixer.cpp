@@ -254,7 +254,6 @@ size_t m3_mixer_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, in
 m3_status m3_mixer_prefill(m3_mixer* m, const m3_mixer_weights* w, const m3_dims* dims, int32_t R, int32_t chunk,
                            const void* u, void* out, const float* h0, float* h_out, m3_decode_state* st,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    if (!m) return m3::set_error(M3_EINVAL, "mixer is NULL");
     m3_status s = check_weights(w);
     if (s != M3_OK) return s;
     if (!dims) return m3::set_error(M3_EINVAL, "dims is NULL");
@@ -273,6 +272,7 @@ m3_status m3_mixer_prefill(m3_mixer* m, const m3_mixer_weights* w, const m3_dims
         if (dims->batch > 0 && (!st->h || !st->carry_B || !st->carry_x))
             return m3::set_error(M3_EINVAL, "decode state buffers are not bound");
     }
+    if (!m) return m3::set_error(M3_EINVAL, "mixer is NULL");
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     float* hfin = st ? st->h : h_out;
@@ -317,7 +317,6 @@ m3_status m3_mixer_prefill(m3_mixer* m, const m3_mixer_weights* w, const m3_dims
 
 m3_status m3_mixer_decode_step(m3_mixer* m, const m3_mixer_weights* w, m3_decode_state* st, const void* u_t,
                                void* out_t, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!m) return m3::set_error(M3_EINVAL, "mixer is NULL");
     m3_status s = check_weights(w);
     if (s != M3_OK) return s;
     if (!st) return m3::set_error(M3_EINVAL, "state is NULL");
@@ -330,8 +329,9 @@ m3_status m3_mixer_decode_step(m3_mixer* m, const m3_mixer_weights* w, m3_decode
     if (!workspace || workspace_bytes < L.total)
         return m3::set_error(M3_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
     const int64_t b = d.batch;
+    if (b > 0 && (!u_t || !out_t)) return m3::set_error(M3_EINVAL, "u_t and out_t must not be NULL");
+    if (!m) return m3::set_error(M3_EINVAL, "mixer is NULL");
     if (b == 0) return M3_OK;
-    if (!u_t || !out_t) return m3::set_error(M3_EINVAL, "u_t and out_t must not be NULL");
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     if ((s = project_in(m, w, &d, R, b, u_t, ws, L, hs)) != M3_OK) return s;

@@ -283,3 +283,45 @@ def test_backward_argument_errors(lib):
     assert st == 7 and "workspace" in msg
     # no tokens: valid, nothing launched
     assert _backward(lib, _dims(b=0))[0] == 0
+
+
+def _mixer_weights(**over):
+    names = ["W_x", "W_z", "W_B", "W_C", "W_dt", "W_lambda", "W_out", "B_weight", "B_bias", "C_weight", "C_bias",
+             "dt_bias", "A", "omega", "D"]
+    ptr = {n: FAKE + (60 + i) * (1 << 30) for i, n in enumerate(names)}
+    ptr.update({k: v for k, v in over.items() if k in ptr})
+    return bd.M3MixerWeights(over.get("d_model", 64), *[ptr[n] for n in names], over.get("eps", 1e-6))
+
+
+def test_mixer_argument_errors(lib):
+    """Every check of m3_mixer_prefill / m3_mixer_decode_step runs before the mixer object is used."""
+    d = _dims(b=2, L=10, H=2, P=16, N=32)
+    need = lib.m3_mixer_workspace_size(ctypes.byref(d), 1, 64, 64)
+    assert need > 0
+    assert lib.m3_mixer_workspace_size(ctypes.byref(_dims(N=15)), 1, 64, 64) == 0
+    assert lib.m3_mixer_workspace_size(ctypes.byref(d), 1, 64, 0) == 0
+    ws, u, out = ctypes.c_void_p(FAKE + 90 * (1 << 30)), ctypes.c_void_p(FAKE + 91 * (1 << 30)), \
+        ctypes.c_void_p(FAKE + 92 * (1 << 30))
+
+    def pre(w, dims=d, ws_bytes=need):
+        st = lib.m3_mixer_prefill(None, None if w is None else ctypes.byref(w), ctypes.byref(dims), 1, 64, u, out,
+                                  None, None, None, ws, ws_bytes, None)
+        return st, lib.m3_last_error().decode()
+
+    assert pre(None)[0] == 1
+    st, msg = pre(_mixer_weights(W_x=None))
+    assert st == 1 and "W_x" in msg
+    assert pre(_mixer_weights(d_model=0))[0] == 1
+    assert pre(_mixer_weights(eps=-1.0))[0] == 1
+    assert pre(_mixer_weights(), dims=_dims(N=15))[0] == 1
+    st, msg = pre(_mixer_weights(), ws_bytes=need - 1)
+    assert st == 7 and "workspace" in msg
+    st, msg = pre(_mixer_weights())                     # everything else valid
+    assert st == 1 and "mixer" in msg
+    # decode step: the state is checked first
+    st = lib.m3_mixer_decode_step(None, ctypes.byref(_mixer_weights()), None, u, out, ws, need, None)
+    assert st == 1 and "state" in lib.m3_last_error().decode()
+    s = bd.M3DecodeState()
+    s.R, s.io_dtype, s.dims = 1, bd.M3_F32, _dims(b=2, L=1, H=2, P=16, N=32)
+    assert lib.m3_mixer_decode_step(None, ctypes.byref(_mixer_weights()), ctypes.byref(s), u, out, ws, need,
+                                    None) == 3
