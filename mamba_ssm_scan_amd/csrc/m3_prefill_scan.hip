@@ -8,16 +8,20 @@
 //   y_t = h^T C_t + D x_t,    U_t = B_t x_t^T (rank R),
 // with alpha = e^{dt A}, gamma = lambda dt, delta = (1 - lambda) dt.
 //
-// One 256-thread workgroup per (b, h); wave w owns state columns 16 w .. 16 w + 15.
-// In row tile nt, lane (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column
-// 16 w + l16 (two whole rotation pairs), which is the accumulator layout of
+// One workgroup per (b, h): wave w owns state columns 16 (w % 4) .. + 15 and,
+// at N above 128 with R <= 4, half of the row tiles (512 threads, two waves per
+// SIMD whose per-token chains overlap). In row tile nt, lane (l16, g4) holds rows
+// 16 nt + 4 g4 .. + 3 of its column (two whole rotation pairs), which is the
+// accumulator layout of
 // v_mfma_f32_16x16x16_bf16, so
 //   U_t[n][p]  = sum_r B_t[r][n] x_t[r][p]   (A: B^T, k = rank; B: x)
 // lands in the lanes that own h[n][p], and
 //   y_t[r][p]  = sum_n C_t[r][n] h[n][p]     (A: C, k = n; B: the new state)
 // takes the lane's four new state values, rounded to bf16, as its B operand
 // (as the chunked kernels feed the carried state to their inter-chunk term;
-// the products in U are exact). No cross-lane reduction is left. Only one
+// the products in U are exact). No cross-lane reduction is left; with the rows
+// split, the two halves' y sums are added in LDS and the block's y is written
+// once, coalesced. Only one
 // operand of each product needs its padding zeroed: x^T past rank R (so the
 // A operand of U may hold any finite values there), and the output rows of y
 // past R are not stored (so the A operand of y takes a clamped row).
@@ -41,7 +45,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short shortx4_tr __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;  // threads: 4 waves, 16 state columns each
+
 constexpr float kInv2Pi = 0.15915494309189535f;
 
 __device__ __forceinline__ u32x2 load_tr(const uint16_t* p) {
@@ -61,10 +65,13 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(unsigned, v);
 }
 
-// sizes of one instance: NTL row tiles (N <= 16 NTL), RG groups of 4 ranks (R <= 4 RG)
-template <int NTL, int RG>
+// sizes of one instance: NTL row tiles (N <= 16 NTL), RG groups of 4 ranks (R <= 4 RG),
+// RS waves per 16-column group, each holding NTL / RS row tiles
+template <int NTL, int RG, int RS>
 struct ScanShape {
+    static constexpr int NT = 256 * RS;                         // threads: 4 column groups x RS
     static constexpr int NMAX = 16 * NTL, KMAX = NMAX / 2, RK = 4 * RG;
+    static constexpr int NTW = NTL / RS;                        // row tiles per wave
     static constexpr int BT = (NTL == 16 && RG == 2) ? 8 : 16;  // tokens per staged block
     static constexpr int NS = NMAX + 4;                         // B, C row stride (bf16)
     static constexpr int XS = 64 + 4;                           // x row stride (bf16)
@@ -74,21 +81,22 @@ struct ScanShape {
     static constexpr int MAXCS = BT * KMAX / NT;
 };
 
-template <int NTL, int RG>
+template <int NTL, int RG, int RS>
 struct ScanLds {
-    typedef ScanShape<NTL, RG> S;
+    typedef ScanShape<NTL, RG, RS> S;
     uint16_t B[S::BT][S::RK][S::NS];  // B rank rows of the block's tokens (rows past R zero)
     uint16_t X[S::BT][S::RK][S::XS];  // x rank rows (rows past R zero)
     uint16_t C[S::BT][S::RK][S::NS];  // C rank rows
     float CS[S::BT][S::KMAX][2];        // alpha * (cos, sin) of each pair's step angle
     float GD[S::BT][2];                 // gamma, delta
+    float Y[RS > 1 ? S::BT : 1][S::RK][64];  // y of the block: the row parts' sums meet here (RS > 1)
 };
 
-template <int NTL, int RG, bool FULL>
-__global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
-    typedef ScanShape<NTL, RG> S;
-    constexpr int BT = S::BT;
-    __shared__ __attribute__((aligned(16))) ScanLds<NTL, RG> s;
+template <int NTL, int RG, bool FULL, int RS>
+__global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
+    typedef ScanShape<NTL, RG, RS> S;
+    constexpr int BT = S::BT, NT = S::NT;
+    __shared__ __attribute__((aligned(16))) ScanLds<NTL, RG, RS> s;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,8 +111,9 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
     const int g = h / (a.H / a.G);
     const int N = FULL ? S::NMAX : a.N, P = a.P, R = a.R, K = N / 2, ntl = FULL ? NTL : N / 16;
     const int64_t L = a.L;
-    const int p = 16 * w + l16;
-    const bool active = 16 * w < P;  // uniform per wave
+    const int cw = w & 3, rh = w >> 2;  // column group, half of the row tiles
+    const int p = 16 * cw + l16;
+    const bool active = 16 * cw < P;    // uniform per wave
     const float Ah = a.A[h], Dh = a.D[h];
     const float* omh = a.omega ? a.omega + int64_t(h) * K : nullptr;
     const int64_t rowB = int64_t(a.G) * R * N, rowX = int64_t(a.H) * R * P;  // per-token strides
@@ -128,13 +137,14 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
     // The walk carries g_t = h_t + delta_{t+1} U_t, the state the next step turns:
     //   h_t = alpha_t Rot g_{t-1} + gamma_t U_t,  y_t = h_t^T C_t + D x_t,  g_t = h_t + delta_{t+1} U_t
     // so U_t is formed once. g_0 = h0 + delta_1 U_0 with U_0 from the caller's carry.
-    float st[NTL][4];
+    // wave (cw, rh) holds row tiles rh NTW .. rh NTW + NTW - 1 of its 16 columns
+    float st[S::NTW][4];
 #pragma unroll
-    for (int nt = 0; nt < NTL; ++nt)
+    for (int i = 0; i < S::NTW; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int n = 16 * nt + 4 * g4 + e;
-            st[nt][e] = (a.h0 && active && nt < ntl) ? a.h0[(bh * N + n) * int64_t(P) + p] : 0.f;
+            const int nt = rh * S::NTW + i, n = 16 * nt + 4 * g4 + e;
+            st[i][e] = (a.h0 && active && nt < ntl) ? a.h0[(bh * N + n) * int64_t(P) + p] : 0.f;
         }
     const u32x2 zero = {0u, 0u};
     const int gk = g4 < RG ? g4 : 0;  // in-range rank group for the lanes whose operand is zero
@@ -151,16 +161,18 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
         __syncthreads();
         const float d1 = delta_at(0);
         if (active) {
-            const u32x2 xv = load_tr(&s.X[0][4 * gk + (l16 >> 2)][16 * w + 4 * (l16 & 3)]);
+            const u32x2 xv = load_tr(&s.X[0][4 * gk + (l16 >> 2)][16 * cw + 4 * (l16 & 3)]);
             const u32x2 xo = g4 < RG ? xv : zero;
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
+            for (int i = 0; i < S::NTW; ++i) {
+                const int nt = rh * S::NTW + i;
                 if (FULL || nt < ntl) {
                     const u32x2 ab = load_tr(&s.B[0][4 * gk + (l16 >> 2)][16 * nt + 4 * (l16 & 3)]);
                     const floatx4 U = mfma16(ab, xo, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) st[nt][e] += d1 * U[e];
+                    for (int e = 0; e < 4; ++e) st[i][e] += d1 * U[e];
                 }
+            }
         }
     }
 
@@ -237,18 +249,20 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
             s.GD[tid][0] = (lmg ? lmg[t * a.H] : 1.f) * dtg[t * a.H];
             s.GD[tid][1] = delta_at(t + 1);
         }
+        if constexpr (RS > 1)
+            for (int e = tid; e < BT * S::RK * 64; e += NT) (&s.Y[0][0][0])[e] = 0.f;
         __syncthreads();
-        if (!active) continue;
 
-        for (int j = 0; j < nt_; ++j) {
+        for (int j = 0; j < (active ? nt_ : 0); ++j) {
             const float gam = s.GD[j][0], dnx = s.GD[j][1];
-            const u32x2 xv = load_tr(&s.X[j][4 * gk + (l16 >> 2)][16 * w + 4 * (l16 & 3)]);
+            const u32x2 xv = load_tr(&s.X[j][4 * gk + (l16 >> 2)][16 * cw + 4 * (l16 & 3)]);
             const u32x2 xo = g4 < RG ? xv : zero;
             floatx4 yacc[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) yacc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
+            for (int i = 0; i < S::NTW; ++i) {
+                const int nt = rh * S::NTW + i;
                 if (!FULL && nt >= ntl) continue;
                 const int n0 = 16 * nt;
                 const u32x2 ab = load_tr(&s.B[j][4 * gk + (l16 >> 2)][n0 + 4 * (l16 & 3)]);
@@ -259,26 +273,36 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int hp = 0; hp < 2; ++hp) {
                     const float c = cs[2 * hp], sn = cs[2 * hp + 1];
-                    const float g0 = st[nt][2 * hp], g1 = st[nt][2 * hp + 1];
+                    const float g0 = st[i][2 * hp], g1 = st[i][2 * hp + 1];
                     nv[2 * hp] = (c * g0 - sn * g1) + gam * U[2 * hp];
                     nv[2 * hp + 1] = (sn * g0 + c * g1) + gam * U[2 * hp + 1];
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) st[nt][e] = nv[e] + dnx * U[e];
+                for (int e = 0; e < 4; ++e) st[i][e] = nv[e] + dnx * U[e];
                 const u32x2 hb = {pk_bf16(nv[0], nv[1]), pk_bf16(nv[2], nv[3])};
                 const u32x2 ac = *reinterpret_cast<const u32x2*>(&s.C[j][rc][n0 + 4 * g4]);
-                yacc[nt & 3] = mfma16(ac, hb, yacc[nt & 3]);
+                yacc[i & 3] = mfma16(ac, hb, yacc[i & 3]);
             }
-            // lane (l16, g4) holds y[r = 4 g4 + e][p]
-            uint16_t* yrow = Yg + (t0 + j) * rowX;
+            // lane (l16, g4) holds this wave's part of y[r = 4 g4 + e][p]
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g4 + e;
-                if (r < R) {
-                    const float xv = bf16_to_f32(s.X[j][r][p]);
-                    const float v = (yacc[0][e] + yacc[1][e]) + (yacc[2][e] + yacc[3][e]);
-                    yrow[r * P + p] = f32_to_bf16(v + Dh * xv);
-                }
+                if (r >= R) continue;
+                const float v = (yacc[0][e] + yacc[1][e]) + (yacc[2][e] + yacc[3][e]);
+                if constexpr (RS > 1)  // two parts added onto zero: the order does not change the result
+                    atomicAdd(&s.Y[j][r][p], v);
+                else
+                    Yg[(t0 + j) * rowX + r * P + p] = f32_to_bf16(v + Dh * bf16_to_f32(s.X[j][r][p]));
+            }
+        }
+        if constexpr (RS > 1) {
+            __syncthreads();
+            // y of the block: D x added, rounded, one 64-column row per wave and step
+            for (int q = w; q < nrow; q += NT / 64) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                if (lane < P)
+                    Yg[(t0 + j) * rowX + r * P + lane] =
+                        f32_to_bf16(s.Y[j][r][lane] + Dh * bf16_to_f32(s.X[j][r][lane]));
             }
         }
     }
@@ -286,19 +310,21 @@ __global__ void __launch_bounds__(NT) prefill_scan_kernel(PrefillArgs a) {
     // after the last token delta_{L+1} = 0, so the carried g is h_L
     if (a.h_out && active)
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt)
+        for (int i = 0; i < S::NTW; ++i) {
+            const int nt = rh * S::NTW + i;
             if (FULL || nt < ntl)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a.h_out[(bh * N + 16 * nt + 4 * g4 + e) * int64_t(P) + p] = st[nt][e];
+                for (int e = 0; e < 4; ++e) a.h_out[(bh * N + 16 * nt + 4 * g4 + e) * int64_t(P) + p] = st[i][e];
+        }
 }
 
-template <int NTL, int RG>
+template <int NTL, int RG, int RS>
 hipError_t launch_ntl_rg(const PrefillArgs& a) {
+    const dim3 grid(unsigned(a.b * a.H)), block(256 * RS);
     if (a.N == 16 * NTL)
-        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, true>), dim3(unsigned(a.b * a.H)), dim3(NT), 0, a.stream, a);
+        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, true, RS>), grid, block, 0, a.stream, a);
     else
-        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, false>), dim3(unsigned(a.b * a.H)), dim3(NT), 0, a.stream,
-                           a);
+        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, false, RS>), grid, block, 0, a.stream, a);
     return hipGetLastError();
 }
 
@@ -311,8 +337,11 @@ bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io) {
 hipError_t launch_prefill_scan(const PrefillArgs& a) {
     if (a.b * a.H > 0x7fffffff) return hipErrorInvalidValue;
     if (!scan_path_supported(a.P, a.N, a.R, a.io)) return hipErrorInvalidValue;
-    if (a.N <= 128) return a.R <= 4 ? launch_ntl_rg<8, 1>(a) : launch_ntl_rg<8, 2>(a);
-    return a.R <= 4 ? launch_ntl_rg<16, 1>(a) : launch_ntl_rg<16, 2>(a);
+    // N <= 128: one wave per 16 columns (8 row tiles each). N <= 256: two waves of 8 row
+    // tiles at R <= 4 (3.5 -> 2.4 ms at N 256, R 1 on b 4 x H 64 x L 2048); at R 5..8 the
+    // larger blocks' staging and the LDS sums cost more than the overlap gains (4.5 vs 5.1 ms)
+    if (a.N <= 128) return a.R <= 4 ? launch_ntl_rg<8, 1, 1>(a) : launch_ntl_rg<8, 2, 1>(a);
+    return a.R <= 4 ? launch_ntl_rg<16, 1, 2>(a) : launch_ntl_rg<16, 2, 1>(a);
 }
 
 }  // namespace m3

@@ -26,6 +26,7 @@ PCASES = [
     (2, 41, 4, 2, 64, 128, 3, "bf16", 64),    # R 3 (the MFMA kernels take 1, 2, 4); b*H = 8: XCD order
     (1, 33, 2, 1, 32, 64, 5, "bf16", 64),     # P 32 (two waves idle), N 64, R 5
     (1, 17, 2, 1, 48, 208, 7, "bf16", 64),    # N 208 (13 row tiles), P 48, R 7
+    (1, 37, 2, 1, 48, 208, 3, "bf16", 64),    # N 208 with R 3: rows split over two waves, a partial half
     (3, 1, 2, 1, 64, 256, 2, "bf16", 64),     # one token
     (1, 45, 2, 1, 16, 256, 8, "f32", 16),     # fp32: the generic kernel
 ]
