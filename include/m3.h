@@ -226,7 +226,7 @@ m3_status m3_prologue(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int64_t
  * The forward inputs are those of m3_prefill (same layouts, same NULL rules for
  * omega, lambda, h0 and the carry). dlambda, domega and dh0 may be NULL (not
  * wanted); dcarry_B / dcarry_x are given together, and only with the carry.
- * Supported: N <= 128, P <= 64, R <= 4 (else M3_EUNSUPPORTED). The arithmetic is
+ * Supported: N <= 128, P <= 64 (even with bf16 I/O), R <= 4 (else M3_EUNSUPPORTED). The arithmetic is
  * fp32; the states are recomputed from checkpoints kept in `workspace` (at least
  * m3_prefill_backward_workspace_size() bytes). The summed gradients are added
  * with device atomics, so their last bits can vary from call to call. No

@@ -182,34 +182,108 @@ struct Bw {
             reinterpret_cast<uint16_t*>(&dst.w)[r] = src ? reinterpret_cast<const uint16_t*>(src)[i] : uint16_t(0);
         }
     }
-    // Stage tokens [t0, t1): B, x also of t0 - 1; C, dy only when full. One pass of
-    // global loads for the whole block (its latency is paid once per block).
+    // Stage tokens [t0, t1): B, x also of t0 - 1; C, dy only when full. Every global
+    // load of the block is issued before the first LDS store (its latency is paid
+    // once per block). Rows are copied a 32-bit word at a time: a row is the N (or P)
+    // entries of one (token, rank), word i holds entries EPW i .. EPW i + EPW - 1, and
+    // they land in the LDS rows' rank slot r (the ranks of an LDS row are contiguous).
+    static constexpr int EPW = 4 / int(sizeof(T));          // entries per 32-bit word
+    static constexpr int WN = 2 * KMAX / EPW, WP = PMAX / EPW;  // most words per B/C, x/dy row
+    static constexpr int PB = NT / WN, PX = NT / WP;           // rows per pass
+    static constexpr int MB = ((BT + 1) * RK + PB - 1) / PB, MC = (BT * RK + PB - 1) / PB;
+    static constexpr int MX = ((BT + 1) * RK + PX - 1) / PX, MY = (BT * RK + PX - 1) / PX;
+    __device__ static void put_word(Row<T, RK>* row, int r, uint32_t v) {  // entries EPW i .. of rows row[0..]
+        if constexpr (sizeof(T) == 4) {
+            reinterpret_cast<float*>(&row[0].w)[r] = __uint_as_float(v);
+        } else {
+            reinterpret_cast<uint16_t*>(&row[0].w)[r] = uint16_t(v);
+            reinterpret_cast<uint16_t*>(&row[1].w)[r] = uint16_t(v >> 16);
+        }
+    }
     __device__ void load_block(int64_t t0, int64_t t1, bool full) {
         const int nt = int(t1 - t0), R = a.R, N = a.N, P = a.P;
-        const int nB = (nt + 1) * R * N, nX = (nt + 1) * R * P;
-        const int nC = full ? nt * R * N : 0, nY = full ? nt * R * P : 0;
-        const int total = nB + nX + nC + nY;
-        for (int e = tid; e < total; e += NT) {
-            if (e < nB) {
-                const int j = e / (R * N), q = e % (R * N), r = q / N, n = q % N;
-                put(s.B[j][n], r, brow(t0 - 1 + j), int64_t(r) * N + n);
-            } else if (e < nB + nX) {
-                const int f = e - nB, j = f / (R * P), q = f % (R * P), r = q / P, p = q % P;
-                put(s.X[j][p], r, xrow(t0 - 1 + j), int64_t(r) * P + p);
-            } else if (e < nB + nX + nC) {
-                const int f = e - nB - nX, j = f / (R * N), q = f % (R * N), r = q / N, n = q % N;
-                put(s.C[j][n], r, static_cast<const T*>(a.C) + ((b * a.L + t0 + j) * a.G + g) * int64_t(R * N),
-                    int64_t(r) * N + n);
-            } else {
-                const int f = e - nB - nX - nC, j = f / (R * P), q = f % (R * P), r = q / P, p = q % P;
-                put(s.DY[j][p], r, static_cast<const T*>(a.dy) + ((b * a.L + t0 + j) * a.H + h) * int64_t(R * P),
-                    int64_t(r) * P + p);
+        const int wn = N / EPW, wp = P / EPW;  // N even; P even for bf16 (checked by the host)
+        const unsigned invR = (65536u + unsigned(R) - 1u) / unsigned(R);  // q / R exact for q < 16384
+        const int bi = tid % WN, bq = tid / WN, xi = tid % WP, xq = tid / WP;
+        uint32_t vb[MB], vc[MC], vx[MX], vy[MY];
+        const int nbr = (nt + 1) * R, ncr = full ? nt * R : 0;
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+            const int q = bq + u * PB;
+            if (q < nbr && bi < wn) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                const T* src = brow(t0 - 1 + j);
+                vb[u] = src ? reinterpret_cast<const uint32_t*>(src + int64_t(r) * N)[bi] : 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MC; ++u) {
+            const int q = bq + u * PB;
+            if (q < ncr && bi < wn) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                const T* src = static_cast<const T*>(a.C) + ((b * a.L + t0 + j) * a.G + g) * int64_t(R * N);
+                vc[u] = reinterpret_cast<const uint32_t*>(src + int64_t(r) * N)[bi];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MX; ++u) {
+            const int q = xq + u * PX;
+            if (q < nbr && xi < wp) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                const T* src = xrow(t0 - 1 + j);
+                vx[u] = src ? reinterpret_cast<const uint32_t*>(src + int64_t(r) * P)[xi] : 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MY; ++u) {
+            const int q = xq + u * PX;
+            if (q < ncr && xi < wp) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                const T* src = static_cast<const T*>(a.dy) + ((b * a.L + t0 + j) * a.H + h) * int64_t(R * P);
+                vy[u] = reinterpret_cast<const uint32_t*>(src + int64_t(r) * P)[xi];
+            }
+        }
+        float dtv = 0.f, lmv = 0.f;
+        if (tid < nt) {
+            const int64_t i = (b * a.L + t0 + tid) * a.H + h;
+            dtv = a.dt[i];
+            lmv = lam_at(a.lam, i);
+        }
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+            const int q = bq + u * PB;
+            if (q < nbr && bi < wn) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                put_word(&s.B[j][EPW * bi], r, vb[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MC; ++u) {
+            const int q = bq + u * PB;
+            if (q < ncr && bi < wn) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                put_word(&s.C[j][EPW * bi], r, vc[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MX; ++u) {
+            const int q = xq + u * PX;
+            if (q < nbr && xi < wp) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                put_word(&s.X[j][EPW * xi], r, vx[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MY; ++u) {
+            const int q = xq + u * PX;
+            if (q < ncr && xi < wp) {
+                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
+                put_word(&s.DY[j][EPW * xi], r, vy[u]);
             }
         }
         if (tid < nt) {
-            const int64_t i = (b * a.L + t0 + tid) * a.H + h;
-            s.dt[tid] = a.dt[i];
-            s.lam[tid] = lam_at(a.lam, i);
+            s.dt[tid] = dtv;
+            s.lam[tid] = lmv;
         }
     }
     __device__ float om_k() const { return k < K ? om_at(a.omega ? a.omega + int64_t(h) * K : nullptr, k) : 0.f; }

@@ -384,6 +384,8 @@ m3_status m3_prefill_backward(const void* x, const float* dt, const float* A, co
     if (!m3::backward_supported((int32_t)P, (int32_t)N, R))
         return fail(M3_EUNSUPPORTED, "backward supports N <= 128, P <= 64, R <= 4 (got N %lld, P %lld, R %d)",
                     (long long)N, (long long)P, R);
+    if (io_dtype == M3_BF16 && (P % 2))
+        return fail(M3_EUNSUPPORTED, "bf16 backward needs an even head dim P (got %lld)", (long long)P);
     const bool tokens = b > 0 && L > 0;
     struct Req { const char* name; const void* p; bool needed; };
     const Req req[] = {{"x", x, tokens}, {"dt", dt, tokens}, {"B", B, tokens}, {"C", C, tokens},

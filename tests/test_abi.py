@@ -267,6 +267,7 @@ def test_backward_argument_errors(lib):
     assert _backward(lib, _dims(N=256))[0] == 5
     assert _backward(lib, _dims(P=65))[0] == 5
     assert _backward(lib, _dims(), R=5)[0] == 5
+    assert _backward(lib, _dims(P=7), io=bd.M3_BF16)[0] == 5                  # odd P with bf16
     st, msg = _backward(lib, _dims(), dy=None)
     assert st == 1 and "dy" in msg
     st, msg = _backward(lib, _dims(), cB=FAKE + 40 * (1 << 30))
