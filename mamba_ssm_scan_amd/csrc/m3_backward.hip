@@ -106,6 +106,18 @@ struct Block {
     float dt[BT], lam[BT];
 };
 
+constexpr float kInv2Pi = 0.15915494309189535f;
+
+// e^{dt A} and (sin, cos)(dt omega) of one step: the hardware exp2 and the
+// hardware sine / cosine, which take revolutions (the per-step angle is a few
+// radians at most, so after fract() the result is good to ~1e-6 absolute)
+__device__ __forceinline__ float step_decay(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ void step_sincos(float theta, float* s, float* c) {
+    const float r = __builtin_amdgcn_fractf(theta * kInv2Pi);
+    *s = __builtin_amdgcn_sinf(r);
+    *c = __builtin_amdgcn_cosf(r);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
@@ -308,9 +320,9 @@ struct Bw {
         float u[2][4];
         outer(j + 1, u);
         const float d = s.dt[j], l = s.lam[j];
-        const float al = expf(d * A), gam = l * d, del = (1.f - l) * d;
+        const float al = step_decay(d * A), gam = l * d, del = (1.f - l) * d;
         float sn, cs;
-        sincosf(d * om, &sn, &cs);
+        step_sincos(d * om, &sn, &cs);
         const float ca = al * cs, sa = al * sn;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -401,9 +413,9 @@ __global__ void __launch_bounds__(NT) backward_kernel(BackwardArgs a) {
             load8(scr + j * int64_t(STATE) + tid * SV, ht);
             w.outer(j, uq);
             const float d = sBlk.dt[j], l = sBlk.lam[j];
-            const float al = expf(d * A), gam = l * d, del = (1.f - l) * d;
+            const float al = step_decay(d * A), gam = l * d, del = (1.f - l) * d;
             float sn, cs;
-            sincosf(d * om, &sn, &cs);
+            step_sincos(d * om, &sn, &cs);
             const Vr<RK> c0 = sBlk.C[j][2 * k].get(), c1 = sBlk.C[j][2 * k + 1].get();
             const Vr<RK> b0 = sBlk.B[j + 1][2 * k].get(), b1 = sBlk.B[j + 1][2 * k + 1].get();
             float dc0[RK], dc1[RK], db0[RK], db1[RK];
