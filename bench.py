@@ -87,7 +87,8 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
     """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
 
     groups: 1 (B, C shared by all heads, the primary reading) or H (one B, C per head).
-    dstate / rank: the workload's shape with a larger state or rank (N 256, R 8: the generic kernel).
+    dstate / rank: the workload's shape with another state size or rank (N 256 or R 8: the token-walk
+    kernel; N 64: the chunked kernels with the rows zero-padded).
     """
     import dataclasses
     import torch
@@ -524,8 +525,8 @@ def main():
                 bench_prefill(1, args.steps, args.warmup, log)
             elif item == "prefill2":
                 bench_prefill(2, args.steps, args.warmup, log)
-            elif item == "prefill1_n256":
-                bench_prefill(1, args.steps, args.warmup, log, dstate=256)
+            elif item in ("prefill1_n256", "prefill1_n64", "prefill2_n64"):
+                bench_prefill(int(item[7]), args.steps, args.warmup, log, dstate=int(item[10:]))
             elif item == "prefill2_r8":
                 bench_prefill(2, args.steps, args.warmup, log, rank=8)
             elif item in ("prefill1_g64", "prefill2_g64"):
@@ -577,9 +578,12 @@ def main():
         # the secondary reading: one B, C per head (64x the B/C bytes)
         out["prefill_groups_eq_heads"] = {f"r{w}": bench_prefill(wid, args.steps, args.warmup, log, groups=64)
                                           for w, wid in ((1, 1), (4, 2))}
-        # larger state / rank on the same token shapes (the generic fp32 kernel)
+        # larger state / rank on the same token shapes (the token-walk kernel)
         out["prefill_larger_sizes"] = {"n256_r1": bench_prefill(1, 3, 1, log, dstate=256),
                                        "n128_r8": bench_prefill(2, 3, 1, log, rank=8)}
+        # half the state (N 64) on the same token shapes (the chunked kernels, rows zero-padded)
+        out["prefill_smaller_state"] = {f"n64_r{R}": bench_prefill(wid, args.steps, args.warmup, log, dstate=64)
+                                        for R, wid in ((1, 1), (4, 2))}
         # the mixer block around the recurrence (d_model 2048), prefill and batch-128 decode
         out["mixer"] = {f"r{R}": bench_mixer(wid, max(3, args.steps // 4), 1, log) for R, wid in ((1, 1), (4, 2))}
         # the backward pass (training) on workloads 1 and 2

@@ -127,6 +127,8 @@ PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32
         w.state_off = off;
         off += up256(bh * size_t(N) * size_t(P) * 4);
     } else if (segments > 1) {
+        // segment states of the chunked kernels, which hold N below 128 zero-padded to 128 rows
+        N = path == M3_PATH_MFMA ? 128 : N;
         const size_t nseg = bh * size_t(segments);
         w.ctrl_off = off;
         off += up256(256 + nseg * 4);

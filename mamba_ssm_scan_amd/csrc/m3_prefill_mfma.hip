@@ -1,5 +1,8 @@
 // m3_prefill_mfma.hip -- chunked prefill on bf16 MFMA (gfx950), N = 128, P = 64,
-// rank R in {1, 2, 4}, chunk <= 64 tokens, bf16 I/O, fp32 state.
+// rank R in {1, 2, 4}, chunk <= 64 tokens, bf16 I/O, fp32 state. A smaller
+// state (N a multiple of 8 below 128) runs zero-padded to 128 rows: the B and
+// C rows past N load as zero, so those state rows stay zero and add nothing to
+// the scores or outputs; h0, h_out, the carry and omega keep the caller's N.
 //
 // One workgroup walks the chunks of one (batch, head). A chunk of Q tokens has
 // Q*R rows rho = i*R + r (token i, rank r), padded to 64*R. With T_i the
@@ -191,6 +194,7 @@ struct ChunkBase {
     const uint16_t* C;
     const uint16_t* x;
     int nq;
+    int nin;  // state rows of the caller's B/C rows (<= N); rows nin..N-1 are zero
 };
 
 __device__ __forceinline__ u32x4 load_tok(const uint16_t* base, int i, int nq, int tok_stride, int off) {
@@ -221,8 +225,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb
         const int i = (tid >> 4) + m * (S::NT / 16);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            cr.b[m][r] = load_tok(cb.B, i, nq, G * R * N, r * N + 8 * pc);
-            if constexpr (S::C_LDS) cr.c[m][r] = load_tok(cb.C, i, nq, G * R * N, r * N + 8 * pc);
+            const bool in = 8 * pc < cb.nin;
+            cr.b[m][r] = in ? load_tok(cb.B, i, nq, G * R * cb.nin, r * cb.nin + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (S::C_LDS)
+                cr.c[m][r] = in ? load_tok(cb.C, i, nq, G * R * cb.nin, r * cb.nin + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 #pragma unroll
@@ -242,8 +248,10 @@ __device__ __forceinline__ void load_strip_c(u32x4 (&c)[4], const ChunkBase& cb,
     const unsigned rho = 16u * s + (lane & 15);
     const int i = int(rho >> S::LR), r = int(rho & (S::R - 1));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        c[ks] = load_tok(cb.C, i, cb.nq, G * S::R * N, r * N + 32 * ks + 8 * (lane >> 4));
+    for (int ks = 0; ks < 4; ++ks) {
+        const int n0 = 32 * ks + 8 * (lane >> 4);
+        c[ks] = n0 < cb.nin ? load_tok(cb.C, i, cb.nq, G * S::R * cb.nin, r * cb.nin + n0) : u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // M_ij (decay x width-2 convolution mask) for row token tj and column token ti.
@@ -286,15 +294,17 @@ __device__ __forceinline__ floatx4 transfer(floatx4 v, float A2, const float* om
     return o;
 }
 
-template <int R, int NW>
+// PAD: N below 128 (rows past Nin_ zero); without it the row count is the constant N
+template <int R, int NW, bool PAD>
 __global__ void __launch_bounds__(64 * NW)
 prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                     const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                     const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                     uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                    int64_t nbh, SegArgs sa) {
+                    int64_t nbh, int Nin_, SegArgs sa) {
     using S = Shape<R, NW>;
+    const int Nin = PAD ? Nin_ : N;
     using CR = ChunkRegs<S>;
     constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW, LR = S::LR;
 
@@ -349,24 +359,27 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     float* wsc = sW[wave];
 
     // rotation rates (revolutions per unit step) of the pairs this thread turns
-    const float* omh = omega ? omega + int64_t(h) * K : nullptr;
+    // (pairs past the caller's Nin / 2 hold zero rows: rate 0)
+    const float* omh = omega ? omega + int64_t(h) * (Nin / 2) : nullptr;
+    auto omk = [&](int k) { return (omh && (!PAD || 2 * k < Nin)) ? omh[k] : 0.f; };
     float omB[4], omC[4], omS[TPW / 4][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) omB[j] = om_at(omh, 4 * (tid & 15) + j) * kInv2Pi;
+    for (int j = 0; j < 4; ++j) omB[j] = omk(4 * (tid & 15) + j) * kInv2Pi;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) omC[ks] = om_at(omh, 16 * ks + 4 * g4 + (l16 & 3)) * kInv2Pi;
+    for (int ks = 0; ks < 4; ++ks) omC[ks] = omk(16 * ks + 4 * g4 + (l16 & 3)) * kInv2Pi;
 #pragma unroll
     for (int mr = 0; mr < TPW / 4; ++mr)
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = om_at(omh, 8 * ((wave * TPW) / 4 + mr) + 2 * g4 + hp) * kInv2Pi;
+        for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omk(8 * ((wave * TPW) / 4 + mr) + 2 * g4 + hp) * kInv2Pi;
 
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
-        cb.B = Bm + (tok0 * G + grp) * int64_t(R * N);
-        cb.C = Cm + (tok0 * G + grp) * int64_t(R * N);
+        cb.B = Bm + (tok0 * G + grp) * int64_t(R * Nin);
+        cb.C = Cm + (tok0 * G + grp) * int64_t(R * Nin);
         cb.x = x + (tok0 * H + h) * int64_t(R * P);
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
+        cb.nin = Nin;
         return cb;
     };
 
@@ -397,12 +410,12 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                float v = h0 ? h0[(bh * N + n) * P + p] : 0.f;
-                if (carry_B) {
+                float v = (h0 && n < Nin) ? h0[(bh * Nin + n) * P + p] : 0.f;
+                if (carry_B && n < Nin) {
                     float s = 0.f;
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * N + n]) *
+                        s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * Nin + n]) *
                              bf16_to_f32(carry_x[(bh * R + r) * P + p]);
                     v += dl0 * s;
                 }
@@ -823,7 +836,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                         CS t[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            t[j] = cs_rev(om_at(omh, 16 * ks + 4 * g4 + j) * kInv2Pi, Ti);
+                            t[j] = cs_rev(omk(16 * ks + 4 * g4 + j) * kInv2Pi, Ti);
                         cr[ks] = u32x4{rot_pair(craw2[ks][0], t[0]), rot_pair(craw2[ks][1], t[1]),
                                        rot_pair(craw2[ks][2], t[2]), rot_pair(craw2[ks][3], t[3])};
                     }
@@ -873,7 +886,10 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
             const int p = 16 * pt + l16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = gst[m][e];
+            for (int e = 0; e < 4; ++e) {
+                const int n = 16 * nt + 4 * g4 + e;
+                if (n < Nin) h_out[(bh * Nin + n) * P + p] = gst[m][e];
+            }
         }
     }
 }
@@ -930,8 +946,9 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int i = (stid >> 4) + TSTEP * m;
-        r.b[m] = load_tok(cb.B, i, nq, G * N, 8 * pc);
-        r.c[m] = load_tok(cb.C, i, nq, G * N, 8 * pc);
+        const bool in = 8 * pc < cb.nin;
+        r.b[m] = in ? load_tok(cb.B, i, nq, G * cb.nin, 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+        r.c[m] = in ? load_tok(cb.C, i, nq, G * cb.nin, 8 * pc) : u32x4{0u, 0u, 0u, 0u};
     }
     if (stid < NXT) {
         const int rho0 = 2 * (stid >> 3);
@@ -1011,15 +1028,16 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
 
 }  // namespace ws1
 
-template <bool ROT>
+template <bool ROT, bool PAD>
 __global__ void __launch_bounds__(64 * (ws1::NCW + ws1::NSW))
 prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                      const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                      const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                      uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                      const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                     int64_t nbh) {
+                     int64_t nbh, int Nin_) {
     using namespace ws1;
+    const int Nin = PAD ? Nin_ : N;  // PAD: N below 128 (rows past Nin_ zero)
     __shared__ __attribute__((aligned(16))) uint16_t sBt[2][QRP * NS];  // B~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NS];  // C~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];    // X^T [p][rho]
@@ -1041,14 +1059,17 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
     const float Dh = Dv[h];
-    const float* omh = omega ? omega + int64_t(h) * K : nullptr;
+    // pairs past the caller's Nin / 2 hold zero rows: rate 0
+    const float* omh = omega ? omega + int64_t(h) * (Nin / 2) : nullptr;
+    auto omk = [&](int k) { return (omh && (!PAD || 2 * k < Nin)) ? omh[k] : 0.f; };
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
-        cb.B = Bm + (tok0 * G + grp) * int64_t(N);
-        cb.C = Cm + (tok0 * G + grp) * int64_t(N);
+        cb.B = Bm + (tok0 * G + grp) * int64_t(Nin);
+        cb.C = Cm + (tok0 * G + grp) * int64_t(Nin);
         cb.x = x + (tok0 * H + h) * int64_t(P);
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
+        cb.nin = Nin;
         return cb;
     };
 
@@ -1061,8 +1082,8 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         double omD[4];  // omega / 2 pi of the thread's four pairs, for the chunk base angles
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            omB[j] = om_at(omh, 4 * (stid & 15) + j) * kInv2Pi;
-            omD[j] = double(om_at(omh, 4 * (stid & 15) + j)) * kInv2PiD;
+            omB[j] = omk(4 * (stid & 15) + j) * kInv2Pi;
+            omD[j] = double(omk(4 * (stid & 15) + j)) * kInv2PiD;
         }
         double Tacc = 0.0;  // total step before the chunk being written
         StageRegs ra, rb;
@@ -1121,9 +1142,9 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                float v = h0 ? h0[(bh * N + n) * P + p] : 0.f;
-                if (carry_B)
-                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * N + n]) * bf16_to_f32(carry_x[bh * P + p]);
+                float v = (h0 && n < Nin) ? h0[(bh * Nin + n) * P + p] : 0.f;
+                if (carry_B && n < Nin)
+                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * Nin + n]) * bf16_to_f32(carry_x[bh * P + p]);
                 gst[m][e] = v;
             }
             *reinterpret_cast<u32x2*>(&sGT[0][p * NS + 16 * nt + 4 * g4]) =
@@ -1288,7 +1309,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             CS t[2];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-                const double rv = double(om_at(omh, 8 * (nt0 + mr) + 2 * g4 + hp)) * kInv2PiD * Tacc;
+                const double rv = double(omk(8 * (nt0 + mr) + 2 * g4 + hp)) * kInv2PiD * Tacc;
                 const float r = float(rv - floor(rv));
                 t[hp] = CS{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
             }
@@ -1304,7 +1325,10 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
                     v[2 * hp + 1] = t[hp].s * a0 + t[hp].c * a1;
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = v[e];
+                for (int e = 0; e < 4; ++e) {
+                    const int n = 16 * nt + 4 * g4 + e;
+                    if (n < Nin) h_out[(bh * Nin + n) * P + p] = v[e];
+                }
             }
         }
     }
@@ -1312,12 +1336,14 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 
 hipError_t launch_ws_r1(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
-    auto kern = a.omega ? prefill_ws_r1_kernel<true> : prefill_ws_r1_kernel<false>;
+    const bool pad = a.N != N;
+    auto kern = a.omega ? (pad ? prefill_ws_r1_kernel<true, true> : prefill_ws_r1_kernel<true, false>)
+                        : (pad ? prefill_ws_r1_kernel<false, true> : prefill_ws_r1_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
                        static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                        static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                        static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
+                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, a.N);
     return hipGetLastError();
 }
 
@@ -1337,18 +1363,21 @@ hipError_t launch_r(const PrefillArgs& a) {
         const hipError_t e = launch_copy_or_zero(sa.ctrl, nullptr, 2 + nbh * sa.nseg, a.stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_mfma_kernel<R, NW>), dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW), 0, a.stream,
+    auto kern = a.N != N ? prefill_mfma_kernel<R, NW, true> : prefill_mfma_kernel<R, NW, false>;
+    hipLaunchKernelGGL(kern, dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW), 0, a.stream,
                        static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                        static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                        static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, sa);
+                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, a.N, sa);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dtype io) {
-    return io == M3_BF16 && N_ == N && P_ == P && (R == 1 || R == 2 || R == 4) && chunk >= 1 && chunk <= 64;
+    // N below 128 runs zero-padded to 128 rows: the loads of B and C rows stop at N_
+    return io == M3_BF16 && N_ >= 8 && N_ <= N && N_ % 8 == 0 && P_ == P && (R == 1 || R == 2 || R == 4) &&
+           chunk >= 1 && chunk <= 64;
 }
 
 bool mfma_segments_supported(int32_t R) { return R != 1; }

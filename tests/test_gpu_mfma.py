@@ -1,4 +1,4 @@
-"""GPU parity of the bf16-MFMA chunked prefill (N = 128, P = 64, R in {1, 2, 4}).
+"""GPU parity of the bf16-MFMA chunked prefill (N = 128, or below zero-padded; P = 64; R in {1, 2, 4}).
 
 Small cases cover every chunk size class, ragged tails, groups, initial state and
 carry; full-size workloads compare sampled (batch, head) walks with the oracle.
@@ -50,6 +50,36 @@ def test_mfma_small(case):
                             dist="lm", wid=800 + CASES.index(case), h0_std=h0s, with_carry=carry)
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+PADDED = [
+    # b, L, H, G, N, R, chunk, h0_std, carry
+    (1, 130, 2, 1, 64, 1, 64, 0.1, True),
+    (2, 97, 2, 2, 32, 1, 33, 0.0, False),
+    (1, 200, 3, 1, 8, 1, 64, 0.1, True),
+    (1, 150, 2, 1, 64, 2, 64, 0.1, True),
+    (1, 257, 2, 2, 120, 4, 64, 0.1, True),
+    (1, 70, 2, 1, 16, 4, 16, 0.0, True),
+    (1, 1100, 2, 1, 64, 4, 64, 0.1, True),  # two sequence segments (look-back) on the padded rows
+]
+
+
+@pytest.mark.parametrize("case", PADDED, ids=[str(c) for c in PADDED])
+def test_mfma_padded_state(case):
+    """N below 128 runs zero-padded to 128 rows inside the kernels: same results as the oracle at N."""
+    b, L, H, G, N, R, chunk, h0s, carry = case
+    plan = binding.plan(binding.dims(b, L, H, G, 64, N), R, chunk, binding.M3_BF16)
+    assert plan.path == binding.M3_PATH_MFMA
+    if L == 1100:
+        assert plan.segments == 2
+    _flush(f"mfma padded-state case {case}")
+    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=N, rank=R, io_dtype="bf16",
+                            dist="lm", wid=850 + PADDED.index(case), h0_std=h0s, with_carry=carry)
+    y_ref, h_ref = oracle.scan(p)
+    y, h = gpu_prefill(p, chunk)
+    assert tuple(h.shape) == (b, H, N, 64)
     assert_close(y, y_ref, TOL["bf16"], "y")
     assert_close(h, h_ref, TOL["bf16"], "h_out")
 
