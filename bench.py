@@ -87,8 +87,8 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
     """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
 
     groups: 1 (B, C shared by all heads, the primary reading) or H (one B, C per head).
-    dstate / rank: the workload's shape with another state size or rank (N 256 or R 8: the token-walk
-    kernel; N 64: the chunked kernels with the rows zero-padded).
+    dstate / rank: the workload's shape with another state size or rank (R 8: the token-walk kernel;
+    N 64 / 256: the chunked kernels, rows zero-padded / in two row passes).
     """
     import dataclasses
     import torch
@@ -578,7 +578,8 @@ def main():
         # the secondary reading: one B, C per head (64x the B/C bytes)
         out["prefill_groups_eq_heads"] = {f"r{w}": bench_prefill(wid, args.steps, args.warmup, log, groups=64)
                                           for w, wid in ((1, 1), (4, 2))}
-        # larger state / rank on the same token shapes (the token-walk kernel)
+        # larger state / rank on the same token shapes (N 256: the chunked kernels in two row passes;
+        # R 8: the token-walk kernel)
         out["prefill_larger_sizes"] = {"n256_r1": bench_prefill(1, 3, 1, log, dstate=256),
                                        "n128_r8": bench_prefill(2, 3, 1, log, rank=8)}
         # half the state (N 64) on the same token shapes (the chunked kernels, rows zero-padded)

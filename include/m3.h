@@ -84,9 +84,10 @@ typedef struct m3_plan {
 } m3_plan;
 
 /* GENERIC: chunked, fp32 arithmetic, any sizes (the fp32 I/O path).
- * MFMA:    chunked on matrix cores, bf16 I/O, N a multiple of 8 up to 128 (below
- *          128 zero-padded to 128 rows inside the kernel), P 64, R 1, 2, 4,
- *          chunk <= 64.
+ * MFMA:    chunked on matrix cores, bf16 I/O, N a multiple of 8 up to 512 (below
+ *          128 zero-padded to 128 rows inside the kernel; above 128 in passes of
+ *          128 rows whose outputs are summed in fp32 in the workspace, so the plan
+ *          then asks for b*L*H*R*P*4 bytes), P 64, R 1, 2, 4, chunk <= 64.
  * SCAN:    token-by-token walk with the state in registers and the rank
  *          contractions on matrix cores, bf16 I/O, N and P multiples of 16 with
  *          N <= 256, P <= 64, R <= 8, where MFMA does not apply (chunk unused). */

@@ -102,12 +102,13 @@ m3_status make_plan(const m3_dims* d, int32_t R, int32_t chunk, m3_dtype io, m3_
     const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
     p->path = mfma ? M3_PATH_MFMA
                    : m3::scan_path_supported(d->headdim, d->dstate, R, io) ? M3_PATH_SCAN : M3_PATH_GENERIC;
-    p->segments = (mfma && m3::mfma_segments_supported(R)) ? choose_segments(d->batch * d->heads, p->n_chunks) : 1;
+    p->segments = (mfma && m3::mfma_segments_supported(R, d->dstate))
+                      ? choose_segments(d->batch * d->heads, p->n_chunks) : 1;
     p->chunks_per_segment = p->segments > 0 ? (p->n_chunks + p->segments - 1) / p->segments : 0;
     if (mfma && p->chunks_per_segment > 0)  // no empty trailing segment
         p->segments = (int32_t)((p->n_chunks + p->chunks_per_segment - 1) / p->chunks_per_segment);
     if (p->segments < 1) p->segments = 1;
-    p->workspace_bytes = m3::prefill_workspace_layout(d->batch, d->heads, d->headdim, d->dstate,
+    p->workspace_bytes = m3::prefill_workspace_layout(d->batch, d->seqlen, d->heads, d->headdim, d->dstate, R,
                                                       p->segments, p->path).total;
     return M3_OK;
 }
@@ -118,8 +119,8 @@ namespace m3 {
 
 static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
-PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32_t N, int32_t segments,
-                                          int32_t path) {
+PrefillWorkspace prefill_workspace_layout(int64_t b, int64_t L, int32_t H, int32_t P, int32_t N, int32_t R,
+                                          int32_t segments, int32_t path) {
     PrefillWorkspace w{};
     const size_t bh = size_t(b) * size_t(H);
     size_t off = 0;
@@ -138,6 +139,9 @@ PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32
         off += up256(nseg * size_t(N) * size_t(P) * 4);
         w.tr_off = off;
         off += up256(nseg * 8);
+    } else if (path == M3_PATH_MFMA && N > 128) {
+        w.ypart_off = off;
+        off += up256(bh * size_t(L) * size_t(R) * size_t(P) * 4);
     }
     w.total = off;
     return w;

@@ -119,15 +119,17 @@ struct PrefillWorkspace {
     size_t agg_off;        // segmented path: per-segment local end state [b*H*S][N][P] fp32
     size_t incl_off;       // segmented path: per-segment inclusive end state
     size_t tr_off;         // segmented path: per-segment total step (sum of dt) [b*H*S] fp64
+    size_t ypart_off;      // chunked path, N above 128: fp32 outputs of the row passes [b][L][H][R][P]
     size_t total;
 };
 
-PrefillWorkspace prefill_workspace_layout(int64_t b, int32_t H, int32_t P, int32_t N, int32_t segments,
-                                          int32_t path);
+PrefillWorkspace prefill_workspace_layout(int64_t b, int64_t L, int32_t H, int32_t P, int32_t N, int32_t R,
+                                          int32_t segments, int32_t path);
 
 bool mfma_path_supported(int32_t P, int32_t N, int32_t R, int32_t chunk, m3_dtype io);
 // the MFMA path splits the sequence into segments (look-back) at these ranks
-bool mfma_segments_supported(int32_t R);
+bool mfma_segments_supported(int32_t R, int32_t N);
+constexpr int32_t kMfmaMaxN = 512;  // largest N of the chunked path (passes of 128 rows)
 
 // the token-walk path (bf16, N, P multiples of 16, N <= 256, P <= 64, R <= 8)
 bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io);

@@ -151,7 +151,7 @@ __global__ void copy_or_zero_kernel(uint32_t* __restrict__ dst, const uint32_t* 
 
 template <typename T>
 hipError_t launch_generic_t(const PrefillArgs& a) {
-    const PrefillWorkspace ws = prefill_workspace_layout(a.b, a.H, a.P, a.N, a.plan.segments, a.plan.path);
+    const PrefillWorkspace ws = prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
     float* state = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ws.state_off);
     const size_t shmem = size_t(3) * a.chunk * sizeof(float);
     const dim3 grid(unsigned(a.b * a.H));

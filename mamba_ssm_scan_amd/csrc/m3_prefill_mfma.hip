@@ -35,6 +35,7 @@
 // each (token, pair) angle is evaluated once: the thread that stages a token's
 // B rows also turns its C rows (into LDS when they fit, R <= 2), and at R = 4
 // the four lanes holding one token's C rows share angles through DPP.
+#include <type_traits>
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -194,7 +195,8 @@ struct ChunkBase {
     const uint16_t* C;
     const uint16_t* x;
     int nq;
-    int nin;  // state rows of the caller's B/C rows (<= N); rows nin..N-1 are zero
+    int nin;   // state rows this pass takes from the caller's B/C rows (<= N); rows nin..N-1 are zero
+    int nrow;  // length of the caller's B/C rows (the caller's N)
 };
 
 __device__ __forceinline__ u32x4 load_tok(const uint16_t* base, int i, int nq, int tok_stride, int off) {
@@ -226,9 +228,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const bool in = 8 * pc < cb.nin;
-            cr.b[m][r] = in ? load_tok(cb.B, i, nq, G * R * cb.nin, r * cb.nin + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+            cr.b[m][r] = in ? load_tok(cb.B, i, nq, G * R * cb.nrow, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
             if constexpr (S::C_LDS)
-                cr.c[m][r] = in ? load_tok(cb.C, i, nq, G * R * cb.nin, r * cb.nin + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+                cr.c[m][r] = in ? load_tok(cb.C, i, nq, G * R * cb.nrow, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 #pragma unroll
@@ -250,7 +252,7 @@ __device__ __forceinline__ void load_strip_c(u32x4 (&c)[4], const ChunkBase& cb,
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int n0 = 32 * ks + 8 * (lane >> 4);
-        c[ks] = n0 < cb.nin ? load_tok(cb.C, i, cb.nq, G * S::R * cb.nin, r * cb.nin + n0) : u32x4{0u, 0u, 0u, 0u};
+        c[ks] = n0 < cb.nin ? load_tok(cb.C, i, cb.nq, G * S::R * cb.nrow, r * cb.nrow + n0) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -294,17 +296,24 @@ __device__ __forceinline__ floatx4 transfer(floatx4 v, float A2, const float* om
     return o;
 }
 
-// PAD: N below 128 (rows past Nin_ zero); without it the row count is the constant N
-template <int R, int NW, bool PAD>
+// PAD: fewer than 128 rows in this pass (rows past Nin_ zero); without it the
+// pass holds the constant N = 128 rows.
+// YM: 0 one pass over the caller's N rows, y written in bf16; a larger N runs
+// in passes of 128 rows (rows n_off_ .. of the caller's Nrow_) whose outputs
+// meet in fp32 in ypart: 1 first pass (writes ypart, with D x), 3 middle pass
+// (adds to ypart), 2 last pass (adds ypart and writes y in bf16).
+template <int R, int NW, bool PAD, int YM>
 __global__ void __launch_bounds__(64 * NW)
 prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                     const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                     const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                     uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                    int64_t nbh, int Nin_, SegArgs sa) {
+                    int64_t nbh, int Nin_, int Nrow_, int n_off_, float* __restrict__ ypart, SegArgs sa) {
     using S = Shape<R, NW>;
     const int Nin = PAD ? Nin_ : N;
+    const int Nrow = YM == 0 ? Nin : Nrow_;
+    const int n_off = YM == 0 ? 0 : n_off_;
     using CR = ChunkRegs<S>;
     constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW, LR = S::LR;
 
@@ -355,12 +364,12 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     const int h = int(bh % H);
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
-    const float Dh = Dv[h];
+    const float Dh = (YM == 2 || YM == 3) ? 0.f : Dv[h];  // D x once, in the first pass
     float* wsc = sW[wave];
 
     // rotation rates (revolutions per unit step) of the pairs this thread turns
     // (pairs past the caller's Nin / 2 hold zero rows: rate 0)
-    const float* omh = omega ? omega + int64_t(h) * (Nin / 2) : nullptr;
+    const float* omh = omega ? omega + int64_t(h) * (Nrow / 2) + n_off / 2 : nullptr;
     auto omk = [&](int k) { return (omh && (!PAD || 2 * k < Nin)) ? omh[k] : 0.f; };
     float omB[4], omC[4], omS[TPW / 4][2];
 #pragma unroll
@@ -375,11 +384,12 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
-        cb.B = Bm + (tok0 * G + grp) * int64_t(R * Nin);
-        cb.C = Cm + (tok0 * G + grp) * int64_t(R * Nin);
+        cb.B = Bm + (tok0 * G + grp) * int64_t(R * Nrow) + n_off;
+        cb.C = Cm + (tok0 * G + grp) * int64_t(R * Nrow) + n_off;
         cb.x = x + (tok0 * H + h) * int64_t(R * P);
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
         cb.nin = Nin;
+        cb.nrow = Nrow;
         return cb;
     };
 
@@ -410,12 +420,12 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                float v = (h0 && n < Nin) ? h0[(bh * Nin + n) * P + p] : 0.f;
+                float v = (h0 && n < Nin) ? h0[(bh * Nrow + n_off + n) * P + p] : 0.f;
                 if (carry_B && n < Nin) {
                     float s = 0.f;
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * Nin + n]) *
+                        s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * Nrow + n_off + n]) *
                              bf16_to_f32(carry_x[(bh * R + r) * P + p]);
                     v += dl0 * s;
                 }
@@ -668,12 +678,16 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             // epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
             if ((rho_i >> LR) < nq) {
                 const int i = rho_i >> LR, r = rho_i & (R - 1);
-                uint16_t* yr = y + ((b * L + c * Q) * H + h) * int64_t(R * P) + (i * H * R + r) * P;
+                const int64_t yo = ((b * L + c * Q) * H + h) * int64_t(R * P) + (i * H * R + r) * P;
 #pragma unroll
                 for (int q = 0; q < S::PTW; ++q) {
                     const int p = 16 * (pt0 + q) + 4 * g4;
-                    *reinterpret_cast<u32x2*>(yr + p) =
-                        u32x2{pack2(acc[q][0], acc[q][1]), pack2(acc[q][2], acc[q][3])};
+                    floatx4 v = acc[q];
+                    if constexpr (YM == 2 || YM == 3) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
+                    if constexpr (YM == 1 || YM == 3)
+                        *reinterpret_cast<floatx4*>(ypart + yo + p) = v;
+                    else
+                        *reinterpret_cast<u32x2*>(y + yo + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
                 }
             }
         }
@@ -730,7 +744,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         lds_barrier();
     }
 
-    if (sa.nseg > 1) {
+    if (YM == 0 && sa.nseg > 1) {
         // ================= sequence segments: look-back and correction
         __shared__ unsigned sFlag;
         const int64_t bs = bh * sa.nseg + seg;
@@ -888,7 +902,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                if (n < Nin) h_out[(bh * Nin + n) * P + p] = gst[m][e];
+                if (n < Nin) h_out[(bh * Nrow + n_off + n) * P + p] = gst[m][e];
             }
         }
     }
@@ -947,8 +961,8 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
     for (int m = 0; m < MT; ++m) {
         const int i = (stid >> 4) + TSTEP * m;
         const bool in = 8 * pc < cb.nin;
-        r.b[m] = in ? load_tok(cb.B, i, nq, G * cb.nin, 8 * pc) : u32x4{0u, 0u, 0u, 0u};
-        r.c[m] = in ? load_tok(cb.C, i, nq, G * cb.nin, 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+        r.b[m] = in ? load_tok(cb.B, i, nq, G * cb.nrow, 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+        r.c[m] = in ? load_tok(cb.C, i, nq, G * cb.nrow, 8 * pc) : u32x4{0u, 0u, 0u, 0u};
     }
     if (stid < NXT) {
         const int rho0 = 2 * (stid >> 3);
@@ -1028,16 +1042,19 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
 
 }  // namespace ws1
 
-template <bool ROT, bool PAD>
+// PAD and YM as for prefill_mfma_kernel
+template <bool ROT, bool PAD, int YM>
 __global__ void __launch_bounds__(64 * (ws1::NCW + ws1::NSW))
 prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                      const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                      const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                      uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                      const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                     int64_t nbh, int Nin_) {
+                     int64_t nbh, int Nin_, int Nrow_, int n_off_, float* __restrict__ ypart) {
     using namespace ws1;
-    const int Nin = PAD ? Nin_ : N;  // PAD: N below 128 (rows past Nin_ zero)
+    const int Nin = PAD ? Nin_ : N;
+    const int Nrow = YM == 0 ? Nin : Nrow_;
+    const int n_off = YM == 0 ? 0 : n_off_;
     __shared__ __attribute__((aligned(16))) uint16_t sBt[2][QRP * NS];  // B~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NS];  // C~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];    // X^T [p][rho]
@@ -1058,18 +1075,19 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     const int h = int(bh % H);
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
-    const float Dh = Dv[h];
+    const float Dh = (YM == 2 || YM == 3) ? 0.f : Dv[h];  // D x once, in the first pass
     // pairs past the caller's Nin / 2 hold zero rows: rate 0
-    const float* omh = omega ? omega + int64_t(h) * (Nin / 2) : nullptr;
+    const float* omh = omega ? omega + int64_t(h) * (Nrow / 2) + n_off / 2 : nullptr;
     auto omk = [&](int k) { return (omh && (!PAD || 2 * k < Nin)) ? omh[k] : 0.f; };
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
-        cb.B = Bm + (tok0 * G + grp) * int64_t(Nin);
-        cb.C = Cm + (tok0 * G + grp) * int64_t(Nin);
+        cb.B = Bm + (tok0 * G + grp) * int64_t(Nrow) + n_off;
+        cb.C = Cm + (tok0 * G + grp) * int64_t(Nrow) + n_off;
         cb.x = x + (tok0 * H + h) * int64_t(P);
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
         cb.nin = Nin;
+        cb.nrow = Nrow;
         return cb;
     };
 
@@ -1142,9 +1160,9 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                float v = (h0 && n < Nin) ? h0[(bh * Nin + n) * P + p] : 0.f;
+                float v = (h0 && n < Nin) ? h0[(bh * Nrow + n_off + n) * P + p] : 0.f;
                 if (carry_B && n < Nin)
-                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * Nin + n]) * bf16_to_f32(carry_x[bh * P + p]);
+                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * Nrow + n_off + n]) * bf16_to_f32(carry_x[bh * P + p]);
                 gst[m][e] = v;
             }
             *reinterpret_cast<u32x2*>(&sGT[0][p * NS + 16 * nt + 4 * g4]) =
@@ -1248,14 +1266,16 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             c1t = n1t;
         }
         if (ti < nq) {
-            uint16_t* yr = y + ((b * L + c * Q + ti) * H + h) * int64_t(P);
+            const int64_t yo = ((b * L + c * Q + ti) * H + h) * int64_t(P);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int p = 16 * q + 4 * g4;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[q][e];
-                *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+                floatx4 v = acc[q];
+                if constexpr (YM == 2 || YM == 3) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
+                if constexpr (YM == 1 || YM == 3)
+                    *reinterpret_cast<floatx4*>(ypart + yo + p) = v;
+                else
+                    *reinterpret_cast<u32x2*>(y + yo + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
             }
         }
 
@@ -1327,32 +1347,61 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int n = 16 * nt + 4 * g4 + e;
-                    if (n < Nin) h_out[(bh * Nin + n) * P + p] = v[e];
+                    if (n < Nin) h_out[(bh * Nrow + n_off + n) * P + p] = v[e];
                 }
             }
         }
     }
 }
 
-hipError_t launch_ws_r1(const PrefillArgs& a) {
+// One pass over rows [n_off, n_off + nin) of the caller's N (ym as YM above).
+struct RowPass {
+    int nin, n_off, ym;
+    float* ypart;
+};
+
+template <class F>
+hipError_t dispatch_pass(const RowPass& rp, F&& launch) {
+    // the instances that exist: every YM without padding; padding only in a
+    // single pass or the last one (the earlier passes hold 128 rows)
+    const bool pad = rp.nin != N;
+    switch (rp.ym) {
+        case 0: return pad ? launch(std::integral_constant<bool, true>{}, std::integral_constant<int, 0>{})
+                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 0>{});
+        case 1: return pad ? hipErrorInvalidValue
+                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 1>{});
+        case 2: return pad ? launch(std::integral_constant<bool, true>{}, std::integral_constant<int, 2>{})
+                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 2>{});
+        case 3: return pad ? hipErrorInvalidValue
+                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 3>{});
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ws_r1(const PrefillArgs& a, const RowPass& rp) {
     const int64_t nbh = a.b * a.H;
-    const bool pad = a.N != N;
-    auto kern = a.omega ? (pad ? prefill_ws_r1_kernel<true, true> : prefill_ws_r1_kernel<true, false>)
-                        : (pad ? prefill_ws_r1_kernel<false, true> : prefill_ws_r1_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
-                       static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
-                       static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
-                       static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, a.N);
-    return hipGetLastError();
+    return dispatch_pass(rp, [&](auto pad, auto ym) {
+        constexpr bool PD = decltype(pad)::value;
+        constexpr int YM = decltype(ym)::value;
+        auto kern = a.omega ? prefill_ws_r1_kernel<true, PD, YM> : prefill_ws_r1_kernel<false, PD, YM>;
+        hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
+                           static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
+                           static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
+                           static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
+                           rp.nin, a.N, rp.n_off, rp.ypart);
+        return hipGetLastError();
+    });
 }
 
 template <int R, int NW>
-hipError_t launch_r(const PrefillArgs& a) {
+hipError_t launch_r(const PrefillArgs& a, const RowPass& rp) {
     const int64_t nbh = a.b * a.H;
     SegArgs sa{a.plan.segments, a.plan.chunks_per_segment, nullptr, nullptr, nullptr, nullptr};
     if (sa.nseg > 1) {
-        const PrefillWorkspace w = prefill_workspace_layout(a.b, a.H, a.P, a.N, a.plan.segments, a.plan.path);
+        if (rp.ym != 0) return hipErrorInvalidValue;  // segments only in a single pass
+        const PrefillWorkspace w =
+            prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
         char* base = static_cast<char*>(a.workspace);
         sa.ctrl = reinterpret_cast<unsigned*>(base + w.ctrl_off);
         sa.agg = reinterpret_cast<float*>(base + w.agg_off);
@@ -1363,34 +1412,53 @@ hipError_t launch_r(const PrefillArgs& a) {
         const hipError_t e = launch_copy_or_zero(sa.ctrl, nullptr, 2 + nbh * sa.nseg, a.stream);
         if (e != hipSuccess) return e;
     }
-    auto kern = a.N != N ? prefill_mfma_kernel<R, NW, true> : prefill_mfma_kernel<R, NW, false>;
-    hipLaunchKernelGGL(kern, dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW), 0, a.stream,
-                       static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
-                       static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
-                       static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, a.N, sa);
-    return hipGetLastError();
+    return dispatch_pass(rp, [&](auto pad, auto ym) {
+        constexpr bool PD = decltype(pad)::value;
+        constexpr int YM = decltype(ym)::value;
+        hipLaunchKernelGGL((prefill_mfma_kernel<R, NW, PD, YM>), dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW), 0,
+                           a.stream, static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
+                           static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
+                           static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
+                           rp.nin, a.N, rp.n_off, rp.ypart, sa);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace
 
+// N up to 128 in one pass (below 128 zero-padded: the loads of B and C rows stop
+// at N_); larger N in passes of 128 rows whose outputs meet in fp32 in the workspace
 bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dtype io) {
-    // N below 128 runs zero-padded to 128 rows: the loads of B and C rows stop at N_
-    return io == M3_BF16 && N_ >= 8 && N_ <= N && N_ % 8 == 0 && P_ == P && (R == 1 || R == 2 || R == 4) &&
-           chunk >= 1 && chunk <= 64;
+    return io == M3_BF16 && N_ >= 8 && N_ <= kMfmaMaxN && N_ % 8 == 0 && P_ == P &&
+           (R == 1 || R == 2 || R == 4) && chunk >= 1 && chunk <= 64;
 }
 
-bool mfma_segments_supported(int32_t R) { return R != 1; }
+bool mfma_segments_supported(int32_t R, int32_t N_) { return R != 1 && N_ <= N; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
     if (a.b * a.H * a.plan.segments > 0x7fffffff) return hipErrorInvalidValue;
     if (a.R == 1 && a.plan.segments != 1) return hipErrorInvalidValue;
-    switch (a.R) {
-        case 1: return launch_ws_r1(a);
-        case 2: return launch_r<2, 4>(a);
-        case 4: return launch_r<4, 4>(a);
+    const int passes = (a.N + N - 1) / N;
+    float* ypart = nullptr;
+    if (passes > 1) {
+        const PrefillWorkspace w =
+            prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
+        ypart = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + w.ypart_off);
     }
-    return hipErrorInvalidValue;
+    for (int k = 0; k < passes; ++k) {
+        const RowPass rp{a.N - k * N < N ? a.N - k * N : N, k * N,
+                         passes == 1 ? 0 : k == 0 ? 1 : k == passes - 1 ? 2 : 3, ypart};
+        hipError_t e;
+        switch (a.R) {
+            case 1: e = launch_ws_r1(a, rp); break;
+            case 2: e = launch_r<2, 4>(a, rp); break;
+            case 4: e = launch_r<4, 4>(a, rp); break;
+            default: e = hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace m3

@@ -1,4 +1,4 @@
-"""GPU parity of the bf16-MFMA chunked prefill (N = 128, or below zero-padded; P = 64; R in {1, 2, 4}).
+"""GPU parity of the bf16-MFMA chunked prefill (N = 128; below zero-padded; above in row passes; P = 64; R in {1, 2, 4}).
 
 Small cases cover every chunk size class, ragged tails, groups, initial state and
 carry; full-size workloads compare sampled (batch, head) walks with the oracle.
@@ -76,7 +76,36 @@ def test_mfma_padded_state(case):
         assert plan.segments == 2
     _flush(f"mfma padded-state case {case}")
     p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=N, rank=R, io_dtype="bf16",
-                            dist="lm", wid=850 + PADDED.index(case), h0_std=h0s, with_carry=carry)
+                            dist="lm", wid=880 + PADDED.index(case), h0_std=h0s, with_carry=carry)
+    y_ref, h_ref = oracle.scan(p)
+    y, h = gpu_prefill(p, chunk)
+    assert tuple(h.shape) == (b, H, N, 64)
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+PASSES = [
+    # b, L, H, G, N, R, chunk, h0_std, carry
+    (1, 150, 2, 1, 256, 1, 64, 0.1, True),
+    (2, 70, 2, 2, 200, 1, 33, 0.0, True),    # last pass zero-padded (72 rows)
+    (1, 100, 2, 1, 384, 2, 64, 0.1, True),   # three passes: a middle one
+    (1, 90, 3, 3, 256, 4, 64, 0.1, True),
+    (1, 77, 2, 1, 136, 4, 16, 0.0, True),    # last pass 8 rows
+    (1, 40, 2, 1, 512, 4, 64, 0.1, False),   # four passes
+    (1, 1100, 2, 1, 256, 4, 64, 0.1, True),  # few walks, long: one segment (no look-back across passes)
+]
+
+
+@pytest.mark.parametrize("case", PASSES, ids=[str(c) for c in PASSES])
+def test_mfma_row_passes(case):
+    """N above 128 in passes of 128 rows (outputs summed in fp32 in the workspace): oracle at N."""
+    b, L, H, G, N, R, chunk, h0s, carry = case
+    plan = binding.plan(binding.dims(b, L, H, G, 64, N), R, chunk, binding.M3_BF16)
+    assert plan.path == binding.M3_PATH_MFMA and plan.segments == 1
+    assert plan.workspace_bytes >= b * L * H * R * 64 * 4
+    _flush(f"mfma row-pass case {case}")
+    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=N, rank=R, io_dtype="bf16",
+                            dist="lm", wid=890 + PASSES.index(case), h0_std=h0s, with_carry=carry)
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
     assert tuple(h.shape) == (b, H, N, 64)
