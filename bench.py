@@ -83,7 +83,7 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, rank=None):
+def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, rank=None, headdim=None):
     """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
 
     groups: 1 (B, C shared by all heads, the primary reading) or H (one B, C per head).
@@ -95,8 +95,8 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
     from mamba_ssm_scan_amd import binding, inputs
     w = inputs.WORKLOADS[wid]
     base = w.name
-    if dstate is not None or rank is not None:
-        w = dataclasses.replace(w, dstate=dstate or w.dstate, rank=rank or w.rank)
+    if dstate is not None or rank is not None or headdim is not None:
+        w = dataclasses.replace(w, dstate=dstate or w.dstate, rank=rank or w.rank, headdim=headdim or w.headdim)
     G = groups
     copies = [inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=G, headdim=w.headdim,
                                   dstate=w.dstate, rank=w.rank, io_dtype=w.io_dtype, dist=w.dist, wid=wid,
@@ -129,8 +129,9 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
         by -= w.batch * w.seqlen * w.heads * 4
     fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
     name = base + (f" ({special})" if special else "") + (f" G={G}" if G != 1 else "")
-    if w.dstate != inputs.WORKLOADS[wid].dstate or w.rank != inputs.WORKLOADS[wid].rank:
-        name += f" with N={w.dstate} R={w.rank}"
+    if (w.dstate, w.rank, w.headdim) != (inputs.WORKLOADS[wid].dstate, inputs.WORKLOADS[wid].rank,
+                                          inputs.WORKLOADS[wid].headdim):
+        name += f" with N={w.dstate} R={w.rank} P={w.headdim}"
     r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
          "bytes": by, "flops": fl, "path": {binding.M3_PATH_MFMA: "mfma", binding.M3_PATH_SCAN: "scan"}.get(plan.path, "generic"),

@@ -102,7 +102,7 @@ m3_status make_plan(const m3_dims* d, int32_t R, int32_t chunk, m3_dtype io, m3_
     const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
     p->path = mfma ? M3_PATH_MFMA
                    : m3::scan_path_supported(d->headdim, d->dstate, R, io) ? M3_PATH_SCAN : M3_PATH_GENERIC;
-    p->segments = (mfma && m3::mfma_segments_supported(R, d->dstate))
+    p->segments = (mfma && m3::mfma_segments_supported(R, d->dstate, d->headdim))
                       ? choose_segments(d->batch * d->heads, p->n_chunks) : 1;
     p->chunks_per_segment = p->segments > 0 ? (p->n_chunks + p->segments - 1) / p->segments : 0;
     if (mfma && p->chunks_per_segment > 0)  // no empty trailing segment

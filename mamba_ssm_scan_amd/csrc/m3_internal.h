@@ -128,8 +128,9 @@ PrefillWorkspace prefill_workspace_layout(int64_t b, int64_t L, int32_t H, int32
 
 bool mfma_path_supported(int32_t P, int32_t N, int32_t R, int32_t chunk, m3_dtype io);
 // the MFMA path splits the sequence into segments (look-back) at these ranks
-bool mfma_segments_supported(int32_t R, int32_t N);
-constexpr int32_t kMfmaMaxN = 512;  // largest N of the chunked path (passes of 128 rows)
+bool mfma_segments_supported(int32_t R, int32_t N, int32_t P);
+constexpr int32_t kMfmaMaxN = 512;   // largest N of the chunked path (passes of 128 rows)
+constexpr int32_t kMfmaMaxP = 1024;  // largest P of the chunked path (passes of 64 columns)
 
 // the token-walk path (bf16, N, P multiples of 16, N <= 256, P <= 64, R <= 8)
 bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io);

@@ -1,8 +1,9 @@
 // m3_prefill_mfma.hip -- chunked prefill on bf16 MFMA (gfx950), N = 128, P = 64,
-// rank R in {1, 2, 4}, chunk <= 64 tokens, bf16 I/O, fp32 state. A smaller
-// state (N a multiple of 8 below 128) runs zero-padded to 128 rows: the B and
-// C rows past N load as zero, so those state rows stay zero and add nothing to
-// the scores or outputs; h0, h_out, the carry and omega keep the caller's N.
+// rank R in {1, 2, 4}, chunk <= 64 tokens, bf16 I/O, fp32 state. Other N and
+// P (multiples of 8) run as passes of at most 128 state rows and 64 columns,
+// zero-padded where a pass holds fewer: B/C rows past the pass's rows and x
+// columns past its columns load as zero, so those state entries stay zero and
+// add nothing to the scores or outputs (PassArgs below).
 //
 // One workgroup walks the chunks of one (batch, head). A chunk of Q tokens has
 // Q*R rows rho = i*R + r (token i, rank r), padded to 64*R. With T_i the
@@ -197,6 +198,20 @@ struct ChunkBase {
     int nq;
     int nin;   // state rows this pass takes from the caller's B/C rows (<= N); rows nin..N-1 are zero
     int nrow;  // length of the caller's B/C rows (the caller's N)
+    int pin;   // columns this pass takes from the caller's x rows (<= P); columns pin..P-1 are zero
+    int pcol;  // length of the caller's x rows (the caller's P)
+};
+
+// One pass of the chunked kernels over rows n_off .. n_off + nin - 1 of the
+// caller's N (= nrow) and columns p_off .. p_off + pin - 1 of its P (= pcol).
+// The state rows evolve independently and so do its columns: a column block
+// is a problem of its own, a row block contributes a share of y that the
+// passes sum in fp32 in ypart ([b][L][H][R][P]). ym: 0 the only row pass (y
+// written in bf16), 1 first (writes ypart, with D x), 3 middle (adds to
+// ypart), 2 last (adds ypart, writes y in bf16).
+struct PassArgs {
+    int nin, nrow, n_off, pin, pcol, p_off, ym;
+    float* ypart;
 };
 
 __device__ __forceinline__ u32x4 load_tok(const uint16_t* base, int i, int nq, int tok_stride, int off) {
@@ -233,14 +248,15 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb
                 cr.c[m][r] = in ? load_tok(cb.C, i, nq, G * R * cb.nrow, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    const bool xin = 8 * (tid & 7) < cb.pin;
 #pragma unroll
     for (int m = 0; m < S::XPT; ++m) {
         if (S::XU % S::NT != 0 && tid + m * S::NT >= S::XU) break;
         const unsigned rho0 = 2u * ((tid >> 3) + m * (S::NT / 8));
         const int i0 = int(rho0 >> S::LR), r0 = int(rho0 & (R - 1));
         const int i1 = int((rho0 + 1) >> S::LR), r1 = int((rho0 + 1) & (R - 1));
-        cr.x0[m] = load_tok(cb.x, i0, nq, H * R * P, r0 * P + 8 * (tid & 7));
-        cr.x1[m] = load_tok(cb.x, i1, nq, H * R * P, r1 * P + 8 * (tid & 7));
+        cr.x0[m] = xin ? load_tok(cb.x, i0, nq, H * R * cb.pcol, r0 * cb.pcol + 8 * (tid & 7)) : u32x4{0u, 0u, 0u, 0u};
+        cr.x1[m] = xin ? load_tok(cb.x, i1, nq, H * R * cb.pcol, r1 * cb.pcol + 8 * (tid & 7)) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -296,24 +312,23 @@ __device__ __forceinline__ floatx4 transfer(floatx4 v, float A2, const float* om
     return o;
 }
 
-// PAD: fewer than 128 rows in this pass (rows past Nin_ zero); without it the
-// pass holds the constant N = 128 rows.
-// YM: 0 one pass over the caller's N rows, y written in bf16; a larger N runs
-// in passes of 128 rows (rows n_off_ .. of the caller's Nrow_) whose outputs
-// meet in fp32 in ypart: 1 first pass (writes ypart, with D x), 3 middle pass
-// (adds to ypart), 2 last pass (adds ypart and writes y in bf16).
-template <int R, int NW, bool PAD, int YM>
+// GEN: the pass described by pa (other sizes, row and column passes); without
+// it the problem is exactly N = 128, P = 64 in one pass and pa is not read.
+// YM is pa.ym and GP (columns other than 0..63 of P = 64) is part of GEN, both
+// at compile time: as run-time values they cost the R 1 kernel 7% and 11%.
+template <int R, int NW, bool GEN, int YM, bool GP>
 __global__ void __launch_bounds__(64 * NW)
 prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                     const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                     const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                     uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                    int64_t nbh, int Nin_, int Nrow_, int n_off_, float* __restrict__ ypart, SegArgs sa) {
+                    int64_t nbh, PassArgs pa, SegArgs sa) {
     using S = Shape<R, NW>;
-    const int Nin = PAD ? Nin_ : N;
-    const int Nrow = YM == 0 ? Nin : Nrow_;
-    const int n_off = YM == 0 ? 0 : n_off_;
+    const int Nin = GEN ? pa.nin : N, Nrow = GEN ? pa.nrow : N, n_off = GEN ? pa.n_off : 0;
+    const int Pin = GP ? pa.pin : P, Pcol = GP ? pa.pcol : P, p_off = GP ? pa.p_off : 0;
+    constexpr int ym = YM;
+    float* const ypart = pa.ypart;
     using CR = ChunkRegs<S>;
     constexpr int QRP = S::QRP, NT = S::NT, XS = S::XS, SPW = S::SPW, TPW = S::TPW, LR = S::LR;
 
@@ -364,13 +379,13 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     const int h = int(bh % H);
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
-    const float Dh = (YM == 2 || YM == 3) ? 0.f : Dv[h];  // D x once, in the first pass
+    const float Dh = ym >= 2 ? 0.f : Dv[h];  // D x once, in the first row pass
     float* wsc = sW[wave];
 
     // rotation rates (revolutions per unit step) of the pairs this thread turns
     // (pairs past the caller's Nin / 2 hold zero rows: rate 0)
     const float* omh = omega ? omega + int64_t(h) * (Nrow / 2) + n_off / 2 : nullptr;
-    auto omk = [&](int k) { return (omh && (!PAD || 2 * k < Nin)) ? omh[k] : 0.f; };
+    auto omk = [&](int k) { return (omh && (!GEN || 2 * k < Nin)) ? omh[k] : 0.f; };
     float omB[4], omC[4], omS[TPW / 4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) omB[j] = omk(4 * (tid & 15) + j) * kInv2Pi;
@@ -386,10 +401,12 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         ChunkBase cb;
         cb.B = Bm + (tok0 * G + grp) * int64_t(R * Nrow) + n_off;
         cb.C = Cm + (tok0 * G + grp) * int64_t(R * Nrow) + n_off;
-        cb.x = x + (tok0 * H + h) * int64_t(R * P);
+        cb.x = x + (tok0 * H + h) * int64_t(R * Pcol) + p_off;
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
         cb.nin = Nin;
         cb.nrow = Nrow;
+        cb.pin = Pin;
+        cb.pcol = Pcol;
         return cb;
     };
 
@@ -420,13 +437,14 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                float v = (h0 && n < Nin) ? h0[(bh * Nrow + n_off + n) * P + p] : 0.f;
-                if (carry_B && n < Nin) {
+                const bool in = n < Nin && p < Pin;
+                float v = (h0 && in) ? h0[(bh * Nrow + n_off + n) * Pcol + p_off + p] : 0.f;
+                if (carry_B && in) {
                     float s = 0.f;
 #pragma unroll
                     for (int r = 0; r < R; ++r)
                         s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * Nrow + n_off + n]) *
-                             bf16_to_f32(carry_x[(bh * R + r) * P + p]);
+                             bf16_to_f32(carry_x[(bh * R + r) * Pcol + p_off + p]);
                     v += dl0 * s;
                 }
                 gst[m][e] = v;
@@ -678,13 +696,15 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             // epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
             if ((rho_i >> LR) < nq) {
                 const int i = rho_i >> LR, r = rho_i & (R - 1);
-                const int64_t yo = ((b * L + c * Q) * H + h) * int64_t(R * P) + (i * H * R + r) * P;
+                const int64_t yo =
+                    ((b * L + c * Q) * H + h) * int64_t(R * Pcol) + int64_t(i * H * R + r) * Pcol + p_off;
 #pragma unroll
                 for (int q = 0; q < S::PTW; ++q) {
                     const int p = 16 * (pt0 + q) + 4 * g4;
+                    if (GP && p >= Pin) continue;  // Pin is a multiple of 8
                     floatx4 v = acc[q];
-                    if constexpr (YM == 2 || YM == 3) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
-                    if constexpr (YM == 1 || YM == 3)
+                    if (ym >= 2) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
+                    if (ym == 1 || ym == 3)
                         *reinterpret_cast<floatx4*>(ypart + yo + p) = v;
                     else
                         *reinterpret_cast<u32x2*>(y + yo + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
@@ -744,7 +764,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         lds_barrier();
     }
 
-    if (YM == 0 && sa.nseg > 1) {
+    if (ym == 0 && sa.nseg > 1) {
         // ================= sequence segments: look-back and correction
         __shared__ unsigned sFlag;
         const int64_t bs = bh * sa.nseg + seg;
@@ -866,12 +886,13 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                         }
                     }
                     if (ti < nq) {
-                        uint16_t* yr = y + ((b * L + c0) * H + h) * int64_t(R * P) +
-                                       (ti * H * R + int(rho & (R - 1))) * P;
+                        uint16_t* yr = y + ((b * L + c0) * H + h) * int64_t(R * Pcol) +
+                                       int64_t(ti * H * R + int(rho & (R - 1))) * Pcol + p_off;
                         const float f = wsc[192 + ti];
 #pragma unroll
                         for (int q = 0; q < S::PTW; ++q) {
                             const int pp = 16 * (pt0 + q) + 4 * g4;
+                            if (GP && pp >= Pin) continue;
                             const u32x2 old = *reinterpret_cast<const u32x2*>(yr + pp);
                             *reinterpret_cast<u32x2*>(yr + pp) =
                                 u32x2{pack2(lo16(old[0]) + f * a[q][0], hi16(old[0]) + f * a[q][1]),
@@ -902,7 +923,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                if (n < Nin) h_out[(bh * Nrow + n_off + n) * P + p] = gst[m][e];
+                if (n < Nin && p < Pin) h_out[(bh * Nrow + n_off + n) * Pcol + p_off + p] = gst[m][e];
             }
         }
     }
@@ -966,8 +987,9 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
     }
     if (stid < NXT) {
         const int rho0 = 2 * (stid >> 3);
-        r.x0 = load_tok(cb.x, rho0, nq, H * P, 8 * (stid & 7));
-        r.x1 = load_tok(cb.x, rho0 + 1, nq, H * P, 8 * (stid & 7));
+        const bool xin = 8 * (stid & 7) < cb.pin;
+        r.x0 = xin ? load_tok(cb.x, rho0, nq, H * cb.pcol, 8 * (stid & 7)) : u32x4{0u, 0u, 0u, 0u};
+        r.x1 = xin ? load_tok(cb.x, rho0 + 1, nq, H * cb.pcol, 8 * (stid & 7)) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -1042,19 +1064,20 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
 
 }  // namespace ws1
 
-// PAD and YM as for prefill_mfma_kernel
-template <bool ROT, bool PAD, int YM>
+// GEN, YM, GP as for prefill_mfma_kernel
+template <bool ROT, bool GEN, int YM, bool GP>
 __global__ void __launch_bounds__(64 * (ws1::NCW + ws1::NSW))
 prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                      const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                      const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                      uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                      const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                     int64_t nbh, int Nin_, int Nrow_, int n_off_, float* __restrict__ ypart) {
+                     int64_t nbh, PassArgs pa) {
     using namespace ws1;
-    const int Nin = PAD ? Nin_ : N;
-    const int Nrow = YM == 0 ? Nin : Nrow_;
-    const int n_off = YM == 0 ? 0 : n_off_;
+    const int Nin = GEN ? pa.nin : N, Nrow = GEN ? pa.nrow : N, n_off = GEN ? pa.n_off : 0;
+    const int Pin = GP ? pa.pin : P, Pcol = GP ? pa.pcol : P, p_off = GP ? pa.p_off : 0;
+    constexpr int ym = YM;
+    float* const ypart = pa.ypart;
     __shared__ __attribute__((aligned(16))) uint16_t sBt[2][QRP * NS];  // B~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NS];  // C~ [rho][n]
     __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];    // X^T [p][rho]
@@ -1075,19 +1098,21 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     const int h = int(bh % H);
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
-    const float Dh = (YM == 2 || YM == 3) ? 0.f : Dv[h];  // D x once, in the first pass
+    const float Dh = ym >= 2 ? 0.f : Dv[h];  // D x once, in the first row pass
     // pairs past the caller's Nin / 2 hold zero rows: rate 0
     const float* omh = omega ? omega + int64_t(h) * (Nrow / 2) + n_off / 2 : nullptr;
-    auto omk = [&](int k) { return (omh && (!PAD || 2 * k < Nin)) ? omh[k] : 0.f; };
+    auto omk = [&](int k) { return (omh && (!GEN || 2 * k < Nin)) ? omh[k] : 0.f; };
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
         cb.B = Bm + (tok0 * G + grp) * int64_t(Nrow) + n_off;
         cb.C = Cm + (tok0 * G + grp) * int64_t(Nrow) + n_off;
-        cb.x = x + (tok0 * H + h) * int64_t(P);
+        cb.x = x + (tok0 * H + h) * int64_t(Pcol) + p_off;
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
         cb.nin = Nin;
         cb.nrow = Nrow;
+        cb.pin = Pin;
+        cb.pcol = Pcol;
         return cb;
     };
 
@@ -1160,9 +1185,11 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * nt + 4 * g4 + e;
-                float v = (h0 && n < Nin) ? h0[(bh * Nrow + n_off + n) * P + p] : 0.f;
-                if (carry_B && n < Nin)
-                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * Nrow + n_off + n]) * bf16_to_f32(carry_x[bh * P + p]);
+                const bool in = n < Nin && p < Pin;
+                float v = (h0 && in) ? h0[(bh * Nrow + n_off + n) * Pcol + p_off + p] : 0.f;
+                if (carry_B && in)
+                    v += dl0 * bf16_to_f32(carry_B[(b * G + grp) * Nrow + n_off + n]) *
+                         bf16_to_f32(carry_x[bh * Pcol + p_off + p]);
                 gst[m][e] = v;
             }
             *reinterpret_cast<u32x2*>(&sGT[0][p * NS + 16 * nt + 4 * g4]) =
@@ -1266,13 +1293,14 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             c1t = n1t;
         }
         if (ti < nq) {
-            const int64_t yo = ((b * L + c * Q + ti) * H + h) * int64_t(P);
+            const int64_t yo = ((b * L + c * Q + ti) * H + h) * int64_t(Pcol) + p_off;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int p = 16 * q + 4 * g4;
+                if (GP && p >= Pin) continue;  // Pin is a multiple of 8
                 floatx4 v = acc[q];
-                if constexpr (YM == 2 || YM == 3) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
-                if constexpr (YM == 1 || YM == 3)
+                if (ym >= 2) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
+                if (ym == 1 || ym == 3)
                     *reinterpret_cast<floatx4*>(ypart + yo + p) = v;
                 else
                     *reinterpret_cast<u32x2*>(y + yo + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
@@ -1347,59 +1375,53 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int n = 16 * nt + 4 * g4 + e;
-                    if (n < Nin) h_out[(bh * Nrow + n_off + n) * P + p] = v[e];
+                    if (n < Nin && p < Pin) h_out[(bh * Nrow + n_off + n) * Pcol + p_off + p] = v[e];
                 }
             }
         }
     }
 }
 
-// One pass over rows [n_off, n_off + nin) of the caller's N (ym as YM above).
-struct RowPass {
-    int nin, n_off, ym;
-    float* ypart;
-};
-
+// Calls f(GEN, YM, GP) with the instance for a pass: the exact N = 128, P = 64
+// problem, or a general pass of the given kind.
 template <class F>
-hipError_t dispatch_pass(const RowPass& rp, F&& launch) {
-    // the instances that exist: every YM without padding; padding only in a
-    // single pass or the last one (the earlier passes hold 128 rows)
-    const bool pad = rp.nin != N;
-    switch (rp.ym) {
-        case 0: return pad ? launch(std::integral_constant<bool, true>{}, std::integral_constant<int, 0>{})
-                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 0>{});
-        case 1: return pad ? hipErrorInvalidValue
-                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 1>{});
-        case 2: return pad ? launch(std::integral_constant<bool, true>{}, std::integral_constant<int, 2>{})
-                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 2>{});
-        case 3: return pad ? hipErrorInvalidValue
-                           : launch(std::integral_constant<bool, false>{}, std::integral_constant<int, 3>{});
-    }
-    return hipErrorInvalidValue;
+hipError_t dispatch_pass(bool gen, const PassArgs& pa, F&& f) {
+    using std::integral_constant;
+    if (!gen) return f(integral_constant<bool, false>{}, integral_constant<int, 0>{}, integral_constant<bool, false>{});
+    const bool gp = pa.pcol != P;
+    auto with_ym = [&](auto g) {
+        switch (pa.ym) {
+            case 0: return f(integral_constant<bool, true>{}, integral_constant<int, 0>{}, g);
+            case 1: return f(integral_constant<bool, true>{}, integral_constant<int, 1>{}, g);
+            case 2: return f(integral_constant<bool, true>{}, integral_constant<int, 2>{}, g);
+            case 3: return f(integral_constant<bool, true>{}, integral_constant<int, 3>{}, g);
+        }
+        return hipErrorInvalidValue;
+    };
+    return gp ? with_ym(integral_constant<bool, true>{}) : with_ym(integral_constant<bool, false>{});
 }
 
-hipError_t launch_ws_r1(const PrefillArgs& a, const RowPass& rp) {
+hipError_t launch_ws_r1(const PrefillArgs& a, const PassArgs& pa, bool gen) {
     const int64_t nbh = a.b * a.H;
-    return dispatch_pass(rp, [&](auto pad, auto ym) {
-        constexpr bool PD = decltype(pad)::value;
+    return dispatch_pass(gen, pa, [&](auto g, auto ym, auto gp) {
+        constexpr bool GEN = decltype(g)::value, GP = decltype(gp)::value;
         constexpr int YM = decltype(ym)::value;
-        auto kern = a.omega ? prefill_ws_r1_kernel<true, PD, YM> : prefill_ws_r1_kernel<false, PD, YM>;
+        auto kern = a.omega ? prefill_ws_r1_kernel<true, GEN, YM, GP> : prefill_ws_r1_kernel<false, GEN, YM, GP>;
         hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws1::NCW + ws1::NSW)), 0, a.stream,
                            static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
-                           rp.nin, a.N, rp.n_off, rp.ypart);
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, pa);
         return hipGetLastError();
     });
 }
 
 template <int R, int NW>
-hipError_t launch_r(const PrefillArgs& a, const RowPass& rp) {
+hipError_t launch_r(const PrefillArgs& a, const PassArgs& pa, bool gen) {
     const int64_t nbh = a.b * a.H;
     SegArgs sa{a.plan.segments, a.plan.chunks_per_segment, nullptr, nullptr, nullptr, nullptr};
     if (sa.nseg > 1) {
-        if (rp.ym != 0) return hipErrorInvalidValue;  // segments only in a single pass
+        if (pa.ym != 0) return hipErrorInvalidValue;  // segments only in a single row pass
         const PrefillWorkspace w =
             prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
         char* base = static_cast<char*>(a.workspace);
@@ -1412,52 +1434,62 @@ hipError_t launch_r(const PrefillArgs& a, const RowPass& rp) {
         const hipError_t e = launch_copy_or_zero(sa.ctrl, nullptr, 2 + nbh * sa.nseg, a.stream);
         if (e != hipSuccess) return e;
     }
-    return dispatch_pass(rp, [&](auto pad, auto ym) {
-        constexpr bool PD = decltype(pad)::value;
+    return dispatch_pass(gen, pa, [&](auto g, auto ym, auto gp) {
+        constexpr bool GEN = decltype(g)::value, GP = decltype(gp)::value;
         constexpr int YM = decltype(ym)::value;
-        hipLaunchKernelGGL((prefill_mfma_kernel<R, NW, PD, YM>), dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW), 0,
-                           a.stream, static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
+        hipLaunchKernelGGL((prefill_mfma_kernel<R, NW, GEN, YM, GP>), dim3(unsigned(nbh * sa.nseg)), dim3(64 * NW),
+                           0, a.stream, static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
-                           rp.nin, a.N, rp.n_off, rp.ypart, sa);
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, pa,
+                           sa);
         return hipGetLastError();
     });
 }
 
 }  // namespace
 
-// N up to 128 in one pass (below 128 zero-padded: the loads of B and C rows stop
-// at N_); larger N in passes of 128 rows whose outputs meet in fp32 in the workspace
+// N and P multiples of 8: up to 128 rows and 64 columns in one pass (zero-padded
+// below: the loads of B, C and x rows stop at the caller's sizes); beyond, in
+// passes of 128 rows (outputs summed in fp32 in the workspace) and 64 columns
 bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dtype io) {
-    return io == M3_BF16 && N_ >= 8 && N_ <= kMfmaMaxN && N_ % 8 == 0 && P_ == P &&
-           (R == 1 || R == 2 || R == 4) && chunk >= 1 && chunk <= 64;
+    return io == M3_BF16 && N_ >= 8 && N_ <= kMfmaMaxN && N_ % 8 == 0 && P_ >= 8 && P_ <= kMfmaMaxP &&
+           P_ % 8 == 0 && (R == 1 || R == 2 || R == 4) && chunk >= 1 && chunk <= 64;
 }
 
-bool mfma_segments_supported(int32_t R, int32_t N_) { return R != 1 && N_ <= N; }
+bool mfma_segments_supported(int32_t R, int32_t N_, int32_t P_) { return R != 1 && N_ <= N && P_ <= P; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
     if (a.b * a.H * a.plan.segments > 0x7fffffff) return hipErrorInvalidValue;
     if (a.R == 1 && a.plan.segments != 1) return hipErrorInvalidValue;
-    const int passes = (a.N + N - 1) / N;
+    const int row_passes = (a.N + N - 1) / N, col_passes = (a.P + P - 1) / P;
+    const bool gen = a.N != N || a.P != P;
     float* ypart = nullptr;
-    if (passes > 1) {
+    if (row_passes > 1) {
         const PrefillWorkspace w =
             prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
         ypart = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + w.ypart_off);
     }
-    for (int k = 0; k < passes; ++k) {
-        const RowPass rp{a.N - k * N < N ? a.N - k * N : N, k * N,
-                         passes == 1 ? 0 : k == 0 ? 1 : k == passes - 1 ? 2 : 3, ypart};
-        hipError_t e;
-        switch (a.R) {
-            case 1: e = launch_ws_r1(a, rp); break;
-            case 2: e = launch_r<2, 4>(a, rp); break;
-            case 4: e = launch_r<4, 4>(a, rp); break;
-            default: e = hipErrorInvalidValue;
+    for (int j = 0; j < col_passes; ++j)
+        for (int k = 0; k < row_passes; ++k) {
+            PassArgs pa;
+            pa.nin = a.N - k * N < N ? a.N - k * N : N;
+            pa.nrow = a.N;
+            pa.n_off = k * N;
+            pa.pin = a.P - j * P < P ? a.P - j * P : P;
+            pa.pcol = a.P;
+            pa.p_off = j * P;
+            pa.ym = row_passes == 1 ? 0 : k == 0 ? 1 : k == row_passes - 1 ? 2 : 3;
+            pa.ypart = ypart;
+            hipError_t e;
+            switch (a.R) {
+                case 1: e = launch_ws_r1(a, pa, gen); break;
+                case 2: e = launch_r<2, 4>(a, pa, gen); break;
+                case 4: e = launch_r<4, 4>(a, pa, gen); break;
+                default: e = hipErrorInvalidValue;
+            }
+            if (e != hipSuccess) return e;
         }
-        if (e != hipSuccess) return e;
-    }
     return hipSuccess;
 }
 

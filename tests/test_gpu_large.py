@@ -4,9 +4,9 @@ and the MIMO rank of "复值SSM × 广义梯形离散 × MIMO" §2.3).
 
 With bf16 I/O the prefill cases here run the token-walk kernel (state in
 registers, rank contractions on MFMA; N, P multiples of 16 up to 256 and 64, R
-up to 8): the shapes the chunked MFMA kernels do not take (P other than 64, R
-3, 5, 6, 7); N 256 at P 64 and R 1, 2, 4 runs the chunked kernels in two row
-passes (its full-size case below). fp32 I/O runs the generic chunked kernel,
+up to 8): the ranks the chunked MFMA kernels do not take (3, 5, 6, 7, 8); N 256
+at R 1, 2, 4 runs the chunked kernels in two row passes (its full-size case
+below). fp32 I/O runs the generic chunked kernel,
 decode the generic step. The oracle runs the
 same problem in fp64; bars are the recurrence's own (1e-4 fp32, 2e-2 bf16 I/O,
 max-relative per (batch, head) slice).
@@ -22,14 +22,14 @@ pytestmark = pytest.mark.gpu
 
 PCASES = [
     # b, L, H, G, P, N, R, io, chunk
-    (1, 150, 2, 1, 48, 256, 1, "bf16", 64),   # N 256 (rows split over two waves), P 48, a ragged last block
+    (1, 150, 2, 1, 48, 256, 3, "bf16", 64),   # N 256 (rows split over two waves), P 48, a ragged last block
     (2, 70, 2, 1, 64, 128, 8, "bf16", 32),    # R 8
     (1, 90, 3, 3, 64, 256, 6, "bf16", 64),    # N 256 and R 6, one B, C per head
     (2, 41, 4, 2, 64, 128, 3, "bf16", 64),    # R 3 (the MFMA kernels take 1, 2, 4); b*H = 8: XCD order
     (1, 33, 2, 1, 32, 64, 5, "bf16", 64),     # P 32 (two waves idle), N 64, R 5
     (1, 17, 2, 1, 48, 208, 7, "bf16", 64),    # N 208 (13 row tiles), P 48, R 7
     (1, 37, 2, 1, 48, 208, 3, "bf16", 64),    # N 208 with R 3: rows split over two waves, a partial half
-    (3, 1, 2, 1, 32, 256, 2, "bf16", 64),     # one token
+    (3, 1, 2, 1, 32, 256, 3, "bf16", 64),     # one token
     (1, 45, 2, 1, 16, 256, 8, "f32", 16),     # fp32: the generic kernel
 ]
 

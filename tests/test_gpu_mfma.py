@@ -1,4 +1,4 @@
-"""GPU parity of the bf16-MFMA chunked prefill (N = 128; below zero-padded; above in row passes; P = 64; R in {1, 2, 4}).
+"""GPU parity of the bf16-MFMA chunked prefill: N = 128, P = 64 (below zero-padded, above in row / column passes), R in {1, 2, 4}.
 
 Small cases cover every chunk size class, ragged tails, groups, initial state and
 carry; full-size workloads compare sampled (batch, head) walks with the oracle.
@@ -109,6 +109,36 @@ def test_mfma_row_passes(case):
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
     assert tuple(h.shape) == (b, H, N, 64)
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+COLS = [
+    # b, L, H, G, P, N, R, chunk, h0_std, carry
+    (1, 130, 2, 1, 32, 128, 1, 64, 0.1, True),
+    (2, 77, 2, 2, 8, 64, 1, 33, 0.0, True),
+    (1, 100, 3, 1, 48, 128, 2, 64, 0.1, True),
+    (1, 150, 2, 1, 128, 128, 1, 64, 0.1, True),    # two column passes
+    (1, 90, 2, 2, 200, 256, 4, 64, 0.1, True),     # 4 column x 2 row passes, last column pass 8 wide
+    (1, 70, 2, 1, 96, 64, 4, 16, 0.0, True),
+    (1, 1100, 2, 1, 32, 64, 4, 64, 0.1, True),     # one pass, padded rows and columns, two segments
+]
+
+
+@pytest.mark.parametrize("case", COLS, ids=[str(c) for c in COLS])
+def test_mfma_column_passes(case):
+    """P other than 64: below zero-padded, above in passes of 64 columns (each its own problem)."""
+    b, L, H, G, P, N, R, chunk, h0s, carry = case
+    plan = binding.plan(binding.dims(b, L, H, G, P, N), R, chunk, binding.M3_BF16)
+    assert plan.path == binding.M3_PATH_MFMA
+    if L == 1100:
+        assert plan.segments == 2
+    _flush(f"mfma column-pass case {case}")
+    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=P, dstate=N, rank=R, io_dtype="bf16",
+                            dist="lm", wid=970 + COLS.index(case), h0_std=h0s, with_carry=carry)
+    y_ref, h_ref = oracle.scan(p)
+    y, h = gpu_prefill(p, chunk)
+    assert tuple(h.shape) == (b, H, N, P)
     assert_close(y, y_ref, TOL["bf16"], "y")
     assert_close(h, h_ref, TOL["bf16"], "h_out")
 
