@@ -41,19 +41,21 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
 #define M3_DECODE_THREADS_R4 1024
 #endif
 
-// N = 128, P = 64: thread (kk, q) owns rows (2k, 2k+1), k = kk + (NTH/16)*it,
-// it < 1024/NTH, and columns 4q..4q+3, loaded and stored as float4 (a wave
-// covers four 256-byte row segments per access).
-template <typename T, int R, int NTH>
+// N in {64, 128, 256}, P in {32, 64, 128}: with QP = P / 4 column quads per
+// row, thread (kk, q), q = tid % QP, owns rows (2k, 2k+1), k = kk + (NTH/QP)*it,
+// it < (N/2) / (NTH/QP), and columns 4q..4q+3, loaded and stored as float4 (a
+// wave covers 64/QP row segments of P floats per access).
+template <typename T, int R, int NTH, int N, int P>
 __global__ void __launch_bounds__(NTH)
-decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
+decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
                        const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                        const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                        const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
                        int G) {
-    constexpr int N = 128, P = 64, K = 64;
-    constexpr int IT = 1024 / NTH;  // row pairs per thread
-    constexpr int KS = NTH / 16;    // row-pair stride between a thread's iterations
+    constexpr int K = N / 2, QP = P / 4;
+    constexpr int KS = NTH / QP;  // row-pair stride between a thread's iterations
+    constexpr int IT = K / KS;    // row pairs per thread
+    static_assert(NTH % QP == 0 && K % KS == 0 && IT >= 1 && QP <= 64 && NTH % 64 == 0, "decode tiling");
     __shared__ float sB[R][N], sBp[R][N], sC[R][N];
     __shared__ float sx[R][P], sxp[R][P];
     __shared__ float red[NTH / 64][R][P];
@@ -65,7 +67,7 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
     const int g = h / (H / G);
     const int64_t bg = b * G + g;
     float* hs = hstate + bh * (N * P);
-    const int q = tid & 15, kk = tid >> 4;
+    const int q = tid % QP, kk = tid / QP;
 
     float4 v0[IT], v1[IT];
 #pragma unroll
@@ -132,16 +134,16 @@ decode_n128_p64_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* _
         *reinterpret_cast<float4*>(hs + (2 * k + 1) * P + 4 * q) = make_float4(e1[0], e1[1], e1[2], e1[3]);
     }
 
-    // reduce over the row groups: 4 in a wave (lanes 16 apart), then across waves
+    // reduce over the row groups: 64/QP in a wave (lanes QP apart), then across waves
     const int wave = tid >> 6;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             float v = yacc[r][c];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            if ((tid & 63) < 16) red[wave][r][4 * q + c] = v;
+#pragma unroll
+            for (int sh = QP; sh < 64; sh <<= 1) v += __shfl_xor(v, sh);
+            if ((tid & 63) < QP) red[wave][r][4 * q + c] = v;
         }
     __syncthreads();
     const float Dh = D[h];
@@ -368,6 +370,43 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
             carry_B[(int64_t(wr) * nb * G + bg) * int64_t(R) * N + e] = Bt[e];
 }
 
+bool rows_kernel_sizes(int N, int P) {
+    return (N == 64 || N == 128 || N == 256) && (P == 32 || P == 64 || P == 128);
+}
+
+// threads per workgroup: 2 row pairs per thread at R 1, one at R 2, 4 (as for
+// N 128, P 64), at most 1024 (512 took 11% longer at N 256 and at P 128)
+template <typename T, int R, int N, int P>
+hipError_t launch_rows(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x, const T* B, const T* C, T* y) {
+    constexpr int per = R == 1 ? 16 : 8;  // state floats per thread
+    constexpr int want = N * P / per, cap = 1024;
+    constexpr int NTH = want < cap ? want : cap;
+    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx, a.rd_slot, x,
+                       a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+    return hipGetLastError();
+}
+
+template <typename T, int N, int P>
+hipError_t launch_rows_r(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x, const T* B, const T* C, T* y) {
+    switch (a.R) {
+        case 1: return launch_rows<T, 1, N, P>(a, grid, cB, cx, x, B, C, y);
+        case 2: return launch_rows<T, 2, N, P>(a, grid, cB, cx, x, B, C, y);
+        case 4: return launch_rows<T, 4, N, P>(a, grid, cB, cx, x, B, C, y);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_rows_sized(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x, const T* B, const T* C, T* y) {
+#define M3_ROWS(NN, PP) \
+    if (a.N == NN && a.P == PP) return launch_rows_r<T, NN, PP>(a, grid, cB, cx, x, B, C, y);
+    M3_ROWS(64, 32) M3_ROWS(64, 64) M3_ROWS(64, 128)
+    M3_ROWS(128, 32) M3_ROWS(128, 128)
+    M3_ROWS(256, 32) M3_ROWS(256, 64) M3_ROWS(256, 128)
+#undef M3_ROWS
+    return hipErrorInvalidValue;
+}
+
 template <typename T>
 hipError_t launch_t(const DecodeArgs& a) {
     const dim3 grid(unsigned(a.b * a.H));
@@ -386,13 +425,18 @@ hipError_t launch_t(const DecodeArgs& a) {
         }
     }
     if (a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4)) {
-        auto kern = a.R == 1 ? decode_n128_p64_kernel<T, 1, M3_DECODE_THREADS_R1>
-                  : a.R == 2 ? decode_n128_p64_kernel<T, 2, M3_DECODE_THREADS_R4>
-                             : decode_n128_p64_kernel<T, 4, M3_DECODE_THREADS_R4>;
+        auto kern = a.R == 1 ? decode_rows_kernel<T, 1, M3_DECODE_THREADS_R1, 128, 64>
+                  : a.R == 2 ? decode_rows_kernel<T, 2, M3_DECODE_THREADS_R4, 128, 64>
+                             : decode_rows_kernel<T, 4, M3_DECODE_THREADS_R4, 128, 64>;
         const int nth = a.R == 1 ? M3_DECODE_THREADS_R1 : M3_DECODE_THREADS_R4;
         hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A,
                            a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     } else {
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            // other state sizes and head dims (bf16 I/O): the same kernel, instantiated per (N, P)
+            if (rows_kernel_sizes(a.N, a.P) && (a.R == 1 || a.R == 2 || a.R == 4))
+                return launch_rows_sized<T>(a, grid, cB, cx, x, B, C, y);
+        }
         hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x,
                            a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G, a.P, a.N, a.R);
     }

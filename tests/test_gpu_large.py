@@ -99,9 +99,18 @@ def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
 
 DCASES = [
     # b, L, H, G, P, N, R, io
-    (2, 8, 2, 1, 64, 256, 1, "bf16"),
-    (2, 8, 2, 1, 64, 128, 8, "bf16"),
+    (2, 8, 2, 1, 64, 256, 1, "bf16"),   # the float4 row kernel at N 256
+    (2, 8, 2, 1, 64, 128, 8, "bf16"),   # the generic step (R 8)
     (1, 6, 3, 3, 64, 256, 6, "f32"),
+    # the float4 row kernel at the other (N, P) it is built for (bf16 I/O, R 1, 2, 4)
+    (2, 6, 2, 1, 32, 64, 1, "bf16"),
+    (1, 6, 3, 1, 64, 64, 4, "bf16"),
+    (2, 5, 2, 2, 128, 64, 2, "bf16"),
+    (1, 6, 2, 1, 32, 128, 4, "bf16"),
+    (2, 6, 2, 1, 128, 128, 1, "bf16"),
+    (1, 6, 2, 1, 32, 256, 2, "bf16"),
+    (1, 5, 4, 2, 64, 256, 4, "bf16"),
+    (1, 6, 2, 1, 128, 256, 1, "bf16"),
 ]
 
 
