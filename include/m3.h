@@ -77,7 +77,10 @@ typedef struct m3_dims {
 typedef struct m3_plan {
     int64_t n_chunks;        /* ceil(L / chunk) */
     int64_t last_chunk_len;  /* L - (n_chunks - 1) * chunk, 0 when L == 0 */
-    int32_t segments;        /* sequence segments per (b, h) walked in parallel */
+    int32_t segments;        /* sequence segments per (b, h) walked in parallel; the
+                                environment variable M3_PREFILL_SEGMENTS (a positive
+                                integer, read at planning time) overrides the count
+                                the plan would choose, where segments apply */
     int64_t chunks_per_segment;
     int32_t path;            /* M3_PATH_* below */
     size_t workspace_bytes;  /* what m3_prefill needs (0 allowed when this is 0) */

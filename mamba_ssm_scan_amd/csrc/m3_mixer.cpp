@@ -30,7 +30,7 @@
 namespace {
 
 constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch inside the caller's workspace
-constexpr int kCandidates = 16;                       // algorithms timed per GEMM shape at first use
+constexpr int kCandidates = 64;                       // algorithms timed per GEMM shape at first use
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
