@@ -154,7 +154,8 @@ struct m3_mixer {
         return M3_OK;
     }
 
-    // index of the fastest candidate: one warm-up call and 3 timed calls each (HIP events on s)
+    // index of the fastest candidate: one warm-up call, then the best of 3 rounds of 3
+    // timed calls each (HIP events on s; a single round let noise pick slower kernels)
     int fastest(const Gemm& g, const hipblasLtMatmulHeuristicResult_t* res, int n, const void* U, const void* W,
                 void* D, void* ws, hipStream_t s) {
         hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -167,14 +168,16 @@ struct m3_mixer {
         for (int i = 0; i < n; ++i) {
             if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > kGemmWorkspace) continue;
             if (run(g, res[i].algo, U, W, D, ws, s) != M3_OK) continue;
-            hipEventRecord(e0, s);
-            for (int k = 0; k < 3; ++k) run(g, res[i].algo, U, W, D, ws, s);
-            hipEventRecord(e1, s);
-            float ms = 0.f;
-            if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
-                ms < best_ms) {
-                best_ms = ms;
-                best = i;
+            for (int round = 0; round < 3; ++round) {
+                hipEventRecord(e0, s);
+                for (int k = 0; k < 3; ++k) run(g, res[i].algo, U, W, D, ws, s);
+                hipEventRecord(e1, s);
+                float ms = 0.f;
+                if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
+                    ms < best_ms) {
+                    best_ms = ms;
+                    best = i;
+                }
             }
         }
         hipEventDestroy(e0);
