@@ -17,7 +17,11 @@
 // chosen GEMM algorithms (per shape), so it must not be shared between threads.
 // The first call for a GEMM shape times the library's candidate algorithms on
 // the call's own operands and synchronises the stream once; calls captured in
-// a graph should therefore follow one eager call of the same sizes.
+// a graph should therefore follow one eager call of the same sizes. For few
+// tokens (a decode step) the input projections fan out to three side streams of
+// the mixer object (fork and join events on the caller's stream, so a captured
+// call captures them too); the object must then not be used from two streams
+// at once.
 #include <hipblaslt/hipblaslt.h>
 
 #include <cstdio>
@@ -29,7 +33,9 @@
 
 namespace {
 
-constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch inside the caller's workspace
+constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch per stream, in the caller's workspace
+constexpr int kSide = 3;                              // side streams the decode-step projections fan out to
+constexpr int64_t kFanOutMaxTokens = 1024;            // fan out only GEMMs this short (they cannot fill the chip)
 constexpr int kCandidates = 64;                       // algorithms timed per GEMM shape at first use
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -67,7 +73,7 @@ MixerLayout layout(const m3_dims* d, int32_t R, int32_t chunk, size_t* pre_bytes
     L.xlast = take(size_t(d->batch) * HRP * 2);
     *pre_bytes = m3_prefill_workspace_size(d, R, chunk, M3_BF16);
     L.pre = take(*pre_bytes);
-    L.gemm = take(kGemmWorkspace);
+    L.gemm = take(kGemmWorkspace * (1 + kSide));
     L.total = o;
     return L;
 }
@@ -77,8 +83,17 @@ MixerLayout layout(const m3_dims* d, int32_t R, int32_t chunk, size_t* pre_bytes
 struct m3_mixer {
     hipblasLtHandle_t lt = nullptr;
     std::map<std::tuple<int64_t, int64_t, int64_t, int>, Gemm> gemms;
+    // short input projections run concurrently: forked from the caller's stream to
+    // these (default priority) and joined back with events
+    hipStream_t side[kSide] = {};
+    hipEvent_t fork = nullptr, join[kSide] = {};
 
     ~m3_mixer() {
+        for (int i = 0; i < kSide; ++i) {
+            if (side[i]) (void)hipStreamDestroy(side[i]);
+            if (join[i]) (void)hipEventDestroy(join[i]);
+        }
+        if (fork) (void)hipEventDestroy(fork);
         for (auto& kv : gemms) {
             Gemm& g = kv.second;
             if (g.a) hipblasLtMatrixLayoutDestroy(g.a);
@@ -203,14 +218,29 @@ m3_status check_weights(const m3_mixer_weights* w) {
 m3_status project_in(m3_mixer* m, const m3_mixer_weights* w, const m3_dims* d, int32_t R, int64_t ntok,
                      const void* u, char* ws, const MixerLayout& L, hipStream_t s) {
     const int64_t K = w->d_model, HRP = int64_t(d->heads) * R * d->headdim, GRN = int64_t(d->groups) * R * d->dstate;
-    void* gws = ws + L.gemm;
+    // Few tokens (a decode step): x on the caller's stream, z, (B, C) and (dt, lambda)
+    // on the side streams, each with its own GEMM scratch, joined before the
+    // prologue. Many tokens: all on the caller's stream (each GEMM fills the chip).
+    const bool fan = ntok <= kFanOutMaxTokens;
+    auto gws = [&](int i) { return static_cast<void*>(ws + L.gemm + size_t(fan ? i : 0) * kGemmWorkspace); };
+    auto on = [&](int i) { return fan && i > 0 ? m->side[i - 1] : s; };
+    if (fan) {
+        if (hipEventRecord(m->fork, s) != hipSuccess) return m3::set_error(M3_EHIP, "event record failed");
+        for (int i = 0; i < kSide; ++i)
+            if (hipStreamWaitEvent(m->side[i], m->fork, 0) != hipSuccess)
+                return m3::set_error(M3_EHIP, "stream wait failed");
+    }
     m3_status st;
-    if ((st = m->gemm(ntok, HRP, K, u, w->W_x, ws + L.x, false, gws, s)) != M3_OK) return st;
-    if ((st = m->gemm(ntok, HRP, K, u, w->W_z, ws + L.z, false, gws, s)) != M3_OK) return st;
-    if ((st = m->gemm(ntok, GRN, K, u, w->W_B, ws + L.B, false, gws, s)) != M3_OK) return st;
-    if ((st = m->gemm(ntok, GRN, K, u, w->W_C, ws + L.C, false, gws, s)) != M3_OK) return st;
-    if ((st = m->gemm(ntok, d->heads, K, u, w->W_dt, ws + L.dt, true, gws, s)) != M3_OK) return st;
-    if ((st = m->gemm(ntok, d->heads, K, u, w->W_lambda, ws + L.lam, true, gws, s)) != M3_OK) return st;
+    if ((st = m->gemm(ntok, HRP, K, u, w->W_x, ws + L.x, false, gws(0), on(0))) != M3_OK) return st;
+    if ((st = m->gemm(ntok, HRP, K, u, w->W_z, ws + L.z, false, gws(1), on(1))) != M3_OK) return st;
+    if ((st = m->gemm(ntok, GRN, K, u, w->W_B, ws + L.B, false, gws(2), on(2))) != M3_OK) return st;
+    if ((st = m->gemm(ntok, GRN, K, u, w->W_C, ws + L.C, false, gws(2), on(2))) != M3_OK) return st;
+    if ((st = m->gemm(ntok, d->heads, K, u, w->W_dt, ws + L.dt, true, gws(3), on(3))) != M3_OK) return st;
+    if ((st = m->gemm(ntok, d->heads, K, u, w->W_lambda, ws + L.lam, true, gws(3), on(3))) != M3_OK) return st;
+    if (fan)
+        for (int i = 0; i < kSide; ++i)
+            if (hipEventRecord(m->join[i], m->side[i]) != hipSuccess || hipStreamWaitEvent(s, m->join[i], 0) != hipSuccess)
+                return m3::set_error(M3_EHIP, "stream join failed");
     float* dt = reinterpret_cast<float*>(ws + L.dt);
     float* lam = reinterpret_cast<float*>(ws + L.lam);
     return m3_prologue(d, R, M3_BF16, ntok, ws + L.B, ws + L.C, w->B_weight, w->B_bias, w->C_weight, w->C_bias, w->eps,
@@ -239,6 +269,14 @@ m3_status m3_mixer_create(m3_mixer** out) {
         m->lt = nullptr;
         delete m;
         return m3::set_error(M3_EHIP, "hipblasLtCreate failed");
+    }
+    bool ok = hipEventCreateWithFlags(&m->fork, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; i < kSide && ok; ++i)
+        ok = hipStreamCreateWithFlags(&m->side[i], hipStreamNonBlocking) == hipSuccess &&
+             hipEventCreateWithFlags(&m->join[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        delete m;
+        return m3::set_error(M3_EHIP, "stream / event creation failed");
     }
     *out = m;
     return M3_OK;
