@@ -509,7 +509,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
