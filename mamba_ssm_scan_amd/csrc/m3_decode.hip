@@ -370,8 +370,11 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
             carry_B[(int64_t(wr) * nb * G + bg) * int64_t(R) * N + e] = Bt[e];
 }
 
-bool rows_kernel_sizes(int N, int P) {
-    return (N == 64 || N == 128 || N == 256) && (P == 32 || P == 64 || P == 128);
+// (N, P, R) the row kernel is instantiated for (bf16 I/O) besides N 128, P 64 at R 1, 2, 4:
+// R 8 only where its LDS (the rank rows and the per-wave y partials) fits
+bool rows_kernel_sizes(int N, int P, int R) {
+    const bool np = (N == 64 || N == 128 || N == 256) && (P == 32 || P == 64 || P == 128);
+    return np && (R == 1 || R == 2 || R == 3 || R == 4 || (R == 8 && N * P <= 128 * 64));
 }
 
 // threads per workgroup: 2 row pairs per thread at R 1, one at R 2, 4 (as for
@@ -391,7 +394,11 @@ hipError_t launch_rows_r(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* 
     switch (a.R) {
         case 1: return launch_rows<T, 1, N, P>(a, grid, cB, cx, x, B, C, y);
         case 2: return launch_rows<T, 2, N, P>(a, grid, cB, cx, x, B, C, y);
+        case 3: return launch_rows<T, 3, N, P>(a, grid, cB, cx, x, B, C, y);
         case 4: return launch_rows<T, 4, N, P>(a, grid, cB, cx, x, B, C, y);
+        case 8:
+            if constexpr (N * P <= 128 * 64) return launch_rows<T, 8, N, P>(a, grid, cB, cx, x, B, C, y);
+            break;
     }
     return hipErrorInvalidValue;
 }
@@ -401,7 +408,7 @@ hipError_t launch_rows_sized(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const
 #define M3_ROWS(NN, PP) \
     if (a.N == NN && a.P == PP) return launch_rows_r<T, NN, PP>(a, grid, cB, cx, x, B, C, y);
     M3_ROWS(64, 32) M3_ROWS(64, 64) M3_ROWS(64, 128)
-    M3_ROWS(128, 32) M3_ROWS(128, 128)
+    M3_ROWS(128, 32) M3_ROWS(128, 64) M3_ROWS(128, 128)
     M3_ROWS(256, 32) M3_ROWS(256, 64) M3_ROWS(256, 128)
 #undef M3_ROWS
     return hipErrorInvalidValue;
@@ -433,8 +440,8 @@ hipError_t launch_t(const DecodeArgs& a) {
                            a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     } else {
         if constexpr (std::is_same<T, bf16_t>::value) {
-            // other state sizes and head dims (bf16 I/O): the same kernel, instantiated per (N, P)
-            if (rows_kernel_sizes(a.N, a.P) && (a.R == 1 || a.R == 2 || a.R == 4))
+            // other state sizes, head dims and ranks (bf16 I/O): the same kernel, instantiated per (N, P, R)
+            if (rows_kernel_sizes(a.N, a.P, a.R))
                 return launch_rows_sized<T>(a, grid, cB, cx, x, B, C, y);
         }
         hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x,

@@ -100,7 +100,7 @@ def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
 DCASES = [
     # b, L, H, G, P, N, R, io
     (2, 8, 2, 1, 64, 256, 1, "bf16"),   # the float4 row kernel at N 256
-    (2, 8, 2, 1, 64, 128, 8, "bf16"),   # the generic step (R 8)
+    (2, 8, 2, 1, 64, 128, 8, "bf16"),   # the float4 row kernel at R 8
     (1, 6, 3, 3, 64, 256, 6, "f32"),
     # the float4 row kernel at the other (N, P) it is built for (bf16 I/O, R 1, 2, 4)
     (2, 6, 2, 1, 32, 64, 1, "bf16"),
@@ -111,6 +111,10 @@ DCASES = [
     (1, 6, 2, 1, 32, 256, 2, "bf16"),
     (1, 5, 4, 2, 64, 256, 4, "bf16"),
     (1, 6, 2, 1, 128, 256, 1, "bf16"),
+    (2, 6, 2, 1, 64, 128, 3, "bf16"),   # R 3 and R 8 on the row kernel
+    (1, 5, 2, 1, 128, 256, 3, "bf16"),
+    (2, 6, 2, 2, 32, 64, 8, "bf16"),
+    (1, 6, 2, 1, 128, 128, 8, "bf16"),  # R 8 past the row kernel's LDS: the generic step
 ]
 
 
