@@ -87,7 +87,7 @@ typedef struct m3_plan {
 } m3_plan;
 
 /* GENERIC: chunked, fp32 arithmetic, any sizes (the fp32 I/O path).
- * MFMA:    chunked on matrix cores, bf16 I/O, R 1, 2, 4, chunk <= 64, N a
+ * MFMA:    chunked on matrix cores, bf16 I/O, R 1 to 4, chunk <= 64, N a
  *          multiple of 8 up to 512 and P a multiple of 8 up to 1024: passes of
  *          at most 128 state rows and 64 columns (zero-padded inside the kernel
  *          where a pass holds fewer); with N above 128 the row passes' outputs
@@ -95,8 +95,7 @@ typedef struct m3_plan {
  *          b*L*H*R*P*4 bytes).
  * SCAN:    token-by-token walk with the state in registers and the rank
  *          contractions on matrix cores, bf16 I/O, N and P multiples of 16 with
- *          N <= 256, P <= 64, R <= 8, where MFMA does not apply (R 3, 5-8;
- *          chunk unused). */
+ *          N <= 256, P <= 64, R 5 to 8 (chunk unused). */
 enum { M3_PATH_GENERIC = 0, M3_PATH_MFMA = 1, M3_PATH_SCAN = 2 };
 
 /*

@@ -1,5 +1,6 @@
 // m3_prefill_mfma.hip -- chunked prefill on bf16 MFMA (gfx950), N = 128, P = 64,
-// rank R in {1, 2, 4}, chunk <= 64 tokens, bf16 I/O, fp32 state. Other N and
+// rank R in {1, 2, 4} (R 3 on the R 4 kernel with a zero fourth rank), chunk <= 64
+// tokens, bf16 I/O, fp32 state. Other N and
 // P (multiples of 8) run as passes of at most 128 state rows and 64 columns,
 // zero-padded where a pass holds fewer: B/C rows past the pass's rows and x
 // columns past its columns load as zero, so those state entries stay zero and
@@ -200,6 +201,7 @@ struct ChunkBase {
     int nrow;  // length of the caller's B/C rows (the caller's N)
     int pin;   // columns this pass takes from the caller's x rows (<= P); columns pin..P-1 are zero
     int pcol;  // length of the caller's x rows (the caller's P)
+    int rin;   // the caller's rank (<= the kernel's R); ranks rin..R-1 are zero rows
 };
 
 // One pass of the chunked kernels over rows n_off .. n_off + nin - 1 of the
@@ -211,6 +213,7 @@ struct ChunkBase {
 // ypart), 2 last (adds ypart, writes y in bf16).
 struct PassArgs {
     int nin, nrow, n_off, pin, pcol, p_off, ym;
+    int rin;  // the caller's rank: R 3 runs on the R 4 kernel with a zero fourth rank
     float* ypart;
 };
 
@@ -242,10 +245,11 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb
         const int i = (tid >> 4) + m * (S::NT / 16);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const bool in = 8 * pc < cb.nin;
-            cr.b[m][r] = in ? load_tok(cb.B, i, nq, G * R * cb.nrow, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+            const bool in = 8 * pc < cb.nin && r < cb.rin;
+            const int ts = G * cb.rin * cb.nrow;
+            cr.b[m][r] = in ? load_tok(cb.B, i, nq, ts, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
             if constexpr (S::C_LDS)
-                cr.c[m][r] = in ? load_tok(cb.C, i, nq, G * R * cb.nrow, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
+                cr.c[m][r] = in ? load_tok(cb.C, i, nq, ts, r * cb.nrow + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
         }
     }
     const bool xin = 8 * (tid & 7) < cb.pin;
@@ -255,8 +259,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb
         const unsigned rho0 = 2u * ((tid >> 3) + m * (S::NT / 8));
         const int i0 = int(rho0 >> S::LR), r0 = int(rho0 & (R - 1));
         const int i1 = int((rho0 + 1) >> S::LR), r1 = int((rho0 + 1) & (R - 1));
-        cr.x0[m] = xin ? load_tok(cb.x, i0, nq, H * R * cb.pcol, r0 * cb.pcol + 8 * (tid & 7)) : u32x4{0u, 0u, 0u, 0u};
-        cr.x1[m] = xin ? load_tok(cb.x, i1, nq, H * R * cb.pcol, r1 * cb.pcol + 8 * (tid & 7)) : u32x4{0u, 0u, 0u, 0u};
+        const int ts = H * cb.rin * cb.pcol;
+        cr.x0[m] = (xin && r0 < cb.rin) ? load_tok(cb.x, i0, nq, ts, r0 * cb.pcol + 8 * (tid & 7)) : u32x4{0u, 0u, 0u, 0u};
+        cr.x1[m] = (xin && r1 < cb.rin) ? load_tok(cb.x, i1, nq, ts, r1 * cb.pcol + 8 * (tid & 7)) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -268,7 +273,8 @@ __device__ __forceinline__ void load_strip_c(u32x4 (&c)[4], const ChunkBase& cb,
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int n0 = 32 * ks + 8 * (lane >> 4);
-        c[ks] = n0 < cb.nin ? load_tok(cb.C, i, cb.nq, G * S::R * cb.nrow, r * cb.nrow + n0) : u32x4{0u, 0u, 0u, 0u};
+        c[ks] = (n0 < cb.nin && r < cb.rin) ? load_tok(cb.C, i, cb.nq, G * cb.rin * cb.nrow, r * cb.nrow + n0)
+                                            : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -327,6 +333,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     using S = Shape<R, NW>;
     const int Nin = GEN ? pa.nin : N, Nrow = GEN ? pa.nrow : N, n_off = GEN ? pa.n_off : 0;
     const int Pin = GP ? pa.pin : P, Pcol = GP ? pa.pcol : P, p_off = GP ? pa.p_off : 0;
+    const int Rin = GEN ? pa.rin : R;  // the caller's rank (rows of rank Rin..R-1 are zero)
     constexpr int ym = YM;
     float* const ypart = pa.ypart;
     using CR = ChunkRegs<S>;
@@ -399,14 +406,15 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
-        cb.B = Bm + (tok0 * G + grp) * int64_t(R * Nrow) + n_off;
-        cb.C = Cm + (tok0 * G + grp) * int64_t(R * Nrow) + n_off;
-        cb.x = x + (tok0 * H + h) * int64_t(R * Pcol) + p_off;
+        cb.B = Bm + (tok0 * G + grp) * int64_t(Rin * Nrow) + n_off;
+        cb.C = Cm + (tok0 * G + grp) * int64_t(Rin * Nrow) + n_off;
+        cb.x = x + (tok0 * H + h) * int64_t(Rin * Pcol) + p_off;
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
         cb.nin = Nin;
         cb.nrow = Nrow;
         cb.pin = Pin;
         cb.pcol = Pcol;
+        cb.rin = Rin;
         return cb;
     };
 
@@ -443,8 +451,9 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                     float s = 0.f;
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * Nrow + n_off + n]) *
-                             bf16_to_f32(carry_x[(bh * R + r) * Pcol + p_off + p]);
+                        if (r < Rin)
+                            s += bf16_to_f32(carry_B[((b * G + grp) * Rin + r) * Nrow + n_off + n]) *
+                                 bf16_to_f32(carry_x[(bh * Rin + r) * Pcol + p_off + p]);
                     v += dl0 * s;
                 }
                 gst[m][e] = v;
@@ -694,10 +703,10 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                 y_pair(xa, xb, m0, m1);
             }
             // epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
-            if ((rho_i >> LR) < nq) {
+            if ((rho_i >> LR) < nq && (rho_i & (R - 1)) < Rin) {
                 const int i = rho_i >> LR, r = rho_i & (R - 1);
                 const int64_t yo =
-                    ((b * L + c * Q) * H + h) * int64_t(R * Pcol) + int64_t(i * H * R + r) * Pcol + p_off;
+                    ((b * L + c * Q) * H + h) * int64_t(Rin * Pcol) + int64_t(i * H * Rin + r) * Pcol + p_off;
 #pragma unroll
                 for (int q = 0; q < S::PTW; ++q) {
                     const int p = 16 * (pt0 + q) + 4 * g4;
@@ -885,9 +894,9 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                             a[q] = mfma32(ga, cr[ks], a[q]);
                         }
                     }
-                    if (ti < nq) {
-                        uint16_t* yr = y + ((b * L + c0) * H + h) * int64_t(R * Pcol) +
-                                       int64_t(ti * H * R + int(rho & (R - 1))) * Pcol + p_off;
+                    if (ti < nq && int(rho & (R - 1)) < Rin) {
+                        uint16_t* yr = y + ((b * L + c0) * H + h) * int64_t(Rin * Pcol) +
+                                       int64_t(ti * H * Rin + int(rho & (R - 1))) * Pcol + p_off;
                         const float f = wsc[192 + ti];
 #pragma unroll
                         for (int q = 0; q < S::PTW; ++q) {
@@ -1113,6 +1122,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
         cb.nrow = Nrow;
         cb.pin = Pin;
         cb.pcol = Pcol;
+        cb.rin = 1;
         return cb;
     };
 
@@ -1454,7 +1464,7 @@ hipError_t launch_r(const PrefillArgs& a, const PassArgs& pa, bool gen) {
 // passes of 128 rows (outputs summed in fp32 in the workspace) and 64 columns
 bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dtype io) {
     return io == M3_BF16 && N_ >= 8 && N_ <= kMfmaMaxN && N_ % 8 == 0 && P_ >= 8 && P_ <= kMfmaMaxP &&
-           P_ % 8 == 0 && (R == 1 || R == 2 || R == 4) && chunk >= 1 && chunk <= 64;
+           P_ % 8 == 0 && R >= 1 && R <= 4 && chunk >= 1 && chunk <= 64;
 }
 
 bool mfma_segments_supported(int32_t R, int32_t N_, int32_t P_) { return R != 1 && N_ <= N && P_ <= P; }
@@ -1463,7 +1473,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a) {
     if (a.b * a.H * a.plan.segments > 0x7fffffff) return hipErrorInvalidValue;
     if (a.R == 1 && a.plan.segments != 1) return hipErrorInvalidValue;
     const int row_passes = (a.N + N - 1) / N, col_passes = (a.P + P - 1) / P;
-    const bool gen = a.N != N || a.P != P;
+    const bool gen = a.N != N || a.P != P || a.R == 3;
     float* ypart = nullptr;
     if (row_passes > 1) {
         const PrefillWorkspace w =
@@ -1479,12 +1489,14 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a) {
             pa.pin = a.P - j * P < P ? a.P - j * P : P;
             pa.pcol = a.P;
             pa.p_off = j * P;
+            pa.rin = a.R;
             pa.ym = row_passes == 1 ? 0 : k == 0 ? 1 : k == row_passes - 1 ? 2 : 3;
             pa.ypart = ypart;
             hipError_t e;
             switch (a.R) {
                 case 1: e = launch_ws_r1(a, pa, gen); break;
                 case 2: e = launch_r<2, 4>(a, pa, gen); break;
+                case 3:  // the R 4 kernel with a zero fourth rank
                 case 4: e = launch_r<4, 4>(a, pa, gen); break;
                 default: e = hipErrorInvalidValue;
             }

@@ -1,6 +1,6 @@
 // m3_prefill_scan.hip -- prefill as a walk over the tokens with the state in
-// registers, for bf16 I/O at the sizes the chunked MFMA kernels are not built
-// for: N a multiple of 16 up to 256, P a multiple of 16 up to 64, R up to 8.
+// registers, for bf16 I/O at the ranks the chunked MFMA kernels are not built
+// for (R 5 to 8): N a multiple of 16 up to 256, P a multiple of 16 up to 64.
 //
 // Each step is the recurrence itself ("复值SSM × 广义梯形离散 × MIMO，线性模型的
 // 全面重构" §2.1-§2.3; "Mamba-3架构技术解析" §2.1):
@@ -8,9 +8,8 @@
 //   y_t = h^T C_t + D x_t,    U_t = B_t x_t^T (rank R),
 // with alpha = e^{dt A}, gamma = lambda dt, delta = (1 - lambda) dt.
 //
-// One workgroup per (b, h): wave w owns state columns 16 (w % 4) .. + 15 and,
-// at N above 128 with R <= 4, half of the row tiles (512 threads, two waves per
-// SIMD whose per-token chains overlap). In row tile nt, lane (l16, g4) holds rows
+// One workgroup per (b, h): wave w owns state columns 16 w .. + 15 and all the
+// row tiles. In row tile nt, lane (l16, g4) holds rows
 // 16 nt + 4 g4 .. + 3 of its column (two whole rotation pairs), which is the
 // accumulator layout of
 // v_mfma_f32_16x16x16_bf16, so
@@ -19,9 +18,7 @@
 //   y_t[r][p]  = sum_n C_t[r][n] h[n][p]     (A: C, k = n; B: the new state)
 // takes the lane's four new state values, rounded to bf16, as its B operand
 // (as the chunked kernels feed the carried state to their inter-chunk term;
-// the products in U are exact). No cross-lane reduction is left; with the rows
-// split, the two halves' y sums are added in LDS and the block's y is written
-// once, coalesced. Only one
+// the products in U are exact). No cross-lane reduction is left. Only one
 // operand of each product needs its padding zeroed: x^T past rank R (so the
 // A operand of U may hold any finite values there), and the output rows of y
 // past R are not stored (so the A operand of y takes a clamped row).
@@ -65,13 +62,12 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(unsigned, v);
 }
 
-// sizes of one instance: NTL row tiles (N <= 16 NTL), RG groups of 4 ranks (R <= 4 RG),
-// RS waves per 16-column group, each holding NTL / RS row tiles
-template <int NTL, int RG, int RS>
+// sizes of one instance: NTL row tiles (N <= 16 NTL), RG groups of 4 ranks (R <= 4 RG)
+template <int NTL, int RG>
 struct ScanShape {
-    static constexpr int NT = 256 * RS;                         // threads: 4 column groups x RS
+    static constexpr int NT = 256;                              // threads: 4 column groups
     static constexpr int NMAX = 16 * NTL, KMAX = NMAX / 2, RK = 4 * RG;
-    static constexpr int NTW = NTL / RS;                        // row tiles per wave
+    static constexpr int NTW = NTL;                             // row tiles per wave
     static constexpr int BT = (NTL == 16 && RG == 2) ? 8 : 16;  // tokens per staged block
     static constexpr int NS = NMAX + 4;                         // B, C row stride (bf16)
     static constexpr int XS = 64 + 4;                           // x row stride (bf16)
@@ -81,22 +77,21 @@ struct ScanShape {
     static constexpr int MAXCS = BT * KMAX / NT;
 };
 
-template <int NTL, int RG, int RS>
+template <int NTL, int RG>
 struct ScanLds {
-    typedef ScanShape<NTL, RG, RS> S;
+    typedef ScanShape<NTL, RG> S;
     uint16_t B[S::BT][S::RK][S::NS];  // B rank rows of the block's tokens (rows past R zero)
     uint16_t X[S::BT][S::RK][S::XS];  // x rank rows (rows past R zero)
     uint16_t C[S::BT][S::RK][S::NS];  // C rank rows
     float CS[S::BT][S::KMAX][2];        // alpha * (cos, sin) of each pair's step angle
     float GD[S::BT][2];                 // gamma, delta
-    float Y[RS > 1 ? S::BT : 1][S::RK][64];  // y of the block: the row parts' sums meet here (RS > 1)
 };
 
-template <int NTL, int RG, bool FULL, int RS>
-__global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
-    typedef ScanShape<NTL, RG, RS> S;
+template <int NTL, int RG, bool FULL>
+__global__ void __launch_bounds__(256) prefill_scan_kernel(PrefillArgs a) {
+    typedef ScanShape<NTL, RG> S;
     constexpr int BT = S::BT, NT = S::NT;
-    __shared__ __attribute__((aligned(16))) ScanLds<NTL, RG, RS> s;
+    __shared__ __attribute__((aligned(16))) ScanLds<NTL, RG> s;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,7 +106,7 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
     const int g = h / (a.H / a.G);
     const int N = FULL ? S::NMAX : a.N, P = a.P, R = a.R, K = N / 2, ntl = FULL ? NTL : N / 16;
     const int64_t L = a.L;
-    const int cw = w & 3, rh = w >> 2;  // column group, half of the row tiles
+    const int cw = w;  // column group
     const int p = 16 * cw + l16;
     const bool active = 16 * cw < P;    // uniform per wave
     const float Ah = a.A[h], Dh = a.D[h];
@@ -137,13 +132,13 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
     // The walk carries g_t = h_t + delta_{t+1} U_t, the state the next step turns:
     //   h_t = alpha_t Rot g_{t-1} + gamma_t U_t,  y_t = h_t^T C_t + D x_t,  g_t = h_t + delta_{t+1} U_t
     // so U_t is formed once. g_0 = h0 + delta_1 U_0 with U_0 from the caller's carry.
-    // wave (cw, rh) holds row tiles rh NTW .. rh NTW + NTW - 1 of its 16 columns
+    // wave cw holds all row tiles of its 16 columns
     float st[S::NTW][4];
 #pragma unroll
     for (int i = 0; i < S::NTW; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int nt = rh * S::NTW + i, n = 16 * nt + 4 * g4 + e;
+            const int nt = i, n = 16 * nt + 4 * g4 + e;
             st[i][e] = (a.h0 && active && nt < ntl) ? a.h0[(bh * N + n) * int64_t(P) + p] : 0.f;
         }
     const u32x2 zero = {0u, 0u};
@@ -165,7 +160,7 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
             const u32x2 xo = g4 < RG ? xv : zero;
 #pragma unroll
             for (int i = 0; i < S::NTW; ++i) {
-                const int nt = rh * S::NTW + i;
+                const int nt = i;
                 if (FULL || nt < ntl) {
                     const u32x2 ab = load_tr(&s.B[0][4 * gk + (l16 >> 2)][16 * nt + 4 * (l16 & 3)]);
                     const floatx4 U = mfma16(ab, xo, floatx4{0.f, 0.f, 0.f, 0.f});
@@ -249,8 +244,6 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
             s.GD[tid][0] = (lmg ? lmg[t * a.H] : 1.f) * dtg[t * a.H];
             s.GD[tid][1] = delta_at(t + 1);
         }
-        if constexpr (RS > 1)
-            for (int e = tid; e < BT * S::RK * 64; e += NT) (&s.Y[0][0][0])[e] = 0.f;
         __syncthreads();
 
         for (int j = 0; j < (active ? nt_ : 0); ++j) {
@@ -262,7 +255,7 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
             for (int q = 0; q < 4; ++q) yacc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < S::NTW; ++i) {
-                const int nt = rh * S::NTW + i;
+                const int nt = i;
                 if (!FULL && nt >= ntl) continue;
                 const int n0 = 16 * nt;
                 const u32x2 ab = load_tr(&s.B[j][4 * gk + (l16 >> 2)][n0 + 4 * (l16 & 3)]);
@@ -289,20 +282,7 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
                 const int r = 4 * g4 + e;
                 if (r >= R) continue;
                 const float v = (yacc[0][e] + yacc[1][e]) + (yacc[2][e] + yacc[3][e]);
-                if constexpr (RS > 1)  // two parts added onto zero: the order does not change the result
-                    atomicAdd(&s.Y[j][r][p], v);
-                else
-                    Yg[(t0 + j) * rowX + r * P + p] = f32_to_bf16(v + Dh * bf16_to_f32(s.X[j][r][p]));
-            }
-        }
-        if constexpr (RS > 1) {
-            __syncthreads();
-            // y of the block: D x added, rounded, one 64-column row per wave and step
-            for (int q = w; q < nrow; q += NT / 64) {
-                const int j = int((unsigned(q) * invR) >> 16), r = q - j * R;
-                if (lane < P)
-                    Yg[(t0 + j) * rowX + r * P + lane] =
-                        f32_to_bf16(s.Y[j][r][lane] + Dh * bf16_to_f32(s.X[j][r][lane]));
+                Yg[(t0 + j) * rowX + r * P + p] = f32_to_bf16(v + Dh * bf16_to_f32(s.X[j][r][p]));
             }
         }
     }
@@ -311,37 +291,35 @@ __global__ void __launch_bounds__(256 * RS) prefill_scan_kernel(PrefillArgs a) {
     if (a.h_out && active)
 #pragma unroll
         for (int i = 0; i < S::NTW; ++i) {
-            const int nt = rh * S::NTW + i;
+            const int nt = i;
             if (FULL || nt < ntl)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a.h_out[(bh * N + 16 * nt + 4 * g4 + e) * int64_t(P) + p] = st[i][e];
         }
 }
 
-template <int NTL, int RG, int RS>
+template <int NTL, int RG>
 hipError_t launch_ntl_rg(const PrefillArgs& a) {
-    const dim3 grid(unsigned(a.b * a.H)), block(256 * RS);
+    const dim3 grid(unsigned(a.b * a.H)), block(256);
     if (a.N == 16 * NTL)
-        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, true, RS>), grid, block, 0, a.stream, a);
+        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, true>), grid, block, 0, a.stream, a);
     else
-        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, false, RS>), grid, block, 0, a.stream, a);
+        hipLaunchKernelGGL((prefill_scan_kernel<NTL, RG, false>), grid, block, 0, a.stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// ranks 1 to 4 run on the chunked kernels
 bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io) {
-    return io == M3_BF16 && N % 16 == 0 && N <= 256 && P % 16 == 0 && P <= 64 && R >= 1 && R <= 8;
+    return io == M3_BF16 && N % 16 == 0 && N <= 256 && P % 16 == 0 && P <= 64 && R >= 5 && R <= 8;
 }
 
 hipError_t launch_prefill_scan(const PrefillArgs& a) {
     if (a.b * a.H > 0x7fffffff) return hipErrorInvalidValue;
     if (!scan_path_supported(a.P, a.N, a.R, a.io)) return hipErrorInvalidValue;
-    // N <= 128: one wave per 16 columns (8 row tiles each). N <= 256: two waves of 8 row
-    // tiles at R <= 4 (3.5 -> 2.4 ms at N 256, R 1 on b 4 x H 64 x L 2048); at R 5..8 the
-    // larger blocks' staging and the LDS sums cost more than the overlap gains (4.5 vs 5.1 ms)
-    if (a.N <= 128) return a.R <= 4 ? launch_ntl_rg<8, 1, 1>(a) : launch_ntl_rg<8, 2, 1>(a);
-    return a.R <= 4 ? launch_ntl_rg<16, 1, 2>(a) : launch_ntl_rg<16, 2, 1>(a);
+    // one wave per 16 columns: 8 row tiles each up to N 128, 16 up to N 256
+    return a.N <= 128 ? launch_ntl_rg<8, 2>(a) : launch_ntl_rg<16, 2>(a);
 }
 
 }  // namespace m3

@@ -68,12 +68,13 @@ def test_plan_generic_workspace(lib):
 
 
 @pytest.mark.parametrize("N,P,R,io,path", [
-    (128, 64, 1, "bf16", "MFMA"), (128, 64, 4, "bf16", "MFMA"), (128, 64, 3, "bf16", "SCAN"),
+    (128, 64, 1, "bf16", "MFMA"), (128, 64, 4, "bf16", "MFMA"), (128, 64, 3, "bf16", "MFMA"),
+    (128, 64, 5, "bf16", "SCAN"), (120, 64, 5, "bf16", "GENERIC"), (128, 72, 6, "bf16", "GENERIC"),
     (256, 64, 1, "bf16", "MFMA"), (128, 64, 8, "bf16", "SCAN"), (256, 32, 6, "bf16", "SCAN"),
-    (256, 64, 3, "bf16", "SCAN"), (512, 64, 4, "bf16", "MFMA"), (520, 64, 1, "bf16", "GENERIC"),
+    (256, 64, 3, "bf16", "MFMA"), (512, 64, 4, "bf16", "MFMA"), (520, 64, 1, "bf16", "GENERIC"),
     (128, 64, 9, "bf16", "GENERIC"), (272, 64, 1, "bf16", "MFMA"), (128, 72, 1, "bf16", "MFMA"),
     (120, 64, 1, "bf16", "MFMA"), (64, 64, 2, "bf16", "MFMA"), (8, 64, 4, "bf16", "MFMA"),
-    (64, 64, 3, "bf16", "SCAN"), (64, 32, 1, "bf16", "MFMA"), (100, 64, 1, "bf16", "GENERIC"),
+    (64, 64, 3, "bf16", "MFMA"), (64, 32, 1, "bf16", "MFMA"), (100, 64, 1, "bf16", "GENERIC"),
     (128, 36, 1, "bf16", "GENERIC"), (128, 1024, 2, "bf16", "MFMA"), (128, 1032, 1, "bf16", "GENERIC"),
     (256, 64, 8, "f32", "GENERIC")])
 def test_plan_path_choice(lib, N, P, R, io, path):

@@ -3,10 +3,10 @@ ranks R = 6 and 8 (the state-size and rank knobs of "Mamba-3架构技术解析" 
 and the MIMO rank of "复值SSM × 广义梯形离散 × MIMO" §2.3).
 
 With bf16 I/O the prefill cases here run the token-walk kernel (state in
-registers, rank contractions on MFMA; N, P multiples of 16 up to 256 and 64, R
-up to 8): the ranks the chunked MFMA kernels do not take (3, 5, 6, 7, 8); N 256
-at R 1, 2, 4 runs the chunked kernels in two row passes (its full-size case
-below). fp32 I/O runs the generic chunked kernel,
+registers, rank contractions on MFMA; N, P multiples of 16 up to 256 and 64):
+the ranks the chunked MFMA kernels do not take (5 to 8); R 3 runs the chunked R 4
+kernel with a zero fourth rank, N 256 at R 1 to 4 the chunked kernels in two row
+passes (its full-size case below). fp32 I/O runs the generic chunked kernel,
 decode the generic step. The oracle runs the
 same problem in fp64; bars are the recurrence's own (1e-4 fp32, 2e-2 bf16 I/O,
 max-relative per (batch, head) slice).
@@ -22,14 +22,14 @@ pytestmark = pytest.mark.gpu
 
 PCASES = [
     # b, L, H, G, P, N, R, io, chunk
-    (1, 150, 2, 1, 48, 256, 3, "bf16", 64),   # N 256 (rows split over two waves), P 48, a ragged last block
+    (1, 150, 2, 1, 48, 256, 5, "bf16", 64),   # N 256, P 48, R 5, a ragged last block
     (2, 70, 2, 1, 64, 128, 8, "bf16", 32),    # R 8
     (1, 90, 3, 3, 64, 256, 6, "bf16", 64),    # N 256 and R 6, one B, C per head
-    (2, 41, 4, 2, 64, 128, 3, "bf16", 64),    # R 3 (the MFMA kernels take 1, 2, 4); b*H = 8: XCD order
+    (2, 41, 4, 2, 64, 128, 7, "bf16", 64),    # R 7; b*H = 8
     (1, 33, 2, 1, 32, 64, 5, "bf16", 64),     # P 32 (two waves idle), N 64, R 5
     (1, 17, 2, 1, 48, 208, 7, "bf16", 64),    # N 208 (13 row tiles), P 48, R 7
-    (1, 37, 2, 1, 48, 208, 3, "bf16", 64),    # N 208 with R 3: rows split over two waves, a partial half
-    (3, 1, 2, 1, 32, 256, 3, "bf16", 64),     # one token
+    (1, 37, 2, 1, 48, 208, 3, "bf16", 64),    # N 208 with R 3: the chunked R 4 kernel, rank and rows padded
+    (3, 1, 2, 1, 32, 256, 6, "bf16", 64),     # one token
     (1, 45, 2, 1, 16, 256, 8, "f32", 16),     # fp32: the generic kernel
 ]
 
@@ -47,7 +47,8 @@ def test_prefill_large_state_and_rank(case):
     print(f"prefill large case {case}", flush=True)
     p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=P, dstate=N, rank=R, io_dtype=io,
                             dist="lm", wid=1000 + PCASES.index(case), h0_std=0.1, with_carry=True)
-    assert _path(p, chunk) == (binding.M3_PATH_SCAN if io == "bf16" else binding.M3_PATH_GENERIC)
+    expect = binding.M3_PATH_GENERIC if io != "bf16" else binding.M3_PATH_MFMA if R <= 4 else binding.M3_PATH_SCAN
+    assert _path(p, chunk) == expect
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
     assert_close(y, y_ref, TOL[io], "y")

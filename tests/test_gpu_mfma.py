@@ -38,6 +38,9 @@ CASES = [
     (1, 41, 2, 1, 4, 1, 0.0, True),
     (1, 1, 2, 1, 4, 64, 0.1, True),
     (1, 65, 1, 1, 1, 33, 0.1, False),
+    (1, 130, 2, 1, 3, 64, 0.1, True),   # R 3: the R 4 kernel with a zero fourth rank
+    (2, 97, 3, 3, 3, 16, 0.0, True),
+    (1, 1100, 2, 1, 3, 64, 0.1, True),  # R 3 with sequence segments (look-back, output correction)
 ]
 
 

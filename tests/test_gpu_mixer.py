@@ -36,7 +36,8 @@ CASES = [
     (2, 70, 64, 2, 1, 16, 32, 1, "MFMA"),    # chunked recurrence, rows and columns zero-padded, ragged chunk
     (1, 100, 128, 2, 1, 64, 128, 1, "MFMA"),  # chunked R 1 kernel
     (2, 65, 96, 2, 2, 64, 128, 4, "MFMA"),    # chunked R 4, one B, C group per head
-    (1, 40, 64, 3, 1, 32, 64, 3, "SCAN"),     # rank 3
+    (1, 40, 64, 3, 1, 32, 64, 5, "SCAN"),     # rank 5: the token-walk recurrence
+    (1, 40, 64, 3, 1, 32, 64, 3, "MFMA"),     # rank 3 on the R 4 kernel
 ]
 
 
