@@ -32,10 +32,10 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # KiB -> bytes; scale from a 1 GiB copy), valid only for the kernel source it was
 # taken on (sha256 prefix of the .hip file); see profiles/.
 MEASURED_TRAFFIC = {
-    "prefill1": ("m3_prefill_mfma.hip", "a116eeb2c8b45405", (2.0 * 39159.104 + 73728.0) * 1024),
-    "prefill2": ("m3_prefill_mfma.hip", "a116eeb2c8b45405", (2.0 * 149713.292 + 270336.0) * 1024),
-    "decode1": ("m3_decode.hip", "8a614493d2ac98cc", (2.0 * 133291.799 + 264224.0) * 1024),
-    "decode4": ("m3_decode.hip", "8a614493d2ac98cc", (2.0 * 139030.807 + 270743.416) * 1024),
+    "prefill1": ("m3_prefill_mfma.hip", "feced3c57cb7a94b", (2.0 * 39159.083 + 73728.0) * 1024),
+    "prefill2": ("m3_prefill_mfma.hip", "feced3c57cb7a94b", (2.0 * 149720.042 + 270336.0) * 1024),
+    "decode1": ("m3_decode.hip", "6412f1bfbcc2473e", (2.0 * 133296.984 + 264224.0) * 1024),
+    "decode4": ("m3_decode.hip", "6412f1bfbcc2473e", (2.0 * 139036.840 + 270768.807) * 1024),
 }
 
 
