@@ -270,8 +270,12 @@ size_t m3_prefill_backward_workspace_size(const m3_dims* dims, int32_t R);
  * projections run as hipBLASLt GEMMs (fp32 accumulation); omega, the norm
  * weights, biases and dt_bias may be NULL as for m3_prologue / m3_prefill.
  * The intermediates live in the caller's workspace. A mixer object holds the
- * hipBLASLt handle and the GEMM algorithms chosen per shape: create it once,
- * use it from one thread at a time, destroy it at the end.
+ * hipBLASLt handle, the GEMM algorithms chosen per shape (timed on the first
+ * call of each shape, which synchronises the stream once: capture a graph only
+ * after one eager call of the same sizes) and three side streams: the input
+ * projections of a call with at most 1024 tokens fan out to them (fork and join
+ * events on `stream`, so a captured call captures them too). Create it once,
+ * use it from one thread and one call at a time, destroy it at the end.
  */
 typedef struct m3_mixer m3_mixer;
 typedef struct m3_mixer_weights {
@@ -294,7 +298,8 @@ typedef struct m3_mixer_weights {
     float eps;
 } m3_mixer_weights;
 
-/* Create / destroy a mixer object (host call; creates a hipBLASLt handle on the current device). */
+/* Create / destroy a mixer object (host call; creates a hipBLASLt handle and three
+ * default-priority streams on the current device). */
 m3_status m3_mixer_create(m3_mixer** out);
 void m3_mixer_destroy(m3_mixer* m);
 
