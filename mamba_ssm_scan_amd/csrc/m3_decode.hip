@@ -181,7 +181,7 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// bf16 I/O, N = 128, P = 64, R in {2, 4}: the rank-R contractions on MFMA
+// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4}: the rank-R contractions on MFMA
 // (v_mfma_f32_16x16x16_bf16). One 256-thread workgroup per (b, h); wave w owns
 // state columns 16 w .. 16 w + 15 and all 128 rows. In row tile nt, lane
 // (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column 16 w + l16: two whole
@@ -194,14 +194,14 @@ __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 
 // takes the lane's 4 new state values as its B operand. h' goes in as two bf16
 // terms (hi + lo), which keeps y at fp32 accuracy; the products of bf16 inputs
 // in U and Up are exact. No cross-lane reduction is left.
-template <int R>
+template <int R, int N>
 __global__ void __launch_bounds__(256)
 decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
                    int rd_slot, const bf16_t* __restrict__ x, const float* __restrict__ dt,
                    const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
-    constexpr int N = 128, P = 64, K = 64, CS_ = N + 4;
+    constexpr int P = 64, K = N / 2, CS_ = N + 4, NT = N / 16;  // NT row tiles
     __shared__ __attribute__((aligned(16))) uint16_t sBt[N][4];   // B^T: ranks contiguous, zero past R
     __shared__ __attribute__((aligned(16))) uint16_t sBpt[N][4];  // B_prev^T
     __shared__ __attribute__((aligned(16))) uint16_t sXt[P][4];   // x^T
@@ -219,9 +219,9 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     float* hs = hstate + bh * (N * P);
     const int p = 16 * w + l16;
 
-    float st[8][4];
+    float st[NT][4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) st[nt][e] = hs[(16 * nt + 4 * g4 + e) * P + p];
 
@@ -267,7 +267,7 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     const int rc = l16 < R ? l16 : 0;
     floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const int n0 = 16 * nt;
         const u32x2 ab = *reinterpret_cast<const u32x2*>(&sBt[n0 + l16][0]);
         const u32x2 abp = *reinterpret_cast<const u32x2*>(&sBpt[n0 + l16][0]);
@@ -424,8 +424,16 @@ hipError_t launch_t(const DecodeArgs& a) {
     const T* C = static_cast<const T*>(a.C);
     T* y = static_cast<T*>(a.y);
     if constexpr (std::is_same<T, bf16_t>::value) {
-        if (a.N == 128 && a.P == 64 && (a.R == 2 || a.R == 4)) {
-            auto kern = a.R == 2 ? decode_mfma_kernel<2> : decode_mfma_kernel<4>;
+        if ((a.N == 64 || a.N == 128) && a.P == 64 && a.R >= 2 && a.R <= 4) {
+            // R 3 runs with a zero fourth rank slot (the staging zero-fills ranks past R); at
+            // N 256 the 64 state values per lane spill (358 us against the row kernel's)
+            using K = void (*)(float*, bf16_t*, bf16_t*, int, const bf16_t*, const float*, const float*,
+                               const float*, const float*, const bf16_t*, const bf16_t*, const float*, bf16_t*,
+                               int64_t, int, int);
+            K kern = a.N == 64 ? (a.R == 2 ? decode_mfma_kernel<2, 64> : a.R == 3 ? decode_mfma_kernel<3, 64>
+                                                                         : decode_mfma_kernel<4, 64>)
+                               : (a.R == 2 ? decode_mfma_kernel<2, 128> : a.R == 3 ? decode_mfma_kernel<3, 128>
+                                                                          : decode_mfma_kernel<4, 128>);
             hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A, a.omega,
                                a.lam, B, C, a.D, y, a.b, a.H, a.G);
             return hipGetLastError();
