@@ -181,7 +181,7 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4}: the rank-R contractions on MFMA
+// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4, 8}: the rank-R contractions on MFMA
 // (v_mfma_f32_16x16x16_bf16). One 256-thread workgroup per (b, h); wave w owns
 // state columns 16 w .. 16 w + 15 and all 128 rows. In row tile nt, lane
 // (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column 16 w + l16: two whole
@@ -202,10 +202,12 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
     constexpr int P = 64, K = N / 2, CS_ = N + 4, NT = N / 16;  // NT row tiles
-    __shared__ __attribute__((aligned(16))) uint16_t sBt[N][4];   // B^T: ranks contiguous, zero past R
-    __shared__ __attribute__((aligned(16))) uint16_t sBpt[N][4];  // B_prev^T
-    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][4];   // x^T
-    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][4];  // x_prev^T
+    // rank slots: 4, or 8 at R above 4 (k = 4 g4 + 0..3 of the K = 16 MFMA, lanes g4 < RS / 4)
+    constexpr int RS = R <= 4 ? 4 : 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sBt[N][RS];   // B^T: ranks contiguous, zero past R
+    __shared__ __attribute__((aligned(16))) uint16_t sBpt[N][RS];  // B_prev^T
+    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][RS];   // x^T
+    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][RS];  // x_prev^T
     __shared__ __attribute__((aligned(16))) uint16_t sC[R][CS_];  // C rows (padded: no bank conflicts)
     __shared__ __attribute__((aligned(16))) float sCS[K][2];      // alpha * (cos, sin) of pair k
 
@@ -230,7 +232,7 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + (int64_t(rd_slot) * nb * G + bg) * (R * N);
     const uint16_t* xt = reinterpret_cast<const uint16_t*>(x) + bh * (R * P);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + (int64_t(rd_slot) * nb * H + bh) * (R * P);
-    for (int e = tid; e < 4 * (N / 2); e += 256) {  // rank r, pair of rows (2 j, 2 j + 1): one 32-bit load
+    for (int e = tid; e < RS * (N / 2); e += 256) {  // rank r, pair of rows (2 j, 2 j + 1): one 32-bit load
         const int r = e / (N / 2), j = e % (N / 2);
         const unsigned vb = r < R ? reinterpret_cast<const unsigned*>(Bt + r * N)[j] : 0u;
         const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(Bp + r * N)[j] : 0u;
@@ -239,7 +241,7 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
         sBpt[2 * j][r] = uint16_t(vp);
         sBpt[2 * j + 1][r] = uint16_t(vp >> 16);
     }
-    for (int e = tid; e < 4 * (P / 2); e += 256) {  // rank r, pair of columns: one 32-bit load
+    for (int e = tid; e < RS * (P / 2); e += 256) {  // rank r, pair of columns: one 32-bit load
         const int r = e / (P / 2), j = e % (P / 2);
         const unsigned vx = r < R ? reinterpret_cast<const unsigned*>(xt + r * P)[j] : 0u;
         const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(xp + r * P)[j] : 0u;
@@ -262,17 +264,19 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     __syncthreads();
 
     const u32x2 zero = {0u, 0u};
-    const u32x2 xo = g4 == 0 ? *reinterpret_cast<const u32x2*>(&sXt[p][0]) : zero;
-    const u32x2 xpo = g4 == 0 ? *reinterpret_cast<const u32x2*>(&sXpt[p][0]) : zero;
+    const bool kin = g4 < RS / 4;  // this lane's k group holds ranks 4 g4 .. 4 g4 + 3
+    const int ko = RS == 4 ? 0 : 4 * g4;
+    const u32x2 xo = kin ? *reinterpret_cast<const u32x2*>(&sXt[p][ko]) : zero;
+    const u32x2 xpo = kin ? *reinterpret_cast<const u32x2*>(&sXpt[p][ko]) : zero;
     const int rc = l16 < R ? l16 : 0;
     floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int nt = 0; nt < NT; ++nt) {
         const int n0 = 16 * nt;
-        const u32x2 ab = *reinterpret_cast<const u32x2*>(&sBt[n0 + l16][0]);
-        const u32x2 abp = *reinterpret_cast<const u32x2*>(&sBpt[n0 + l16][0]);
-        const floatx4 U = mfma_k16(g4 == 0 ? ab : zero, xo, floatx4{0.f, 0.f, 0.f, 0.f});
-        const floatx4 Up = mfma_k16(g4 == 0 ? abp : zero, xpo, floatx4{0.f, 0.f, 0.f, 0.f});
+        const u32x2 ab = *reinterpret_cast<const u32x2*>(&sBt[n0 + l16][ko]);
+        const u32x2 abp = *reinterpret_cast<const u32x2*>(&sBpt[n0 + l16][ko]);
+        const floatx4 U = mfma_k16(kin ? ab : zero, xo, floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 Up = mfma_k16(kin ? abp : zero, xpo, floatx4{0.f, 0.f, 0.f, 0.f});
         // pairs 8 nt + 2 g4 (rows e = 0, 1) and 8 nt + 2 g4 + 1 (rows e = 2, 3)
         const floatx4 cs = *reinterpret_cast<const floatx4*>(&sCS[8 * nt + 2 * g4][0]);
         float nv[4];
@@ -296,12 +300,23 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
         yacc = mfma_k16(ac, lo, yacc);
     }
     // yacc lane (g4 = 0) holds y[r = e][p]
-    if (g4 == 0) {
+    if constexpr (RS == 4) {  // yacc lane (g4 = 0) holds y[r = e][p]
+        if (g4 == 0) {
+            const float Dh = D[h];
+#pragma unroll
+            for (int e = 0; e < R; ++e) {
+                const float xv = __uint_as_float(unsigned(sXt[p][e]) << 16);
+                Io<bf16_t>::store(y, bh * (R * P) + e * P + p, yacc[e] + Dh * xv);
+            }
+        }
+    } else if (4 * g4 < R) {  // lane (l16, g4) holds y[r = 4 g4 + e][p]
         const float Dh = D[h];
 #pragma unroll
-        for (int e = 0; e < R; ++e) {
-            const float xv = __uint_as_float(unsigned(sXt[p][e]) << 16);
-            Io<bf16_t>::store(y, bh * (R * P) + e * P + p, yacc[e] + Dh * xv);
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            if (r >= R) continue;
+            const float xv = __uint_as_float(unsigned(sXt[p][r]) << 16);
+            Io<bf16_t>::store(y, bh * (R * P) + r * P + p, yacc[e] + Dh * xv);
         }
     }
 
@@ -424,16 +439,20 @@ hipError_t launch_t(const DecodeArgs& a) {
     const T* C = static_cast<const T*>(a.C);
     T* y = static_cast<T*>(a.y);
     if constexpr (std::is_same<T, bf16_t>::value) {
-        if ((a.N == 64 || a.N == 128) && a.P == 64 && a.R >= 2 && a.R <= 4) {
+        if ((a.N == 64 || a.N == 128) && a.P == 64 && ((a.R >= 2 && a.R <= 4) || a.R == 8)) {
             // R 3 runs with a zero fourth rank slot (the staging zero-fills ranks past R); at
             // N 256 the 64 state values per lane spill (358 us against the row kernel's)
             using K = void (*)(float*, bf16_t*, bf16_t*, int, const bf16_t*, const float*, const float*,
                                const float*, const float*, const bf16_t*, const bf16_t*, const float*, bf16_t*,
                                int64_t, int, int);
-            K kern = a.N == 64 ? (a.R == 2 ? decode_mfma_kernel<2, 64> : a.R == 3 ? decode_mfma_kernel<3, 64>
-                                                                         : decode_mfma_kernel<4, 64>)
-                               : (a.R == 2 ? decode_mfma_kernel<2, 128> : a.R == 3 ? decode_mfma_kernel<3, 128>
-                                                                          : decode_mfma_kernel<4, 128>);
+            K kern = a.N == 64 ? (a.R == 2   ? decode_mfma_kernel<2, 64>
+                                  : a.R == 3 ? decode_mfma_kernel<3, 64>
+                                  : a.R == 4 ? decode_mfma_kernel<4, 64>
+                                             : decode_mfma_kernel<8, 64>)
+                               : (a.R == 2   ? decode_mfma_kernel<2, 128>
+                                  : a.R == 3 ? decode_mfma_kernel<3, 128>
+                                  : a.R == 4 ? decode_mfma_kernel<4, 128>
+                                             : decode_mfma_kernel<8, 128>);
             hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A, a.omega,
                                a.lam, B, C, a.D, y, a.b, a.H, a.G);
             return hipGetLastError();

@@ -101,7 +101,8 @@ def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
 DCASES = [
     # b, L, H, G, P, N, R, io
     (2, 8, 2, 1, 64, 256, 1, "bf16"),   # the float4 row kernel at N 256
-    (2, 8, 2, 1, 64, 128, 8, "bf16"),   # the float4 row kernel at R 8
+    (2, 8, 2, 1, 64, 128, 8, "bf16"),   # the MFMA decode kernel at R 8 (two k groups of ranks)
+    (1, 6, 3, 1, 64, 64, 8, "bf16"),
     (1, 6, 3, 3, 64, 256, 6, "f32"),
     # the float4 row kernel at the other (N, P) it is built for (bf16 I/O, R 1, 2, 4)
     (2, 6, 2, 1, 32, 64, 1, "bf16"),
