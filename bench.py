@@ -34,8 +34,8 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 MEASURED_TRAFFIC = {
     "prefill1": ("m3_prefill_mfma.hip", "feced3c57cb7a94b", (2.0 * 39159.083 + 73728.0) * 1024),
     "prefill2": ("m3_prefill_mfma.hip", "feced3c57cb7a94b", (2.0 * 149720.042 + 270336.0) * 1024),
-    "decode1": ("m3_decode.hip", "79971b8f87ff83f6", (2.0 * 133293.093 + 264224.000) * 1024),
-    "decode4": ("m3_decode.hip", "79971b8f87ff83f6", (2.0 * 139041.734 + 270762.699) * 1024),
+    "decode1": ("m3_decode.hip", "2455ff93ed6fcc8d", (2.0 * 133301.623 + 264224.000) * 1024),
+    "decode4": ("m3_decode.hip", "2455ff93ed6fcc8d", (2.0 * 139049.603 + 270763.248) * 1024),
 }
 
 
