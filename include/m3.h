@@ -132,6 +132,32 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
 /* Workspace bytes m3_prefill needs for these sizes (0 on invalid sizes). Host only. */
 size_t m3_prefill_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype);
 
+/*
+ * m3_prefill_noalloc -- m3_prefill for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * it): the same computation, arguments and results, with the workspace taken
+ * from a fixed scratch array that the library holds in device memory instead of
+ * a caller buffer. Nothing is allocated or freed by this call.
+ *
+ * The scratch is M3_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the first
+ * call on that GPU until the process ends. Sizes whose m3_prefill_workspace_size()
+ * exceeds it are rejected with M3_EWORKSPACE before anything is launched (at
+ * the workloads' sizes the segmented long prefill of b 1, H 64, L 32768, R 4
+ * needs 16 MiB; N above 128 needs b*L*H*R*P*4 bytes). Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents; what must start
+ * at zero is cleared by a kernel on `stream`. Calls that overlap in time on one
+ * GPU (other streams, other threads) race on the scratch and must not be issued.
+ */
+#define M3_NOALLOC_SCRATCH_BYTES (32u << 20)
+m3_status m3_prefill_noalloc(const void* x, const float* dt, const float* A, const float* omega,
+                             const float* lambda, const void* B, const void* C, const float* D,
+                             int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
+                             const m3_dims* dims, m3_dtype io_dtype,
+                             const void* carry_B, const void* carry_x, void* stream);
+
+/* Bytes of m3_prefill_noalloc's fixed scratch (M3_NOALLOC_SCRATCH_BYTES). Host only. */
+size_t m3_noalloc_scratch_bytes(void);
+
 /* Fill *plan with the integers m3_prefill will use. Host only, no HIP call. */
 m3_status m3_prefill_plan(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype,
                           m3_plan* plan);

@@ -25,7 +25,8 @@ STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EAL
 EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_decode_carry_bytes",
            "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_prefill_backward",
            "m3_prefill_backward_workspace_size", "m3_mixer_create", "m3_mixer_destroy", "m3_mixer_workspace_size",
-           "m3_mixer_prefill", "m3_mixer_decode_step", "m3_status_string", "m3_last_error", "m3_abi_version"]
+           "m3_mixer_prefill", "m3_mixer_decode_step", "m3_status_string", "m3_last_error", "m3_abi_version",
+           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes"]
 
 
 class M3Dims(ctypes.Structure):
@@ -73,6 +74,10 @@ def load(path: str = LIB_PATH):
     dims_p = ctypes.POINTER(M3Dims)
     lib.m3_prefill.argtypes = [vp] * 8 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.m3_prefill.restype = ctypes.c_int
+    lib.m3_prefill_noalloc.argtypes = [vp] * 8 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp]
+    lib.m3_prefill_noalloc.restype = ctypes.c_int
+    lib.m3_noalloc_scratch_bytes.argtypes = []
+    lib.m3_noalloc_scratch_bytes.restype = sz
     lib.m3_prefill_workspace_size.argtypes = [dims_p, i32, i32, ctypes.c_int]
     lib.m3_prefill_workspace_size.restype = sz
     lib.m3_prefill_plan.argtypes = [dims_p, i32, i32, ctypes.c_int, ctypes.POINTER(M3Plan)]

@@ -132,6 +132,23 @@ def test_prefill_argument_errors(lib):
     assert st == 4 and "workspace" in msg
 
 
+def test_noalloc_rejects_before_any_launch(lib):
+    """m3_prefill_noalloc: same argument checks as m3_prefill; sizes whose workspace
+    exceeds the fixed scratch are refused (M3_EWORKSPACE) before any HIP call."""
+    assert lib.m3_noalloc_scratch_bytes() == 32 << 20
+    def call(d, R=1, chunk=64, io=bd.M3_BF16, x=FAKE):
+        return lib.m3_prefill_noalloc(x, FAKE + (1 << 30), FAKE + (2 << 30), None, None, FAKE + (3 << 30),
+                                      FAKE + (4 << 30), FAKE + (5 << 30), R, chunk, None, FAKE + (6 << 30), None,
+                                      ctypes.byref(d), io, None, None, None)
+    assert call(_dims(N=15)) == 1
+    assert call(_dims(), x=None) == 1
+    # N 256 takes two row passes whose fp32 partial outputs need b*L*H*R*P*4 bytes: 48 MiB here
+    d = bd.dims(1, 8192, 24, 1, 64, 256)
+    assert lib.m3_prefill_workspace_size(ctypes.byref(d), 1, 64, bd.M3_BF16) > (32 << 20)
+    assert call(d) == 7
+    assert "scratch" in lib.m3_last_error().decode()
+
+
 def test_prefill_empty_batch_is_a_no_op(lib):
     # b = 0: valid, nothing to launch
     assert _call(lib, _dims(b=0))[0] == 0
