@@ -141,6 +141,9 @@ hipError_t launch_gate(void* y, const void* z, int64_t n, hipStream_t s);
 // set the thread's error detail (m3_last_error) and return s
 m3_status set_error(m3_status s, const char* fmt, ...);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
+// the wave-specialised R 4 kernel for N 128, P 64 (m3_prefill_ws4.hip)
+bool ws4_supported(const PrefillArgs& a);
+hipError_t launch_prefill_ws4(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prologue(const PrologueArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);

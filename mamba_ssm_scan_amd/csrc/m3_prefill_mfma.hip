@@ -40,110 +40,10 @@
 #include <type_traits>
 #include "m3_device.h"
 #include "m3_internal.h"
+#include "m3_mfma_common.h"
 
 namespace m3 {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int N = 128;     // state rows
-constexpr int P = 64;      // head dim
-constexpr int K = 64;      // rotation pairs
-constexpr int NS = N + 8;  // LDS row stride (bf16 elements) of B~, C~ and g^T
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kInv2Pi = 0.15915494309189535f;
-constexpr double kInv2PiD = 0.15915494309189533577;
-
-__device__ __forceinline__ floatx4 mfma32(u32x4 a, u32x4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(u32x2 a, u32x2 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b),
-                                                     c, 0, 0, 0);
-}
-// two floats -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32)
-__device__ __forceinline__ unsigned pack2(float lo, float hi) {
-    bf16x2 v;
-    v[0] = (__bf16)lo;
-    v[1] = (__bf16)hi;
-    return __builtin_bit_cast(unsigned, v);
-}
-__device__ __forceinline__ float lo16(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-// (cos, sin) of 2 pi * rev
-struct CS {
-    float c, s;
-};
-__device__ __forceinline__ CS cs_rev(float om_rev, float T) {
-    const float r = __builtin_amdgcn_fractf(om_rev * T);
-    return CS{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
-}
-// one packed pair (b0, b1) turned by -Phi: (c b0 + s b1, c b1 - s b0)
-__device__ __forceinline__ unsigned rot_pair(unsigned w, CS t) {
-    const float b0 = lo16(w), b1 = hi16(w);
-    return pack2(t.c * b0 + t.s * b1, t.c * b1 - t.s * b0);
-}
-// Transposing LDS load (ds_read_b64_tr_b16): in each group of 16 lanes, lane t
-// gives the address of 4 consecutive 16-bit values of row t / 4 (columns
-// 4 (t % 4) ..); lane j receives column j of those 4 rows. From a row-major
-// [k][m] tile this yields the MFMA operand layout "lane = m, 4 consecutive k".
-typedef short shortx4_tr __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 load_tr(const uint16_t* p) {
-    const shortx4_tr v =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_tr*)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
-// a packed bf16 pair times (wl, wh), repacked
-__device__ __forceinline__ unsigned scale2(unsigned w, float wl, float wh) { return pack2(lo16(w) * wl, hi16(w) * wh); }
-// broadcast lane j of every DPP quad
-template <int J>
-__device__ __forceinline__ float quad_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float lane_read(float v, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-// Inclusive prefix sum over the 64 lanes of a wavefront, kept off the LDS
-// crossbar (a ds_bpermute shuffle would queue behind the MFMA operand reads and
-// serialise every step): DPP right shifts inside each 16-lane row, then the
-// row totals carried across rows through scalar registers.
-__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));
-    const float r0 = lane_read(v, 15), r1 = lane_read(v, 31), r2 = lane_read(v, 47);
-    const int row = lane >> 4;
-    return v + ((row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f));
-}
-// value of lane 16 * (lane / 16) + 15 (the last lane of each row)
-__device__ __forceinline__ float row_last(float v, int lane) {
-    const float r0 = lane_read(v, 15), r1 = lane_read(v, 31), r2 = lane_read(v, 47), r3 = lane_read(v, 63);
-    const int row = lane >> 4;
-    return row == 0 ? r0 : row == 1 ? r1 : row == 2 ? r2 : r3;
-}
-// value of the last lane of each group of 16 / R lanes (lane = token: the last
-// token whose rows fall in the same 16-row tile)
-template <int LR>
-__device__ __forceinline__ float tile_last(float v, int lane) {
-    if constexpr (LR == 2) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false));
-    } else if constexpr (LR == 1) {
-        const int q = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false);  // lane 4k+3
-        const int u = __builtin_amdgcn_update_dpp(q, q, 0x104, 0xf, 0xf, false);  // row_shl:4 -> lane 8k+7
-        return __builtin_bit_cast(float, (lane & 4) ? q : u);
-    } else {
-        return row_last(v, lane);
-    }
-}
 
 template <int R_, int NW_>
 struct Shape {
@@ -171,10 +71,6 @@ __device__ __forceinline__ int strip_of(int wave, int si) {
     return si * NW + ((si & 1) ? (NW - 1 - wave) : wave);
 }
 
-// Wait for this wave's LDS traffic, then meet the other waves. Unlike
-// __syncthreads() this does not wait for outstanding global loads, so the next
-// chunk's prefetch stays in flight across it.
-__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Global operands of one chunk, held in registers until they are staged.
 template <class S>
@@ -183,44 +79,7 @@ struct ChunkRegs {
     u32x4 b[S::UPT][S::R];                 // B rows (token, rank) of this thread's units
     u32x4 c[S::C_LDS ? S::UPT : 1][S::R];  // C rows, when staged in LDS
     u32x4 x0[S::XPT], x1[S::XPT];
-    u32x4 cs[S::C_LDS ? 1 : 4];            // C rows of the wave's first strip, when not in LDS
 };
-
-// Row addressing inside one chunk: token i, rank r of B/C sits at (i*G*R + r)*N
-// elements past the chunk's first row, of x/y at (i*H*R + r)*P. Tokens past
-// the chunk's end are clamped to its last token, so every load is
-// unconditional and finite; such rows never reach a result: their mask
-// entries and state weights are zero (their dt is taken as 0) and their
-// outputs are not stored.
-struct ChunkBase {
-    const uint16_t* B;
-    const uint16_t* C;
-    const uint16_t* x;
-    int nq;
-    int nin;   // state rows this pass takes from the caller's B/C rows (<= N); rows nin..N-1 are zero
-    int nrow;  // length of the caller's B/C rows (the caller's N)
-    int pin;   // columns this pass takes from the caller's x rows (<= P); columns pin..P-1 are zero
-    int pcol;  // length of the caller's x rows (the caller's P)
-    int rin;   // the caller's rank (<= the kernel's R); ranks rin..R-1 are zero rows
-};
-
-// One pass of the chunked kernels over rows n_off .. n_off + nin - 1 of the
-// caller's N (= nrow) and columns p_off .. p_off + pin - 1 of its P (= pcol).
-// The state rows evolve independently and so do its columns: a column block
-// is a problem of its own, a row block contributes a share of y that the
-// passes sum in fp32 in ypart ([b][L][H][R][P]). ym: 0 the only row pass (y
-// written in bf16), 1 first (writes ypart, with D x), 3 middle (adds to
-// ypart), 2 last (adds ypart, writes y in bf16).
-struct PassArgs {
-    int nin, nrow, n_off, pin, pcol, p_off, ym;
-    int rin;  // the caller's rank: R 3 runs on the R 4 kernel with a zero fourth rank
-    float* ypart;
-};
-
-__device__ __forceinline__ u32x4 load_tok(const uint16_t* base, int i, int nq, int tok_stride, int off) {
-    const int ic = i < nq ? i : nq - 1;
-    return *reinterpret_cast<const u32x4*>(base + (ic * tok_stride + off));
-}
 
 template <class S>
 __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb, const float* __restrict__ dt,
@@ -276,46 +135,6 @@ __device__ __forceinline__ void load_strip_c(u32x4 (&c)[4], const ChunkBase& cb,
         c[ks] = (n0 < cb.nin && r < cb.rin) ? load_tok(cb.C, i, cb.nq, G * cb.rin * cb.nrow, r * cb.nrow + n0)
                                             : u32x4{0u, 0u, 0u, 0u};
     }
-}
-
-// M_ij (decay x width-2 convolution mask) for row token tj and column token ti.
-// Branch-free: the loads are always in range (tj < 64) and the causal cut is a
-// select, so a wavefront whose lanes straddle the diagonal does not diverge.
-__device__ __forceinline__ float mask_coef(int tj, int ti, float S2i, const float* w) {
-    const float s2j = w[tj], gam = w[64 + tj], dln = w[128 + tj];
-    const float coef = __builtin_amdgcn_exp2f(S2i - s2j) * (gam + (tj < ti ? dln : 0.f));
-    return tj > ti ? 0.f : coef;
-}
-
-// Sequence segments (decoupled look-back). Workspace layout, per (b, h, segment)
-// index bs = (b*H + h) * nseg + seg: ctrl[0] ticket counter, ctrl[1] error flag
-// (a look-back wait that ran out of patience), ctrl[2 + bs] state flag
-// (1 = local end state published, 2 = inclusive end state published);
-// agg/incl [bs][N][P] fp32; tr[bs] the segment's total step (sum of dt).
-struct SegArgs {
-    int nseg;
-    int64_t cps;  // chunks per segment
-    unsigned* ctrl;
-    float* agg;
-    float* incl;
-    double* tr;
-};
-constexpr long kSpinLimit = 1L << 24;
-
-// The state map of a stretch with total step T: pair k turned by omega_k T and
-// scaled by e^{A T}; om_rev = omega_k / 2 pi of the lane's two pairs.
-__device__ __forceinline__ floatx4 transfer(floatx4 v, float A2, const float* om_rev, double T) {
-    const float dec = __builtin_amdgcn_exp2f(float(double(A2) * T));
-    floatx4 o;
-#pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-        const double rv = double(om_rev[hp]) * T;
-        const float r = float(rv - floor(rv));
-        const float c = __builtin_amdgcn_cosf(r) * dec, sn = __builtin_amdgcn_sinf(r) * dec;
-        o[2 * hp] = c * v[2 * hp] - sn * v[2 * hp + 1];
-        o[2 * hp + 1] = sn * v[2 * hp] + c * v[2 * hp + 1];
-    }
-    return o;
 }
 
 // GEN: the pass described by pa (other sizes, row and column passes); without
@@ -422,7 +241,6 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     {
         const ChunkBase cb = chunk_base(c_begin);
         load_chunk<S>(pre, cb, dt + h, lam ? lam + h : nullptr, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
-        if constexpr (!S::C_LDS) load_strip_c<S>(pre.cs, cb, strip_of<NW>(wave, 0) / S::PTG, G, lane);
     }
 
     // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
@@ -522,12 +340,6 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                     (pre.x0[m][j] >> 16) | (pre.x1[m][j] & 0xffff0000u);
             }
         }
-        u32x4 craw[4];
-        if constexpr (!S::C_LDS) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) craw[ks] = pre.cs[ks];
-        }
-
         // ---- 3. prefetch the next chunk's scalars, B, C and X (in flight through the compute below)
         const bool more = c + 1 < c_end;
         const ChunkBase cbn = chunk_base(more ? c + 1 : c);
@@ -535,196 +347,25 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         segT += double(Te);
         lds_barrier();
 
-        // ---- 4. outputs: work item = (16-row strip, group of PTW p tiles), y^T accumulated
-        //         (an accumulator lane holds y[rho_i][p..p+3] of one row: 8-byte stores)
-        // The g^T operands of the inter-chunk part are the same for all of a
-        // wave's strips (its p tiles do not change): loaded once per chunk.
-        static_assert(S::PTG == 1, "one p-tile group per wave");
-        u32x4 gop[S::PTW][4];
+        // This wave's output strips (16 rows each), ascending. The snake order deals
+        // the triangle's score work evenly (strip s needs s + 1 score tiles), and
+        // with an even wave count two strips that follow each other never share
+        // a diagonal pair (when they differ by one row tile the first is odd).
+        static_assert(S::PTG == 1 && S::PTW == 4, "a wave takes whole strips");
+        static_assert(NW % 2 == 0, "snake order with an even wave count");
+        int strip[SPW];
 #pragma unroll
-        for (int q = 0; q < S::PTW; ++q)
+        for (int k = 0; k < SPW; ++k) strip[k] = strip_of<NW>(wave, k);
+
+        // ---- 4. raw C rows of every strip of the wave (R = 4: not staged in LDS);
+        //         their latency is covered by the state update below
+        u32x4 craw[S::C_LDS ? 1 : SPW][4];
+        if constexpr (!S::C_LDS) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                gop[q][ks] = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
-#pragma unroll 1
-        for (int si = 0; si < SPW; ++si) {
-            const int item = strip_of<NW>(wave, si);
-            const int s = item / S::PTG, pt0 = (item % S::PTG) * S::PTW;
-            u32x4 cr[4];  // C~ rows of the strip, B-operand layout (col rho_i = 16 s + l16, k = n)
-            if constexpr (S::C_LDS) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    cr[ks] = *reinterpret_cast<const u32x4*>(sCt + (16 * s + l16) * NS + 32 * ks + 8 * g4);
-            } else {
-                // the 4 lanes of a DPP quad hold the 4 ranks of one token: each
-                // evaluates one of the quad's 4 angles and shares it
-                const float Ti = wsc[320 + ((16 * s + l16) >> LR)];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const CS own = cs_rev(omC[ks], Ti);
-                    const CS t0{quad_bcast<0>(own.c), quad_bcast<0>(own.s)};
-                    const CS t1{quad_bcast<1>(own.c), quad_bcast<1>(own.s)};
-                    const CS t2{quad_bcast<2>(own.c), quad_bcast<2>(own.s)};
-                    const CS t3{quad_bcast<3>(own.c), quad_bcast<3>(own.s)};
-                    const u32x4 v = craw[ks];
-                    cr[ks] = u32x4{rot_pair(v[0], t0), rot_pair(v[1], t1), rot_pair(v[2], t2), rot_pair(v[3], t3)};
-                }
-                if (si + 1 < SPW) load_strip_c<S>(craw, cb, strip_of<NW>(wave, si + 1) / S::PTG, G, lane);
-            }
-            const int ti = int((16u * s + l16) >> LR);  // token of this lane's column rho_i
-            const float S2i = wsc[ti];
-            // inter-chunk part: y^T[p][rho_i] = e^{S_i} sum_n g^T[p][n] C~[rho_i][n]
-            // (the p tiles' accumulation chains interleaved)
-            floatx4 acc[S::PTW];
-#pragma unroll
-            for (int q = 0; q < S::PTW; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int q = 0; q < S::PTW; ++q) acc[q] = mfma32(gop[q][ks], cr[ks], acc[q]);
-#pragma unroll
-            for (int q = 0; q < S::PTW; ++q) acc[q] *= wsc[192 + ti];
-            // M o scores for row tile jt. Below the diagonal tile (jt < s: every
-            // row token precedes every column token) the decay splits at the
-            // tile's last token r: e^{S_i-S_j} = e^{S_i-S_r} e^{S_r-S_j}, both
-            // factors <= 1, the second staged per token with the width-2
-            // weight, so one exp per lane and tile. The diagonal tile takes the
-            // full mask, plus D on rho_j = rho_i (the skip term D x rides along
-            // in the same contraction).
-            const int rho_i = 16 * s + l16;
-            auto read_below = [&](int jt, float& sr, float (&tw)[4]) {
-                const unsigned rj = 16u * jt + 4u * g4;
-                sr = wsc[(16 * jt + 15) >> LR];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tw[e] = wsc[384 + ((rj + e) >> LR)];
-            };
-            auto mask_below = [&](const floatx4& t, float sr, const float (&tw)[4], float* m) {
-                const float a = __builtin_amdgcn_exp2f(S2i - sr);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) m[e] = t[e] * (tw[e] * a);
-            };
-            auto mask_diag = [&](const floatx4& t, int jt, float* m) {
-                const unsigned rj = 16u * jt + 4u * g4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    m[e] = t[e] * mask_coef(int((rj + e) >> LR), ti, S2i, wsc) + (int(rj + e) == rho_i ? Dh : 0.f);
-            };
-            // Score tiles go in pairs (jt, jt + 1): two 16x16 tiles make one K = 32
-            // operand of the y^T contraction. Software pipeline: the MFMAs of pair
-            // jt + 2 are issued before pair jt is masked, and the B~ operands of
-            // pair jt + 4 are loaded meanwhile. The pairs wholly below the
-            // diagonal tile run a branch-free body that issues its LDS reads for
-            // the mask and X^T before that prefetch (LDS loads complete in order,
-            // so waiting for a later load would also wait for the prefetch); the
-            // pair holding the diagonal tile comes last. Operand rows past the
-            // chunk (the prefetch beyond the strip, the tile after an even
-            // diagonal tile) are clamped to valid rows; their products are never
-            // used or are masked to zero.
-            auto load_pair = [&](int jt, u32x4* a0, u32x4* a1) {
-                const int r0 = 16 * jt + l16 < QRP ? 16 * jt + l16 : QRP - 1;
-                const int r1 = r0 + 16 < QRP ? r0 + 16 : QRP - 1;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    a0[ks] = *reinterpret_cast<const u32x4*>(sBt + r0 * NS + 32 * ks + 8 * g4);
-                    a1[ks] = *reinterpret_cast<const u32x4*>(sBt + r1 * NS + 32 * ks + 8 * g4);
-                }
-            };
-            auto score_pair = [&](const u32x4* a0, const u32x4* a1, floatx4& t0, floatx4& t1) {
-                t0 = floatx4{0.f, 0.f, 0.f, 0.f};
-                t1 = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    t0 = mfma32(a0[ks], cr[ks], t0);
-                    t1 = mfma32(a1[ks], cr[ks], t1);
-                }
-            };
-            // X^T operands of pair jt: columns 16 jt .. 16 jt + 31 (always inside the chunk)
-            auto load_x = [&](int jt, u32x2* xa, u32x2* xb) {
-#pragma unroll
-                for (int q = 0; q < S::PTW; ++q) {
-                    const uint16_t* xr = sXT + (16 * (pt0 + q) + l16) * XS + 16 * jt + 4 * g4;
-                    xa[q] = *reinterpret_cast<const u32x2*>(xr);
-                    xb[q] = *reinterpret_cast<const u32x2*>(xr + 16);
-                }
-            };
-            // y^T[p][rho_i] += sum_{rho_j} X^T[p][rho_j] (M o scores^T)[rho_j][rho_i]
-            auto y_pair = [&](const u32x2* xa, const u32x2* xb, const float* m0, const float* m1) {
-                const u32x4 pb = {pack2(m0[0], m0[1]), pack2(m0[2], m0[3]), pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
-#pragma unroll
-                for (int q = 0; q < S::PTW; ++q)
-                    acc[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, acc[q]);
-            };
-            u32x4 pa0[4], pa1[4];
-            load_pair(0, pa0, pa1);
-            floatx4 c0t, c1t;
-            score_pair(pa0, pa1, c0t, c1t);
-            if (2 <= s) load_pair(2, pa0, pa1);
-            int jt = 0;
-#pragma unroll 1
-            for (; jt + 1 < s; jt += 2) {
-                // The phases are fenced off from the scheduler so the loads keep
-                // this order: mask scalars, X^T, prefetch. The memory clobber
-                // after the prefetch also keeps the compiler from folding the
-                // loop-carried operands into loads at their use in the next
-                // iteration, which would undo the pipeline.
-                float sr0, sr1, tw0[4], tw1[4];
-                read_below(jt, sr0, tw0);
-                read_below(jt + 1, sr1, tw1);
-                __builtin_amdgcn_sched_barrier(0);
-                u32x2 xa[S::PTW], xb[S::PTW];
-                load_x(jt, xa, xb);
-                floatx4 n0t, n1t;
-                score_pair(pa0, pa1, n0t, n1t);  // pair jt + 2 <= s
-                __builtin_amdgcn_sched_barrier(0);
-                load_pair(jt + 4, pa0, pa1);
-                __asm__ volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                float m0[4], m1[4];
-                mask_below(c0t, sr0, tw0, m0);
-                mask_below(c1t, sr1, tw1, m1);
-                y_pair(xa, xb, m0, m1);
-                c0t = n0t;
-                c1t = n1t;
-            }
-            {  // the pair holding the diagonal tile: jt = s & ~1
-                u32x2 xa[S::PTW], xb[S::PTW];
-                load_x(jt, xa, xb);
-                float m0[4], m1[4];
-                if (s & 1) {
-                    float sr0, tw0[4];
-                    read_below(jt, sr0, tw0);
-                    mask_below(c0t, sr0, tw0, m0);
-                    mask_diag(c1t, jt + 1, m1);
-                } else {
-                    mask_diag(c0t, jt, m0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) m1[e] = 0.f;
-                }
-                y_pair(xa, xb, m0, m1);
-            }
-            // epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
-            if ((rho_i >> LR) < nq && (rho_i & (R - 1)) < Rin) {
-                const int i = rho_i >> LR, r = rho_i & (R - 1);
-                const int64_t yo =
-                    ((b * L + c * Q) * H + h) * int64_t(Rin * Pcol) + int64_t(i * H * Rin + r) * Pcol + p_off;
-#pragma unroll
-                for (int q = 0; q < S::PTW; ++q) {
-                    const int p = 16 * (pt0 + q) + 4 * g4;
-                    if (GP && p >= Pin) continue;  // Pin is a multiple of 8
-                    floatx4 v = acc[q];
-                    if (ym >= 2) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
-                    if (ym == 1 || ym == 3)
-                        *reinterpret_cast<floatx4*>(ypart + yo + p) = v;
-                    else
-                        *reinterpret_cast<u32x2*>(y + yo + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
-                }
-            }
+            for (int k = 0; k < SPW; ++k) load_strip_c<S>(craw[k], cb, strip[k], G, lane);
         }
 
         // ---- 5. state passed to the next chunk (written to the other g^T buffer)
-        if constexpr (!S::C_LDS) {
-            if (more) load_strip_c<S>(pre.cs, cbn, strip_of<NW>(wave, 0) / S::PTG, G, lane);
-        }
         const int te = nq - 1;
         const float decE = wsc[192 + te];
 #pragma unroll
@@ -768,6 +409,211 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                 const int p = 16 * pt + l16;
                 *reinterpret_cast<u32x2*>(gTn + p * NS + 16 * nt + 4 * g4) =
                     u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
+            }
+        }
+
+        // ---- 6. C~ rows of the strips in the B-operand layout (col rho_i = 16 s + l16, k = n)
+        u32x4 cr[SPW][4];
+        float S2i[SPW], eSi[SPW];
+        int tii[SPW];
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int s = strip[k];
+            tii[k] = int((16u * s + l16) >> LR);
+            S2i[k] = wsc[tii[k]];
+            eSi[k] = wsc[192 + tii[k]];
+            if constexpr (S::C_LDS) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    cr[k][ks] = *reinterpret_cast<const u32x4*>(sCt + (16 * s + l16) * NS + 32 * ks + 8 * g4);
+            } else {
+                // the 4 lanes of a DPP quad hold the 4 ranks of one token: each
+                // evaluates one of the quad's 4 angles and shares it
+                const float Ti = wsc[320 + tii[k]];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const CS own = cs_rev(omC[ks], Ti);
+                    const CS t0{quad_bcast<0>(own.c), quad_bcast<0>(own.s)};
+                    const CS t1{quad_bcast<1>(own.c), quad_bcast<1>(own.s)};
+                    const CS t2{quad_bcast<2>(own.c), quad_bcast<2>(own.s)};
+                    const CS t3{quad_bcast<3>(own.c), quad_bcast<3>(own.s)};
+                    const u32x4 v = craw[k][ks];
+                    cr[k][ks] = u32x4{rot_pair(v[0], t0), rot_pair(v[1], t1), rot_pair(v[2], t2), rot_pair(v[3], t3)};
+                }
+            }
+        }
+
+        // ---- 7. inter-chunk part y^T[p][rho_i] = e^{S_i} sum_n g^T[p][n] C~[rho_i][n]:
+        //         each g^T operand serves every strip of the wave
+        floatx4 acc[SPW][4];
+#pragma unroll
+        for (int k = 0; k < SPW; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[k][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 ga[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ga[q] = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int k = 0; k < SPW; ++k) acc[k][q] = mfma32(ga[q], cr[k][ks], acc[k][q]);
+        }
+#pragma unroll
+        for (int k = 0; k < SPW; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[k][q] *= eSi[k];
+
+        // ---- 8. intra-chunk part, pair-major: the score tiles (jt, jt + 1) of every
+        //         strip at or below the pair, masked (decay x width-2 convolution),
+        //         then y^T[p][rho_i] += X^T[p][rho_j] (M o scores^T)[rho_j][rho_i].
+        // Each pair's B~ operands (A operand of the scores, loaded one pair ahead),
+        // its X^T operands and its mask scalars are loaded once for all strips.
+        // Below the diagonal tile (every row token precedes every column token) the
+        // decay splits at the tile's last token r: e^{S_i-S_j} = e^{S_i-S_r}
+        // e^{S_r-S_j}, both factors <= 1, the second staged per token with the
+        // width-2 weight, leaving one exp per lane and tile. The diagonal tile
+        // takes the full mask, plus D on rho_j = rho_i (the skip term D x rides
+        // in the same contraction).
+        auto load_pair = [&](int jp, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
+            // operand rows past the chunk's padded rows (the prefetch after the last
+            // pair) are clamped to valid rows; their products are never used
+            const int r0 = 32 * jp + l16 < QRP ? 32 * jp + l16 : QRP - 1;
+            const int r1 = r0 + 16 < QRP ? r0 + 16 : QRP - 1;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                a0[ks] = *reinterpret_cast<const u32x4*>(sBt + r0 * NS + 32 * ks + 8 * g4);
+                a1[ks] = *reinterpret_cast<const u32x4*>(sBt + r1 * NS + 32 * ks + 8 * g4);
+            }
+        };
+        auto read_below = [&](int jt, float& sr, float (&tw)[4]) {
+            const unsigned rj = 16u * jt + 4u * g4;
+            sr = wsc[(16 * jt + 15) >> LR];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tw[e] = wsc[384 + ((rj + e) >> LR)];
+        };
+        auto load_x = [&](int jp, u32x2 (&xa)[4], u32x2 (&xb)[4]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t* xr = sXT + (16 * q + l16) * XS + 32 * jp + 4 * g4;
+                xa[q] = *reinterpret_cast<const u32x2*>(xr);
+                xb[q] = *reinterpret_cast<const u32x2*>(xr + 16);
+            }
+        };
+        auto score = [&](const u32x4 (&a)[4], const u32x4 (&c)[4]) {
+            floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) t = mfma32(a[ks], c[ks], t);
+            return t;
+        };
+        auto mask_below = [&](const floatx4& t, float sr, const float (&tw)[4], float S2, float* m) {
+            const float a = __builtin_amdgcn_exp2f(S2 - sr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] = t[e] * (tw[e] * a);
+        };
+        auto mask_diag = [&](const floatx4& t, int jt, int k, float* m) {
+            const unsigned rj = 16u * jt + 4u * g4;
+            const int rho_i = 16 * strip[k] + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                m[e] = t[e] * mask_coef(int((rj + e) >> LR), tii[k], S2i[k], wsc) + (int(rj + e) == rho_i ? Dh : 0.f);
+        };
+        auto y_pair = [&](floatx4 (&ac)[4], const u32x2 (&xa)[4], const u32x2 (&xb)[4], const float* m0,
+                          const float* m1) {
+            const u32x4 pb = {pack2(m0[0], m0[1]), pack2(m0[2], m0[3]), pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ac[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, ac[q]);
+        };
+        // pair jp for strips k0 .. SPW-1; strip k0 holds its diagonal tile in this
+        // pair when DIAG (its last pair), every other strip lies wholly below it
+        auto pair_step = [&](auto k0c, auto diagc, int jp, const u32x4 (&a0)[4], const u32x4 (&a1)[4]) {
+            constexpr int K0 = decltype(k0c)::value;
+            constexpr bool DIAG = decltype(diagc)::value;
+            float sr0, sr1, tw0[4], tw1[4];
+            read_below(2 * jp, sr0, tw0);
+            read_below(2 * jp + 1, sr1, tw1);
+            u32x2 xa[4], xb[4];
+            load_x(jp, xa, xb);
+            floatx4 t0[SPW], t1[SPW];
+#pragma unroll
+            for (int k = K0; k < SPW; ++k) {
+                t0[k] = score(a0, cr[k]);
+                t1[k] = score(a1, cr[k]);
+            }
+#pragma unroll
+            for (int k = K0; k < SPW; ++k) {
+                float m0[4], m1[4];
+                if (DIAG && k == K0) {
+                    if (strip[k] & 1) {
+                        mask_below(t0[k], sr0, tw0, S2i[k], m0);
+                        mask_diag(t1[k], 2 * jp + 1, k, m1);
+                    } else {
+                        mask_diag(t0[k], 2 * jp, k, m0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) m1[e] = 0.f;
+                    }
+                } else {
+                    mask_below(t0[k], sr0, tw0, S2i[k], m0);
+                    mask_below(t1[k], sr1, tw1, S2i[k], m1);
+                }
+                y_pair(acc[k], xa, xb, m0, m1);
+            }
+        };
+        {
+            u32x4 pa0[4], pa1[4];
+            load_pair(0, pa0, pa1);
+            int jp = 0;
+            auto run_strip = [&](auto k0c) {
+                constexpr int K0 = decltype(k0c)::value;
+                const int jd = strip[K0] >> 1;  // the pair holding strip K0's diagonal tile
+#pragma unroll 1
+                for (; jp < jd; ++jp) {
+                    u32x4 a0[4], a1[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        a0[ks] = pa0[ks];
+                        a1[ks] = pa1[ks];
+                    }
+                    load_pair(jp + 1, pa0, pa1);
+                    pair_step(k0c, std::false_type{}, jp, a0, a1);
+                }
+                u32x4 a0[4], a1[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    a0[ks] = pa0[ks];
+                    a1[ks] = pa1[ks];
+                }
+                if (K0 + 1 < SPW) load_pair(jp + 1, pa0, pa1);
+                pair_step(k0c, std::true_type{}, jp, a0, a1);
+                ++jp;
+            };
+            run_strip(std::integral_constant<int, 0>{});
+            if constexpr (SPW > 1) run_strip(std::integral_constant<int, 1>{});
+            if constexpr (SPW > 2) run_strip(std::integral_constant<int, 2>{});
+            if constexpr (SPW > 3) run_strip(std::integral_constant<int, 3>{});
+            static_assert(SPW <= 4, "at most four strips per wave");
+        }
+
+        // ---- 9. epilogue: 4 consecutive p of row rho_i per lane (D x is already in)
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int rho_i = 16 * strip[k] + l16;
+            if ((rho_i >> LR) < nq && (rho_i & (R - 1)) < Rin) {
+                const int i = rho_i >> LR, r = rho_i & (R - 1);
+                const int64_t yo =
+                    ((b * L + c * Q) * H + h) * int64_t(Rin * Pcol) + int64_t(i * H * Rin + r) * Pcol + p_off;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int p = 16 * q + 4 * g4;
+                    if (GP && p >= Pin) continue;  // Pin is a multiple of 8
+                    floatx4 v = acc[k][q];
+                    if (ym >= 2) v += *reinterpret_cast<const floatx4*>(ypart + yo + p);
+                    if (ym == 1 || ym == 3)
+                        *reinterpret_cast<floatx4*>(ypart + yo + p) = v;
+                    else
+                        *reinterpret_cast<u32x2*>(y + yo + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+                }
             }
         }
         lds_barrier();
@@ -1470,6 +1316,7 @@ bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dt
 bool mfma_segments_supported(int32_t R, int32_t N_, int32_t P_) { return R != 1 && N_ <= N && P_ <= P; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
+    if (ws4_supported(a)) return launch_prefill_ws4(a);
     if (a.b * a.H * a.plan.segments > 0x7fffffff) return hipErrorInvalidValue;
     if (a.R == 1 && a.plan.segments != 1) return hipErrorInvalidValue;
     const int row_passes = (a.N + N - 1) / N, col_passes = (a.P + P - 1) / P;

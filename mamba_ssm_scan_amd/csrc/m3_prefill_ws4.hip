@@ -1,0 +1,585 @@
+// m3_prefill_ws4.hip -- chunked prefill at MIMO rank R = 4 for the state of the
+// workloads (N = 128 rows, P = 64 columns), chunk <= 64 tokens, bf16 I/O, fp32
+// state, with wave specialisation.
+//
+// The recurrence and its chunked form are those of m3_prefill_mfma.hip (the
+// complex transition as data-dependent RoPE on B and C, the decay x width-2
+// convolution mask, MIMO: "复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构",
+// §2.1-§2.3, Fig. 2 and Fig. 3). One workgroup walks the chunks of one
+// (batch, head) with two kinds of waves, two waves per SIMD:
+//
+//   output waves (0-3): the chunk's outputs. Wave w holds four 16-row strips of
+//     the chunk's 256 rows (strips w, 7-w, 8+w, 15-w: an even share of the
+//     triangle), their C~ rows and their y accumulators in registers, and walks
+//     the score tiles pair by pair: each B~ pair, X^T pair and mask-scalar load
+//     serves all four strips. Inter-chunk term e^{S_i} C~_i g from g^T in LDS.
+//   state waves (4-7): the state update of the chunk (the fp32 state lives in
+//     their registers, 32 rows per wave), the loads of the next chunk's B, x
+//     and token scalars, its RoPE (B~ rows, plus a bf16 (cos, sin) table from
+//     which the output waves turn their C rows) and their staging into LDS.
+//
+// Two barriers per chunk: X (the output waves are done with the chunk's LDS
+// operands: the state waves may overwrite them with the next chunk) and Y (the
+// next chunk is staged). The state update of chunk c writes g^T of chunk c+1 to
+// the other of two buffers while the output waves read g^T of chunk c.
+#include "m3_internal.h"
+#include "m3_mfma_common.h"
+
+namespace m3 {
+namespace {
+namespace ws4 {
+
+constexpr int R = 4, LR = 2;
+constexpr int QRP = 64 * R;     // rows (token, rank) per chunk
+constexpr int XS = QRP + 8;     // X^T row stride (bf16)
+constexpr int NOW = 4;          // output waves
+constexpr int NSW = 4;          // state waves
+constexpr int NST = 64 * NSW;   // state-wave threads
+constexpr int UPT = 64 * 16 / NST;   // (token, 8-column piece) units of B per state thread
+constexpr int XPT = QRP * 4 / NST;   // (row pair, 8 columns) units of X per state thread
+constexpr int SPW = QRP / 16 / NOW;  // strips per output wave
+constexpr int TPW = 32 / NSW;        // 16x16 state tiles per state wave
+static_assert(UPT == 4 && XPT == 4 && SPW == 4 && TPW == 8, "split");
+
+// the four strips of output wave w, ascending (snake order over the 16 strips)
+__device__ __forceinline__ int strip4(int w, int k) { return k * NOW + ((k & 1) ? (NOW - 1 - w) : w); }
+
+// Global operands of one chunk for a state thread, held until they are staged.
+struct Pre {
+    float d, l, dn, ln;  // lane = token: dt, lambda, and of the next token
+    u32x4 b[UPT][R];     // B rows (token (stid >> 4) + 16 m, rank r), 8 columns at 8 (stid & 15)
+};
+
+// X rows of one chunk for a state thread: rows 2u, 2u + 1 (u = (stid >> 3) + 32 m),
+// 8 columns at 8 (stid & 7)
+struct PreX {
+    u32x4 x0[XPT], x1[XPT];
+};
+
+__device__ __forceinline__ void load_prex(PreX& px, const ChunkBase& cb, int H, int stid) {
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+        const int rho0 = 2 * ((stid >> 3) + m * (NST / 8));
+        const int col = 8 * (stid & 7);
+        px.x0[m] = load_tok(cb.x, rho0 >> LR, cb.nq, H * R * P, (rho0 & (R - 1)) * P + col);
+        px.x1[m] = load_tok(cb.x, (rho0 + 1) >> LR, cb.nq, H * R * P, ((rho0 + 1) & (R - 1)) * P + col);
+    }
+}
+
+// X^T [p][rho] from the rows in px: pairs of consecutive rows packed per column
+__device__ __forceinline__ void stage_x(const PreX& px, uint16_t* sxt, int stid) {
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+        const int rho0 = 2 * ((stid >> 3) + m * (NST / 8));
+        const int pcx = stid & 7;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = 8 * pcx + 2 * j;
+            *reinterpret_cast<unsigned*>(sxt + p * XS + rho0) = (px.x0[m][j] & 0xffffu) | (px.x1[m][j] << 16);
+            *reinterpret_cast<unsigned*>(sxt + (p + 1) * XS + rho0) = (px.x0[m][j] >> 16) | (px.x1[m][j] & 0xffff0000u);
+        }
+    }
+}
+
+// C~ pair from a raw pair (c0, c1) and a packed bf16 (cos, sin): turned by -Phi,
+// (c c0 + s c1, c c1 - s c0), as two bf16 dot products accumulated in fp32
+__device__ __forceinline__ unsigned rot_dot(unsigned w, unsigned cs) {
+    const unsigned ms_c = __builtin_amdgcn_perm(cs, cs, 0x01000302u) ^ 0x00008000u;  // (-s, c)
+    const float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cs), __builtin_bit_cast(bf16x2, w),
+                                                    0.f, false);
+    const float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ms_c), __builtin_bit_cast(bf16x2, w),
+                                                    0.f, false);
+    return pack2(a, b);
+}
+
+}  // namespace ws4
+
+template <bool ROT>
+__global__ void __launch_bounds__(64 * (ws4::NOW + ws4::NSW))
+prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
+                   const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
+                   const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
+                   uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
+                   const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks, int64_t nbh) {
+    using namespace ws4;
+    // LDS: B~ [rho][n]; X^T [p][rho]; g^T [p][n] bf16, two buffers; per-token
+    // scalars (S2 = log2 decay, gamma, delta_next, e^{S}, state weight, T, tile
+    // weight); (cos, sin) of every (token, pair) angle as packed bf16
+    __shared__ __attribute__((aligned(16))) uint16_t sBt[QRP * NS];
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[P * XS];
+    __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];
+    __shared__ __attribute__((aligned(16))) float sSc[7 * 64];
+    __shared__ __attribute__((aligned(16))) unsigned sCS[64 * K];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    int64_t bh;
+    {
+        // XCD-aware order: the 8 XCDs take blocks round-robin; each gets a
+        // contiguous run of (b, h), so heads sharing B/C share an L2
+        const int64_t bid = blockIdx.x, q8 = nbh / 8, r8 = nbh % 8;
+        const int64_t xcd = bid % 8, slot = bid / 8;
+        bh = xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+    }
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const int grp = h / (H / G);
+    const float A2 = Av[h] * kLog2e;
+    const float Dh = Dv[h];
+    const float* omh = (ROT && omega) ? omega + int64_t(h) * K : nullptr;
+    auto omk = [&](int k) { return omh ? omh[k] : 0.f; };
+    auto chunk_base = [&](int64_t cc) {
+        const int64_t c0 = cc * Q, tok0 = b * L + c0;
+        ChunkBase cb;
+        cb.B = Bm + (tok0 * G + grp) * int64_t(R * N);
+        cb.C = Cm + (tok0 * G + grp) * int64_t(R * N);
+        cb.x = x + (tok0 * H + h) * int64_t(R * P);
+        cb.nq = int(L - c0 < Q ? L - c0 : Q);
+        cb.nin = N;
+        cb.nrow = N;
+        cb.pin = P;
+        cb.pcol = P;
+        cb.rin = R;
+        return cb;
+    };
+
+    if (wave >= NOW) {
+        // ============================ state waves
+        const int sw = wave - NOW, stid = tid - 64 * NOW;
+        float omB[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) omB[j] = omk(4 * (stid & 15) + j) * kInv2Pi;
+        float omS[TPW / 4][2];  // rates of the pairs of this wave's state rows
+#pragma unroll
+        for (int mr = 0; mr < TPW / 4; ++mr)
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omk(8 * ((sw * TPW) / 4 + mr) + 2 * g4 + hp) * kInv2Pi;
+
+        // Operands of the next chunk: the X rows are loaded before the state
+        // update, the token scalars and B rows after it (so that they are not held
+        // through it: the output waves take longer per chunk than the state
+        // update, the loads and the RoPE together).
+        Pre pre;
+        PreX px;
+        auto load = [&](int64_t cc) {
+            const ChunkBase cb = chunk_base(cc);
+            const int nq = cb.nq, pc = stid & 15;
+            const int64_t c0 = cc * Q;
+            const int ic = lane < nq ? lane : nq - 1;
+            const int64_t ti = (b * L + c0 + ic) * H + h;
+            const float d = dt[ti], l = lam_at(lam, ti);
+            const bool has_next = c0 + ic + 1 < L;
+            const float dn = dt[has_next ? ti + H : ti], ln = lam_at(lam, has_next ? ti + H : ti);
+            pre.d = lane < nq ? d : 0.f;
+            pre.l = lane < nq ? l : 0.f;
+            pre.dn = (lane < nq && has_next) ? dn : 0.f;
+            pre.ln = (lane < nq && has_next) ? ln : 0.f;
+#pragma unroll
+            for (int m = 0; m < UPT; ++m) {
+                const int i = (stid >> 4) + m * (NST / 16);
+#pragma unroll
+                for (int r = 0; r < R; ++r) pre.b[m][r] = load_tok(cb.B, i, nq, G * R * N, r * N + 8 * pc);
+            }
+        };
+        // RoPE of the loaded chunk in registers (B rows turned in place; the
+        // (cos, sin) table and the token scalars kept for the LDS writes)
+        u32x4 cs4[UPT];
+        float sc[7];
+        auto rope = [&](int nq) -> float {
+            const float T = wave_prefix_sum(pre.d, lane);
+            const float Te = lane_read(T, nq - 1);
+            {
+                const float S2 = A2 * T, S2e = A2 * Te;
+                const float gam = pre.l * pre.d, dln = (1.f - pre.ln) * pre.dn;
+                sc[0] = S2;
+                sc[1] = gam;
+                sc[2] = dln;
+                sc[3] = __builtin_amdgcn_exp2f(S2);
+                sc[4] = __builtin_amdgcn_exp2f(S2e - S2) * (gam + dln);
+                sc[5] = T;
+                // weight of row token j against the last token of its 16-row tile
+                sc[6] = __builtin_amdgcn_exp2f(tile_last<LR>(S2, lane) - S2) * (gam + dln);
+            }
+            // a wave's lanes cover tokens tb + row + 16 m (row = lane / 16)
+            const int tb = __builtin_amdgcn_readfirstlane(stid >> 4) & ~3;
+            const int row = lane >> 4;
+#pragma unroll
+            for (int m = 0; m < UPT; ++m) {
+                const float t0 = lane_read(T, tb + 16 * m), t1 = lane_read(T, tb + 16 * m + 1);
+                const float t2 = lane_read(T, tb + 16 * m + 2), t3 = lane_read(T, tb + 16 * m + 3);
+                const float Ti = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : t3;
+                CS t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = cs_rev(omB[j], Ti);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const u32x4 vb = pre.b[m][r];
+                    pre.b[m][r] =
+                        u32x4{rot_pair(vb[0], t[0]), rot_pair(vb[1], t[1]), rot_pair(vb[2], t[2]), rot_pair(vb[3], t[3])};
+                }
+                cs4[m] = u32x4{pack2(t[0].c, t[0].s), pack2(t[1].c, t[1].s), pack2(t[2].c, t[2].s), pack2(t[3].c, t[3].s)};
+            }
+            return Te;
+        };
+        auto write_lds = [&]() {
+            if (sw == 0) {
+#pragma unroll
+                for (int k = 0; k < 7; ++k) sSc[64 * k + lane] = sc[k];
+            }
+            const int pc = stid & 15;
+#pragma unroll
+            for (int m = 0; m < UPT; ++m) {
+                const int i = (stid >> 4) + 16 * m;
+#pragma unroll
+                for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(sBt + (i * R + r) * NS + 8 * pc) = pre.b[m][r];
+                *reinterpret_cast<u32x4*>(sCS + i * K + 4 * pc) = cs4[m];
+            }
+            stage_x(px, sXT, stid);
+        };
+
+        // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
+        floatx4 gst[TPW];
+        {
+            const int64_t t0 = (b * L) * H + h;
+            const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                const int u = sw * TPW + m, nt = u >> 2, pt = u & 3;
+                const int p = 16 * pt + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = 16 * nt + 4 * g4 + e;
+                    float v = h0 ? h0[(bh * N + n) * P + p] : 0.f;
+                    if (carry_B) {
+                        float s = 0.f;
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * N + n]) *
+                                 bf16_to_f32(carry_x[(bh * R + r) * P + p]);
+                        v += dl0 * s;
+                    }
+                    gst[m][e] = v;
+                }
+                *reinterpret_cast<u32x2*>(&sGT[0][p * NS + 16 * nt + 4 * g4]) =
+                    u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
+            }
+        }
+        // Per chunk c = -1 .. n_chunks - 1: update the state with chunk c (its
+        // operands are in LDS), load and turn chunk c + 1, wait for the output
+        // waves to finish chunk c (X), write chunk c + 1 into LDS (Y).
+        float Te = 0.f;
+#pragma unroll 1
+        for (int64_t c = -1; c < n_chunks; ++c) {
+            const bool more = c + 1 < n_chunks;
+            // the X rows come from HBM: issued first, so the state update covers their latency
+            if (more) load_prex(px, chunk_base(c + 1), H, stid);
+            if (c >= 0) {
+                const int nq = chunk_base(c).nq;
+                uint16_t* gTn = sGT[(c + 1) & 1];
+                // ---- state passed to the next chunk: g' = Rot(Phi_e) [e^{S_e} g + sum w_j B~_j x_j^T]
+                const float decE = sSc[192 + nq - 1];
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) gst[m] *= decE;
+                // A operand (w B~)^T: row n, k = 8 consecutive rho, read straight from
+                // the row-major B~ with transposing LDS loads and scaled by the state
+                // weight; the operands of step ks + 1 are loaded during step ks
+                struct Ops {
+                    u32x4 xb[4];
+                    u32x2 lo[TPW / 4], hi[TPW / 4];
+                    float w0, w1;
+                };
+                auto ops = [&](int ks, Ops& o) {
+                    const unsigned rb = 32u * ks + 8u * g4;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt)
+                        o.xb[pt] = *reinterpret_cast<const u32x4*>(sXT + (16 * pt + l16) * XS + rb);
+                    o.w0 = sSc[256 + (rb >> LR)];
+                    o.w1 = sSc[256 + ((rb + 4) >> LR)];
+#pragma unroll
+                    for (int mr = 0; mr < TPW / 4; ++mr) {
+                        const int n0 = 16 * ((sw * TPW) / 4 + mr);
+                        o.lo[mr] = load_tr(sBt + (rb + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                        o.hi[mr] = load_tr(sBt + (rb + 4 + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                    }
+                };
+                Ops cur, nxt;
+                ops(0, cur);
+#pragma unroll
+                for (int ks = 0; ks < QRP / 32; ++ks) {
+                    if (ks + 1 < QRP / 32) ops(ks + 1, nxt);
+#pragma unroll
+                    for (int mr = 0; mr < TPW / 4; ++mr) {
+                        const u32x4 a = {scale2(cur.lo[mr][0], cur.w0, cur.w0), scale2(cur.lo[mr][1], cur.w0, cur.w0),
+                                         scale2(cur.hi[mr][0], cur.w1, cur.w1), scale2(cur.hi[mr][1], cur.w1, cur.w1)};
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt) gst[mr * 4 + pt] = mfma32(a, cur.xb[pt], gst[mr * 4 + pt]);
+                    }
+                    cur = nxt;
+                }
+#pragma unroll
+                for (int mr = 0; mr < TPW / 4; ++mr) {
+                    const CS t0 = cs_rev(omS[mr][0], Te), t1 = cs_rev(omS[mr][1], Te);
+                    const int nt = (sw * TPW) / 4 + mr;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const int m = mr * 4 + pt;
+                        float a0 = gst[m][0], a1 = gst[m][1];
+                        gst[m][0] = t0.c * a0 - t0.s * a1;
+                        gst[m][1] = t0.s * a0 + t0.c * a1;
+                        a0 = gst[m][2];
+                        a1 = gst[m][3];
+                        gst[m][2] = t1.c * a0 - t1.s * a1;
+                        gst[m][3] = t1.s * a0 + t1.c * a1;
+                        const int p = 16 * pt + l16;
+                        *reinterpret_cast<u32x2*>(gTn + p * NS + 16 * nt + 4 * g4) =
+                            u32x2{pack2(gst[m][0], gst[m][1]), pack2(gst[m][2], gst[m][3])};
+                    }
+                }
+            }
+            if (more) {
+                load(c + 1);
+                Te = rope(chunk_base(c + 1).nq);
+            }
+            if (c >= 0) lds_barrier();  // X(c): the output waves are done with chunk c's operands
+            if (more) write_lds();
+            lds_barrier();  // Y(c + 1)
+        }
+        if (h_out) {
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                const int u = sw * TPW + m, nt = u >> 2, pt = u & 3;
+                const int p = 16 * pt + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = gst[m][e];
+            }
+        }
+        return;
+    }
+
+    // ================================ output waves
+    const int ow = wave;
+    int strip[SPW];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) strip[k] = strip4(ow, k);
+    // raw C rows of the wave's strips in the B-operand layout (col rho_i = 16 s + l16, k = n)
+    u32x4 craw[SPW][4];
+    auto load_c = [&](int64_t cc) {
+        const ChunkBase cb = chunk_base(cc);
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int rho = 16 * strip[k] + l16;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                craw[k][ks] = load_tok(cb.C, rho >> LR, cb.nq, G * R * N, (rho & (R - 1)) * N + 32 * ks + 8 * g4);
+        }
+    };
+    lds_barrier();  // Y(0)
+
+#pragma unroll 1
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        const int nq = chunk_base(c).nq;
+        const uint16_t* gT = sGT[c & 1];
+        load_c(c);
+
+        // ---- C~ rows of the strips, turned with the staged (cos, sin) table
+        u32x4 cr[SPW][4];
+        float S2i[SPW], eSi[SPW];
+        int tii[SPW];
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            tii[k] = (16 * strip[k] + l16) >> LR;
+            S2i[k] = sSc[tii[k]];
+            eSi[k] = sSc[192 + tii[k]];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 cs = *reinterpret_cast<const u32x4*>(sCS + tii[k] * K + 16 * ks + 4 * g4);
+                const u32x4 v = craw[k][ks];
+                cr[k][ks] = u32x4{rot_dot(v[0], cs[0]), rot_dot(v[1], cs[1]), rot_dot(v[2], cs[2]),
+                                  rot_dot(v[3], cs[3])};
+            }
+        }
+
+        // ---- inter-chunk part y^T[p][rho_i] = e^{S_i} sum_n g^T[p][n] C~[rho_i][n]
+        floatx4 acc[SPW][4];
+#pragma unroll
+        for (int k = 0; k < SPW; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[k][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 ga[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ga[q] = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int k = 0; k < SPW; ++k) acc[k][q] = mfma32(ga[q], cr[k][ks], acc[k][q]);
+        }
+#pragma unroll
+        for (int k = 0; k < SPW; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[k][q] *= eSi[k];
+
+        // ---- intra-chunk part, pair-major: the score tiles (jt, jt + 1) of every
+        //      strip at or below the pair, masked, then y^T += X^T (M o scores^T).
+        // Below the diagonal tile (every row token precedes every column token)
+        // the decay splits at the tile's last token r: e^{S_i-S_j} =
+        // e^{S_i-S_r} e^{S_r-S_j}, both factors <= 1, the second staged per token
+        // with the width-2 weight: one exp per lane and tile. The diagonal tile
+        // takes the full mask, plus D on rho_j = rho_i (the skip term D x rides in
+        // the same contraction).
+        auto load_pair = [&](int jp, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
+            // rows past the chunk's padded rows (the prefetch after the last pair)
+            // are clamped to valid rows; their products are never used
+            const int r0 = 32 * jp + l16 < QRP ? 32 * jp + l16 : QRP - 1;
+            const int r1 = r0 + 16 < QRP ? r0 + 16 : QRP - 1;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                a0[ks] = *reinterpret_cast<const u32x4*>(sBt + r0 * NS + 32 * ks + 8 * g4);
+                a1[ks] = *reinterpret_cast<const u32x4*>(sBt + r1 * NS + 32 * ks + 8 * g4);
+            }
+        };
+        auto read_below = [&](int jt, float& sr, float (&tw)[4]) {
+            const unsigned rj = 16u * jt + 4u * g4;
+            sr = sSc[(16 * jt + 15) >> LR];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tw[e] = sSc[384 + ((rj + e) >> LR)];
+        };
+        auto load_x = [&](int jp, u32x2 (&xa)[4], u32x2 (&xb)[4]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t* xr = sXT + (16 * q + l16) * XS + 32 * jp + 4 * g4;
+                xa[q] = *reinterpret_cast<const u32x2*>(xr);
+                xb[q] = *reinterpret_cast<const u32x2*>(xr + 16);
+            }
+        };
+        auto score = [&](const u32x4 (&a)[4], const u32x4 (&cc)[4]) {
+            floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) t = mfma32(a[ks], cc[ks], t);
+            return t;
+        };
+        auto mask_below = [&](const floatx4& t, float sr, const float (&tw)[4], float S2, float* m) {
+            const float a = __builtin_amdgcn_exp2f(S2 - sr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] = t[e] * (tw[e] * a);
+        };
+        auto mask_diag = [&](const floatx4& t, int jt, int k, float* m) {
+            const unsigned rj = 16u * jt + 4u * g4;
+            const int rho_i = 16 * strip[k] + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                m[e] = t[e] * mask_coef(int((rj + e) >> LR), tii[k], S2i[k], sSc) + (int(rj + e) == rho_i ? Dh : 0.f);
+        };
+        auto y_pair = [&](floatx4 (&ac)[4], const u32x2 (&xa)[4], const u32x2 (&xb)[4], const float* m0,
+                          const float* m1) {
+            const u32x4 pb = {pack2(m0[0], m0[1]), pack2(m0[2], m0[3]), pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ac[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, ac[q]);
+        };
+        // pair jp for strips k0 .. SPW-1; strip k0 holds its diagonal tile in this
+        // pair when DIAG (its last pair); every other strip lies wholly below it
+        // (two strips that follow each other never share a diagonal pair: when
+        // they differ by one row tile, the first is odd)
+        auto pair_step = [&](auto k0c, auto diagc, int jp, const u32x4 (&a0)[4], const u32x4 (&a1)[4]) {
+            constexpr int K0 = decltype(k0c)::value;
+            constexpr bool DIAG = decltype(diagc)::value;
+            float sr0, sr1, tw0[4], tw1[4];
+            read_below(2 * jp, sr0, tw0);
+            read_below(2 * jp + 1, sr1, tw1);
+            u32x2 xa[4], xb[4];
+            load_x(jp, xa, xb);
+            // the strips in two halves: score tiles of two strips in flight at a time
+#pragma unroll
+            for (int hk = 0; hk < SPW; hk += 2) {
+            floatx4 t0[2], t1[2];
+#pragma unroll
+            for (int k = hk > K0 ? hk : K0; k < hk + 2; ++k) {
+                t0[k - hk] = score(a0, cr[k]);
+                t1[k - hk] = score(a1, cr[k]);
+            }
+#pragma unroll
+            for (int k = hk > K0 ? hk : K0; k < hk + 2; ++k) {
+                float m0[4], m1[4];
+                if (DIAG && k == K0) {
+                    if (strip[k] & 1) {
+                        mask_below(t0[k - hk], sr0, tw0, S2i[k], m0);
+                        mask_diag(t1[k - hk], 2 * jp + 1, k, m1);
+                    } else {
+                        mask_diag(t0[k - hk], 2 * jp, k, m0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) m1[e] = 0.f;
+                    }
+                } else {
+                    mask_below(t0[k - hk], sr0, tw0, S2i[k], m0);
+                    mask_below(t1[k - hk], sr1, tw1, S2i[k], m1);
+                }
+                y_pair(acc[k], xa, xb, m0, m1);
+            }
+            }
+        };
+        {
+            int jp = 0;
+            auto run_strip = [&](auto k0c) {
+                constexpr int K0 = decltype(k0c)::value;
+                const int jd = strip[K0] >> 1;  // the pair holding strip K0's diagonal tile
+#pragma unroll 1
+                for (; jp < jd; ++jp) {
+                    u32x4 a0[4], a1[4];
+                    load_pair(jp, a0, a1);
+                    pair_step(k0c, std::false_type{}, jp, a0, a1);
+                }
+                u32x4 a0[4], a1[4];
+                load_pair(jp, a0, a1);
+                pair_step(k0c, std::true_type{}, jp, a0, a1);
+                ++jp;
+            };
+            run_strip(std::integral_constant<int, 0>{});
+            run_strip(std::integral_constant<int, 1>{});
+            run_strip(std::integral_constant<int, 2>{});
+            run_strip(std::integral_constant<int, 3>{});
+        }
+
+        lds_barrier();  // X(c)
+        // ---- epilogue: 4 consecutive p of row rho_i per lane (D x is already in),
+        //      stored while the state waves write the next chunk into LDS
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int rho_i = 16 * strip[k] + l16;
+            if ((rho_i >> LR) < nq) {
+                const int i = rho_i >> LR, r = rho_i & (R - 1);
+                uint16_t* yr = y + ((b * L + c * Q + i) * H + h) * int64_t(R * P) + r * P;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int p = 16 * q + 4 * g4;
+                    const floatx4 v = acc[k][q];
+                    *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+                }
+            }
+        }
+        lds_barrier();  // Y(c + 1)
+    }
+}
+
+}  // namespace
+
+// the exact workload shape at R 4 in one pass (no sequence segments)
+bool ws4_supported(const PrefillArgs& a) {
+    return a.io == M3_BF16 && a.R == 4 && a.N == N && a.P == P && a.chunk >= 1 && a.chunk <= 64 &&
+           a.plan.segments == 1;
+}
+
+hipError_t launch_prefill_ws4(const PrefillArgs& a) {
+    const int64_t nbh = a.b * a.H;
+    if (!ws4_supported(a) || nbh > 0x7fffffff) return hipErrorInvalidValue;
+    auto kern = a.omega ? prefill_ws4_kernel<true> : prefill_ws4_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws4::NOW + ws4::NSW)), 0, a.stream,
+                       static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
+                       static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
+                       static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
+                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
+    return hipGetLastError();
+}
+
+}  // namespace m3
