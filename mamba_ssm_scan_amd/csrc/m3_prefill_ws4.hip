@@ -1,6 +1,6 @@
-// m3_prefill_ws4.hip -- chunked prefill at MIMO rank R = 4 for the state of the
-// workloads (N = 128 rows, P = 64 columns), chunk <= 64 tokens, bf16 I/O, fp32
-// state, with wave specialisation.
+// m3_prefill_ws4.hip -- chunked prefill at MIMO ranks R = 2, 4 for the state of
+// the workloads (N = 128 rows, P = 64 columns), chunk <= 64 tokens, bf16 I/O,
+// fp32 state, with wave specialisation.
 //
 // The recurrence and its chunked form are those of m3_prefill_mfma.hip (the
 // complex transition as data-dependent RoPE on B and C, the decay x width-2
@@ -8,11 +8,11 @@
 // §2.1-§2.3, Fig. 2 and Fig. 3). One workgroup walks the chunks of one
 // (batch, head) with two kinds of waves, two waves per SIMD:
 //
-//   output waves (0-3): the chunk's outputs. Wave w holds four 16-row strips of
-//     the chunk's 256 rows (strips w, 7-w, 8+w, 15-w: an even share of the
+//   output waves (0-3): the chunk's outputs. Wave w holds R of the chunk's 4R
+//     16-row strips (at R 4 strips w, 7-w, 8+w, 15-w: an even share of the
 //     triangle), their C~ rows and their y accumulators in registers, and walks
 //     the score tiles pair by pair: each B~ pair, X^T pair and mask-scalar load
-//     serves all four strips. Inter-chunk term e^{S_i} C~_i g from g^T in LDS.
+//     serves all its strips. Inter-chunk term e^{S_i} C~_i g from g^T in LDS.
 //   state waves (4-7): the state update of the chunk (the fp32 state lives in
 //     their registers, 32 rows per wave), the loads of the next chunk's B, x
 //     and token scalars, its RoPE (B~ rows, plus a bf16 (cos, sin) table from
@@ -29,49 +29,68 @@ namespace m3 {
 namespace {
 namespace ws4 {
 
-constexpr int R = 4, LR = 2;
-constexpr int QRP = 64 * R;     // rows (token, rank) per chunk
-constexpr int XS = QRP + 8;     // X^T row stride (bf16)
 constexpr int NOW = 4;          // output waves
 constexpr int NSW = 4;          // state waves
 constexpr int NST = 64 * NSW;   // state-wave threads
-constexpr int UPT = 64 * 16 / NST;   // (token, 8-column piece) units of B per state thread
-constexpr int XPT = QRP * 4 / NST;   // (row pair, 8 columns) units of X per state thread
-constexpr int SPW = QRP / 16 / NOW;  // strips per output wave
-constexpr int TPW = 32 / NSW;        // 16x16 state tiles per state wave
-static_assert(UPT == 4 && XPT == 4 && SPW == 4 && TPW == 8, "split");
 
-// the four strips of output wave w, ascending (snake order over the 16 strips)
+// sizes at rank R
+template <int R>
+struct Cfg {
+    static constexpr int LR = R == 1 ? 0 : R == 2 ? 1 : 2;  // log2 R
+    static constexpr int QRP = 64 * R;                      // rows (token, rank) per chunk
+    static constexpr int XS = QRP + 8;                      // X^T row stride (bf16)
+    static constexpr int PT = P / 16;                       // 16-column tiles of the state
+    static constexpr int PC = P / 8;                        // 8-column pieces of an X row
+    static constexpr int UPT = 64 * 16 / NST;               // (token, 8-column piece) units of B per state thread
+    static constexpr int XU = QRP / 2 * PC;                 // (row pair, 8 columns) units of X
+    static constexpr int XPT = (XU + NST - 1) / NST;        // ... per state thread
+    static constexpr int SPW = QRP / 16 / NOW;              // strips per output wave
+    static constexpr int TPW = 8 * PT / NSW;                // 16x16 state tiles per state wave
+    static constexpr int MR = TPW / PT;                     // 16-row state tiles per state wave
+    static_assert(UPT == 4 && SPW == R && MR == 2 && (R == 1 || R == 2 || R == 4), "split");
+};
+
+// the strips of output wave w, ascending (snake order over the chunk's strips)
 __device__ __forceinline__ int strip4(int w, int k) { return k * NOW + ((k & 1) ? (NOW - 1 - w) : w); }
 
 // Global operands of one chunk for a state thread, held until they are staged.
+template <int R>
 struct Pre {
-    float d, l, dn, ln;  // lane = token: dt, lambda, and of the next token
-    u32x4 b[UPT][R];     // B rows (token (stid >> 4) + 16 m, rank r), 8 columns at 8 (stid & 15)
+    float d, l, dn, ln;              // lane = token: dt, lambda, and of the next token
+    u32x4 b[Cfg<R>::UPT][R];      // B rows (token (stid >> 4) + 16 m, rank r), 8 columns at 8 (stid & 15)
 };
 
-// X rows of one chunk for a state thread: rows 2u, 2u + 1 (u = (stid >> 3) + 32 m),
-// 8 columns at 8 (stid & 7)
+// X rows of one chunk for a state thread: rows 2u, 2u + 1 (u = stid / PC + m NST / PC),
+// 8 columns at 8 (stid % PC)
+template <int R>
 struct PreX {
-    u32x4 x0[XPT], x1[XPT];
+    u32x4 x0[Cfg<R>::XPT], x1[Cfg<R>::XPT];
 };
 
-__device__ __forceinline__ void load_prex(PreX& px, const ChunkBase& cb, int H, int stid) {
+template <int R>
+__device__ __forceinline__ void load_prex(PreX<R>& px, const ChunkBase& cb, int H, int stid) {
+    using CF = Cfg<R>;
+    constexpr int LR = CF::LR;
 #pragma unroll
-    for (int m = 0; m < XPT; ++m) {
-        const int rho0 = 2 * ((stid >> 3) + m * (NST / 8));
-        const int col = 8 * (stid & 7);
+    for (int m = 0; m < CF::XPT; ++m) {
+        if (CF::XU % NST != 0 && stid + m * NST >= CF::XU) break;
+        const int rho0 = 2 * (stid / CF::PC + m * (NST / CF::PC));
+        const int col = 8 * (stid % CF::PC);
         px.x0[m] = load_tok(cb.x, rho0 >> LR, cb.nq, H * R * P, (rho0 & (R - 1)) * P + col);
         px.x1[m] = load_tok(cb.x, (rho0 + 1) >> LR, cb.nq, H * R * P, ((rho0 + 1) & (R - 1)) * P + col);
     }
 }
 
 // X^T [p][rho] from the rows in px: pairs of consecutive rows packed per column
-__device__ __forceinline__ void stage_x(const PreX& px, uint16_t* sxt, int stid) {
+template <int R>
+__device__ __forceinline__ void stage_x(const PreX<R>& px, uint16_t* sxt, int stid) {
+    using CF = Cfg<R>;
+    constexpr int XS = CF::XS;
 #pragma unroll
-    for (int m = 0; m < XPT; ++m) {
-        const int rho0 = 2 * ((stid >> 3) + m * (NST / 8));
-        const int pcx = stid & 7;
+    for (int m = 0; m < CF::XPT; ++m) {
+        if (CF::XU % NST != 0 && stid + m * NST >= CF::XU) break;
+        const int rho0 = 2 * (stid / CF::PC + m * (NST / CF::PC));
+        const int pcx = stid % CF::PC;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int p = 8 * pcx + 2 * j;
@@ -94,7 +113,7 @@ __device__ __forceinline__ unsigned rot_dot(unsigned w, unsigned cs) {
 
 }  // namespace ws4
 
-template <bool ROT>
+template <int R, bool ROT>
 __global__ void __launch_bounds__(64 * (ws4::NOW + ws4::NSW))
 prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                    const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
@@ -102,6 +121,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                    uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                    const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks, int64_t nbh) {
     using namespace ws4;
+    using CF = Cfg<R>;
+    constexpr int LR = CF::LR, QRP = CF::QRP, XS = CF::XS, UPT = CF::UPT, SPW = CF::SPW, TPW = CF::TPW;
+    constexpr int PT = CF::PT, MR = CF::MR;
     // LDS: B~ [rho][n]; X^T [p][rho]; g^T [p][n] bf16, two buffers; per-token
     // scalars (S2 = log2 decay, gamma, delta_next, e^{S}, state weight, T, tile
     // weight); (cos, sin) of every (token, pair) angle as packed bf16
@@ -150,18 +172,18 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         float omB[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) omB[j] = omk(4 * (stid & 15) + j) * kInv2Pi;
-        float omS[TPW / 4][2];  // rates of the pairs of this wave's state rows
+        float omS[MR][2];  // rates of the pairs of this wave's state rows
 #pragma unroll
-        for (int mr = 0; mr < TPW / 4; ++mr)
+        for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
-            for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omk(8 * ((sw * TPW) / 4 + mr) + 2 * g4 + hp) * kInv2Pi;
+            for (int hp = 0; hp < 2; ++hp) omS[mr][hp] = omk(8 * (sw * MR + mr) + 2 * g4 + hp) * kInv2Pi;
 
         // Operands of the next chunk: the X rows are loaded before the state
         // update, the token scalars and B rows after it (so that they are not held
         // through it: the output waves take longer per chunk than the state
         // update, the loads and the RoPE together).
-        Pre pre;
-        PreX px;
+        Pre<R> pre;
+        PreX<R> px;
         auto load = [&](int64_t cc) {
             const ChunkBase cb = chunk_base(cc);
             const int nq = cb.nq, pc = stid & 15;
@@ -245,7 +267,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
-                const int u = sw * TPW + m, nt = u >> 2, pt = u & 3;
+                const int nt = sw * MR + m / PT, pt = m % PT;
                 const int p = 16 * pt + l16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -285,20 +307,20 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                 // the row-major B~ with transposing LDS loads and scaled by the state
                 // weight; the operands of step ks + 1 are loaded during step ks
                 struct Ops {
-                    u32x4 xb[4];
-                    u32x2 lo[TPW / 4], hi[TPW / 4];
-                    float w0, w1;
+                    u32x4 xb[PT];
+                    u32x2 lo[MR], hi[MR];
+                    float w[8];  // state weight of the 8 rows rb .. rb + 7
                 };
                 auto ops = [&](int ks, Ops& o) {
                     const unsigned rb = 32u * ks + 8u * g4;
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt)
+                    for (int pt = 0; pt < PT; ++pt)
                         o.xb[pt] = *reinterpret_cast<const u32x4*>(sXT + (16 * pt + l16) * XS + rb);
-                    o.w0 = sSc[256 + (rb >> LR)];
-                    o.w1 = sSc[256 + ((rb + 4) >> LR)];
 #pragma unroll
-                    for (int mr = 0; mr < TPW / 4; ++mr) {
-                        const int n0 = 16 * ((sw * TPW) / 4 + mr);
+                    for (int j = 0; j < 8; ++j) o.w[j] = sSc[256 + ((rb + j) >> LR)];
+#pragma unroll
+                    for (int mr = 0; mr < MR; ++mr) {
+                        const int n0 = 16 * (sw * MR + mr);
                         o.lo[mr] = load_tr(sBt + (rb + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
                         o.hi[mr] = load_tr(sBt + (rb + 4 + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
                     }
@@ -309,21 +331,21 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                 for (int ks = 0; ks < QRP / 32; ++ks) {
                     if (ks + 1 < QRP / 32) ops(ks + 1, nxt);
 #pragma unroll
-                    for (int mr = 0; mr < TPW / 4; ++mr) {
-                        const u32x4 a = {scale2(cur.lo[mr][0], cur.w0, cur.w0), scale2(cur.lo[mr][1], cur.w0, cur.w0),
-                                         scale2(cur.hi[mr][0], cur.w1, cur.w1), scale2(cur.hi[mr][1], cur.w1, cur.w1)};
+                    for (int mr = 0; mr < MR; ++mr) {
+                        const u32x4 a = {scale2(cur.lo[mr][0], cur.w[0], cur.w[1]), scale2(cur.lo[mr][1], cur.w[2], cur.w[3]),
+                                         scale2(cur.hi[mr][0], cur.w[4], cur.w[5]), scale2(cur.hi[mr][1], cur.w[6], cur.w[7])};
 #pragma unroll
-                        for (int pt = 0; pt < 4; ++pt) gst[mr * 4 + pt] = mfma32(a, cur.xb[pt], gst[mr * 4 + pt]);
+                        for (int pt = 0; pt < PT; ++pt) gst[mr * PT + pt] = mfma32(a, cur.xb[pt], gst[mr * PT + pt]);
                     }
                     cur = nxt;
                 }
 #pragma unroll
-                for (int mr = 0; mr < TPW / 4; ++mr) {
+                for (int mr = 0; mr < MR; ++mr) {
                     const CS t0 = cs_rev(omS[mr][0], Te), t1 = cs_rev(omS[mr][1], Te);
-                    const int nt = (sw * TPW) / 4 + mr;
+                    const int nt = sw * MR + mr;
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const int m = mr * 4 + pt;
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const int m = mr * PT + pt;
                         float a0 = gst[m][0], a1 = gst[m][1];
                         gst[m][0] = t0.c * a0 - t0.s * a1;
                         gst[m][1] = t0.s * a0 + t0.c * a1;
@@ -348,7 +370,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         if (h_out) {
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
-                const int u = sw * TPW + m, nt = u >> 2, pt = u & 3;
+                const int nt = sw * MR + m / PT, pt = m % PT;
                 const int p = 16 * pt + l16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + p] = gst[m][e];
@@ -401,25 +423,25 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         }
 
         // ---- inter-chunk part y^T[p][rho_i] = e^{S_i} sum_n g^T[p][n] C~[rho_i][n]
-        floatx4 acc[SPW][4];
+        floatx4 acc[SPW][PT];
 #pragma unroll
         for (int k = 0; k < SPW; ++k)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[k][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < PT; ++q) acc[k][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            u32x4 ga[4];
+            u32x4 ga[PT];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ga[q] = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
+            for (int q = 0; q < PT; ++q) ga[q] = *reinterpret_cast<const u32x4*>(gT + (16 * q + l16) * NS + 32 * ks + 8 * g4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < PT; ++q)
 #pragma unroll
                 for (int k = 0; k < SPW; ++k) acc[k][q] = mfma32(ga[q], cr[k][ks], acc[k][q]);
         }
 #pragma unroll
         for (int k = 0; k < SPW; ++k)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[k][q] *= eSi[k];
+            for (int q = 0; q < PT; ++q) acc[k][q] *= eSi[k];
 
         // ---- intra-chunk part, pair-major: the score tiles (jt, jt + 1) of every
         //      strip at or below the pair, masked, then y^T += X^T (M o scores^T).
@@ -446,9 +468,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 #pragma unroll
             for (int e = 0; e < 4; ++e) tw[e] = sSc[384 + ((rj + e) >> LR)];
         };
-        auto load_x = [&](int jp, u32x2 (&xa)[4], u32x2 (&xb)[4]) {
+        auto load_x = [&](int jp, u32x2 (&xa)[PT], u32x2 (&xb)[PT]) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < PT; ++q) {
                 const uint16_t* xr = sXT + (16 * q + l16) * XS + 32 * jp + 4 * g4;
                 xa[q] = *reinterpret_cast<const u32x2*>(xr);
                 xb[q] = *reinterpret_cast<const u32x2*>(xr + 16);
@@ -472,11 +494,11 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             for (int e = 0; e < 4; ++e)
                 m[e] = t[e] * mask_coef(int((rj + e) >> LR), tii[k], S2i[k], sSc) + (int(rj + e) == rho_i ? Dh : 0.f);
         };
-        auto y_pair = [&](floatx4 (&ac)[4], const u32x2 (&xa)[4], const u32x2 (&xb)[4], const float* m0,
+        auto y_pair = [&](floatx4 (&ac)[PT], const u32x2 (&xa)[PT], const u32x2 (&xb)[PT], const float* m0,
                           const float* m1) {
             const u32x4 pb = {pack2(m0[0], m0[1]), pack2(m0[2], m0[3]), pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ac[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, ac[q]);
+            for (int q = 0; q < PT; ++q) ac[q] = mfma32(u32x4{xa[q][0], xa[q][1], xb[q][0], xb[q][1]}, pb, ac[q]);
         };
         // pair jp for strips k0 .. SPW-1; strip k0 holds its diagonal tile in this
         // pair when DIAG (its last pair); every other strip lies wholly below it
@@ -488,19 +510,19 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             float sr0, sr1, tw0[4], tw1[4];
             read_below(2 * jp, sr0, tw0);
             read_below(2 * jp + 1, sr1, tw1);
-            u32x2 xa[4], xb[4];
+            u32x2 xa[PT], xb[PT];
             load_x(jp, xa, xb);
             // the strips in two halves: score tiles of two strips in flight at a time
 #pragma unroll
             for (int hk = 0; hk < SPW; hk += 2) {
             floatx4 t0[2], t1[2];
 #pragma unroll
-            for (int k = hk > K0 ? hk : K0; k < hk + 2; ++k) {
+            for (int k = hk > K0 ? hk : K0; k < hk + 2 && k < SPW; ++k) {
                 t0[k - hk] = score(a0, cr[k]);
                 t1[k - hk] = score(a1, cr[k]);
             }
 #pragma unroll
-            for (int k = hk > K0 ? hk : K0; k < hk + 2; ++k) {
+            for (int k = hk > K0 ? hk : K0; k < hk + 2 && k < SPW; ++k) {
                 float m0[4], m1[4];
                 if (DIAG && k == K0) {
                     if (strip[k] & 1) {
@@ -536,9 +558,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                 ++jp;
             };
             run_strip(std::integral_constant<int, 0>{});
-            run_strip(std::integral_constant<int, 1>{});
-            run_strip(std::integral_constant<int, 2>{});
-            run_strip(std::integral_constant<int, 3>{});
+            if constexpr (SPW > 1) run_strip(std::integral_constant<int, 1>{});
+            if constexpr (SPW > 2) run_strip(std::integral_constant<int, 2>{});
+            if constexpr (SPW > 3) run_strip(std::integral_constant<int, 3>{});
         }
 
         lds_barrier();  // X(c)
@@ -551,7 +573,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                 const int i = rho_i >> LR, r = rho_i & (R - 1);
                 uint16_t* yr = y + ((b * L + c * Q + i) * H + h) * int64_t(R * P) + r * P;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < PT; ++q) {
                     const int p = 16 * q + 4 * g4;
                     const floatx4 v = acc[k][q];
                     *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
@@ -564,22 +586,30 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 
 }  // namespace
 
-// the exact workload shape at R 4 in one pass (no sequence segments)
+// the state of the workloads (N 128, P 64) at R 2 or 4 in one pass, without sequence
+// segments (R 1 runs on the 12-wave kernel of m3_prefill_mfma.hip, faster there)
 bool ws4_supported(const PrefillArgs& a) {
-    return a.io == M3_BF16 && a.R == 4 && a.N == N && a.P == P && a.chunk >= 1 && a.chunk <= 64 &&
+    return a.io == M3_BF16 && (a.R == 2 || a.R == 4) && a.N == N && a.P == P && a.chunk >= 1 && a.chunk <= 64 &&
            a.plan.segments == 1;
 }
 
 hipError_t launch_prefill_ws4(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
     if (!ws4_supported(a) || nbh > 0x7fffffff) return hipErrorInvalidValue;
-    auto kern = a.omega ? prefill_ws4_kernel<true> : prefill_ws4_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws4::NOW + ws4::NSW)), 0, a.stream,
-                       static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
-                       static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
-                       static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                       static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
-    return hipGetLastError();
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws4::NOW + ws4::NSW)), 0, a.stream,
+                           static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
+                           static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
+                           static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
+        return hipGetLastError();
+    };
+    const bool rot = a.omega != nullptr;
+    switch (a.R) {
+        case 2: return rot ? launch(prefill_ws4_kernel<2, true>) : launch(prefill_ws4_kernel<2, false>);
+        case 4: return rot ? launch(prefill_ws4_kernel<4, true>) : launch(prefill_ws4_kernel<4, false>);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace m3
