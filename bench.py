@@ -362,7 +362,7 @@ def bench_mixer(wid, steps, warmup, log, d_model=2048, decode_batch=128, decode_
     e1.record()
     torch.cuda.synchronize()
     dms = e0.elapsed_time(e1) / decode_steps
-    # the same steps captured once (an even number of steps: the carry slots end where they began)
+    # the same steps captured once
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

@@ -4,15 +4,17 @@
 // (exponential-trapezoidal rule, "复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构"
 // §2.2) and the rotation of pair k by +dt*omega_k (complex state, same digest §2.1):
 //
-//   g   = h + delta * B_prev x_prev^T            (previous token, from the carry slot)
+//   g   = h + delta * B_prev x_prev^T            (previous token, from the carry)
 //   h'  = alpha * Rot(dt omega) g + gamma * B x^T   (rank-R: N x R times R x P, §2.3)
 //   y   = h'^T C + D x
 //
 // The fp32 state is read and written once (the step is bound by that traffic:
 // "Mamba-3架构技术解析：新一代语言建模的范式转移" §2.3 on decode being state-I/O
-// bound). The current (B, x) is copied into the other carry slot for the next
-// step; slots alternate, so no workgroup overwrites a value another one of the
-// same launch still reads (B is shared by the H/G heads of a group).
+// bound). Every head keeps its own copy of the previous token's (B, x) rows:
+// the workgroup of (b, h) reads its carry into LDS and, after a barrier,
+// overwrites it with the current token's rows. No other workgroup touches it,
+// so the step needs no slot parity from the host and a captured graph of any
+// number of steps replays correctly.
 #include <type_traits>
 
 #include "m3_device.h"
@@ -47,7 +49,7 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
 // wave covers 64/QP row segments of P floats per access).
 template <typename T, int R, int NTH, int N, int P>
 __global__ void __launch_bounds__(NTH)
-decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
+decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x,
                        const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                        const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                        const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
@@ -79,9 +81,9 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
 
     const T* Bt = B + bg * (R * N);
     const T* Ct = C + bg * (R * N);
-    const T* Bp = carry_B + (int64_t(rd_slot) * nb * G + bg) * (R * N);
+    const T* Bp = carry_B + bh * (R * N);
     const T* xt = x + bh * (R * P);
-    const T* xp = carry_x + (int64_t(rd_slot) * nb * H + bh) * (R * P);
+    const T* xp = carry_x + bh * (R * P);
     for (int e = tid; e < R * N; e += NTH) {
         (&sB[0][0])[e] = Io<T>::load(Bt, e);
         (&sBp[0][0])[e] = Io<T>::load(Bp, e);
@@ -155,11 +157,10 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
         Io<T>::store(y, bh * (R * P) + e, s + Dh * sx[r][p]);
     }
 
-    // this token becomes the carry of the next step
-    const int wr = rd_slot ^ 1;
-    for (int e = tid; e < R * P; e += NTH) carry_x[(int64_t(wr) * nb * H + bh) * (R * P) + e] = xt[e];
-    if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += NTH) carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = Bt[e];
+    // this token becomes the carry of the next step (the carry was read into
+    // LDS before the barrier above)
+    for (int e = tid; e < R * P; e += NTH) carry_x[bh * (R * P) + e] = xt[e];
+    for (int e = tid; e < R * N; e += NTH) carry_B[bh * (R * N) + e] = Bt[e];
 }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -197,7 +198,7 @@ __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 
 template <int R, int N>
 __global__ void __launch_bounds__(256)
 decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
-                   int rd_slot, const bf16_t* __restrict__ x, const float* __restrict__ dt,
+                   const bf16_t* __restrict__ x, const float* __restrict__ dt,
                    const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
@@ -229,9 +230,9 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
 
     const uint16_t* Bt = reinterpret_cast<const uint16_t*>(B) + bg * (R * N);
     const uint16_t* Ct = reinterpret_cast<const uint16_t*>(C) + bg * (R * N);
-    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + (int64_t(rd_slot) * nb * G + bg) * (R * N);
+    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + bh * (R * N);
     const uint16_t* xt = reinterpret_cast<const uint16_t*>(x) + bh * (R * P);
-    const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + (int64_t(rd_slot) * nb * H + bh) * (R * P);
+    const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + bh * (R * P);
     for (int e = tid; e < RS * (N / 2); e += 256) {  // rank r, pair of rows (2 j, 2 j + 1): one 32-bit load
         const int r = e / (N / 2), j = e % (N / 2);
         const unsigned vb = r < R ? reinterpret_cast<const unsigned*>(Bt + r * N)[j] : 0u;
@@ -320,18 +321,16 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
         }
     }
 
-    // this token becomes the carry of the next step
-    const int wr = rd_slot ^ 1;
-    for (int e = tid; e < R * P; e += 256) carry_x[(int64_t(wr) * nb * H + bh) * (R * P) + e] = x[bh * (R * P) + e];
-    if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += 256)
-            carry_B[(int64_t(wr) * nb * G + bg) * (R * N) + e] = B[bg * (R * N) + e];
+    // this token becomes the carry of the next step (the carry was read into
+    // LDS before the barrier above)
+    for (int e = tid; e < R * P; e += 256) carry_x[bh * (R * P) + e] = x[bh * (R * P) + e];
+    for (int e = tid; e < R * N; e += 256) carry_B[bh * (R * N) + e] = B[bg * (R * N) + e];
 }
 
 // Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x, int rd_slot,
+decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x,
                       const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                       const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                       const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
@@ -346,9 +345,9 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
     float* hs = hstate + bh * int64_t(N) * P;
     const T* Bt = B + bg * int64_t(R) * N;
     const T* Ct = C + bg * int64_t(R) * N;
-    const T* Bp = carry_B + (int64_t(rd_slot) * nb * G + bg) * int64_t(R) * N;
+    const T* Bp = carry_B + bh * int64_t(R) * N;
     const T* xt = x + bh * int64_t(R) * P;
-    const T* xp = carry_x + (int64_t(rd_slot) * nb * H + bh) * int64_t(R) * P;
+    const T* xp = carry_x + bh * int64_t(R) * P;
     const float d = dt[bh], lm = lam_at(lam, bh);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
@@ -378,11 +377,10 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
         for (int n = 0; n < N; ++n) s += hs[int64_t(n) * P + p] * Io<T>::load(Ct, int64_t(r) * N + n);
         Io<T>::store(y, bh * int64_t(R) * P + e, s + Dh * Io<T>::load(xt, e));
     }
-    const int wr = rd_slot ^ 1;
-    for (int e = tid; e < R * P; e += kThreads) carry_x[(int64_t(wr) * nb * H + bh) * int64_t(R) * P + e] = xt[e];
-    if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += kThreads)
-            carry_B[(int64_t(wr) * nb * G + bg) * int64_t(R) * N + e] = Bt[e];
+    // this token becomes the carry of the next step (every read of the carry
+    // precedes the barrier above)
+    for (int e = tid; e < R * P; e += kThreads) carry_x[bh * int64_t(R) * P + e] = xt[e];
+    for (int e = tid; e < R * N; e += kThreads) carry_B[bh * int64_t(R) * N + e] = Bt[e];
 }
 
 // (N, P, R) the row kernel is instantiated for (bf16 I/O) besides N 128, P 64 at R 1, 2, 4:
@@ -399,7 +397,7 @@ hipError_t launch_rows(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x,
     constexpr int per = R == 1 ? 16 : 8;  // state floats per thread
     constexpr int want = N * P / per, cap = 1024;
     constexpr int NTH = want < cap ? want : cap;
-    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx, a.rd_slot, x,
+    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx, x,
                        a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     return hipGetLastError();
 }
@@ -442,7 +440,7 @@ hipError_t launch_t(const DecodeArgs& a) {
         if ((a.N == 64 || a.N == 128) && a.P == 64 && ((a.R >= 2 && a.R <= 4) || a.R == 8)) {
             // R 3 runs with a zero fourth rank slot (the staging zero-fills ranks past R); at
             // N 256 the 64 state values per lane spill (358 us against the row kernel's)
-            using K = void (*)(float*, bf16_t*, bf16_t*, int, const bf16_t*, const float*, const float*,
+            using K = void (*)(float*, bf16_t*, bf16_t*, const bf16_t*, const float*, const float*,
                                const float*, const float*, const bf16_t*, const bf16_t*, const float*, bf16_t*,
                                int64_t, int, int);
             K kern = a.N == 64 ? (a.R == 2   ? decode_mfma_kernel<2, 64>
@@ -453,7 +451,7 @@ hipError_t launch_t(const DecodeArgs& a) {
                                   : a.R == 3 ? decode_mfma_kernel<3, 128>
                                   : a.R == 4 ? decode_mfma_kernel<4, 128>
                                              : decode_mfma_kernel<8, 128>);
-            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A, a.omega,
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, x, a.dt, a.A, a.omega,
                                a.lam, B, C, a.D, y, a.b, a.H, a.G);
             return hipGetLastError();
         }
@@ -463,7 +461,7 @@ hipError_t launch_t(const DecodeArgs& a) {
                   : a.R == 2 ? decode_rows_kernel<T, 2, M3_DECODE_THREADS_R4, 128, 64>
                              : decode_rows_kernel<T, 4, M3_DECODE_THREADS_R4, 128, 64>;
         const int nth = a.R == 1 ? M3_DECODE_THREADS_R1 : M3_DECODE_THREADS_R4;
-        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, a.rd_slot, x, a.dt, a.A,
+        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, x, a.dt, a.A,
                            a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     } else {
         if constexpr (std::is_same<T, bf16_t>::value) {
@@ -471,13 +469,32 @@ hipError_t launch_t(const DecodeArgs& a) {
             if (rows_kernel_sizes(a.N, a.P, a.R))
                 return launch_rows_sized<T>(a, grid, cB, cx, x, B, C, y);
         }
-        hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, a.rd_slot, x,
+        hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, x,
                            a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G, a.P, a.N, a.R);
     }
     return hipGetLastError();
 }
 
+// carry[b][h] = src[b][h / (H / G)] (rows of `words` 32-bit words), or zero
+__global__ void carry_init_kernel(uint32_t* __restrict__ carry, const uint32_t* __restrict__ src, int64_t nb, int H,
+                                  int G, int words) {
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const uint32_t* s = src ? src + (b * G + h / (H / G)) * int64_t(words) : nullptr;
+    for (int e = threadIdx.x; e < words; e += blockDim.x) carry[bh * int64_t(words) + e] = s ? s[e] : 0u;
+}
+
 }  // namespace
+
+hipError_t launch_carry_init(void* carry, const void* src, int64_t b, int H, int G, int64_t row_bytes,
+                             hipStream_t s) {
+    if (b * H == 0) return hipSuccess;
+    if (b * H > 0x7fffffff || row_bytes % 4 || row_bytes / 4 > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(carry_init_kernel, dim3(unsigned(b * H)), dim3(256), 0, s, static_cast<uint32_t*>(carry),
+                       static_cast<const uint32_t*>(src), b, H, G, int(row_bytes / 4));
+    return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a) {
     if (a.b * a.H > 0x7fffffff) return hipErrorInvalidValue;

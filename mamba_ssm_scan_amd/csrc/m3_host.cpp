@@ -263,8 +263,8 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
 size_t m3_decode_carry_bytes(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int32_t which) {
     if (check_dims(dims, R) != M3_OK || check_dtype(io_dtype) != M3_OK) return 0;
     const size_t es = io_size(io_dtype);
-    if (which == 0) return 2 * size_t(dims->batch) * dims->groups * R * dims->dstate * es;
-    if (which == 1) return 2 * size_t(dims->batch) * dims->heads * R * dims->headdim * es;
+    if (which == 0) return size_t(dims->batch) * dims->heads * R * dims->dstate * es;
+    if (which == 1) return size_t(dims->batch) * dims->heads * R * dims->headdim * es;
     return 0;
 }
 
@@ -289,11 +289,10 @@ m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(M3_EALIGN, "%s is not 16-byte aligned", names[i]);
     const size_t es = io_size(io_dtype);
     const size_t hbytes = size_t(b) * dims->heads * dims->dstate * dims->headdim * 4;
-    const size_t cb = size_t(b) * dims->groups * R * dims->dstate * es;  // one slot
-    const size_t cx = size_t(b) * dims->heads * R * dims->headdim * es;
+    const size_t rowB = size_t(R) * dims->dstate * es, rowx = size_t(R) * dims->headdim * es;  // one head's carry rows
     if (h0 && h0 != h_buf && overlaps(rng("h0", h0, hbytes), rng("h", h_buf, hbytes)))
         return fail(M3_EINVAL, "h0 partially overlaps the state buffer");
-    if ((cb % 4) || (cx % 4)) return fail(M3_EUNSUPPORTED, "carry slot size not a multiple of 4 bytes");
+    if ((rowB % 4) || (rowx % 4)) return fail(M3_EUNSUPPORTED, "carry row size not a multiple of 4 bytes");
 
     st->h = h_buf;
     st->carry_B = carry_B_buf;
@@ -306,17 +305,15 @@ m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t
     if (b == 0) return M3_OK;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    const int slot = int((t0 + 1) & 1);  // slot holding token t0 - 1
     hipError_t e = hipSuccess;
     if (h0 != h_buf)
         e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(h_buf), reinterpret_cast<const uint32_t*>(h0),
                                     int64_t(hbytes / 4), hs);
+    // every head gets its own copy of its group's B rows; x is per head already
     if (e == hipSuccess)
-        e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(static_cast<char*>(carry_B_buf) + slot * cb),
-                                    reinterpret_cast<const uint32_t*>(B_last), int64_t(cb / 4), hs);
+        e = m3::launch_carry_init(carry_B_buf, B_last, b, dims->heads, dims->groups, int64_t(rowB), hs);
     if (e == hipSuccess)
-        e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(static_cast<char*>(carry_x_buf) + slot * cx),
-                                    reinterpret_cast<const uint32_t*>(x_last), int64_t(cx / 4), hs);
+        e = m3::launch_carry_init(carry_x_buf, x_last, b, dims->heads, dims->heads, int64_t(rowx), hs);
     if (e != hipSuccess) return fail(M3_EHIP, "state init failed: %s", hipGetErrorString(e));
     return M3_OK;
 }
@@ -353,12 +350,12 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
                             rng("lambda_t", lambda_t, size_t(b) * H * 4),
                             rng("B_t", B_t, size_t(b) * G * R * N * es), rng("C_t", C_t, size_t(b) * G * R * N * es),
                             rng("state h", st->h, size_t(b) * H * N * P * 4),
-                            rng("state carry_B", st->carry_B, 2 * size_t(b) * G * R * N * es),
-                            rng("state carry_x", st->carry_x, 2 * size_t(b) * H * R * P * es)};
+                            rng("state carry_B", st->carry_B, size_t(b) * H * R * N * es),
+                            rng("state carry_x", st->carry_x, size_t(b) * H * R * P * es)};
     for (const Range& r : others)
         if (overlaps(ry, r)) return fail(M3_EINVAL, "y_t overlaps %s", r.name);
 
-    m3::DecodeArgs a{st->h, st->carry_B, st->carry_x, int32_t((st->t + 1) & 1), x_t, dt_t, A, omega,
+    m3::DecodeArgs a{st->h, st->carry_B, st->carry_x, x_t, dt_t, A, omega,
                      lambda_t, B_t, C_t, D, y_t, b, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R,
                      st->io_dtype, reinterpret_cast<hipStream_t>(stream)};
     hipError_t e = m3::launch_decode(a);

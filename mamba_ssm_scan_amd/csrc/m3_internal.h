@@ -33,9 +33,8 @@ struct PrefillArgs {
 
 struct DecodeArgs {
     float* h;
-    void* carry_B;         // [2][b][G][R][N]
-    void* carry_x;         // [2][b][H][R][P]
-    int32_t rd_slot;       // slot holding the previous token
+    void* carry_B;         // [b][H][R][N]: each head's copy of the previous token's B rows
+    void* carry_x;         // [b][H][R][P]
     const void* x;
     const float* dt;
     const float* A;
@@ -145,6 +144,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a);
 bool ws4_supported(const PrefillArgs& a);
 hipError_t launch_prefill_ws4(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+// carry[b][h] = src[b][h / (H / G)], rows of row_bytes (a multiple of 4), or zero when src is NULL
+hipError_t launch_carry_init(void* carry, const void* src, int64_t b, int H, int G, int64_t row_bytes,
+                             hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 // dst[i] = src ? src[i] : 0 for n 32-bit words (a kernel, so it is safe under graph capture)

@@ -179,9 +179,10 @@ def test_decode_argument_errors(lib):
 
 
 def test_carry_bytes(lib):
+    # one copy of the previous token's rows per head: B [b][H][R][N], x [b][H][R][P]
     d = _dims(b=3, H=4, G=2, P=8, N=16)
-    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 0) == 2 * 3 * 2 * 2 * 16 * 2
-    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 1) == 2 * 3 * 4 * 2 * 8 * 2
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 0) == 3 * 4 * 2 * 16 * 2
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 1) == 3 * 4 * 2 * 8 * 2
 
 
 def test_plan_segments_for_few_heads(lib):

@@ -13,7 +13,9 @@ look-back of the segmented prefill).
 import pytest
 import torch
 
+import oracle
 from mamba_ssm_scan_amd import binding, inputs
+from tests.util import TOL, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -105,7 +107,7 @@ def test_decode_steps_replay():
     reset()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        calls()  # an even number of steps: the carry slots end where they started
+        calls()
     for rep in range(3):
         reset()
         ys.zero_()
@@ -115,3 +117,43 @@ def test_decode_steps_replay():
         assert torch.equal(ys, y_ref), f"replay {rep}: y differs"
         assert torch.equal(st.h, h_ref), f"replay {rep}: state differs"
     assert st.t == t_after + steps  # the host counter advanced once, at capture
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_decode_odd_graph_replays_continue(R):
+    """A captured graph of an odd number of steps (5), replayed twice back to back
+    with nothing reset in between, continues the sequence: the 10 outputs and the
+    final state equal the oracle over the 5 tokens fed twice. Each step reads
+    only device buffers (the previous token's rows are each head's own carry),
+    so the replays do not depend on how many steps were captured."""
+    print(f"case odd graph (5 steps, R {R}) replayed twice", flush=True)
+    b, H, G, P, N, steps = 2, 4, 1, 64, 128, 5
+    di = {k: (v.cuda() if isinstance(v, torch.Tensor) else v)
+          for k, v in inputs.decode_inputs(3, steps, device="cpu", rank=R, batch=b).items()}
+    Hs = slice(0, H)
+    x = di["x"][:, :, Hs].contiguous()
+    dtv, lamv = di["dt"][:, :, Hs].contiguous(), di["lam"][:, :, Hs].contiguous()
+    A, om, D = di["A"][Hs].contiguous(), di["omega"][Hs].contiguous(), di["D"][Hs].contiguous()
+    h0 = di["h0"][:, Hs].contiguous()
+    Bv, Cv = di["B"].contiguous(), di["C"].contiguous()
+    ys = torch.empty_like(x)
+    st = binding.DecodeState(b, H, G, P, N, R, io_dtype=torch.bfloat16, h0=h0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(steps):
+            st.step(x[t], dtv[t], A, om, lamv[t], Bv[t], Cv[t], D, y_t=ys[t])
+    outs = []
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        outs.append(ys.clone())
+    # oracle over the 10 tokens (the 5 fed twice), batch-major
+    twice = lambda t: torch.cat([t, t], 0).transpose(0, 1).contiguous().cpu()
+    prob = {"x": twice(x), "B": twice(Bv), "C": twice(Cv), "dt": twice(dtv), "lam": twice(lamv),
+            "A": A.cpu(), "omega": om.cpu(), "D": D.cpu(), "h0": h0.cpu(), "R": R, "io_dtype": "bf16",
+            "carry_B": None, "carry_x": None}
+    y_ref, h_ref = oracle.scan(prob)
+    y = torch.cat(outs, 0).transpose(0, 1).contiguous()
+    assert_close(y, y_ref, TOL["bf16"], "y over both replays")
+    assert_close(st.h, h_ref, TOL["bf16"], "state after both replays")
