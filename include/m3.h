@@ -60,7 +60,8 @@ typedef enum m3_status {
     M3_EALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
     M3_EUNSUPPORTED = 5, /* valid but not implemented (chunk above 4096) */
     M3_EHIP = 6,         /* a HIP runtime call or kernel launch failed */
-    M3_EWORKSPACE = 7    /* workspace missing or smaller than m3_prefill_workspace_size() */
+    M3_EWORKSPACE = 7,   /* workspace missing or smaller than m3_prefill_workspace_size() */
+    M3_ELOOKBACK = 8     /* (m3_prefill_check) a look-back wait of the last call gave up: its outputs are not valid */
 } m3_status;
 
 /* Problem sizes. seqlen is ignored by the decode calls. */
@@ -131,6 +132,26 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
 
 /* Workspace bytes m3_prefill needs for these sizes (0 on invalid sizes). Host only. */
 size_t m3_prefill_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype);
+
+/*
+ * m3_prefill_check -- did the last m3_prefill call on this workspace complete its
+ * sequence-segment hand-offs?
+ *
+ * When the plan splits each sequence into segments (m3_plan.segments > 1), a
+ * segment waits for its predecessors' end states (a decoupled look-back). A
+ * predecessor always holds an earlier ticket and is running or done, so the wait
+ * ends; it is bounded all the same (about a second of polling), and a wait that
+ * gives up sets an error flag in the workspace and lets the call finish with
+ * invalid outputs. This call synchronises `stream`, reads that flag and returns
+ * M3_ELOOKBACK if it is set, M3_OK otherwise (at once, with no HIP call, when the
+ * plan has one segment). workspace, workspace_bytes: as passed to m3_prefill;
+ * NULL checks the fixed scratch of the last m3_prefill_noalloc call on the
+ * current device. The environment variable M3_LOOKBACK_SPIN_LIMIT (polls, read
+ * by each m3_prefill call) overrides the bound; 0 makes every wait give up at
+ * once, for testing this report.
+ */
+m3_status m3_prefill_check(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype,
+                           const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * m3_prefill_noalloc -- m3_prefill for callers that cannot allocate device

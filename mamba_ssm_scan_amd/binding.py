@@ -19,14 +19,14 @@ LIB_PATH = os.path.join(HERE, "libm3.so")
 M3_F32, M3_BF16 = 0, 1
 M3_PATH_GENERIC, M3_PATH_MFMA, M3_PATH_SCAN = 0, 1, 2
 STATUS = {0: "M3_OK", 1: "M3_EINVAL", 2: "M3_ESHAPE", 3: "M3_EDTYPE", 4: "M3_EALIGN",
-          5: "M3_EUNSUPPORTED", 6: "M3_EHIP", 7: "M3_EWORKSPACE"}
+          5: "M3_EUNSUPPORTED", 6: "M3_EHIP", 7: "M3_EWORKSPACE", 8: "M3_ELOOKBACK"}
 
 # every symbol include/m3.h declares
 EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_decode_carry_bytes",
            "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_prefill_backward",
            "m3_prefill_backward_workspace_size", "m3_mixer_create", "m3_mixer_destroy", "m3_mixer_workspace_size",
            "m3_mixer_prefill", "m3_mixer_decode_step", "m3_status_string", "m3_last_error", "m3_abi_version",
-           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes"]
+           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes", "m3_prefill_check"]
 
 
 class M3Dims(ctypes.Structure):
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH):
     lib.m3_prefill.restype = ctypes.c_int
     lib.m3_prefill_noalloc.argtypes = [vp] * 8 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp]
     lib.m3_prefill_noalloc.restype = ctypes.c_int
+    lib.m3_prefill_check.argtypes = [dims_p, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.m3_prefill_check.restype = ctypes.c_int
     lib.m3_noalloc_scratch_bytes.argtypes = []
     lib.m3_noalloc_scratch_bytes.restype = sz
     lib.m3_prefill_workspace_size.argtypes = [dims_p, i32, i32, ctypes.c_int]

@@ -165,6 +165,7 @@ const char* m3_status_string(m3_status s) {
         case M3_EUNSUPPORTED: return "unsupported configuration";
         case M3_EHIP: return "HIP runtime error";
         case M3_EWORKSPACE: return "workspace missing or too small";
+        case M3_ELOOKBACK: return "a sequence-segment look-back gave up; outputs not valid";
     }
     return "unknown status";
 }
@@ -179,6 +180,33 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, 
     m3_plan p;
     if (make_plan(dims, R, chunk, io_dtype, &p) != M3_OK) return 0;
     return p.workspace_bytes;
+}
+
+m3_status m3_prefill_check(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype,
+                           const void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    m3_plan plan;
+    m3_status s = make_plan(dims, R, chunk, io_dtype, &plan);
+    if (s != M3_OK) return s;
+    if (plan.segments <= 1 || dims->batch == 0 || dims->seqlen == 0) return M3_OK;
+    const void* ws = workspace;
+    if (!ws) {
+        void* p = nullptr;
+        if ((s = m3::noalloc_scratch(&p)) != M3_OK) return s;
+        ws = p;
+    } else if (workspace_bytes < plan.workspace_bytes) {
+        return fail(M3_EWORKSPACE, "workspace %zu bytes < %zu of this plan", workspace_bytes, plan.workspace_bytes);
+    }
+    const m3::PrefillWorkspace w = m3::prefill_workspace_layout(dims->batch, dims->seqlen, dims->heads,
+                                                                dims->headdim, dims->dstate, R, plan.segments,
+                                                                plan.path);
+    uint32_t flag = 0;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(&flag, static_cast<const char*>(ws) + w.ctrl_off + 4, 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(M3_EHIP, "reading the look-back flag failed: %s", hipGetErrorString(e));
+    if (flag) return fail(M3_ELOOKBACK, "a look-back wait of the last call on this workspace gave up");
+    return M3_OK;
 }
 
 m3_status m3_prefill(const void* x, const float* dt, const float* A, const float* omega,

@@ -126,6 +126,10 @@ PrefillWorkspace prefill_workspace_layout(int64_t b, int64_t L, int32_t H, int32
                                           int32_t segments, int32_t path);
 
 bool mfma_path_supported(int32_t P, int32_t N, int32_t R, int32_t chunk, m3_dtype io);
+// polls of a look-back wait before it gives up (about a second; a wait normally ends in microseconds)
+constexpr long kLookbackSpinLimit = 1L << 24;
+// device address of m3_prefill_noalloc's scratch on the current device
+m3_status noalloc_scratch(void** ptr);
 // the MFMA path splits the sequence into segments (look-back) at these ranks
 bool mfma_segments_supported(int32_t R, int32_t N, int32_t P);
 constexpr int32_t kMfmaMaxN = 512;   // largest N of the chunked path (passes of 128 rows)

@@ -174,8 +174,8 @@ struct SegArgs {
     float* agg;
     float* incl;
     double* tr;
+    long spin_limit;  // polls before a look-back wait gives up (0: give up at once)
 };
-constexpr long kSpinLimit = 1L << 24;
 
 // The state map of a stretch with total step T: pair k turned by omega_k T and
 // scaled by e^{A T}; om_rev = omega_k / 2 pi of the lane's two pairs.

@@ -22,8 +22,10 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void* g_ptr[kMaxDevices] = {};
 
+}  // namespace
+
 // device address of this device's copy of the scratch array (looked up once)
-m3_status scratch_ptr(void** out) {
+m3_status m3::noalloc_scratch(void** out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return m3::set_error(M3_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
@@ -41,8 +43,6 @@ m3_status scratch_ptr(void** out) {
     return M3_OK;
 }
 
-}  // namespace
-
 extern "C" size_t m3_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" m3_status m3_prefill_noalloc(const void* x, const float* dt, const float* A, const float* omega,
@@ -59,7 +59,7 @@ extern "C" m3_status m3_prefill_noalloc(const void* x, const float* dt, const fl
                              plan.workspace_bytes, kScratchBytes);
     void* ws = nullptr;
     if (plan.workspace_bytes > 0 && dims->batch > 0 && dims->seqlen > 0) {
-        if ((s = scratch_ptr(&ws)) != M3_OK) return s;
+        if ((s = m3::noalloc_scratch(&ws)) != M3_OK) return s;
     }
     return m3_prefill(x, dt, A, omega, lambda, B, C, D, R, chunk, h0, y, h_out, dims, io_dtype, carry_B, carry_x,
                       ws, ws ? kScratchBytes : 0, stream);

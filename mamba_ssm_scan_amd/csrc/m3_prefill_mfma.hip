@@ -37,6 +37,7 @@
 // each (token, pair) angle is evaluated once: the thread that stages a token's
 // B rows also turns its C rows (into LDS when they fit, R <= 2), and at R = 4
 // the four lanes holding one token's C rows share angles through DPP.
+#include <cstdlib>
 #include <type_traits>
 #include "m3_device.h"
 #include "m3_internal.h"
@@ -652,16 +653,20 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
             for (int j = seg - 1; j >= 0; --j) {
                 const int64_t bj = bh * sa.nseg + j;
                 if (tid == 0) {
-                    unsigned f;
+                    // A predecessor holds a lower ticket, so it is running or done and
+                    // this wait ends; the bound guards against a hang all the same.
+                    // Giving up sets the workspace's error flag (m3_prefill_check
+                    // reports it); the outputs of this call are then not valid.
+                    unsigned f = 0u;
                     long spins = 0;
-                    while ((f = __hip_atomic_load(&sa.ctrl[2 + bj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-                           0u) {
+                    while (sa.spin_limit > 0 && (f = __hip_atomic_load(&sa.ctrl[2 + bj], __ATOMIC_RELAXED,
+                                                                        __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
                         __builtin_amdgcn_s_sleep(2);
-                        if (++spins > kSpinLimit) {
-                            __hip_atomic_store(&sa.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            f = 2u;
-                            break;
-                        }
+                        if (++spins > sa.spin_limit) break;
+                    }
+                    if (f == 0u) {
+                        __hip_atomic_store(&sa.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        f = 2u;
                     }
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                     sFlag = f;
@@ -1275,7 +1280,10 @@ hipError_t launch_ws_r1(const PrefillArgs& a, const PassArgs& pa, bool gen) {
 template <int R, int NW>
 hipError_t launch_r(const PrefillArgs& a, const PassArgs& pa, bool gen) {
     const int64_t nbh = a.b * a.H;
-    SegArgs sa{a.plan.segments, a.plan.chunks_per_segment, nullptr, nullptr, nullptr, nullptr};
+    SegArgs sa{a.plan.segments, a.plan.chunks_per_segment, nullptr, nullptr, nullptr, nullptr, kLookbackSpinLimit};
+    // M3_LOOKBACK_SPIN_LIMIT (polls, >= 0) overrides the bound: 0 makes every wait
+    // give up at once, which exercises the error report
+    if (const char* env = getenv("M3_LOOKBACK_SPIN_LIMIT")) sa.spin_limit = atol(env) > 0 ? atol(env) : 0;
     if (sa.nseg > 1) {
         if (pa.ym != 0) return hipErrorInvalidValue;  // segments only in a single row pass
         const PrefillWorkspace w =

@@ -149,6 +149,22 @@ def test_noalloc_rejects_before_any_launch(lib):
     assert "scratch" in lib.m3_last_error().decode()
 
 
+def test_prefill_check_without_segments_needs_no_gpu(lib):
+    """m3_prefill_check returns M3_OK at once (no HIP call) when the plan has one segment,
+    and rejects bad sizes like the other entry points."""
+    d = bd.dims(4, 2048, 64, 1, 64, 128)
+    assert bd.plan(d, 4, 64, bd.M3_BF16).segments == 1
+    assert lib.m3_prefill_check(ctypes.byref(d), 4, 64, bd.M3_BF16, None, 0, None) == 0
+    assert lib.m3_prefill_check(ctypes.byref(_dims(N=15)), 1, 64, bd.M3_BF16, None, 0, None) == 1
+    assert lib.m3_status_string(8) == b"a sequence-segment look-back gave up; outputs not valid"
+    # a segmented plan with a workspace smaller than the plan's is refused before any HIP call
+    d4 = bd.dims(1, 32768, 64, 1, 64, 128)
+    p4 = bd.plan(d4, 4, 64, bd.M3_BF16)
+    assert p4.segments > 1
+    assert lib.m3_prefill_check(ctypes.byref(d4), 4, 64, bd.M3_BF16, ctypes.c_void_p(FAKE),
+                                p4.workspace_bytes - 1, None) == 7
+
+
 def test_prefill_empty_batch_is_a_no_op(lib):
     # b = 0: valid, nothing to launch
     assert _call(lib, _dims(b=0))[0] == 0
