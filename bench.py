@@ -2,13 +2,16 @@
 
 One step = one m3_prefill call over the SISO prefill workload (batch 4, 64
 heads, P 64, N 128, 2048 tokens, chunk 64, bf16 I/O, fp32 state, B/C shared by
-all heads). `value` is prefill tokens/s. The same run measures the decode step
-loop (batch 128, 64 heads, 1024 steps, R = 1 and R = 4), the MIMO R = 4 prefill
-and the long R = 4 prefill (32768 tokens) + 256 decode steps, and reports each
-against the HBM and bf16-MFMA roofline with algorithmic bytes / flops. The CPU
-oracle is timed on the host cores on a bounded sample of the prefill workload.
+all heads). `value` is prefill tokens/s (mean over the timed calls; median,
+p10 and p90 of the per-call event times are reported beside it). The same run
+measures the decode step loop (batch 128, 64 heads, 1024 steps, R = 1 and
+R = 4, with batch 64 and 256 beside it and a plain 1 GiB copy as the DRAM
+reference), the MIMO R = 4 prefill and the long R = 4 prefill (32768 tokens)
++ 256 decode steps, each against the HBM and bf16-MFMA roofline with
+algorithmic bytes / flops. The CPU oracle is timed on the host cores on a
+bounded sample of the SISO, MIMO, long prefill and both decode workloads.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -29,23 +32,45 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (VALU), TFLOP/s
 N_COPIES = 4                 # input copies rotated through so the 256 MB MALL cannot hold them
 
 # HBM traffic per launch measured with rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
-# KiB -> bytes; scale from a 1 GiB copy), valid only for the kernel source it was
-# taken on (sha256 prefix of the .hip file); see profiles/.
+# KiB -> bytes; the factors come from a 1 GiB copy), valid only for the kernel
+# sources it was taken on (sha256 prefix over the listed files, in order); the
+# summaries with the commands are in profiles/. None until a kernel is profiled.
 MEASURED_TRAFFIC = {
-    "prefill1": ("m3_prefill_mfma.hip", "feced3c57cb7a94b", (2.0 * 39159.083 + 73728.0) * 1024),
-    "prefill2": ("m3_prefill_mfma.hip", "feced3c57cb7a94b", (2.0 * 149720.042 + 270336.0) * 1024),
-    "decode1": ("m3_decode.hip", "2455ff93ed6fcc8d", (2.0 * 133301.623 + 264224.000) * 1024),
-    "decode4": ("m3_decode.hip", "2455ff93ed6fcc8d", (2.0 * 139049.603 + 270763.248) * 1024),
+    "prefill1": ("5ed749538c20f1ec", (2.0 * 39159.5 + 73728.0) * 1024),
+    "prefill2": ("9c5d768e2232a5df", (2.0 * 149809.3 + 270336.0) * 1024),
+    "long": ("5ed749538c20f1ec", (2.0 * 727753.8 + 1083772.1) * 1024),
+    "decode1": ("d300d65e7a08e628", (2.0 * 134152.2 + 266240.0) * 1024),
+    "decode4": ("d300d65e7a08e628", (2.0 * 142681.3 + 278683.1) * 1024),
+}
+
+
+def source_sha(files):
+    """sha256 prefix over the concatenated kernel sources (the key of a measured traffic figure)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mamba_ssm_scan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# kernel sources behind each timed workload (their sha256 prefix keys the traffic figures)
+SOURCES = {
+    "prefill1": ("m3_prefill_mfma.hip", "m3_mfma_common.h"),
+    "prefill2": ("m3_prefill_ws4.hip", "m3_mfma_common.h"),
+    "long": ("m3_prefill_mfma.hip", "m3_mfma_common.h"),
+    "decode1": ("m3_decode.hip",),
+    "decode4": ("m3_decode.hip",),
 }
 
 
 def measured_traffic(key):
-    """Counter-measured bytes per launch, or None if the kernel source changed since."""
-    import hashlib
-    src, sha, nbytes = MEASURED_TRAFFIC[key]
-    path = os.path.join(ROOT, "mamba_ssm_scan_amd", "csrc", src)
+    """Counter-measured bytes per launch, or None if the kernel source changed since (or never taken)."""
+    if key not in MEASURED_TRAFFIC:
+        return None
+    sha, nbytes = MEASURED_TRAFFIC[key]
     try:
-        cur = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+        cur = source_sha(SOURCES[key])
     except OSError:
         return None
     return nbytes if cur == sha else None
@@ -83,6 +108,46 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+def time_calls(run, steps, warmup):
+    """`warmup` untimed calls of run(k), then two timed passes of `steps` calls each.
+
+    Pass 1 (the throughput figure): the calls back to back between two HIP
+    events, with the device synchronised on both sides; mean = elapsed / steps.
+    Pass 2 (the spread): an event before the first call and after every call,
+    giving per-call times (median, p10, p90). An event between two calls keeps
+    the next launch from overlapping the previous one's tail, so pass 2's times
+    carry that gap (a few microseconds) on top of pass 1's mean. All events are
+    recorded on torch's current stream, the stream the library launches on.
+    """
+    import numpy as np
+    import torch
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for k in range(steps):
+        run(warmup + k)
+    e1.record()
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for k in range(steps):
+        run(warmup + steps + k)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
+    p10, p50, p90 = np.percentile(per, [10, 50, 90])
+    return {"mean": mean, "median": float(p50), "p10": float(p10), "p90": float(p90), "n": steps}
+
+
+def _pct(t, scale=1.0, unit="ms"):
+    """median / p10 / p90 of a time_calls result (its per-call pass), scaled (e.g. per step of a loop)."""
+    return {f"median_{unit}": t["median"] * scale, f"p10_{unit}": t["p10"] * scale,
+            f"p90_{unit}": t["p90"] * scale, "timed_calls": t["n"]}
+
+
 def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, rank=None, headdim=None):
     """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
 
@@ -114,16 +179,8 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
         binding.prefill(p["x"], p["dt"], p["A"], None if no_om else p["omega"], None if no_lam else p["lam"],
                         p["B"], p["C"], p["D"], w.rank, w.chunk, y=y, h_out=h, workspace=ws)
 
-    for k in range(warmup):
-        run(k)
-    torch.cuda.synchronize()
-    e0, e1 = _events()
-    e0.record()
-    for k in range(steps):
-        run(k)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    t = time_calls(run, steps, warmup)
+    ms = t["mean"]
     by = prefill_bytes(w.batch, w.seqlen, w.heads, G, w.headdim, w.dstate, w.rank)
     if no_lam:
         by -= w.batch * w.seqlen * w.heads * 4
@@ -135,10 +192,11 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
     r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
          "bytes": by, "flops": fl, "path": {binding.M3_PATH_MFMA: "mfma", binding.M3_PATH_SCAN: "scan"}.get(plan.path, "generic"),
-         "segments": plan.segments}
+         "segments": plan.segments, **_pct(t)}
     r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
     r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
-    log(f"prefill {name}: {ms * 1e3:.1f} us/call, {r['tokens_per_s'] / 1e6:.1f} M tok/s, "
+    log(f"prefill {name}: {ms * 1e3:.1f} us/call (median {t['median'] * 1e3:.1f}, p10 {t['p10'] * 1e3:.1f}, "
+        f"p90 {t['p90'] * 1e3:.1f}), {r['tokens_per_s'] / 1e6:.1f} M tok/s, "
         f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM), {r['mfma_tflops']:.1f} TFLOP/s "
         f"({100 * r['mfma_frac']:.1f}% bf16 MFMA)")
     return r
@@ -161,19 +219,14 @@ def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
         for (xp, dp, lp, bp, cp, yp) in ptrs:
             st.step_raw(xp, dp, A, om, lp, bp, cp, D, yp, sh)
 
-    loop()  # warm-up pass over all steps
-    torch.cuda.synchronize()
-    e0, e1 = _events()
-    e0.record()
-    for _ in range(reps):
-        loop()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / (reps * steps_total)
+    # one call = one loop over all the steps (the first is the warm-up pass)
+    t = time_calls(lambda k: loop(), reps, 1)
+    ms_step = t["mean"] / steps_total
     by = decode_bytes(b, w.heads, 1, w.headdim, w.dstate, R)
     r = {"workload": f"decode_b{b}_h{w.heads}_p{w.headdim}_n{w.dstate}_r{R}_{steps_total}_steps",
          "us_per_step": ms_step * 1e3, "steps_per_s": 1e3 / ms_step, "hbm_gbs": by / (ms_step * 1e-3) / 1e9,
-         "bytes_per_step": by}
+         "bytes_per_step": by, **_pct(t, 1e3 / steps_total, "us_per_step")}
+    r["timed_loops"] = r.pop("timed_calls")
     r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
     # the rank-R contractions of a step (u_t = B_t x_t^T and y_t = h_t^T C_t, 2 N P R flops each per
     # head; the previous token's u is the last step's): what the MFMA decode kernel puts on the matrix
@@ -181,13 +234,15 @@ def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
     fl = 4 * b * w.heads * w.dstate * w.headdim * R
     r["mfma_tflops"] = fl / (ms_step * 1e-3) / 1e12
     r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
-    log(f"decode R={R} b={b}: {ms_step * 1e3:.1f} us/step, {r['steps_per_s']:.0f} steps/s, "
+    log(f"decode R={R} b={b}: {ms_step * 1e3:.1f} us/step (median {r['median_us_per_step']:.1f}, p10 "
+        f"{r['p10_us_per_step']:.1f}, p90 {r['p90_us_per_step']:.1f} over {reps} loops of {steps_total}), "
+        f"{r['steps_per_s']:.0f} steps/s, "
         f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM), rank contractions "
         f"{r['mfma_tflops']:.1f} TFLOP/s ({100 * r['mfma_frac']:.2f}% of bf16 MFMA peak)")
     return r
 
 
-def bench_long(log):
+def bench_long(log, reps=20):
     """Workload 4: prefill of 32768 tokens (R = 4) then 256 decode steps, batch 1."""
     import torch
     from mamba_ssm_scan_amd import binding, inputs
@@ -204,17 +259,9 @@ def bench_long(log):
         binding.prefill(pre["x"], pre["dt"], pre["A"], pre["omega"], pre["lam"], pre["B"], pre["C"], pre["D"],
                         w.rank, w.chunk, y=y, h_out=h, workspace=ws)
 
-    for _ in range(2):
-        pf()
-    torch.cuda.synchronize()
+    tp = time_calls(lambda k: pf(), reps, 3)
+    ms = tp["mean"]
     e0, e1 = _events()
-    reps = 5
-    e0.record()
-    for _ in range(reps):
-        pf()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
     by = prefill_bytes(1, L, w.heads, 1, w.headdim, w.dstate, w.rank)
     fl = prefill_flops(1, L, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
     # decode handoff: 256 steps from the prefill's final state
@@ -255,8 +302,10 @@ def bench_long(log):
     torch.cuda.synchronize()
     gms = e0.elapsed_time(e1) / steps
     r = {"workload": w.name, "prefill_ms": ms, "prefill_tokens_per_s": L / (ms * 1e-3),
-         "prefill_hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+         "prefill_hbm_gbs": by / (ms * 1e-3) / 1e9, "prefill_mfma_tflops": fl / (ms * 1e-3) / 1e12,
+         "prefill_hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "prefill_bytes": by, "prefill_flops": fl,
          "prefill_mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "segments": plan.segments,
+         "prefill_timing": _pct(tp),
          "decode_us_per_step": dms * 1e3, "decode_steps_per_s": 1e3 / dms,
          "decode_graph_us_per_step": gms * 1e3, "decode_graph_steps_per_s": 1e3 / gms}
     log(f"long prefill {L} tokens R=4: {ms:.3f} ms, {r['prefill_tokens_per_s'] / 1e6:.1f} M tok/s "
@@ -446,62 +495,108 @@ def bench_prologue(log, steps=20, warmup=3, wid=2, tokens=None, copies=16):
     return r
 
 
-def copy_probe(log, nbytes=1 << 30):
-    """A plain device-to-device copy of known size (reference for the HBM byte counters)."""
+def copy_probe(log, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of known size: the DRAM rate a streaming kernel can reach
+    (2 GiB of traffic per call, 8x the 256 MB MALL), and the reference for the HBM byte counters."""
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = _events()
-    e0.record()
-    dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    log(f"copy {nbytes >> 20} MiB: {ms * 1e3:.1f} us, {2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s (read + write)")
+    t = time_calls(lambda k: dst.copy_(src), reps, 3)
+    gbs = 2 * nbytes / (t["median"] * 1e-3) / 1e9
+    log(f"copy {nbytes >> 20} MiB: {t['median'] * 1e3:.1f} us (median of {reps}), {gbs:.0f} GB/s (read + write)")
+    return {"bytes_moved": 2 * nbytes, "median_ms": t["median"], "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
-def cpu_baseline(log, budget_s=12.0, max_s=30.0):
-    """The oracle (fp64 C, OpenMP) on the host cores, on a bounded sample of the prefill workload.
-
-    The sample is the workload's heads in blocks (all batches, all tokens), taken
-    in order and repeated from the first head if the whole workload takes less
-    than `budget_s`; tokens/s is scaled by the fraction of heads processed.
-    """
+def _cpu_problem(p):
     import torch
+    return {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+
+
+def _oracle_loop(subs, budget_s, max_s, threads):
+    """oracle.scan over the sub-problems in order, cycling, until budget_s seconds of it.
+    Returns (calls, list of the sub-problem indices run, seconds)."""
+    import oracle
+    done, secs, k = [], 0.0, 0
+    while secs < budget_s and secs < max_s:
+        i = k % len(subs)
+        t0 = time.perf_counter()
+        oracle.scan(subs[i], nthreads=threads)
+        secs += time.perf_counter() - t0
+        done.append(i)
+        k += 1
+    return done, secs
+
+
+def cpu_baseline_prefill(log, wid, budget_s=8.0, max_s=30.0, block=None):
+    """The oracle (fp64 C, OpenMP over the (batch, head) walks) on the host cores, on a bounded
+    sample of a prefill workload: its heads in blocks (all batches, all tokens), in order and
+    cycling from the first block if the whole workload takes less than budget_s; tokens/s is
+    scaled by the fraction of the heads processed."""
     import oracle
     from mamba_ssm_scan_amd import inputs
-    w = inputs.WORKLOADS[1]
-    p = inputs.workload_prefill(1, device="cuda")
+    w = inputs.WORKLOADS[wid]
     threads = oracle.default_threads()
-    block = 8
-    subs = [{k: (v.cpu() if isinstance(v, torch.Tensor) else v)
-             for k, v in inputs.select_heads(p, range(h0, min(w.heads, h0 + block))).items()}
+    if wid == 4:
+        p = inputs.slice_tokens(inputs.long_sequence(4, device="cuda"), 0, w.seqlen)
+    else:
+        p = inputs.workload_prefill(wid, device="cuda")
+    block = block or max(1, min(w.heads, (threads + w.batch - 1) // w.batch if wid == 4 else 8))
+    subs = [_cpu_problem(inputs.select_heads(p, range(h0, min(w.heads, h0 + block))))
             for h0 in range(0, w.heads, block)]
-    heads_done, secs, k = 0, 0.0, 0
-    while secs < budget_s and secs < max_s:
-        sub = subs[k % len(subs)]
-        t0 = time.perf_counter()
-        oracle.scan(sub, nthreads=threads)
-        secs += time.perf_counter() - t0
-        heads_done += sub["A"].shape[0]
-        k += 1
+    del p
+    done, secs = _oracle_loop(subs, budget_s, max_s, threads)
+    heads_done = sum(subs[i]["A"].shape[0] for i in done)
     tok_s = w.batch * w.seqlen * (heads_done / w.heads) / secs
-    log(f"cpu oracle: {heads_done} head-walks of {w.heads} x {w.batch} batches x {w.seqlen} tokens in "
+    log(f"cpu oracle {w.name}: {heads_done} head-walks of {w.heads} x {w.batch} batches x {w.seqlen} tokens in "
         f"{secs:.1f} s on {threads} threads -> {tok_s:.0f} tokens/s")
     return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: {heads_done} (batch x {w.batch}) head walks of {w.seqlen} tokens "
+            "sample": f"{w.name}: {heads_done} (x {w.batch} batches) head walks of {w.seqlen} tokens "
                       f"(heads in blocks of {block}, cycling), fp64 sequential recurrence, {secs:.1f} s wall; "
                       f"tokens/s = batch*seqlen*heads_done/heads/seconds"}
+
+
+def cpu_baseline_decode(log, R, steps=1024, budget_s=8.0, max_s=30.0, block=4):
+    """The oracle on a bounded sample of the batch-128 decode loop: all 1024 steps of every head
+    of `block` sequences at a time (the decode loop is the recurrence over the step axis, from
+    h0 with zero carries), cycling over the blocks; steps/s is scaled from the fraction of the
+    batch processed (steps / (seconds * batch / sequences done))."""
+    import oracle
+    from mamba_ssm_scan_amd import inputs
+    w = inputs.WORKLOADS[3]
+    threads = oracle.default_threads()
+    di = inputs.decode_inputs(3, steps, device="cuda", rank=R)
+    subs = []
+    for b0 in range(0, w.batch, block):
+        sl = slice(b0, b0 + block)
+        # step-major [steps][b]... -> the prefill layout [b][steps]... (a transpose, no arithmetic)
+        sub = {k: di[k][:, sl].transpose(0, 1).contiguous() for k in ("x", "B", "C", "dt", "lam")}
+        sub.update(A=di["A"], omega=di["omega"], D=di["D"], h0=di["h0"][sl].contiguous())
+        subs.append(_cpu_problem(sub))
+        if len(subs) * block >= 32:  # the sample never needs more than 32 sequences
+            break
+    del di
+    done, secs = _oracle_loop(subs, budget_s, max_s, threads)
+    seqs = block * len(done)
+    steps_s = steps / (secs * w.batch / seqs)
+    log(f"cpu oracle decode R={R}: {seqs} sequences x {w.heads} heads x {steps} steps in {secs:.1f} s on "
+        f"{threads} threads -> {steps_s:.2f} batch-{w.batch} steps/s")
+    return {"value": steps_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"decode R {R}: {seqs} of {w.batch} sequences (blocks of {block}, all {w.heads} heads, "
+                      f"all {steps} steps, cycling over the first 32), fp64 sequential recurrence, {secs:.1f} s "
+                      f"wall; steps/s = steps / (seconds * {w.batch} / sequences done)"}
+
+
+def roofline(bound, achieved, peak, unit, traffic, kernel, per_launch, **extra):
+    """The bench line's roofline object for one workload's dominant kernel."""
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": traffic, "kernel": kernel, **per_launch, **extra}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy,prologue, "
                                                "prefill1_real/_euler/_real_euler: run just these (profiling runs); "
@@ -536,6 +631,8 @@ def main():
                 bench_prefill(1, args.steps, args.warmup, log, special=item[len("prefill1_"):])
             elif item in ("decode1", "decode4"):
                 bench_decode(int(item[-1]), 1024, 1, log)
+            elif item.startswith("decode") and "_b" in item:  # decode1_b256: R 1 at batch 256, 256 steps
+                bench_decode(int(item[6]), 256, 1, log, batch=int(item.split("_b")[1]))
             elif item == "long":
                 bench_long(log)
             elif item == "copy":
@@ -560,19 +657,41 @@ def main():
         "config": {"workload": head["workload"], "batch": 4, "seqlen": 2048, "heads": 64, "groups": 1,
                    "headdim": 64, "dstate": 128, "rank": 1, "chunk": 64, "state_dtype": "f32",
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["hbm_frac"], "traffic": measured_traffic("prefill1"),
-                     "kernel": "prefill_ws_r1_kernel", "bytes_per_launch": head["bytes"],
-                     "mfma": {"achieved": head["mfma_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": head["mfma_frac"], "flops_per_launch": head["flops"]}},
+        "timing": {k: head[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls")},
+        "roofline": roofline("hbm", head["hbm_gbs"], HBM_PEAK_GBS, "GB/s", measured_traffic("prefill1"),
+                             "prefill_ws_r1_kernel", {"bytes_per_launch": head["bytes"]},
+                             mfma={"achieved": head["mfma_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": head["mfma_frac"], "flops_per_launch": head["flops"]}),
     }
     if not args.quick:
-        out["decode"] = {f"r{R}": bench_decode(R, 1024, 3, log) for R in (1, 4)}
+        # the batch-128 decode loop (1024 steps, 20 timed loops) at R 1 and R 4: HBM-bound
+        kern = {1: "decode_rows_kernel", 4: "decode_mfma_kernel"}
+        out["decode"] = {}
         for R in (1, 4):
-            out["decode"][f"r{R}"]["traffic"] = measured_traffic(f"decode{R}")
-        out["prefill_mimo_r4"] = bench_prefill(2, args.steps, args.warmup, log)
-        out["prefill_mimo_r4"]["traffic"] = measured_traffic("prefill2")
-        out["long_prefill_decode"] = bench_long(log)
+            d = bench_decode(R, 1024, 20, log)
+            d["roofline"] = roofline("hbm", d["hbm_gbs"], HBM_PEAK_GBS, "GB/s", measured_traffic(f"decode{R}"),
+                                     kern[R], {"bytes_per_launch": d["bytes_per_step"]})
+            out["decode"][f"r{R}"] = d
+        # the same step at batch 64 and 256 (state 128 / 512 MiB against the 256 MB MALL), and a
+        # plain 1 GiB copy: the DRAM rate that bounds a stream larger than the MALL
+        out["decode_batch_sweep"] = {f"r{R}_b{b}": bench_decode(R, 256, 5, log, batch=b)
+                                     for R in (1, 4) for b in (64, 256)}
+        out["dram_copy"] = copy_probe(log)
+        # the MIMO R 4 prefill: at the ridge of the bf16 MFMA / HBM roofline
+        p2 = bench_prefill(2, args.steps, args.warmup, log)
+        p2["roofline"] = roofline("mfma", p2["mfma_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s",
+                                  measured_traffic("prefill2"), "prefill_ws4_kernel<4>",
+                                  {"flops_per_launch": p2["flops"]},
+                                  hbm={"achieved": p2["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": p2["hbm_frac"], "bytes_per_launch": p2["bytes"]})
+        out["prefill_mimo_r4"] = p2
+        lg = bench_long(log)
+        lg["roofline"] = roofline("mfma", lg["prefill_mfma_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s",
+                                  measured_traffic("long"), "prefill_mfma_kernel<4>",
+                                  {"flops_per_launch": lg["prefill_flops"]},
+                                  hbm={"achieved": lg["prefill_hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": lg["prefill_hbm_frac"], "bytes_per_launch": lg["prefill_bytes"]})
+        out["long_prefill_decode"] = lg
         # the pages' special cases on the same workload: omega = 0 (no rotation), lambda = 1 (Euler)
         out["prefill_special_cases"] = {sp: bench_prefill(1, args.steps, args.warmup, log, special=sp)
                                         for sp in ("real", "euler", "real_euler")}
@@ -581,8 +700,8 @@ def main():
                                           for w, wid in ((1, 1), (4, 2))}
         # larger state / rank on the same token shapes (N 256: the chunked kernels in two row passes;
         # R 8: the token-walk kernel)
-        out["prefill_larger_sizes"] = {"n256_r1": bench_prefill(1, 3, 1, log, dstate=256),
-                                       "n128_r8": bench_prefill(2, 3, 1, log, rank=8)}
+        out["prefill_larger_sizes"] = {"n256_r1": bench_prefill(1, 5, 1, log, dstate=256),
+                                       "n128_r8": bench_prefill(2, 5, 1, log, rank=8)}
         # half the state (N 64) on the same token shapes (the chunked kernels, rows zero-padded)
         out["prefill_smaller_state"] = {f"n64_r{R}": bench_prefill(wid, args.steps, args.warmup, log, dstate=64)
                                         for R, wid in ((1, 1), (4, 2))}
@@ -594,7 +713,12 @@ def main():
         out["prologue"] = {"prefill_r4": bench_prologue(log, args.steps, args.warmup),
                            "decode_step_b128": bench_prologue(log, args.steps, args.warmup, wid=3, tokens=(128,))}
     if not args.no_cpu and not args.quick:
-        out["cpu_baseline"] = cpu_baseline(log)
+        # the oracle on the host cores, on a bounded sample of each workload, next to its GPU figure
+        out["cpu_baseline"] = cpu_baseline_prefill(log, 1)
+        out["prefill_mimo_r4"]["cpu_baseline"] = cpu_baseline_prefill(log, 2)
+        out["long_prefill_decode"]["cpu_baseline"] = cpu_baseline_prefill(log, 4)
+        for R in (1, 4):
+            out["decode"][f"r{R}"]["cpu_baseline"] = cpu_baseline_decode(log, R)
     print(json.dumps(out), flush=True)
 
 

@@ -76,12 +76,9 @@ def test_scan_special_cases(drop):
     assert_close(h, h_ref, TOL["bf16"], "h_out")
 
 
-SAMPLE_HEADS = [0, 37, 63]
-
-
 @pytest.mark.parametrize("wid,dstate,rank", [(1, 256, None), (2, None, 8)])
 def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
-    """Workload 1's shape with N 256, workload 2's with R 8 (b 4, L 2048, H 64): oracle on 3 heads x all batches."""
+    """Workload 1's shape with N 256, workload 2's with R 8 (b 4, L 2048, H 64): the oracle runs every walk."""
     w = inputs.WORKLOADS[wid]
     N, R = dstate or w.dstate, rank or w.rank
     print(f"workload {wid} shape with N {N}, R {R}", flush=True)
@@ -90,12 +87,9 @@ def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
     assert _path(p, w.chunk) == (binding.M3_PATH_MFMA if R in (1, 2, 4) else binding.M3_PATH_SCAN)
     y, h = binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], R, w.chunk)
     torch.cuda.synchronize()
-    sub = to_host(inputs.select_heads(p, SAMPLE_HEADS))
-    y_ref, h_ref = oracle.scan(sub)
-    idx = torch.tensor(SAMPLE_HEADS, device="cuda")
-    assert_close(y.index_select(2, idx), y_ref, TOL["bf16"], "y")
-    assert_close(h.index_select(1, idx), h_ref, TOL["bf16"], "h_out")
-    assert torch.isfinite(y).all()
+    y_ref, h_ref = oracle.scan(to_host(p))
+    assert_close(y, y_ref, TOL["bf16"], "y, all heads and batches")
+    assert_close(h, h_ref, TOL["bf16"], "h_out, all heads and batches")
 
 
 DCASES = [

@@ -1,7 +1,8 @@
 """GPU parity of the bf16-MFMA chunked prefill: N = 128, P = 64 (below zero-padded, above in row / column passes), R in {1, 2, 4}.
 
 Small cases cover every chunk size class, ragged tails, groups, initial state and
-carry; full-size workloads compare sampled (batch, head) walks with the oracle.
+carry; full-size workloads compare every (batch, head) walk with the oracle
+(the decode workload: every head of 3 of its 128 sequences).
 Tolerance: max-relative error per (batch, head) slice <= 2e-2 (bf16 I/O, fp32 state).
 """
 import numpy as np
@@ -188,13 +189,11 @@ def test_mfma_chunk_sweep_agrees():
         assert_close(h, h_ref, TOL["bf16"], f"h chunk {Q}")
 
 
-SAMPLE_HEADS = [0, 21, 42, 63]
-
-
 @pytest.mark.parametrize("groups", [1, 64])
 @pytest.mark.parametrize("wid", [1, 2])
 def test_workload_full_size(wid, groups):
-    """Workloads 1 (R=1) and 2 (R=4) at full size, chunk 64; oracle on 4 heads x all batches.
+    """Workloads 1 (R=1) and 2 (R=4) at full size, chunk 64, in the launch bench.py
+    times; the oracle runs every (batch, head) walk (4 x 64 x 2048 tokens).
 
     groups 1 is the primary reading (B, C shared by all heads); groups 64 gives
     every head its own B, C (the secondary reading, 64x the B/C bytes).
@@ -205,16 +204,14 @@ def test_workload_full_size(wid, groups):
     assert _path(w.batch, w.seqlen, w.heads, groups, w.rank, w.chunk) == binding.M3_PATH_MFMA
     y, h = binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], w.rank, w.chunk)
     torch.cuda.synchronize()
-    sub = to_host(inputs.select_heads(p, SAMPLE_HEADS))
-    y_ref, h_ref = oracle.scan(sub)
-    idx = torch.tensor(SAMPLE_HEADS, device="cuda")
-    assert_close(y.index_select(2, idx), y_ref, TOL["bf16"], "y")
-    assert_close(h.index_select(1, idx), h_ref, TOL["bf16"], "h_out")
-    assert torch.isfinite(y).all()
+    y_ref, h_ref = oracle.scan(to_host(p))
+    assert_close(y, y_ref, TOL["bf16"], "y, all heads and batches")
+    assert_close(h, h_ref, TOL["bf16"], "h_out, all heads and batches")
 
 
 def test_workload4_prefill_then_decode():
-    """Workload 4: prefill of 32768 tokens (R=4), then 256 decode steps, against one 33024-token oracle run."""
+    """Workload 4: prefill of 32768 tokens (R=4), then 256 decode steps, against one
+    33024-token oracle run of every head."""
     w = inputs.WORKLOADS[4]
     _flush("workload 4: long prefill + decode handoff")
     p = inputs.long_sequence(4, device="cuda")
@@ -226,13 +223,11 @@ def test_workload4_prefill_then_decode():
                              B_last=p["B"][:, L - 1].contiguous(), x_last=p["x"][:, L - 1].contiguous(), t0=L)
     y2, st = run_decode(p, steps_from=L, state=st)
     assert st.t == L + w.decode_steps
-    heads = [5, 40]
-    sub = to_host(inputs.select_heads(p, heads))
-    y_ref, h_ref = oracle.scan(sub)
-    idx = torch.tensor(heads, device="cuda")
-    y = torch.cat([y1, y2], 1).index_select(2, idx)
-    assert_close(y, y_ref, TOL["bf16"], "y (prefill + decode)")
-    assert_close(st.h.index_select(1, idx), h_ref, TOL["bf16"], "final state")
+    torch.cuda.synchronize()
+    y_ref, h_ref = oracle.scan(to_host(p))
+    assert_close(y1, y_ref[:, :L], TOL["bf16"], "y prefill, all heads")
+    assert_close(y2, y_ref[:, L:], TOL["bf16"], "y decode, all heads")
+    assert_close(st.h, h_ref, TOL["bf16"], "final state, all heads")
 
 
 def test_mfma_long_siso_absolute_angle():
@@ -253,8 +248,8 @@ def test_mfma_long_siso_absolute_angle():
 @pytest.mark.parametrize("R", [1, 4])
 def test_workload3_decode_full_size(R):
     """Workload 3 at full size, as bench.py runs it: b 128, H 64, 1024 decode steps,
-    bf16 I/O from an fp32 state h0 ~ N(0, 0.1); the oracle runs 3 x 3 sampled
-    (batch, head) walks over all 1024 tokens."""
+    bf16 I/O from an fp32 state h0 ~ N(0, 0.1); the oracle runs every head of
+    3 of the 128 sequences over all 1024 steps."""
     w = inputs.WORKLOADS[3]
     steps = 1024
     _flush(f"workload 3 full size, R={R}")
@@ -263,16 +258,14 @@ def test_workload3_decode_full_size(R):
     ys = [st.step(di["x"][t], di["dt"][t], di["A"], di["omega"], di["lam"][t], di["B"][t], di["C"][t], di["D"])
           for t in range(steps)]
     torch.cuda.synchronize()
-    bs, hs = [0, 77, 127], [0, 31, 63]
-    bi, hi = torch.tensor(bs, device="cuda"), torch.tensor(hs, device="cuda")
+    bs = [0, 77, 127]
+    bi = torch.tensor(bs, device="cuda")
     sel = lambda t: t.index_select(1, bi).transpose(0, 1)      # [steps][b]... -> [b'][steps]...
-    sub = {"x": sel(di["x"]).index_select(2, hi), "B": sel(di["B"]), "C": sel(di["C"]),
-           "dt": sel(di["dt"]).index_select(2, hi), "lam": sel(di["lam"]).index_select(2, hi),
-           "A": di["A"][hi], "omega": di["omega"][hi], "D": di["D"][hi],
-           "h0": di["h0"].index_select(0, bi).index_select(1, hi), "R": R, "io_dtype": "bf16",
-           "carry_B": None, "carry_x": None}
+    sub = {"x": sel(di["x"]), "B": sel(di["B"]), "C": sel(di["C"]), "dt": sel(di["dt"]), "lam": sel(di["lam"]),
+           "A": di["A"], "omega": di["omega"], "D": di["D"], "h0": di["h0"].index_select(0, bi), "R": R,
+           "io_dtype": "bf16", "carry_B": None, "carry_x": None}
     y_ref, h_ref = oracle.scan(to_host({k: (v.contiguous() if isinstance(v, torch.Tensor) else v)
                                         for k, v in sub.items()}))
-    y = torch.stack(ys, 1).index_select(0, bi).index_select(2, hi)
-    assert_close(y, y_ref, TOL["bf16"], "y (1024 steps)")
-    assert_close(st.h.index_select(0, bi).index_select(1, hi), h_ref, TOL["bf16"], "state after 1024 steps")
+    y = torch.stack(ys, 1).index_select(0, bi)
+    assert_close(y, y_ref, TOL["bf16"], "y (1024 steps), all heads of 3 sequences")
+    assert_close(st.h.index_select(0, bi), h_ref, TOL["bf16"], "state after 1024 steps, all heads of 3 sequences")

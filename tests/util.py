@@ -6,6 +6,10 @@ import oracle
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}   # max-relative error per (batch, head) slice
 
+# every comparison made in this process: (test id, what, error, tolerance); the
+# session summary prints the full-size ones and the worst error / tolerance ratio
+ERRORS = []
+
 
 def to_dev(p, device="cuda"):
     return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
@@ -29,7 +33,9 @@ def gpu_prefill(p, chunk, **kw):
 
 
 def assert_close(got, ref, tol, what=""):
+    import os
     err = oracle.max_rel_err(f64(got) if isinstance(got, torch.Tensor) else got, ref)
     print(f"  {what}: max-rel error {err:.3e} (tol {tol:.0e})", flush=True)
+    ERRORS.append((os.environ.get("PYTEST_CURRENT_TEST", "?").split(" (")[0], what, float(err), float(tol)))
     assert np.isfinite(err) and err <= tol, f"{what}: max-rel error {err:.3e} > {tol:.1e}"
     return err
