@@ -187,13 +187,20 @@ m3_status m3_prefill_plan(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtyp
  * Decode state: the fp32 state plus the previous token's (B, x), which the
  * trapezoid rule needs for the next step. Buffers are caller-owned device memory:
  *   h        [b][H][N][P] fp32
- *   carry_B  [b][H][R][N] io dtype  (each head's copy of its group's previous B rows)
+ *   carry_B  m3_decode_carry_bytes(.., 0) bytes, opaque: two slots [2][b][G][R][N]
+ *            of the group's previous B rows (io dtype), then one 32-bit slot
+ *            parity word per (b, h) at the next 16-byte boundary
  *   carry_x  [b][H][R][P] io dtype
- * Everything a step needs lives in these device buffers: the kernels read no
- * host-side counter, so a step captured in a HIP graph, and a graph of any
- * number of steps, replays correctly. t counts the tokens consumed by the
- * calls made on this struct (a prefill of L tokens hands over t = L); it is
- * bookkeeping for the caller (graph replays do not advance it).
+ * Everything a step needs lives in these device buffers: a step reads B_prev
+ * from the slot its parity word names and writes B_t into the other one, so
+ * the kernels read no host-side counter for their results, and a step captured
+ * in a HIP graph, and a graph of any number of steps, replays correctly. t
+ * counts the tokens consumed by the calls made on this struct (a prefill of L
+ * tokens hands over t = L); it is bookkeeping for the caller (graph replays do
+ * not advance it). Its parity also picks the order in which a step walks the
+ * (b, h) workgroups (backwards on odd t, so the states written last are read
+ * first while the memory-side cache still holds them): a speed hint that does
+ * not change any result.
  */
 typedef struct m3_decode_state {
     float* h;
@@ -212,7 +219,7 @@ size_t m3_decode_carry_bytes(const m3_dims* dims, int32_t R, m3_dtype io_dtype, 
  * m3_decode_state_init -- bind caller buffers and set the starting point.
  *
  * Copies h0 (or zeros) into h_buf and (B_last, x_last) (or zeros) into the
- * carry (B_last's rows to every head of their group), on `stream`. B_last [b][G][R][N] and x_last
+ * carry (B_last into slot 0, every parity word to 0), on `stream`. B_last [b][G][R][N] and x_last
  * [b][H][R][P] are the last token already consumed (e.g. the prefill's last
  * token); both or neither. t0 >= 0 is the number of tokens already consumed.
  * h0 may equal h_buf (then it is left in place).

@@ -222,7 +222,8 @@ def prefill(x, dt, A, omega, lam, B, C, D, R: int, chunk: int, h0=None, *, carry
 
 
 class DecodeState:
-    """Caller-owned decode state: fp32 h plus each head's carry (the previous token's B and x rows), bound to libm3."""
+    """Caller-owned decode state: fp32 h plus the carry (the previous token's B rows per group and x rows per
+    head), bound to libm3."""
 
     def __init__(self, batch, heads, groups, headdim, dstate, R, io_dtype=torch.bfloat16, device="cuda",
                  h0=None, B_last=None, x_last=None, t0: int = 0, stream=None):
@@ -230,7 +231,11 @@ class DecodeState:
         self.R = R
         self.io_dtype = io_dtype
         self.h = torch.empty((batch, heads, dstate, headdim), dtype=torch.float32, device=device)
-        self.carry_B = torch.empty((batch, heads, R, dstate), dtype=io_dtype, device=device)
+        # carry_B is opaque: two slots of the group's previous B rows and a parity word per head
+        nB = load().m3_decode_carry_bytes(ctypes.byref(self.dims), R, _io_code(io_dtype), 0)
+        if nB == 0 and batch > 0:
+            raise M3Error(1, "invalid decode state sizes")
+        self.carry_B = torch.empty((max(nB, 16),), dtype=torch.uint8, device=device)
         self.carry_x = torch.empty((batch, heads, R, headdim), dtype=io_dtype, device=device)
         h0 = _need(h0, "h0", torch.float32, self.h.shape)
         B_last = _need(B_last, "B_last", io_dtype, (batch, groups, R, dstate))

@@ -10,11 +10,18 @@
 //
 // The fp32 state is read and written once (the step is bound by that traffic:
 // "Mamba-3架构技术解析：新一代语言建模的范式转移" §2.3 on decode being state-I/O
-// bound). Every head keeps its own copy of the previous token's (B, x) rows:
-// the workgroup of (b, h) reads its carry into LDS and, after a barrier,
-// overwrites it with the current token's rows. No other workgroup touches it,
-// so the step needs no slot parity from the host and a captured graph of any
-// number of steps replays correctly.
+// bound). The previous token's rows: x per head (the workgroup of (b, h) reads
+// its carry into LDS and, after a barrier, overwrites it with the current
+// token's rows); B once per group, in two slots. Each head keeps a parity word:
+// a step reads B_prev from the slot its parity names, the group's first head
+// writes B_t into the other slot, and the head flips its parity. No slot is
+// read and written in the same launch, and everything lives in device memory,
+// so a captured graph of any number of steps replays correctly.
+//
+// Block order: `rev` (the host's step parity) walks the (b, h) workgroups
+// backwards on every other step, so a step first reads the states the previous
+// step wrote last, which the 256 MB memory-side cache (MALL) still holds when
+// the state is about its size. A hint only: results do not depend on it.
 #include <type_traits>
 
 #include "m3_device.h"
@@ -50,7 +57,7 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
 template <typename T, int R, int NTH, int N, int P>
 __global__ void __launch_bounds__(NTH)
 decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x,
-                       const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+                       unsigned* __restrict__ par, int rev, const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                        const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                        const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
                        int G) {
@@ -63,11 +70,12 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
     __shared__ float red[NTH / 64][R][P];
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = rev ? int64_t(gridDim.x) - 1 - blockIdx.x : int64_t(blockIdx.x);
     const int64_t b = bh / H;
     const int h = int(bh % H);
     const int g = h / (H / G);
     const int64_t bg = b * G + g;
+    const unsigned pr = par[bh] & 1u;  // slot of B_prev
     float* hs = hstate + bh * (N * P);
     const int q = tid % QP, kk = tid / QP;
 
@@ -81,7 +89,7 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
 
     const T* Bt = B + bg * (R * N);
     const T* Ct = C + bg * (R * N);
-    const T* Bp = carry_B + bh * (R * N);
+    const T* Bp = carry_B + (int64_t(pr) * nb * G + bg) * (R * N);
     const T* xt = x + bh * (R * P);
     const T* xp = carry_x + bh * (R * P);
     for (int e = tid; e < R * N; e += NTH) {
@@ -160,7 +168,9 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
     // this token becomes the carry of the next step (the carry was read into
     // LDS before the barrier above)
     for (int e = tid; e < R * P; e += NTH) carry_x[bh * (R * P) + e] = xt[e];
-    for (int e = tid; e < R * N; e += NTH) carry_B[bh * (R * N) + e] = Bt[e];
+    if (h % (H / G) == 0)
+        for (int e = tid; e < R * N; e += NTH) carry_B[(int64_t(pr ^ 1u) * nb * G + bg) * (R * N) + e] = Bt[e];
+    if (tid == 0) par[bh] = pr ^ 1u;
 }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -198,7 +208,7 @@ __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 
 template <int R, int N>
 __global__ void __launch_bounds__(256)
 decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
-                   const bf16_t* __restrict__ x, const float* __restrict__ dt,
+                   unsigned* __restrict__ par, int rev, const bf16_t* __restrict__ x, const float* __restrict__ dt,
                    const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
@@ -215,10 +225,11 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = rev ? int64_t(gridDim.x) - 1 - blockIdx.x : int64_t(blockIdx.x);
     const int64_t b = bh / H;
     const int h = int(bh % H);
     const int64_t bg = b * G + h / (H / G);
+    const unsigned pr = par[bh] & 1u;  // slot of B_prev
     float* hs = hstate + bh * (N * P);
     const int p = 16 * w + l16;
 
@@ -230,7 +241,7 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
 
     const uint16_t* Bt = reinterpret_cast<const uint16_t*>(B) + bg * (R * N);
     const uint16_t* Ct = reinterpret_cast<const uint16_t*>(C) + bg * (R * N);
-    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + bh * (R * N);
+    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + (int64_t(pr) * nb * G + bg) * (R * N);
     const uint16_t* xt = reinterpret_cast<const uint16_t*>(x) + bh * (R * P);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + bh * (R * P);
     for (int e = tid; e < RS * (N / 2); e += 256) {  // rank r, pair of rows (2 j, 2 j + 1): one 32-bit load
@@ -324,28 +335,32 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     // this token becomes the carry of the next step (the carry was read into
     // LDS before the barrier above)
     for (int e = tid; e < R * P; e += 256) carry_x[bh * (R * P) + e] = x[bh * (R * P) + e];
-    for (int e = tid; e < R * N; e += 256) carry_B[bh * (R * N) + e] = B[bg * (R * N) + e];
+    if (h % (H / G) == 0)
+        for (int e = tid; e < R * N; e += 256)
+            carry_B[(int64_t(pr ^ 1u) * nb * G + bg) * (R * N) + e] = B[bg * (R * N) + e];
+    if (tid == 0) par[bh] = pr ^ 1u;
 }
 
 // Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x,
-                      const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+                      unsigned* __restrict__ par, int rev, const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                       const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                       const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
                       int G, int P, int N, int R) {
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = rev ? int64_t(gridDim.x) - 1 - blockIdx.x : int64_t(blockIdx.x);
     const int64_t b = bh / H;
     const int h = int(bh % H);
     const int g = h / (H / G);
     const int64_t bg = b * G + g;
+    const unsigned pr = par[bh] & 1u;  // slot of B_prev
     const int K = N / 2;
     float* hs = hstate + bh * int64_t(N) * P;
     const T* Bt = B + bg * int64_t(R) * N;
     const T* Ct = C + bg * int64_t(R) * N;
-    const T* Bp = carry_B + bh * int64_t(R) * N;
+    const T* Bp = carry_B + (int64_t(pr) * nb * G + bg) * int64_t(R) * N;
     const T* xt = x + bh * int64_t(R) * P;
     const T* xp = carry_x + bh * int64_t(R) * P;
     const float d = dt[bh], lm = lam_at(lam, bh);
@@ -380,7 +395,16 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
     // this token becomes the carry of the next step (every read of the carry
     // precedes the barrier above)
     for (int e = tid; e < R * P; e += kThreads) carry_x[bh * int64_t(R) * P + e] = xt[e];
-    for (int e = tid; e < R * N; e += kThreads) carry_B[bh * int64_t(R) * N + e] = Bt[e];
+    if (h % (H / G) == 0)
+        for (int e = tid; e < R * N; e += kThreads)
+            carry_B[(int64_t(pr ^ 1u) * nb * G + bg) * int64_t(R) * N + e] = Bt[e];
+    if (tid == 0) par[bh] = pr ^ 1u;
+}
+
+// the per-head parity words behind the two B slots of the carry buffer
+unsigned* parity_words(const DecodeArgs& a) {
+    return reinterpret_cast<unsigned*>(static_cast<char*>(a.carry_B) +
+                                       decode_carry_B_slots_bytes(a.b, a.G, a.R, a.N, a.io == M3_BF16 ? 2 : 4));
 }
 
 // (N, P, R) the row kernel is instantiated for (bf16 I/O) besides N 128, P 64 at R 1, 2, 4:
@@ -397,8 +421,8 @@ hipError_t launch_rows(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x,
     constexpr int per = R == 1 ? 16 : 8;  // state floats per thread
     constexpr int want = N * P / per, cap = 1024;
     constexpr int NTH = want < cap ? want : cap;
-    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx, x,
-                       a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx,
+                       parity_words(a), a.rev, x, a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     return hipGetLastError();
 }
 
@@ -440,7 +464,7 @@ hipError_t launch_t(const DecodeArgs& a) {
         if ((a.N == 64 || a.N == 128) && a.P == 64 && ((a.R >= 2 && a.R <= 4) || a.R == 8)) {
             // R 3 runs with a zero fourth rank slot (the staging zero-fills ranks past R); at
             // N 256 the 64 state values per lane spill (358 us against the row kernel's)
-            using K = void (*)(float*, bf16_t*, bf16_t*, const bf16_t*, const float*, const float*,
+            using K = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, const bf16_t*, const float*, const float*,
                                const float*, const float*, const bf16_t*, const bf16_t*, const float*, bf16_t*,
                                int64_t, int, int);
             K kern = a.N == 64 ? (a.R == 2   ? decode_mfma_kernel<2, 64>
@@ -451,8 +475,8 @@ hipError_t launch_t(const DecodeArgs& a) {
                                   : a.R == 3 ? decode_mfma_kernel<3, 128>
                                   : a.R == 4 ? decode_mfma_kernel<4, 128>
                                              : decode_mfma_kernel<8, 128>);
-            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, x, a.dt, a.A, a.omega,
-                               a.lam, B, C, a.D, y, a.b, a.H, a.G);
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, parity_words(a), a.rev, x, a.dt,
+                               a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
             return hipGetLastError();
         }
     }
@@ -461,16 +485,17 @@ hipError_t launch_t(const DecodeArgs& a) {
                   : a.R == 2 ? decode_rows_kernel<T, 2, M3_DECODE_THREADS_R4, 128, 64>
                              : decode_rows_kernel<T, 4, M3_DECODE_THREADS_R4, 128, 64>;
         const int nth = a.R == 1 ? M3_DECODE_THREADS_R1 : M3_DECODE_THREADS_R4;
-        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, x, a.dt, a.A,
-                           a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, parity_words(a), a.rev, x, a.dt,
+                           a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     } else {
         if constexpr (std::is_same<T, bf16_t>::value) {
             // other state sizes, head dims and ranks (bf16 I/O): the same kernel, instantiated per (N, P, R)
             if (rows_kernel_sizes(a.N, a.P, a.R))
                 return launch_rows_sized<T>(a, grid, cB, cx, x, B, C, y);
         }
-        hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx, x,
-                           a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G, a.P, a.N, a.R);
+        hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx,
+                           parity_words(a), a.rev, x, a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G,
+                           a.P, a.N, a.R);
     }
     return hipGetLastError();
 }

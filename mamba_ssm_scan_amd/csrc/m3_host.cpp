@@ -291,7 +291,9 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
 size_t m3_decode_carry_bytes(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int32_t which) {
     if (check_dims(dims, R) != M3_OK || check_dtype(io_dtype) != M3_OK) return 0;
     const size_t es = io_size(io_dtype);
-    if (which == 0) return size_t(dims->batch) * dims->heads * R * dims->dstate * es;
+    if (which == 0)  // two slots of the group's B rows, then one parity word per head
+        return m3::decode_carry_B_slots_bytes(dims->batch, dims->groups, R, dims->dstate, es) +
+               size_t(dims->batch) * dims->heads * 4;
     if (which == 1) return size_t(dims->batch) * dims->heads * R * dims->headdim * es;
     return 0;
 }
@@ -337,9 +339,14 @@ m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t
     if (h0 != h_buf)
         e = m3::launch_copy_or_zero(reinterpret_cast<uint32_t*>(h_buf), reinterpret_cast<const uint32_t*>(h0),
                                     int64_t(hbytes / 4), hs);
-    // every head gets its own copy of its group's B rows; x is per head already
+    // B_last into slot 0 (one row per group), every head's parity word to 0 (slot 0
+    // holds B_prev), x_last per head
+    const size_t slots = m3::decode_carry_B_slots_bytes(b, dims->groups, R, dims->dstate, es);
     if (e == hipSuccess)
-        e = m3::launch_carry_init(carry_B_buf, B_last, b, dims->heads, dims->groups, int64_t(rowB), hs);
+        e = m3::launch_carry_init(carry_B_buf, B_last, b, dims->groups, dims->groups, int64_t(rowB), hs);
+    if (e == hipSuccess)
+        e = m3::launch_carry_init(static_cast<char*>(carry_B_buf) + slots, nullptr, 1, 1, 1,
+                                  int64_t(b) * dims->heads * 4, hs);
     if (e == hipSuccess)
         e = m3::launch_carry_init(carry_x_buf, x_last, b, dims->heads, dims->heads, int64_t(rowx), hs);
     if (e != hipSuccess) return fail(M3_EHIP, "state init failed: %s", hipGetErrorString(e));
@@ -378,14 +385,14 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
                             rng("lambda_t", lambda_t, size_t(b) * H * 4),
                             rng("B_t", B_t, size_t(b) * G * R * N * es), rng("C_t", C_t, size_t(b) * G * R * N * es),
                             rng("state h", st->h, size_t(b) * H * N * P * 4),
-                            rng("state carry_B", st->carry_B, size_t(b) * H * R * N * es),
+                            rng("state carry_B", st->carry_B, m3_decode_carry_bytes(&d, R, st->io_dtype, 0)),
                             rng("state carry_x", st->carry_x, size_t(b) * H * R * P * es)};
     for (const Range& r : others)
         if (overlaps(ry, r)) return fail(M3_EINVAL, "y_t overlaps %s", r.name);
 
     m3::DecodeArgs a{st->h, st->carry_B, st->carry_x, x_t, dt_t, A, omega,
                      lambda_t, B_t, C_t, D, y_t, b, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R,
-                     st->io_dtype, reinterpret_cast<hipStream_t>(stream)};
+                     st->io_dtype, reinterpret_cast<hipStream_t>(stream), int(st->t & 1)};
     hipError_t e = m3::launch_decode(a);
     if (e != hipSuccess) return fail(M3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
     st->t += 1;

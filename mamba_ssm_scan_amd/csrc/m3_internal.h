@@ -33,7 +33,7 @@ struct PrefillArgs {
 
 struct DecodeArgs {
     float* h;
-    void* carry_B;         // [b][H][R][N]: each head's copy of the previous token's B rows
+    void* carry_B;         // two slots [2][b][G][R][N] of the previous token's B rows, then parity words [b][H]
     void* carry_x;         // [b][H][R][P]
     const void* x;
     const float* dt;
@@ -48,7 +48,14 @@ struct DecodeArgs {
     int32_t H, G, P, N, R;
     m3_dtype io;
     hipStream_t stream;
+    int rev;               // walk the (b, h) workgroups backwards (a block-order hint: every other step)
 };
+
+// Bytes of the two B slots at the start of a decode carry_B buffer (16-byte
+// aligned end; the per-head parity words follow).
+inline size_t decode_carry_B_slots_bytes(int64_t b, int64_t G, int64_t R, int64_t N, size_t es) {
+    return (size_t(2 * b * G * R * N) * es + 15) / 16 * 16;
+}
 
 struct PrologueArgs {
     const void* B_raw;     // [ntok][G][R][N] io dtype (with B, or both NULL)

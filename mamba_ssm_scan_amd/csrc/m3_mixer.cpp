@@ -175,7 +175,7 @@ struct m3_mixer {
                 void* D, void* ws, hipStream_t s) {
         hipEvent_t e0 = nullptr, e1 = nullptr;
         if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-            if (e0) hipEventDestroy(e0);
+            if (e0) (void)hipEventDestroy(e0);
             return 0;
         }
         int best = 0;
@@ -184,9 +184,9 @@ struct m3_mixer {
             if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > kGemmWorkspace) continue;
             if (run(g, res[i].algo, U, W, D, ws, s) != M3_OK) continue;
             for (int round = 0; round < 3; ++round) {
-                hipEventRecord(e0, s);
+                if (hipEventRecord(e0, s) != hipSuccess) break;
                 for (int k = 0; k < 3; ++k) run(g, res[i].algo, U, W, D, ws, s);
-                hipEventRecord(e1, s);
+                if (hipEventRecord(e1, s) != hipSuccess) break;
                 float ms = 0.f;
                 if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
                     ms < best_ms) {
@@ -195,8 +195,8 @@ struct m3_mixer {
                 }
             }
         }
-        hipEventDestroy(e0);
-        hipEventDestroy(e1);
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
         return best;
     }
 };

@@ -195,10 +195,15 @@ def test_decode_argument_errors(lib):
 
 
 def test_carry_bytes(lib):
-    # one copy of the previous token's rows per head: B [b][H][R][N], x [b][H][R][P]
+    # B: two slots [2][b][G][R][N] (to a 16-byte boundary), then a 32-bit parity word per (b, h);
+    # x: [b][H][R][P]
     d = _dims(b=3, H=4, G=2, P=8, N=16)
-    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 0) == 3 * 4 * 2 * 16 * 2
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 0) == 2 * 3 * 2 * 2 * 16 * 2 + 3 * 4 * 4
     assert lib.m3_decode_carry_bytes(ctypes.byref(d), 2, bd.M3_BF16, 1) == 3 * 4 * 2 * 8 * 2
+    d = _dims(b=1, H=3, G=1, P=8, N=2)   # slots of 2 * 1 * 1 * 1 * 2 * 4 = 16 bytes (f32)
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 1, bd.M3_F32, 0) == 16 + 3 * 4
+    d = _dims(b=1, H=3, G=1, P=8, N=2)   # 8 bytes of bf16 slots, padded to 16
+    assert lib.m3_decode_carry_bytes(ctypes.byref(d), 1, bd.M3_BF16, 0) == 16 + 3 * 4
 
 
 def test_plan_segments_for_few_heads(lib):

@@ -119,17 +119,18 @@ def test_decode_steps_replay():
     assert st.t == t_after + steps  # the host counter advanced once, at capture
 
 
-@pytest.mark.parametrize("R", [1, 4])
-def test_decode_odd_graph_replays_continue(R):
+@pytest.mark.parametrize("R,G", [(1, 1), (4, 1), (1, 2), (4, 2)])
+def test_decode_odd_graph_replays_continue(R, G):
     """A captured graph of an odd number of steps (5), replayed twice back to back
     with nothing reset in between, continues the sequence: the 10 outputs and the
     final state equal the oracle over the 5 tokens fed twice. Each step reads
-    only device buffers (the previous token's rows are each head's own carry),
-    so the replays do not depend on how many steps were captured."""
-    print(f"case odd graph (5 steps, R {R}) replayed twice", flush=True)
-    b, H, G, P, N, steps = 2, 4, 1, 64, 128, 5
+    only device buffers (B_prev from the slot each head's parity word names, x_prev
+    from the head's own carry), so the replays do not depend on how many steps
+    were captured; G 2 puts two heads in each group."""
+    print(f"case odd graph (5 steps, R {R}, G {G}) replayed twice", flush=True)
+    b, H, P, N, steps = 2, 4, 64, 128, 5
     di = {k: (v.cuda() if isinstance(v, torch.Tensor) else v)
-          for k, v in inputs.decode_inputs(3, steps, device="cpu", rank=R, batch=b).items()}
+          for k, v in inputs.decode_inputs(3, steps, device="cpu", rank=R, batch=b, groups=G).items()}
     Hs = slice(0, H)
     x = di["x"][:, :, Hs].contiguous()
     dtv, lamv = di["dt"][:, :, Hs].contiguous(), di["lam"][:, :, Hs].contiguous()
