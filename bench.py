@@ -202,7 +202,11 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
     return r
 
 
-def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
+def bench_decode(R, steps_total, reps, log, batch=None, wid=3, fused=False):
+    """The decode loop: steps_total steps of m3_decode_step at batch b, timed per loop over all steps.
+
+    fused: m3_decode_step_fused on raw projections (the input prologue in the step kernel) instead.
+    """
     import torch
     from mamba_ssm_scan_amd import binding, inputs
     w = inputs.WORKLOADS[wid]
@@ -212,10 +216,23 @@ def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
     st = binding.DecodeState(b, w.heads, 1, w.headdim, w.dstate, R, io_dtype=torch.bfloat16, h0=di["h0"])
     sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     A, om, D = di["A"].data_ptr(), di["omega"].data_ptr(), di["D"].data_ptr()
+    if fused:  # raw B, C, dt, lambda for every step, and the prologue's weights
+        raw = inputs.prologue_inputs(tokens=(steps_total, b), heads=w.heads, groups=1, rank=R, dstate=w.dstate,
+                                     io_dtype="bf16", wid=320, device="cuda")
+        di.update(B=raw["B_raw"], C=raw["C_raw"], dt=raw["dt_raw"], lam=raw["lambda_raw"])
+        lib = binding.load()
+        vp = ctypes.c_void_p
+        wts = [vp(raw[k].data_ptr()) for k in ("B_weight", "B_bias", "C_weight", "C_bias")]
+        dtb, eps = vp(raw["dt_bias"].data_ptr()), ctypes.c_float(1e-6)
     ptrs = [(di["x"][t].data_ptr(), di["dt"][t].data_ptr(), di["lam"][t].data_ptr(), di["B"][t].data_ptr(),
              di["C"][t].data_ptr(), y[t].data_ptr()) for t in range(steps_total)]
 
     def loop():
+        if fused:
+            for (xp, dp, lp, bp, cp, yp) in ptrs:
+                binding.check(lib.m3_decode_step_fused(ctypes.byref(st._st), vp(xp), vp(dp), dtb, vp(A), vp(om),
+                                                       vp(lp), vp(bp), vp(cp), *wts, eps, vp(D), R, vp(yp), sh))
+            return
         for (xp, dp, lp, bp, cp, yp) in ptrs:
             st.step_raw(xp, dp, A, om, lp, bp, cp, D, yp, sh)
 
@@ -223,7 +240,8 @@ def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
     t = time_calls(lambda k: loop(), reps, 1)
     ms_step = t["mean"] / steps_total
     by = decode_bytes(b, w.heads, 1, w.headdim, w.dstate, R)
-    r = {"workload": f"decode_b{b}_h{w.heads}_p{w.headdim}_n{w.dstate}_r{R}_{steps_total}_steps",
+    r = {"workload": f"decode_b{b}_h{w.heads}_p{w.headdim}_n{w.dstate}_r{R}_{steps_total}_steps"
+                     + ("_fused_prologue" if fused else ""),
          "us_per_step": ms_step * 1e3, "steps_per_s": 1e3 / ms_step, "hbm_gbs": by / (ms_step * 1e-3) / 1e9,
          "bytes_per_step": by, **_pct(t, 1e3 / steps_total, "us_per_step")}
     r["timed_loops"] = r.pop("timed_calls")
@@ -234,7 +252,7 @@ def bench_decode(R, steps_total, reps, log, batch=None, wid=3):
     fl = 4 * b * w.heads * w.dstate * w.headdim * R
     r["mfma_tflops"] = fl / (ms_step * 1e-3) / 1e12
     r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
-    log(f"decode R={R} b={b}: {ms_step * 1e3:.1f} us/step (median {r['median_us_per_step']:.1f}, p10 "
+    log(f"decode{' fused' if fused else ''} R={R} b={b}: {ms_step * 1e3:.1f} us/step (median {r['median_us_per_step']:.1f}, p10 "
         f"{r['p10_us_per_step']:.1f}, p90 {r['p90_us_per_step']:.1f} over {reps} loops of {steps_total}), "
         f"{r['steps_per_s']:.0f} steps/s, "
         f"{r['hbm_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% HBM), rank contractions "
@@ -631,6 +649,8 @@ def main():
                 bench_prefill(1, args.steps, args.warmup, log, special=item[len("prefill1_"):])
             elif item in ("decode1", "decode4"):
                 bench_decode(int(item[-1]), 1024, 1, log)
+            elif item in ("decode1_fused", "decode4_fused"):
+                bench_decode(int(item[6]), 1024, 1, log, fused=True)
             elif item.startswith("decode") and "_b" in item:  # decode1_b256: R 1 at batch 256, 256 steps
                 bench_decode(int(item[6]), 256, 1, log, batch=int(item.split("_b")[1]))
             elif item == "long":
@@ -671,6 +691,8 @@ def main():
             d = bench_decode(R, 1024, 20, log)
             d["roofline"] = roofline("hbm", d["hbm_gbs"], HBM_PEAK_GBS, "GB/s", measured_traffic(f"decode{R}"),
                                      kern[R], {"bytes_per_launch": d["bytes_per_step"]})
+            # the same loop on the raw projections, the input prologue in the step kernel
+            d["fused_prologue"] = bench_decode(R, 1024, 5, log, fused=True)
             out["decode"][f"r{R}"] = d
         # the same step at batch 64 and 256 (state 128 / 512 MiB against the 256 MB MALL), and a
         # plain 1 GiB copy: the DRAM rate that bounds a stream larger than the MALL

@@ -247,6 +247,31 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
                          const float* D, int32_t R, void* y_t, void* stream);
 
 /*
+ * m3_decode_step_fused -- m3_decode_step on the raw projections, with the
+ * input prologue (m3_prologue's reading, below) computed inside the step
+ * kernel instead of a separate launch.
+ *
+ * Passage: the QK-norm and bias sit between the B/C projection and the
+ * recurrence ("复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构", §2.4 and Fig. 4);
+ * at decode every (b, h) workgroup normalises its group's rows itself.
+ *
+ * x_t [b][H][R][P], B_raw_t / C_raw_t [b][G][R][N] (io dtype); dt_raw_t and
+ * lambda_raw_t [b][H] fp32 (lambda_raw_t NULL: lambda = 1); dt_bias [H],
+ * B_weight / B_bias / C_weight / C_bias [G][R][N] fp32, each NULL for zero bias
+ * or unit weight; eps >= 0. The step uses dt = softplus(dt_raw + dt_bias),
+ * lambda = sigmoid(lambda_raw) and the normalised rows rounded to the io dtype,
+ * exactly as m3_prologue would store them, so the call equals m3_prologue
+ * followed by m3_decode_step (up to the summation order of the norm); the B
+ * carry holds the normalised rows. Other arguments, the state and the errors
+ * as for m3_decode_step; R * N above 8192 is M3_EUNSUPPORTED.
+ */
+m3_status m3_decode_step_fused(m3_decode_state* st, const void* x_t, const float* dt_raw_t, const float* dt_bias,
+                               const float* A, const float* omega, const float* lambda_raw_t, const void* B_raw_t,
+                               const void* C_raw_t, const float* B_weight, const float* B_bias,
+                               const float* C_weight, const float* C_bias, float eps, const float* D, int32_t R,
+                               void* y_t, void* stream);
+
+/*
  * m3_prologue -- the input prologue in front of the recurrence, one pass over
  * the raw projections of ntok tokens (b * L for a prefill, b for a decode step).
  *

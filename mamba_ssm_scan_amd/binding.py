@@ -26,7 +26,7 @@ EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_dec
            "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_prefill_backward",
            "m3_prefill_backward_workspace_size", "m3_mixer_create", "m3_mixer_destroy", "m3_mixer_workspace_size",
            "m3_mixer_prefill", "m3_mixer_decode_step", "m3_status_string", "m3_last_error", "m3_abi_version",
-           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes", "m3_prefill_check"]
+           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes", "m3_prefill_check", "m3_decode_step_fused"]
 
 
 class M3Dims(ctypes.Structure):
@@ -91,6 +91,9 @@ def load(path: str = LIB_PATH):
     lib.m3_decode_state_init.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [ctypes.POINTER(M3DecodeState)] + [vp] * 8 + [i32, vp, vp]
     lib.m3_decode_step.restype = ctypes.c_int
+    lib.m3_decode_step_fused.argtypes = ([ctypes.POINTER(M3DecodeState)] + [vp] * 12 + [ctypes.c_float, vp, i32, vp,
+                                                                                       vp])
+    lib.m3_decode_step_fused.restype = ctypes.c_int
     lib.m3_prologue.argtypes = [dims_p, i32, ctypes.c_int, i64] + [vp] * 6 + [ctypes.c_float] + [vp] * 7 + [vp]
     lib.m3_prologue.restype = ctypes.c_int
     lib.m3_prefill_backward.argtypes = [vp] * 8 + [i32] + [vp] * 16 + [dims_p, ctypes.c_int, vp, sz, vp]
@@ -267,6 +270,32 @@ class DecodeState:
         _need_out(y_t, "y_t", self.io_dtype, x_t.shape)
         check(load().m3_decode_step(ctypes.byref(self._st), _ptr(x_t), _ptr(dt_t), _ptr(A), _ptr(omega),
                                     _ptr(lam_t), _ptr(B_t), _ptr(C_t), _ptr(D), R, _ptr(y_t), _stream(stream)))
+        return y_t
+
+    def step_fused(self, x_t, dt_raw_t, A, omega, lambda_raw_t, B_raw_t, C_raw_t, D, *, dt_bias=None, B_weight=None,
+                   B_bias=None, C_weight=None, C_bias=None, eps: float = 1e-6, y_t=None, stream=None):
+        """m3_decode_step_fused: one token from the raw projections (norm, weight and bias on B_t and C_t,
+        softplus on dt_raw_t + dt_bias, sigmoid on lambda_raw_t) in the step kernel; returns y_t."""
+        b, H, G = self.dims.batch, self.dims.heads, self.dims.groups
+        P, N, R = self.dims.headdim, self.dims.dstate, self.R
+        x_t = _need(x_t, "x_t", self.io_dtype, (b, H, R, P))
+        B_raw_t = _need(B_raw_t, "B_raw_t", self.io_dtype, (b, G, R, N))
+        C_raw_t = _need(C_raw_t, "C_raw_t", self.io_dtype, (b, G, R, N))
+        dt_raw_t = _need(dt_raw_t, "dt_raw_t", torch.float32, (b, H))
+        lambda_raw_t = _need(lambda_raw_t, "lambda_raw_t", torch.float32, (b, H))
+        A = _need(A, "A", torch.float32, (H,))
+        D = _need(D, "D", torch.float32, (H,))
+        omega = _need(omega, "omega", torch.float32, (H, N // 2))
+        dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,))
+        w = [_need(v, n, torch.float32, (G, R, N)) for v, n in
+             ((B_weight, "B_weight"), (B_bias, "B_bias"), (C_weight, "C_weight"), (C_bias, "C_bias"))]
+        if y_t is None:
+            y_t = torch.empty_like(x_t)
+        _need_out(y_t, "y_t", self.io_dtype, x_t.shape)
+        check(load().m3_decode_step_fused(ctypes.byref(self._st), _ptr(x_t), _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A),
+                                          _ptr(omega), _ptr(lambda_raw_t), _ptr(B_raw_t), _ptr(C_raw_t),
+                                          *[_ptr(v) for v in w], float(eps), _ptr(D), R, _ptr(y_t),
+                                          _stream(stream)))
         return y_t
 
     def step_raw(self, x_t, dt_t, A, omega, lam_t, B_t, C_t, D, y_t, stream_handle: ctypes.c_void_p):

@@ -42,6 +42,93 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
     *c = __builtin_amdgcn_cosf(r);
 }
 
+// The input prologue of m3_decode_step_fused (m3_prologue's reading, see
+// m3_prologue.hip): softplus with the head's bias on the step, sigmoid on
+// lambda, and per (group, rank) row of B and C an RMS norm with weight and
+// bias, the result rounded to the io dtype as m3_prologue stores it.
+// softplus(x) = max(x, 0) + ln(1 + e^-|x|) and sigmoid through the hardware
+// exp2 / log2 (a few ulp): below e^-|x| = 2^-24 the log term is taken as e^-|x|
+// itself, where 1 + e^-|x| would round to 1
+__device__ __forceinline__ float softplus_f(float x) {
+    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float l = e < 5.9604645e-8f ? e : __builtin_amdgcn_logf(1.f + e) * kLn2;
+    return fmaxf(x, 0.f) + l;
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);  // e^-|x| in (0, 1]
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
+    return x >= 0.f ? r : e * r;
+}
+template <typename T>
+__device__ __forceinline__ float round_io(float v) {
+    if constexpr (std::is_same<T, bf16_t>::value) return bf16_to_f32(f32_to_bf16(v));
+    return v;
+}
+// the step's dt and lambda: as given, or through the prologue
+template <bool PRO>
+__device__ __forceinline__ void step_scalars(const float* dt, const float* lam, const DecodePrologue& pro, int64_t bh,
+                                             int h, float* d, float* lm) {
+    if constexpr (PRO) {
+        *d = softplus_f(dt[bh] + (pro.dt_bias ? pro.dt_bias[h] : 0.f));
+        *lm = lam ? sigmoid_f(lam[bh]) : 1.f;
+    } else {
+        *d = dt[bh];
+        *lm = lam_at(lam, bh);
+    }
+}
+// sum over aligned groups of GL lanes (32 or 64), off the LDS crossbar:
+// inclusive prefix sums inside each 16-lane row by DPP row shifts, then the
+// row totals (lanes 15, 31, 47, 63) read into scalar registers and added
+template <int CTL>
+__device__ __forceinline__ float dpp_shr(float u) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, u), CTL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_of(float u, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), l));
+}
+template <int GL>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(GL == 32 || GL == 64, "lane group");
+    v += dpp_shr<0x111>(v);
+    v += dpp_shr<0x112>(v);
+    v += dpp_shr<0x114>(v);
+    v += dpp_shr<0x118>(v);
+    const float r0 = lane_of(v, 15), r1 = lane_of(v, 31), r2 = lane_of(v, 47), r3 = lane_of(v, 63);
+    if constexpr (GL == 64) return (r0 + r1) + (r2 + r3);
+    return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+}
+// one element of a normalised row: raw * scale * weight + bias, rounded to the io dtype
+template <typename T>
+__device__ __forceinline__ float norm_elem(float v, float scale, const float* w, const float* bb, int64_t i) {
+    return round_io<T>(v * scale * (w ? w[i] : 1.f) + (bb ? bb[i] : 0.f));
+}
+
+// RMS-normalise the R rows of B (rb) and of C (rc), N fp32 values each in LDS,
+// in place, with the weights and biases of group g; one wave per row. The
+// caller synchronises before (rows staged) and after (rows read).
+template <typename T>
+__device__ void qk_norm_rows(float* rb, float* rc, int R, int N, int g, const DecodePrologue& pro, int tid,
+                             int nthreads) {
+    const int lane = tid & 63, nw = nthreads >> 6;
+    for (int row = tid >> 6; row < 2 * R; row += nw) {
+        const bool isC = row >= R;
+        const int r = isC ? row - R : row;
+        float* v = (isC ? rc : rb) + r * N;
+        float ss = 0.f;
+        for (int n = lane; n < N; n += 64) ss += v[n] * v[n];
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1) ss += __shfl_xor(ss, sh);
+        const float scale = 1.f / sqrtf(ss / float(N) + pro.eps);
+        const float* w = isC ? pro.C_weight : pro.B_weight;
+        const float* bb = isC ? pro.C_bias : pro.B_bias;
+        const int64_t o = (int64_t(g) * R + r) * N;
+        for (int n = lane; n < N; n += 64)
+            v[n] = round_io<T>(v[n] * scale * (w ? w[o + n] : 1.f) + (bb ? bb[o + n] : 0.f));
+    }
+}
+
 // Threads per workgroup of the N = 128, P = 64 kernel, per rank class.
 #ifndef M3_DECODE_THREADS_R1
 #define M3_DECODE_THREADS_R1 512
@@ -54,10 +141,11 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
 // row, thread (kk, q), q = tid % QP, owns rows (2k, 2k+1), k = kk + (NTH/QP)*it,
 // it < (N/2) / (NTH/QP), and columns 4q..4q+3, loaded and stored as float4 (a
 // wave covers 64/QP row segments of P floats per access).
-template <typename T, int R, int NTH, int N, int P>
+template <typename T, int R, int NTH, int N, int P, bool PRO>
 __global__ void __launch_bounds__(NTH)
 decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x,
-                       unsigned* __restrict__ par, int rev, const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+                       unsigned* __restrict__ par, int rev, DecodePrologue pro,
+                       const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                        const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                        const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
                        int G) {
@@ -79,6 +167,35 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
     float* hs = hstate + bh * (N * P);
     const int q = tid % QP, kk = tid / QP;
 
+    // With the prologue, each rank row of B_t and C_t is normalised by the GL
+    // lanes that load it (PE consecutive entries per lane): its sum of squares
+    // never leaves them. Rows of B first, then of C, in whole lane groups (2 R GL
+    // and NTH are multiples of GL). The rows and their weights are loaded first,
+    // ahead of the state, so their latency hides under the state stream.
+    constexpr int PE = N >= 256 ? N / 64 : 2, GL = N / PE;
+    constexpr int NIT = PRO ? (2 * R * GL + NTH - 1) / NTH : 0;
+    static_assert(GL <= 64 && (GL & (GL - 1)) == 0, "row lanes");
+    float pv[NIT > 0 ? NIT : 1][PE], pw[NIT > 0 ? NIT : 1][PE], pb[NIT > 0 ? NIT : 1][PE];
+    if constexpr (PRO) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + it * NTH;
+            if (e >= 2 * R * GL) continue;
+            const bool isC = e >= R * GL;
+            const int r = (isC ? e - R * GL : e) / GL, n0 = (e % GL) * PE;
+            const T* src = (isC ? C : B) + bg * (R * N);
+            const float* w = isC ? pro.C_weight : pro.B_weight;
+            const float* bb = isC ? pro.C_bias : pro.B_bias;
+            const int64_t o = (int64_t(g) * R + r) * N + n0;
+#pragma unroll
+            for (int i = 0; i < PE; ++i) {
+                pv[it][i] = Io<T>::load(src, r * N + n0 + i);
+                pw[it][i] = w ? w[o + i] : 1.f;
+                pb[it][i] = bb ? bb[o + i] : 0.f;
+            }
+        }
+    }
+
     float4 v0[IT], v1[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -93,15 +210,35 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
     const T* xt = x + bh * (R * P);
     const T* xp = carry_x + bh * (R * P);
     for (int e = tid; e < R * N; e += NTH) {
-        (&sB[0][0])[e] = Io<T>::load(Bt, e);
+        if constexpr (!PRO) {
+            (&sB[0][0])[e] = Io<T>::load(Bt, e);
+            (&sC[0][0])[e] = Io<T>::load(Ct, e);
+        }
         (&sBp[0][0])[e] = Io<T>::load(Bp, e);
-        (&sC[0][0])[e] = Io<T>::load(Ct, e);
+    }
+    if constexpr (PRO) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + it * NTH;
+            if (e >= 2 * R * GL) continue;  // whole lane groups skip together
+            const bool isC = e >= R * GL;
+            const int r = (isC ? e - R * GL : e) / GL, n0 = (e % GL) * PE;
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < PE; ++i) ss += pv[it][i] * pv[it][i];
+            ss = group_sum<GL>(ss);
+            const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
+            float* dst = isC ? &sC[r][n0] : &sB[r][n0];
+#pragma unroll
+            for (int i = 0; i < PE; ++i) dst[i] = round_io<T>(pv[it][i] * k * pw[it][i] + pb[it][i]);
+        }
     }
     for (int e = tid; e < R * P; e += NTH) {
         (&sx[0][0])[e] = Io<T>::load(xt, e);
         (&sxp[0][0])[e] = Io<T>::load(xp, e);
     }
-    const float d = dt[bh], lm = lam_at(lam, bh);
+    float d, lm;
+    step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
     __syncthreads();
@@ -169,7 +306,13 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
     // LDS before the barrier above)
     for (int e = tid; e < R * P; e += NTH) carry_x[bh * (R * P) + e] = xt[e];
     if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += NTH) carry_B[(int64_t(pr ^ 1u) * nb * G + bg) * (R * N) + e] = Bt[e];
+        for (int e = tid; e < R * N; e += NTH) {
+            T* dst = carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N);
+            if constexpr (PRO)
+                Io<T>::store(dst, e, (&sB[0][0])[e]);  // the normalised row, already in the io dtype
+            else
+                dst[e] = Bt[e];
+        }
     if (tid == 0) par[bh] = pr ^ 1u;
 }
 
@@ -205,10 +348,11 @@ __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 
 // takes the lane's 4 new state values as its B operand. h' goes in as two bf16
 // terms (hi + lo), which keeps y at fp32 accuracy; the products of bf16 inputs
 // in U and Up are exact. No cross-lane reduction is left.
-template <int R, int N>
+template <int R, int N, bool PRO>
 __global__ void __launch_bounds__(256)
 decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
-                   unsigned* __restrict__ par, int rev, const bf16_t* __restrict__ x, const float* __restrict__ dt,
+                   unsigned* __restrict__ par, int rev, DecodePrologue pro,
+                   const bf16_t* __restrict__ x, const float* __restrict__ dt,
                    const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
@@ -232,6 +376,41 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     const unsigned pr = par[bh] & 1u;  // slot of B_prev
     float* hs = hstate + bh * (N * P);
     const int p = 16 * w + l16;
+    const int gi = h / (H / G);
+
+    // With the prologue, a rank row's N / 2 pairs are staged by N / 2
+    // consecutive lanes (a whole wave at N 128): they reduce its sum of squares
+    // among themselves and stage the normalised pairs, with no pass of their
+    // own. The raw pairs and their weights are loaded first, ahead of the state.
+    constexpr int BIT = PRO ? (RS * (N / 2) + 255) / 256 : 0;  // B pairs per thread
+    constexpr int CIT = PRO ? (R * (N / 2) + 255) / 256 : 0;   // C pairs per thread
+    unsigned braw[BIT > 0 ? BIT : 1], craw[CIT > 0 ? CIT : 1];
+    float2 bw[BIT > 0 ? BIT : 1], bb2[BIT > 0 ? BIT : 1], cw[CIT > 0 ? CIT : 1], cb2[CIT > 0 ? CIT : 1];
+    if constexpr (PRO) {
+        const unsigned* B32 = reinterpret_cast<const unsigned*>(B + bg * (R * N));
+        const unsigned* C32 = reinterpret_cast<const unsigned*>(C + bg * (R * N));
+        auto wpair = [&](const float* v, int r, int j, float dflt) {
+            if (!v) return float2{dflt, dflt};
+            const int64_t o = (int64_t(gi) * R + r) * N + 2 * j;
+            return float2{v[o], v[o + 1]};
+        };
+#pragma unroll
+        for (int it = 0; it < BIT; ++it) {
+            const int e = tid + 256 * it, r = e / (N / 2), j = e % (N / 2);
+            const bool in = e < RS * (N / 2) && r < R;
+            braw[it] = in ? B32[r * (N / 2) + j] : 0u;
+            bw[it] = in ? wpair(pro.B_weight, r, j, 1.f) : float2{1.f, 1.f};
+            bb2[it] = in ? wpair(pro.B_bias, r, j, 0.f) : float2{0.f, 0.f};
+        }
+#pragma unroll
+        for (int it = 0; it < CIT; ++it) {
+            const int e = tid + 256 * it, r = e / (N / 2), j = e % (N / 2);
+            const bool in = e < R * (N / 2);
+            craw[it] = in ? C32[e] : 0u;
+            cw[it] = in ? wpair(pro.C_weight, r, j, 1.f) : float2{1.f, 1.f};
+            cb2[it] = in ? wpair(pro.C_bias, r, j, 0.f) : float2{0.f, 0.f};
+        }
+    }
 
     float st[NT][4];
 #pragma unroll
@@ -244,9 +423,26 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + (int64_t(pr) * nb * G + bg) * (R * N);
     const uint16_t* xt = reinterpret_cast<const uint16_t*>(x) + bh * (R * P);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + bh * (R * P);
-    for (int e = tid; e < RS * (N / 2); e += 256) {  // rank r, pair of rows (2 j, 2 j + 1): one 32-bit load
+    // the normalised pair from a raw pair, its weights and biases; the lane group
+    // holding one rank row shares the same r
+    auto norm_pair = [&](unsigned raw, int r, float2 wv, float2 bv) -> unsigned {
+        const float v0 = bf_lo(raw), v1 = bf_hi(raw);
+        const float ss = group_sum<N / 2>(v0 * v0 + v1 * v1);
+        if (r >= R) return 0u;
+        const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
+        return pk_bf16(v0 * k * wv.x + bv.x, v1 * k * wv.y + bv.y);
+    };
+    constexpr int NBI = (RS * (N / 2) + 255) / 256, NCI = (R * (N / 2) + 255) / 256;
+#pragma unroll
+    for (int it = 0; it < NBI; ++it) {  // rank r, pair of rows (2 j, 2 j + 1)
+        const int e = tid + 256 * it;
+        if (e >= RS * (N / 2)) break;
         const int r = e / (N / 2), j = e % (N / 2);
-        const unsigned vb = r < R ? reinterpret_cast<const unsigned*>(Bt + r * N)[j] : 0u;
+        unsigned vb;
+        if constexpr (PRO)
+            vb = norm_pair(braw[it], r, bw[it], bb2[it]);
+        else
+            vb = r < R ? reinterpret_cast<const unsigned*>(Bt + r * N)[j] : 0u;
         const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(Bp + r * N)[j] : 0u;
         sBt[2 * j][r] = uint16_t(vb);
         sBt[2 * j + 1][r] = uint16_t(vb >> 16);
@@ -262,9 +458,19 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
         sXpt[2 * j][r] = uint16_t(vp);
         sXpt[2 * j + 1][r] = uint16_t(vp >> 16);
     }
-    for (int e = tid; e < R * (N / 2); e += 256)
-        reinterpret_cast<unsigned*>(&sC[e / (N / 2)][0])[e % (N / 2)] = reinterpret_cast<const unsigned*>(Ct)[e];
-    const float d = dt[bh], lm = lam_at(lam, bh);
+#pragma unroll
+    for (int it = 0; it < NCI; ++it) {
+        const int e = tid + 256 * it;
+        if (e >= R * (N / 2)) break;
+        unsigned cv;
+        if constexpr (PRO)
+            cv = norm_pair(craw[it], e / (N / 2), cw[it], cb2[it]);
+        else
+            cv = reinterpret_cast<const unsigned*>(Ct)[e];
+        reinterpret_cast<unsigned*>(&sC[e / (N / 2)][0])[e % (N / 2)] = cv;
+    }
+    float d, lm;
+    step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
     if (tid < K) {
@@ -336,16 +542,22 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     // LDS before the barrier above)
     for (int e = tid; e < R * P; e += 256) carry_x[bh * (R * P) + e] = x[bh * (R * P) + e];
     if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += 256)
-            carry_B[(int64_t(pr ^ 1u) * nb * G + bg) * (R * N) + e] = B[bg * (R * N) + e];
+        for (int e = tid; e < R * N; e += 256) {
+            bf16_t* dst = carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N);
+            if constexpr (PRO)
+                dst[e].bits = sBt[e % N][e / N];  // the normalised row, staged transposed
+            else
+                dst[e] = B[bg * (R * N) + e];
+        }
     if (tid == 0) par[bh] = pr ^ 1u;
 }
 
 // Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
-template <typename T>
+template <typename T, bool PRO>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __restrict__ carry_x,
-                      unsigned* __restrict__ par, int rev, const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+                      unsigned* __restrict__ par, int rev, DecodePrologue pro,
+                      const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
                       const float* __restrict__ omega, const float* __restrict__ lam, const T* __restrict__ B,
                       const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y, int64_t nb, int H,
                       int G, int P, int N, int R) {
@@ -363,9 +575,23 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
     const T* Bp = carry_B + (int64_t(pr) * nb * G + bg) * int64_t(R) * N;
     const T* xt = x + bh * int64_t(R) * P;
     const T* xp = carry_x + bh * int64_t(R) * P;
-    const float d = dt[bh], lm = lam_at(lam, bh);
+    float d, lm;
+    step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
     const float alpha = expf(d * A[h]);
     const float gamma = lm * d, delta = (1.f - lm) * d;
+    // with the prologue, B_t and C_t are read from their normalised copies in LDS
+    extern __shared__ float sNorm[];  // [2][R][N] when PRO
+    if constexpr (PRO) {
+        for (int e = tid; e < R * N; e += kThreads) {
+            sNorm[e] = Io<T>::load(Bt, e);
+            sNorm[R * N + e] = Io<T>::load(Ct, e);
+        }
+        __syncthreads();
+        qk_norm_rows<T>(sNorm, sNorm + R * N, R, N, g, pro, tid, kThreads);
+        __syncthreads();
+    }
+    auto Bv = [&](int64_t i) { return PRO ? sNorm[i] : Io<T>::load(Bt, i); };
+    auto Cv = [&](int64_t i) { return PRO ? sNorm[R * N + i] : Io<T>::load(Ct, i); };
 
     for (int e = tid; e < K * P; e += kThreads) {
         const int k = e / P, p = e % P;
@@ -374,8 +600,8 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
             const float xpv = Io<T>::load(xp, int64_t(r) * P + p), xv = Io<T>::load(xt, int64_t(r) * P + p);
             up0 += Io<T>::load(Bp, int64_t(r) * N + 2 * k) * xpv;
             up1 += Io<T>::load(Bp, int64_t(r) * N + 2 * k + 1) * xpv;
-            u0 += Io<T>::load(Bt, int64_t(r) * N + 2 * k) * xv;
-            u1 += Io<T>::load(Bt, int64_t(r) * N + 2 * k + 1) * xv;
+            u0 += Bv(int64_t(r) * N + 2 * k) * xv;
+            u1 += Bv(int64_t(r) * N + 2 * k + 1) * xv;
         }
         float sn, cs;
         sincos_step(d * om_at(omega, int64_t(h) * K + k), &sn, &cs);
@@ -389,15 +615,20 @@ decode_generic_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __
     for (int e = tid; e < R * P; e += kThreads) {
         const int r = e / P, p = e % P;
         float s = 0.f;
-        for (int n = 0; n < N; ++n) s += hs[int64_t(n) * P + p] * Io<T>::load(Ct, int64_t(r) * N + n);
+        for (int n = 0; n < N; ++n) s += hs[int64_t(n) * P + p] * Cv(int64_t(r) * N + n);
         Io<T>::store(y, bh * int64_t(R) * P + e, s + Dh * Io<T>::load(xt, e));
     }
     // this token becomes the carry of the next step (every read of the carry
     // precedes the barrier above)
     for (int e = tid; e < R * P; e += kThreads) carry_x[bh * int64_t(R) * P + e] = xt[e];
     if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += kThreads)
-            carry_B[(int64_t(pr ^ 1u) * nb * G + bg) * int64_t(R) * N + e] = Bt[e];
+        for (int e = tid; e < R * N; e += kThreads) {
+            T* dst = carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * int64_t(R) * N;
+            if constexpr (PRO)
+                Io<T>::store(dst, e, sNorm[e]);
+            else
+                dst[e] = Bt[e];
+        }
     if (tid == 0) par[bh] = pr ^ 1u;
 }
 
@@ -414,36 +645,39 @@ bool rows_kernel_sizes(int N, int P, int R) {
     return np && (R == 1 || R == 2 || R == 3 || R == 4 || (R == 8 && N * P <= 128 * 64));
 }
 
+// the step's prologue arguments (zeros when the step takes its inputs as given)
+DecodePrologue pro_of(const DecodeArgs& a) { return a.pro ? *a.pro : DecodePrologue{}; }
+
 // threads per workgroup: 2 row pairs per thread at R 1, one at R 2, 4 (as for
 // N 128, P 64), at most 1024 (512 took 11% longer at N 256 and at P 128)
-template <typename T, int R, int N, int P>
+template <typename T, int R, int N, int P, bool PRO>
 hipError_t launch_rows(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x, const T* B, const T* C, T* y) {
     constexpr int per = R == 1 ? 16 : 8;  // state floats per thread
     constexpr int want = N * P / per, cap = 1024;
     constexpr int NTH = want < cap ? want : cap;
-    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx,
-                       parity_words(a), a.rev, x, a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+    hipLaunchKernelGGL((decode_rows_kernel<T, R, NTH, N, P, PRO>), grid, dim3(NTH), 0, a.stream, a.h, cB, cx,
+                       parity_words(a), a.rev, pro_of(a), x, a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     return hipGetLastError();
 }
 
-template <typename T, int N, int P>
+template <typename T, int N, int P, bool PRO>
 hipError_t launch_rows_r(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x, const T* B, const T* C, T* y) {
     switch (a.R) {
-        case 1: return launch_rows<T, 1, N, P>(a, grid, cB, cx, x, B, C, y);
-        case 2: return launch_rows<T, 2, N, P>(a, grid, cB, cx, x, B, C, y);
-        case 3: return launch_rows<T, 3, N, P>(a, grid, cB, cx, x, B, C, y);
-        case 4: return launch_rows<T, 4, N, P>(a, grid, cB, cx, x, B, C, y);
+        case 1: return launch_rows<T, 1, N, P, PRO>(a, grid, cB, cx, x, B, C, y);
+        case 2: return launch_rows<T, 2, N, P, PRO>(a, grid, cB, cx, x, B, C, y);
+        case 3: return launch_rows<T, 3, N, P, PRO>(a, grid, cB, cx, x, B, C, y);
+        case 4: return launch_rows<T, 4, N, P, PRO>(a, grid, cB, cx, x, B, C, y);
         case 8:
-            if constexpr (N * P <= 128 * 64) return launch_rows<T, 8, N, P>(a, grid, cB, cx, x, B, C, y);
+            if constexpr (N * P <= 128 * 64) return launch_rows<T, 8, N, P, PRO>(a, grid, cB, cx, x, B, C, y);
             break;
     }
     return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <typename T, bool PRO>
 hipError_t launch_rows_sized(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const T* x, const T* B, const T* C, T* y) {
 #define M3_ROWS(NN, PP) \
-    if (a.N == NN && a.P == PP) return launch_rows_r<T, NN, PP>(a, grid, cB, cx, x, B, C, y);
+    if (a.N == NN && a.P == PP) return launch_rows_r<T, NN, PP, PRO>(a, grid, cB, cx, x, B, C, y);
     M3_ROWS(64, 32) M3_ROWS(64, 64) M3_ROWS(64, 128)
     M3_ROWS(128, 32) M3_ROWS(128, 64) M3_ROWS(128, 128)
     M3_ROWS(256, 32) M3_ROWS(256, 64) M3_ROWS(256, 128)
@@ -451,7 +685,20 @@ hipError_t launch_rows_sized(const DecodeArgs& a, dim3 grid, T* cB, T* cx, const
     return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <bool PRO>
+using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodePrologue, const bf16_t*, const float*,
+                          const float*, const float*, const float*, const bf16_t*, const bf16_t*, const float*,
+                          bf16_t*, int64_t, int, int);
+
+template <int N, bool PRO>
+MfmaKern<PRO> mfma_kernel_for(int R) {
+    return R == 2 ? decode_mfma_kernel<2, N, PRO>
+         : R == 3 ? decode_mfma_kernel<3, N, PRO>
+         : R == 4 ? decode_mfma_kernel<4, N, PRO>
+                  : decode_mfma_kernel<8, N, PRO>;
+}
+
+template <typename T, bool PRO>
 hipError_t launch_t(const DecodeArgs& a) {
     const dim3 grid(unsigned(a.b * a.H));
     T* cB = static_cast<T*>(a.carry_B);
@@ -464,38 +711,31 @@ hipError_t launch_t(const DecodeArgs& a) {
         if ((a.N == 64 || a.N == 128) && a.P == 64 && ((a.R >= 2 && a.R <= 4) || a.R == 8)) {
             // R 3 runs with a zero fourth rank slot (the staging zero-fills ranks past R); at
             // N 256 the 64 state values per lane spill (358 us against the row kernel's)
-            using K = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, const bf16_t*, const float*, const float*,
-                               const float*, const float*, const bf16_t*, const bf16_t*, const float*, bf16_t*,
-                               int64_t, int, int);
-            K kern = a.N == 64 ? (a.R == 2   ? decode_mfma_kernel<2, 64>
-                                  : a.R == 3 ? decode_mfma_kernel<3, 64>
-                                  : a.R == 4 ? decode_mfma_kernel<4, 64>
-                                             : decode_mfma_kernel<8, 64>)
-                               : (a.R == 2   ? decode_mfma_kernel<2, 128>
-                                  : a.R == 3 ? decode_mfma_kernel<3, 128>
-                                  : a.R == 4 ? decode_mfma_kernel<4, 128>
-                                             : decode_mfma_kernel<8, 128>);
-            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, parity_words(a), a.rev, x, a.dt,
-                               a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+            const auto kern = a.N == 64 ? mfma_kernel_for<64, PRO>(a.R) : mfma_kernel_for<128, PRO>(a.R);
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.h, cB, cx, parity_words(a), a.rev, pro_of(a), x,
+                               a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
             return hipGetLastError();
         }
     }
     if (a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4)) {
-        auto kern = a.R == 1 ? decode_rows_kernel<T, 1, M3_DECODE_THREADS_R1, 128, 64>
-                  : a.R == 2 ? decode_rows_kernel<T, 2, M3_DECODE_THREADS_R4, 128, 64>
-                             : decode_rows_kernel<T, 4, M3_DECODE_THREADS_R4, 128, 64>;
+        auto kern = a.R == 1 ? decode_rows_kernel<T, 1, M3_DECODE_THREADS_R1, 128, 64, PRO>
+                  : a.R == 2 ? decode_rows_kernel<T, 2, M3_DECODE_THREADS_R4, 128, 64, PRO>
+                             : decode_rows_kernel<T, 4, M3_DECODE_THREADS_R4, 128, 64, PRO>;
         const int nth = a.R == 1 ? M3_DECODE_THREADS_R1 : M3_DECODE_THREADS_R4;
-        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, parity_words(a), a.rev, x, a.dt,
-                           a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
+        hipLaunchKernelGGL(kern, grid, dim3(nth), 0, a.stream, a.h, cB, cx, parity_words(a), a.rev, pro_of(a), x,
+                           a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G);
     } else {
         if constexpr (std::is_same<T, bf16_t>::value) {
             // other state sizes, head dims and ranks (bf16 I/O): the same kernel, instantiated per (N, P, R)
             if (rows_kernel_sizes(a.N, a.P, a.R))
-                return launch_rows_sized<T>(a, grid, cB, cx, x, B, C, y);
+                return launch_rows_sized<T, PRO>(a, grid, cB, cx, x, B, C, y);
         }
-        hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(kThreads), 0, a.stream, a.h, cB, cx,
-                           parity_words(a), a.rev, x, a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H, a.G,
-                           a.P, a.N, a.R);
+        // the fused step keeps B_t and C_t in LDS: [2][R][N] fp32
+        const size_t lds = PRO ? size_t(2) * a.R * a.N * sizeof(float) : 0;
+        if (PRO && int64_t(a.R) * a.N > kDecodeFusedGenericRN) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_generic_kernel<T, PRO>), grid, dim3(kThreads), lds, a.stream, a.h, cB, cx,
+                           parity_words(a), a.rev, pro_of(a), x, a.dt, a.A, a.omega, a.lam, B, C, a.D, y, a.b, a.H,
+                           a.G, a.P, a.N, a.R);
     }
     return hipGetLastError();
 }
@@ -523,7 +763,8 @@ hipError_t launch_carry_init(void* carry, const void* src, int64_t b, int H, int
 
 hipError_t launch_decode(const DecodeArgs& a) {
     if (a.b * a.H > 0x7fffffff) return hipErrorInvalidValue;
-    return a.io == M3_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
+    if (a.pro) return a.io == M3_BF16 ? launch_t<bf16_t, true>(a) : launch_t<float, true>(a);
+    return a.io == M3_BF16 ? launch_t<bf16_t, false>(a) : launch_t<float, false>(a);
 }
 
 }  // namespace m3

@@ -353,9 +353,14 @@ m3_status m3_decode_state_init(m3_decode_state* st, const m3_dims* dims, int32_t
     return M3_OK;
 }
 
-m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t, const float* A,
-                         const float* omega, const float* lambda_t, const void* B_t, const void* C_t,
-                         const float* D, int32_t R, void* y_t, void* stream) {
+namespace {
+
+// m3_decode_step and m3_decode_step_fused: the checks and the launch; pro is
+// NULL for the plain step (dt_t / lambda_t are then the step and the weight,
+// B_t / C_t the normalised rows)
+m3_status decode_step_impl(m3_decode_state* st, const void* x_t, const float* dt_t, const float* A,
+                           const float* omega, const float* lambda_t, const void* B_t, const void* C_t,
+                           const float* D, int32_t R, void* y_t, void* stream, const m3::DecodePrologue* pro) {
     g_err[0] = 0;
     if (!st) return fail(M3_EINVAL, "state is NULL");
     m3_status s = check_dims(&st->dims, st->R);
@@ -364,11 +369,18 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
     if (R != st->R) return fail(M3_ESHAPE, "R %d differs from the state's %d", R, st->R);
     const m3_dims& d = st->dims;
     const int64_t b = d.batch;
+    if (pro) {
+        if (!(pro->eps >= 0.f)) return fail(M3_EINVAL, "eps must be >= 0");
+        if (int64_t(R) * d.dstate > m3::kDecodeFusedGenericRN)
+            return fail(M3_EUNSUPPORTED, "R * N = %lld above %lld for the fused step", (long long)R * d.dstate,
+                        (long long)m3::kDecodeFusedGenericRN);
+    }
     if (b == 0) { st->t += 1; return M3_OK; }
     struct Req { const char* name; const void* p; bool optional; };
     // omega and lambda_t may be NULL: omega = 0 (real-valued state) and lambda = 1 (Euler / Mamba-2)
-    const Req req[] = {{"x_t", x_t, false}, {"dt_t", dt_t, false}, {"A", A, false}, {"omega", omega, true},
-                       {"lambda_t", lambda_t, true}, {"B_t", B_t, false}, {"C_t", C_t, false}, {"D", D, false},
+    const Req req[] = {{"x_t", x_t, false}, {pro ? "dt_raw_t" : "dt_t", dt_t, false}, {"A", A, false},
+                       {"omega", omega, true}, {pro ? "lambda_raw_t" : "lambda_t", lambda_t, true},
+                       {pro ? "B_raw_t" : "B_t", B_t, false}, {pro ? "C_raw_t" : "C_t", C_t, false}, {"D", D, false},
                        {"y_t", y_t, false}, {"state h", st->h, false}, {"state carry_B", st->carry_B, false},
                        {"state carry_x", st->carry_x, false}};
     for (const Req& r : req) {
@@ -392,11 +404,35 @@ m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t
 
     m3::DecodeArgs a{st->h, st->carry_B, st->carry_x, x_t, dt_t, A, omega,
                      lambda_t, B_t, C_t, D, y_t, b, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R,
-                     st->io_dtype, reinterpret_cast<hipStream_t>(stream), int(st->t & 1)};
+                     st->io_dtype, reinterpret_cast<hipStream_t>(stream), int(st->t & 1), pro};
     hipError_t e = m3::launch_decode(a);
     if (e != hipSuccess) return fail(M3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
     st->t += 1;
     return M3_OK;
+}
+
+}  // namespace
+
+m3_status m3_decode_step(m3_decode_state* st, const void* x_t, const float* dt_t, const float* A,
+                         const float* omega, const float* lambda_t, const void* B_t, const void* C_t,
+                         const float* D, int32_t R, void* y_t, void* stream) {
+    return decode_step_impl(st, x_t, dt_t, A, omega, lambda_t, B_t, C_t, D, R, y_t, stream, nullptr);
+}
+
+m3_status m3_decode_step_fused(m3_decode_state* st, const void* x_t, const float* dt_raw_t, const float* dt_bias,
+                               const float* A, const float* omega, const float* lambda_raw_t, const void* B_raw_t,
+                               const void* C_raw_t, const float* B_weight, const float* B_bias,
+                               const float* C_weight, const float* C_bias, float eps, const float* D, int32_t R,
+                               void* y_t, void* stream) {
+    const void* opt[] = {dt_bias, B_weight, B_bias, C_weight, C_bias};
+    const char* names[] = {"dt_bias", "B_weight", "B_bias", "C_weight", "C_bias"};
+    for (int i = 0; i < 5; ++i)
+        if (opt[i] && !aligned16(opt[i])) {
+            g_err[0] = 0;
+            return fail(M3_EALIGN, "%s is not 16-byte aligned", names[i]);
+        }
+    const m3::DecodePrologue pro{B_weight, B_bias, C_weight, C_bias, dt_bias, eps};
+    return decode_step_impl(st, x_t, dt_raw_t, A, omega, lambda_raw_t, B_raw_t, C_raw_t, D, R, y_t, stream, &pro);
 }
 
 size_t m3_prefill_backward_workspace_size(const m3_dims* dims, int32_t R) {

@@ -31,6 +31,17 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+// The input prologue fused into a decode step (m3_decode_step_fused): the step
+// reads raw B_t, C_t, dt_t, lambda_t and applies m3_prologue's reading itself.
+struct DecodePrologue {
+    const float* B_weight;  // [G][R][N] or NULL (1)
+    const float* B_bias;    // [G][R][N] or NULL (0)
+    const float* C_weight;
+    const float* C_bias;
+    const float* dt_bias;   // [H] or NULL (0)
+    float eps;
+};
+
 struct DecodeArgs {
     float* h;
     void* carry_B;         // two slots [2][b][G][R][N] of the previous token's B rows, then parity words [b][H]
@@ -49,7 +60,11 @@ struct DecodeArgs {
     m3_dtype io;
     hipStream_t stream;
     int rev;               // walk the (b, h) workgroups backwards (a block-order hint: every other step)
+    const DecodePrologue* pro;  // NULL: B, C, dt, lambda are the recurrence's inputs as given
 };
+
+// rows of R * N of the fused decode step's generic kernel held in LDS (B and C, fp32)
+constexpr int64_t kDecodeFusedGenericRN = 8192;
 
 // Bytes of the two B slots at the start of a decode carry_B buffer (16-byte
 // aligned end; the per-head parity words follow).

@@ -57,6 +57,16 @@ __device__ __forceinline__ unsigned rot_pair(unsigned w, CS t) {
     const float b0 = lo16(w), b1 = hi16(w);
     return pack2(t.c * b0 + t.s * b1, t.c * b1 - t.s * b0);
 }
+// sum of the two products of packed bf16 pairs, in fp32
+__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), 0.f, false);
+}
+// one packed bf16 pair (b0, b1) turned by -Phi, with cs = packed bf16 (cos Phi,
+// sin Phi): (c b0 + s b1, c b1 - s b0), two dot products
+__device__ __forceinline__ unsigned rot_cs(unsigned w, unsigned cs) {
+    const unsigned ms_c = __builtin_amdgcn_perm(cs, cs, 0x01000302u) ^ 0x00008000u;  // (-s, c)
+    return pack2(dot2_bf16(cs, w), dot2_bf16(ms_c, w));
+}
 // Transposing LDS load (ds_read_b64_tr_b16): in each group of 16 lanes, lane t
 // gives the address of 4 consecutive 16-bit values of row t / 4 (columns
 // 4 (t % 4) ..); lane j receives column j of those 4 rows. From a row-major

@@ -102,14 +102,7 @@ __device__ __forceinline__ void stage_x(const PreX<R>& px, uint16_t* sxt, int st
 
 // C~ pair from a raw pair (c0, c1) and a packed bf16 (cos, sin): turned by -Phi,
 // (c c0 + s c1, c c1 - s c0), as two bf16 dot products accumulated in fp32
-__device__ __forceinline__ unsigned rot_dot(unsigned w, unsigned cs) {
-    const unsigned ms_c = __builtin_amdgcn_perm(cs, cs, 0x01000302u) ^ 0x00008000u;  // (-s, c)
-    const float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cs), __builtin_bit_cast(bf16x2, w),
-                                                    0.f, false);
-    const float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ms_c), __builtin_bit_cast(bf16x2, w),
-                                                    0.f, false);
-    return pack2(a, b);
-}
+__device__ __forceinline__ unsigned rot_dot(unsigned w, unsigned cs) { return rot_cs(w, cs); }
 
 }  // namespace ws4
 

@@ -192,6 +192,20 @@ def test_decode_argument_errors(lib):
     assert lib.m3_decode_step(ctypes.byref(st), *args[:7], None, 2, f(30), None) == 1   # D NULL
     assert lib.m3_decode_step(ctypes.byref(st), *args, 2, ctypes.c_void_p(FAKE + 10 * (1 << 30) + 64), None) == 1
     assert st.t == 5                                  # failed steps do not advance the counter
+    # the fused step: the same checks, plus its prologue arguments
+    fused = lambda R=2, eps=1e-6, D=f(17), dtb=None: lib.m3_decode_step_fused(
+        ctypes.byref(st), f(10), f(11), dtb, f(12), f(13), f(14), f(15), f(16), None, None, None, None,
+        ctypes.c_float(eps), D, R, f(30), None)
+    assert fused(R=1) == 2
+    assert fused(eps=-1.0) == 1
+    assert fused(D=None) == 1
+    assert fused(dtb=ctypes.c_void_p(FAKE + 8)) == 4
+    big = bd.M3DecodeState()
+    big.h, big.carry_B, big.carry_x, big.t = FAKE, FAKE + (1 << 30), FAKE + 2 * (1 << 30), 0
+    big.dims, big.R, big.io_dtype = _dims(N=4096), 4, 0  # R * N = 16384 rows of LDS: unsupported
+    assert lib.m3_decode_step_fused(ctypes.byref(big), f(10), f(11), None, f(12), f(13), f(14), f(15), f(16), None,
+                                    None, None, None, ctypes.c_float(1e-6), f(17), 4, f(30), None) == 5
+    assert st.t == 5 and big.t == 0
 
 
 def test_carry_bytes(lib):

@@ -14,7 +14,7 @@ import torch
 
 from oracle import backward as bw
 from mamba_ssm_scan_amd import binding, inputs
-from util import TOL, f64
+from tests.util import TOL, f64
 
 pytestmark = pytest.mark.gpu
 

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from mamba_ssm_scan_amd import inputs
-from util import TOL, assert_close, f64
+from tests.util import TOL, assert_close, f64
 
 pytestmark = pytest.mark.gpu
 
