@@ -184,14 +184,16 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
     by = prefill_bytes(w.batch, w.seqlen, w.heads, G, w.headdim, w.dstate, w.rank)
     if no_lam:
         by -= w.batch * w.seqlen * w.heads * 4
-    fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, w.chunk)
+    # algorithmic flops at the chunk the kernel walks (the plan's: at most 32 tokens at R 8)
+    qk = -(-w.seqlen // plan.n_chunks) if plan.n_chunks else w.chunk
+    fl = prefill_flops(w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank, qk)
     name = base + (f" ({special})" if special else "") + (f" G={G}" if G != 1 else "")
     if (w.dstate, w.rank, w.headdim) != (inputs.WORKLOADS[wid].dstate, inputs.WORKLOADS[wid].rank,
                                           inputs.WORKLOADS[wid].headdim):
         name += f" with N={w.dstate} R={w.rank} P={w.headdim}"
     r = {"workload": name, "ms_per_call": ms, "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
          "hbm_gbs": by / (ms * 1e-3) / 1e9, "mfma_tflops": fl / (ms * 1e-3) / 1e12,
-         "bytes": by, "flops": fl, "path": {binding.M3_PATH_MFMA: "mfma", binding.M3_PATH_SCAN: "scan"}.get(plan.path, "generic"),
+         "bytes": by, "flops": fl, "chunk": qk, "path": {binding.M3_PATH_MFMA: "mfma", binding.M3_PATH_SCAN: "scan"}.get(plan.path, "generic"),
          "segments": plan.segments, **_pct(t)}
     r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
     r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS

@@ -97,9 +97,10 @@ m3_status make_plan(const m3_dims* d, int32_t R, int32_t chunk, m3_dtype io, m3_
     if (chunk > 4096) return fail(M3_EUNSUPPORTED, "chunk %d above 4096", chunk);
     std::memset(p, 0, sizeof *p);
     const int64_t L = d->seqlen;
+    const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
+    if (mfma) chunk = m3::mfma_kernel_chunk(R, chunk);
     p->n_chunks = (L + chunk - 1) / chunk;
     p->last_chunk_len = L == 0 ? 0 : L - (p->n_chunks - 1) * chunk;
-    const bool mfma = m3::mfma_path_supported(d->headdim, d->dstate, R, chunk, io);
     p->path = mfma ? M3_PATH_MFMA
                    : m3::scan_path_supported(d->headdim, d->dstate, R, io) ? M3_PATH_SCAN : M3_PATH_GENERIC;
     p->segments = (mfma && m3::mfma_segments_supported(R, d->dstate, d->headdim))
@@ -277,8 +278,9 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
         else
             e = hipSuccess;
     } else {
+        const int32_t kchunk = plan.path == M3_PATH_MFMA ? m3::mfma_kernel_chunk(R, chunk) : chunk;
         m3::PrefillArgs a{x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x,
-                          b, L, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R, chunk, io_dtype,
+                          b, L, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R, kchunk, io_dtype,
                           plan, workspace, st};
         e = plan.path == M3_PATH_MFMA   ? m3::launch_prefill_mfma(a)
             : plan.path == M3_PATH_SCAN ? m3::launch_prefill_scan(a)

@@ -153,6 +153,7 @@ constexpr long kLookbackSpinLimit = 1L << 24;
 // device address of m3_prefill_noalloc's scratch on the current device
 m3_status noalloc_scratch(void** ptr);
 // the MFMA path splits the sequence into segments (look-back) at these ranks
+int32_t mfma_kernel_chunk(int32_t R, int32_t chunk);
 bool mfma_segments_supported(int32_t R, int32_t N, int32_t P);
 constexpr int32_t kMfmaMaxN = 512;   // largest N of the chunked path (passes of 128 rows)
 constexpr int32_t kMfmaMaxP = 1024;  // largest P of the chunked path (passes of 64 columns)

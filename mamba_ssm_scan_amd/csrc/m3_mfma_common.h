@@ -111,7 +111,9 @@ __device__ __forceinline__ float row_last(float v, int lane) {
 // token whose rows fall in the same 16-row tile)
 template <int LR>
 __device__ __forceinline__ float tile_last(float v, int lane) {
-    if constexpr (LR == 2) {
+    if constexpr (LR == 3) {  // two tokens per tile: lane 2k + 1 (DPP quad_perm [1, 1, 3, 3])
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xf5, 0xf, 0xf, false));
+    } else if constexpr (LR == 2) {
         return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false));
     } else if constexpr (LR == 1) {
         const int q = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false);  // lane 4k+3

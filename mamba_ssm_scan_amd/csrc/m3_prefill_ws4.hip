@@ -1,6 +1,8 @@
-// m3_prefill_ws4.hip -- chunked prefill at MIMO ranks R = 2, 4 for the state of
-// the workloads (N = 128 rows, P = 64 columns), chunk <= 64 tokens, bf16 I/O,
-// fp32 state, with wave specialisation.
+// m3_prefill_ws4.hip -- chunked prefill at MIMO ranks R = 2, 4 and 8 for the
+// state of the workloads (N = 128 rows, P = 64 columns), bf16 I/O, fp32 state,
+// with wave specialisation. A chunk holds at most 64 tokens at R 2 and 4 and at
+// most 32 at R 8, so that it has at most 256 (token, rank) rows: the score tile
+// count, the LDS carve and the register budget of R 4 at 64 tokens.
 //
 // The recurrence and its chunked form are those of m3_prefill_mfma.hip (the
 // complex transition as data-dependent RoPE on B and C, the decay x width-2
@@ -8,9 +10,9 @@
 // §2.1-§2.3, Fig. 2 and Fig. 3). One workgroup walks the chunks of one
 // (batch, head) with two kinds of waves, two waves per SIMD:
 //
-//   output waves (0-3): the chunk's outputs. Wave w holds R of the chunk's 4R
-//     16-row strips (at R 4 strips w, 7-w, 8+w, 15-w: an even share of the
-//     triangle), their C~ rows and their y accumulators in registers, and walks
+//   output waves (0-3): the chunk's outputs. Wave w holds a quarter of the
+//     chunk's 16-row strips (with 16 strips, strips w, 7-w, 8+w, 15-w: an even
+//     share of the triangle), their C~ rows and their y accumulators in registers, and walks
 //     the score tiles pair by pair: each B~ pair, X^T pair and mask-scalar load
 //     serves all its strips. Inter-chunk term e^{S_i} C~_i g from g^T in LDS.
 //   state waves (4-7): the state update of the chunk (the fp32 state lives in
@@ -36,18 +38,21 @@ constexpr int NST = 64 * NSW;   // state-wave threads
 // sizes at rank R
 template <int R>
 struct Cfg {
-    static constexpr int LR = R == 1 ? 0 : R == 2 ? 1 : 2;  // log2 R
-    static constexpr int QRP = 64 * R;                      // rows (token, rank) per chunk
+    static constexpr int LR = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;  // log2 R
+    static constexpr int TQ = R <= 4 ? 64 : 256 / R;        // most tokens per chunk
+    static constexpr int QRP = TQ * R;                      // rows (token, rank) per chunk
     static constexpr int XS = QRP + 8;                      // X^T row stride (bf16)
     static constexpr int PT = P / 16;                       // 16-column tiles of the state
     static constexpr int PC = P / 8;                        // 8-column pieces of an X row
-    static constexpr int UPT = 64 * 16 / NST;               // (token, 8-column piece) units of B per state thread
+    static constexpr int UPT = TQ * 16 / NST;               // (token, 8-column piece) units of B per state thread
     static constexpr int XU = QRP / 2 * PC;                 // (row pair, 8 columns) units of X
     static constexpr int XPT = (XU + NST - 1) / NST;        // ... per state thread
     static constexpr int SPW = QRP / 16 / NOW;              // strips per output wave
     static constexpr int TPW = 8 * PT / NSW;                // 16x16 state tiles per state wave
     static constexpr int MR = TPW / PT;                     // 16-row state tiles per state wave
-    static_assert(UPT == 4 && SPW == R && MR == 2 && (R == 1 || R == 2 || R == 4), "split");
+    static_assert(UPT >= 1 && UPT * NST == TQ * 16 && SPW >= 1 && SPW <= 4 && MR == 2 &&
+                      (R == 2 || R == 4 || R == 8),
+                  "split");
 };
 
 // the strips of output wave w, ascending (snake order over the chunk's strips)
@@ -579,11 +584,13 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 
 }  // namespace
 
-// the state of the workloads (N 128, P 64) at R 2 or 4 in one pass, without sequence
-// segments (R 1 runs on the 12-wave kernel of m3_prefill_mfma.hip, faster there)
+// the state of the workloads (N 128, P 64) at R 2, 4 (chunks of at most 64
+// tokens) or 8 (at most 32) in one pass, without sequence segments (R 1 runs on
+// the 12-wave kernel of m3_prefill_mfma.hip, faster there)
 bool ws4_supported(const PrefillArgs& a) {
-    return a.io == M3_BF16 && (a.R == 2 || a.R == 4) && a.N == N && a.P == P && a.chunk >= 1 && a.chunk <= 64 &&
-           a.plan.segments == 1;
+    const int most = a.R == 8 ? 32 : 64;
+    return a.io == M3_BF16 && (a.R == 2 || a.R == 4 || a.R == 8) && a.N == N && a.P == P && a.chunk >= 1 &&
+           a.chunk <= most && a.plan.segments == 1;
 }
 
 hipError_t launch_prefill_ws4(const PrefillArgs& a) {
@@ -601,6 +608,7 @@ hipError_t launch_prefill_ws4(const PrefillArgs& a) {
     switch (a.R) {
         case 2: return rot ? launch(prefill_ws4_kernel<2, true>) : launch(prefill_ws4_kernel<2, false>);
         case 4: return rot ? launch(prefill_ws4_kernel<4, true>) : launch(prefill_ws4_kernel<4, false>);
+        case 8: return rot ? launch(prefill_ws4_kernel<8, true>) : launch(prefill_ws4_kernel<8, false>);
     }
     return hipErrorInvalidValue;
 }

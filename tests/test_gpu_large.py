@@ -34,6 +34,13 @@ PCASES = [
 ]
 
 
+def _expected_path(io, N, P, R):
+    """bf16: the chunked MFMA kernels at R 1-4 and at R 8 with N 128, P 64; the token walk for the rest."""
+    if io != "bf16":
+        return binding.M3_PATH_GENERIC
+    return binding.M3_PATH_MFMA if R <= 4 or (R == 8 and N == 128 and P == 64) else binding.M3_PATH_SCAN
+
+
 def _path(p, chunk):
     b, L, H, R, P = p["x"].shape
     G, N = p["B"].shape[2], p["B"].shape[4]
@@ -47,12 +54,58 @@ def test_prefill_large_state_and_rank(case):
     print(f"prefill large case {case}", flush=True)
     p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=P, dstate=N, rank=R, io_dtype=io,
                             dist="lm", wid=1000 + PCASES.index(case), h0_std=0.1, with_carry=True)
-    expect = binding.M3_PATH_GENERIC if io != "bf16" else binding.M3_PATH_MFMA if R <= 4 else binding.M3_PATH_SCAN
-    assert _path(p, chunk) == expect
+    assert _path(p, chunk) == _expected_path(io, N, P, R)
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
     assert_close(y, y_ref, TOL[io], "y")
     assert_close(h, h_ref, TOL[io], "h_out")
+
+
+R8CASES = [
+    # b, L, H, G, chunk, h0_std, carry
+    (1, 100, 2, 1, 32, 0.1, True),    # four chunks of 32 tokens, a ragged last one
+    (2, 77, 3, 3, 64, 0.0, False),    # chunk 64 asked: walked in chunks of 32; one B, C per head
+    (1, 45, 2, 2, 16, 0.1, True),     # chunk 16, two groups
+    (1, 33, 2, 1, 7, 0.1, False),     # chunk 7
+    (2, 5, 2, 1, 32, 0.1, True),      # fewer tokens than a chunk
+]
+
+
+@pytest.mark.parametrize("case", R8CASES, ids=[str(c) for c in R8CASES])
+def test_prefill_r8_chunked(case):
+    """R 8 at N 128, P 64 on the wave-specialised chunked kernel (chunks of at most 32 tokens)."""
+    b, L, H, G, chunk, h0s, carry = case
+    print(f"R 8 chunked case {case}", flush=True)
+    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=128, rank=8, io_dtype="bf16",
+                            dist="lm", wid=1100 + R8CASES.index(case), h0_std=h0s, with_carry=carry)
+    assert _path(p, chunk) == binding.M3_PATH_MFMA
+    plan = binding.plan(binding.dims(b, L, H, G, 64, 128), 8, chunk, binding.M3_BF16)
+    assert plan.n_chunks == (L + min(chunk, 32) - 1) // min(chunk, 32)
+    y_ref, h_ref = oracle.scan(p)
+    y, h = gpu_prefill(p, chunk)
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
+
+
+@pytest.mark.parametrize("drop", ["omega", "lam", "both"])
+def test_prefill_r8_chunked_special_cases(drop):
+    """omega NULL (omega = 0) and lambda NULL (lambda = 1) on the R 8 chunked kernel."""
+    print(f"R 8 chunked special case {drop}", flush=True)
+    p = inputs.make_problem(batch=1, seqlen=70, heads=2, groups=1, headdim=64, dstate=128, rank=8, io_dtype="bf16",
+                            dist="lm", wid=1120, h0_std=0.1, with_carry=True)
+    q = dict(p)
+    no_om, no_lam = drop in ("omega", "both"), drop in ("lam", "both")
+    if no_om:
+        q["omega"] = torch.zeros_like(p["omega"])
+    if no_lam:
+        q["lam"] = torch.ones_like(p["lam"])
+    y_ref, h_ref = oracle.scan(q)
+    d = to_dev(p)
+    y, h = binding.prefill(d["x"], d["dt"], d["A"], None if no_om else d["omega"], None if no_lam else d["lam"],
+                           d["B"], d["C"], d["D"], 8, 32, d["h0"], carry_B=d["carry_B"], carry_x=d["carry_x"])
+    torch.cuda.synchronize()
+    assert_close(y, y_ref, TOL["bf16"], "y")
+    assert_close(h, h_ref, TOL["bf16"], "h_out")
 
 
 @pytest.mark.parametrize("drop", ["omega", "lam", "both"])
@@ -84,7 +137,7 @@ def test_workload_shapes_larger_state_and_rank(wid, dstate, rank):
     print(f"workload {wid} shape with N {N}, R {R}", flush=True)
     p = inputs.make_problem(batch=w.batch, seqlen=w.seqlen, heads=w.heads, groups=1, headdim=w.headdim, dstate=N,
                             rank=R, io_dtype=w.io_dtype, dist=w.dist, wid=wid, device="cuda")
-    assert _path(p, w.chunk) == (binding.M3_PATH_MFMA if R in (1, 2, 4) else binding.M3_PATH_SCAN)
+    assert _path(p, w.chunk) == binding.M3_PATH_MFMA  # R 8 at N 128, P 64: the wave-specialised chunked kernel
     y, h = binding.prefill(p["x"], p["dt"], p["A"], p["omega"], p["lam"], p["B"], p["C"], p["D"], R, w.chunk)
     torch.cuda.synchronize()
     y_ref, h_ref = oracle.scan(to_host(p))
