@@ -77,8 +77,8 @@ typedef struct m3_dims {
 /* How m3_prefill will split the work (all integers, exact). */
 typedef struct m3_plan {
     int64_t n_chunks;        /* ceil(L / chunk'), chunk' the chunk the kernels walk: the chunk
-                                asked for, except on the MFMA path at R 8, where chunks hold
-                                at most 32 tokens (the result does not depend on it) */
+                                asked for, except on the MFMA path at R 5 to 8, where chunks
+                                hold at most 32 tokens (the result does not depend on it) */
     int64_t last_chunk_len;  /* L - (n_chunks - 1) * chunk', 0 when L == 0 */
     int32_t segments;        /* sequence segments per (b, h) walked in parallel; the
                                 environment variable M3_PREFILL_SEGMENTS (a positive
@@ -95,12 +95,12 @@ typedef struct m3_plan {
  *          at most 128 state rows and 64 columns (zero-padded inside the kernel
  *          where a pass holds fewer); with N above 128 the row passes' outputs
  *          are summed in fp32 in the workspace (the plan then asks for
- *          b*L*H*R*P*4 bytes); also R 8 at exactly N 128, P 64 (any chunk,
- *          walked in chunks of at most 32 tokens, no sequence segments).
+ *          b*L*H*R*P*4 bytes); also R 5 to 8 at exactly N 128, P 64 (any
+ *          chunk, walked in chunks of at most 32 tokens, no sequence segments).
  * SCAN:    token-by-token walk with the state in registers and the rank
  *          contractions on matrix cores, bf16 I/O, N and P multiples of 16 with
- *          N <= 256, P <= 64, R 5 to 8 (chunk unused; R 8 at N 128, P 64 takes
- *          the MFMA path). */
+ *          N <= 256, P <= 64, R 5 to 8 (chunk unused; at N 128, P 64 these
+ *          ranks take the MFMA path). */
 enum { M3_PATH_GENERIC = 0, M3_PATH_MFMA = 1, M3_PATH_SCAN = 2 };
 
 /*

@@ -76,13 +76,16 @@ template <int R>
 __device__ __forceinline__ void load_prex(PreX<R>& px, const ChunkBase& cb, int H, int stid) {
     using CF = Cfg<R>;
     constexpr int LR = CF::LR;
+    const int rin = cb.rin;  // the caller's rank: x rows of ranks rin .. R-1 are zero
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int m = 0; m < CF::XPT; ++m) {
         if (CF::XU % NST != 0 && stid + m * NST >= CF::XU) break;
         const int rho0 = 2 * (stid / CF::PC + m * (NST / CF::PC));
         const int col = 8 * (stid % CF::PC);
-        px.x0[m] = load_tok(cb.x, rho0 >> LR, cb.nq, H * R * P, (rho0 & (R - 1)) * P + col);
-        px.x1[m] = load_tok(cb.x, (rho0 + 1) >> LR, cb.nq, H * R * P, ((rho0 + 1) & (R - 1)) * P + col);
+        const int r0 = rho0 & (R - 1), r1 = (rho0 + 1) & (R - 1);
+        px.x0[m] = r0 < rin ? load_tok(cb.x, rho0 >> LR, cb.nq, H * rin * P, r0 * P + col) : z;
+        px.x1[m] = r1 < rin ? load_tok(cb.x, (rho0 + 1) >> LR, cb.nq, H * rin * P, r1 * P + col) : z;
     }
 }
 
@@ -111,13 +114,17 @@ __device__ __forceinline__ unsigned rot_dot(unsigned w, unsigned cs) { return ro
 
 }  // namespace ws4
 
-template <int R, bool ROT>
+// RP: the caller's rank rin_ is below R (3 on the R 4 kernel, 5 to 7 on the R 8
+// one): ranks rin_ .. R-1 are zero rows of B, C and x and their y rows are not
+// stored; without RP, rin_ is R.
+template <int R, bool ROT, bool RP>
 __global__ void __launch_bounds__(64 * (ws4::NOW + ws4::NSW))
 prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                    const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                    const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                    uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
-                   const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks, int64_t nbh) {
+                   const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks, int64_t nbh,
+                   int rin_) {
     using namespace ws4;
     using CF = Cfg<R>;
     constexpr int LR = CF::LR, QRP = CF::QRP, XS = CF::XS, UPT = CF::UPT, SPW = CF::SPW, TPW = CF::TPW;
@@ -134,6 +141,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int RI = RP ? rin_ : R;  // the caller's rank: row strides of B, C, x, y, the carry
     int64_t bh;
     {
         // XCD-aware order: the 8 XCDs take blocks round-robin; each gets a
@@ -152,15 +160,15 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
     auto chunk_base = [&](int64_t cc) {
         const int64_t c0 = cc * Q, tok0 = b * L + c0;
         ChunkBase cb;
-        cb.B = Bm + (tok0 * G + grp) * int64_t(R * N);
-        cb.C = Cm + (tok0 * G + grp) * int64_t(R * N);
-        cb.x = x + (tok0 * H + h) * int64_t(R * P);
+        cb.B = Bm + (tok0 * G + grp) * int64_t(RI * N);
+        cb.C = Cm + (tok0 * G + grp) * int64_t(RI * N);
+        cb.x = x + (tok0 * H + h) * int64_t(RI * P);
         cb.nq = int(L - c0 < Q ? L - c0 : Q);
         cb.nin = N;
         cb.nrow = N;
         cb.pin = P;
         cb.pcol = P;
-        cb.rin = R;
+        cb.rin = RI;
         return cb;
     };
 
@@ -199,7 +207,8 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             for (int m = 0; m < UPT; ++m) {
                 const int i = (stid >> 4) + m * (NST / 16);
 #pragma unroll
-                for (int r = 0; r < R; ++r) pre.b[m][r] = load_tok(cb.B, i, nq, G * R * N, r * N + 8 * pc);
+                for (int r = 0; r < R; ++r)
+                    pre.b[m][r] = r < RI ? load_tok(cb.B, i, nq, G * RI * N, r * N + 8 * pc) : u32x4{0u, 0u, 0u, 0u};
             }
         };
         // RoPE of the loaded chunk in registers (B rows turned in place; the
@@ -274,9 +283,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                     if (carry_B) {
                         float s = 0.f;
 #pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            s += bf16_to_f32(carry_B[((b * G + grp) * R + r) * N + n]) *
-                                 bf16_to_f32(carry_x[(bh * R + r) * P + p]);
+                        for (int r = 0; r < RI; ++r)
+                            s += bf16_to_f32(carry_B[((b * G + grp) * RI + r) * N + n]) *
+                                 bf16_to_f32(carry_x[(bh * RI + r) * P + p]);
                         v += dl0 * s;
                     }
                     gst[m][e] = v;
@@ -391,7 +400,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             const int rho = 16 * strip[k] + l16;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                craw[k][ks] = load_tok(cb.C, rho >> LR, cb.nq, G * R * N, (rho & (R - 1)) * N + 32 * ks + 8 * g4);
+                craw[k][ks] = (rho & (R - 1)) < RI ? load_tok(cb.C, rho >> LR, cb.nq, G * RI * N,
+                                                              (rho & (R - 1)) * N + 32 * ks + 8 * g4)
+                                                     : u32x4{0u, 0u, 0u, 0u};
         }
     };
     lds_barrier();  // Y(0)
@@ -567,9 +578,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 #pragma unroll
         for (int k = 0; k < SPW; ++k) {
             const int rho_i = 16 * strip[k] + l16;
-            if ((rho_i >> LR) < nq) {
+            if ((rho_i >> LR) < nq && (rho_i & (R - 1)) < RI) {
                 const int i = rho_i >> LR, r = rho_i & (R - 1);
-                uint16_t* yr = y + ((b * L + c * Q + i) * H + h) * int64_t(R * P) + r * P;
+                uint16_t* yr = y + ((b * L + c * Q + i) * H + h) * int64_t(RI * P) + r * P;
 #pragma unroll
                 for (int q = 0; q < PT; ++q) {
                     const int p = 16 * q + 4 * g4;
@@ -588,9 +599,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 // tokens) or 8 (at most 32) in one pass, without sequence segments (R 1 runs on
 // the 12-wave kernel of m3_prefill_mfma.hip, faster there)
 bool ws4_supported(const PrefillArgs& a) {
-    const int most = a.R == 8 ? 32 : 64;
-    return a.io == M3_BF16 && (a.R == 2 || a.R == 4 || a.R == 8) && a.N == N && a.P == P && a.chunk >= 1 &&
-           a.chunk <= most && a.plan.segments == 1;
+    const int most = a.R > 4 ? 32 : 64;  // R 3 on the R 4 kernel, R 5 to 7 on the R 8 one (zero ranks)
+    return a.io == M3_BF16 && a.R >= 2 && a.R <= 8 && a.N == N && a.P == P && a.chunk >= 1 && a.chunk <= most &&
+           a.plan.segments == 1;
 }
 
 hipError_t launch_prefill_ws4(const PrefillArgs& a) {
@@ -601,14 +612,19 @@ hipError_t launch_prefill_ws4(const PrefillArgs& a) {
                            static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh);
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
+                           a.R);
         return hipGetLastError();
     };
     const bool rot = a.omega != nullptr;
     switch (a.R) {
-        case 2: return rot ? launch(prefill_ws4_kernel<2, true>) : launch(prefill_ws4_kernel<2, false>);
-        case 4: return rot ? launch(prefill_ws4_kernel<4, true>) : launch(prefill_ws4_kernel<4, false>);
-        case 8: return rot ? launch(prefill_ws4_kernel<8, true>) : launch(prefill_ws4_kernel<8, false>);
+        case 2: return rot ? launch(prefill_ws4_kernel<2, true, false>) : launch(prefill_ws4_kernel<2, false, false>);
+        case 3: return rot ? launch(prefill_ws4_kernel<4, true, true>) : launch(prefill_ws4_kernel<4, false, true>);
+        case 4: return rot ? launch(prefill_ws4_kernel<4, true, false>) : launch(prefill_ws4_kernel<4, false, false>);
+        case 5:
+        case 6:
+        case 7: return rot ? launch(prefill_ws4_kernel<8, true, true>) : launch(prefill_ws4_kernel<8, false, true>);
+        case 8: return rot ? launch(prefill_ws4_kernel<8, true, false>) : launch(prefill_ws4_kernel<8, false, false>);
     }
     return hipErrorInvalidValue;
 }

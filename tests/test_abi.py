@@ -69,9 +69,10 @@ def test_plan_generic_workspace(lib):
 
 @pytest.mark.parametrize("N,P,R,io,path", [
     (128, 64, 1, "bf16", "MFMA"), (128, 64, 4, "bf16", "MFMA"), (128, 64, 3, "bf16", "MFMA"),
-    (128, 64, 5, "bf16", "SCAN"), (120, 64, 5, "bf16", "GENERIC"), (128, 72, 6, "bf16", "GENERIC"),
+    (128, 64, 5, "bf16", "MFMA"), (120, 64, 5, "bf16", "GENERIC"), (128, 72, 6, "bf16", "GENERIC"),
     (256, 64, 1, "bf16", "MFMA"), (128, 64, 8, "bf16", "MFMA"), (256, 32, 6, "bf16", "SCAN"),
-    (256, 64, 8, "bf16", "SCAN"), (128, 32, 8, "bf16", "SCAN"), (128, 64, 7, "bf16", "SCAN"),
+    (256, 64, 8, "bf16", "SCAN"), (128, 32, 8, "bf16", "SCAN"), (128, 64, 7, "bf16", "MFMA"),
+    (64, 64, 6, "bf16", "SCAN"), (128, 64, 6, "bf16", "MFMA"),
     (256, 64, 3, "bf16", "MFMA"), (512, 64, 4, "bf16", "MFMA"), (520, 64, 1, "bf16", "GENERIC"),
     (128, 64, 9, "bf16", "GENERIC"), (272, 64, 1, "bf16", "MFMA"), (128, 72, 1, "bf16", "MFMA"),
     (120, 64, 1, "bf16", "MFMA"), (64, 64, 2, "bf16", "MFMA"), (8, 64, 4, "bf16", "MFMA"),
@@ -84,7 +85,7 @@ def test_plan_path_choice(lib, N, P, R, io, path):
     assert p.path == getattr(bd, "M3_PATH_" + path)
     if path == "SCAN":
         assert p.workspace_bytes == 0 and p.segments == 1
-    if path == "MFMA" and R == 8:  # chunks of at most 32 tokens, no sequence segments
+    if path == "MFMA" and R > 4:  # chunks of at most 32 tokens, no sequence segments
         assert p.segments == 1 and p.n_chunks == (100 + 31) // 32 and p.last_chunk_len == 100 - 3 * 32
 
 

@@ -38,7 +38,7 @@ def _expected_path(io, N, P, R):
     """bf16: the chunked MFMA kernels at R 1-4 and at R 8 with N 128, P 64; the token walk for the rest."""
     if io != "bf16":
         return binding.M3_PATH_GENERIC
-    return binding.M3_PATH_MFMA if R <= 4 or (R == 8 and N == 128 and P == 64) else binding.M3_PATH_SCAN
+    return binding.M3_PATH_MFMA if R <= 4 or (N == 128 and P == 64) else binding.M3_PATH_SCAN
 
 
 def _path(p, chunk):
@@ -62,25 +62,32 @@ def test_prefill_large_state_and_rank(case):
 
 
 R8CASES = [
-    # b, L, H, G, chunk, h0_std, carry
-    (1, 100, 2, 1, 32, 0.1, True),    # four chunks of 32 tokens, a ragged last one
-    (2, 77, 3, 3, 64, 0.0, False),    # chunk 64 asked: walked in chunks of 32; one B, C per head
-    (1, 45, 2, 2, 16, 0.1, True),     # chunk 16, two groups
-    (1, 33, 2, 1, 7, 0.1, False),     # chunk 7
-    (2, 5, 2, 1, 32, 0.1, True),      # fewer tokens than a chunk
+    # b, L, H, G, R, chunk, h0_std, carry
+    (1, 100, 2, 1, 8, 32, 0.1, True),   # four chunks of 32 tokens, a ragged last one
+    (2, 77, 3, 3, 8, 64, 0.0, False),   # chunk 64 asked: walked in chunks of 32; one B, C per head
+    (1, 45, 2, 2, 8, 16, 0.1, True),    # chunk 16, two groups
+    (1, 33, 2, 1, 8, 7, 0.1, False),    # chunk 7
+    (2, 5, 2, 1, 8, 32, 0.1, True),     # fewer tokens than a chunk
+    (1, 70, 2, 1, 5, 32, 0.1, True),    # R 5, 6, 7: the R 8 kernel with zero ranks
+    (2, 41, 2, 2, 6, 64, 0.0, True),
+    (1, 90, 3, 1, 7, 32, 0.1, False),
+    (1, 130, 2, 1, 3, 64, 0.1, True),   # R 3: the R 4 kernel with a zero fourth rank
+    (2, 50, 2, 2, 3, 16, 0.0, False),
 ]
 
 
 @pytest.mark.parametrize("case", R8CASES, ids=[str(c) for c in R8CASES])
 def test_prefill_r8_chunked(case):
-    """R 8 at N 128, P 64 on the wave-specialised chunked kernel (chunks of at most 32 tokens)."""
-    b, L, H, G, chunk, h0s, carry = case
-    print(f"R 8 chunked case {case}", flush=True)
-    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=128, rank=8, io_dtype="bf16",
+    """R 3 and R 5-8 at N 128, P 64 on the wave-specialised chunked kernels (at R > 4 chunks of at most
+    32 tokens), the ranks above R zero."""
+    b, L, H, G, R, chunk, h0s, carry = case
+    print(f"wave-specialised chunked case {case}", flush=True)
+    p = inputs.make_problem(batch=b, seqlen=L, heads=H, groups=G, headdim=64, dstate=128, rank=R, io_dtype="bf16",
                             dist="lm", wid=1100 + R8CASES.index(case), h0_std=h0s, with_carry=carry)
     assert _path(p, chunk) == binding.M3_PATH_MFMA
-    plan = binding.plan(binding.dims(b, L, H, G, 64, 128), 8, chunk, binding.M3_BF16)
-    assert plan.n_chunks == (L + min(chunk, 32) - 1) // min(chunk, 32)
+    plan = binding.plan(binding.dims(b, L, H, G, 64, 128), R, chunk, binding.M3_BF16)
+    q = min(chunk, 32) if R > 4 else chunk
+    assert plan.n_chunks == (L + q - 1) // q
     y_ref, h_ref = oracle.scan(p)
     y, h = gpu_prefill(p, chunk)
     assert_close(y, y_ref, TOL["bf16"], "y")
