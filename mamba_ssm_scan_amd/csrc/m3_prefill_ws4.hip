@@ -24,6 +24,20 @@
 // operands: the state waves may overwrite them with the next chunk) and Y (the
 // next chunk is staged). The state update of chunk c writes g^T of chunk c+1 to
 // the other of two buffers while the output waves read g^T of chunk c.
+//
+// Sequence segments (few (b, h) walks over long sequences): the workgroup of
+// segment s walks its chunks from a zero state (segment 0 from h0 and the
+// carry), then waits for segment s-1's inclusive end state g_in (the true state
+// entering segment s), publishes its own (the transfer of g_in over the
+// segment plus its local end state), and adds e^{S_t} C~_t^T g_c to the
+// outputs of its first chunks, g_c being g_in carried to chunk c, until that
+// carry's decay underflows. Segments are handed out by a ticket counter,
+// segment-major, so a workgroup only waits for lower tickets, which are
+// running; and it reads only its predecessor's inclusive state, so the result
+// does not depend on timing.
+#include <cstdlib>
+#include <type_traits>
+
 #include "m3_internal.h"
 #include "m3_mfma_common.h"
 
@@ -116,15 +130,15 @@ __device__ __forceinline__ unsigned rot_dot(unsigned w, unsigned cs) { return ro
 
 // RP: the caller's rank rin_ is below R (3 on the R 4 kernel, 5 to 7 on the R 8
 // one): ranks rin_ .. R-1 are zero rows of B, C and x and their y rows are not
-// stored; without RP, rin_ is R.
-template <int R, bool ROT, bool RP>
+// stored; without RP, rin_ is R. SEG: sequence segments (sa.nseg > 1).
+template <int R, bool ROT, bool RP, bool SEG>
 __global__ void __launch_bounds__(64 * (ws4::NOW + ws4::NSW))
 prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Av,
                    const float* __restrict__ omega, const float* __restrict__ lam, const uint16_t* __restrict__ Bm,
                    const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                    uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                    const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks, int64_t nbh,
-                   int rin_) {
+                   int rin_, SegArgs sa) {
     using namespace ws4;
     using CF = Cfg<R>;
     constexpr int LR = CF::LR, QRP = CF::QRP, XS = CF::XS, UPT = CF::UPT, SPW = CF::SPW, TPW = CF::TPW;
@@ -142,14 +156,27 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int RI = RP ? rin_ : R;  // the caller's rank: row strides of B, C, x, y, the carry
+    __shared__ unsigned sTicket, sFlag;
     int64_t bh;
-    {
+    int seg = 0;
+    if constexpr (SEG) {
+        // segments in ticket order, segment-major: a workgroup only ever waits
+        // for lower tickets, which are already running
+        if (tid == 0) sTicket = __hip_atomic_fetch_add(&sa.ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int64_t t = sTicket;
+        seg = int(t / nbh);
+        bh = t % nbh;
+    } else {
         // XCD-aware order: the 8 XCDs take blocks round-robin; each gets a
         // contiguous run of (b, h), so heads sharing B/C share an L2
         const int64_t bid = blockIdx.x, q8 = nbh / 8, r8 = nbh % 8;
         const int64_t xcd = bid % 8, slot = bid / 8;
         bh = xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
     }
+    const int64_t c_begin = int64_t(seg) * sa.cps;
+    const int64_t c_end = c_begin + sa.cps < n_chunks ? c_begin + sa.cps : n_chunks;
+    const int64_t bs = bh * sa.nseg + seg;  // this segment's slot in the look-back arrays
     const int64_t b = bh / H;
     const int h = int(bh % H);
     const int grp = h / (H / G);
@@ -267,11 +294,13 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             stage_x(px, sXT, stid);
         };
 
-        // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
+        // ---- initial state g = h0 + delta_0 carry_B^T carry_x (segment 0; later
+        //      segments start from zero), tiles (nt, pt) of this wave
         floatx4 gst[TPW];
         {
             const int64_t t0 = (b * L) * H + h;
             const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
+            const bool first = seg == 0;
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
                 const int nt = sw * MR + m / PT, pt = m % PT;
@@ -279,8 +308,8 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int n = 16 * nt + 4 * g4 + e;
-                    float v = h0 ? h0[(bh * N + n) * P + p] : 0.f;
-                    if (carry_B) {
+                    float v = (first && h0) ? h0[(bh * N + n) * P + p] : 0.f;
+                    if (first && carry_B) {
                         float s = 0.f;
 #pragma unroll
                         for (int r = 0; r < RI; ++r)
@@ -298,14 +327,16 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         // operands are in LDS), load and turn chunk c + 1, wait for the output
         // waves to finish chunk c (X), write chunk c + 1 into LDS (Y).
         float Te = 0.f;
+        double segT = 0.0;  // total step of this segment's chunks
 #pragma unroll 1
-        for (int64_t c = -1; c < n_chunks; ++c) {
-            const bool more = c + 1 < n_chunks;
+        for (int64_t c = c_begin - 1; c < c_end; ++c) {
+            const bool more = c + 1 < c_end;
             // the X rows come from HBM: issued first, so the state update covers their latency
             if (more) load_prex(px, chunk_base(c + 1), H, stid);
-            if (c >= 0) {
+            if (c >= c_begin) {
                 const int nq = chunk_base(c).nq;
-                uint16_t* gTn = sGT[(c + 1) & 1];
+                segT += double(Te);
+                uint16_t* gTn = sGT[(c - c_begin + 1) & 1];
                 // ---- state passed to the next chunk: g' = Rot(Phi_e) [e^{S_e} g + sum w_j B~_j x_j^T]
                 const float decE = sSc[192 + nq - 1];
 #pragma unroll
@@ -370,11 +401,109 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                 load(c + 1);
                 Te = rope(chunk_base(c + 1).nq);
             }
-            if (c >= 0) lds_barrier();  // X(c): the output waves are done with chunk c's operands
+            if (c >= c_begin) lds_barrier();  // X(c): the output waves are done with chunk c's operands
             if (more) write_lds();
             lds_barrier();  // Y(c + 1)
         }
-        if (h_out) {
+        if constexpr (SEG) {
+            // ---- look-back: the predecessor's inclusive end state, then this
+            //      segment's; barriers A1 .. A3 match the output waves'
+            auto tile_ptr = [&](float* base, int m) {
+                const int nt = sw * MR + m / PT, pt = m % PT;
+                return base + bs * (N * P) + (16 * nt + 4 * g4) * P + 16 * pt + l16;
+            };
+            if (seg == 0) {
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    float* q = tile_ptr(sa.incl, m);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) q[e * P] = gst[m][e];
+                }
+            }
+            __syncthreads();  // A1
+            if (stid == 0) {
+                if (seg == 0) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    __hip_atomic_store(&sa.ctrl[2 + bs], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    // The predecessor holds a lower ticket, so it is running or done
+                    // and this wait ends; the bound guards against a hang all the
+                    // same. Giving up sets the workspace's error flag
+                    // (m3_prefill_check reports it); the outputs are then not valid.
+                    unsigned f = 0u;
+                    long spins = 0;
+                    while (sa.spin_limit > 0 && (f = __hip_atomic_load(&sa.ctrl[2 + bs - 1], __ATOMIC_RELAXED,
+                                                                        __HIP_MEMORY_SCOPE_AGENT)) != 2u) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins > sa.spin_limit) break;
+                    }
+                    if (f != 2u) __hip_atomic_store(&sa.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                }
+            }
+            __syncthreads();  // A2
+            floatx4 gcur[TPW];  // g_in carried to the chunk being corrected
+            if (seg > 0) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    const float* q = tile_ptr(sa.incl, m) - N * P;  // slot bs - 1
+                    gcur[m] = floatx4{q[0], q[P], q[2 * P], q[3 * P]};
+                    gst[m] += transfer(gcur[m], A2, omS[m / PT], segT);
+                    float* o = tile_ptr(sa.incl, m);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e * P] = gst[m][e];
+                }
+                if (h_out && seg == sa.nseg - 1) {  // the final state: the last segment's inclusive one
+#pragma unroll
+                    for (int m = 0; m < TPW; ++m) {
+                        const int nt = sw * MR + m / PT, pt = m % PT;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            h_out[(bh * N + 16 * nt + 4 * g4 + e) * P + 16 * pt + l16] = gst[m][e];
+                    }
+                }
+            }
+            __syncthreads();  // A3
+            if (seg > 0 && stid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(&sa.ctrl[2 + bs], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // ---- correction of the first chunks (barriers B1, B2 per chunk, matching
+            //      the output waves'): stage chunk c's token scalars, (cos, sin)
+            //      table and g_c, then carry g to the next chunk
+            double Tcum = 0.0;
+#pragma unroll 1
+            for (int64_t c = c_begin; seg > 0 && c < c_end; ++c) {
+                const bool stop = __builtin_amdgcn_exp2f(float(double(A2) * Tcum)) == 0.f;
+                if (stid == 0) sFlag = stop ? 1u : 0u;
+                float Tc = 0.f;
+                if (!stop) {
+                    load(c);
+                    Tc = rope(chunk_base(c).nq);
+                    if (sw == 0) {
+#pragma unroll
+                        for (int k = 0; k < 7; ++k) sSc[64 * k + lane] = sc[k];
+                    }
+#pragma unroll
+                    for (int m = 0; m < UPT; ++m)
+                        *reinterpret_cast<u32x4*>(sCS + ((stid >> 4) + 16 * m) * K + 4 * (stid & 15)) = cs4[m];
+#pragma unroll
+                    for (int m = 0; m < TPW; ++m) {
+                        const int nt = sw * MR + m / PT, pt = m % PT;
+                        *reinterpret_cast<u32x2*>(&sGT[0][(16 * pt + l16) * NS + 16 * nt + 4 * g4]) =
+                            u32x2{pack2(gcur[m][0], gcur[m][1]), pack2(gcur[m][2], gcur[m][3])};
+                    }
+                }
+                __syncthreads();  // B1
+                if (sFlag) break;
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) gcur[m] = transfer(gcur[m], A2, omS[m / PT], double(Tc));
+                Tcum += double(Tc);
+                __syncthreads();  // B2
+            }
+        }
+        if (h_out && !SEG) {
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
                 const int nt = sw * MR + m / PT, pt = m % PT;
@@ -408,9 +537,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
     lds_barrier();  // Y(0)
 
 #pragma unroll 1
-    for (int64_t c = 0; c < n_chunks; ++c) {
+    for (int64_t c = c_begin; c < c_end; ++c) {
         const int nq = chunk_base(c).nq;
-        const uint16_t* gT = sGT[c & 1];
+        const uint16_t* gT = sGT[(c - c_begin) & 1];
         load_c(c);
 
         // ---- C~ rows of the strips, turned with the staged (cos, sin) table
@@ -591,6 +720,69 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         }
         lds_barrier();  // Y(c + 1)
     }
+    if constexpr (SEG) {
+        // ---- look-back (done by the state waves): barriers A1 .. A3
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        // ---- correction of the first chunks: y_t += e^{S_t} C~_t^T g_c, with the
+        //      chunk's (cos, sin) table, token scalars and g_c staged by the state
+        //      waves (B1), until they report that g_c's decay has underflowed
+#pragma unroll 1
+        for (int64_t c = c_begin; seg > 0 && c < c_end; ++c) {
+            __syncthreads();  // B1
+            if (sFlag) break;
+            const int nq = chunk_base(c).nq;
+            load_c(c);
+            u32x4 cr[SPW][4];
+            float eSi[SPW];
+#pragma unroll
+            for (int k = 0; k < SPW; ++k) {
+                const int ti = (16 * strip[k] + l16) >> LR;
+                eSi[k] = sSc[192 + ti];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u32x4 cs = *reinterpret_cast<const u32x4*>(sCS + ti * K + 16 * ks + 4 * g4);
+                    const u32x4 v = craw[k][ks];
+                    cr[k][ks] = u32x4{rot_dot(v[0], cs[0]), rot_dot(v[1], cs[1]), rot_dot(v[2], cs[2]),
+                                      rot_dot(v[3], cs[3])};
+                }
+            }
+            floatx4 acc[SPW][PT];
+#pragma unroll
+            for (int k = 0; k < SPW; ++k)
+#pragma unroll
+                for (int q = 0; q < PT; ++q) acc[k][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x4 ga[PT];
+#pragma unroll
+                for (int q = 0; q < PT; ++q)
+                    ga[q] = *reinterpret_cast<const u32x4*>(sGT[0] + (16 * q + l16) * NS + 32 * ks + 8 * g4);
+#pragma unroll
+                for (int q = 0; q < PT; ++q)
+#pragma unroll
+                    for (int k = 0; k < SPW; ++k) acc[k][q] = mfma32(ga[q], cr[k][ks], acc[k][q]);
+            }
+#pragma unroll
+            for (int k = 0; k < SPW; ++k) {
+                const int rho_i = 16 * strip[k] + l16;
+                if ((rho_i >> LR) < nq && (rho_i & (R - 1)) < RI) {
+                    const int i = rho_i >> LR, r = rho_i & (R - 1);
+                    uint16_t* yr = y + ((b * L + c * Q + i) * H + h) * int64_t(RI * P) + r * P;
+#pragma unroll
+                    for (int q = 0; q < PT; ++q) {
+                        const int p = 16 * q + 4 * g4;
+                        const floatx4 v = acc[k][q] * eSi[k];
+                        const u32x2 old = *reinterpret_cast<const u32x2*>(yr + p);
+                        *reinterpret_cast<u32x2*>(yr + p) = u32x2{pack2(lo16(old[0]) + v[0], hi16(old[0]) + v[1]),
+                                                                  pack2(lo16(old[1]) + v[2], hi16(old[1]) + v[3])};
+                    }
+                }
+            }
+            __syncthreads();  // B2
+        }
+    }
 }
 
 }  // namespace
@@ -601,30 +793,63 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
 bool ws4_supported(const PrefillArgs& a) {
     const int most = a.R > 4 ? 32 : 64;  // R 3 on the R 4 kernel, R 5 to 7 on the R 8 one (zero ranks)
     return a.io == M3_BF16 && a.R >= 2 && a.R <= 8 && a.N == N && a.P == P && a.chunk >= 1 && a.chunk <= most &&
-           a.plan.segments == 1;
+           (a.plan.segments == 1 || a.R <= 4);
 }
 
 hipError_t launch_prefill_ws4(const PrefillArgs& a) {
     const int64_t nbh = a.b * a.H;
-    if (!ws4_supported(a) || nbh > 0x7fffffff) return hipErrorInvalidValue;
+    if (!ws4_supported(a) || nbh * a.plan.segments > 0x7fffffff) return hipErrorInvalidValue;
+    SegArgs sa{a.plan.segments, a.plan.chunks_per_segment, nullptr, nullptr, nullptr, nullptr, kLookbackSpinLimit};
+    // M3_LOOKBACK_SPIN_LIMIT (polls, >= 0) overrides the bound: 0 makes every wait
+    // give up at once, which exercises the error report
+    if (const char* env = getenv("M3_LOOKBACK_SPIN_LIMIT")) sa.spin_limit = atol(env) > 0 ? atol(env) : 0;
+    if (sa.nseg > 1) {
+        const PrefillWorkspace w =
+            prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
+        char* base = static_cast<char*>(a.workspace);
+        sa.ctrl = reinterpret_cast<unsigned*>(base + w.ctrl_off);
+        sa.agg = reinterpret_cast<float*>(base + w.agg_off);
+        sa.incl = reinterpret_cast<float*>(base + w.incl_off);
+        sa.tr = reinterpret_cast<double*>(base + w.tr_off);
+        // ticket, error flag and per-segment flags start at zero (a kernel, so
+        // the call stays capturable in a graph)
+        const hipError_t e = launch_copy_or_zero(sa.ctrl, nullptr, 2 + nbh * sa.nseg, a.stream);
+        if (e != hipSuccess) return e;
+    }
     auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(unsigned(nbh)), dim3(64 * (ws4::NOW + ws4::NSW)), 0, a.stream,
+        hipLaunchKernelGGL(kern, dim3(unsigned(nbh * sa.nseg)), dim3(64 * (ws4::NOW + ws4::NSW)), 0, a.stream,
                            static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
                            static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
-                           a.R);
+                           a.R, sa);
         return hipGetLastError();
     };
     const bool rot = a.omega != nullptr;
+    // the instance for (R, rank padding): with and without rotation, with and
+    // without sequence segments (R <= 4 only)
+    auto pick = [&](auto rc, auto rpc) -> hipError_t {
+        constexpr int KR = decltype(rc)::value;
+        constexpr bool RPAD = decltype(rpc)::value;
+        if constexpr (KR <= 4) {
+            if (sa.nseg > 1)
+                return rot ? launch(prefill_ws4_kernel<KR, true, RPAD, true>)
+                           : launch(prefill_ws4_kernel<KR, false, RPAD, true>);
+        }
+        return rot ? launch(prefill_ws4_kernel<KR, true, RPAD, false>)
+                   : launch(prefill_ws4_kernel<KR, false, RPAD, false>);
+    };
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
     switch (a.R) {
-        case 2: return rot ? launch(prefill_ws4_kernel<2, true, false>) : launch(prefill_ws4_kernel<2, false, false>);
-        case 3: return rot ? launch(prefill_ws4_kernel<4, true, true>) : launch(prefill_ws4_kernel<4, false, true>);
-        case 4: return rot ? launch(prefill_ws4_kernel<4, true, false>) : launch(prefill_ws4_kernel<4, false, false>);
+        case 2: return pick(I2{}, std::false_type{});
+        case 3: return pick(I4{}, std::true_type{});
+        case 4: return pick(I4{}, std::false_type{});
         case 5:
         case 6:
-        case 7: return rot ? launch(prefill_ws4_kernel<8, true, true>) : launch(prefill_ws4_kernel<8, false, true>);
-        case 8: return rot ? launch(prefill_ws4_kernel<8, true, false>) : launch(prefill_ws4_kernel<8, false, false>);
+        case 7: return pick(I8{}, std::true_type{});
+        case 8: return pick(I8{}, std::false_type{});
     }
     return hipErrorInvalidValue;
 }

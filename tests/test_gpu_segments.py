@@ -1,4 +1,5 @@
-"""Sequence-segment parallelism (look-back + correction) of the MFMA prefill.
+"""Sequence-segment parallelism (look-back + correction) of the MFMA prefill (at N 128,
+P 64 on the wave-specialised kernel, elsewhere on the single-role one).
 
 Segments are forced with M3_PREFILL_SEGMENTS on small problems; every case is
 compared with the oracle, and the workspace's look-back error flag must stay 0
@@ -23,6 +24,7 @@ CASES = [
     (2, 1000, 2, 2, 2, 64, 5, 0.1, False),
     (1, 333, 2, 1, 4, 16, 4, 0.1, True),
     (1, 257, 1, 1, 2, 32, 7, 0.0, False),
+    (1, 520, 2, 1, 3, 64, 3, 0.1, True),   # R 3: zero fourth rank, with segments
 ]
 
 
