@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libm3.so")
+# the in-tree build; M3_LIBRARY names another build of the same ABI (the
+# host-only sanitizer build of the tests)
+LIB_PATH = os.environ.get("M3_LIBRARY") or os.path.join(HERE, "libm3.so")
 
 M3_F32, M3_BF16 = 0, 1
 M3_PATH_GENERIC, M3_PATH_MFMA, M3_PATH_SCAN = 0, 1, 2

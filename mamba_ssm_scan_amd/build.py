@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 
 SOURCES = ["m3_host.cpp", "m3_prefill_generic.hip", "m3_prefill_mfma.hip", "m3_decode.hip", "m3_prologue.hip",
            "m3_backward.hip", "m3_prefill_scan.hip", "m3_gate.hip", "m3_mixer.cpp", "m3_noalloc.hip",
-           "m3_prefill_ws4.hip"]
+           "m3_prefill_ws4.hip", "m3_paths.cpp"]
 # per-source flags: the token-walk kernel reads every MFMA result with VALU
 # ops, so its MFMAs write arch VGPRs (no accumulator-register copies)
 EXTRA = {"m3_prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -48,6 +48,7 @@ constexpr int PMAX = 64;          // columns (P <= 64)
 constexpr int SV = 8;             // state entries per thread
 constexpr int BT = kBackwardCheckpoint;  // tokens per block: staged in LDS at once, one checkpoint each
 constexpr int STATE = NT * SV;    // floats per stored state (covers 128 x 64)
+static_assert(STATE == kBackwardStateFloats && 2 * KMAX == 128 && PMAX == 64, "sizes the planner assumes");
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -603,13 +604,6 @@ struct Z0 {
     int64_t n;
     const float* src;
 };
-
-size_t backward_workspace_bytes(int64_t b, int32_t H, int64_t L) {
-    const int64_t nblk = (L + BT - 1) / BT;
-    return size_t(b) * size_t(H) * size_t(nblk + BT) * STATE * sizeof(float);
-}
-
-bool backward_supported(int32_t P, int32_t N, int32_t R) { return N <= 2 * KMAX && P <= PMAX && R <= 4; }
 
 hipError_t launch_backward(const BackwardArgs& a) {
     if (a.b * a.H == 0) return hipSuccess;

@@ -290,6 +290,28 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
     return M3_OK;
 }
 
+// m3_prefill_noalloc: m3_prefill on the fixed device array of m3_noalloc.hip
+size_t m3_noalloc_scratch_bytes(void) { return size_t(M3_NOALLOC_SCRATCH_BYTES); }
+
+m3_status m3_prefill_noalloc(const void* x, const float* dt, const float* A, const float* omega, const float* lambda,
+                             const void* B, const void* C, const float* D, int32_t R, int32_t chunk, const float* h0,
+                             void* y, float* h_out, const m3_dims* dims, m3_dtype io_dtype, const void* carry_B,
+                             const void* carry_x, void* stream) {
+    const size_t cap = size_t(M3_NOALLOC_SCRATCH_BYTES);
+    m3_plan plan;
+    m3_status s = m3_prefill_plan(dims, R, chunk, io_dtype, &plan);
+    if (s != M3_OK) return s;
+    if (plan.workspace_bytes > cap)
+        return fail(M3_EWORKSPACE, "these sizes need %zu bytes of scratch, above the fixed %zu bytes of m3_prefill_noalloc",
+                    plan.workspace_bytes, cap);
+    void* ws = nullptr;
+    if (plan.workspace_bytes > 0 && dims->batch > 0 && dims->seqlen > 0) {
+        if ((s = m3::noalloc_scratch(&ws)) != M3_OK) return s;
+    }
+    return m3_prefill(x, dt, A, omega, lambda, B, C, D, R, chunk, h0, y, h_out, dims, io_dtype, carry_B, carry_x,
+                      ws, ws ? cap : 0, stream);
+}
+
 size_t m3_decode_carry_bytes(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int32_t which) {
     if (check_dims(dims, R) != M3_OK || check_dtype(io_dtype) != M3_OK) return 0;
     const size_t es = io_size(io_dtype);
@@ -563,7 +585,7 @@ m3_status m3_prologue(const m3_dims* dims, int32_t R, m3_dtype io_dtype, int64_t
         for (int q = o + 1; q < 4; ++q)
             if (overlaps(out[o], out[q])) return fail(M3_EINVAL, "%s overlaps %s", out[o].name, out[q].name);
     }
-    if (ntok == 0) return M3_OK;
+    if (ntok == 0 || !(B || C || dt || lambda)) return M3_OK;  // nothing to do: no launch
     const int64_t rows = ntok * G * R;
     if ((B || C) && (rows + 15) / 16 > 0x3fffffff) return fail(M3_EUNSUPPORTED, "too many rows");
     if ((dt || lambda) && (ntok * H + 255) / 256 > 0x3fffffff) return fail(M3_EUNSUPPORTED, "too many tokens");

@@ -130,6 +130,7 @@ struct BackwardArgs {
 
 // Tokens between the backward's state checkpoints, and its workspace size.
 constexpr int kBackwardCheckpoint = 16;
+constexpr int kBackwardStateFloats = 128 * 64;  // floats of one stored backward state (N <= 128, P <= 64)
 size_t backward_workspace_bytes(int64_t b, int32_t H, int64_t L);
 bool backward_supported(int32_t P, int32_t N, int32_t R);
 
@@ -157,6 +158,8 @@ int32_t mfma_kernel_chunk(int32_t R, int32_t chunk);
 bool mfma_segments_supported(int32_t R, int32_t N, int32_t P);
 constexpr int32_t kMfmaMaxN = 512;   // largest N of the chunked path (passes of 128 rows)
 constexpr int32_t kMfmaMaxP = 1024;  // largest P of the chunked path (passes of 64 columns)
+constexpr int32_t kMfmaN = 128;      // state rows of one pass of the chunked kernels
+constexpr int32_t kMfmaP = 64;       // state columns of one pass
 
 // the token-walk path (bf16, N, P multiples of 16, N <= 256, P <= 64, R <= 8)
 bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io);

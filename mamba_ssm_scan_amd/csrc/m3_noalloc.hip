@@ -1,6 +1,7 @@
-// m3_noalloc.hip -- m3_prefill_noalloc: m3_prefill with the workspace taken from
-// a fixed device array instead of a caller buffer, for callers that cannot
-// allocate device memory (code under stream capture, tight serving loops).
+// m3_noalloc.hip -- the fixed device array behind m3_prefill_noalloc (the entry
+// point is in m3_host.cpp): m3_prefill with the workspace taken from it instead
+// of a caller buffer, for callers that cannot allocate device memory (code
+// under stream capture, tight serving loops).
 //
 // The array is a file-scope __device__ variable: every GPU the library runs on
 // holds its own copy (at its own address) until the process ends. In host code
@@ -41,26 +42,4 @@ m3_status m3::noalloc_scratch(void** out) {
     }
     *out = g_ptr[dev];
     return M3_OK;
-}
-
-extern "C" size_t m3_noalloc_scratch_bytes(void) { return kScratchBytes; }
-
-extern "C" m3_status m3_prefill_noalloc(const void* x, const float* dt, const float* A, const float* omega,
-                                        const float* lambda, const void* B, const void* C, const float* D,
-                                        int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
-                                        const m3_dims* dims, m3_dtype io_dtype, const void* carry_B,
-                                        const void* carry_x, void* stream) {
-    m3_plan plan;
-    m3_status s = m3_prefill_plan(dims, R, chunk, io_dtype, &plan);
-    if (s != M3_OK) return s;
-    if (plan.workspace_bytes > kScratchBytes)
-        return m3::set_error(M3_EWORKSPACE,
-                             "these sizes need %zu bytes of scratch, above the fixed %zu bytes of m3_prefill_noalloc",
-                             plan.workspace_bytes, kScratchBytes);
-    void* ws = nullptr;
-    if (plan.workspace_bytes > 0 && dims->batch > 0 && dims->seqlen > 0) {
-        if ((s = m3::noalloc_scratch(&ws)) != M3_OK) return s;
-    }
-    return m3_prefill(x, dt, A, omega, lambda, B, C, D, R, chunk, h0, y, h_out, dims, io_dtype, carry_B, carry_x,
-                      ws, ws ? kScratchBytes : 0, stream);
 }

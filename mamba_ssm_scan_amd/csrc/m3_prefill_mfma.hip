@@ -1316,19 +1316,7 @@ hipError_t launch_r(const PrefillArgs& a, const PassArgs& pa, bool gen) {
 // N and P multiples of 8: up to 128 rows and 64 columns in one pass (zero-padded
 // below: the loads of B, C and x rows stop at the caller's sizes); beyond, in
 // passes of 128 rows (outputs summed in fp32 in the workspace) and 64 columns
-bool mfma_path_supported(int32_t P_, int32_t N_, int32_t R, int32_t chunk, m3_dtype io) {
-    // R 5 to 8 at the workloads' state (N 128, P 64): the R 8 wave-specialised kernel (zero ranks below 8)
-    if (io == M3_BF16 && R >= 5 && R <= 8 && N_ == N && P_ == P && chunk >= 1) return true;
-    return io == M3_BF16 && N_ >= 8 && N_ <= kMfmaMaxN && N_ % 8 == 0 && P_ >= 8 && P_ <= kMfmaMaxP &&
-           P_ % 8 == 0 && R >= 1 && R <= 4 && chunk >= 1 && chunk <= 64;
-}
-
-// The chunk the MFMA kernels walk: the one asked for, except at R 5 to 8 (the
-// R 8 kernel), whose chunks hold at most 32 tokens (256 (token, rank) rows). The
-// chunk size only tiles the work: the recurrence's result does not depend on it.
-int32_t mfma_kernel_chunk(int32_t R, int32_t chunk) { return R > 4 && chunk > 32 ? 32 : chunk; }
-
-bool mfma_segments_supported(int32_t R, int32_t N_, int32_t P_) { return R != 1 && R <= 4 && N_ <= N && P_ <= P; }
+static_assert(N == kMfmaN && P == kMfmaP, "one pass of the chunked kernels");
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a) {
     if (ws4_supported(a)) return launch_prefill_ws4(a);

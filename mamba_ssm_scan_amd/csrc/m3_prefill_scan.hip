@@ -310,11 +310,6 @@ hipError_t launch_ntl_rg(const PrefillArgs& a) {
 
 }  // namespace
 
-// ranks 1 to 4 run on the chunked kernels
-bool scan_path_supported(int32_t P, int32_t N, int32_t R, m3_dtype io) {
-    return io == M3_BF16 && N % 16 == 0 && N <= 256 && P % 16 == 0 && P <= 64 && R >= 5 && R <= 8;
-}
-
 hipError_t launch_prefill_scan(const PrefillArgs& a) {
     if (a.b * a.H > 0x7fffffff) return hipErrorInvalidValue;
     if (!scan_path_supported(a.P, a.N, a.R, a.io)) return hipErrorInvalidValue;

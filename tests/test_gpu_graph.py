@@ -71,10 +71,12 @@ def test_prologue_and_segmented_prefill_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(Bn, B_ref) and torch.equal(dt, dt_ref), f"replay {rep}: prologue differs"
+        # segments wait for their predecessor's inclusive state only: every replay
+        # combines the same values in the same order, so the outputs are bit-identical
         ey = ((y.float() - y_ref.float()).abs().max() / y_ref.float().abs().max()).item()
         eh = ((h - h_ref).abs().max() / h_ref.abs().max()).item()
         print(f"  replay {rep}: y {ey:.2e}, h_out {eh:.2e}", flush=True)
-        assert ey <= 2 ** -7 and eh <= 1e-5, f"replay {rep}: y {ey:.2e}, h_out {eh:.2e}"
+        assert torch.equal(y, y_ref) and torch.equal(h, h_ref), f"replay {rep}: y {ey:.2e}, h_out {eh:.2e}"
 
 
 def test_decode_steps_replay():
