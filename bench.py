@@ -36,11 +36,11 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # sources it was taken on (sha256 prefix over the listed files, in order); the
 # summaries with the commands are in profiles/. None until a kernel is profiled.
 MEASURED_TRAFFIC = {
-    "prefill1": ("5ed749538c20f1ec", (2.0 * 39159.5 + 73728.0) * 1024),
-    "prefill2": ("9c5d768e2232a5df", (2.0 * 149809.3 + 270336.0) * 1024),
-    "long": ("5ed749538c20f1ec", (2.0 * 727753.8 + 1083772.1) * 1024),
-    "decode1": ("d300d65e7a08e628", (2.0 * 134152.2 + 266240.0) * 1024),
-    "decode4": ("d300d65e7a08e628", (2.0 * 142681.3 + 278683.1) * 1024),
+    "prefill1": ("7f51053fff5ed60f", (2.0 * 39158.9 + 73728.0) * 1024),
+    "prefill2": ("f39f6d3b0ef598cc", (2.0 * 149809.1 + 270336.0) * 1024),
+    "long": ("f39f6d3b0ef598cc", (2.0 * 741749.8 + 1079920.1) * 1024),
+    "decode1": ("eb03525986fbf79a", (2.0 * 133579.7 + 264517.3) * 1024),
+    "decode4": ("eb03525986fbf79a", (2.0 * 139358.8 + 271082.0) * 1024),
 }
 
 
@@ -58,7 +58,7 @@ def source_sha(files):
 SOURCES = {
     "prefill1": ("m3_prefill_mfma.hip", "m3_mfma_common.h"),
     "prefill2": ("m3_prefill_ws4.hip", "m3_mfma_common.h"),
-    "long": ("m3_prefill_mfma.hip", "m3_mfma_common.h"),
+    "long": ("m3_prefill_ws4.hip", "m3_mfma_common.h"),
     "decode1": ("m3_decode.hip",),
     "decode4": ("m3_decode.hip",),
 }
@@ -704,14 +704,14 @@ def main():
         # the MIMO R 4 prefill: at the ridge of the bf16 MFMA / HBM roofline
         p2 = bench_prefill(2, args.steps, args.warmup, log)
         p2["roofline"] = roofline("mfma", p2["mfma_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s",
-                                  measured_traffic("prefill2"), "prefill_ws4_kernel<4>",
+                                  measured_traffic("prefill2"), "prefill_ws4_kernel<4> (1 segment)",
                                   {"flops_per_launch": p2["flops"]},
                                   hbm={"achieved": p2["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": p2["hbm_frac"], "bytes_per_launch": p2["bytes"]})
         out["prefill_mimo_r4"] = p2
         lg = bench_long(log)
         lg["roofline"] = roofline("mfma", lg["prefill_mfma_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s",
-                                  measured_traffic("long"), "prefill_mfma_kernel<4>",
+                                  measured_traffic("long"), "prefill_ws4_kernel<4> (4 segments)",
                                   {"flops_per_launch": lg["prefill_flops"]},
                                   hbm={"achieved": lg["prefill_hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": lg["prefill_hbm_frac"], "bytes_per_launch": lg["prefill_bytes"]})
