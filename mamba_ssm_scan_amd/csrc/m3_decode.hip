@@ -321,6 +321,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx4 mfma_k32(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
 __device__ __forceinline__ floatx4 mfma_k16(u32x2 a, u32x2 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c,
                                                      0, 0, 0);
@@ -335,7 +341,7 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4, 8}: the rank-R contractions on MFMA
+// bf16 I/O, N in {64, 128}, P = 64, R = 8: the rank-R contractions on MFMA
 // (v_mfma_f32_16x16x16_bf16). One 256-thread workgroup per (b, h); wave w owns
 // state columns 16 w .. 16 w + 15 and all 128 rows. In row tile nt, lane
 // (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column 16 w + l16: two whole
@@ -552,6 +558,211 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     if (tid == 0) par[bh] = pr ^ 1u;
 }
 
+// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4}: the step in two MFMAs per row
+// tile. One 256-thread workgroup per (b, h); wave w owns state columns
+// 16 w .. 16 w + 15 and all rows; in row tile nt, lane (l16, g4) holds rows
+// 16 nt + 4 g4 .. + 3 of column 16 w + l16 (two whole rotation pairs: the
+// accumulator layout of the MFMA). With the exponential-trapezoidal step
+//   h' = alpha Rot(h) + M,   M = gamma B^T x + alpha delta Rot(B_prev)^T x_prev,
+// both input terms are one K = 16 contraction over k = (term, rank): the A
+// operand holds gamma B and alpha delta Rot(B_prev) per row n, each as a bf16
+// pair (hi, lo) whose sum is the fp32 value to 2^-16, and the B operand holds
+// x (against the gamma B terms) and x_prev (against the B_prev terms), exact
+// in bf16. The rotation of B_prev's rows is the rotation the previous term
+// takes in the state (it acts on the rows n only). Then
+//   y[r][p] = sum_n C[r][n] h'[n][p]
+// is one K = 32 contraction per tile: k = 8 g4 + j takes the hi (j < 4) and lo
+// (j >= 4) bf16 terms of the lane's own 4 rows, against C of those rows twice,
+// which keeps y at fp32 accuracy with no cross-lane movement. The step's small
+// rows (B_t, C_t, B_prev, x_t, x_prev) and the rotation frequencies are loaded
+// before the state, so their staging runs while the state streams in.
+template <int R, int N, bool PRO>
+__global__ void __launch_bounds__(256)
+decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
+                    unsigned* __restrict__ par, int rev, DecodePrologue pro,
+                    const bf16_t* __restrict__ x, const float* __restrict__ dt,
+                    const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
+                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
+                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
+    static_assert(R >= 2 && R <= 4, "ranks 2-4 (R 3 with a zero rank slot)");
+    constexpr int P = 64, K = N / 2, CS_ = N + 4, NT = N / 16;
+    constexpr int NBI = (4 * K + 255) / 256;  // (rank slot, pair) items of B per thread
+    constexpr int NCI = (R * K + 255) / 256;  // (rank, pair) items of C per thread
+    constexpr int AS = 20;                    // sA row stride (bf16): 16 used, padded against bank conflicts
+    // per row n, k = 0..15: (gamma B)_hi, (gamma B)_lo, (alpha delta Rot B_prev)_hi, _lo; four rank slots each
+    __shared__ __attribute__((aligned(16))) uint16_t sA[N][AS];
+    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][4];   // x^T, zero past R
+    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][4];  // x_prev^T
+    __shared__ __attribute__((aligned(16))) uint16_t sC[R][CS_];  // C rows (padded)
+    __shared__ __attribute__((aligned(16))) float sCS[K][2];      // alpha * (cos, sin) of pair k
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t bh = rev ? int64_t(gridDim.x) - 1 - blockIdx.x : int64_t(blockIdx.x);
+    const int64_t b = bh / H;
+    const int h = int(bh % H);
+    const int gi = h / (H / G);
+    const int64_t bg = b * G + gi;
+    const unsigned pr = par[bh] & 1u;  // slot of B_prev
+    float* hs = hstate + bh * (N * P);
+    const int p = 16 * w + l16;
+
+    // The small rows first (raw with the prologue, with the norm weights).
+    // Thread item e of B: rank slot r = e / K, pair j = e % K (rows 2 j, 2 j + 1).
+    const unsigned* Bt32 = reinterpret_cast<const unsigned*>(B + bg * (R * N));
+    const unsigned* Ct32 = reinterpret_cast<const unsigned*>(C + bg * (R * N));
+    const unsigned* Bp32 = reinterpret_cast<const unsigned*>(carry_B + (int64_t(pr) * nb * G + bg) * (R * N));
+    const unsigned* xt32 = reinterpret_cast<const unsigned*>(x + bh * (R * P));
+    const unsigned* xp32 = reinterpret_cast<const unsigned*>(carry_x + bh * (R * P));
+    auto wpair = [&](const float* v, int r, int j, float dflt) {
+        if (!v) return float2{dflt, dflt};
+        const int64_t o = (int64_t(gi) * R + r) * N + 2 * j;
+        return float2{v[o], v[o + 1]};
+    };
+    unsigned rb[NBI], rbp[NBI], rc[NCI];
+    float rom[NBI];
+    float2 bw[PRO ? NBI : 1], bb2[PRO ? NBI : 1], cw[PRO ? NCI : 1], cb2[PRO ? NCI : 1];
+#pragma unroll
+    for (int it = 0; it < NBI; ++it) {
+        const int e = tid + 256 * it, r = e / K, j = e % K;
+        const bool in = e < 4 * K && r < R;
+        rb[it] = in ? Bt32[r * K + j] : 0u;
+        rbp[it] = in ? Bp32[r * K + j] : 0u;
+        rom[it] = e < 4 * K ? om_at(omega, int64_t(h) * K + j) : 0.f;
+        if constexpr (PRO) {
+            bw[it] = in ? wpair(pro.B_weight, r, j, 1.f) : float2{1.f, 1.f};
+            bb2[it] = in ? wpair(pro.B_bias, r, j, 0.f) : float2{0.f, 0.f};
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < NCI; ++it) {
+        const int e = tid + 256 * it;
+        const bool in = e < R * K;
+        rc[it] = in ? Ct32[e] : 0u;
+        if constexpr (PRO) {
+            cw[it] = in ? wpair(pro.C_weight, e / K, e % K, 1.f) : float2{1.f, 1.f};
+            cb2[it] = in ? wpair(pro.C_bias, e / K, e % K, 0.f) : float2{0.f, 0.f};
+        }
+    }
+    // x_t, x_prev: thread tid < 4 P / 2 takes rank slot tid / (P / 2), column pair tid % (P / 2)
+    const bool xin = tid < 4 * (P / 2) && tid / (P / 2) < R;
+    const unsigned rx = xin ? xt32[tid] : 0u, rxp = xin ? xp32[tid] : 0u;
+
+    float st[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[nt][e] = hs[(16 * nt + 4 * g4 + e) * P + p];
+
+    float d, lm;
+    step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
+    const float alpha = expf(d * A[h]);
+    const float gamma = lm * d, ad = alpha * (1.f - lm) * d;
+
+    // the normalised pair from a raw pair, its weights and biases; the K lanes
+    // holding one rank row (a whole wave at N 128) reduce its sum of squares
+    auto norm_pair = [&](unsigned raw, int r, float2 wv, float2 bv) -> unsigned {
+        const float v0 = bf_lo(raw), v1 = bf_hi(raw);
+        const float ss = group_sum<K>(v0 * v0 + v1 * v1);
+        if (r >= R) return 0u;
+        const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
+        return pk_bf16(v0 * k * wv.x + bv.x, v1 * k * wv.y + bv.y);
+    };
+#pragma unroll
+    for (int it = 0; it < NBI; ++it) {
+        const int e = tid + 256 * it;
+        if (e >= 4 * K) break;  // whole waves
+        const int r = e / K, j = e % K;
+        if constexpr (PRO) rb[it] = norm_pair(rb[it], r, bw[it], bb2[it]);  // kept for the carry
+        float sn, cs;
+        sincos_step(d * rom[it], &sn, &cs);
+        if (r == 0) {
+            sCS[j][0] = alpha * cs;
+            sCS[j][1] = alpha * sn;
+        }
+        const float g0 = gamma * bf_lo(rb[it]), g1 = gamma * bf_hi(rb[it]);
+        const float p0 = bf_lo(rbp[it]), p1 = bf_hi(rbp[it]);
+        const float q0 = ad * (cs * p0 - sn * p1), q1 = ad * (sn * p0 + cs * p1);
+        const unsigned gh = pk_bf16(g0, g1), qh = pk_bf16(q0, q1);
+        const unsigned gl = pk_bf16(g0 - bf_lo(gh), g1 - bf_hi(gh)), ql = pk_bf16(q0 - bf_lo(qh), q1 - bf_hi(qh));
+        sA[2 * j][r] = uint16_t(gh);
+        sA[2 * j + 1][r] = uint16_t(gh >> 16);
+        sA[2 * j][4 + r] = uint16_t(gl);
+        sA[2 * j + 1][4 + r] = uint16_t(gl >> 16);
+        sA[2 * j][8 + r] = uint16_t(qh);
+        sA[2 * j + 1][8 + r] = uint16_t(qh >> 16);
+        sA[2 * j][12 + r] = uint16_t(ql);
+        sA[2 * j + 1][12 + r] = uint16_t(ql >> 16);
+    }
+    if (tid < 4 * (P / 2)) {
+        const int r = tid / (P / 2), j = tid % (P / 2);
+        sXt[2 * j][r] = uint16_t(rx);
+        sXt[2 * j + 1][r] = uint16_t(rx >> 16);
+        sXpt[2 * j][r] = uint16_t(rxp);
+        sXpt[2 * j + 1][r] = uint16_t(rxp >> 16);
+    }
+#pragma unroll
+    for (int it = 0; it < NCI; ++it) {
+        const int e = tid + 256 * it;
+        if (e >= R * K) break;  // whole waves
+        unsigned cv = rc[it];
+        if constexpr (PRO) cv = norm_pair(cv, e / K, cw[it], cb2[it]);
+        reinterpret_cast<unsigned*>(&sC[e / K][0])[e % K] = cv;
+    }
+    __syncthreads();
+
+    // B operand of the input MFMA: k = 4 g4 .. 4 g4 + 3 -> ranks 0..3 of x (g4 0, 1) or x_prev (g4 2, 3)
+    const u32x2 bx = *reinterpret_cast<const u32x2*>(g4 < 2 ? &sXt[p][0] : &sXpt[p][0]);
+    const int rcl = l16 < R ? l16 : 0;
+    const u32x2 zero = {0u, 0u};
+    floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n0 = 16 * nt;
+        const u32x2 a = *reinterpret_cast<const u32x2*>(&sA[n0 + l16][4 * g4]);
+        const floatx4 M = mfma_k16(a, bx, floatx4{0.f, 0.f, 0.f, 0.f});
+        // alpha (cos, sin) of pairs 8 nt + 2 g4 (rows e = 0, 1) and 8 nt + 2 g4 + 1 (rows e = 2, 3)
+        const floatx4 cs = *reinterpret_cast<const floatx4*>(&sCS[8 * nt + 2 * g4][0]);
+        float nv[4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            const float c = cs[2 * hp], sn = cs[2 * hp + 1];
+            const float h0 = st[nt][2 * hp], h1 = st[nt][2 * hp + 1];
+            nv[2 * hp] = (c * h0 - sn * h1) + M[2 * hp];
+            nv[2 * hp + 1] = (sn * h0 + c * h1) + M[2 * hp + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hs[(n0 + 4 * g4 + e) * P + p] = nv[e];
+        const unsigned h01 = pk_bf16(nv[0], nv[1]), h23 = pk_bf16(nv[2], nv[3]);
+        const u32x4 hl = {h01, h23, pk_bf16(nv[0] - bf_lo(h01), nv[1] - bf_hi(h01)),
+                          pk_bf16(nv[2] - bf_lo(h23), nv[3] - bf_hi(h23))};
+        const u32x2 cv = l16 < R ? *reinterpret_cast<const u32x2*>(&sC[rcl][n0 + 4 * g4]) : zero;
+        yacc = mfma_k32(u32x4{cv[0], cv[1], cv[0], cv[1]}, hl, yacc);
+    }
+    if (g4 == 0) {  // lane (l16, 0) holds y[r = e][p]
+        const float Dh = D[h];
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const float xv = __uint_as_float(unsigned(sXt[p][e]) << 16);
+            Io<bf16_t>::store(y, bh * (R * P) + e * P + p, yacc[e] + Dh * xv);
+        }
+    }
+
+    // this token becomes the carry of the next step, from the registers it was
+    // staged from (the carry was read before the barrier above)
+    if (tid < R * (P / 2)) reinterpret_cast<unsigned*>(carry_x + bh * (R * P))[tid] = rx;
+    if (h % (H / G) == 0) {
+        unsigned* cb32 = reinterpret_cast<unsigned*>(carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N));
+#pragma unroll
+        for (int it = 0; it < NBI; ++it) {  // the normalised row with the prologue
+            const int e = tid + 256 * it;
+            if (e < R * K) cb32[e] = rb[it];
+        }
+    }
+    if (tid == 0) par[bh] = pr ^ 1u;
+}
+
 // Any sizes: thread loops over (pair k, column p); y is a second pass over the new state.
 template <typename T, bool PRO>
 __global__ void __launch_bounds__(kThreads)
@@ -692,9 +903,9 @@ using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodeProlog
 
 template <int N, bool PRO>
 MfmaKern<PRO> mfma_kernel_for(int R) {
-    return R == 2 ? decode_mfma_kernel<2, N, PRO>
-         : R == 3 ? decode_mfma_kernel<3, N, PRO>
-         : R == 4 ? decode_mfma_kernel<4, N, PRO>
+    return R == 2 ? decode_mfma4_kernel<2, N, PRO>
+         : R == 3 ? decode_mfma4_kernel<3, N, PRO>
+         : R == 4 ? decode_mfma4_kernel<4, N, PRO>
                   : decode_mfma_kernel<8, N, PRO>;
 }
 
