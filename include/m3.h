@@ -134,6 +134,35 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
                      const void* carry_B, const void* carry_x,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * m3_prefill_fused -- m3_prefill on the raw projections of the step and the
+ * trapezoid weight: the scalar part of the input prologue is applied where the
+ * kernels load them, with no pass of its own.
+ *
+ * Passage: the block computes the step as a softplus of its projection plus a
+ * learnt bias and the trapezoid weight as a sigmoid of its projection, next to
+ * the QK-norm of B and C ("复值SSM × 广义梯形离散 × MIMO，线性模型的全面重构",
+ * §2.4 and Fig. 4; m3_prologue's reading).
+ *
+ * dt_raw:     [b][L][H] fp32; the step is dt = softplus(dt_raw + dt_bias[h]).
+ * dt_bias:    [H] fp32, or NULL for 0.
+ * lambda_raw: [b][L][H] fp32, lambda = sigmoid(lambda_raw); or NULL for
+ *             lambda = 1 (no sigmoid).
+ * B, C:       the recurrence's B and C as m3_prefill takes them (the QK-norm
+ *             stays with m3_prologue: at G < H it is per group, and a fused
+ *             form would repeat it in every head of the group).
+ * Everything else, the plan, the workspace and the errors: as m3_prefill
+ * (dt_bias, when given, is checked like the other inputs: 16-byte aligned, not
+ * overlapping y). Equal to m3_prologue on dt and lambda followed by m3_prefill
+ * up to the rounding of softplus and sigmoid (hardware exp2 / log2 / rcp here,
+ * a few ulp).
+ */
+m3_status m3_prefill_fused(const void* x, const float* dt_raw, const float* dt_bias, const float* A,
+                           const float* omega, const float* lambda_raw, const void* B, const void* C,
+                           const float* D, int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
+                           const m3_dims* dims, m3_dtype io_dtype, const void* carry_B, const void* carry_x,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes m3_prefill needs for these sizes (0 on invalid sizes). Host only. */
 size_t m3_prefill_workspace_size(const m3_dims* dims, int32_t R, int32_t chunk, m3_dtype io_dtype);
 

@@ -28,7 +28,8 @@ EXPORTS = ["m3_prefill", "m3_prefill_workspace_size", "m3_prefill_plan", "m3_dec
            "m3_decode_state_init", "m3_decode_step", "m3_prologue", "m3_prefill_backward",
            "m3_prefill_backward_workspace_size", "m3_mixer_create", "m3_mixer_destroy", "m3_mixer_workspace_size",
            "m3_mixer_prefill", "m3_mixer_decode_step", "m3_status_string", "m3_last_error", "m3_abi_version",
-           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes", "m3_prefill_check", "m3_decode_step_fused"]
+           "m3_prefill_noalloc", "m3_noalloc_scratch_bytes", "m3_prefill_check", "m3_decode_step_fused",
+           "m3_prefill_fused"]
 
 
 class M3Dims(ctypes.Structure):
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
     dims_p = ctypes.POINTER(M3Dims)
     lib.m3_prefill.argtypes = [vp] * 8 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.m3_prefill.restype = ctypes.c_int
+    lib.m3_prefill_fused.argtypes = [vp] * 9 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.m3_prefill_fused.restype = ctypes.c_int
     lib.m3_prefill_noalloc.argtypes = [vp] * 8 + [i32, i32, vp, vp, vp, dims_p, ctypes.c_int, vp, vp, vp]
     lib.m3_prefill_noalloc.restype = ctypes.c_int
     lib.m3_prefill_check.argtypes = [dims_p, i32, i32, ctypes.c_int, vp, sz, vp]
@@ -183,11 +186,14 @@ def plan(d: M3Dims, R: int, chunk: int, io_dtype: int) -> M3Plan:
 
 
 def prefill(x, dt, A, omega, lam, B, C, D, R: int, chunk: int, h0=None, *, carry_B=None, carry_x=None,
-            y=None, h_out=None, workspace=None, return_state: bool = True, stream=None):
+            y=None, h_out=None, workspace=None, return_state: bool = True, stream=None, raw_steps: bool = False,
+            dt_bias=None):
     """m3_prefill on torch device tensors; returns (y, h_out).
 
     x [b][L][H][R][P], B/C [b][L][G][R][N] (bf16 or fp32, one dtype), dt/lam
     [b][L][H] fp32, A/D [H], omega [H][N/2], h0 [b][H][N][P] fp32 or None.
+    raw_steps: m3_prefill_fused -- dt and lam are raw projections (softplus with
+    dt_bias [H] or None, sigmoid).
     """
     if x.dim() != 5 or B.dim() != 5:
         raise ValueError("x must be [b][L][H][R][P] and B [b][L][G][R][N]")
@@ -207,6 +213,9 @@ def prefill(x, dt, A, omega, lam, B, C, D, R: int, chunk: int, h0=None, *, carry
     h0 = _need(h0, "h0", torch.float32, (b, H, N, P))
     carry_B = _need(carry_B, "carry_B", io, (b, G, R, N))
     carry_x = _need(carry_x, "carry_x", io, (b, H, R, P))
+    dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,))
+    if dt_bias is not None and not raw_steps:
+        raise ValueError("dt_bias is only read with raw_steps")
     if y is None:
         y = torch.empty_like(x)
     _need_out(y, "y", io, x.shape)
@@ -220,6 +229,11 @@ def prefill(x, dt, A, omega, lam, B, C, D, R: int, chunk: int, h0=None, *, carry
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if raw_steps:
+        check(lib.m3_prefill_fused(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(omega), _ptr(lam), _ptr(B),
+                                   _ptr(C), _ptr(D), R, chunk, _ptr(h0), _ptr(y), _ptr(h_out), ctypes.byref(d), code,
+                                   _ptr(carry_B), _ptr(carry_x), _ptr(workspace), ws_bytes, _stream(stream)))
+        return y, h_out
     check(lib.m3_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(omega), _ptr(lam), _ptr(B), _ptr(C), _ptr(D),
                          R, chunk, _ptr(h0), _ptr(y), _ptr(h_out), ctypes.byref(d), code,
                          _ptr(carry_B), _ptr(carry_x), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -44,23 +44,9 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
 
 // The input prologue of m3_decode_step_fused (m3_prologue's reading, see
 // m3_prologue.hip): softplus with the head's bias on the step, sigmoid on
-// lambda, and per (group, rank) row of B and C an RMS norm with weight and
-// bias, the result rounded to the io dtype as m3_prologue stores it.
-// softplus(x) = max(x, 0) + ln(1 + e^-|x|) and sigmoid through the hardware
-// exp2 / log2 (a few ulp): below e^-|x| = 2^-24 the log term is taken as e^-|x|
-// itself, where 1 + e^-|x| would round to 1
-__device__ __forceinline__ float softplus_f(float x) {
-    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
-    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-    const float l = e < 5.9604645e-8f ? e : __builtin_amdgcn_logf(1.f + e) * kLn2;
-    return fmaxf(x, 0.f) + l;
-}
-__device__ __forceinline__ float sigmoid_f(float x) {
-    constexpr float kLog2e = 1.4426950408889634f;
-    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);  // e^-|x| in (0, 1]
-    const float r = __builtin_amdgcn_rcpf(1.f + e);
-    return x >= 0.f ? r : e * r;
-}
+// lambda (softplus_f, sigmoid_f of m3_device.h), and per (group, rank) row of B
+// and C an RMS norm with weight and bias, the result rounded to the io dtype as
+// m3_prologue stores it.
 template <typename T>
 __device__ __forceinline__ float round_io(float v) {
     if constexpr (std::is_same<T, bf16_t>::value) return bf16_to_f32(f32_to_bf16(v));
@@ -341,7 +327,7 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// bf16 I/O, N in {64, 128}, P = 64, R = 8: the rank-R contractions on MFMA
+// bf16 I/O, N in {64, 128}, P = 64, R = 8 (and R 2-4 of the fused step): the rank-R contractions on MFMA
 // (v_mfma_f32_16x16x16_bf16). One 256-thread workgroup per (b, h); wave w owns
 // state columns 16 w .. 16 w + 15 and all 128 rows. In row tile nt, lane
 // (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column 16 w + l16: two whole
@@ -901,8 +887,16 @@ using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodeProlog
                           const float*, const float*, const float*, const bf16_t*, const bf16_t*, const float*,
                           bf16_t*, int64_t, int, int);
 
+// The fused step (PRO) at R 2-4 stays on the kernel with separate input sums:
+// with the prologue's registers on top, the merged-input kernel measured slower
+// there (R 4, N 128, b 128: 98.2 against 97.0 us per step).
 template <int N, bool PRO>
 MfmaKern<PRO> mfma_kernel_for(int R) {
+    if constexpr (PRO)
+        return R == 2 ? decode_mfma_kernel<2, N, PRO>
+             : R == 3 ? decode_mfma_kernel<3, N, PRO>
+             : R == 4 ? decode_mfma_kernel<4, N, PRO>
+                      : decode_mfma_kernel<8, N, PRO>;
     return R == 2 ? decode_mfma4_kernel<2, N, PRO>
          : R == 3 ? decode_mfma4_kernel<3, N, PRO>
          : R == 4 ? decode_mfma4_kernel<4, N, PRO>

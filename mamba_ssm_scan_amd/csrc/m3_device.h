@@ -18,6 +18,38 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ float lam_at(const float* lam, int64_t i) { return lam ? lam[i] : 1.f; }
 __device__ __forceinline__ float om_at(const float* om, int64_t i) { return om ? om[i] : 0.f; }
 
+// The input prologue's scalar maps (m3_prologue's reading): softplus for the
+// step and sigmoid for the trapezoid weight, through the hardware exp2 / log2 /
+// rcp (a few ulp). softplus(x) = max(x, 0) + ln(1 + e^-|x|); below e^-|x| =
+// 2^-24 the log term is taken as e^-|x| itself, where 1 + e^-|x| would round to 1.
+__device__ __forceinline__ float softplus_f(float x) {
+    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float l = e < 5.9604645e-8f ? e : __builtin_amdgcn_logf(1.f + e) * kLn2;
+    return fmaxf(x, 0.f) + l;
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);  // e^-|x| in (0, 1]
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
+    return x >= 0.f ? r : e * r;
+}
+
+// The step inputs as a prefill kernel reads them: dt and lambda as given
+// (raw = 0), or from their raw projections (raw = 1): dt = softplus(dt_raw +
+// the head's bias), lambda = sigmoid(lambda_raw), applied where the kernel
+// loads them. A NULL lambda array is lambda = 1 either way.
+struct StepIn {
+    float bias;  // the head's dt bias (raw only)
+    int raw;
+    __device__ __forceinline__ float dt(float v) const { return raw ? softplus_f(v + bias) : v; }
+    __device__ __forceinline__ float lamv(float v) const { return raw ? sigmoid_f(v) : v; }
+    __device__ __forceinline__ float lam(const float* l, int64_t i) const { return l ? lamv(l[i]) : 1.f; }
+};
+__device__ __forceinline__ StepIn step_in(const float* dt_bias, int raw, int h) {
+    return StepIn{raw && dt_bias ? dt_bias[h] : 0.f, raw};
+}
+
 // fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);

@@ -210,12 +210,16 @@ m3_status m3_prefill_check(const m3_dims* dims, int32_t R, int32_t chunk, m3_dty
     return M3_OK;
 }
 
-m3_status m3_prefill(const void* x, const float* dt, const float* A, const float* omega,
-                     const float* lambda, const void* B, const void* C, const float* D,
-                     int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
-                     const m3_dims* dims, m3_dtype io_dtype,
-                     const void* carry_B, const void* carry_x,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// m3_prefill and m3_prefill_fused: the checks and the launch. raw: dt and
+// lambda are raw projections, mapped (softplus with dt_bias, sigmoid) where the
+// kernels load them.
+m3_status prefill_impl(const void* x, const float* dt, const float* dt_bias, const float* A, const float* omega,
+                       const float* lambda, const void* B, const void* C, const float* D, int32_t R, int32_t chunk,
+                       const float* h0, void* y, float* h_out, const m3_dims* dims, m3_dtype io_dtype,
+                       const void* carry_B, const void* carry_x, void* workspace, size_t workspace_bytes,
+                       void* stream, bool raw) {
     g_err[0] = 0;
     m3_plan plan;
     m3_status s = make_plan(dims, R, chunk, io_dtype, &plan);
@@ -235,9 +239,9 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
     if ((carry_B == nullptr) != (carry_x == nullptr))
         return fail(M3_EINVAL, "carry_B and carry_x must be given together");
 
-    const void* ptrs[] = {x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x};
+    const void* ptrs[] = {x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x, dt_bias};
     const char* names[] = {"x", "dt", "A", "omega", "lambda", "B", "C", "D", "h0", "y", "h_out",
-                           "carry_B", "carry_x"};
+                           "carry_B", "carry_x", "dt_bias"};
     for (size_t i = 0; i < sizeof ptrs / sizeof ptrs[0]; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(M3_EALIGN, "%s is not 16-byte aligned", names[i]);
 
@@ -250,7 +254,8 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
                             rng("h0", h0, size_t(b) * H * N * P * 4),
                             rng("h_out", h_out, size_t(b) * H * N * P * 4),
                             rng("carry_B", carry_B, size_t(b) * G * R * N * es),
-                            rng("carry_x", carry_x, size_t(b) * H * R * P * es)};
+                            rng("carry_x", carry_x, size_t(b) * H * R * P * es),
+                            rng("dt_bias", dt_bias, H * 4)};
     for (const Range& r : inputs)
         if (overlaps(ry, r)) return fail(M3_EINVAL, "y overlaps %s", r.name);
     const Range rh = rng("h_out", h_out, size_t(b) * H * N * P * 4);
@@ -282,12 +287,35 @@ m3_status m3_prefill(const void* x, const float* dt, const float* A, const float
         m3::PrefillArgs a{x, dt, A, omega, lambda, B, C, D, h0, y, h_out, carry_B, carry_x,
                           b, L, (int32_t)H, (int32_t)G, (int32_t)P, (int32_t)N, R, kchunk, io_dtype,
                           plan, workspace, st};
+        a.dt_bias = raw ? dt_bias : nullptr;
+        a.raw_steps = raw ? 1 : 0;
         e = plan.path == M3_PATH_MFMA   ? m3::launch_prefill_mfma(a)
             : plan.path == M3_PATH_SCAN ? m3::launch_prefill_scan(a)
                                         : m3::launch_prefill_generic(a);
     }
     if (e != hipSuccess) return fail(M3_EHIP, "launch failed: %s", hipGetErrorString(e));
     return M3_OK;
+}
+
+}  // namespace
+
+m3_status m3_prefill(const void* x, const float* dt, const float* A, const float* omega,
+                     const float* lambda, const void* B, const void* C, const float* D,
+                     int32_t R, int32_t chunk, const float* h0, void* y, float* h_out,
+                     const m3_dims* dims, m3_dtype io_dtype,
+                     const void* carry_B, const void* carry_x,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(x, dt, nullptr, A, omega, lambda, B, C, D, R, chunk, h0, y, h_out, dims, io_dtype, carry_B,
+                        carry_x, workspace, workspace_bytes, stream, false);
+}
+
+m3_status m3_prefill_fused(const void* x, const float* dt_raw, const float* dt_bias, const float* A,
+                           const float* omega, const float* lambda_raw, const void* B, const void* C, const float* D,
+                           int32_t R, int32_t chunk, const float* h0, void* y, float* h_out, const m3_dims* dims,
+                           m3_dtype io_dtype, const void* carry_B, const void* carry_x, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return prefill_impl(x, dt_raw, dt_bias, A, omega, lambda_raw, B, C, D, R, chunk, h0, y, h_out, dims, io_dtype,
+                        carry_B, carry_x, workspace, workspace_bytes, stream, true);
 }
 
 // m3_prefill_noalloc: m3_prefill on the fixed device array of m3_noalloc.hip

@@ -29,6 +29,10 @@ struct PrefillArgs {
     m3_plan plan;
     void* workspace;
     hipStream_t stream;
+    // m3_prefill_fused: dt and lambda are raw projections (softplus with the
+    // head's bias dt_bias[H] (NULL: 0), sigmoid), applied where the kernels load them
+    const float* dt_bias;
+    int raw_steps;
 };
 
 // The input prologue fused into a decode step (m3_decode_step_fused): the step

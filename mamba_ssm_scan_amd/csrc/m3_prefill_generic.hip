@@ -29,7 +29,8 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
                        const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ D,
                        const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_out,
                        const T* __restrict__ carry_B, const T* __restrict__ carry_x, float* __restrict__ state,
-                       int64_t L, int H, int G, int P, int N, int R, int Q) {
+                       int64_t L, int H, int G, int P, int N, int R, int Q, const float* __restrict__ dt_bias,
+                       int raw) {
     extern __shared__ float sm[];
     float* Tc = sm;          // [Q] chunk-local cumulative dt
     float* gam = sm + Q;     // [Q] lambda*dt
@@ -44,9 +45,10 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
     const float Ah = A[h], Dh = D[h];
     const float* om = omega ? omega + int64_t(h) * K : nullptr;
     float* st = state + bh * int64_t(N) * P;
+    const StepIn si = step_in(dt_bias, raw, h);  // dt and lambda as given, or from raw projections
 
     // g = h0 + delta_0 * carry_B^T carry_x
-    const float d0 = (1.f - lam_at(lam, (b * L) * H + h)) * dt[(b * L) * H + h];
+    const float d0 = (1.f - si.lam(lam, (b * L) * H + h)) * si.dt(dt[(b * L) * H + h]);
     for (int e = tid; e < N * P; e += kThreads) {
         const int n = e / P, p = e % P;
         float v = h0 ? h0[bh * int64_t(N) * P + e] : 0.f;
@@ -67,12 +69,12 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
             float acc = 0.f;
             for (int i = 0; i < nt; ++i) {
                 const int64_t ti = (b * L + c0 + i) * H + h;
-                const float d = dt[ti];
+                const float d = si.dt(dt[ti]);
                 acc += d;
                 Tc[i] = acc;
-                gam[i] = lam_at(lam, ti) * d;
+                gam[i] = si.lam(lam, ti) * d;
                 const int64_t tn = c0 + i + 1;
-                dln[i] = tn < L ? (1.f - lam_at(lam, (b * L + tn) * H + h)) * dt[(b * L + tn) * H + h] : 0.f;
+                dln[i] = tn < L ? (1.f - si.lam(lam, (b * L + tn) * H + h)) * si.dt(dt[(b * L + tn) * H + h]) : 0.f;
             }
         }
         __syncthreads();
@@ -159,7 +161,7 @@ hipError_t launch_generic_t(const PrefillArgs& a) {
                        static_cast<const T*>(a.x), a.dt, a.A, a.omega, a.lam, static_cast<const T*>(a.B),
                        static_cast<const T*>(a.C), a.D, a.h0, static_cast<T*>(a.y), a.h_out,
                        static_cast<const T*>(a.carry_B), static_cast<const T*>(a.carry_x), state, a.L, a.H, a.G,
-                       a.P, a.N, a.R, a.chunk);
+                       a.P, a.N, a.R, a.chunk, a.dt_bias, a.raw_steps);
     return hipGetLastError();
 }
 

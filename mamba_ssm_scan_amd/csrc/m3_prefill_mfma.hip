@@ -84,16 +84,16 @@ struct ChunkRegs {
 
 template <class S>
 __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb, const float* __restrict__ dt,
-                                           const float* __restrict__ lam, int64_t tok0, int64_t L, int64_t c0, int H,
-                                           int G, int tid, int lane) {
+                                           const float* __restrict__ lam, const StepIn& si, int64_t tok0, int64_t L,
+                                           int64_t c0, int H, int G, int tid, int lane) {
     constexpr int R = S::R;
     const int nq = cb.nq;
     {
         const int ic = lane < nq ? lane : nq - 1;
         const int64_t ti = (tok0 + ic) * H;
-        const float d = dt[ti], l = lam_at(lam, ti);
+        const float d = si.dt(dt[ti]), l = si.lam(lam, ti);
         const bool has_next = c0 + ic + 1 < L;
-        const float dn = dt[has_next ? ti + H : ti], ln = lam_at(lam, has_next ? ti + H : ti);
+        const float dn = si.dt(dt[has_next ? ti + H : ti]), ln = si.lam(lam, has_next ? ti + H : ti);
         cr.d = lane < nq ? d : 0.f;
         cr.l = lane < nq ? l : 0.f;
         cr.dn = (lane < nq && has_next) ? dn : 0.f;
@@ -149,7 +149,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                     const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                     uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                     const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                    int64_t nbh, PassArgs pa, SegArgs sa) {
+                    int64_t nbh, PassArgs pa, SegArgs sa, const float* __restrict__ dt_bias, int raw) {
     using S = Shape<R, NW>;
     const int Nin = GEN ? pa.nin : N, Nrow = GEN ? pa.nrow : N, n_off = GEN ? pa.n_off : 0;
     const int Pin = GP ? pa.pin : P, Pcol = GP ? pa.pcol : P, p_off = GP ? pa.p_off : 0;
@@ -206,6 +206,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     const int h = int(bh % H);
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
+    const StepIn si = step_in(dt_bias, raw, h);  // dt and lambda as given, or from raw projections
     const float Dh = ym >= 2 ? 0.f : Dv[h];  // D x once, in the first row pass
     float* wsc = sW[wave];
 
@@ -241,7 +242,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     CR pre;
     {
         const ChunkBase cb = chunk_base(c_begin);
-        load_chunk<S>(pre, cb, dt + h, lam ? lam + h : nullptr, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
+        load_chunk<S>(pre, cb, dt + h, lam ? lam + h : nullptr, si, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
     }
 
     // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
@@ -256,7 +257,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         }
     } else {
         const int64_t t0 = (b * L) * H + h;
-        const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
+        const float dl0 = (1.f - si.lam(lam, t0)) * si.dt(dt[t0]);
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int u = wave * TPW + m, nt = u >> 2, pt = u & 3;
@@ -344,7 +345,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         // ---- 3. prefetch the next chunk's scalars, B, C and X (in flight through the compute below)
         const bool more = c + 1 < c_end;
         const ChunkBase cbn = chunk_base(more ? c + 1 : c);
-        if (more) load_chunk<S>(pre, cbn, dt + h, lam ? lam + h : nullptr, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
+        if (more) load_chunk<S>(pre, cbn, dt + h, lam ? lam + h : nullptr, si, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
         segT += double(Te);
         lds_barrier();
 
@@ -709,7 +710,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
                 const int64_t c0 = c * Q;
                 const int nq = int(L - c0 < Q ? L - c0 : Q);
                 float T = 0.f;
-                if (lane < nq) T = dt[(b * L + c0 + lane) * H + h];
+                if (lane < nq) T = si.dt(dt[(b * L + c0 + lane) * H + h]);
                 T = wave_prefix_sum(T, lane);
                 const float Te = lane_read(T, nq - 1);
                 wsc[192 + lane] = __builtin_amdgcn_exp2f(A2 * T);
@@ -862,15 +863,15 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const ChunkBase& cb, co
 template <bool ROT>
 __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A2, const float* omB, const float* base,
                                              uint16_t* sBt, uint16_t* sCt, uint16_t* sXT, float* sSc, int stid,
-                                             int lane, bool scal) {
-    const float rd = (r.ok & 1u) ? r.d : 0.f;
+                                             int lane, bool scal, const StepIn& si) {
+    const float rd = (r.ok & 1u) ? si.dt(r.d) : 0.f;
     const float T = wave_prefix_sum(rd, lane);
     if (scal) {
         const float S2 = A2 * T;
         const float S2e = lane_read(S2, nq - 1);
-        const float rdn = (r.ok & 2u) ? r.dn : 0.f;
-        const float rl = (r.ok & 1u) ? ((r.ok & 4u) ? r.l : 1.f) : 0.f;
-        const float rln = (r.ok & 2u) ? ((r.ok & 4u) ? r.ln : 1.f) : 0.f;
+        const float rdn = (r.ok & 2u) ? si.dt(r.dn) : 0.f;
+        const float rl = (r.ok & 1u) ? ((r.ok & 4u) ? si.lamv(r.l) : 1.f) : 0.f;
+        const float rln = (r.ok & 2u) ? ((r.ok & 4u) ? si.lamv(r.ln) : 1.f) : 0.f;
         const float gam = rl * rd, dln = (1.f - rln) * rdn;
         sSc[lane] = S2;
         sSc[64 + lane] = gam;
@@ -932,7 +933,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
                      const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                      uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                      const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks,
-                     int64_t nbh, PassArgs pa) {
+                     int64_t nbh, PassArgs pa, const float* __restrict__ dt_bias, int raw) {
     using namespace ws1;
     const int Nin = GEN ? pa.nin : N, Nrow = GEN ? pa.nrow : N, n_off = GEN ? pa.n_off : 0;
     const int Pin = GP ? pa.pin : P, Pcol = GP ? pa.pcol : P, p_off = GP ? pa.p_off : 0;
@@ -958,6 +959,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     const int h = int(bh % H);
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
+    const StepIn si = step_in(dt_bias, raw, h);  // dt and lambda as given, or from raw projections
     const float Dh = ym >= 2 ? 0.f : Dv[h];  // D x once, in the first row pass
     // pairs past the caller's Nin / 2 hold zero rows: rate 0
     const float* omh = omega ? omega + int64_t(h) * (Nrow / 2) + n_off / 2 : nullptr;
@@ -1003,7 +1005,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
                 base[j] = float(rv - floor(rv));
             }
             Tacc += stage_write<ROT>(r, chunk_base(cc).nq, A2, omB, base, sBt[bn], sCt[bn], sXT[bn], sSc[bn], stid,
-                                     lane, scal);
+                                     lane, scal, si);
         };
         load(ra, 0);
         if (n_chunks > 1) load(rb, 1);
@@ -1036,7 +1038,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     floatx4 gst[MRW * 4];
     {
         const int64_t t0 = (b * L) * H + h;
-        const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
+        const float dl0 = (1.f - si.lam(lam, t0)) * si.dt(dt[t0]);
 #pragma unroll
         for (int m = 0; m < MRW * 4; ++m) {
             gst[m] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1272,7 +1274,8 @@ hipError_t launch_ws_r1(const PrefillArgs& a, const PassArgs& pa, bool gen) {
                            static_cast<const uint16_t*>(a.x), a.dt, a.A, a.omega, a.lam,
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
-                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, pa);
+                           static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, pa,
+                           a.dt_bias, a.raw_steps);
         return hipGetLastError();
     });
 }
@@ -1306,7 +1309,7 @@ hipError_t launch_r(const PrefillArgs& a, const PassArgs& pa, bool gen) {
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
                            static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh, pa,
-                           sa);
+                           sa, a.dt_bias, a.raw_steps);
         return hipGetLastError();
     });
 }

@@ -118,6 +118,7 @@ __global__ void __launch_bounds__(256) prefill_scan_kernel(PrefillArgs a) {
     uint16_t* Yg = static_cast<uint16_t*>(a.y) + (b * L * a.H + h) * int64_t(R) * P;
     const float* dtg = a.dt + b * L * a.H + h;
     const float* lmg = a.lam ? a.lam + b * L * a.H + h : nullptr;
+    const StepIn si = step_in(a.dt_bias, a.raw_steps, h);  // dt and lambda as given, or from raw projections
 
     // ranks past R stay zero in B^T and x^T for the whole walk
     for (int e = tid; e < int(sizeof(s.B) / 4); e += NT) reinterpret_cast<uint32_t*>(&s.B)[e] = 0u;
@@ -126,7 +127,7 @@ __global__ void __launch_bounds__(256) prefill_scan_kernel(PrefillArgs a) {
     // (token j, rank r) of staging row q: j = q / R for q < 128, R <= 8 (exact)
     const unsigned invR = (65536u + unsigned(R) - 1u) / unsigned(R);
     auto delta_at = [&](int64_t t) {  // (1 - lambda) dt of token t, zero past the end
-        return t < L ? (1.f - (lmg ? lmg[t * a.H] : 1.f)) * dtg[t * a.H] : 0.f;
+        return t < L ? (1.f - si.lam(lmg, t * a.H)) * si.dt(dtg[t * a.H]) : 0.f;
     };
 
     // The walk carries g_t = h_t + delta_{t+1} U_t, the state the next step turns:
@@ -207,7 +208,7 @@ __global__ void __launch_bounds__(256) prefill_scan_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < S::MAXCS; ++u) {
                 const int e = tid + u * NT, j = e / K;
-                if (j < nt_) dcs[u] = db[unsigned(j) * unsigned(a.H)];
+                if (j < nt_) dcs[u] = si.dt(db[unsigned(j) * unsigned(a.H)]);
             }
             __syncthreads();  // every wave is done reading the previous block (its loads are in flight)
 #pragma unroll
@@ -241,7 +242,7 @@ __global__ void __launch_bounds__(256) prefill_scan_kernel(PrefillArgs a) {
         }
         if (tid < nt_) {
             const int64_t t = t0 + tid;
-            s.GD[tid][0] = (lmg ? lmg[t * a.H] : 1.f) * dtg[t * a.H];
+            s.GD[tid][0] = si.lam(lmg, t * a.H) * si.dt(dtg[t * a.H]);
             s.GD[tid][1] = delta_at(t + 1);
         }
         __syncthreads();

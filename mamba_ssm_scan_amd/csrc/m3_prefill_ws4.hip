@@ -138,7 +138,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
                    const uint16_t* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ h0,
                    uint16_t* __restrict__ y, float* __restrict__ h_out, const uint16_t* __restrict__ carry_B,
                    const uint16_t* __restrict__ carry_x, int64_t L, int H, int G, int Q, int64_t n_chunks, int64_t nbh,
-                   int rin_, SegArgs sa) {
+                   int rin_, SegArgs sa, const float* __restrict__ dt_bias, int raw) {
     using namespace ws4;
     using CF = Cfg<R>;
     constexpr int LR = CF::LR, QRP = CF::QRP, XS = CF::XS, UPT = CF::UPT, SPW = CF::SPW, TPW = CF::TPW;
@@ -182,6 +182,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
     const int grp = h / (H / G);
     const float A2 = Av[h] * kLog2e;
     const float Dh = Dv[h];
+    const StepIn si = step_in(dt_bias, raw, h);  // dt and lambda as given, or from raw projections
     const float* omh = (ROT && omega) ? omega + int64_t(h) * K : nullptr;
     auto omk = [&](int k) { return omh ? omh[k] : 0.f; };
     auto chunk_base = [&](int64_t cc) {
@@ -223,9 +224,9 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             const int64_t c0 = cc * Q;
             const int ic = lane < nq ? lane : nq - 1;
             const int64_t ti = (b * L + c0 + ic) * H + h;
-            const float d = dt[ti], l = lam_at(lam, ti);
+            const float d = si.dt(dt[ti]), l = si.lam(lam, ti);
             const bool has_next = c0 + ic + 1 < L;
-            const float dn = dt[has_next ? ti + H : ti], ln = lam_at(lam, has_next ? ti + H : ti);
+            const float dn = si.dt(dt[has_next ? ti + H : ti]), ln = si.lam(lam, has_next ? ti + H : ti);
             pre.d = lane < nq ? d : 0.f;
             pre.l = lane < nq ? l : 0.f;
             pre.dn = (lane < nq && has_next) ? dn : 0.f;
@@ -299,7 +300,7 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         floatx4 gst[TPW];
         {
             const int64_t t0 = (b * L) * H + h;
-            const float dl0 = (1.f - lam_at(lam, t0)) * dt[t0];
+            const float dl0 = (1.f - si.lam(lam, t0)) * si.dt(dt[t0]);
             const bool first = seg == 0;
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
@@ -822,7 +823,7 @@ hipError_t launch_prefill_ws4(const PrefillArgs& a) {
                            static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C), a.D, a.h0,
                            static_cast<uint16_t*>(a.y), a.h_out, static_cast<const uint16_t*>(a.carry_B),
                            static_cast<const uint16_t*>(a.carry_x), a.L, a.H, a.G, a.chunk, a.plan.n_chunks, nbh,
-                           a.R, sa);
+                           a.R, sa, a.dt_bias, a.raw_steps);
         return hipGetLastError();
     };
     const bool rot = a.omega != nullptr;

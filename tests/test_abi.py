@@ -136,6 +136,24 @@ def test_prefill_argument_errors(lib):
     assert st == 4 and "workspace" in msg
 
 
+def test_prefill_fused_argument_errors(lib):
+    """m3_prefill_fused: m3_prefill's checks, plus dt_bias (16-byte aligned, not under y)."""
+    d = _dims()
+    v = ctypes.c_void_p
+
+    def call(dtb=None, y=FAKE + 9 * (1 << 30), x=FAKE):
+        return lib.m3_prefill_fused(v(x) if x else None, v(FAKE + (1 << 30)), v(dtb) if dtb else None,
+                                    v(FAKE + (2 << 30)), None, None, v(FAKE + (5 << 30)), v(FAKE + (6 << 30)),
+                                    v(FAKE + (7 << 30)), 1, 16, None, v(y), None, ctypes.byref(d), bd.M3_F32, None,
+                                    None, None, 0, None)
+    assert call(x=None) == 1
+    assert call(dtb=FAKE + 14 * (1 << 30) + 8) == 4                      # misaligned bias
+    assert "dt_bias" in lib.m3_last_error().decode()
+    assert call(dtb=FAKE + 9 * (1 << 30) + 64) == 1                      # bias inside y
+    assert "dt_bias" in lib.m3_last_error().decode()
+    assert call(dtb=FAKE + 14 * (1 << 30)) == 7                          # valid: the generic path needs a workspace
+
+
 def test_noalloc_rejects_before_any_launch(lib):
     """m3_prefill_noalloc: same argument checks as m3_prefill; sizes whose workspace
     exceeds the fixed scratch are refused (M3_EWORKSPACE) before any HIP call."""
