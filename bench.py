@@ -149,7 +149,8 @@ def _pct(t, scale=1.0, unit="ms"):
 
 
 def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, rank=None, headdim=None):
-    """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both.
+    """special: "" (the workload), "real" (omega NULL: omega = 0), "euler" (lambda NULL: lambda = 1) or both;
+    "raw": m3_prefill_fused on raw dt / lambda projections (softplus with a per-head bias, sigmoid in the kernels).
 
     groups: 1 (B, C shared by all heads, the primary reading) or H (one B, C per head).
     dstate / rank: the workload's shape with another state size or rank (R 8: the token-walk kernel;
@@ -172,12 +173,18 @@ def bench_prefill(wid, steps, warmup, log, special="", groups=1, dstate=None, ra
                         binding.M3_BF16)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
 
-    no_om, no_lam = "real" in special, "euler" in special
+    no_om, no_lam, raw = "real" in special, "euler" in special, "raw" in special
+    if raw:  # raw projections of the step and the trapezoid weight
+        for k, p in enumerate(copies):
+            r = inputs.prologue_inputs(tokens=(w.batch, w.seqlen), heads=w.heads, groups=G, rank=w.rank,
+                                       dstate=w.dstate, io_dtype=w.io_dtype, wid=400 + wid, step=k, device="cuda")
+            p.update(dt=r["dt_raw"], lam=r["lambda_raw"], dt_bias=r["dt_bias"])
 
     def run(k):
         p = copies[k % N_COPIES]
         binding.prefill(p["x"], p["dt"], p["A"], None if no_om else p["omega"], None if no_lam else p["lam"],
-                        p["B"], p["C"], p["D"], w.rank, w.chunk, y=y, h_out=h, workspace=ws)
+                        p["B"], p["C"], p["D"], w.rank, w.chunk, y=y, h_out=h, workspace=ws, raw_steps=raw,
+                        dt_bias=p.get("dt_bias"))
 
     t = time_calls(run, steps, warmup)
     ms = t["mean"]
@@ -619,7 +626,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--only", default="", help="comma list of prefill1,prefill2,decode1,decode4,long,copy,prologue, "
-                                               "prefill1_real/_euler/_real_euler: run just these (profiling runs); "
+                                               "prefill1_real/_euler/_real_euler/_raw, prefill2_raw: run just these (profiling runs); "
                                                "copy = a 1 GiB device copy for counter scaling")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -647,6 +654,8 @@ def main():
                 bench_prefill(2, args.steps, args.warmup, log, rank=8)
             elif item in ("prefill1_g64", "prefill2_g64"):
                 bench_prefill(int(item[7]), args.steps, args.warmup, log, groups=64)
+            elif item == "prefill2_raw":
+                bench_prefill(2, args.steps, args.warmup, log, special="raw")
             elif item.startswith("prefill1_"):
                 bench_prefill(1, args.steps, args.warmup, log, special=item[len("prefill1_"):])
             elif item in ("decode1", "decode4"):
@@ -717,6 +726,9 @@ def main():
                                        "frac": lg["prefill_hbm_frac"], "bytes_per_launch": lg["prefill_bytes"]})
         out["long_prefill_decode"] = lg
         # the pages' special cases on the same workload: omega = 0 (no rotation), lambda = 1 (Euler)
+        # dt and lambda from raw projections, mapped inside the prefill kernels (m3_prefill_fused)
+        out["prefill_raw_steps"] = {"siso_r1": bench_prefill(1, args.steps, args.warmup, log, special="raw"),
+                                    "mimo_r4": bench_prefill(2, args.steps, args.warmup, log, special="raw")}
         out["prefill_special_cases"] = {sp: bench_prefill(1, args.steps, args.warmup, log, special=sp)
                                         for sp in ("real", "euler", "real_euler")}
         # the secondary reading: one B, C per head (64x the B/C bytes)

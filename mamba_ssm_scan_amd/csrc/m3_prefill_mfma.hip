@@ -76,7 +76,8 @@ __device__ __forceinline__ int strip_of(int wave, int si) {
 // Global operands of one chunk, held in registers until they are staged.
 template <class S>
 struct ChunkRegs {
-    float d, l, dn, ln;                    // lane = token: dt, lambda, and of the next token
+    float d, l, dn, ln;                    // lane = token: dt, lambda, and of the next token, as loaded
+    unsigned ok;                           // bit 0: token in the chunk; bit 1: and a next token exists; bit 2: lambda given
     u32x4 b[S::UPT][S::R];                 // B rows (token, rank) of this thread's units
     u32x4 c[S::C_LDS ? S::UPT : 1][S::R];  // C rows, when staged in LDS
     u32x4 x0[S::XPT], x1[S::XPT];
@@ -84,20 +85,22 @@ struct ChunkRegs {
 
 template <class S>
 __device__ __forceinline__ void load_chunk(ChunkRegs<S>& cr, const ChunkBase& cb, const float* __restrict__ dt,
-                                           const float* __restrict__ lam, const StepIn& si, int64_t tok0, int64_t L,
-                                           int64_t c0, int H, int G, int tid, int lane) {
+                                           const float* __restrict__ lam, int64_t tok0, int64_t L, int64_t c0, int H,
+                                           int G, int tid, int lane) {
     constexpr int R = S::R;
     const int nq = cb.nq;
     {
         const int ic = lane < nq ? lane : nq - 1;
         const int64_t ti = (tok0 + ic) * H;
-        const float d = si.dt(dt[ti]), l = si.lam(lam, ti);
+        // kept as loaded and mapped at use (see the staging below); without
+        // lambda, dt stands in as a valid address and the value is replaced at use
         const bool has_next = c0 + ic + 1 < L;
-        const float dn = si.dt(dt[has_next ? ti + H : ti]), ln = si.lam(lam, has_next ? ti + H : ti);
-        cr.d = lane < nq ? d : 0.f;
-        cr.l = lane < nq ? l : 0.f;
-        cr.dn = (lane < nq && has_next) ? dn : 0.f;
-        cr.ln = (lane < nq && has_next) ? ln : 0.f;
+        const float* lp = lam ? lam : dt;
+        cr.d = dt[ti];
+        cr.l = lp[ti];
+        cr.dn = dt[has_next ? ti + H : ti];
+        cr.ln = lp[has_next ? ti + H : ti];
+        cr.ok = (lane < nq ? 1u : 0u) | ((lane < nq && has_next) ? 2u : 0u) | (lam ? 4u : 0u);
     }
     const int pc = tid & 15;
 #pragma unroll
@@ -242,7 +245,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
     CR pre;
     {
         const ChunkBase cb = chunk_base(c_begin);
-        load_chunk<S>(pre, cb, dt + h, lam ? lam + h : nullptr, si, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
+        load_chunk<S>(pre, cb, dt + h, lam ? lam + h : nullptr, b * L + c_begin * Q, L, c_begin * Q, H, G, tid, lane);
     }
 
     // ---- initial state g = h0 + delta_0 carry_B^T carry_x, tiles (nt, pt) of this wave
@@ -292,12 +295,15 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         uint16_t* gTn = sGT[(c - c_begin + 1) & 1];
 
         // ---- 1. per-token scalars, computed by every wave for itself (lane = token)
-        const float T = wave_prefix_sum(pre.d, lane);
+        const bool v0 = pre.ok & 1u, v1 = pre.ok & 2u, hl = pre.ok & 4u;
+        const float d = v0 ? si.dt(pre.d) : 0.f, l = v0 ? (hl ? si.lamv(pre.l) : 1.f) : 0.f;
+        const float dn = v1 ? si.dt(pre.dn) : 0.f, ln = v1 ? (hl ? si.lamv(pre.ln) : 1.f) : 0.f;
+        const float T = wave_prefix_sum(d, lane);
         const float S2 = A2 * T;
         const float S2e = lane_read(S2, nq - 1);
         const float Te = lane_read(T, nq - 1);
         {
-            const float gam = pre.l * pre.d, dln = (1.f - pre.ln) * pre.dn;
+            const float gam = l * d, dln = (1.f - ln) * dn;
             wsc[lane] = S2;
             wsc[64 + lane] = gam;
             wsc[128 + lane] = dln;
@@ -345,7 +351,7 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
         // ---- 3. prefetch the next chunk's scalars, B, C and X (in flight through the compute below)
         const bool more = c + 1 < c_end;
         const ChunkBase cbn = chunk_base(more ? c + 1 : c);
-        if (more) load_chunk<S>(pre, cbn, dt + h, lam ? lam + h : nullptr, si, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
+        if (more) load_chunk<S>(pre, cbn, dt + h, lam ? lam + h : nullptr, b * L + (c + 1) * Q, L, (c + 1) * Q, H, G, tid, lane);
         segT += double(Te);
         lds_barrier();
 

@@ -75,7 +75,8 @@ __device__ __forceinline__ int strip4(int w, int k) { return k * NOW + ((k & 1) 
 // Global operands of one chunk for a state thread, held until they are staged.
 template <int R>
 struct Pre {
-    float d, l, dn, ln;              // lane = token: dt, lambda, and of the next token
+    float d, l, dn, ln;              // lane = token: dt, lambda, and of the next token, as loaded
+    unsigned ok;                     // bit 0: token in the chunk; bit 1: and a next token exists; bit 2: lambda given
     u32x4 b[Cfg<R>::UPT][R];      // B rows (token (stid >> 4) + 16 m, rank r), 8 columns at 8 (stid & 15)
 };
 
@@ -224,13 +225,17 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
             const int64_t c0 = cc * Q;
             const int ic = lane < nq ? lane : nq - 1;
             const int64_t ti = (b * L + c0 + ic) * H + h;
-            const float d = si.dt(dt[ti]), l = si.lam(lam, ti);
+            // Kept as loaded and mapped at use (rope): masking or mapping them
+            // here would wait for these loads, and with them for the loads issued
+            // before. Without lambda (lambda = 1) dt stands in as a valid
+            // address and the value is replaced at use.
             const bool has_next = c0 + ic + 1 < L;
-            const float dn = si.dt(dt[has_next ? ti + H : ti]), ln = si.lam(lam, has_next ? ti + H : ti);
-            pre.d = lane < nq ? d : 0.f;
-            pre.l = lane < nq ? l : 0.f;
-            pre.dn = (lane < nq && has_next) ? dn : 0.f;
-            pre.ln = (lane < nq && has_next) ? ln : 0.f;
+            const float* lp = lam ? lam : dt;
+            pre.d = dt[ti];
+            pre.l = lp[ti];
+            pre.dn = dt[has_next ? ti + H : ti];
+            pre.ln = lp[has_next ? ti + H : ti];
+            pre.ok = (lane < nq ? 1u : 0u) | ((lane < nq && has_next) ? 2u : 0u) | (lam ? 4u : 0u);
 #pragma unroll
             for (int m = 0; m < UPT; ++m) {
                 const int i = (stid >> 4) + m * (NST / 16);
@@ -244,11 +249,14 @@ prefill_ws4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt,
         u32x4 cs4[UPT];
         float sc[7];
         auto rope = [&](int nq) -> float {
-            const float T = wave_prefix_sum(pre.d, lane);
+            const bool v0 = pre.ok & 1u, v1 = pre.ok & 2u, hl = pre.ok & 4u;
+            const float d = v0 ? si.dt(pre.d) : 0.f, l = v0 ? (hl ? si.lamv(pre.l) : 1.f) : 0.f;
+            const float dn = v1 ? si.dt(pre.dn) : 0.f, ln = v1 ? (hl ? si.lamv(pre.ln) : 1.f) : 0.f;
+            const float T = wave_prefix_sum(d, lane);
             const float Te = lane_read(T, nq - 1);
             {
                 const float S2 = A2 * T, S2e = A2 * Te;
-                const float gam = pre.l * pre.d, dln = (1.f - pre.ln) * pre.dn;
+                const float gam = l * d, dln = (1.f - ln) * dn;
                 sc[0] = S2;
                 sc[1] = gam;
                 sc[2] = dln;
