@@ -117,7 +117,7 @@ __device__ void qk_norm_rows(float* rb, float* rc, int R, int N, int g, const De
 
 // Threads per workgroup of the N = 128, P = 64 kernel, per rank class.
 #ifndef M3_DECODE_THREADS_R1
-#define M3_DECODE_THREADS_R1 512
+#define M3_DECODE_THREADS_R1 256
 #endif
 #ifndef M3_DECODE_THREADS_R4
 #define M3_DECODE_THREADS_R4 1024
