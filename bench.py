@@ -36,11 +36,11 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # sources it was taken on (sha256 prefix over the listed files, in order); the
 # summaries with the commands are in profiles/. None until a kernel is profiled.
 MEASURED_TRAFFIC = {
-    "prefill1": ("7f51053fff5ed60f", (2.0 * 39158.9 + 73728.0) * 1024),
-    "prefill2": ("f39f6d3b0ef598cc", (2.0 * 149809.1 + 270336.0) * 1024),
-    "long": ("f39f6d3b0ef598cc", (2.0 * 741749.8 + 1079920.1) * 1024),
-    "decode1": ("eb03525986fbf79a", (2.0 * 133579.7 + 264517.3) * 1024),
-    "decode4": ("eb03525986fbf79a", (2.0 * 139358.8 + 271082.0) * 1024),
+    "prefill1": ("9fa100e3b9e5d3cc", (2.0 * 39179.9 + 73728.0) * 1024),
+    "prefill2": ("91c0da9e1364c8c6", (2.0 * 150009.3 + 270336.0) * 1024),
+    "long": ("91c0da9e1364c8c6", (2.0 * 746988.6 + 1079920.3) * 1024),
+    "decode1": ("d7d1f0e786db61f9", (2.0 * 133817.7 + 264550.2) * 1024),
+    "decode4": ("d7d1f0e786db61f9", (2.0 * 137561.6 + 271276.6) * 1024),
 }
 
 
@@ -56,11 +56,11 @@ def source_sha(files):
 
 # kernel sources behind each timed workload (their sha256 prefix keys the traffic figures)
 SOURCES = {
-    "prefill1": ("m3_prefill_mfma.hip", "m3_mfma_common.h"),
-    "prefill2": ("m3_prefill_ws4.hip", "m3_mfma_common.h"),
-    "long": ("m3_prefill_ws4.hip", "m3_mfma_common.h"),
-    "decode1": ("m3_decode.hip",),
-    "decode4": ("m3_decode.hip",),
+    "prefill1": ("m3_prefill_mfma.hip", "m3_mfma_common.h", "m3_device.h"),
+    "prefill2": ("m3_prefill_ws4.hip", "m3_mfma_common.h", "m3_device.h"),
+    "long": ("m3_prefill_ws4.hip", "m3_mfma_common.h", "m3_device.h"),
+    "decode1": ("m3_decode.hip", "m3_device.h"),
+    "decode4": ("m3_decode.hip", "m3_device.h"),
 }
 
 
