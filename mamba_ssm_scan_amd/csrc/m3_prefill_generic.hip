@@ -13,7 +13,13 @@
 // rows of the decay x width-2 convolution mask (same digest, Fig. 2), e is
 // the chunk's last token and delta_{j+1} is the next token's (zero past the
 // end). g is the state entering the chunk with the previous token's trapezoid
-// term already added, so chunks couple only through g.
+// term already added, so chunks couple only through g. C~_i . B~_j is C_i^T
+// Rot(Phi_i - Phi_j) B_j, the relative turn. When the chunk's B~ and C~ fit
+// in LDS next to the token scalars (2 Q R N floats, up to kRotCacheBytes),
+// they are formed once per chunk and every contraction is a plain dot
+// product; when the chunk's masked scores fit as well (Q^2 R^2 more floats),
+// they are formed once per chunk too (cached = 2); otherwise the turns are
+// recomputed where they are used.
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -21,6 +27,7 @@ namespace m3 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr size_t kRotCacheBytes = 128 * 1024;  // dynamic LDS limit of the cached forms
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
@@ -30,11 +37,14 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
                        const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_out,
                        const T* __restrict__ carry_B, const T* __restrict__ carry_x, float* __restrict__ state,
                        int64_t L, int H, int G, int P, int N, int R, int Q, const float* __restrict__ dt_bias,
-                       int raw) {
+                       int raw, int cached) {
     extern __shared__ float sm[];
     float* Tc = sm;          // [Q] chunk-local cumulative dt
     float* gam = sm + Q;     // [Q] lambda*dt
     float* dln = sm + 2 * Q; // [Q] (1-lambda)*dt of the following token
+    float* Bt = sm + 3 * Q;                    // cached: [Q][R][N] B~ of the chunk
+    float* Ct = Bt + int64_t(Q) * R * N;       // cached: [Q][R][N] C~
+    float* Wm = Ct + int64_t(Q) * R * N;       // cached 2: [Q][R][Q][R] masked scores M_ij (C~_i . B~_j)
 
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -78,9 +88,68 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
             }
         }
         __syncthreads();
+        if (cached) {  // B~_j = Rot(-Phi_j) B_j and C~_j for every (token, rank, pair) of the chunk
+            for (int e = tid; e < nt * R * K; e += kThreads) {
+                const int j = e / (R * K), r = (e / K) % R, k = e % K;
+                float s, c;
+                sincosf(om_at(om, k) * Tc[j], &s, &c);
+                const int64_t src = ((b * L + c0 + j) * G + g) * int64_t(R) * N + int64_t(r) * N + 2 * k;
+                const float b0 = Io<T>::load(B, src), b1 = Io<T>::load(B, src + 1);
+                const float c0v = Io<T>::load(C, src), c1v = Io<T>::load(C, src + 1);
+                const int64_t o = (int64_t(j) * R + r) * N + 2 * k;
+                Bt[o] = c * b0 + s * b1;
+                Bt[o + 1] = c * b1 - s * b0;
+                Ct[o] = c * c0v + s * c1v;
+                Ct[o + 1] = c * c1v - s * c0v;
+            }
+            __syncthreads();
+        }
+        if (cached == 2) {  // the masked scores of the chunk's causal (i, j) pairs, rank by rank
+            const int QR = Q * R;
+            for (int e = tid; e < nt * R * nt * R; e += kThreads) {
+                const int ir = e / (nt * R), jr = e % (nt * R);
+                const int i = ir / R, j = jr / R;
+                float v = 0.f;
+                if (j <= i) {
+                    const float* Ci = Ct + int64_t(ir) * N;
+                    const float* Bj = Bt + int64_t(jr) * N;
+                    for (int n = 0; n < N; ++n) v += Ci[n] * Bj[n];
+                    v *= expf(Ah * (Tc[i] - Tc[j])) * (gam[j] + (j < i ? dln[j] : 0.f));
+                }
+                Wm[int64_t(ir) * QR + jr] = v;
+            }
+            __syncthreads();
+        }
 
         // outputs of the chunk
-        for (int e = tid; e < nt * R * P; e += kThreads) {
+        for (int e = tid; cached && e < nt * R * P; e += kThreads) {
+            const int i = e / (R * P), r = (e / P) % R, p = e % P;
+            const float* Cti = Ct + (int64_t(i) * R + r) * N;
+            const float Ti = Tc[i];
+            float inter = 0.f;
+            for (int n = 0; n < N; ++n) inter += Cti[n] * st[n * P + p];
+            float acc = expf(Ah * Ti) * inter;
+            if (cached == 2) {
+                const float* Wi = Wm + (int64_t(i) * R + r) * (int64_t(Q) * R);
+                for (int j = 0; j <= i; ++j) {
+                    const T* xj = x + ((b * L + c0 + j) * H + h) * int64_t(R) * P;
+                    for (int rr = 0; rr < R; ++rr) acc += Wi[j * R + rr] * Io<T>::load(xj, int64_t(rr) * P + p);
+                }
+            }
+            for (int j = 0; cached == 1 && j <= i; ++j) {
+                const float m = expf(Ah * (Ti - Tc[j])) * (gam[j] + (j < i ? dln[j] : 0.f));
+                const T* xj = x + ((b * L + c0 + j) * H + h) * int64_t(R) * P;
+                for (int rr = 0; rr < R; ++rr) {
+                    const float* Btj = Bt + (int64_t(j) * R + rr) * N;
+                    float sc = 0.f;
+                    for (int n = 0; n < N; ++n) sc += Cti[n] * Btj[n];
+                    acc += m * sc * Io<T>::load(xj, int64_t(rr) * P + p);
+                }
+            }
+            const int64_t yi = ((b * L + c0 + i) * H + h) * int64_t(R) * P + int64_t(r) * P + p;
+            Io<T>::store(y, yi, acc + Dh * Io<T>::load(x, yi));
+        }
+        for (int e = tid; !cached && e < nt * R * P; e += kThreads) {
             const int i = e / (R * P), r = (e / P) % R, p = e % P;
             const T* Ci = C + ((b * L + c0 + i) * G + g) * int64_t(R) * N + int64_t(r) * N;
             const float Ti = Tc[i];
@@ -123,10 +192,19 @@ prefill_generic_kernel(const T* __restrict__ x, const float* __restrict__ dt, co
             float a0 = dec * st[(2 * k) * P + p], a1 = dec * st[(2 * k + 1) * P + p];
             for (int j = 0; j < nt; ++j) {
                 const float w = expf(Ah * (Te - Tc[j])) * (gam[j] + dln[j]);
+                const T* xj = x + ((b * L + c0 + j) * H + h) * int64_t(R) * P;
+                if (cached) {
+                    for (int r = 0; r < R; ++r) {
+                        const float* Btj = Bt + (int64_t(j) * R + r) * N + 2 * k;
+                        const float xv = w * Io<T>::load(xj, int64_t(r) * P + p);
+                        a0 += Btj[0] * xv;
+                        a1 += Btj[1] * xv;
+                    }
+                    continue;
+                }
                 float s, c;
                 sincosf(om_at(om, k) * Tc[j], &s, &c);
                 const T* Bj = B + ((b * L + c0 + j) * G + g) * int64_t(R) * N;
-                const T* xj = x + ((b * L + c0 + j) * H + h) * int64_t(R) * P;
                 for (int r = 0; r < R; ++r) {
                     const float b0 = Io<T>::load(Bj, int64_t(r) * N + 2 * k);
                     const float b1 = Io<T>::load(Bj, int64_t(r) * N + 2 * k + 1);
@@ -155,13 +233,18 @@ template <typename T>
 hipError_t launch_generic_t(const PrefillArgs& a) {
     const PrefillWorkspace ws = prefill_workspace_layout(a.b, a.L, a.H, a.P, a.N, a.R, a.plan.segments, a.plan.path);
     float* state = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ws.state_off);
-    const size_t shmem = size_t(3) * a.chunk * sizeof(float);
+    // the chunk's B~ and C~ in LDS when they fit (chunk <= L does not change the need)
+    const size_t base = size_t(3) * a.chunk * sizeof(float);
+    const size_t rot = size_t(2) * a.chunk * a.R * a.N * sizeof(float);
+    const size_t scores = size_t(a.chunk) * a.R * a.chunk * a.R * sizeof(float);
+    const int cached = base + rot + scores <= kRotCacheBytes ? 2 : base + rot <= kRotCacheBytes ? 1 : 0;
+    const size_t shmem = cached == 2 ? base + rot + scores : cached ? base + rot : base;
     const dim3 grid(unsigned(a.b * a.H));
     hipLaunchKernelGGL(prefill_generic_kernel<T>, grid, dim3(kThreads), shmem, a.stream,
                        static_cast<const T*>(a.x), a.dt, a.A, a.omega, a.lam, static_cast<const T*>(a.B),
                        static_cast<const T*>(a.C), a.D, a.h0, static_cast<T*>(a.y), a.h_out,
                        static_cast<const T*>(a.carry_B), static_cast<const T*>(a.carry_x), state, a.L, a.H, a.G,
-                       a.P, a.N, a.R, a.chunk, a.dt_bias, a.raw_steps);
+                       a.P, a.N, a.R, a.chunk, a.dt_bias, a.raw_steps, cached);
     return hipGetLastError();
 }
 

@@ -30,7 +30,10 @@ def test_workload0_prefill_chunk16():
     assert_close(h, h_ref, 1e-4, "h_out")
 
 
-@pytest.mark.parametrize("chunk", [1, 2, 3, 5, 7, 16, 64, 127, 128, 200])
+# the generic kernel's three forms (workload 0: R 1, N 16): up to chunk 128 the
+# chunk's turned B, C and masked scores fit its LDS cache, at 200 the turned B
+# and C only, at 4096 neither (the turns are recomputed where they are used)
+@pytest.mark.parametrize("chunk", [1, 2, 3, 5, 7, 16, 64, 127, 128, 200, 4096])
 def test_workload0_any_chunk(chunk):
     p = inputs.workload_prefill(0)
     y_ref, h_ref = oracle.scan(p)

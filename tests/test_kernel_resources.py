@@ -21,9 +21,10 @@ LLVM = "/opt/rocm/llvm/bin"
 LDS_PER_CU = 160 * 1024
 
 # the largest dynamic LDS each kernel that takes it can be launched with:
-#   the generic fp32 prefill: 3 floats per token of a chunk, chunk <= 4096;
+#   the generic fp32 prefill: 3 floats per token of a chunk (chunk <= 4096), or with the
+#   chunk's turned B and C (and its masked scores) cached, at most 128 KiB in all;
 #   the fused decode step's generic kernel: B_t and C_t rows, R * N <= 8192 floats each
-DYNAMIC = {"prefill_generic_kernel": 3 * 4096 * 4, "decode_generic_kernel": 2 * 8192 * 4}
+DYNAMIC = {"prefill_generic_kernel": max(3 * 4096 * 4, 128 * 1024), "decode_generic_kernel": 2 * 8192 * 4}
 
 # instances on the workloads' paths: no spills allowed
 NO_SCRATCH = [r"prefill_ws_r1_kernelILb[01]ELb0ELi0ELb0E", r"prefill_ws4_kernelILi[248]ELb[01]ELb[01]ELb0E",
