@@ -160,14 +160,20 @@ DCASES = [
     (1, 6, 3, 3, 64, 256, 6, "f32"),
     # the float4 row kernel at the other (N, P) it is built for (bf16 I/O, R 1, 2, 4)
     (2, 6, 2, 1, 32, 64, 1, "bf16"),
-    (1, 6, 3, 1, 64, 64, 4, "bf16"),
+    (1, 6, 3, 1, 64, 64, 4, "bf16"),   # (P 64, N 64, R 4: the merged-input MFMA kernel)
     (2, 5, 2, 2, 128, 64, 2, "bf16"),
     (1, 6, 2, 1, 32, 128, 4, "bf16"),
     (2, 6, 2, 1, 128, 128, 1, "bf16"),
     (1, 6, 2, 1, 32, 256, 2, "bf16"),
     (1, 5, 4, 2, 64, 256, 4, "bf16"),
     (1, 6, 2, 1, 128, 256, 1, "bf16"),
-    (2, 6, 2, 1, 64, 128, 3, "bf16"),   # R 3 and R 8 on the row kernel
+    (2, 6, 2, 1, 64, 128, 3, "bf16"),   # R 3: the merged-input MFMA kernel with a zero rank slot
+    # the merged-input MFMA kernel at R 2, 3 and N 64, 128, with groups
+    (2, 6, 4, 2, 64, 64, 2, "bf16"),
+    (1, 6, 2, 1, 64, 64, 3, "bf16"),
+    (2, 6, 4, 2, 64, 128, 2, "bf16"),
+    (1, 7, 4, 2, 64, 128, 4, "bf16"),
+    # R 3 and R 8 on the row kernel
     (1, 5, 2, 1, 128, 256, 3, "bf16"),
     (2, 6, 2, 2, 32, 64, 8, "bf16"),
     (1, 6, 2, 1, 128, 128, 8, "bf16"),  # R 8 past the row kernel's LDS: the generic step
