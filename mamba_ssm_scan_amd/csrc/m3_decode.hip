@@ -85,11 +85,21 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (GL == 64) return (r0 + r1) + (r2 + r3);
     return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
 }
-// one element of a normalised row: raw * scale * weight + bias, rounded to the io dtype
+// io elements as loaded, in 32-bit words (two bf16, or one float), and the
+// value of element i of them: loads kept in this form until their use need no
+// wait where they are issued
 template <typename T>
-__device__ __forceinline__ float norm_elem(float v, float scale, const float* w, const float* bb, int64_t i) {
-    return round_io<T>(v * scale * (w ? w[i] : 1.f) + (bb ? bb[i] : 0.f));
-}
+struct RawIo {
+    static constexpr int per_word = 1;
+    __device__ __forceinline__ static float val(const unsigned* w, int i) { return __uint_as_float(w[i]); }
+};
+template <>
+struct RawIo<bf16_t> {
+    static constexpr int per_word = 2;
+    __device__ __forceinline__ static float val(const unsigned* w, int i) {
+        return __uint_as_float((i & 1) ? w[i >> 1] & 0xffff0000u : w[i >> 1] << 16);
+    }
+};
 
 // RMS-normalise the R rows of B (rb) and of C (rc), N fp32 values each in LDS,
 // in place, with the weights and biases of group g; one wave per row. The
@@ -157,11 +167,15 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
     // lanes that load it (PE consecutive entries per lane): its sum of squares
     // never leaves them. Rows of B first, then of C, in whole lane groups (2 R GL
     // and NTH are multiples of GL). The rows and their weights are loaded first,
-    // ahead of the state, so their latency hides under the state stream.
+    // ahead of the state, so their latency hides under the state stream; the
+    // rows stay raw until their use (a conversion here would wait for them
+    // before the state loads are issued).
     constexpr int PE = N >= 256 ? N / 64 : 2, GL = N / PE;
     constexpr int NIT = PRO ? (2 * R * GL + NTH - 1) / NTH : 0;
     static_assert(GL <= 64 && (GL & (GL - 1)) == 0, "row lanes");
-    float pv[NIT > 0 ? NIT : 1][PE], pw[NIT > 0 ? NIT : 1][PE], pb[NIT > 0 ? NIT : 1][PE];
+    constexpr int PW = PE / RawIo<T>::per_word;  // 32-bit words per item (rows start 16-byte aligned)
+    unsigned pv[NIT > 0 ? NIT : 1][PW];
+    float pw[NIT > 0 ? NIT : 1][PE], pb[NIT > 0 ? NIT : 1][PE];
     if constexpr (PRO) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -173,13 +187,45 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
             const float* w = isC ? pro.C_weight : pro.B_weight;
             const float* bb = isC ? pro.C_bias : pro.B_bias;
             const int64_t o = (int64_t(g) * R + r) * N + n0;
+            const unsigned* src32 = reinterpret_cast<const unsigned*>(src + r * N + n0);
+#pragma unroll
+            for (int i = 0; i < PW; ++i) pv[it][i] = src32[i];
 #pragma unroll
             for (int i = 0; i < PE; ++i) {
-                pv[it][i] = Io<T>::load(src, r * N + n0 + i);
                 pw[it][i] = w ? w[o + i] : 1.f;
                 pb[it][i] = bb ? bb[o + i] : 0.f;
             }
         }
+    }
+
+    // The step's other small rows (B_t and C_t unless the prologue loaded them,
+    // B_prev, x_t, x_prev) as 32-bit words, also ahead of the state: staging
+    // them then waits for them alone (completion counts are in order).
+    constexpr int WPE = RawIo<T>::per_word;              // io elements per word
+    constexpr int NWB = R * N / WPE, NWX = R * P / WPE;  // words per row set
+    constexpr int IB = (NWB + NTH - 1) / NTH, IX = (NWX + NTH - 1) / NTH;
+    const unsigned* Bt32 = reinterpret_cast<const unsigned*>(B + bg * (R * N));
+    const unsigned* Ct32 = reinterpret_cast<const unsigned*>(C + bg * (R * N));
+    const unsigned* Bp32 = reinterpret_cast<const unsigned*>(carry_B + (int64_t(pr) * nb * G + bg) * (R * N));
+    const unsigned* xt32 = reinterpret_cast<const unsigned*>(x + bh * (R * P));
+    const unsigned* xp32 = reinterpret_cast<const unsigned*>(carry_x + bh * (R * P));
+    unsigned wb[PRO ? 1 : IB], wc[PRO ? 1 : IB], wbp[IB], wx[IX], wxp[IX];
+#pragma unroll
+    for (int it = 0; it < IB; ++it) {
+        const int e = tid + it * NTH;
+        if (e >= NWB) continue;
+        if constexpr (!PRO) {
+            wb[it] = Bt32[e];
+            wc[it] = Ct32[e];
+        }
+        wbp[it] = Bp32[e];
+    }
+#pragma unroll
+    for (int it = 0; it < IX; ++it) {
+        const int e = tid + it * NTH;
+        if (e >= NWX) continue;
+        wx[it] = xt32[e];
+        wxp[it] = xp32[e];
     }
 
     float4 v0[IT], v1[IT];
@@ -190,17 +236,18 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
         v1[it] = *reinterpret_cast<const float4*>(hs + (2 * k + 1) * P + 4 * q);
     }
 
-    const T* Bt = B + bg * (R * N);
-    const T* Ct = C + bg * (R * N);
-    const T* Bp = carry_B + (int64_t(pr) * nb * G + bg) * (R * N);
-    const T* xt = x + bh * (R * P);
-    const T* xp = carry_x + bh * (R * P);
-    for (int e = tid; e < R * N; e += NTH) {
-        if constexpr (!PRO) {
-            (&sB[0][0])[e] = Io<T>::load(Bt, e);
-            (&sC[0][0])[e] = Io<T>::load(Ct, e);
+#pragma unroll
+    for (int it = 0; it < IB; ++it) {
+        const int e = tid + it * NTH;
+        if (e >= NWB) continue;
+#pragma unroll
+        for (int i = 0; i < WPE; ++i) {
+            if constexpr (!PRO) {
+                (&sB[0][0])[WPE * e + i] = RawIo<T>::val(&wb[it], i);
+                (&sC[0][0])[WPE * e + i] = RawIo<T>::val(&wc[it], i);
+            }
+            (&sBp[0][0])[WPE * e + i] = RawIo<T>::val(&wbp[it], i);
         }
-        (&sBp[0][0])[e] = Io<T>::load(Bp, e);
     }
     if constexpr (PRO) {
 #pragma unroll
@@ -209,19 +256,28 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
             if (e >= 2 * R * GL) continue;  // whole lane groups skip together
             const bool isC = e >= R * GL;
             const int r = (isC ? e - R * GL : e) / GL, n0 = (e % GL) * PE;
-            float ss = 0.f;
+            float v[PE], ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < PE; ++i) ss += pv[it][i] * pv[it][i];
+            for (int i = 0; i < PE; ++i) {
+                v[i] = RawIo<T>::val(pv[it], i);
+                ss += v[i] * v[i];
+            }
             ss = group_sum<GL>(ss);
             const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
             float* dst = isC ? &sC[r][n0] : &sB[r][n0];
 #pragma unroll
-            for (int i = 0; i < PE; ++i) dst[i] = round_io<T>(pv[it][i] * k * pw[it][i] + pb[it][i]);
+            for (int i = 0; i < PE; ++i) dst[i] = round_io<T>(v[i] * k * pw[it][i] + pb[it][i]);
         }
     }
-    for (int e = tid; e < R * P; e += NTH) {
-        (&sx[0][0])[e] = Io<T>::load(xt, e);
-        (&sxp[0][0])[e] = Io<T>::load(xp, e);
+#pragma unroll
+    for (int it = 0; it < IX; ++it) {
+        const int e = tid + it * NTH;
+        if (e >= NWX) continue;
+#pragma unroll
+        for (int i = 0; i < WPE; ++i) {
+            (&sx[0][0])[WPE * e + i] = RawIo<T>::val(&wx[it], i);
+            (&sxp[0][0])[WPE * e + i] = RawIo<T>::val(&wxp[it], i);
+        }
     }
     float d, lm;
     step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
@@ -288,17 +344,26 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
         Io<T>::store(y, bh * (R * P) + e, s + Dh * sx[r][p]);
     }
 
-    // this token becomes the carry of the next step (the carry was read into
-    // LDS before the barrier above)
-    for (int e = tid; e < R * P; e += NTH) carry_x[bh * (R * P) + e] = xt[e];
-    if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += NTH) {
-            T* dst = carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N);
-            if constexpr (PRO)
+    // this token becomes the carry of the next step, from the words it was
+    // staged from (the carry was read before the barrier above)
+#pragma unroll
+    for (int it = 0; it < IX; ++it) {
+        const int e = tid + it * NTH;
+        if (e < NWX) reinterpret_cast<unsigned*>(carry_x + bh * (R * P))[e] = wx[it];
+    }
+    if (h % (H / G) == 0) {
+        T* dst = carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N);
+        if constexpr (PRO) {
+            for (int e = tid; e < R * N; e += NTH)
                 Io<T>::store(dst, e, (&sB[0][0])[e]);  // the normalised row, already in the io dtype
-            else
-                dst[e] = Bt[e];
+        } else {
+#pragma unroll
+            for (int it = 0; it < IB; ++it) {
+                const int e = tid + it * NTH;
+                if (e < NWB) reinterpret_cast<unsigned*>(dst)[e] = wb[it];
+            }
         }
+    }
     if (tid == 0) par[bh] = pr ^ 1u;
 }
 
