@@ -806,7 +806,17 @@ prefill_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ dt
 namespace ws1 {
 
 constexpr int QRP = 64;             // rows per chunk (R = 1)
-constexpr int XS = QRP + 8;         // X^T row stride
+// LDS row strides (bf16) and the X^T column swizzle, chosen with the device's
+// bank-conflict counter (32 banks of 4 bytes): rows of 144 make the 16-byte
+// reads of B~ and C~ rows by 16 lanes conflict-free (136 costs 4 cycles per
+// read) and leave the staging writes and the transposing loads as they were.
+// X^T rows of 80 with the 16-byte column blocks of row p XORed with
+// (p / 8) mod 8 make the staging waves' transposed writes conflict-free (8
+// lanes on one bank at 72 unswizzled) and keep the 8-byte y-operand reads so.
+constexpr int NSB = N + 16;         // B~, C~ row stride
+constexpr int XS = QRP + 16;        // X^T row stride
+// column c of X^T row p is stored at c ^ xsw(p)
+__device__ __forceinline__ int xsw(int p) { return 8 * ((p >> 3) & 7); }
 constexpr int NCW = 4;              // compute waves
 constexpr int NSW = 8;              // staging waves
 constexpr int NST = 64 * NSW;       // staging threads
@@ -897,8 +907,8 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
     for (int m = 0; m < MT; ++m) {
         const int i = (stid >> 4) + TSTEP * m;
         if constexpr (!ROT) {
-            *reinterpret_cast<u32x4*>(sBt + i * NS + 8 * pc) = r.b[m];
-            *reinterpret_cast<u32x4*>(sCt + i * NS + 8 * pc) = r.c[m];
+            *reinterpret_cast<u32x4*>(sBt + i * NSB + 8 * pc) = r.b[m];
+            *reinterpret_cast<u32x4*>(sCt + i * NSB + 8 * pc) = r.c[m];
             continue;
         }
         const float t0 = lane_read(T, tb + TSTEP * m), t1 = lane_read(T, tb + TSTEP * m + 1);
@@ -911,19 +921,20 @@ __device__ __forceinline__ float stage_write(const StageRegs& r, int nq, float A
             t[j] = CS{__builtin_amdgcn_cosf(rv), __builtin_amdgcn_sinf(rv)};
         }
         const u32x4 vb = r.b[m], vc = r.c[m];
-        *reinterpret_cast<u32x4*>(sBt + i * NS + 8 * pc) =
+        *reinterpret_cast<u32x4*>(sBt + i * NSB + 8 * pc) =
             u32x4{rot_pair(vb[0], t[0]), rot_pair(vb[1], t[1]), rot_pair(vb[2], t[2]), rot_pair(vb[3], t[3])};
-        *reinterpret_cast<u32x4*>(sCt + i * NS + 8 * pc) =
+        *reinterpret_cast<u32x4*>(sCt + i * NSB + 8 * pc) =
             u32x4{rot_pair(vc[0], t[0]), rot_pair(vc[1], t[1]), rot_pair(vc[2], t[2]), rot_pair(vc[3], t[3])};
     }
     if (stid < NXT) {
         const int rho0 = 2 * (stid >> 3);
         const int pcx = stid & 7;
+        // the thread's rows 8 pcx .. 8 pcx + 7 share one swizzle
+        uint16_t* xw = sXT + 8 * pcx * XS + (rho0 ^ xsw(8 * pcx));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int p = 8 * pcx + 2 * j;
-            *reinterpret_cast<unsigned*>(sXT + p * XS + rho0) = (r.x0[j] & 0xffffu) | (r.x1[j] << 16);
-            *reinterpret_cast<unsigned*>(sXT + (p + 1) * XS + rho0) = (r.x0[j] >> 16) | (r.x1[j] & 0xffff0000u);
+            *reinterpret_cast<unsigned*>(xw + 2 * j * XS) = (r.x0[j] & 0xffffu) | (r.x1[j] << 16);
+            *reinterpret_cast<unsigned*>(xw + (2 * j + 1) * XS) = (r.x0[j] >> 16) | (r.x1[j] & 0xffff0000u);
         }
     }
     return lane_read(T, 63);  // tokens past the chunk's end carry dt = 0
@@ -945,9 +956,9 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
     const int Pin = GP ? pa.pin : P, Pcol = GP ? pa.pcol : P, p_off = GP ? pa.p_off : 0;
     constexpr int ym = YM;
     float* const ypart = pa.ypart;
-    __shared__ __attribute__((aligned(16))) uint16_t sBt[2][QRP * NS];  // B~ [rho][n]
-    __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NS];  // C~ [rho][n]
-    __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];    // X^T [p][rho]
+    __shared__ __attribute__((aligned(16))) uint16_t sBt[2][QRP * NSB];  // B~ [rho][n]
+    __shared__ __attribute__((aligned(16))) uint16_t sCt[2][QRP * NSB];  // C~ [rho][n]
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[2][P * XS];     // X^T [p][rho], swizzled (xsw)
     __shared__ __attribute__((aligned(16))) uint16_t sGT[2][P * NS];    // g^T [p][n], bf16
     // per token: S2 (log2 decay), gamma, delta_next, e^{S}, state weight, T, tile weight
     __shared__ float sSc[2][7 * 64];
@@ -1069,6 +1080,11 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 
     const int s = wave;
     const int ti = 16 * s + l16;  // token of this lane's column
+    // X^T reads: row 16 q + l16 swizzles by 16 q + 8 (l16 / 8), so column
+    // 16 jt + 4 g4 sits at 16 (jt ^ q) + (4 g4 ^ 8 (l16 / 8)) (disjoint bits),
+    // and column 32 ks + 8 g4 of row 16 pt + l16 at xs[pt & 1] + 32 (ks ^ (pt / 2))
+    const int xy = (4 * g4) ^ (8 * (l16 >> 3));
+    const int xs[2] = {(8 * g4) ^ (8 * (l16 >> 3)), ((8 * g4) ^ (8 * (l16 >> 3))) ^ 16};
 #pragma unroll 1
     for (int64_t c = 0; c < n_chunks; ++c) {
         const int buf = int(c & 1);
@@ -1082,7 +1098,7 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
 
         u32x4 cr[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) cr[ks] = *reinterpret_cast<const u32x4*>(Ct + ti * NS + 32 * ks + 8 * g4);
+        for (int ks = 0; ks < 4; ++ks) cr[ks] = *reinterpret_cast<const u32x4*>(Ct + ti * NSB + 32 * ks + 8 * g4);
         const float S2i = sc[ti];
         floatx4 acc[4];  // the p tiles' accumulation chains interleaved
 #pragma unroll
@@ -1119,13 +1135,14 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             t1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(Bt + (16 * jt + l16) * NS + 32 * ks + 8 * g4);
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(Bt + (16 * jt + l16) * NSB + 32 * ks + 8 * g4);
                 t0 = mfma32(a0, cr[ks], t0);
             }
             if (jt + 1 <= s) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(Bt + (16 * jt + 16 + l16) * NS + 32 * ks + 8 * g4);
+                    const u32x4 a1 =
+                        *reinterpret_cast<const u32x4*>(Bt + (16 * jt + 16 + l16) * NSB + 32 * ks + 8 * g4);
                     t1 = mfma32(a1, cr[ks], t1);
                 }
             }
@@ -1145,16 +1162,16 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
                 const u32x4 pb = {p00, p01, pack2(m1[0], m1[1]), pack2(m1[2], m1[3])};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint16_t* xr = XT + (16 * q + l16) * XS + 16 * jt + 4 * g4;
-                    const u32x2 xa = *reinterpret_cast<const u32x2*>(xr);
-                    const u32x2 xb = *reinterpret_cast<const u32x2*>(xr + 16);
+                    const uint16_t* xr = XT + (16 * q + l16) * XS + xy;
+                    const u32x2 xa = *reinterpret_cast<const u32x2*>(xr + 16 * (jt ^ q));
+                    const u32x2 xb = *reinterpret_cast<const u32x2*>(xr + 16 * ((jt + 1) ^ q));
                     acc[q] = mfma32(u32x4{xa[0], xa[1], xb[0], xb[1]}, pb, acc[q]);
                 }
             } else {
                 const u32x2 pb = {p00, p01};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const u32x2 xa = *reinterpret_cast<const u32x2*>(XT + (16 * q + l16) * XS + 16 * jt + 4 * g4);
+                    const u32x2 xa = *reinterpret_cast<const u32x2*>(XT + (16 * q + l16) * XS + xy + 16 * (jt ^ q));
                     acc[q] = mfma16(xa, pb, acc[q]);
                 }
             }
@@ -1189,15 +1206,16 @@ prefill_ws_r1_kernel(const uint16_t* __restrict__ x, const float* __restrict__ d
             const int rb = 32 * ks + 8 * g4;
             u32x4 xb[4];
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) xb[pt] = *reinterpret_cast<const u32x4*>(XT + (16 * pt + l16) * XS + rb);
+            for (int pt = 0; pt < 4; ++pt)
+                xb[pt] = *reinterpret_cast<const u32x4*>(XT + (16 * pt + l16) * XS + xs[pt & 1] + 32 * (ks ^ (pt >> 1)));
             const floatx4 w0 = *reinterpret_cast<const floatx4*>(sc + 256 + rb);
             const floatx4 w1 = *reinterpret_cast<const floatx4*>(sc + 260 + rb);
 #pragma unroll
             for (int mr = 0; mr < MRW; ++mr) {
                 if (mr >= ntc) continue;
                 const int n0 = 16 * (nt0 + mr);
-                const u32x2 lo = load_tr(Bt + (rb + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
-                const u32x2 hi = load_tr(Bt + (rb + 4 + (l16 >> 2)) * NS + n0 + 4 * (l16 & 3));
+                const u32x2 lo = load_tr(Bt + (rb + (l16 >> 2)) * NSB + n0 + 4 * (l16 & 3));
+                const u32x2 hi = load_tr(Bt + (rb + 4 + (l16 >> 2)) * NSB + n0 + 4 * (l16 & 3));
                 const u32x4 a = {scale2(lo[0], w0[0], w0[1]), scale2(lo[1], w0[2], w0[3]), scale2(hi[0], w1[0], w1[1]),
                                  scale2(hi[1], w1[2], w1[3])};
 #pragma unroll
