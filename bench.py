@@ -36,11 +36,11 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # sources it was taken on (sha256 prefix over the listed files, in order); the
 # summaries with the commands are in profiles/. None until a kernel is profiled.
 MEASURED_TRAFFIC = {
-    "prefill1": ("9fa100e3b9e5d3cc", (2.0 * 39179.7 + 73728.0) * 1024),
-    "prefill2": ("91c0da9e1364c8c6", (2.0 * 150043.3 + 270336.0) * 1024),
-    "long": ("91c0da9e1364c8c6", (2.0 * 725631.9 + 1079920.0) * 1024),
-    "decode1": ("70cc7987573f0ae7", (2.0 * 133329.2 + 264563.5) * 1024),
-    "decode4": ("70cc7987573f0ae7", (2.0 * 137567.1 + 271288.4) * 1024),
+    "prefill1": ("f96f57ce3e0e1d1f", (2.0 * 39182.5 + 73728.0) * 1024),
+    "prefill2": ("91c0da9e1364c8c6", (2.0 * 150047.5 + 270336.0) * 1024),
+    "long": ("91c0da9e1364c8c6", (2.0 * 741808.9 + 1079920.9) * 1024),
+    "decode1": ("70cc7987573f0ae7", (2.0 * 133329.3 + 264563.9) * 1024),
+    "decode4": ("70cc7987573f0ae7", (2.0 * 137566.5 + 271287.5) * 1024),
 }
 
 
