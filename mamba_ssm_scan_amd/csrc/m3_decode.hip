@@ -964,8 +964,9 @@ using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodeProlog
                           bf16_t*, int64_t, int, int);
 
 // The fused step (PRO) at R 2-4 stays on the kernel with separate input sums:
-// with the prologue's registers on top, the merged-input kernel measured slower
-// there (R 4, N 128, b 128: 98.2 against 97.0 us per step).
+// with the prologue's registers on top, the merged-input kernel is no faster
+// there (R 4, N 128, b 128: 97.0 against 97.2 us per step; R 2 92.0 against
+// 92.2).
 template <int N, bool PRO>
 MfmaKern<PRO> mfma_kernel_for(int R) {
     if constexpr (PRO)
