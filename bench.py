@@ -36,11 +36,11 @@ N_COPIES = 4                 # input copies rotated through so the 256 MB MALL c
 # sources it was taken on (sha256 prefix over the listed files, in order); the
 # summaries with the commands are in profiles/. None until a kernel is profiled.
 MEASURED_TRAFFIC = {
-    "prefill1": ("f96f57ce3e0e1d1f", (2.0 * 39182.5 + 73728.0) * 1024),
-    "prefill2": ("91c0da9e1364c8c6", (2.0 * 150047.5 + 270336.0) * 1024),
-    "long": ("91c0da9e1364c8c6", (2.0 * 741808.9 + 1079920.9) * 1024),
-    "decode1": ("70cc7987573f0ae7", (2.0 * 133329.3 + 264563.9) * 1024),
-    "decode4": ("70cc7987573f0ae7", (2.0 * 137566.5 + 271287.5) * 1024),
+    "prefill1": ("f96f57ce3e0e1d1f", (2.0 * 39182.0 + 73728.0) * 1024),
+    "prefill2": ("91c0da9e1364c8c6", (2.0 * 150050.3 + 270336.0) * 1024),
+    "long": ("91c0da9e1364c8c6", (2.0 * 744735.6 + 1079920.3) * 1024),
+    "decode1": ("3c37545b1d60c04a", (2.0 * 133329.4 + 264563.7) * 1024),
+    "decode4": ("3c37545b1d60c04a", (2.0 * 137560.5 + 272836.0) * 1024),
 }
 
 
