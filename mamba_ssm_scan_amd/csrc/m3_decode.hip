@@ -46,7 +46,9 @@ __device__ __forceinline__ void sincos_step(float theta, float* s, float* c) {
 // m3_prologue.hip): softplus with the head's bias on the step, sigmoid on
 // lambda (softplus_f, sigmoid_f of m3_device.h), and per (group, rank) row of B
 // and C an RMS norm with weight and bias, the result rounded to the io dtype as
-// m3_prologue stores it.
+// m3_prologue stores it. The norm's reciprocal square root is the hardware one
+// (v_rsq_f32, about 1 ulp; the row is rounded to bf16 after it): the precise
+// square root and division cost 0.7 us per step at R 4, b 128, H 64.
 template <typename T>
 __device__ __forceinline__ float round_io(float v) {
     if constexpr (std::is_same<T, bf16_t>::value) return bf16_to_f32(f32_to_bf16(v));
@@ -127,7 +129,7 @@ __device__ void qk_norm_rows(float* rb, float* rc, int R, int N, int g, const De
         for (int n = lane; n < N; n += 64) ss += v[n] * v[n];
 #pragma unroll
         for (int sh = 32; sh >= 1; sh >>= 1) ss += __shfl_xor(ss, sh);
-        const float scale = 1.f / sqrtf(ss / float(N) + pro.eps);
+        const float scale = __builtin_amdgcn_rsqf(ss / float(N) + pro.eps);
         const float* w = isC ? pro.C_weight : pro.B_weight;
         const float* bb = isC ? pro.C_bias : pro.B_bias;
         const int64_t o = (int64_t(g) * R + r) * N;
@@ -274,7 +276,7 @@ decode_rows_kernel(float* __restrict__ hstate, T* __restrict__ carry_B, T* __res
                 ss += v[i] * v[i];
             }
             ss = group_sum<GL>(ss);
-            const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
+            const float k = __builtin_amdgcn_rsqf(ss * (1.f / float(N)) + pro.eps);
             float* dst = isC ? &sC[r][n0] : &sB[r][n0];
 #pragma unroll
             for (int i = 0; i < PE; ++i) dst[i] = round_io<T>(v[i] * k * pw[it][i] + pb[it][i]);
@@ -497,7 +499,7 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
         const float v0 = bf_lo(raw), v1 = bf_hi(raw);
         const float ss = group_sum<N / 2>(v0 * v0 + v1 * v1);
         if (r >= R) return 0u;
-        const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
+        const float k = __builtin_amdgcn_rsqf(ss * (1.f / float(N)) + pro.eps);
         return pk_bf16(v0 * k * wv.x + bv.x, v1 * k * wv.y + bv.y);
     };
     constexpr int NBI = (RS * (N / 2) + 255) / 256, NCI = (R * (N / 2) + 255) / 256;
@@ -728,7 +730,7 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
         const float v0 = bf_lo(raw), v1 = bf_hi(raw);
         const float ss = group_sum<K>(v0 * v0 + v1 * v1);
         if (r >= R) return 0u;
-        const float k = 1.f / sqrtf(ss / float(N) + pro.eps);
+        const float k = __builtin_amdgcn_rsqf(ss * (1.f / float(N)) + pro.eps);
         return pk_bf16(v0 * k * wv.x + bv.x, v1 * k * wv.y + bv.y);
     };
 #pragma unroll
@@ -963,17 +965,10 @@ using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodeProlog
                           const float*, const float*, const float*, const bf16_t*, const bf16_t*, const float*,
                           bf16_t*, int64_t, int, int);
 
-// The fused step (PRO) at R 2-4 stays on the kernel with separate input sums:
-// with the prologue's registers on top, the merged-input kernel is no faster
-// there (R 4, N 128, b 128: 97.0 against 97.2 us per step; R 2 92.0 against
-// 92.2).
+// R 2-4 (fused step included) on the merged-input kernel, R 8 on the one with
+// separate input sums.
 template <int N, bool PRO>
 MfmaKern<PRO> mfma_kernel_for(int R) {
-    if constexpr (PRO)
-        return R == 2 ? decode_mfma_kernel<2, N, PRO>
-             : R == 3 ? decode_mfma_kernel<3, N, PRO>
-             : R == 4 ? decode_mfma_kernel<4, N, PRO>
-                      : decode_mfma_kernel<8, N, PRO>;
     return R == 2 ? decode_mfma4_kernel<2, N, PRO>
          : R == 3 ? decode_mfma4_kernel<3, N, PRO>
          : R == 4 ? decode_mfma4_kernel<4, N, PRO>
