@@ -641,7 +641,11 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
 // rows (B_t, C_t, B_prev, x_t, x_prev) and the rotation frequencies are loaded
 // before the state, so their staging runs while the state streams in.
 template <int R, int N, bool PRO>
-__global__ void __launch_bounds__(256)
+// The fused step's instances are held to 4 waves per SIMD (122 VGPRs, no
+// spills): with the prologue's registers they would take 140 and run 3
+// (R 4 96.3 -> 92.7 us per step, R 2 91.3 -> 88.7; the plain instances gain
+// nothing from the bound, and 5 waves spill).
+__global__ void __launch_bounds__(256, PRO ? 4 : 1)
 decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
                     unsigned* __restrict__ par, int rev, DecodePrologue pro,
                     const bf16_t* __restrict__ x, const float* __restrict__ dt,
