@@ -387,10 +387,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ floatx4 mfma_k32(u32x4 a, u32x4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
 __device__ __forceinline__ floatx4 mfma_k16(u32x2 a, u32x2 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c,
                                                      0, 0, 0);
@@ -622,51 +618,66 @@ decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf1
     if (tid == 0) par[bh] = pr ^ 1u;
 }
 
-// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4}: the step in two MFMAs per row
-// tile. One 256-thread workgroup per (b, h); wave w owns state columns
-// 16 w .. 16 w + 15 and all rows; in row tile nt, lane (l16, g4) holds rows
-// 16 nt + 4 g4 .. + 3 of column 16 w + l16 (two whole rotation pairs: the
-// accumulator layout of the MFMA). With the exponential-trapezoidal step
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ floatx16 mfma32_k16(u32x4 a, u32x4 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4}: the step on 32 x 32 MFMA
+// tiles (v_mfma_f32_32x32x16_bf16). With the exponential-trapezoidal step
 //   h' = alpha Rot(h) + M,   M = gamma B^T x + alpha delta Rot(B_prev)^T x_prev,
 // both input terms are one K = 16 contraction over k = (term, rank): the A
 // operand holds gamma B and alpha delta Rot(B_prev) per row n, each as a bf16
-// pair (hi, lo) whose sum is the fp32 value to 2^-16, and the B operand holds
-// x (against the gamma B terms) and x_prev (against the B_prev terms), exact
-// in bf16. The rotation of B_prev's rows is the rotation the previous term
-// takes in the state (it acts on the rows n only). Then
-//   y[r][p] = sum_n C[r][n] h'[n][p]
-// is one K = 32 contraction per tile: k = 8 g4 + j takes the hi (j < 4) and lo
-// (j >= 4) bf16 terms of the lane's own 4 rows, against C of those rows twice,
-// which keeps y at fp32 accuracy with no cross-lane movement. The step's small
-// rows (B_t, C_t, B_prev, x_t, x_prev) and the rotation frequencies are loaded
-// before the state, so their staging runs while the state streams in.
+// pair (hi, lo) whose sum is the fp32 value to 2^-16 (k = 8 g2 + t: t < 4 the
+// hi, t >= 4 the lo terms; g2 = 0 gamma B, g2 = 1 B_prev, four rank slots
+// each), and the B operand holds x (against the gamma B terms) and x_prev
+// (against the B_prev terms), exact in bf16. The rotation of B_prev's rows is
+// the rotation the previous term takes in the state (it acts on the rows n
+// only). Then y[r][p] = sum_n C[r][n] h'[n][p] takes one K = 16 MFMA per
+// (tile, j): k = 8 g2 + t holds the hi (t < 4) and lo (t >= 4) bf16 terms of
+// the lane's rows 8 j + 4 g2 + (t & 3), against C of those rows twice, which
+// keeps y at fp32 accuracy with no cross-lane movement.
+//
+// One 256-thread workgroup per (b, h); wave w owns state columns
+// 32 (w & 1) .. + 31 and the row tiles (32 rows each) of half (w >> 1) of the
+// rows. In row tile nt, lane (l32, g2) holds column 32 (w & 1) + l32 of rows
+// 32 nt + 8 j + 4 g2 + e (j, e = 0..3): the accumulator layout of the 32 x 32
+// MFMA, with two whole rotation pairs per (j, lane). A state load or store of
+// one wave covers two whole 128-byte row segments (32 consecutive floats of
+// two rows); on 16 x 16 tiles (lane = 4 rows of one column) it moved 64-byte
+// halves of four rows, and the step took 89.1 against 85.7 us (R 4, b 128,
+// H 64) and 185.3 against 170.8 us at b 256. The two waves of a column half
+// add their partial y through LDS. The step's small rows (B_t, C_t, B_prev,
+// x_t, x_prev) and the rotation frequencies are loaded before the state, so
+// their staging runs while the state streams in.
 template <int R, int N, bool PRO>
-// The fused step's instances are held to 4 waves per SIMD (122 VGPRs, no
-// spills): with the prologue's registers they would take 140 and run 3
-// (R 4 96.3 -> 92.7 us per step, R 2 91.3 -> 88.7; the plain instances gain
-// nothing from the bound, and 5 waves spill).
-__global__ void __launch_bounds__(256, PRO ? 4 : 1)
-decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
-                    unsigned* __restrict__ par, int rev, DecodePrologue pro,
-                    const bf16_t* __restrict__ x, const float* __restrict__ dt,
-                    const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
-                    const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
-                    bf16_t* __restrict__ y, int64_t nb, int H, int G) {
+// Held to 4 waves per SIMD (no spills; without the bound the plain instances
+// take 156 registers and run 3: 88.0 against 85.7 us per step at R 4, b 128;
+// at 5 the plain ones gain nothing and the fused ones lose 1.2 us).
+__global__ void __launch_bounds__(256, 4)
+decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
+                     unsigned* __restrict__ par, int rev, DecodePrologue pro,
+                     const bf16_t* __restrict__ x, const float* __restrict__ dt,
+                     const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
+                     const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
+                     bf16_t* __restrict__ y, int64_t nb, int H, int G) {
     static_assert(R >= 2 && R <= 4, "ranks 2-4 (R 3 with a zero rank slot)");
-    constexpr int P = 64, K = N / 2, CS_ = N + 4, NT = N / 16;
-    constexpr int NBI = (4 * K + 255) / 256;  // (rank slot, pair) items of B per thread
-    constexpr int NCI = (R * K + 255) / 256;  // (rank, pair) items of C per thread
-    constexpr int AS = 20;                    // sA row stride (bf16): 16 used, padded against bank conflicts
+    constexpr int NTH = 256, P = 64, K = N / 2, CS_ = N + 8, NT = N / 32, NTW = NT / 2;
+    constexpr int NBI = (4 * K + NTH - 1) / NTH;  // (rank slot, pair) items of B per thread
+    constexpr int NCI = (R * K + NTH - 1) / NTH;  // (rank, pair) items of C per thread
+    constexpr int AS = 24;                        // sA row stride (bf16): 16 used, 16-byte aligned rows
     // per row n, k = 0..15: (gamma B)_hi, (gamma B)_lo, (alpha delta Rot B_prev)_hi, _lo; four rank slots each
     __shared__ __attribute__((aligned(16))) uint16_t sA[N][AS];
     __shared__ __attribute__((aligned(16))) uint16_t sXt[P][4];   // x^T, zero past R
     __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][4];  // x_prev^T
     __shared__ __attribute__((aligned(16))) uint16_t sC[R][CS_];  // C rows (padded)
     __shared__ __attribute__((aligned(16))) float sCS[K][2];      // alpha * (cos, sin) of pair k
+    __shared__ float sY[2][4][32];  // partial y of the second row half, per column half
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, g4 = lane >> 4;
+    const int l32 = lane & 31, g2 = lane >> 5;
     const int64_t bh = rev ? int64_t(gridDim.x) - 1 - blockIdx.x : int64_t(blockIdx.x);
     const int64_t b = bh / H;
     const int h = int(bh % H);
@@ -674,7 +685,7 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     const int64_t bg = b * G + gi;
     const unsigned pr = par[bh] & 1u;  // slot of B_prev
     float* hs = hstate + bh * (N * P);
-    const int p = 16 * w + l16;
+    const int p = 32 * (w & 1) + l32;
 
     // The small rows first (raw with the prologue, with the norm weights).
     // Thread item e of B: rank slot r = e / K, pair j = e % K (rows 2 j, 2 j + 1).
@@ -693,7 +704,7 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     float2 bw[PRO ? NBI : 1], bb2[PRO ? NBI : 1], cw[PRO ? NCI : 1], cb2[PRO ? NCI : 1];
 #pragma unroll
     for (int it = 0; it < NBI; ++it) {
-        const int e = tid + 256 * it, r = e / K, j = e % K;
+        const int e = tid + NTH * it, r = e / K, j = e % K;
         const bool in = e < 4 * K && r < R;
         rb[it] = in ? Bt32[r * K + j] : 0u;
         rbp[it] = in ? Bp32[r * K + j] : 0u;
@@ -705,7 +716,7 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     }
 #pragma unroll
     for (int it = 0; it < NCI; ++it) {
-        const int e = tid + 256 * it;
+        const int e = tid + NTH * it;
         const bool in = e < R * K;
         rc[it] = in ? Ct32[e] : 0u;
         if constexpr (PRO) {
@@ -717,11 +728,12 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     const bool xin = tid < 4 * (P / 2) && tid / (P / 2) < R;
     const unsigned rx = xin ? load_stream(&xt32[tid]) : 0u, rxp = xin ? xp32[tid] : 0u;
 
-    float st[NT][4];
+    const int nt0 = (w >> 1) * NTW;  // the wave's first row tile
+    float st[NTW][16];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[nt][e] = hs[(16 * nt + 4 * g4 + e) * P + p];
+        for (int v = 0; v < 16; ++v) st[i][v] = hs[(32 * (nt0 + i) + 8 * (v >> 2) + 4 * g2 + (v & 3)) * P + p];
 
     float d, lm;
     step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
@@ -729,7 +741,7 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     const float gamma = lm * d, ad = alpha * (1.f - lm) * d;
 
     // the normalised pair from a raw pair, its weights and biases; the K lanes
-    // holding one rank row (a whole wave at N 128) reduce its sum of squares
+    // holding one rank row (a whole wave at N 128, half a wave at N 64) reduce its sum of squares
     auto norm_pair = [&](unsigned raw, int r, float2 wv, float2 bv) -> unsigned {
         const float v0 = bf_lo(raw), v1 = bf_hi(raw);
         const float ss = group_sum<K>(v0 * v0 + v1 * v1);
@@ -739,8 +751,8 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     };
 #pragma unroll
     for (int it = 0; it < NBI; ++it) {
-        const int e = tid + 256 * it;
-        if (e >= 4 * K) break;  // whole waves
+        const int e = tid + NTH * it;
+        if (e >= 4 * K) break;  // whole lane groups
         const int r = e / K, j = e % K;
         if constexpr (PRO) rb[it] = norm_pair(rb[it], r, bw[it], bb2[it]);  // kept for the carry
         float sn, cs;
@@ -772,48 +784,62 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
     }
 #pragma unroll
     for (int it = 0; it < NCI; ++it) {
-        const int e = tid + 256 * it;
-        if (e >= R * K) break;  // whole waves
+        const int e = tid + NTH * it;
+        if (e >= R * K) break;  // whole lane groups
         unsigned cv = rc[it];
         if constexpr (PRO) cv = norm_pair(cv, e / K, cw[it], cb2[it]);
         reinterpret_cast<unsigned*>(&sC[e / K][0])[e % K] = cv;
     }
     __syncthreads();
 
-    // B operand of the input MFMA: k = 4 g4 .. 4 g4 + 3 -> ranks 0..3 of x (g4 0, 1) or x_prev (g4 2, 3)
-    const u32x2 bx = *reinterpret_cast<const u32x2*>(g4 < 2 ? &sXt[p][0] : &sXpt[p][0]);
-    const int rcl = l16 < R ? l16 : 0;
+    // B operand of the input MFMA: k = 8 g2 .. 8 g2 + 7 -> ranks 0..3 of x twice (g2 0) or of x_prev twice (g2 1)
+    const u32x2 xr = *reinterpret_cast<const u32x2*>(g2 == 0 ? &sXt[p][0] : &sXpt[p][0]);
+    const u32x4 bx = {xr[0], xr[1], xr[0], xr[1]};
+    const int rcl = l32 < R ? l32 : 0;
     const u32x2 zero = {0u, 0u};
-    floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
+    floatx16 yacc;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int n0 = 16 * nt;
-        const u32x2 a = *reinterpret_cast<const u32x2*>(&sA[n0 + l16][4 * g4]);
-        const floatx4 M = mfma_k16(a, bx, floatx4{0.f, 0.f, 0.f, 0.f});
-        // alpha (cos, sin) of pairs 8 nt + 2 g4 (rows e = 0, 1) and 8 nt + 2 g4 + 1 (rows e = 2, 3)
-        const floatx4 cs = *reinterpret_cast<const floatx4*>(&sCS[8 * nt + 2 * g4][0]);
-        float nv[4];
+    for (int v = 0; v < 16; ++v) yacc[v] = 0.f;
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp) {
-            const float c = cs[2 * hp], sn = cs[2 * hp + 1];
-            const float h0 = st[nt][2 * hp], h1 = st[nt][2 * hp + 1];
-            nv[2 * hp] = (c * h0 - sn * h1) + M[2 * hp];
-            nv[2 * hp + 1] = (sn * h0 + c * h1) + M[2 * hp + 1];
+    for (int i = 0; i < NTW; ++i) {
+        const int n0 = 32 * (nt0 + i);
+        floatx16 M;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) M[v] = 0.f;
+        M = mfma32_k16(*reinterpret_cast<const u32x4*>(&sA[n0 + l32][8 * g2]), bx, M);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r0 = n0 + 8 * j + 4 * g2;  // the lane's rows r0 .. r0 + 3: pairs r0 / 2, r0 / 2 + 1
+            // alpha (cos, sin) of those two pairs
+            const floatx4 cs = *reinterpret_cast<const floatx4*>(&sCS[r0 >> 1][0]);
+            float nv[4];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                const float c = cs[2 * hp], sn = cs[2 * hp + 1];
+                const float h0 = st[i][4 * j + 2 * hp], h1 = st[i][4 * j + 2 * hp + 1];
+                nv[2 * hp] = (c * h0 - sn * h1) + M[4 * j + 2 * hp];
+                nv[2 * hp + 1] = (sn * h0 + c * h1) + M[4 * j + 2 * hp + 1];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hs[(r0 + e) * P + p] = nv[e];
+            const unsigned h01 = pk_bf16(nv[0], nv[1]), h23 = pk_bf16(nv[2], nv[3]);
+            const u32x4 hl = {h01, h23, pk_bf16(nv[0] - bf_lo(h01), nv[1] - bf_hi(h01)),
+                              pk_bf16(nv[2] - bf_lo(h23), nv[3] - bf_hi(h23))};
+            const u32x2 cv = l32 < R ? *reinterpret_cast<const u32x2*>(&sC[rcl][r0]) : zero;
+            yacc = mfma32_k16(u32x4{cv[0], cv[1], cv[0], cv[1]}, hl, yacc);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hs[(n0 + 4 * g4 + e) * P + p] = nv[e];
-        const unsigned h01 = pk_bf16(nv[0], nv[1]), h23 = pk_bf16(nv[2], nv[3]);
-        const u32x4 hl = {h01, h23, pk_bf16(nv[0] - bf_lo(h01), nv[1] - bf_hi(h01)),
-                          pk_bf16(nv[2] - bf_lo(h23), nv[3] - bf_hi(h23))};
-        const u32x2 cv = l16 < R ? *reinterpret_cast<const u32x2*>(&sC[rcl][n0 + 4 * g4]) : zero;
-        yacc = mfma_k32(u32x4{cv[0], cv[1], cv[0], cv[1]}, hl, yacc);
     }
-    if (g4 == 0) {  // lane (l16, 0) holds y[r = e][p]
+    // lane (l32, 0) holds the partial y[r = v][p] in yacc[v], v < 4
+    if (w >= 2 && g2 == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sY[w & 1][r][l32] = yacc[r];
+    __syncthreads();
+    if (w < 2 && g2 == 0) {
         const float Dh = D[h];
 #pragma unroll
-        for (int e = 0; e < R; ++e) {
-            const float xv = __uint_as_float(unsigned(sXt[p][e]) << 16);
-            store_stream(y, bh * (R * P) + e * P + p, yacc[e] + Dh * xv);
+        for (int r = 0; r < R; ++r) {
+            const float xv = __uint_as_float(unsigned(sXt[p][r]) << 16);
+            store_stream(y, bh * (R * P) + r * P + p, (yacc[r] + sY[w][r][l32]) + Dh * xv);
         }
     }
 
@@ -824,7 +850,7 @@ decode_mfma4_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf
         unsigned* cb32 = reinterpret_cast<unsigned*>(carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N));
 #pragma unroll
         for (int it = 0; it < NBI; ++it) {  // the normalised row with the prologue
-            const int e = tid + 256 * it;
+            const int e = tid + NTH * it;
             if (e < R * K) cb32[e] = rb[it];
         }
     }
@@ -973,9 +999,9 @@ using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodeProlog
 // separate input sums.
 template <int N, bool PRO>
 MfmaKern<PRO> mfma_kernel_for(int R) {
-    return R == 2 ? decode_mfma4_kernel<2, N, PRO>
-         : R == 3 ? decode_mfma4_kernel<3, N, PRO>
-         : R == 4 ? decode_mfma4_kernel<4, N, PRO>
+    return R == 2 ? decode_mfma32_kernel<2, N, PRO>
+         : R == 3 ? decode_mfma32_kernel<3, N, PRO>
+         : R == 4 ? decode_mfma32_kernel<4, N, PRO>
                   : decode_mfma_kernel<8, N, PRO>;
 }
 

@@ -28,7 +28,7 @@ DYNAMIC = {"prefill_generic_kernel": max(3 * 4096 * 4, 128 * 1024), "decode_gene
 
 # instances on the workloads' paths: no spills allowed
 NO_SCRATCH = [r"prefill_ws_r1_kernelILb[01]ELb0ELi0ELb0E", r"prefill_ws4_kernelILi[248]ELb[01]ELb[01]ELb0E",
-              r"decode_rows_kernel", r"decode_mfma4?_kernel", r"prologue_kernel"]
+              r"decode_rows_kernel", r"decode_mfma(32)?_kernel", r"prologue_kernel"]
 
 
 def _code_objects():
