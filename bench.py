@@ -696,7 +696,7 @@ def main():
     }
     if not args.quick:
         # the batch-128 decode loop (1024 steps, 20 timed loops) at R 1 and R 4: HBM-bound
-        kern = {1: "decode_rows_kernel", 4: "decode_mfma_kernel"}
+        kern = {1: "decode_rows_kernel", 4: "decode_mfma32_kernel"}
         out["decode"] = {}
         for R in (1, 4):
             d = bench_decode(R, 1024, 20, log)
