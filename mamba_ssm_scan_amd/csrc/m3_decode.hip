@@ -387,10 +387,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ floatx4 mfma_k16(u32x2 a, u32x2 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c,
-                                                     0, 0, 0);
-}
 // two floats -> packed bf16 (round to nearest even)
 __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
     bf16x2 v;
@@ -401,238 +397,23 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// bf16 I/O, N in {64, 128}, P = 64, R = 8 (and R 2-4 of the fused step): the rank-R contractions on MFMA
-// (v_mfma_f32_16x16x16_bf16). One 256-thread workgroup per (b, h); wave w owns
-// state columns 16 w .. 16 w + 15 and all 128 rows. In row tile nt, lane
-// (l16, g4) holds rows 16 nt + 4 g4 .. + 3 of column 16 w + l16: two whole
-// rotation pairs, and exactly the accumulator layout of the MFMA, so
-//   U[n][p]  = sum_r B[r][n] x[r][p]      (A: B^T, rows n, k = r; B: x, k = r,
-//   Up[n][p] = the same for the previous token   cols p; k = R..15 are zero)
-// land in the lanes that own h[n][p], and
-//   y[r][p] += sum_n C[r][n] h'[n][p]      (A: C, rows r (zero past R), k = n;
-//                                           B: h', k = n, cols p)
-// takes the lane's 4 new state values as its B operand. h' goes in as two bf16
-// terms (hi + lo), which keeps y at fp32 accuracy; the products of bf16 inputs
-// in U and Up are exact. No cross-lane reduction is left.
-template <int R, int N, bool PRO>
-__global__ void __launch_bounds__(256)
-decode_mfma_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, bf16_t* __restrict__ carry_x,
-                   unsigned* __restrict__ par, int rev, DecodePrologue pro,
-                   const bf16_t* __restrict__ x, const float* __restrict__ dt,
-                   const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
-                   const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
-                   bf16_t* __restrict__ y, int64_t nb, int H, int G) {
-    constexpr int P = 64, K = N / 2, CS_ = N + 4, NT = N / 16;  // NT row tiles
-    // rank slots: 4, or 8 at R above 4 (k = 4 g4 + 0..3 of the K = 16 MFMA, lanes g4 < RS / 4)
-    constexpr int RS = R <= 4 ? 4 : 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sBt[N][RS];   // B^T: ranks contiguous, zero past R
-    __shared__ __attribute__((aligned(16))) uint16_t sBpt[N][RS];  // B_prev^T
-    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][RS];   // x^T
-    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][RS];  // x_prev^T
-    __shared__ __attribute__((aligned(16))) uint16_t sC[R][CS_];  // C rows (padded: no bank conflicts)
-    __shared__ __attribute__((aligned(16))) float sCS[K][2];      // alpha * (cos, sin) of pair k
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int64_t bh = rev ? int64_t(gridDim.x) - 1 - blockIdx.x : int64_t(blockIdx.x);
-    const int64_t b = bh / H;
-    const int h = int(bh % H);
-    const int64_t bg = b * G + h / (H / G);
-    const unsigned pr = par[bh] & 1u;  // slot of B_prev
-    float* hs = hstate + bh * (N * P);
-    const int p = 16 * w + l16;
-    const int gi = h / (H / G);
-
-    // With the prologue, a rank row's N / 2 pairs are staged by N / 2
-    // consecutive lanes (a whole wave at N 128): they reduce its sum of squares
-    // among themselves and stage the normalised pairs, with no pass of their
-    // own. The raw pairs and their weights are loaded first, ahead of the state.
-    constexpr int BIT = PRO ? (RS * (N / 2) + 255) / 256 : 0;  // B pairs per thread
-    constexpr int CIT = PRO ? (R * (N / 2) + 255) / 256 : 0;   // C pairs per thread
-    unsigned braw[BIT > 0 ? BIT : 1], craw[CIT > 0 ? CIT : 1];
-    float2 bw[BIT > 0 ? BIT : 1], bb2[BIT > 0 ? BIT : 1], cw[CIT > 0 ? CIT : 1], cb2[CIT > 0 ? CIT : 1];
-    if constexpr (PRO) {
-        const unsigned* B32 = reinterpret_cast<const unsigned*>(B + bg * (R * N));
-        const unsigned* C32 = reinterpret_cast<const unsigned*>(C + bg * (R * N));
-        auto wpair = [&](const float* v, int r, int j, float dflt) {
-            if (!v) return float2{dflt, dflt};
-            const int64_t o = (int64_t(gi) * R + r) * N + 2 * j;
-            return float2{v[o], v[o + 1]};
-        };
-#pragma unroll
-        for (int it = 0; it < BIT; ++it) {
-            const int e = tid + 256 * it, r = e / (N / 2), j = e % (N / 2);
-            const bool in = e < RS * (N / 2) && r < R;
-            braw[it] = in ? B32[r * (N / 2) + j] : 0u;
-            bw[it] = in ? wpair(pro.B_weight, r, j, 1.f) : float2{1.f, 1.f};
-            bb2[it] = in ? wpair(pro.B_bias, r, j, 0.f) : float2{0.f, 0.f};
-        }
-#pragma unroll
-        for (int it = 0; it < CIT; ++it) {
-            const int e = tid + 256 * it, r = e / (N / 2), j = e % (N / 2);
-            const bool in = e < R * (N / 2);
-            craw[it] = in ? C32[e] : 0u;
-            cw[it] = in ? wpair(pro.C_weight, r, j, 1.f) : float2{1.f, 1.f};
-            cb2[it] = in ? wpair(pro.C_bias, r, j, 0.f) : float2{0.f, 0.f};
-        }
-    }
-
-    float st[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st[nt][e] = hs[(16 * nt + 4 * g4 + e) * P + p];
-
-    const uint16_t* Bt = reinterpret_cast<const uint16_t*>(B) + bg * (R * N);
-    const uint16_t* Ct = reinterpret_cast<const uint16_t*>(C) + bg * (R * N);
-    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(carry_B) + (int64_t(pr) * nb * G + bg) * (R * N);
-    const uint16_t* xt = reinterpret_cast<const uint16_t*>(x) + bh * (R * P);
-    const uint16_t* xp = reinterpret_cast<const uint16_t*>(carry_x) + bh * (R * P);
-    // the normalised pair from a raw pair, its weights and biases; the lane group
-    // holding one rank row shares the same r
-    auto norm_pair = [&](unsigned raw, int r, float2 wv, float2 bv) -> unsigned {
-        const float v0 = bf_lo(raw), v1 = bf_hi(raw);
-        const float ss = group_sum<N / 2>(v0 * v0 + v1 * v1);
-        if (r >= R) return 0u;
-        const float k = __builtin_amdgcn_rsqf(ss * (1.f / float(N)) + pro.eps);
-        return pk_bf16(v0 * k * wv.x + bv.x, v1 * k * wv.y + bv.y);
-    };
-    constexpr int NBI = (RS * (N / 2) + 255) / 256, NCI = (R * (N / 2) + 255) / 256;
-#pragma unroll
-    for (int it = 0; it < NBI; ++it) {  // rank r, pair of rows (2 j, 2 j + 1)
-        const int e = tid + 256 * it;
-        if (e >= RS * (N / 2)) break;
-        const int r = e / (N / 2), j = e % (N / 2);
-        unsigned vb;
-        if constexpr (PRO)
-            vb = norm_pair(braw[it], r, bw[it], bb2[it]);
-        else
-            vb = r < R ? reinterpret_cast<const unsigned*>(Bt + r * N)[j] : 0u;
-        const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(Bp + r * N)[j] : 0u;
-        sBt[2 * j][r] = uint16_t(vb);
-        sBt[2 * j + 1][r] = uint16_t(vb >> 16);
-        sBpt[2 * j][r] = uint16_t(vp);
-        sBpt[2 * j + 1][r] = uint16_t(vp >> 16);
-    }
-    for (int e = tid; e < RS * (P / 2); e += 256) {  // rank r, pair of columns: one 32-bit load
-        const int r = e / (P / 2), j = e % (P / 2);
-        const unsigned vx = r < R ? reinterpret_cast<const unsigned*>(xt + r * P)[j] : 0u;
-        const unsigned vp = r < R ? reinterpret_cast<const unsigned*>(xp + r * P)[j] : 0u;
-        sXt[2 * j][r] = uint16_t(vx);
-        sXt[2 * j + 1][r] = uint16_t(vx >> 16);
-        sXpt[2 * j][r] = uint16_t(vp);
-        sXpt[2 * j + 1][r] = uint16_t(vp >> 16);
-    }
-#pragma unroll
-    for (int it = 0; it < NCI; ++it) {
-        const int e = tid + 256 * it;
-        if (e >= R * (N / 2)) break;
-        unsigned cv;
-        if constexpr (PRO)
-            cv = norm_pair(craw[it], e / (N / 2), cw[it], cb2[it]);
-        else
-            cv = reinterpret_cast<const unsigned*>(Ct)[e];
-        reinterpret_cast<unsigned*>(&sC[e / (N / 2)][0])[e % (N / 2)] = cv;
-    }
-    float d, lm;
-    step_scalars<PRO>(dt, lam, pro, bh, h, &d, &lm);
-    const float alpha = expf(d * A[h]);
-    const float gamma = lm * d, delta = (1.f - lm) * d;
-    if (tid < K) {
-        float sn, cs;
-        sincos_step(d * om_at(omega, int64_t(h) * K + tid), &sn, &cs);
-        sCS[tid][0] = alpha * cs;
-        sCS[tid][1] = alpha * sn;
-    }
-    __syncthreads();
-
-    const u32x2 zero = {0u, 0u};
-    const bool kin = g4 < RS / 4;  // this lane's k group holds ranks 4 g4 .. 4 g4 + 3
-    const int ko = RS == 4 ? 0 : 4 * g4;
-    const u32x2 xo = kin ? *reinterpret_cast<const u32x2*>(&sXt[p][ko]) : zero;
-    const u32x2 xpo = kin ? *reinterpret_cast<const u32x2*>(&sXpt[p][ko]) : zero;
-    const int rc = l16 < R ? l16 : 0;
-    floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int nt = 0; nt < NT; ++nt) {
-        const int n0 = 16 * nt;
-        const u32x2 ab = *reinterpret_cast<const u32x2*>(&sBt[n0 + l16][ko]);
-        const u32x2 abp = *reinterpret_cast<const u32x2*>(&sBpt[n0 + l16][ko]);
-        const floatx4 U = mfma_k16(kin ? ab : zero, xo, floatx4{0.f, 0.f, 0.f, 0.f});
-        const floatx4 Up = mfma_k16(kin ? abp : zero, xpo, floatx4{0.f, 0.f, 0.f, 0.f});
-        // pairs 8 nt + 2 g4 (rows e = 0, 1) and 8 nt + 2 g4 + 1 (rows e = 2, 3)
-        const floatx4 cs = *reinterpret_cast<const floatx4*>(&sCS[8 * nt + 2 * g4][0]);
-        float nv[4];
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp) {
-            const float c = cs[2 * hp], sn = cs[2 * hp + 1];
-            const float g0 = st[nt][2 * hp] + delta * Up[2 * hp];
-            const float g1 = st[nt][2 * hp + 1] + delta * Up[2 * hp + 1];
-            nv[2 * hp] = (c * g0 - sn * g1) + gamma * U[2 * hp];
-            nv[2 * hp + 1] = (sn * g0 + c * g1) + gamma * U[2 * hp + 1];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hs[(n0 + 4 * g4 + e) * P + p] = nv[e];
-        const unsigned h01 = pk_bf16(nv[0], nv[1]), h23 = pk_bf16(nv[2], nv[3]);
-        const u32x2 hi = {h01, h23};
-        const u32x2 lo = {pk_bf16(nv[0] - bf_lo(h01), nv[1] - bf_hi(h01)),
-                          pk_bf16(nv[2] - bf_lo(h23), nv[3] - bf_hi(h23))};
-        const u32x2 cv = *reinterpret_cast<const u32x2*>(&sC[rc][n0 + 4 * g4]);
-        const u32x2 ac = l16 < R ? cv : zero;
-        yacc = mfma_k16(ac, hi, yacc);
-        yacc = mfma_k16(ac, lo, yacc);
-    }
-    // yacc lane (g4 = 0) holds y[r = e][p]
-    if constexpr (RS == 4) {  // yacc lane (g4 = 0) holds y[r = e][p]
-        if (g4 == 0) {
-            const float Dh = D[h];
-#pragma unroll
-            for (int e = 0; e < R; ++e) {
-                const float xv = __uint_as_float(unsigned(sXt[p][e]) << 16);
-                Io<bf16_t>::store(y, bh * (R * P) + e * P + p, yacc[e] + Dh * xv);
-            }
-        }
-    } else if (4 * g4 < R) {  // lane (l16, g4) holds y[r = 4 g4 + e][p]
-        const float Dh = D[h];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            if (r >= R) continue;
-            const float xv = __uint_as_float(unsigned(sXt[p][r]) << 16);
-            Io<bf16_t>::store(y, bh * (R * P) + r * P + p, yacc[e] + Dh * xv);
-        }
-    }
-
-    // this token becomes the carry of the next step (the carry was read into
-    // LDS before the barrier above)
-    for (int e = tid; e < R * P; e += 256) carry_x[bh * (R * P) + e] = x[bh * (R * P) + e];
-    if (h % (H / G) == 0)
-        for (int e = tid; e < R * N; e += 256) {
-            bf16_t* dst = carry_B + (int64_t(pr ^ 1u) * nb * G + bg) * (R * N);
-            if constexpr (PRO)
-                dst[e].bits = sBt[e % N][e / N];  // the normalised row, staged transposed
-            else
-                dst[e] = B[bg * (R * N) + e];
-        }
-    if (tid == 0) par[bh] = pr ^ 1u;
-}
-
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ floatx16 mfma32_k16(u32x4 a, u32x4 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
 }
 
-// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4}: the step on 32 x 32 MFMA
+// bf16 I/O, N in {64, 128}, P = 64, R in {2, 3, 4, 8}: the step on 32 x 32 MFMA
 // tiles (v_mfma_f32_32x32x16_bf16). With the exponential-trapezoidal step
 //   h' = alpha Rot(h) + M,   M = gamma B^T x + alpha delta Rot(B_prev)^T x_prev,
-// both input terms are one K = 16 contraction over k = (term, rank): the A
-// operand holds gamma B and alpha delta Rot(B_prev) per row n, each as a bf16
-// pair (hi, lo) whose sum is the fp32 value to 2^-16 (k = 8 g2 + t: t < 4 the
-// hi, t >= 4 the lo terms; g2 = 0 gamma B, g2 = 1 B_prev, four rank slots
-// each), and the B operand holds x (against the gamma B terms) and x_prev
-// (against the B_prev terms), exact in bf16. The rotation of B_prev's rows is
+// both input terms are one K = 16 contraction over k = (term, rank) at R <= 4
+// and two at R 8: the A operand holds gamma B and alpha delta Rot(B_prev) per
+// row n, each as a bf16 pair (hi, lo) whose sum is the fp32 value to 2^-16
+// (R <= 4, four rank slots: k = 8 g2 + t, t < 4 the hi, t >= 4 the lo terms,
+// g2 = 0 gamma B, g2 = 1 B_prev; R 8: the first MFMA takes the hi (g2 = 0) and
+// lo (g2 = 1) terms of gamma B over the 8 ranks, the second those of B_prev),
+// and the B operand holds x (against the gamma B terms) and x_prev (against
+// the B_prev terms), exact in bf16. The rotation of B_prev's rows is
 // the rotation the previous term takes in the state (it acts on the rows n
 // only). Then y[r][p] = sum_n C[r][n] h'[n][p] takes one K = 16 MFMA per
 // (tile, j): k = 8 g2 + t holds the hi (t < 4) and lo (t >= 4) bf16 terms of
@@ -647,7 +428,9 @@ __device__ __forceinline__ floatx16 mfma32_k16(u32x4 a, u32x4 b, floatx16 c) {
 // one wave covers two whole 128-byte row segments (32 consecutive floats of
 // two rows); on 16 x 16 tiles (lane = 4 rows of one column) it moved 64-byte
 // halves of four rows, and the step took 89.1 against 85.7 us (R 4, b 128,
-// H 64) and 185.3 against 170.8 us at b 256. The two waves of a column half
+// H 64) and 185.3 against 170.8 us at b 256; R 8, where an earlier kernel
+// summed the two input terms in separate K = 16 MFMAs on 16 x 16 tiles:
+// 103.2 against 92.9 us at b 128. The two waves of a column half
 // add their partial y through LDS. The step's small rows (B_t, C_t, B_prev,
 // x_t, x_prev) and the rotation frequencies are loaded before the state, so
 // their staging runs while the state streams in.
@@ -662,18 +445,19 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
                      const float* __restrict__ A, const float* __restrict__ omega, const float* __restrict__ lam,
                      const bf16_t* __restrict__ B, const bf16_t* __restrict__ C, const float* __restrict__ D,
                      bf16_t* __restrict__ y, int64_t nb, int H, int G) {
-    static_assert(R >= 2 && R <= 4, "ranks 2-4 (R 3 with a zero rank slot)");
+    static_assert((R >= 2 && R <= 4) || R == 8, "ranks 2-4 (R 3 with a zero rank slot) and 8");
     constexpr int NTH = 256, P = 64, K = N / 2, CS_ = N + 8, NT = N / 32, NTW = NT / 2;
-    constexpr int NBI = (4 * K + NTH - 1) / NTH;  // (rank slot, pair) items of B per thread
+    constexpr int RS = R <= 4 ? 4 : 8;           // rank slots
+    constexpr int NBI = (RS * K + NTH - 1) / NTH;  // (rank slot, pair) items of B per thread
     constexpr int NCI = (R * K + NTH - 1) / NTH;  // (rank, pair) items of C per thread
-    constexpr int AS = 24;                        // sA row stride (bf16): 16 used, 16-byte aligned rows
-    // per row n, k = 0..15: (gamma B)_hi, (gamma B)_lo, (alpha delta Rot B_prev)_hi, _lo; four rank slots each
+    constexpr int AS = 4 * RS + 8;                // sA row stride (bf16): 4 RS used, 16-byte aligned rows
+    // per row n, k = 0 .. 4 RS - 1: (gamma B)_hi, (gamma B)_lo, (alpha delta Rot B_prev)_hi, _lo; RS rank slots each
     __shared__ __attribute__((aligned(16))) uint16_t sA[N][AS];
-    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][4];   // x^T, zero past R
-    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][4];  // x_prev^T
+    __shared__ __attribute__((aligned(16))) uint16_t sXt[P][RS];   // x^T, zero past R
+    __shared__ __attribute__((aligned(16))) uint16_t sXpt[P][RS];  // x_prev^T
     __shared__ __attribute__((aligned(16))) uint16_t sC[R][CS_];  // C rows (padded)
     __shared__ __attribute__((aligned(16))) float sCS[K][2];      // alpha * (cos, sin) of pair k
-    __shared__ float sY[2][4][32];  // partial y of the second row half, per column half
+    __shared__ float sY[2][RS][32];  // partial y of the second row half, per column half
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -705,10 +489,10 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
 #pragma unroll
     for (int it = 0; it < NBI; ++it) {
         const int e = tid + NTH * it, r = e / K, j = e % K;
-        const bool in = e < 4 * K && r < R;
+        const bool in = e < RS * K && r < R;
         rb[it] = in ? Bt32[r * K + j] : 0u;
         rbp[it] = in ? Bp32[r * K + j] : 0u;
-        rom[it] = e < 4 * K ? om_at(omega, int64_t(h) * K + j) : 0.f;
+        rom[it] = e < RS * K ? om_at(omega, int64_t(h) * K + j) : 0.f;
         if constexpr (PRO) {
             bw[it] = in ? wpair(pro.B_weight, r, j, 1.f) : float2{1.f, 1.f};
             bb2[it] = in ? wpair(pro.B_bias, r, j, 0.f) : float2{0.f, 0.f};
@@ -724,8 +508,8 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
             cb2[it] = in ? wpair(pro.C_bias, e / K, e % K, 0.f) : float2{0.f, 0.f};
         }
     }
-    // x_t, x_prev: thread tid < 4 P / 2 takes rank slot tid / (P / 2), column pair tid % (P / 2)
-    const bool xin = tid < 4 * (P / 2) && tid / (P / 2) < R;
+    // x_t, x_prev: thread tid < RS P / 2 takes rank slot tid / (P / 2), column pair tid % (P / 2)
+    const bool xin = tid < RS * (P / 2) && tid / (P / 2) < R;
     const unsigned rx = xin ? load_stream(&xt32[tid]) : 0u, rxp = xin ? xp32[tid] : 0u;
 
     const int nt0 = (w >> 1) * NTW;  // the wave's first row tile
@@ -752,7 +536,7 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
 #pragma unroll
     for (int it = 0; it < NBI; ++it) {
         const int e = tid + NTH * it;
-        if (e >= 4 * K) break;  // whole lane groups
+        if (e >= RS * K) break;  // whole lane groups
         const int r = e / K, j = e % K;
         if constexpr (PRO) rb[it] = norm_pair(rb[it], r, bw[it], bb2[it]);  // kept for the carry
         float sn, cs;
@@ -768,14 +552,14 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
         const unsigned gl = pk_bf16(g0 - bf_lo(gh), g1 - bf_hi(gh)), ql = pk_bf16(q0 - bf_lo(qh), q1 - bf_hi(qh));
         sA[2 * j][r] = uint16_t(gh);
         sA[2 * j + 1][r] = uint16_t(gh >> 16);
-        sA[2 * j][4 + r] = uint16_t(gl);
-        sA[2 * j + 1][4 + r] = uint16_t(gl >> 16);
-        sA[2 * j][8 + r] = uint16_t(qh);
-        sA[2 * j + 1][8 + r] = uint16_t(qh >> 16);
-        sA[2 * j][12 + r] = uint16_t(ql);
-        sA[2 * j + 1][12 + r] = uint16_t(ql >> 16);
+        sA[2 * j][RS + r] = uint16_t(gl);
+        sA[2 * j + 1][RS + r] = uint16_t(gl >> 16);
+        sA[2 * j][2 * RS + r] = uint16_t(qh);
+        sA[2 * j + 1][2 * RS + r] = uint16_t(qh >> 16);
+        sA[2 * j][3 * RS + r] = uint16_t(ql);
+        sA[2 * j + 1][3 * RS + r] = uint16_t(ql >> 16);
     }
-    if (tid < 4 * (P / 2)) {
+    if (tid < RS * (P / 2)) {
         const int r = tid / (P / 2), j = tid % (P / 2);
         sXt[2 * j][r] = uint16_t(rx);
         sXt[2 * j + 1][r] = uint16_t(rx >> 16);
@@ -792,9 +576,17 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
     }
     __syncthreads();
 
-    // B operand of the input MFMA: k = 8 g2 .. 8 g2 + 7 -> ranks 0..3 of x twice (g2 0) or of x_prev twice (g2 1)
-    const u32x2 xr = *reinterpret_cast<const u32x2*>(g2 == 0 ? &sXt[p][0] : &sXpt[p][0]);
-    const u32x4 bx = {xr[0], xr[1], xr[0], xr[1]};
+    // B operand of the input MFMA(s): k = 8 g2 .. 8 g2 + 7 -> RS 4: ranks 0..3 of x twice (g2 0) or of
+    // x_prev twice (g2 1); RS 8: ranks 0..7 of x (against the gamma B terms) and of x_prev (second MFMA)
+    u32x4 bx, bxp;
+    if constexpr (RS == 4) {
+        const u32x2 xr = *reinterpret_cast<const u32x2*>(g2 == 0 ? &sXt[p][0] : &sXpt[p][0]);
+        bx = u32x4{xr[0], xr[1], xr[0], xr[1]};
+        bxp = bx;
+    } else {
+        bx = *reinterpret_cast<const u32x4*>(&sXt[p][0]);
+        bxp = *reinterpret_cast<const u32x4*>(&sXpt[p][0]);
+    }
     const int rcl = l32 < R ? l32 : 0;
     const u32x2 zero = {0u, 0u};
     floatx16 yacc;
@@ -807,6 +599,7 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
 #pragma unroll
         for (int v = 0; v < 16; ++v) M[v] = 0.f;
         M = mfma32_k16(*reinterpret_cast<const u32x4*>(&sA[n0 + l32][8 * g2]), bx, M);
+        if constexpr (RS == 8) M = mfma32_k16(*reinterpret_cast<const u32x4*>(&sA[n0 + l32][16 + 8 * g2]), bxp, M);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r0 = n0 + 8 * j + 4 * g2;  // the lane's rows r0 .. r0 + 3: pairs r0 / 2, r0 / 2 + 1
@@ -829,17 +622,19 @@ decode_mfma32_kernel(float* __restrict__ hstate, bf16_t* __restrict__ carry_B, b
             yacc = mfma32_k16(u32x4{cv[0], cv[1], cv[0], cv[1]}, hl, yacc);
         }
     }
-    // lane (l32, 0) holds the partial y[r = v][p] in yacc[v], v < 4
-    if (w >= 2 && g2 == 0)
+    // lane (l32, g2) holds the partial y[r = 4 g2 + e][p] in yacc[e], e < 4
+    if (w >= 2 && 4 * g2 < RS)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sY[w & 1][r][l32] = yacc[r];
+        for (int e = 0; e < 4; ++e) sY[w & 1][4 * g2 + e][l32] = yacc[e];
     __syncthreads();
-    if (w < 2 && g2 == 0) {
+    if (w < 2 && 4 * g2 < R) {
         const float Dh = D[h];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g2 + e;
+            if (r >= R) break;
             const float xv = __uint_as_float(unsigned(sXt[p][r]) << 16);
-            store_stream(y, bh * (R * P) + r * P + p, (yacc[r] + sY[w][r][l32]) + Dh * xv);
+            store_stream(y, bh * (R * P) + r * P + p, (yacc[e] + sY[w][r][l32]) + Dh * xv);
         }
     }
 
@@ -995,14 +790,13 @@ using MfmaKern = void (*)(float*, bf16_t*, bf16_t*, unsigned*, int, DecodeProlog
                           const float*, const float*, const float*, const bf16_t*, const bf16_t*, const float*,
                           bf16_t*, int64_t, int, int);
 
-// R 2-4 (fused step included) on the merged-input kernel, R 8 on the one with
-// separate input sums.
+// R 2-4 and 8 (fused step included) on the 32 x 32 kernel.
 template <int N, bool PRO>
 MfmaKern<PRO> mfma_kernel_for(int R) {
     return R == 2 ? decode_mfma32_kernel<2, N, PRO>
          : R == 3 ? decode_mfma32_kernel<3, N, PRO>
          : R == 4 ? decode_mfma32_kernel<4, N, PRO>
-                  : decode_mfma_kernel<8, N, PRO>;
+                  : decode_mfma32_kernel<8, N, PRO>;
 }
 
 template <typename T, bool PRO>
