@@ -39,8 +39,8 @@ MEASURED_TRAFFIC = {
     "prefill1": ("f96f57ce3e0e1d1f", (2.0 * 39182.0 + 73728.0) * 1024),
     "prefill2": ("91c0da9e1364c8c6", (2.0 * 150050.3 + 270336.0) * 1024),
     "long": ("91c0da9e1364c8c6", (2.0 * 744735.6 + 1079920.3) * 1024),
-    "decode1": ("92a882cb76dfe9f3", (2.0 * 133328.9 + 264562.8) * 1024),
-    "decode4": ("92a882cb76dfe9f3", (2.0 * 137559.5 + 270876.3) * 1024),
+    "decode1": ("0d01cb79fbad41c3", (2.0 * 133328.6 + 264563.3) * 1024),
+    "decode4": ("0d01cb79fbad41c3", (2.0 * 137557.3 + 270875.6) * 1024),
 }
 
 
